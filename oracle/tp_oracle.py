@@ -1,0 +1,292 @@
+"""CPU oracle for one rank of a Megatron-style tensor-parallel transformer block.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
+execute this module: only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` use it.  It shares no code with the HIP
+library; the two meet only in the seeded inputs of
+``megatron_tensor_transformer_colwise_amd/inputs.py``.
+
+Everything here is plain numpy in float64 on the exact input values (bf16
+inputs are widened exactly).  Intermediates are not rounded to bf16.  Where a
+step has a plain definition it is that definition written out; sharding is
+done here from the unsharded tensors, on its own.
+
+Sources (the "Tensor parallelism" page of itwiki, by section):
+
+* "Matmul split": a column-parallel linear splits ``A = [A_1 ... A_t]`` by
+  columns and rank i computes ``X A_i`` from the full input; a row-parallel
+  linear splits ``A`` by rows, rank i computes ``X_i A_i`` and the result is the
+  sum over ranks.
+* "MLP": ``Z = GeLU(X A) B``; with A split by columns and B by rows,
+  ``Z = sum_i GeLU(X A_i) B_i``; splitting A by rows instead would need a sync
+  before the GeLU.  The same split holds for the SwiGLU form
+  ``W2 (SiLU(X W1) * X W3)`` with W1, W3 by columns and W2 by rows.
+* "Self-attention": heads are independent; Q, K, V projections are split by
+  columns so each rank holds a/t heads, o_proj is split by rows and summed.  a
+  must be divisible by t.  With grouped-query attention, KV heads are
+  replicated across ranks when there are fewer KV heads than t.
+* "f and g": norms and residual connections are replicated on every rank; a
+  block has one sum after attention and one after the MLP.
+
+Readings where the pages say nothing (each stated where it is used):
+erf GeLU (the page's example uses PyTorch's default GeLU, which is the erf
+form); softmax scale 1/sqrt(d); query j uses KV head floor(j / (a/kv)); RoPE in
+the rotate-half form with positions restarting in every sequence; RMSNorm
+``x / sqrt(mean(x^2) + eps) * gain``; pre-norm residual structure; the
+shard-sum adds partials in ascending rank order.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+from scipy.special import erf as _erf
+
+# --------------------------------------------------------------------------
+# scalar nonlinearities
+# --------------------------------------------------------------------------
+
+
+def gelu(x):
+    """GeLU(x) = x * Phi(x) = x/2 * (1 + erf(x / sqrt 2)).
+
+    The page's MLP example calls PyTorch's default GeLU, which is this exact
+    erf form (not the tanh approximation)."""
+    x = np.asarray(x, dtype=np.float64)
+    return 0.5 * x * (1.0 + _erf(x / math.sqrt(2.0)))
+
+
+def silu(x):
+    """SiLU(x) = x * sigmoid(x), the gate of the SwiGLU MLP ("MLP" section)."""
+    x = np.asarray(x, dtype=np.float64)
+    return x / (1.0 + np.exp(-x))
+
+
+# --------------------------------------------------------------------------
+# sharding ("Matmul split")
+# --------------------------------------------------------------------------
+
+
+def split_columns(a: np.ndarray, t: int) -> list[np.ndarray]:
+    """Column-parallel shards A_1..A_t: equal contiguous column blocks."""
+    n = a.shape[1]
+    if n % t:
+        raise ValueError(f"{n} columns do not split {t} ways")
+    w = n // t
+    return [a[:, i * w:(i + 1) * w] for i in range(t)]
+
+
+def split_rows(b: np.ndarray, t: int) -> list[np.ndarray]:
+    """Row-parallel shards B_1..B_t: equal contiguous row blocks."""
+    n = b.shape[0]
+    if n % t:
+        raise ValueError(f"{n} rows do not split {t} ways")
+    w = n // t
+    return [b[i * w:(i + 1) * w, :] for i in range(t)]
+
+
+def shard_sum(partials) -> np.ndarray:
+    """The sum over ranks that the all-reduce produces, in ascending rank order."""
+    out = np.array(partials[0], dtype=np.float64, copy=True)
+    for p in partials[1:]:
+        out = out + p
+    return out
+
+
+def shard_sum_f32(partials, residual=None) -> np.ndarray:
+    """The same sum carried out in float32 with one rounding per add, ascending
+    rank order, then the residual added last.  This is the precision and order
+    the GPU shard-sum uses, so integer-free inputs can be compared bit for bit."""
+    out = np.array(partials[0], dtype=np.float32, copy=True)
+    for p in partials[1:]:
+        out = (out + np.asarray(p, dtype=np.float32)).astype(np.float32)
+    if residual is not None:
+        out = (out + np.asarray(residual, dtype=np.float32)).astype(np.float32)
+    return out
+
+
+# --------------------------------------------------------------------------
+# MLP ("MLP" section)
+# --------------------------------------------------------------------------
+
+
+def mlp_gelu(x, a, b) -> np.ndarray:
+    """Z = GeLU(X A) B.  With the full A and B this is the unsharded layer; with
+    A_i and B_i it is rank i's partial."""
+    return gelu(x @ a) @ b
+
+
+def mlp_gelu_partials(x, a, b, t: int) -> list[np.ndarray]:
+    """partial_i = GeLU(X A_i) B_i for the column shards of A and row shards of B."""
+    return [mlp_gelu(x, ai, bi) for ai, bi in zip(split_columns(a, t), split_rows(b, t))]
+
+
+def mlp_gelu_row_split(x, a, t: int) -> tuple[np.ndarray, np.ndarray]:
+    """The split the page rules out: A by rows, X by columns.  Returns
+    (GeLU(sum_i X_i A_i), sum_i GeLU(X_i A_i)), which differ in general."""
+    xs = split_columns(x, t)
+    aps = split_rows(a, t)
+    pre = [xi @ ai for xi, ai in zip(xs, aps)]
+    return gelu(shard_sum(pre)), shard_sum([gelu(p) for p in pre])
+
+
+def colwise_act(x, w_in, act: str, w_gate_up=None) -> np.ndarray:
+    """Rank-local colwise output Y_i: GeLU(X A_i), or SiLU(X W1_i) * (X W3_i)."""
+    if act == "gelu":
+        return gelu(x @ w_in)
+    if act == "swiglu":
+        w1, w3 = w_gate_up
+        return silu(x @ w1) * (x @ w3)
+    if act == "none":
+        return x @ w_in
+    raise ValueError(act)
+
+
+def mlp_swiglu(x, w1, w3, w2) -> np.ndarray:
+    """Z = (SiLU(X W1) * (X W3)) W2; full weights give the unsharded layer."""
+    return (silu(x @ w1) * (x @ w3)) @ w2
+
+
+def mlp_swiglu_partials(x, w1, w3, w2, t: int) -> list[np.ndarray]:
+    """partial_i with W1, W3 split by columns and W2 by rows."""
+    return [
+        mlp_swiglu(x, a, c, b)
+        for a, c, b in zip(split_columns(w1, t), split_columns(w3, t), split_rows(w2, t))
+    ]
+
+
+# --------------------------------------------------------------------------
+# attention ("Self-attention" section)
+# --------------------------------------------------------------------------
+
+
+def kv_head_of(j: int, heads: int, kv_heads: int) -> int:
+    """KV head used by query head j: consecutive groups of heads/kv_heads query
+    heads share one KV head (reading; the page only says KV heads must be
+    taken into account and replicated when fewer than t)."""
+    return j // (heads // kv_heads)
+
+
+def rank_query_heads(rank: int, heads: int, t: int) -> list[int]:
+    """Query heads of a rank: a/t consecutive heads; t must divide a."""
+    if heads % t:
+        raise ValueError(f"t={t} does not divide {heads} heads")
+    hq = heads // t
+    return list(range(rank * hq, (rank + 1) * hq))
+
+
+def rank_kv_heads(rank: int, heads: int, kv_heads: int, t: int) -> list[int]:
+    """KV heads a rank must hold: those its query heads use.  With fewer KV
+    heads than t the same KV head appears on several ranks (replication)."""
+    return sorted({kv_head_of(j, heads, kv_heads) for j in rank_query_heads(rank, heads, t)})
+
+
+def rope(x: np.ndarray, pos: np.ndarray, base: float) -> np.ndarray:
+    """Rotary position embedding, rotate-half form (reading: the pages do not
+    name RoPE's convention).  x [..., n, d], pos [n]; the pair (k, k + d/2) is
+    rotated by the angle pos * base^(-2k/d)."""
+    d = x.shape[-1]
+    half = d // 2
+    k = np.arange(half, dtype=np.float64)
+    theta = base ** (-2.0 * k / d)
+    ang = np.asarray(pos, dtype=np.float64)[:, None] * theta[None, :]
+    c, s = np.cos(ang), np.sin(ang)
+    x1, x2 = x[..., :half], x[..., half:]
+    return np.concatenate([x1 * c - x2 * s, x2 * c + x1 * s], axis=-1)
+
+
+def causal_attention(q, k, v, q_pos=None) -> np.ndarray:
+    """softmax(q k^T / sqrt(d)) v with key p' visible to query p iff p' <= p.
+
+    q [nq, d] at positions q_pos (default 0..nq-1); k, v [n, d] at 0..n-1."""
+    d = q.shape[-1]
+    nq = q.shape[0]
+    if q_pos is None:
+        q_pos = np.arange(nq)
+    s = (q @ k.T) / math.sqrt(d)
+    mask = np.arange(k.shape[0])[None, :] > np.asarray(q_pos)[:, None]
+    s = np.where(mask, -np.inf, s)
+    s = s - s.max(axis=1, keepdims=True)
+    p = np.exp(s)
+    p = p / p.sum(axis=1, keepdims=True)
+    return p @ v
+
+
+def attn_heads_output(x, wq, wk, wv, heads: int, kv_heads: int, head_dim: int,
+                      batch: int, seq: int, rope_base: float, q_heads: list[int],
+                      rows=None) -> np.ndarray:
+    """Concatenated outputs of the given query heads, [len(rows), len(q_heads)*d].
+
+    x [batch*seq, h]; wq [h, heads*d]; wk, wv [h, kv_heads*d] (math convention).
+    ``rows`` selects output token rows (default: all); K and V are still
+    computed for every token, since a row sees its whole causal prefix."""
+    d = head_dim
+    m = batch * seq
+    rows = np.arange(m) if rows is None else np.asarray(rows)
+    out = np.zeros((len(rows), len(q_heads) * d))
+    pos_all = np.arange(seq)
+    kv_needed = sorted({kv_head_of(j, heads, kv_heads) for j in q_heads})
+    for b in range(batch):
+        sel = np.nonzero((rows >= b * seq) & (rows < (b + 1) * seq))[0]
+        if len(sel) == 0:
+            continue
+        xb = x[b * seq:(b + 1) * seq]
+        qpos = rows[sel] - b * seq
+        kv = {}
+        for g in kv_needed:
+            kh = rope(xb @ wk[:, g * d:(g + 1) * d], pos_all, rope_base)
+            vh = xb @ wv[:, g * d:(g + 1) * d]
+            kv[g] = (kh, vh)
+        xq = xb[qpos]
+        for c, j in enumerate(q_heads):
+            qh = rope(xq @ wq[:, j * d:(j + 1) * d], qpos, rope_base)
+            kh, vh = kv[kv_head_of(j, heads, kv_heads)]
+            out[sel, c * d:(c + 1) * d] = causal_attention(qh, kh, vh, qpos)
+    return out
+
+
+def attn_partial(x, w: dict, case, rank: int, t: int | None = None, rows=None) -> np.ndarray:
+    """Rank ``rank``'s o_proj partial: the outputs of its a/t heads times the
+    rows of Wo that belong to those heads.  ``t = 1`` gives the unsharded layer."""
+    t = case.t if t is None else t
+    q_heads = rank_query_heads(rank, case.heads, t)
+    o = attn_heads_output(x, w["Wq"], w["Wk"], w["Wv"], case.heads, case.kv_heads,
+                          case.head_dim, case.batch, case.seq, case.rope_base, q_heads, rows)
+    d = case.head_dim
+    wo_rows = w["Wo"][q_heads[0] * d:(q_heads[-1] + 1) * d]
+    return o @ wo_rows
+
+
+# --------------------------------------------------------------------------
+# norm and block ("f and g": norms and residuals are replicated)
+# --------------------------------------------------------------------------
+
+
+def rmsnorm(x, gain=None, eps: float = 1e-5) -> np.ndarray:
+    """x / sqrt(mean(x^2) + eps) * gain, per row (reading: eps and the gain are
+    not given by the pages)."""
+    x = np.asarray(x, dtype=np.float64)
+    r = 1.0 / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)
+    y = x * r
+    if gain is not None:
+        y = y * np.asarray(gain, dtype=np.float64)
+    return y
+
+
+def block(x, w: dict, case, t: int | None = None, rows=None) -> dict:
+    """One pre-norm block computed rank by rank and summed:
+
+    h1 = X + sum_i Attn_i(RMSNorm(X)),  Z = h1 + sum_i MLP_i(RMSNorm(h1)).
+
+    Returns the sampled rows of h1 and Z (all rows by default); ``t = 1`` is
+    the unsharded block."""
+    t = case.t if t is None else t
+    m = case.tokens
+    rows = np.arange(m) if rows is None else np.asarray(rows)
+    xn = rmsnorm(x, w.get("g_attn"), case.eps)
+    attn_parts = [attn_partial(xn, w, case, r, t, rows) for r in range(t)]
+    h1 = x[rows] + shard_sum(attn_parts)
+    hn = rmsnorm(h1, w.get("g_mlp"), case.eps)
+    mlp_parts = mlp_swiglu_partials(hn, w["W1"], w["W3"], w["W2"], t)
+    z = h1 + shard_sum(mlp_parts)
+    return {"h1": h1, "z": z, "attn_partials": attn_parts, "mlp_partials": mlp_parts}

@@ -1,0 +1,346 @@
+"""Pins of the CPU oracle to facts fixed outside it.
+
+Each test checks the oracle against something other than itself: the worked
+example of the "Tensor parallelism" page (section "MLP"), closed forms,
+invariants, textbook constants, PyTorch CPU library routines in float64, or
+brute-force scalar loops on tiny inputs.  None of these needs a GPU.
+"""
+import json
+import math
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle
+from megatron_tensor_transformer_colwise_amd import inputs
+
+GOLDEN = __import__("pathlib").Path(__file__).parent / "golden"
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+# ---------------------------------------------------------------- worked example
+
+
+def test_worked_example_predicate_holds():
+    """The page's example: seed 0, b,h,t = 4,16,4; the summed partials match the
+    unsharded GeLU(XA)B under allclose(atol=1e-4), printed as True.
+
+    The page's program is restated in torch float32 (its dtype) and compared
+    with the oracle's float64 results on the same inputs, so the oracle's GeLU,
+    split and sum are checked against PyTorch's."""
+    g = json.loads((GOLDEN / "mlp_identity_example.json").read_text())
+    b, h, t = g["b"], g["h"], g["t"]
+    torch.manual_seed(0)
+    X = torch.randn(b, h)
+    A = torch.randn(h, 4 * h)
+    B = torch.randn(4 * h, h)
+    ref_t = F.gelu(X @ A) @ B
+    out_t = sum(F.gelu(X @ ai) @ bi for ai, bi in zip(A.chunk(t, dim=1), B.chunk(t, dim=0)))
+    assert torch.allclose(out_t, ref_t, atol=g["atol"], rtol=g["rtol"]) == (g["printed"] == "True")
+
+    # same inputs through the shared generator
+    case = inputs.CONFIGS["tiny_mlp_f32"]
+    w = inputs.gen_mlp(case)
+    assert np.array_equal(w["X"].data, X.numpy())
+    assert np.array_equal(w["A"].data, A.numpy())
+    assert np.array_equal(w["B"].data, B.numpy())
+
+    x, a, bb = w["X"].f64(), w["A"].f64(), w["B"].f64()
+    ref = oracle.mlp_gelu(x, a, bb)
+    parts = oracle.mlp_gelu_partials(x, a, bb, t)
+    out = oracle.shard_sum(parts)
+    # the page's predicate on the oracle's own sharded vs unsharded results
+    assert np.allclose(out, ref, atol=g["atol"], rtol=g["rtol"])
+    # the oracle agrees with PyTorch's float32 evaluation of the same program
+    assert np.max(np.abs(ref - ref_t.double().numpy())) < 1e-4
+    assert np.max(np.abs(out - out_t.double().numpy())) < 1e-4
+    for p, (ai, bi) in zip(parts, zip(A.chunk(t, 1), B.chunk(t, 0))):
+        assert np.max(np.abs(p - (F.gelu(X @ ai) @ bi).double().numpy())) < 1e-4
+
+
+def test_row_split_negative_control():
+    """Splitting A by rows does not commute with GeLU: GeLU(sum X_i A_i) differs
+    from sum GeLU(X_i A_i) by far more than the tolerance ("MLP" section)."""
+    w = inputs.gen_mlp(inputs.CONFIGS["tiny_mlp_f32"])
+    lhs, rhs = oracle.mlp_gelu_row_split(w["X"].f64(), w["A"].f64(), 4)
+    assert np.max(np.abs(lhs - rhs)) > 1.0
+    # while the column split of the same A is exact
+    x, a = w["X"].f64(), w["A"].f64()
+    cols = np.concatenate([oracle.gelu(x @ ai) for ai in oracle.split_columns(a, 4)], axis=1)
+    assert np.max(np.abs(cols - oracle.gelu(x @ a))) < 1e-12
+
+
+# ---------------------------------------------------------------- scalar functions
+
+
+def test_gelu_closed_forms_and_library():
+    x = np.linspace(-8, 8, 4001)
+    gx = oracle.gelu(x)
+    assert oracle.gelu(0.0) == 0.0
+    # erf is odd, so GeLU(x) - GeLU(-x) = x
+    assert np.max(np.abs(gx - oracle.gelu(-x) - x)) < 1e-14
+    # GeLU(1) = Phi(1), the standard normal CDF at 1 (textbook value)
+    assert abs(oracle.gelu(1.0) - 0.8413447460685429) < 1e-15
+    # GeLU(x)/x -> 1 and GeLU(-x) -> 0 for large x
+    assert abs(oracle.gelu(40.0) / 40.0 - 1.0) < 1e-15
+    assert abs(oracle.gelu(-40.0)) < 1e-300
+    # PyTorch's default (erf) GeLU in float64
+    ref = F.gelu(torch.from_numpy(x)).numpy()
+    assert np.max(np.abs(gx - ref)) < 1e-14
+    # and not the tanh approximation
+    tanh = F.gelu(torch.from_numpy(x), approximate="tanh").numpy()
+    assert np.max(np.abs(gx - tanh)) > 1e-4
+
+
+def test_silu_closed_forms_and_library():
+    x = np.linspace(-30, 30, 3001)
+    s = oracle.silu(x)
+    assert oracle.silu(0.0) == 0.0
+    assert np.max(np.abs(s - oracle.silu(-x) - x)) < 1e-12
+    assert abs(oracle.silu(1.0) - 1.0 / (1.0 + math.exp(-1.0))) < 1e-16
+    assert np.max(np.abs(s - F.silu(torch.from_numpy(x)).numpy())) < 1e-13
+
+
+# ---------------------------------------------------------------- MLP identities
+
+
+def test_gelu_mlp_split_identity_and_brute_force():
+    r = _rng(1)
+    m, h, f, t = 7, 24, 48, 4
+    x, a, b = r.standard_normal((m, h)), r.standard_normal((h, f)), r.standard_normal((f, h))
+    parts = oracle.mlp_gelu_partials(x, a, b, t)
+    full = oracle.mlp_gelu(x, a, b)
+    assert np.max(np.abs(oracle.shard_sum(parts) - full)) <= 1e-12 * np.max(np.abs(full))
+
+    # brute force: scalar loops over one shard of a tiny case
+    m, h, f, t = 2, 4, 8, 2
+    x, a, b = r.standard_normal((m, h)), r.standard_normal((h, f)), r.standard_normal((f, h))
+    parts = oracle.mlp_gelu_partials(x, a, b, t)
+    fs = f // t
+    for i in range(t):
+        for row in range(m):
+            for col in range(h):
+                acc = 0.0
+                for j in range(fs):
+                    u = sum(x[row, k] * a[k, i * fs + j] for k in range(h))
+                    acc += 0.5 * u * (1 + math.erf(u / math.sqrt(2))) * b[i * fs + j, col]
+                assert abs(parts[i][row, col] - acc) < 1e-12
+
+
+def test_swiglu_mlp_split_identity_and_brute_force():
+    r = _rng(2)
+    m, h, f, t = 9, 32, 64, 8
+    x = r.standard_normal((m, h))
+    w1, w3, w2 = (r.standard_normal(s) for s in ((h, f), (h, f), (f, h)))
+    parts = oracle.mlp_swiglu_partials(x, w1, w3, w2, t)
+    full = oracle.mlp_swiglu(x, w1, w3, w2)
+    assert np.max(np.abs(oracle.shard_sum(parts) - full)) <= 1e-12 * np.max(np.abs(full))
+    # gate and up swapped gives a different layer (the operands are not symmetric)
+    assert np.max(np.abs(oracle.mlp_swiglu(x, w3, w1, w2) - full)) > 1e-3
+
+    m, h, f, t = 2, 3, 4, 2
+    x = r.standard_normal((m, h))
+    w1, w3, w2 = (r.standard_normal(s) for s in ((h, f), (h, f), (f, h)))
+    parts = oracle.mlp_swiglu_partials(x, w1, w3, w2, t)
+    fs = f // t
+    for i in range(t):
+        for row in range(m):
+            for col in range(h):
+                acc = 0.0
+                for j in range(fs):
+                    g = sum(x[row, k] * w1[k, i * fs + j] for k in range(h))
+                    u = sum(x[row, k] * w3[k, i * fs + j] for k in range(h))
+                    acc += g / (1 + math.exp(-g)) * u * w2[i * fs + j, col]
+                assert abs(parts[i][row, col] - acc) < 1e-12
+
+
+def test_shard_sum_orders_and_precision():
+    r = _rng(3)
+    ints = [r.integers(-1000, 1000, size=257).astype(np.float32) for _ in range(16)]
+    exact = np.sum(np.stack(ints).astype(np.int64), axis=0)
+    assert np.array_equal(oracle.shard_sum_f32(ints), exact.astype(np.float32))
+    assert np.array_equal(oracle.shard_sum(ints), exact.astype(np.float64))
+    ps = [r.standard_normal(1000).astype(np.float32) for _ in range(8)]
+    res = r.standard_normal(1000).astype(np.float32)
+    exact = oracle.shard_sum([p.astype(np.float64) for p in ps]) + res
+    got = oracle.shard_sum_f32(ps, res).astype(np.float64)
+    bound = 9 * np.finfo(np.float32).eps * (np.sum(np.abs(np.stack(ps)), axis=0) + np.abs(res))
+    assert np.all(np.abs(got - exact) <= bound)
+
+
+# ---------------------------------------------------------------- RoPE
+
+
+def test_rope_invariants_and_complex_form():
+    r = _rng(4)
+    d, n, base = 16, 12, 500000.0
+    x = r.standard_normal((n, d))
+    pos = np.arange(n) * 37
+    y = oracle.rope(x, pos, base)
+    # position 0 is the identity
+    assert np.array_equal(oracle.rope(x[:1], np.array([0]), base), x[:1])
+    # rotation preserves the norm of every vector
+    assert np.allclose(np.linalg.norm(y, axis=1), np.linalg.norm(x, axis=1), rtol=1e-13)
+    # the pair (k, k + d/2) is the complex number x_k + i x_{k+d/2} times e^{i p theta_k}
+    half = d // 2
+    theta = base ** (-np.arange(half) * 2.0 / d)
+    z = (x[:, :half] + 1j * x[:, half:]) * np.exp(1j * pos[:, None] * theta[None, :])
+    assert np.allclose(y[:, :half], z.real, atol=1e-12)
+    assert np.allclose(y[:, half:], z.imag, atol=1e-12)
+    # q(m) . k(n) depends only on m - n
+    q, k = r.standard_normal(d), r.standard_normal(d)
+    dots = [oracle.rope(q[None], np.array([m]), base)[0] @ oracle.rope(k[None], np.array([m - 5]), base)[0]
+            for m in (5, 9, 300)]
+    assert np.allclose(dots, dots[0], rtol=1e-11)
+
+
+# ---------------------------------------------------------------- attention
+
+
+def test_causal_attention_special_cases_and_sdpa():
+    r = _rng(5)
+    n, d = 10, 8
+    q, k, v = r.standard_normal((n, d)), r.standard_normal((n, d)), r.standard_normal((n, d))
+    o = oracle.causal_attention(q, k, v)
+    # query 0 sees only key 0
+    assert np.allclose(o[0], v[0], atol=1e-15)
+    # zero keys give the running mean of the values
+    oz = oracle.causal_attention(q, np.zeros_like(k), v)
+    assert np.allclose(oz, np.cumsum(v, axis=0) / np.arange(1, n + 1)[:, None], atol=1e-14)
+    # PyTorch's scaled_dot_product_attention (float64, causal)
+    ref = F.scaled_dot_product_attention(*(torch.from_numpy(a)[None, None] for a in (q, k, v)),
+                                         is_causal=True)[0, 0].numpy()
+    assert np.max(np.abs(o - ref)) < 1e-13
+    # brute force for one query row
+    p = 6
+    s = [sum(q[p, e] * k[j, e] for e in range(d)) / math.sqrt(d) for j in range(p + 1)]
+    mx = max(s)
+    wgt = [math.exp(u - mx) for u in s]
+    tot = sum(wgt)
+    bf = [sum(wgt[j] / tot * v[j, e] for j in range(p + 1)) for e in range(d)]
+    assert np.allclose(o[p], bf, atol=1e-14)
+
+
+def test_gqa_head_mapping_matches_sdpa_enable_gqa():
+    """Query head j uses KV head floor(j / (a/kv)), which is PyTorch's grouping
+    in scaled_dot_product_attention(enable_gqa=True)."""
+    r = _rng(6)
+    heads, kvh, d, n = 8, 2, 4, 6
+    q = r.standard_normal((heads, n, d))
+    k = r.standard_normal((kvh, n, d))
+    v = r.standard_normal((kvh, n, d))
+    ref = F.scaled_dot_product_attention(torch.from_numpy(q)[None], torch.from_numpy(k)[None],
+                                         torch.from_numpy(v)[None], is_causal=True,
+                                         enable_gqa=True)[0].numpy()
+    for j in range(heads):
+        g = oracle.kv_head_of(j, heads, kvh)
+        assert np.max(np.abs(oracle.causal_attention(q[j], k[g], v[g]) - ref[j])) < 1e-13
+    assert [oracle.kv_head_of(j, heads, kvh) for j in range(heads)] == [0, 0, 0, 0, 1, 1, 1, 1]
+
+
+@pytest.mark.parametrize("t", [1, 2, 4, 8, 16])
+def test_head_split_attention_identity(t):
+    """sum over ranks of the o_proj partials equals unsharded attention,
+    including t = 16 > kv_heads where a KV head is replicated on two ranks."""
+    case = inputs.AttnCase("tiny", batch=2, seq=9, hidden=32, heads=16, kv_heads=8, head_dim=8,
+                           t=t, rope_base=10000.0, seed=11, dtype="f32", w_std=0.3)
+    w = {k: v.f64() for k, v in inputs.gen_attn(case).items()}
+    full = oracle.attn_partial(w["X"], w, case, 0, t=1)
+    parts = [oracle.attn_partial(w["X"], w, case, rk, t=t) for rk in range(t)]
+    assert np.max(np.abs(oracle.shard_sum(parts) - full)) <= 1e-12 * np.max(np.abs(full))
+    if t == 16:
+        assert oracle.rank_kv_heads(0, 16, 8, 16) == oracle.rank_kv_heads(1, 16, 8, 16) == [0]
+    # sampled rows equal the same rows of the full computation
+    rows = np.array([0, 4, 8, 9, 17])
+    part_rows = oracle.attn_partial(w["X"], w, case, 0, t=t, rows=rows)
+    assert np.max(np.abs(part_rows - parts[0][rows])) < 1e-13
+
+
+def test_attention_brute_force_with_rope():
+    """One head of a tiny layer from scalar loops: projections, rotate-half RoPE,
+    causal softmax, value sum and o_proj."""
+    case = inputs.AttnCase("bf", batch=1, seq=4, hidden=6, heads=2, kv_heads=1, head_dim=4,
+                           t=2, rope_base=100.0, seed=12, dtype="f32", w_std=0.5)
+    w = {k: v.f64() for k, v in inputs.gen_attn(case).items()}
+    x, d, S = w["X"], 4, 4
+    got = oracle.attn_partial(x, w, case, 1, t=2)   # rank 1: query head 1, KV head 0
+    j, g = 1, 0
+
+    def proj(wm, col0, p):
+        return [sum(x[p, e] * wm[e, col0 + c] for e in range(6)) for c in range(d)]
+
+    def rot(vec, p):
+        out = list(vec)
+        for kk in range(d // 2):
+            th = 100.0 ** (-2.0 * kk / d)
+            c, s = math.cos(p * th), math.sin(p * th)
+            out[kk] = vec[kk] * c - vec[kk + d // 2] * s
+            out[kk + d // 2] = vec[kk + d // 2] * c + vec[kk] * s
+        return out
+
+    for p in range(S):
+        qv = rot(proj(w["Wq"], j * d, p), p)
+        ks = [rot(proj(w["Wk"], g * d, pp), pp) for pp in range(p + 1)]
+        vs = [proj(w["Wv"], g * d, pp) for pp in range(p + 1)]
+        sc = [sum(a * b for a, b in zip(qv, kk)) / 2.0 for kk in ks]
+        mx = max(sc)
+        e = [math.exp(s - mx) for s in sc]
+        o = [sum(e[i] * vs[i][c] for i in range(p + 1)) / sum(e) for c in range(d)]
+        for col in range(6):
+            ref = sum(o[c] * w["Wo"][j * d + c, col] for c in range(d))
+            assert abs(got[p, col] - ref) < 1e-12
+
+
+# ---------------------------------------------------------------- RMSNorm and block
+
+
+def test_rmsnorm_closed_form_and_library():
+    r = _rng(7)
+    x = r.standard_normal((5, 64)) * 3
+    eps = 1e-5
+    y = oracle.rmsnorm(x, None, eps)
+    ms = np.mean(x * x, axis=1)
+    assert np.allclose(np.sqrt(np.mean(y * y, axis=1)), np.sqrt(ms / (ms + eps)), rtol=1e-13)
+    gain = 1 + 0.1 * r.standard_normal(64)
+    ref = F.rms_norm(torch.from_numpy(x), (64,), torch.from_numpy(gain), eps).numpy()
+    assert np.max(np.abs(oracle.rmsnorm(x, gain, eps) - ref)) < 1e-13
+
+
+def test_block_is_t_invariant():
+    """The block computed rank by rank at t = 2, 4 and 8 equals the unsharded
+    block; sampled rows equal the full result's rows."""
+    case = inputs.BlockCase("tinyblock", batch=2, seq=6, hidden=32, heads=8, kv_heads=2,
+                            head_dim=4, inter=64, t=4, rope_base=10000.0, seed=13, gain_std=0.1,
+                            dtype="f32", w_std=0.2)
+    w = {k: v.f64() for k, v in inputs.gen_block(case).items()}
+    ref = oracle.block(w["X"], w, case, t=1)["z"]
+    for t in (2, 4, 8):
+        z = oracle.block(w["X"], w, case, t=t)["z"]
+        assert np.max(np.abs(z - ref)) <= 1e-12 * np.max(np.abs(ref))
+    rows = np.array([0, 5, 6, 11])
+    zs = oracle.block(w["X"], w, case, t=4, rows=rows)["z"]
+    assert np.max(np.abs(zs - ref[rows])) < 1e-12
+
+
+# ---------------------------------------------------------------- inputs
+
+
+def test_synthetic_inputs_are_seeded_and_gaussian():
+    a = inputs.normal(7, 3, (1000, 100), 1.0, "f32").data
+    b = inputs.normal(7, 3, (1000, 100), 1.0, "f32").data
+    c = inputs.normal(7, 4, (1000, 100), 1.0, "f32").data
+    assert np.array_equal(a, b) and not np.array_equal(a, c)
+    assert abs(a.mean()) < 0.01 and abs(a.std() - 1) < 0.01
+    # bf16 draw is the f32 draw rounded to nearest-even (checked against torch)
+    s = inputs.normal(7, 3, (1000, 100), 0.02, "f32").data
+    hb = inputs.normal(7, 3, (1000, 100), 0.02, "bf16")
+    tb = torch.from_numpy(s).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(hb.data, tb)
+    assert np.array_equal(hb.torch().float().numpy(), hb.f32())
+    ints = inputs.integers(1, 2, (64, 64), -2, 2)
+    assert set(np.unique(ints.f32())) == {-2.0, -1.0, 0.0, 1.0, 2.0}
