@@ -1,0 +1,253 @@
+"""Throughput of one tensor-parallel block shard on one MI355X.
+
+A step is one forward pass of a 70B-shaped pre-norm block (h=8192, 64 query /
+8 KV heads of 128, SwiGLU intermediate 28672, batch 4 x 2048 tokens, causal)
+at t=8, with every rank's work run on this GPU one after another:
+
+  RMSNorm(X) -> for each rank: QKV+RoPE GEMM, flash attention, o_proj GEMM
+  -> shard-sum (+X) -> RMSNorm(h1) -> for each rank: SwiGLU GEMM, down GEMM
+  -> shard-sum (+h1).
+
+``value`` is the algorithmic bf16 flop rate of the step (2 flops per
+multiply-add of every GEMM, causal attention counting only unmasked pairs)
+over the wall time of the whole step, norms and sums included.  It equals the
+per-shard rate, since the shards are identical work run back to back.
+
+The JSON line also carries the dominant kernel's roofline (the SwiGLU
+column-parallel GEMM, timed with HIP events around each of its launches on
+the stream it runs on) and the CPU oracle timed on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+from pathlib import Path
+
+REPO = Path(__file__).resolve().parent
+sys.path.insert(0, str(REPO))
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16, published
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, published
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def block_flops(case, t: int) -> dict:
+    """Algorithmic flops of one rank's share of the block, by kernel."""
+    m, h, d = case.tokens, case.hidden, case.head_dim
+    hq = case.heads // t
+    group = case.heads // case.kv_heads
+    hkv = (hq - 1) // group + 1 if hq >= group else 1
+    f = case.inter // t
+    pairs = case.seq * (case.seq + 1) / 2
+    return {
+        "qkv": 2.0 * m * h * (hq + 2 * hkv) * d,
+        "attn_core": 4.0 * d * pairs * case.batch * hq,
+        "o_proj": 2.0 * m * hq * d * h,
+        "swiglu_gemm": 2.0 * m * h * 2 * f,
+        "down_gemm": 2.0 * m * f * h,
+    }
+
+
+def cpu_baseline(case, w_host, budget_s: float = 20.0) -> dict:
+    """The float64 oracle on a bounded sample of the workload: the same block
+    (same weights, t ranks) over one sequence of S tokens, S doubled from 16
+    while the time stays within the budget."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import oracle
+    from megatron_tensor_transformer_colwise_amd import inputs
+
+    log("cpu baseline: widening weights to float64")
+    W = {k: v.f64() for k, v in w_host.items() if k != "X"}
+    x_all = w_host["X"]
+    best = None
+    s = 16
+    while True:
+        sub = inputs.BlockCase(case.name + "-sample", 1, s, case.hidden, case.heads, case.kv_heads,
+                               case.head_dim, case.inter, case.t, case.rope_base, case.seed)
+        Ws = dict(W)
+        Ws["X"] = x_all.f32()[:s].astype(np.float64)
+        t0 = time.perf_counter()
+        oracle.block(Ws["X"], Ws, sub)
+        dt = time.perf_counter() - t0
+        fl = sum(block_flops(sub, case.t).values()) * case.t
+        best = (s, dt, fl)
+        log(f"cpu baseline: {s} tokens in {dt:.2f}s")
+        if dt * 2.2 > budget_s or s >= case.seq:
+            break
+        s *= 2
+    s, dt, fl = best
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    return {
+        "value": fl / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"one sequence of {s} tokens through the same block (all {case.t} ranks, "
+                  f"float64 numpy), {fl / 1e9:.1f} GFLOP in {dt:.2f} s",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="llama70b_block_t8")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=20.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(--gpus {args.gpus} requested)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from megatron_tensor_transformer_colwise_amd import inputs, shard, tpshard as tp
+
+    if not tp.LIB_PATH.exists():
+        import __graft_entry__
+
+        __graft_entry__.build()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    tp.tp_device_check()
+
+    case = inputs.CONFIGS[args.config]
+    t = case.t
+    log(f"generating inputs for {case.name}")
+    t0 = time.time()
+    w = inputs.gen_block(case)
+    log(f"inputs drawn in {time.time() - t0:.1f}s; uploading")
+    dw = {k: v.torch().to(dev) for k, v in w.items()}
+    blk = shard.BlockShards(dw["X"], dw, case)
+    mlp, attn = blk.mlp, blk.attn
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    log("weights sharded")
+
+    ev_pairs = []
+
+    def step(record: bool):
+        blk.norm_attn()
+        attn.forward(residual=blk.x, residual_dt="bf16")
+        blk.norm_mlp()
+        for r in range(t):
+            if record:
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                mlp.colwise(r)
+                e1.record(stream)
+                ev_pairs.append((e0, e1))
+            else:
+                mlp.colwise(r)
+            mlp.rowwise(r)
+        mlp.reduce(residual=attn.out, residual_dt="f32")
+
+    for i in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    log(f"warmup done ({args.warmup} steps)")
+
+    # timed region (the dominant kernel is bracketed by events inside it)
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(args.steps):
+        step(True)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    ms_per_step = total_ms / args.steps
+    fl = block_flops(case, t)
+    step_flops = sum(fl.values()) * t
+    value = step_flops / (ms_per_step * 1e-3) / 1e12
+    col_ms = sum(a.elapsed_time(b) for a, b in ev_pairs) / len(ev_pairs)
+    col_tflops = fl["swiglu_gemm"] / (col_ms * 1e-3) / 1e12
+    log(f"step {ms_per_step:.3f} ms, {value:.1f} TFLOP/s; swiglu gemm {col_ms * 1e3:.1f} us "
+        f"= {col_tflops:.1f} TFLOP/s")
+
+    # per-call breakdown (outside the timed region)
+    def time_call(fn, reps=5):
+        fn()
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    attn_ms = time_call(lambda: attn.rank(0))
+    mlp_ms = time_call(lambda: mlp.rank(0))
+    sum_ms = time_call(lambda: mlp.reduce(residual=attn.out, residual_dt="f32"))
+    norm_ms = time_call(lambda: blk.norm_mlp())
+    n = case.tokens * case.hidden
+    detail = {
+        "attn_call_ms": round(attn_ms, 4),
+        "attn_call_tflops": round((fl["qkv"] + fl["attn_core"] + fl["o_proj"]) / attn_ms / 1e9, 1),
+        "mlp_call_ms": round(mlp_ms, 4),
+        "mlp_call_tflops": round((fl["swiglu_gemm"] + fl["down_gemm"]) / mlp_ms / 1e9, 1),
+        "shard_sum_ms": round(sum_ms, 4),
+        "shard_sum_gbs": round((t + 2) * 4 * n / sum_ms / 1e6, 1),
+        "rmsnorm_f32_ms": round(norm_ms, 4),
+        "rmsnorm_gbs": round(6 * n / norm_ms / 1e6, 1),
+    }
+    log(f"detail {detail}")
+
+    out = {
+        "metric": "TFLOP/s per TP shard (MLP + attention, bf16) and % of MFMA bf16 peak",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded Gaussian inputs and weights, no checkpoint)",
+        "pct_of_mfma_peak": round(100.0 * value / MFMA_BF16_PEAK_TFLOPS, 2),
+        "config": {
+            "workload": f"{case.name}: 70B-shaped block shard, h={case.hidden}, heads {case.heads}/"
+                        f"{case.kv_heads}x{case.head_dim}, SwiGLU {case.inter}, t={t} (all ranks "
+                        f"on one GPU), batch {case.batch} x seq {case.seq}, causal",
+            "global_batch": case.batch,
+            "seq_len": case.seq,
+            "tp": t,
+            "parallelism": f"tp{t} (ranks serialised on one GPU)",
+        },
+        "roofline": {
+            "kernel": "gemm_bf16_kernel<SWIGLU> (column-parallel W1|W3 GEMM + SwiGLU)",
+            "bound": "mfma",
+            "achieved": round(col_tflops, 2),
+            "peak": MFMA_BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(col_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+            "traffic": None,
+            "avg_launch_us": round(col_ms * 1e3, 2),
+            "flops_per_launch": fl["swiglu_gemm"],
+        },
+        "detail": detail,
+    }
+    if not args.no_cpu_baseline and int(os.environ.get("RANK", "0")) == 0:
+        out["cpu_baseline"] = cpu_baseline(case, w, args.cpu_budget)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

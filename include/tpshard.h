@@ -1,0 +1,206 @@
+/*
+ * tpshard -- one rank of a Megatron-style tensor-parallel transformer block,
+ * as HIP kernels for MI355X (gfx950) behind a plain C ABI.
+ *
+ * The operations follow the "Tensor parallelism" page of itwiki (텐서 병렬화):
+ *
+ *   section "Matmul split"  a column-parallel linear holds a block of columns
+ *                           A_i of A and computes Y_i = X A_i from the full X;
+ *                           a row-parallel linear holds a block of rows B_i and
+ *                           yields a partial sum; the sum over ranks is the
+ *                           layer output.  A column split feeds a row split
+ *                           with no exchange in between.
+ *   section "MLP"           Z = GeLU(X A) B with A by columns and B by rows:
+ *                           GeLU is applied per rank and Z = sum_i GeLU(X A_i) B_i.
+ *                           The SwiGLU form W2 (SiLU(X W1) * X W3) splits the
+ *                           same way (W1, W3 by columns, W2 by rows).
+ *   section "Self-attention" heads are split across ranks: the Q/K/V
+ *                           projections by columns (a/t heads per rank, a
+ *                           divisible by t), attention per head with no
+ *                           exchange, o_proj by rows.  With grouped-query
+ *                           attention a KV head is replicated on several ranks
+ *                           when there are fewer KV heads than ranks.
+ *   section "f and g"       the forward exchange is one all-reduce after each
+ *                           sublayer; norms and residuals are replicated.
+ *
+ * On one GPU the all-reduce is stood in for by tp_shard_sum, which adds the
+ * ranks' partials inside one device (no collective).
+ *
+ * Conventions for every call
+ * --------------------------
+ *  - Device pointers, row-major, contiguous, 16-byte aligned.  The caller owns
+ *    every buffer; the library never allocates, frees or synchronises.  Work is
+ *    enqueued on `stream` (a hipStream_t; NULL is the null stream) and the
+ *    call returns at once; buffers must stay valid until the stream passes.
+ *  - Weights are in nn.Linear layout [out_features, in_features], so both
+ *    operands of every product are contiguous along the reduction dimension.
+ *    (The pages write A as [in, out]; a rank's weight here is A_i transposed.)
+ *  - bf16 tensors hold bfloat16 values; arithmetic accumulates in float32.
+ *    Every float32 -> bf16 conversion rounds to nearest-even.
+ *  - Reduction and feature dimensions (k, n, h, f_shard) must be multiples of
+ *    8; m (tokens) may be any value >= 0 (m == 0 enqueues nothing).
+ *  - Errors are returned before anything is enqueued, never replaced by a
+ *    fallback: TP_ERR_INVALID_ARG (null/misaligned pointer, unknown enum),
+ *    TP_ERR_SHAPE (a size or divisibility rule), TP_ERR_WORKSPACE (too small),
+ *    TP_ERR_UNSUPPORTED (dtype/option not built, or the device is not gfx950),
+ *    TP_ERR_HIP (a HIP launch error).  tp_last_error() gives a message for the
+ *    calling thread's last failure.
+ *  - Results are deterministic: no atomics, fixed summation order.
+ */
+#ifndef TPSHARD_H
+#define TPSHARD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum tp_status {
+  TP_OK = 0,
+  TP_ERR_INVALID_ARG = 1,
+  TP_ERR_SHAPE = 2,
+  TP_ERR_WORKSPACE = 3,
+  TP_ERR_UNSUPPORTED = 4,
+  TP_ERR_HIP = 5
+} tp_status;
+
+typedef enum tp_dtype { TP_F32 = 0, TP_BF16 = 1 } tp_dtype;
+
+/* Nonlinearity applied by the column-parallel GEMM, per rank ("MLP" section). */
+typedef enum tp_act {
+  TP_ACT_NONE = 0,   /* plain colwise projection, Y_i = X A_i                    */
+  TP_ACT_GELU = 1,   /* Y_i = GeLU(X A_i), exact erf form x/2 (1 + erf(x/sqrt2))  */
+  TP_ACT_SWIGLU = 2  /* Y_i = SiLU(X W1_i) * (X W3_i), SiLU(x) = x / (1 + e^-x)  */
+} tp_act;
+
+/* Maximum number of partials one tp_shard_sum call adds. */
+#define TP_MAX_SHARDS 16
+
+/* --------------------------------------------------------------------------
+ * Column-parallel linear with a fused nonlinearity ("Matmul split", "MLP").
+ *
+ *   x  [m, k]      the replicated input (dt)
+ *   w  [n, k]      rank i's weight A_i^T                     (act NONE, GELU)
+ *      [2n, k]     [W1_i^T ; W3_i^T]: the rank's gate rows then its up rows,
+ *                  each block sliced from its own tensor   (act SWIGLU)
+ *   y  [m, n]      rank i's output slice Y_i (dt)
+ *
+ * dt is TP_BF16 (bf16 in and out, float32 accumulate) or TP_F32 (float32 in,
+ * out and arithmetic; meant for small checks).
+ * ------------------------------------------------------------------------ */
+tp_status tp_colwise(tp_act act, tp_dtype dt, int64_t m, int64_t k, int64_t n,
+                     const void* x, const void* w, void* y, void* stream);
+
+/* --------------------------------------------------------------------------
+ * Row-parallel linear to a float32 partial sum ("Matmul split").
+ *
+ *   y        [m, k]  the rank's column slice of the activations (dt)
+ *   w        [n, k]  the rank's weight rows B_i, transposed
+ *   partial  [m, n]  float32, overwritten with Y_i B_i (the rank's share of
+ *                    the sum; no reduction across ranks here)
+ * ------------------------------------------------------------------------ */
+tp_status tp_rowwise(tp_dtype dt, int64_t m, int64_t k, int64_t n,
+                     const void* y, const void* w, float* partial, void* stream);
+
+/* --------------------------------------------------------------------------
+ * One rank's MLP: tp_colwise(act) then tp_rowwise ("MLP" section).
+ *
+ *   x        [m, h]                      replicated input
+ *   w_in     [f_shard, h] or [2 f_shard, h]   as tp_colwise's w
+ *   w_out    [h, f_shard]                B_i^T (or W2_i^T)
+ *   act_ws   [m, f_shard]  dt            workspace receiving Y_i
+ *   partial  [m, h]  float32             overwritten with the rank's partial
+ * act must be GELU or SWIGLU.
+ * ------------------------------------------------------------------------ */
+tp_status tp_shard_mlp(tp_act act, tp_dtype dt, int64_t m, int64_t h, int64_t f_shard,
+                       const void* x, const void* w_in, const void* w_out,
+                       void* act_ws, float* partial, void* stream);
+
+/* --------------------------------------------------------------------------
+ * Column-parallel Q/K/V projection of one rank with rotary embedding
+ * ("Self-attention" section), bf16 only.
+ *
+ *   x      [batch*seq, h]   replicated input; token row r is position r % seq
+ *                           of sequence r / seq
+ *   w_qkv  [(hq + 2 hkv) * d, h]  the rank's rows: its hq query heads, then
+ *                           its hkv key heads, then its hkv value heads, each
+ *                           head d consecutive rows
+ *   q      [batch*seq, hq*d]    RoPE(x Wq_i), head j in columns [j d, (j+1) d)
+ *   k      [batch*seq, hkv*d]   RoPE(x Wk_i)
+ *   vt     [batch, hkv, d, seq_pad]  (x Wv_i) transposed per sequence and
+ *                           head, seq_pad = seq rounded up to 64; columns
+ *                           >= seq are written as zero
+ * RoPE rotates the pair (c, c + d/2) of every head by the angle
+ * pos * rope_base^(-2c/d) (rotate-half form).  d must be 128.
+ * ------------------------------------------------------------------------ */
+tp_status tp_qkv_rope(int64_t batch, int64_t seq, int64_t h, int32_t hq, int32_t hkv,
+                      int32_t head_dim, float rope_base, const void* x, const void* w_qkv,
+                      void* q, void* k, void* vt, void* stream);
+
+/* --------------------------------------------------------------------------
+ * Attention of one rank's heads ("Self-attention" section), bf16 only.
+ *
+ *   q, k, vt  as written by tp_qkv_rope
+ *   o         [batch*seq, hq*d]  softmax(q k^T / sqrt(d)) v per query head,
+ *             query head j of the rank reading KV head j / (hq / hkv);
+ *             causal != 0 lets position p see positions <= p of its own
+ *             sequence, causal == 0 all positions of its sequence.
+ * hq must be a multiple of hkv; d must be 128.
+ * ------------------------------------------------------------------------ */
+tp_status tp_flash_attn(int64_t batch, int64_t seq, int32_t hq, int32_t hkv, int32_t head_dim,
+                        int32_t causal, const void* q, const void* k, const void* vt, void* o,
+                        void* stream);
+
+/* Bytes of workspace tp_shard_attn needs (q, k, vt and o, each 256-byte aligned). */
+size_t tp_shard_attn_workspace_bytes(int64_t batch, int64_t seq, int32_t hq, int32_t hkv,
+                                     int32_t head_dim);
+
+/* --------------------------------------------------------------------------
+ * One rank's attention sublayer: tp_qkv_rope, tp_flash_attn, then the
+ * row-parallel o_proj to a float32 partial ("Self-attention" section).
+ *
+ *   w_o      [h, hq*d]   rows of Wo for this rank's heads, transposed
+ *   ws       workspace of at least tp_shard_attn_workspace_bytes(...) bytes
+ *   partial  [batch*seq, h] float32, overwritten
+ * ------------------------------------------------------------------------ */
+tp_status tp_shard_attn(int64_t batch, int64_t seq, int64_t h, int32_t hq, int32_t hkv,
+                        int32_t head_dim, float rope_base, int32_t causal, const void* x,
+                        const void* w_qkv, const void* w_o, void* ws, size_t ws_bytes,
+                        float* partial, void* stream);
+
+/* --------------------------------------------------------------------------
+ * Sum of the ranks' partials -- the forward all-reduce ("f and g" section),
+ * computed inside one device:
+ *
+ *   out[e] = (((partials[0][e] + partials[1][e]) + ...) + partials[t-1][e])
+ *            + residual[e]
+ *
+ * in float32, ascending rank order, residual (optional, NULL for none) added
+ * last.  partials is a HOST array of t device pointers (1 <= t <= 16), each
+ * [n] float32; residual is [n] of residual_dt; out [n] float32 may alias
+ * residual when residual_dt is TP_F32, but no partial.
+ * ------------------------------------------------------------------------ */
+tp_status tp_shard_sum(int32_t t, int64_t n, const float* const* partials, const void* residual,
+                       tp_dtype residual_dt, float* out, void* stream);
+
+/* --------------------------------------------------------------------------
+ * Replicated RMSNorm ("f and g" section: norms run on every rank):
+ *   y[r, c] = bf16( x[r, c] / sqrt(mean_c x[r, c]^2 + eps) * gain[c] )
+ *   x [m, h] of in_dt, gain [h] float32 or NULL (all ones), y [m, h] bf16.
+ * ------------------------------------------------------------------------ */
+tp_status tp_rmsnorm(tp_dtype in_dt, int64_t m, int64_t h, const void* x, const float* gain,
+                     float eps, void* y, void* stream);
+
+/* Message for the calling thread's last error ("" if none). */
+const char* tp_last_error(void);
+
+/* TP_OK if the current HIP device is gfx950, else TP_ERR_UNSUPPORTED. */
+tp_status tp_device_check(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TPSHARD_H */

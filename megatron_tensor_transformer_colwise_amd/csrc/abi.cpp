@@ -1,0 +1,301 @@
+// C ABI of libtpshard: argument validation, then kernel launches on the
+// caller's stream.  Every check runs on the host before anything is enqueued;
+// failures return a status and leave a message for tp_last_error().
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+
+#include "kernels.h"
+#include "tpshard.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+tp_status fail(tp_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+tp_status ok() {
+  g_err[0] = '\0';
+  return TP_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+const int64_t kMaxOffset = (int64_t)1 << 31;  // buffer offsets are 32-bit, signed headroom
+
+tp_status check_ptr(const void* p, const char* name) {
+  if (!p) return fail(TP_ERR_INVALID_ARG, "%s is NULL", name);
+  if (!aligned16(p)) return fail(TP_ERR_INVALID_ARG, "%s is not 16-byte aligned", name);
+  return TP_OK;
+}
+
+#define TRY(expr)                      \
+  do {                                 \
+    tp_status _s = (expr);             \
+    if (_s != TP_OK) return _s;        \
+  } while (0)
+
+tp_status check_dim8(int64_t v, const char* name) {
+  if (v <= 0 || (v & 7)) return fail(TP_ERR_SHAPE, "%s = %lld must be a positive multiple of 8", name, (long long)v);
+  return TP_OK;
+}
+
+// Device check, cached per device id.
+std::mutex g_dev_mu;
+int g_dev_ok[64];  // 0 unknown, 1 gfx950, 2 other
+
+tp_status device_check() {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(TP_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= 64) return fail(TP_ERR_UNSUPPORTED, "device id %d out of range", dev);
+  std::lock_guard<std::mutex> lk(g_dev_mu);
+  if (g_dev_ok[dev] == 0) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) return fail(TP_ERR_HIP, "hipGetDeviceProperties: %s", hipGetErrorString(e));
+    g_dev_ok[dev] = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+    if (g_dev_ok[dev] == 2)
+      return fail(TP_ERR_UNSUPPORTED, "device %d is %s; this library is built for gfx950", dev, prop.gcnArchName);
+  }
+  if (g_dev_ok[dev] != 1) return fail(TP_ERR_UNSUPPORTED, "device %d is not gfx950", dev);
+  return TP_OK;
+}
+
+tp_status launched(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(TP_ERR_HIP, "%s launch failed: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+int64_t seq_pad_of(int64_t seq) { return (seq + 63) / 64 * 64; }
+
+size_t align256(size_t v) { return (v + 255) / 256 * 256; }
+
+struct AttnLayout {
+  size_t q, k, vt, o, total;
+};
+
+AttnLayout attn_layout(int64_t batch, int64_t seq, int32_t hq, int32_t hkv, int32_t d) {
+  const size_t m = (size_t)batch * (size_t)seq;
+  AttnLayout L;
+  L.q = 0;
+  L.k = L.q + align256(m * hq * d * 2);
+  L.vt = L.k + align256(m * hkv * d * 2);
+  L.o = L.vt + align256((size_t)batch * hkv * d * (size_t)seq_pad_of(seq) * 2);
+  L.total = L.o + align256(m * hq * d * 2);
+  return L;
+}
+
+// Shared checks of one GEMM call: sizes, pointers, 32-bit offset ranges.
+tp_status check_gemm(tp_act act, tp_dtype dt, int64_t m, int64_t k, int64_t n, const void* x,
+                     const void* w, const void* out, const char* xn, const char* wn, const char* on) {
+  if (dt != TP_F32 && dt != TP_BF16) return fail(TP_ERR_INVALID_ARG, "unknown dtype %d", (int)dt);
+  if (act != TP_ACT_NONE && act != TP_ACT_GELU && act != TP_ACT_SWIGLU)
+    return fail(TP_ERR_INVALID_ARG, "unknown activation %d", (int)act);
+  if (m < 0) return fail(TP_ERR_SHAPE, "m = %lld is negative", (long long)m);
+  TRY(check_dim8(k, "k"));
+  TRY(check_dim8(n, "n"));
+  const int64_t esz = dt == TP_BF16 ? 2 : 4;
+  const int64_t wrows = act == TP_ACT_SWIGLU ? 2 * n : n;
+  if (dt == TP_BF16 && (wrows + 256) * k * esz >= kMaxOffset)
+    return fail(TP_ERR_SHAPE, "weight of %lld x %lld exceeds the 2 GiB per-operand limit",
+                (long long)wrows, (long long)k);
+  if (dt == TP_BF16 && 256 * k * esz >= kMaxOffset) return fail(TP_ERR_SHAPE, "k = %lld too large", (long long)k);
+  if (m == 0) return TP_OK;
+  TRY(check_ptr(x, xn));
+  TRY(check_ptr(w, wn));
+  TRY(check_ptr(out, on));
+  return TP_OK;
+}
+
+int epi_of(tp_act act) {
+  switch (act) {
+    case TP_ACT_GELU: return tpk::EPI_GELU;
+    case TP_ACT_SWIGLU: return tpk::EPI_SWIGLU;
+    default: return tpk::EPI_BF16;
+  }
+}
+
+tp_status check_attn_shape(int64_t batch, int64_t seq, int32_t hq, int32_t hkv, int32_t d) {
+  if (batch < 0 || seq < 0) return fail(TP_ERR_SHAPE, "batch and seq must be >= 0");
+  if (d != 128) return fail(TP_ERR_UNSUPPORTED, "head_dim = %d; only 128 is built", d);
+  if (hq <= 0 || hkv <= 0) return fail(TP_ERR_SHAPE, "hq = %d and hkv = %d must be positive", hq, hkv);
+  if (hq % hkv) return fail(TP_ERR_SHAPE, "hq = %d is not a multiple of hkv = %d", hq, hkv);
+  if (seq * (int64_t)hq * d * 2 >= kMaxOffset || seq * (int64_t)hkv * d * 2 >= kMaxOffset)
+    return fail(TP_ERR_SHAPE, "one sequence of q or k exceeds 2 GiB");
+  if ((int64_t)d * seq_pad_of(seq) * 2 >= kMaxOffset) return fail(TP_ERR_SHAPE, "seq too long");
+  if (batch * seq * (int64_t)hq > ((int64_t)1 << 31)) return fail(TP_ERR_SHAPE, "too many query rows");
+  return TP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* tp_last_error(void) { return g_err; }
+
+tp_status tp_device_check(void) {
+  TRY(device_check());
+  return ok();
+}
+
+tp_status tp_colwise(tp_act act, tp_dtype dt, int64_t m, int64_t k, int64_t n, const void* x,
+                     const void* w, void* y, void* stream) {
+  TRY(check_gemm(act, dt, m, k, n, x, w, y, "x", "w", "y"));
+  if (m == 0) return ok();
+  TRY(device_check());
+  hipError_t e;
+  if (dt == TP_BF16)
+    e = tpk::launch_gemm_bf16(epi_of(act), m, n, k, x, w, y, nullptr, as_stream(stream));
+  else
+    e = tpk::launch_gemm_f32(epi_of(act), m, n, k, static_cast<const float*>(x),
+                             static_cast<const float*>(w), static_cast<float*>(y), as_stream(stream));
+  return launched(e, "tp_colwise");
+}
+
+tp_status tp_rowwise(tp_dtype dt, int64_t m, int64_t k, int64_t n, const void* y, const void* w,
+                     float* partial, void* stream) {
+  TRY(check_gemm(TP_ACT_NONE, dt, m, k, n, y, w, partial, "y", "w", "partial"));
+  if (m == 0) return ok();
+  TRY(device_check());
+  hipError_t e;
+  if (dt == TP_BF16)
+    e = tpk::launch_gemm_bf16(tpk::EPI_F32, m, n, k, y, w, partial, nullptr, as_stream(stream));
+  else
+    e = tpk::launch_gemm_f32(tpk::EPI_F32, m, n, k, static_cast<const float*>(y),
+                             static_cast<const float*>(w), partial, as_stream(stream));
+  return launched(e, "tp_rowwise");
+}
+
+tp_status tp_shard_mlp(tp_act act, tp_dtype dt, int64_t m, int64_t h, int64_t f_shard,
+                       const void* x, const void* w_in, const void* w_out, void* act_ws,
+                       float* partial, void* stream) {
+  if (act != TP_ACT_GELU && act != TP_ACT_SWIGLU)
+    return fail(TP_ERR_INVALID_ARG, "tp_shard_mlp needs GELU or SWIGLU, got %d", (int)act);
+  TRY(check_gemm(act, dt, m, h, f_shard, x, w_in, act_ws, "x", "w_in", "act_ws"));
+  TRY(check_gemm(TP_ACT_NONE, dt, m, f_shard, h, act_ws, w_out, partial, "act_ws", "w_out", "partial"));
+  TRY(tp_colwise(act, dt, m, h, f_shard, x, w_in, act_ws, stream));
+  return tp_rowwise(dt, m, f_shard, h, act_ws, w_out, partial, stream);
+}
+
+tp_status tp_qkv_rope(int64_t batch, int64_t seq, int64_t h, int32_t hq, int32_t hkv,
+                      int32_t head_dim, float rope_base, const void* x, const void* w_qkv, void* q,
+                      void* k, void* vt, void* stream) {
+  TRY(check_attn_shape(batch, seq, hq, hkv, head_dim));
+  if (!(rope_base > 1.0f)) return fail(TP_ERR_INVALID_ARG, "rope_base must be > 1");
+  const int64_t n = (int64_t)(hq + 2 * hkv) * head_dim;
+  TRY(check_gemm(TP_ACT_NONE, TP_BF16, batch * seq, h, n, x, w_qkv, q, "x", "w_qkv", "q"));
+  const int64_t m = batch * seq;
+  if (m == 0) return ok();
+  TRY(check_ptr(k, "k"));
+  TRY(check_ptr(vt, "vt"));
+  TRY(device_check());
+  tpk::QkvOut o;
+  o.q = q;
+  o.k = k;
+  o.vt = vt;
+  o.seq = seq;
+  o.seq_pad = seq_pad_of(seq);
+  o.hq = hq;
+  o.hkv = hkv;
+  o.log2_base = log2f(rope_base);
+  return launched(tpk::launch_gemm_bf16(tpk::EPI_QKV, m, n, h, x, w_qkv, nullptr, &o, as_stream(stream)),
+                  "tp_qkv_rope");
+}
+
+tp_status tp_flash_attn(int64_t batch, int64_t seq, int32_t hq, int32_t hkv, int32_t head_dim,
+                        int32_t causal, const void* q, const void* k, const void* vt, void* o,
+                        void* stream) {
+  TRY(check_attn_shape(batch, seq, hq, hkv, head_dim));
+  if (batch * seq == 0) return ok();
+  TRY(check_ptr(q, "q"));
+  TRY(check_ptr(k, "k"));
+  TRY(check_ptr(vt, "vt"));
+  TRY(check_ptr(o, "o"));
+  TRY(device_check());
+  return launched(tpk::launch_flash_attn(batch, seq, seq_pad_of(seq), hq, hkv, causal, q, k, vt, o,
+                                         as_stream(stream)),
+                  "tp_flash_attn");
+}
+
+size_t tp_shard_attn_workspace_bytes(int64_t batch, int64_t seq, int32_t hq, int32_t hkv,
+                                     int32_t head_dim) {
+  if (batch < 0 || seq < 0 || hq <= 0 || hkv <= 0 || head_dim <= 0) return 0;
+  return attn_layout(batch, seq, hq, hkv, head_dim).total;
+}
+
+tp_status tp_shard_attn(int64_t batch, int64_t seq, int64_t h, int32_t hq, int32_t hkv,
+                        int32_t head_dim, float rope_base, int32_t causal, const void* x,
+                        const void* w_qkv, const void* w_o, void* ws, size_t ws_bytes,
+                        float* partial, void* stream) {
+  TRY(check_attn_shape(batch, seq, hq, hkv, head_dim));
+  const int64_t m = batch * seq;
+  const int64_t qd = (int64_t)hq * head_dim;
+  TRY(check_gemm(TP_ACT_NONE, TP_BF16, m, qd, h, x, w_o, partial, "x", "w_o", "partial"));
+  const AttnLayout L = attn_layout(batch, seq, hq, hkv, head_dim);
+  if (m == 0) return ok();
+  TRY(check_ptr(ws, "ws"));
+  if (ws_bytes < L.total)
+    return fail(TP_ERR_WORKSPACE, "workspace of %zu bytes < %zu needed", ws_bytes, L.total);
+  char* base = static_cast<char*>(ws);
+  TRY(tp_qkv_rope(batch, seq, h, hq, hkv, head_dim, rope_base, x, w_qkv, base + L.q, base + L.k,
+                  base + L.vt, stream));
+  TRY(tp_flash_attn(batch, seq, hq, hkv, head_dim, causal, base + L.q, base + L.k, base + L.vt,
+                    base + L.o, stream));
+  return tp_rowwise(TP_BF16, m, qd, h, base + L.o, w_o, partial, stream);
+}
+
+tp_status tp_shard_sum(int32_t t, int64_t n, const float* const* partials, const void* residual,
+                       tp_dtype residual_dt, float* out, void* stream) {
+  if (t < 1 || t > TP_MAX_SHARDS) return fail(TP_ERR_SHAPE, "t = %d outside 1..%d", t, TP_MAX_SHARDS);
+  if (n < 0) return fail(TP_ERR_SHAPE, "n = %lld is negative", (long long)n);
+  if (residual && residual_dt != TP_F32 && residual_dt != TP_BF16)
+    return fail(TP_ERR_INVALID_ARG, "unknown residual dtype %d", (int)residual_dt);
+  if (n == 0) return ok();
+  if (!partials) return fail(TP_ERR_INVALID_ARG, "partials is NULL");
+  for (int i = 0; i < t; ++i) {
+    char name[32];
+    snprintf(name, sizeof(name), "partials[%d]", i);
+    TRY(check_ptr(partials[i], name));
+    if (partials[i] == out) return fail(TP_ERR_INVALID_ARG, "out aliases partials[%d]", i);
+  }
+  if (residual) {
+    TRY(check_ptr(residual, "residual"));
+    if (residual == out && residual_dt != TP_F32)
+      return fail(TP_ERR_INVALID_ARG, "out may alias residual only for a float32 residual");
+  }
+  TRY(check_ptr(out, "out"));
+  TRY(device_check());
+  return launched(tpk::launch_shard_sum(t, n, partials, residual, residual_dt == TP_BF16, out,
+                                        as_stream(stream)),
+                  "tp_shard_sum");
+}
+
+tp_status tp_rmsnorm(tp_dtype in_dt, int64_t m, int64_t h, const void* x, const float* gain,
+                     float eps, void* y, void* stream) {
+  if (in_dt != TP_F32 && in_dt != TP_BF16) return fail(TP_ERR_INVALID_ARG, "unknown dtype %d", (int)in_dt);
+  if (m < 0) return fail(TP_ERR_SHAPE, "m = %lld is negative", (long long)m);
+  TRY(check_dim8(h, "h"));
+  if (!(eps >= 0.0f)) return fail(TP_ERR_INVALID_ARG, "eps must be >= 0");
+  if (m == 0) return ok();
+  if (m > 0x7FFFFFFF) return fail(TP_ERR_SHAPE, "m too large");
+  TRY(check_ptr(x, "x"));
+  if (gain) TRY(check_ptr(gain, "gain"));
+  TRY(check_ptr(y, "y"));
+  TRY(device_check());
+  return launched(tpk::launch_rmsnorm(in_dt == TP_BF16, m, h, x, gain, eps, y, as_stream(stream)),
+                  "tp_rmsnorm");
+}
+
+}  // extern "C"

@@ -1,0 +1,351 @@
+// bf16 MFMA GEMM for gfx950:  out[m, n] = epi( sum_k X[m, k] * W[row(n), k] ).
+//
+// This is the contraction of both tensor-parallel linears of the "Tensor
+// parallelism" page ("Matmul split"): the column-parallel one, whose output
+// slice goes straight through the per-rank nonlinearity ("MLP": GeLU, or
+// SwiGLU) or through RoPE ("Self-attention": the Q/K/V projection), and the
+// row-parallel one, whose output is the rank's float32 partial sum.
+//
+// Both operands are contiguous along k (X row-major, W in nn.Linear layout), so
+// every MFMA operand of a lane is 16 contiguous bytes of one row.
+//
+// Tiling: 256 x 256 output tile per workgroup of 4 waves, each wave a
+// 128 x 128 sub-tile of 4 x 4 v_mfma_f32_32x32x16_bf16 blocks (256 float32
+// accumulators per lane).  k advances 64 at a time through a two-stage LDS
+// ring (2 x 64 KiB); tiles are fetched with 16-byte buffer loads that write
+// LDS directly (no register staging).  Out-of-range rows and the k tail are
+// fetched as zeros by the buffer's range check.  Each LDS row is 128 bytes;
+// its eight 16-byte chunks are XOR-permuted by swz(row) so the 32 rows one
+// fragment read touches spread over all banks.
+#include "common.h"
+#include "kernels.h"
+
+namespace tpk {
+namespace {
+
+constexpr int BM = 256;
+constexpr int BN = 256;
+constexpr int BK = 64;
+constexpr int NT = 256;
+constexpr int TILE_BYTES = 256 * BK * 2;       // one operand, one stage
+constexpr int STAGE_BYTES = 2 * TILE_BYTES;    // A then B
+constexpr int SMEM_BYTES = 2 * STAGE_BYTES;    // two stages
+
+struct Args {
+  const bf16_t* x;
+  const bf16_t* w;
+  void* out;
+  int64_t M, N, K;
+  int num_bm, num_bn;
+  QkvOut qkv;
+};
+
+__device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
+
+// Launch index -> output tile.  Workgroups are dealt to the 8 XCDs round-robin;
+// first undo that so each XCD owns a contiguous range of logical tiles, then
+// walk tiles in groups of 8 tile-rows so a range is a compact patch whose X
+// rows and W rows stay in that XCD's L2.
+__device__ __forceinline__ void tile_coords(int id, int nb, int num_bm, int num_bn, int& bm,
+                                            int& bn) {
+  const int xcd = id & 7, local = id >> 3;
+  const int per = nb >> 3, rem = nb & 7;
+  const int L = (xcd < rem) ? xcd * (per + 1) + local
+                            : rem * (per + 1) + (xcd - rem) * per + local;
+  constexpr int G = 8;
+  const int span = G * num_bn;
+  const int g = L / span;
+  const int first = g * G;
+  const int gs = min(num_bm - first, G);
+  const int inner = L - g * span;
+  bm = first + inner % gs;
+  bn = inner / gs;
+}
+
+template <int EPI>
+__global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(Args args) {
+  __shared__ __attribute__((aligned(1024))) char smem[SMEM_BYTES];
+
+  const int lane = lane_id();
+  const int wave = wave_id();
+  int bm, bn;
+  tile_coords(blockIdx.x, gridDim.x, args.num_bm, args.num_bn, bm, bn);
+
+  const int64_t M = args.M, N = args.N, K = args.K;
+  const int64_t m0 = (int64_t)bm * BM;
+  const uint32_t row_bytes = (uint32_t)(K * 2);
+
+  // ---- global -> LDS addressing -------------------------------------------
+  // Slot s = (j * 4 + wave) * 64 + lane of a stage holds tile row s / 8,
+  // physical chunk s % 8, i.e. logical chunk (s % 8) ^ swz(row).
+  const int m_rows = (int)min<int64_t>(BM, M - m0);
+  __amdgpu_buffer_rsrc_t rsrc_a =
+      make_rsrc(args.x + m0 * K, (uint32_t)m_rows * row_bytes);
+
+  __amdgpu_buffer_rsrc_t rsrc_b;
+  int n_valid;  // valid weight rows (plain) or valid output columns (SwiGLU)
+  if (EPI == EPI_SWIGLU) {
+    const int64_t o0 = (int64_t)bn * (BN / 2);
+    n_valid = (int)min<int64_t>(BN / 2, N - o0);
+    rsrc_b = make_rsrc(args.w + o0 * K, (uint32_t)((N + n_valid) * K * 2));
+  } else {
+    const int64_t n0 = (int64_t)bn * BN;
+    n_valid = (int)min<int64_t>(BN, N - n0);
+    rsrc_b = make_rsrc(args.w + n0 * K, (uint32_t)n_valid * row_bytes);
+  }
+
+  uint32_t a_off[8], b_off[8];
+  int a_k[8], b_k[8];  // element offset of the chunk within the k-block
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int r = (j * 4 + wave) * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ swz(r);
+    a_k[j] = c * 8;
+    a_off[j] = (uint32_t)r * row_bytes + (uint32_t)c * 16;
+    b_k[j] = c * 8;
+    if (EPI == EPI_SWIGLU) {
+      const int wn = r >> 7, qq = r & 127;
+      const int o_rel = wn * 64 + (qq & 63);
+      const int64_t rel_row = (qq < 64) ? o_rel : N + o_rel;
+      b_off[j] = (o_rel < n_valid) ? (uint32_t)(rel_row * K * 2) + (uint32_t)c * 16 : TP_OOB_OFFSET;
+    } else {
+      b_off[j] = (uint32_t)r * row_bytes + (uint32_t)c * 16;
+    }
+  }
+
+  auto load_stage = [&](int stage, int64_t k0) {
+    char* sa = smem + stage * STAGE_BYTES;
+    char* sb = sa + TILE_BYTES;
+    const uint32_t kb = (uint32_t)(k0 * 2);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const bool ka = (k0 + a_k[j]) < K;
+      buffer_load_lds16(rsrc_a, sa + (j * 4 + wave) * 1024, ka ? a_off[j] + kb : TP_OOB_OFFSET);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const bool kbv = (k0 + b_k[j]) < K && b_off[j] != TP_OOB_OFFSET;
+      buffer_load_lds16(rsrc_b, sb + (j * 4 + wave) * 1024, kbv ? b_off[j] + kb : TP_OOB_OFFSET);
+    }
+  };
+
+  // ---- LDS -> registers addressing ----------------------------------------
+  const int wm = wave >> 1, wn = wave & 1;
+  const int l31 = lane & 31, hk = lane >> 5;
+  uint32_t ra[4][4], rb[4][4];  // [i or j][s] byte offsets within a tile
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r_a = wm * 128 + i * 32 + l31;
+    const int r_b = wn * 128 + i * 32 + l31;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int c = 2 * s + hk;
+      ra[i][s] = (uint32_t)(r_a * 128 + ((c ^ swz(r_a)) << 4));
+      rb[i][s] = (uint32_t)(r_b * 128 + ((c ^ swz(r_b)) << 4));
+    }
+  }
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+
+  const int nk = (int)((K + BK - 1) / BK);
+  load_stage(0, 0);
+  for (int kt = 0; kt < nk; ++kt) {
+    wait_vmcnt0();
+    __syncthreads();
+    if (kt + 1 < nk) load_stage((kt + 1) & 1, (int64_t)(kt + 1) * BK);
+    const char* sa = smem + (kt & 1) * STAGE_BYTES;
+    const char* sb = sa + TILE_BYTES;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      u32x4 a[4], b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = lds_read16(sa + ra[i][s]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) b[j] = lds_read16(sb + rb[j][s]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = mfma32x32x16(a[i], b[j], acc[i][j]);
+    }
+  }
+
+  // ---- epilogue -----------------------------------------------------------
+  // Accumulator element r of block (i, j) in lane L is output row
+  // 32 i + 8 (r / 4) + 4 (L / 32) + r % 4 and column 32 j + L % 32 of the
+  // wave's 128 x 128 sub-tile.
+  const int64_t row_base = m0 + wm * 128 + 4 * hk;
+  if (EPI == EPI_F32 || EPI == EPI_BF16 || EPI == EPI_GELU) {
+    const int64_t col_base = (int64_t)bn * BN + wn * 128 + l31;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int64_t col = col_base + j * 32;
+        if (col >= N) continue;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int64_t row = row_base + i * 32 + 8 * (r >> 2) + (r & 3);
+          if (row >= M) continue;
+          float v = acc[i][j][r];
+          if (EPI == EPI_F32) {
+            reinterpret_cast<float*>(args.out)[row * N + col] = v;
+          } else {
+            if (EPI == EPI_GELU) v = gelu_erf(v);
+            reinterpret_cast<bf16_t*>(args.out)[row * N + col] = f32_to_bf16(v);
+          }
+        }
+      }
+  } else if (EPI == EPI_SWIGLU) {
+    const int64_t col_base = (int64_t)bn * (BN / 2) + wn * 64 + l31;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int64_t col = col_base + j * 32;
+        if (col >= N) continue;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int64_t row = row_base + i * 32 + 8 * (r >> 2) + (r & 3);
+          if (row >= M) continue;
+          const float g = acc[i][j][r], u = acc[i][j + 2][r];
+          reinterpret_cast<bf16_t*>(args.out)[row * N + col] = f32_to_bf16(silu(g) * u);
+        }
+      }
+  } else {  // EPI_QKV: this wave's 128 columns are exactly one head
+    const QkvOut& o = args.qkv;
+    const int hd = bn * 2 + wn;
+    const int nheads = o.hq + 2 * o.hkv;
+    if (hd >= nheads) return;
+    const uint32_t seq = (uint32_t)o.seq;
+    // Rows 8 g4 + e, e = 0..3, of block i are 4 consecutive tokens; one
+    // division per group gives (sequence, position) of its first token.
+    if (hd < o.hq + o.hkv) {
+      const bool is_q = hd < o.hq;
+      bf16_t* dst = reinterpret_cast<bf16_t*>(is_q ? o.q : o.k);
+      const int64_t ld = (int64_t)(is_q ? o.hq : o.hkv) * 128;
+      dst += (int64_t)(is_q ? hd : hd - o.hq) * 128;
+      // angle = pos * base^(-2 c1 / 128) radians for the pair (c1, c1 + 64),
+      // taken in turns (1 turn = 2 pi) in float64 so only the fraction of a
+      // turn is rounded to float32; v_sin/v_cos take their argument in turns.
+      double tpp[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        tpp[j] = exp2(-(double)(2 * (j * 32 + l31)) * (1.0 / 128.0) * (double)o.log2_base) *
+                 0.15915494309189533577;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int64_t row0 = row_base + i * 32 + 8 * g4;
+          if (row0 >= M) continue;
+          const uint32_t p0 = (uint32_t)row0 % seq;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int64_t row = row0 + e;
+            if (row >= M) continue;
+            uint32_t pos = p0 + e;
+            if (pos >= seq) pos -= seq;
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+              const int c1 = j * 32 + l31;
+              const double turns = (double)pos * tpp[j];
+              const float frac = (float)(turns - floor(turns));
+              const float sn = __builtin_amdgcn_sinf(frac), cs = __builtin_amdgcn_cosf(frac);
+              const float x1 = acc[i][j][4 * g4 + e], x2 = acc[i][j + 2][4 * g4 + e];
+              dst[row * ld + c1] = f32_to_bf16(x1 * cs - x2 * sn);
+              dst[row * ld + c1 + 64] = f32_to_bf16(x2 * cs + x1 * sn);
+            }
+          }
+        }
+    } else {
+      const int g = hd - o.hq - o.hkv;
+      bf16_t* vt = reinterpret_cast<bf16_t*>(o.vt);
+      const bool vec = (seq & 3u) == 0;  // groups of 4 never straddle sequences
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int64_t row0 = row_base + i * 32 + 8 * g4;
+          if (row0 >= M) continue;
+          const uint32_t b0 = (uint32_t)row0 / seq, p0 = (uint32_t)row0 - b0 * seq;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int c = j * 32 + l31;
+            if (vec && row0 + 3 < M) {
+              bf16_t* line = vt + (((int64_t)b0 * o.hkv + g) * 128 + c) * o.seq_pad;
+              const u32x2 pr = {pack_bf16x2(acc[i][j][4 * g4 + 0], acc[i][j][4 * g4 + 1]),
+                                pack_bf16x2(acc[i][j][4 * g4 + 2], acc[i][j][4 * g4 + 3])};
+              *reinterpret_cast<u32x2*>(line + p0) = pr;
+            } else {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                if (row0 + e >= M) continue;
+                uint32_t b = b0, pos = p0 + e;
+                if (pos >= seq) {
+                  pos -= seq;
+                  ++b;
+                }
+                vt[(((int64_t)b * o.hkv + g) * 128 + c) * o.seq_pad + pos] =
+                    f32_to_bf16(acc[i][j][4 * g4 + e]);
+              }
+            }
+          }
+        }
+    }
+  }
+}
+
+// Zeroes the padding columns [seq, seq_pad) of every row of the transposed V,
+// so attention over a partial last key tile reads zeros there.
+__global__ void vt_pad_zero_kernel(bf16_t* vt, int64_t rows, int64_t seq, int64_t seq_pad) {
+  const int64_t w = seq_pad - seq;
+  const int64_t total = rows * w;
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total;
+       e += (int64_t)gridDim.x * blockDim.x)
+    vt[(e / w) * seq_pad + seq + e % w] = 0;
+}
+
+}  // namespace
+
+hipError_t launch_gemm_bf16(int epi, int64_t M, int64_t N, int64_t K, const void* x, const void* w,
+                            void* out, const QkvOut* qkv, hipStream_t s) {
+  Args a;
+  a.x = reinterpret_cast<const bf16_t*>(x);
+  a.w = reinterpret_cast<const bf16_t*>(w);
+  a.out = out;
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  const int64_t bn_cols = (epi == EPI_SWIGLU) ? BN / 2 : BN;
+  a.num_bm = (int)((M + BM - 1) / BM);
+  a.num_bn = (int)((N + bn_cols - 1) / bn_cols);
+  if (qkv) a.qkv = *qkv; else a.qkv = QkvOut{};
+  const int nb = a.num_bm * a.num_bn;
+  if (nb == 0) return hipSuccess;
+  dim3 grid(nb), block(NT);
+  switch (epi) {
+    case EPI_F32: hipLaunchKernelGGL(gemm_bf16_kernel<EPI_F32>, grid, block, 0, s, a); break;
+    case EPI_BF16: hipLaunchKernelGGL(gemm_bf16_kernel<EPI_BF16>, grid, block, 0, s, a); break;
+    case EPI_GELU: hipLaunchKernelGGL(gemm_bf16_kernel<EPI_GELU>, grid, block, 0, s, a); break;
+    case EPI_SWIGLU: hipLaunchKernelGGL(gemm_bf16_kernel<EPI_SWIGLU>, grid, block, 0, s, a); break;
+    case EPI_QKV: {
+      if (a.qkv.seq_pad > a.qkv.seq) {
+        const int64_t rows = (M / a.qkv.seq) * a.qkv.hkv * 128;
+        const int64_t total = rows * (a.qkv.seq_pad - a.qkv.seq);
+        const int64_t blocks = total < 256 * 1024 ? (total + 255) / 256 : 1024;
+        hipLaunchKernelGGL(vt_pad_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
+                           reinterpret_cast<bf16_t*>(a.qkv.vt), rows, a.qkv.seq, a.qkv.seq_pad);
+      }
+      hipLaunchKernelGGL(gemm_bf16_kernel<EPI_QKV>, grid, block, 0, s, a);
+      break;
+    }
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace tpk

@@ -1,0 +1,48 @@
+// Launch functions of the gfx950 kernels (host side).  Each returns the
+// hipError_t of its launch; argument checks happen in the C ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tpk {
+
+enum Epi : int {
+  EPI_F32 = 0,     // float32 output (row-parallel partial)
+  EPI_BF16 = 1,    // bf16 output, no nonlinearity
+  EPI_GELU = 2,    // bf16 GeLU(acc)
+  EPI_SWIGLU = 3,  // bf16 SiLU(gate) * up, weight rows [gate block ; up block]
+  EPI_QKV = 4      // Q/K with RoPE, V transposed per sequence
+};
+
+struct QkvOut {
+  void* q;
+  void* k;
+  void* vt;
+  int64_t seq;
+  int64_t seq_pad;
+  int hq;
+  int hkv;
+  float log2_base;
+};
+
+// out[m, n] = epi( sum_k x[m, k] * w[row(n), k] ), bf16 operands, float32 accumulate.
+hipError_t launch_gemm_bf16(int epi, int64_t M, int64_t N, int64_t K, const void* x, const void* w,
+                            void* out, const QkvOut* qkv, hipStream_t s);
+
+// Same contraction in float32 throughout (EPI_F32 / EPI_BF16 meaning "no
+// nonlinearity, float32 out", EPI_GELU, EPI_SWIGLU).
+hipError_t launch_gemm_f32(int epi, int64_t M, int64_t N, int64_t K, const float* x, const float* w,
+                           float* out, hipStream_t s);
+
+hipError_t launch_flash_attn(int64_t batch, int64_t seq, int64_t seq_pad, int hq, int hkv,
+                             int causal, const void* q, const void* k, const void* vt, void* o,
+                             hipStream_t s);
+
+hipError_t launch_shard_sum(int t, int64_t n, const float* const* partials, const void* residual,
+                            int residual_bf16, float* out, hipStream_t s);
+
+hipError_t launch_rmsnorm(int in_bf16, int64_t m, int64_t h, const void* x, const float* gain,
+                          float eps, void* y, hipStream_t s);
+
+}  // namespace tpk

@@ -80,7 +80,8 @@ class HostTensor:
         return bf16_bits_to_f32(self.data)
 
     def f64(self) -> np.ndarray:
-        return self.f32().astype(np.float64)
+        """Exact float64 copy (widened with torch's multithreaded conversion)."""
+        return self.torch().to(dtype=_torch().float64).numpy()
 
     def torch(self):
         import torch
@@ -88,6 +89,12 @@ class HostTensor:
         if self.dtype == "f32":
             return torch.from_numpy(np.ascontiguousarray(self.data))
         return torch.from_numpy(np.ascontiguousarray(self.data).view(np.int16)).view(torch.bfloat16)
+
+
+def _torch():
+    import torch
+
+    return torch
 
 
 def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:

@@ -1,0 +1,157 @@
+"""Python binding of ``libtpshard.so`` (declared in ``include/tpshard.h``).
+
+Argument marshalling only: every function here forwards to the C function of
+the same name.  Tensor arguments may be torch tensors (their ``data_ptr()`` is
+passed) or raw integer device addresses; ``stream`` defaults to torch's current
+stream.  A non-OK status raises :class:`TpError` with the library's message.
+There is no fallback: if the library is not built, loading it raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import re
+from pathlib import Path
+
+LIB_PATH = Path(__file__).resolve().parent / "libtpshard.so"
+HEADER = Path(__file__).resolve().parent.parent / "include" / "tpshard.h"
+
+TP_OK = 0
+TP_ERR_INVALID_ARG = 1
+TP_ERR_SHAPE = 2
+TP_ERR_WORKSPACE = 3
+TP_ERR_UNSUPPORTED = 4
+TP_ERR_HIP = 5
+STATUS_NAMES = {0: "TP_OK", 1: "TP_ERR_INVALID_ARG", 2: "TP_ERR_SHAPE", 3: "TP_ERR_WORKSPACE",
+                4: "TP_ERR_UNSUPPORTED", 5: "TP_ERR_HIP"}
+
+TP_F32, TP_BF16 = 0, 1
+TP_ACT_NONE, TP_ACT_GELU, TP_ACT_SWIGLU = 0, 1, 2
+DTYPES = {"f32": TP_F32, "bf16": TP_BF16}
+ACTS = {"none": TP_ACT_NONE, "gelu": TP_ACT_GELU, "swiglu": TP_ACT_SWIGLU}
+TP_MAX_SHARDS = 16
+
+
+class TpError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+        self.message = message
+
+
+_lib = None
+
+_i64, _i32, _f32, _vp = ctypes.c_int64, ctypes.c_int32, ctypes.c_float, ctypes.c_void_p
+_SIGS = {
+    "tp_colwise": [_i32, _i32, _i64, _i64, _i64, _vp, _vp, _vp, _vp],
+    "tp_rowwise": [_i32, _i64, _i64, _i64, _vp, _vp, _vp, _vp],
+    "tp_shard_mlp": [_i32, _i32, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp],
+    "tp_qkv_rope": [_i64, _i64, _i64, _i32, _i32, _i32, _f32, _vp, _vp, _vp, _vp, _vp, _vp],
+    "tp_flash_attn": [_i64, _i64, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp],
+    "tp_shard_attn_workspace_bytes": [_i64, _i64, _i32, _i32, _i32],
+    "tp_shard_attn": [_i64, _i64, _i64, _i32, _i32, _i32, _f32, _i32, _vp, _vp, _vp, _vp,
+                      ctypes.c_size_t, _vp, _vp],
+    "tp_shard_sum": [_i32, _i64, ctypes.POINTER(_vp), _vp, _i32, _vp, _vp],
+    "tp_rmsnorm": [_i32, _i64, _i64, _vp, _vp, _f32, _vp, _vp],
+    "tp_last_error": [],
+    "tp_device_check": [],
+}
+
+
+def lib() -> ctypes.CDLL:
+    """Loads ``libtpshard.so``; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not LIB_PATH.exists():
+            raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build() first")
+        L = ctypes.CDLL(str(LIB_PATH))
+        for name, args in _SIGS.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = ctypes.c_int
+        L.tp_last_error.restype = ctypes.c_char_p
+        L.tp_shard_attn_workspace_bytes.restype = ctypes.c_size_t
+        _lib = L
+    return _lib
+
+
+def header_exports() -> list[str]:
+    """Function names declared in include/tpshard.h."""
+    text = re.sub(r"/\*.*?\*/", "", HEADER.read_text(), flags=re.S)
+    return sorted(set(re.findall(r"\b(tp_[a-z_0-9]+)\s*\(", text)))
+
+
+def _p(x) -> int | None:
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _s(stream) -> int | None:
+    if stream is None:
+        import torch
+
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _e(v, table):
+    return table[v] if isinstance(v, str) else int(v)
+
+
+def _check(status: int) -> None:
+    if status != TP_OK:
+        raise TpError(status, lib().tp_last_error().decode())
+
+
+def tp_last_error() -> str:
+    return lib().tp_last_error().decode()
+
+
+def tp_device_check() -> None:
+    _check(lib().tp_device_check())
+
+
+def tp_colwise(act, dt, m, k, n, x, w, y, stream=None) -> None:
+    _check(lib().tp_colwise(_e(act, ACTS), _e(dt, DTYPES), m, k, n, _p(x), _p(w), _p(y), _s(stream)))
+
+
+def tp_rowwise(dt, m, k, n, y, w, partial, stream=None) -> None:
+    _check(lib().tp_rowwise(_e(dt, DTYPES), m, k, n, _p(y), _p(w), _p(partial), _s(stream)))
+
+
+def tp_shard_mlp(act, dt, m, h, f_shard, x, w_in, w_out, act_ws, partial, stream=None) -> None:
+    _check(lib().tp_shard_mlp(_e(act, ACTS), _e(dt, DTYPES), m, h, f_shard, _p(x), _p(w_in),
+                              _p(w_out), _p(act_ws), _p(partial), _s(stream)))
+
+
+def tp_qkv_rope(batch, seq, h, hq, hkv, head_dim, rope_base, x, w_qkv, q, k, vt, stream=None) -> None:
+    _check(lib().tp_qkv_rope(batch, seq, h, hq, hkv, head_dim, rope_base, _p(x), _p(w_qkv), _p(q),
+                             _p(k), _p(vt), _s(stream)))
+
+
+def tp_flash_attn(batch, seq, hq, hkv, head_dim, causal, q, k, vt, o, stream=None) -> None:
+    _check(lib().tp_flash_attn(batch, seq, hq, hkv, head_dim, int(causal), _p(q), _p(k), _p(vt),
+                               _p(o), _s(stream)))
+
+
+def tp_shard_attn_workspace_bytes(batch, seq, hq, hkv, head_dim) -> int:
+    return int(lib().tp_shard_attn_workspace_bytes(batch, seq, hq, hkv, head_dim))
+
+
+def tp_shard_attn(batch, seq, h, hq, hkv, head_dim, rope_base, causal, x, w_qkv, w_o, ws, ws_bytes,
+                  partial, stream=None) -> None:
+    _check(lib().tp_shard_attn(batch, seq, h, hq, hkv, head_dim, rope_base, int(causal), _p(x),
+                               _p(w_qkv), _p(w_o), _p(ws), ws_bytes, _p(partial), _s(stream)))
+
+
+def tp_shard_sum(t, n, partials, residual, residual_dt, out, stream=None) -> None:
+    arr = (_vp * max(len(partials), 1))(*[_p(p) for p in partials])
+    _check(lib().tp_shard_sum(t, n, arr, _p(residual), _e(residual_dt, DTYPES), _p(out), _s(stream)))
+
+
+def tp_rmsnorm(in_dt, m, h, x, gain, eps, y, stream=None) -> None:
+    _check(lib().tp_rmsnorm(_e(in_dt, DTYPES), m, h, _p(x), _p(gain), eps, _p(y), _s(stream)))

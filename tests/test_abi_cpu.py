@@ -1,0 +1,164 @@
+"""C-ABI contract checks that need no GPU.
+
+The library must load, export every function ``include/tpshard.h`` declares,
+and reject bad arguments with the documented status before touching a device
+(argument checks run on the host first, so these calls never reach HIP).
+"""
+import ctypes
+
+import pytest
+import torch
+
+from megatron_tensor_transformer_colwise_amd import shard, tpshard as tp
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not tp.LIB_PATH.exists():
+        import __graft_entry__
+
+        __graft_entry__.build()
+    return tp.lib()
+
+
+def test_exports_match_header(L):
+    names = tp.header_exports()
+    assert "tp_shard_mlp" in names and "tp_shard_attn" in names and "tp_shard_sum" in names
+    for n in names:
+        assert hasattr(L, n), f"{n} declared in the header but not exported"
+    assert set(names) == set(tp._SIGS)
+
+
+A16 = 1 << 20        # a fake, 16-byte aligned "device address" (never dereferenced)
+MIS = A16 + 4        # misaligned
+
+
+def status(fn, *args):
+    return getattr(tp.lib(), fn)(*args)
+
+
+def test_colwise_rowwise_validation(L):
+    # k not a multiple of 8
+    assert status("tp_colwise", 1, 1, 4, 12, 16, A16, A16, A16, None) == tp.TP_ERR_SHAPE
+    assert "k = 12" in tp.tp_last_error()
+    # n not positive
+    assert status("tp_colwise", 1, 1, 4, 16, 0, A16, A16, A16, None) == tp.TP_ERR_SHAPE
+    # negative m
+    assert status("tp_rowwise", 1, -1, 16, 16, A16, A16, A16, None) == tp.TP_ERR_SHAPE
+    # unknown dtype / activation
+    assert status("tp_colwise", 1, 7, 4, 16, 16, A16, A16, A16, None) == tp.TP_ERR_INVALID_ARG
+    assert status("tp_colwise", 9, 1, 4, 16, 16, A16, A16, A16, None) == tp.TP_ERR_INVALID_ARG
+    # null and misaligned pointers
+    assert status("tp_colwise", 1, 1, 4, 16, 16, None, A16, A16, None) == tp.TP_ERR_INVALID_ARG
+    assert "x is NULL" in tp.tp_last_error()
+    assert status("tp_rowwise", 1, 4, 16, 16, A16, MIS, A16, None) == tp.TP_ERR_INVALID_ARG
+    assert "w is not 16-byte aligned" in tp.tp_last_error()
+    # weight over the 2 GiB operand limit
+    assert status("tp_colwise", 2, 1, 4, 65536, 65536, A16, A16, A16, None) == tp.TP_ERR_SHAPE
+
+
+def test_m_zero_is_a_noop(L):
+    # nothing to do: OK without touching pointers or the device
+    assert status("tp_colwise", 1, 1, 0, 16, 16, None, None, None, None) == tp.TP_OK
+    assert status("tp_rowwise", 1, 0, 16, 16, None, None, None, None) == tp.TP_OK
+    assert status("tp_shard_mlp", 2, 1, 0, 16, 16, None, None, None, None, None, None) == tp.TP_OK
+    arr = (ctypes.c_void_p * 1)(None)
+    assert status("tp_shard_sum", 1, 0, arr, None, 0, None, None) == tp.TP_OK
+    assert status("tp_rmsnorm", 1, 0, 16, None, None, 1e-5, None, None) == tp.TP_OK
+
+
+def test_shard_mlp_needs_an_activation(L):
+    assert status("tp_shard_mlp", 0, 1, 4, 16, 16, A16, A16, A16, A16, A16, None) == tp.TP_ERR_INVALID_ARG
+
+
+def test_attention_validation(L):
+    args = dict(batch=2, seq=64, h=256, hq=4, hkv=2, d=128)
+
+    def attn(**kw):
+        a = {**args, **kw}
+        return status("tp_shard_attn", a["batch"], a["seq"], a["h"], a["hq"], a["hkv"], a["d"],
+                      500000.0, 1, A16, A16, A16, A16, 1 << 30, A16, None)
+
+    assert attn(d=64) == tp.TP_ERR_UNSUPPORTED
+    assert attn(hq=3, hkv=2) == tp.TP_ERR_SHAPE
+    assert "multiple of hkv" in tp.tp_last_error()
+    assert attn(hkv=0) == tp.TP_ERR_SHAPE
+    assert attn(h=260) == tp.TP_ERR_SHAPE
+    ws_need = tp.tp_shard_attn_workspace_bytes(2, 64, 4, 2, 128)
+    m = 2 * 64
+    expect = 4 * 128 * m * 2 + 2 * 128 * m * 2 + 2 * 2 * 128 * 64 * 2 + 4 * 128 * m * 2
+    assert ws_need == expect
+    st = status("tp_shard_attn", 2, 64, 256, 4, 2, 128, 500000.0, 1, A16, A16, A16, A16, ws_need - 1,
+                A16, None)
+    assert st == tp.TP_ERR_WORKSPACE
+    assert status("tp_qkv_rope", 2, 64, 256, 4, 2, 128, 0.5, A16, A16, A16, A16, A16, None) == tp.TP_ERR_INVALID_ARG
+    assert status("tp_flash_attn", 2, 64, 4, 2, 128, 1, A16, A16, None, A16, None) == tp.TP_ERR_INVALID_ARG
+    # seq padding to 64 in the transposed-V region
+    assert tp.tp_shard_attn_workspace_bytes(1, 65, 1, 1, 128) >= 128 * 128 * 2
+
+
+def test_shard_sum_validation(L):
+    ptrs = (ctypes.c_void_p * 17)(*([A16 + 64 * i for i in range(17)]))
+    assert status("tp_shard_sum", 0, 16, ptrs, None, 0, A16 + 4096, None) == tp.TP_ERR_SHAPE
+    assert status("tp_shard_sum", 17, 16, ptrs, None, 0, A16 + 4096, None) == tp.TP_ERR_SHAPE
+    assert status("tp_shard_sum", 2, 16, ptrs, None, 0, A16, None) == tp.TP_ERR_INVALID_ARG  # out aliases
+    assert "aliases partials[0]" in tp.tp_last_error()
+    bad = (ctypes.c_void_p * 2)(A16, MIS)
+    assert status("tp_shard_sum", 2, 16, bad, None, 0, A16 + 4096, None) == tp.TP_ERR_INVALID_ARG
+    assert "partials[1]" in tp.tp_last_error()
+    # out may alias a float32 residual but not a bf16 one
+    assert status("tp_shard_sum", 2, 16, ptrs, A16 + 4096, 1, A16 + 4096, None) == tp.TP_ERR_INVALID_ARG
+    assert status("tp_shard_sum", 2, 16, ptrs, A16 + 4096, 5, A16 + 8192, None) == tp.TP_ERR_INVALID_ARG
+
+
+def test_rmsnorm_validation(L):
+    assert status("tp_rmsnorm", 1, 4, 12, A16, None, 1e-5, A16, None) == tp.TP_ERR_SHAPE
+    assert status("tp_rmsnorm", 3, 4, 16, A16, None, 1e-5, A16, None) == tp.TP_ERR_INVALID_ARG
+    assert status("tp_rmsnorm", 1, 4, 16, A16, None, -1.0, A16, None) == tp.TP_ERR_INVALID_ARG
+    assert status("tp_rmsnorm", 1, 4, 16, A16, MIS, 1e-5, A16, None) == tp.TP_ERR_INVALID_ARG
+
+
+def test_binding_raises_with_message(L):
+    with pytest.raises(tp.TpError) as e:
+        tp.tp_colwise("gelu", "bf16", 4, 12, 16, A16, A16, A16, stream=0)
+    assert e.value.status == tp.TP_ERR_SHAPE
+
+
+# ---------------------------------------------------------------- sharding rules
+
+
+def test_sharding_rules_raise_value_error():
+    with pytest.raises(ValueError):
+        shard.attn_heads(heads=32, kv_heads=8, t=3, rank=0)      # t does not divide heads
+    with pytest.raises(ValueError):
+        shard.attn_heads(heads=12, kv_heads=8, t=4, rank=0)      # kv does not divide heads
+    with pytest.raises(ValueError):
+        shard.attn_heads(heads=24, kv_heads=6, t=4, rank=0)      # neither split nor replicate
+    with pytest.raises(ValueError):
+        shard.colwise_weight(torch.zeros(4, 10), 4, 0)
+
+
+def test_sharding_layouts():
+    a = torch.arange(6 * 8, dtype=torch.float32).reshape(6, 8)
+    w = shard.colwise_weight(a, 2, 1)
+    assert w.shape == (4, 6) and torch.equal(w, a[:, 4:8].t())
+    b = torch.arange(8 * 6, dtype=torch.float32).reshape(8, 6)
+    assert torch.equal(shard.rowwise_weight(b, 4, 3), b[6:8].t())
+    g = shard.packed_gate_up(a, a + 1000, 2, 0)
+    assert torch.equal(g[:4], a[:, :4].t()) and torch.equal(g[4:], (a + 1000)[:, :4].t())
+    # GQA: 64 query heads / 8 KV heads; t = 16 replicates each KV head on 2 ranks
+    assert shard.attn_heads(64, 8, 16, 0) == ([0, 1, 2, 3], [0])
+    assert shard.attn_heads(64, 8, 16, 1) == ([4, 5, 6, 7], [0])
+    assert shard.attn_heads(64, 8, 16, 15)[1] == [7]
+    assert shard.attn_heads(32, 8, 4, 1) == ([8, 9, 10, 11, 12, 13, 14, 15], [2, 3])
+    d = 2
+    wq = torch.arange(3 * 8 * d, dtype=torch.float32).reshape(3, 8 * d)
+    wk = -torch.arange(3 * 2 * d, dtype=torch.float32).reshape(3, 2 * d)
+    wv = wk - 100
+    wo = torch.arange(8 * d * 3, dtype=torch.float32).reshape(8 * d, 3)
+    r = shard.attn_rank(wq, wk, wv, wo, heads=8, kv_heads=2, head_dim=d, t=4, rank=3)
+    assert (r.hq, r.hkv) == (2, 1)
+    assert torch.equal(r.w_qkv[: 2 * d], wq[:, 6 * d:8 * d].t())
+    assert torch.equal(r.w_qkv[2 * d:3 * d], wk[:, d:2 * d].t())
+    assert torch.equal(r.w_qkv[3 * d:], wv[:, d:2 * d].t())
+    assert torch.equal(r.w_o, wo[6 * d:8 * d].t())

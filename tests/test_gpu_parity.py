@@ -1,0 +1,379 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Every comparison uses the same seeded inputs on both sides.  Bars:
+* float32 cases: max |gpu - oracle| <= 1e-4 (the worked example's atol);
+* bf16 cases: max |gpu - oracle| / max |oracle| <= 2e-2 per compared tensor;
+* integer-valued GEMMs and the shard-sum: bit-exact.
+Small cases are compared element by element; the full-size workloads on
+sampled token rows (every op but attention is row-local, and attention rows
+need only K and V, which the oracle computes for every token).
+"""
+import time
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from megatron_tensor_transformer_colwise_amd import inputs, shard, tpshard as tp
+
+pytestmark = pytest.mark.gpu
+
+BF16_TOL = 2e-2
+F32_ATOL = 1e-4
+
+
+@pytest.fixture(scope="module", autouse=True)
+def device():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    if not tp.LIB_PATH.exists():
+        raise RuntimeError("libtpshard.so is not built")
+    torch.cuda.set_device(0)
+    tp.tp_device_check()
+    return torch.device("cuda:0")
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+def rel_err(got, ref):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    assert np.all(np.isfinite(got)), "non-finite GPU output"
+    return float(np.max(np.abs(got - ref)) / max(np.max(np.abs(ref)), 1e-30))
+
+
+def to_dev(ht, dev):
+    return ht.torch().to(dev)
+
+
+def host(t, rows=None):
+    if rows is not None:
+        t = t[torch.from_numpy(np.asarray(rows)).to(t.device)]
+    return t.detach().float().cpu().double().numpy()
+
+
+# ---------------------------------------------------------------- worked example (float32)
+
+
+def test_tiny_mlp_f32_worked_example(device):
+    """Seed-0 example of the "MLP" section, float32: every partial and the sum
+    within atol 1e-4 of the oracle, and the page's allclose predicate holds."""
+    case = inputs.CONFIGS["tiny_mlp_f32"]
+    say(f"case {case.name}")
+    w = inputs.gen_mlp(case)
+    dw = {k: to_dev(v, device) for k, v in w.items()}
+    mlp = shard.MLPShards(dw["X"], dw, case.t, "gelu", "f32")
+    out = mlp.forward()
+    torch.cuda.synchronize()
+    x, a, b = w["X"].f64(), w["A"].f64(), w["B"].f64()
+    ref = oracle.mlp_gelu(x, a, b)
+    parts = oracle.mlp_gelu_partials(x, a, b, case.t)
+    for r in range(case.t):
+        assert np.max(np.abs(host(mlp.partials[r]) - parts[r])) <= F32_ATOL
+    got = host(out)
+    assert np.max(np.abs(got - ref)) <= F32_ATOL
+    assert np.allclose(got, ref, atol=1e-4, rtol=1e-5)
+
+
+# ---------------------------------------------------------------- exact GEMMs
+
+
+@pytest.mark.parametrize("m,k,n", [(300, 520, 264), (520, 1032, 520), (1, 8, 8), (257, 64, 256)])
+def test_rowwise_gemm_integer_bit_exact(device, m, k, n):
+    """Integer inputs in [-2, 2]: every product and sum is exact in float32, so
+    the partial must equal the oracle's float64 product bit for bit.  Shapes
+    cover one and several 256 x 256 tiles, ragged m/n and a k tail."""
+    say(f"case rowwise int m={m} k={k} n={n}")
+    y = inputs.integers(7, 0, (m, k), -2, 2)
+    w = inputs.integers(7, 1, (n, k), -2, 2)
+    out = torch.empty(m, n, dtype=torch.float32, device=device)
+    tp.tp_rowwise("bf16", m, k, n, to_dev(y, device), to_dev(w, device), out)
+    torch.cuda.synchronize()
+    ref = y.f64() @ w.f64().T
+    assert np.array_equal(host(out), ref)
+
+
+@pytest.mark.parametrize("m,k,n", [(300, 40, 264), (64, 48, 512)])
+def test_colwise_none_integer_bit_exact(device, m, k, n):
+    """Plain colwise projection, integers small enough (|sum| <= 2*2*48 < 256)
+    that the bf16 output is exact."""
+    say(f"case colwise int m={m} k={k} n={n}")
+    x = inputs.integers(8, 0, (m, k), -2, 2)
+    w = inputs.integers(8, 1, (n, k), -2, 2)
+    out = torch.empty(m, n, dtype=torch.bfloat16, device=device)
+    tp.tp_colwise("none", "bf16", m, k, n, to_dev(x, device), to_dev(w, device), out)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(out), x.f64() @ w.f64().T)
+
+
+# ---------------------------------------------------------------- MLP, small
+
+
+@pytest.mark.parametrize("act,m,h,inter,t", [("gelu", 300, 264, 400, 2), ("swiglu", 333, 256, 544, 2),
+                                             ("gelu", 64, 128, 1024, 4), ("swiglu", 512, 512, 2048, 4)])
+def test_mlp_small(device, act, m, h, inter, t):
+    say(f"case mlp {act} m={m} h={h} inter={inter} t={t}")
+    case = inputs.MLPCase("small", m, h, inter, t, act, "bf16", seed=21)
+    w = inputs.gen_mlp(case)
+    dw = {k: to_dev(v, device) for k, v in w.items()}
+    mlp = shard.MLPShards(dw["X"], dw, t, act)
+    out = mlp.forward()
+    torch.cuda.synchronize()
+    W = {k: v.f64() for k, v in w.items()}
+    if act == "gelu":
+        parts = oracle.mlp_gelu_partials(W["X"], W["A"], W["B"], t)
+        full = oracle.mlp_gelu(W["X"], W["A"], W["B"])
+    else:
+        parts = oracle.mlp_swiglu_partials(W["X"], W["W1"], W["W3"], W["W2"], t)
+        full = oracle.mlp_swiglu(W["X"], W["W1"], W["W3"], W["W2"])
+    for r in range(t):
+        e = rel_err(host(mlp.partials[r]), parts[r])
+        assert e <= BF16_TOL, (r, e)
+    assert rel_err(host(out), full) <= BF16_TOL
+
+
+def test_colwise_activation_slices(device):
+    """The colwise output Y_i itself (bf16) against the oracle's activation."""
+    say("case colwise slices")
+    m, h, f, t = 200, 128, 512, 2
+    for act in ("gelu", "swiglu"):
+        case = inputs.MLPCase("slices", m, h, f, t, act, "bf16", seed=22)
+        w = inputs.gen_mlp(case)
+        dw = {k: to_dev(v, device) for k, v in w.items()}
+        mlp = shard.MLPShards(dw["X"], dw, t, act)
+        W = {k: v.f64() for k, v in w.items()}
+        for r in range(t):
+            mlp.colwise(r)
+            torch.cuda.synchronize()
+            if act == "gelu":
+                ref = oracle.colwise_act(W["X"], oracle.split_columns(W["A"], t)[r], "gelu")
+            else:
+                ref = oracle.colwise_act(W["X"], None, "swiglu",
+                                         (oracle.split_columns(W["W1"], t)[r], oracle.split_columns(W["W3"], t)[r]))
+            assert rel_err(host(mlp.act_ws), ref) <= BF16_TOL
+
+
+# ---------------------------------------------------------------- attention, small
+
+
+@pytest.mark.parametrize("batch,seq,h,heads,kv,t,causal", [
+    (2, 200, 256, 8, 2, 2, True),     # ragged seq (not a multiple of 64 or 128)
+    (1, 128, 128, 4, 1, 4, True),     # one head per rank
+    (2, 96, 256, 8, 2, 8, True),      # kv < t: each KV head replicated on 4 ranks
+    (3, 64, 256, 4, 4, 1, True),      # MHA, one rank
+    (1, 1, 128, 2, 1, 1, True),       # a single token
+])
+def test_attention_small(device, batch, seq, h, heads, kv, t, causal):
+    say(f"case attn b={batch} s={seq} h={h} heads={heads} kv={kv} t={t} causal={causal}")
+    case = inputs.AttnCase("small", batch, seq, h, heads, kv, 128, t, 500000.0, seed=31)
+    w = inputs.gen_attn(case)
+    dw = {k: to_dev(v, device) for k, v in w.items()}
+    at = shard.AttnShards(dw["X"], dw, case, causal=causal)
+    out = at.forward()
+    torch.cuda.synchronize()
+    W = {k: v.f64() for k, v in w.items()}
+    full = oracle.attn_partial(W["X"], W, case, 0, t=1)
+    for r in range(t):
+        ref = oracle.attn_partial(W["X"], W, case, r, t=t)
+        e = rel_err(host(at.partials[r]), ref)
+        assert e <= BF16_TOL, (r, e)
+    assert rel_err(host(out), full) <= BF16_TOL
+
+
+def test_attention_core_non_causal(device):
+    """Non-causal core on its own: Q/K/V written by tp_qkv_rope, compared with
+    softmax(q k^T / sqrt d) v over the whole sequence in float64."""
+    say("case attn core non-causal")
+    batch, seq, hq, hkv, d = 2, 130, 4, 2, 128
+    m = batch * seq
+    g = torch.Generator().manual_seed(5)
+    q = torch.randn(m, hq * d, generator=g).to(torch.bfloat16)
+    k = torch.randn(m, hkv * d, generator=g).to(torch.bfloat16)
+    v = torch.randn(m, hkv * d, generator=g).to(torch.bfloat16)
+    seq_pad = (seq + 63) // 64 * 64
+    vt = torch.zeros(batch, hkv, d, seq_pad, dtype=torch.bfloat16)
+    vt[..., :seq] = v.view(batch, seq, hkv, d).permute(0, 2, 3, 1)
+    o = torch.empty(m, hq * d, dtype=torch.bfloat16, device=device)
+    tp.tp_flash_attn(batch, seq, hq, hkv, d, 0, q.to(device), k.to(device), vt.to(device), o)
+    torch.cuda.synchronize()
+    qh, kh, vh = (a.double().numpy() for a in (q, k, v))
+    got = host(o)
+    for b in range(batch):
+        rows = slice(b * seq, (b + 1) * seq)
+        for j in range(hq):
+            gk = j // (hq // hkv)
+            qq, kk, vv = qh[rows, j * d:(j + 1) * d], kh[rows, gk * d:(gk + 1) * d], vh[rows, gk * d:(gk + 1) * d]
+            s = qq @ kk.T / np.sqrt(d)
+            p = np.exp(s - s.max(1, keepdims=True))
+            ref = (p / p.sum(1, keepdims=True)) @ vv
+            assert rel_err(got[rows, j * d:(j + 1) * d], ref) <= BF16_TOL
+
+
+# ---------------------------------------------------------------- shard-sum and norm
+
+
+@pytest.mark.parametrize("t,n,res", [(1, 7, None), (2, 1000003, "f32"), (5, 4099, "bf16"),
+                                     (16, 262147, "f32"), (8, 4, None), (3, 1 << 20, "bf16")])
+def test_shard_sum_bit_exact(device, t, n, res):
+    """Ascending-rank float32 sum (+ residual last) is bit-exact to the
+    oracle's float32 mode; n covers ragged tails."""
+    say(f"case shard_sum t={t} n={n} res={res}")
+    parts = [inputs.normal(41, s, (n,), 1.0, "f32").data for s in range(t)]
+    dparts = torch.stack([torch.from_numpy(p) for p in parts]).to(device)
+    out = torch.empty(n, dtype=torch.float32, device=device)
+    r_host = None
+    r_dev = None
+    if res is not None:
+        rt = inputs.normal(41, 99, (n,), 1.0, res)
+        r_host = rt.f32()
+        r_dev = to_dev(rt, device)
+    tp.tp_shard_sum(t, n, list(dparts), r_dev, res or "f32", out)
+    torch.cuda.synchronize()
+    ref = oracle.shard_sum_f32(parts, r_host)
+    assert np.array_equal(out.cpu().numpy(), ref)
+
+
+def test_shard_sum_in_place_residual(device):
+    say("case shard_sum in place")
+    n, t = 10000, 4
+    parts = [inputs.normal(42, s, (n,), 1.0, "f32").data for s in range(t)]
+    res = inputs.normal(42, 50, (n,), 1.0, "f32").data
+    dparts = torch.stack([torch.from_numpy(p) for p in parts]).to(device)
+    acc = torch.from_numpy(res.copy()).to(device)
+    tp.tp_shard_sum(t, n, list(dparts), acc, "f32", acc)
+    torch.cuda.synchronize()
+    assert np.array_equal(acc.cpu().numpy(), oracle.shard_sum_f32(parts, res))
+
+
+@pytest.mark.parametrize("in_dt,m,h,gain", [("bf16", 37, 8192, True), ("f32", 5, 136, False),
+                                            ("f32", 300, 4096, True), ("bf16", 1, 16392, True)])
+def test_rmsnorm(device, in_dt, m, h, gain):
+    say(f"case rmsnorm {in_dt} m={m} h={h} gain={gain}")
+    x = inputs.normal(51, 0, (m, h), 3.0, in_dt)
+    gv = (inputs.normal(51, 1, (h,), 0.1, "f32").data + np.float32(1)) if gain else None
+    y = torch.empty(m, h, dtype=torch.bfloat16, device=device)
+    tp.tp_rmsnorm(in_dt, m, h, to_dev(x, device), None if gv is None else torch.from_numpy(gv).to(device),
+                  1e-5, y)
+    torch.cuda.synchronize()
+    ref = oracle.rmsnorm(x.f64(), None if gv is None else gv.astype(np.float64), 1e-5)
+    got = host(y)
+    # bf16 output: one rounding (2^-9 relative) plus float32 arithmetic
+    assert np.all(np.abs(got - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-6)
+
+
+# ---------------------------------------------------------------- determinism
+
+
+def test_bitwise_deterministic(device):
+    say("case determinism")
+    case = inputs.AttnCase("det", 2, 256, 512, 8, 2, 128, 2, 500000.0, seed=61)
+    w = inputs.gen_attn(case)
+    dw = {k: to_dev(v, device) for k, v in w.items()}
+    at = shard.AttnShards(dw["X"], dw, case)
+    a = at.forward().clone()
+    b = at.forward().clone()
+    assert torch.equal(a, b)
+    mc = inputs.MLPCase("det", 512, 512, 2048, 2, "swiglu", "bf16", seed=62)
+    mw = {k: to_dev(v, device) for k, v in inputs.gen_mlp(mc).items()}
+    mlp = shard.MLPShards(mw["X"], mw, 2, "swiglu")
+    a = mlp.forward().clone()
+    b = mlp.forward().clone()
+    assert torch.equal(a, b)
+
+
+# ---------------------------------------------------------------- full-size workloads
+
+
+def test_config_gpt_gelu_mlp(device):
+    """GPT-style GeLU MLP, 2048 tokens, h=1024, inter 4096, t=4: all partials
+    and the shard-sum against the full float64 oracle."""
+    case = inputs.CONFIGS["gpt_gelu_mlp"]
+    say(f"case {case.name}")
+    t0 = time.time()
+    w = inputs.gen_mlp(case)
+    dw = {k: to_dev(v, device) for k, v in w.items()}
+    mlp = shard.MLPShards(dw["X"], dw, case.t, "gelu")
+    out = mlp.forward()
+    torch.cuda.synchronize()
+    W = {k: v.f64() for k, v in w.items()}
+    parts = oracle.mlp_gelu_partials(W["X"], W["A"], W["B"], case.t)
+    for r in range(case.t):
+        assert rel_err(host(mlp.partials[r]), parts[r]) <= BF16_TOL
+    assert rel_err(host(out), oracle.mlp_gelu(W["X"], W["A"], W["B"])) <= BF16_TOL
+    say(f"  done in {time.time() - t0:.1f}s")
+
+
+def test_config_llama8b_swiglu_mlp(device):
+    """Llama-3-8B-shaped SwiGLU MLP, 4096 tokens, t=4, on 64 sampled rows."""
+    case = inputs.CONFIGS["llama8b_swiglu_mlp"]
+    say(f"case {case.name}")
+    t0 = time.time()
+    w = inputs.gen_mlp(case)
+    dw = {k: to_dev(v, device) for k, v in w.items()}
+    mlp = shard.MLPShards(dw["X"], dw, case.t, "swiglu")
+    out = mlp.forward()
+    torch.cuda.synchronize()
+    rows = inputs.sample_rows(1, case.tokens, 61, seed=3)
+    X = w["X"].f64()[rows]
+    W1, W3, W2 = w["W1"].f64(), w["W3"].f64(), w["W2"].f64()
+    parts = oracle.mlp_swiglu_partials(X, W1, W3, W2, case.t)
+    for r in range(case.t):
+        assert rel_err(host(mlp.partials[r], rows), parts[r]) <= BF16_TOL
+    assert rel_err(host(out, rows), oracle.shard_sum(parts)) <= BF16_TOL
+    say(f"  done in {time.time() - t0:.1f}s")
+
+
+def test_config_llama8b_attn(device):
+    """Llama-3-8B-shaped attention, batch 2 x 2048, 32/8 heads, t=4, sampled rows."""
+    case = inputs.CONFIGS["llama8b_attn"]
+    say(f"case {case.name}")
+    t0 = time.time()
+    w = inputs.gen_attn(case)
+    dw = {k: to_dev(v, device) for k, v in w.items()}
+    at = shard.AttnShards(dw["X"], dw, case)
+    out = at.forward()
+    torch.cuda.synchronize()
+    rows = inputs.sample_rows(case.batch, case.seq, 29, seed=4)
+    W = {k: v.f64() for k, v in w.items()}
+    parts = [oracle.attn_partial(W["X"], W, case, r, rows=rows) for r in range(case.t)]
+    for r in range(case.t):
+        assert rel_err(host(at.partials[r], rows), parts[r]) <= BF16_TOL
+    assert rel_err(host(out, rows), oracle.shard_sum(parts)) <= BF16_TOL
+    say(f"  done in {time.time() - t0:.1f}s")
+
+
+@pytest.fixture(scope="module")
+def block70b():
+    case = inputs.CONFIGS["llama70b_block_t8"]
+    w = inputs.gen_block(case)
+    rows = inputs.sample_rows(case.batch, case.seq, 13, seed=5)
+    W = {k: v.f64() for k, v in w.items()}
+    ref = oracle.block(W["X"], W, case, t=1, rows=rows)
+    return case, w, rows, ref
+
+
+@pytest.mark.parametrize("t", [8, 16])
+def test_config_70b_block(device, block70b, t):
+    """70B-shaped block (attention + SwiGLU MLP, RMSNorm replicated), batch
+    4 x 2048, at t=8 and t=16 (a KV head on 2 ranks): sampled rows of h1 and Z
+    against the unsharded float64 block, and the same rows at t=8 and t=16."""
+    case, w, rows, ref = block70b
+    say(f"case llama70b block t={t}")
+    t0 = time.time()
+    dw = {k: to_dev(v, device) for k, v in w.items()}
+    blk = shard.BlockShards(dw["X"], dw, case, t=t)
+    z = blk.forward()
+    torch.cuda.synchronize()
+    assert rel_err(host(blk.attn.out, rows), ref["h1"]) <= BF16_TOL
+    assert rel_err(host(z, rows), ref["z"]) <= BF16_TOL
+    say(f"  done in {time.time() - t0:.1f}s")
+
+
+def test_smoke_entry(device):
+    import __graft_entry__
+
+    __graft_entry__.smoke()
