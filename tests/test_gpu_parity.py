@@ -223,7 +223,8 @@ def test_shard_sum_bit_exact(device, t, n, res):
     oracle's float32 mode; n covers ragged tails."""
     say(f"case shard_sum t={t} n={n} res={res}")
     parts = [inputs.normal(41, s, (n,), 1.0, "f32").data for s in range(t)]
-    dparts = torch.stack([torch.from_numpy(p) for p in parts]).to(device)
+    # one allocation per partial: the ABI requires 16-byte aligned pointers
+    dparts = [torch.from_numpy(p).to(device) for p in parts]
     out = torch.empty(n, dtype=torch.float32, device=device)
     r_host = None
     r_dev = None
@@ -231,7 +232,7 @@ def test_shard_sum_bit_exact(device, t, n, res):
         rt = inputs.normal(41, 99, (n,), 1.0, res)
         r_host = rt.f32()
         r_dev = to_dev(rt, device)
-    tp.tp_shard_sum(t, n, list(dparts), r_dev, res or "f32", out)
+    tp.tp_shard_sum(t, n, dparts, r_dev, res or "f32", out)
     torch.cuda.synchronize()
     ref = oracle.shard_sum_f32(parts, r_host)
     assert np.array_equal(out.cpu().numpy(), ref)
