@@ -11,12 +11,12 @@
 //
 // Tiling: 256 x 256 output tile per workgroup of 4 waves, each wave a
 // 128 x 128 sub-tile of 4 x 4 v_mfma_f32_32x32x16_bf16 blocks (256 float32
-// accumulators per lane).  k advances 64 at a time through a two-stage LDS
-// ring (2 x 64 KiB); tiles are fetched with 16-byte buffer loads that write
-// LDS directly (no register staging).  Out-of-range rows and the k tail are
-// fetched as zeros by the buffer's range check.  Each LDS row is 128 bytes;
-// its eight 16-byte chunks are XOR-permuted by swz(row) so the 32 rows one
-// fragment read touches spread over all banks.
+// accumulators per lane).  k advances BK at a time through an NSTAGE-deep LDS
+// ring; tiles are fetched with 16-byte buffer loads that write LDS directly (no
+// register staging), NSTAGE - 1 k-steps ahead of the MFMAs.  Out-of-range rows
+// and the k tail are fetched as zeros by the buffer's range check.  Each LDS
+// row holds BK bf16; its 16-byte chunks are XOR-permuted by swz(row) so the 32
+// rows one fragment read touches spread over all banks.
 #include "common.h"
 #include "kernels.h"
 
@@ -25,11 +25,24 @@ namespace {
 
 constexpr int BM = 256;
 constexpr int BN = 256;
-constexpr int BK = 64;
 constexpr int NT = 256;
-constexpr int TILE_BYTES = 256 * BK * 2;       // one operand, one stage
-constexpr int STAGE_BYTES = 2 * TILE_BYTES;    // A then B
-constexpr int SMEM_BYTES = 2 * STAGE_BYTES;    // two stages
+#ifndef TP_GEMM_BK
+#define TP_GEMM_BK 64
+#endif
+#ifndef TP_GEMM_NSTAGE
+#define TP_GEMM_NSTAGE 2
+#endif
+constexpr int BK = TP_GEMM_BK;                  // k per stage (32 or 64)
+constexpr int NSTAGE = TP_GEMM_NSTAGE;          // LDS ring depth
+constexpr int CH = BK / 8;                      // 16-byte chunks per tile row
+constexpr int ROWB = BK * 2;                    // bytes per tile row
+constexpr int KSUB = BK / 16;                   // MFMA k-steps per stage
+constexpr int LPT = CH;                         // loads per thread per operand per stage
+constexpr int TILE_BYTES = 256 * ROWB;          // one operand, one stage
+constexpr int STAGE_BYTES = 2 * TILE_BYTES;     // A then B
+constexpr int SMEM_BYTES = NSTAGE * STAGE_BYTES;
+static_assert(BK == 32 || BK == 64, "BK");
+static_assert(SMEM_BYTES <= 160 * 1024, "LDS");
 
 struct Args {
   const bf16_t* x;
@@ -40,7 +53,12 @@ struct Args {
   QkvOut qkv;
 };
 
-__device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
+// Chunk permutation of tile row r.  Reads of one fragment touch 32 consecutive
+// rows at one logical chunk; the permutation makes every 8-row group (128-byte
+// bank window) and every 16-row group (256-byte window) hit distinct banks.
+__device__ __forceinline__ int swz(int r) {
+  return BK == 64 ? ((r ^ (r >> 3)) & 7) : (((r >> 1) ^ (r >> 3)) & 3);
+}
 
 // Launch index -> output tile.  Workgroups are dealt to the 8 XCDs round-robin;
 // first undo that so each XCD owns a contiguous range of logical tiles, then
@@ -76,8 +94,6 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(Args args) {
   const uint32_t row_bytes = (uint32_t)(K * 2);
 
   // ---- global -> LDS addressing -------------------------------------------
-  // Slot s = (j * 4 + wave) * 64 + lane of a stage holds tile row s / 8,
-  // physical chunk s % 8, i.e. logical chunk (s % 8) ^ swz(row).
   const int m_rows = (int)min<int64_t>(BM, M - m0);
   __amdgpu_buffer_rsrc_t rsrc_a =
       make_rsrc(args.x + m0 * K, (uint32_t)m_rows * row_bytes);
@@ -94,15 +110,17 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(Args args) {
     rsrc_b = make_rsrc(args.w + n0 * K, (uint32_t)n_valid * row_bytes);
   }
 
-  uint32_t a_off[8], b_off[8];
-  int a_k[8], b_k[8];  // element offset of the chunk within the k-block
+  // Slot s = (j * 4 + wave) * 64 + lane of a stage holds tile row s / CH,
+  // physical chunk s % CH, i.e. logical chunk (s % CH) ^ swz(row).
+  uint32_t a_off[LPT], b_off[LPT];
+  int a_k[LPT];  // element offset of the chunk within the k-block
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int r = (j * 4 + wave) * 8 + (lane >> 3);
-    const int c = (lane & 7) ^ swz(r);
+  for (int j = 0; j < LPT; ++j) {
+    const int slot = (j * 4 + wave) * 64 + lane;
+    const int r = slot / CH;
+    const int c = (slot % CH) ^ swz(r);
     a_k[j] = c * 8;
     a_off[j] = (uint32_t)r * row_bytes + (uint32_t)c * 16;
-    b_k[j] = c * 8;
     if (EPI == EPI_SWIGLU) {
       const int wn = r >> 7, qq = r & 127;
       const int o_rel = wn * 64 + (qq & 63);
@@ -113,35 +131,28 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(Args args) {
     }
   }
 
-  auto load_stage = [&](int stage, int64_t k0) {
-    char* sa = smem + stage * STAGE_BYTES;
-    char* sb = sa + TILE_BYTES;
+  // load j (0 .. LPT-1) of both operands of the stage at k0
+  auto load_one = [&](char* stage, int j, int64_t k0) {
     const uint32_t kb = (uint32_t)(k0 * 2);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const bool ka = (k0 + a_k[j]) < K;
-      buffer_load_lds16(rsrc_a, sa + (j * 4 + wave) * 1024, ka ? a_off[j] + kb : TP_OOB_OFFSET);
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const bool kbv = (k0 + b_k[j]) < K && b_off[j] != TP_OOB_OFFSET;
-      buffer_load_lds16(rsrc_b, sb + (j * 4 + wave) * 1024, kbv ? b_off[j] + kb : TP_OOB_OFFSET);
-    }
+    const bool kin = (k0 + a_k[j]) < K;
+    buffer_load_lds16(rsrc_a, stage + (j * 4 + wave) * 1024, kin ? a_off[j] + kb : TP_OOB_OFFSET);
+    buffer_load_lds16(rsrc_b, stage + TILE_BYTES + (j * 4 + wave) * 1024,
+                      (kin && b_off[j] != TP_OOB_OFFSET) ? b_off[j] + kb : TP_OOB_OFFSET);
   };
 
   // ---- LDS -> registers addressing ----------------------------------------
   const int wm = wave >> 1, wn = wave & 1;
   const int l31 = lane & 31, hk = lane >> 5;
-  uint32_t ra[4][4], rb[4][4];  // [i or j][s] byte offsets within a tile
+  uint32_t ra[4][KSUB], rb[4][KSUB];  // [i or j][s] byte offsets within a tile
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int r_a = wm * 128 + i * 32 + l31;
     const int r_b = wn * 128 + i * 32 + l31;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
+    for (int s = 0; s < KSUB; ++s) {
       const int c = 2 * s + hk;
-      ra[i][s] = (uint32_t)(r_a * 128 + ((c ^ swz(r_a)) << 4));
-      rb[i][s] = (uint32_t)(r_b * 128 + ((c ^ swz(r_b)) << 4));
+      ra[i][s] = (uint32_t)(r_a * ROWB + ((c ^ swz(r_a)) << 4));
+      rb[i][s] = (uint32_t)(r_b * ROWB + ((c ^ swz(r_b)) << 4));
     }
   }
 
@@ -151,27 +162,53 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(Args args) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
 
+  // Fragments are double-buffered in registers: while the 16 MFMAs of k-step
+  // s run, the 8 fragment reads of step s + 1 are in flight, so LDS latency
+  // does not stall the matrix pipe inside a stage.
+  u32x4 fa[2][4], fb[2][4];
   const int nk = (int)((K + BK - 1) / BK);
-  load_stage(0, 0);
+#pragma unroll
+  for (int st = 0; st < NSTAGE - 1; ++st)
+#pragma unroll
+    for (int j = 0; j < LPT; ++j) load_one(smem + st * STAGE_BYTES, j, (int64_t)st * BK);
   for (int kt = 0; kt < nk; ++kt) {
-    wait_vmcnt0();
+    // this wave's loads of stage kt have landed once at most the later
+    // NSTAGE - 2 stages' loads are outstanding; the barrier extends that to
+    // every wave, and retires all reads of the buffer about to be refilled
+    wait_vmcnt<2 * LPT * (NSTAGE - 2)>();
     __syncthreads();
-    if (kt + 1 < nk) load_stage((kt + 1) & 1, (int64_t)(kt + 1) * BK);
-    const char* sa = smem + (kt & 1) * STAGE_BYTES;
+    const char* sa = smem + (kt % NSTAGE) * STAGE_BYTES;
     const char* sb = sa + TILE_BYTES;
+    char* nstage = smem + ((kt + NSTAGE - 1) % NSTAGE) * STAGE_BYTES;
+    const int64_t kn = (int64_t)(kt + NSTAGE - 1) * BK;  // beyond K at the end: loads read zeros
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      u32x4 a[4], b[4];
+    for (int i = 0; i < 4; ++i) fa[0][i] = lds_read16(sa + ra[i][0]);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) a[i] = lds_read16(sa + ra[i][s]);
+    for (int j = 0; j < 4; ++j) fb[0][j] = lds_read16(sb + rb[j][0]);
+    // every load of the stage NSTAGE - 1 ahead goes out at once: the vector
+    // memory path sustains its throughput only with many requests in flight
 #pragma unroll
-      for (int j = 0; j < 4; ++j) b[j] = lds_read16(sb + rb[j][s]);
+    for (int j = 0; j < LPT; ++j) load_one(nstage, j, kn);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int s = 0; s < KSUB; ++s) {
+      const int cur = s & 1, nxt = cur ^ 1;
+      if (s + 1 < KSUB) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) fa[nxt][i] = lds_read16(sa + ra[i][s + 1]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) fb[nxt][j] = lds_read16(sb + rb[j][s + 1]);
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = mfma32x32x16(a[i], b[j], acc[i][j]);
+        for (int j = 0; j < 4; ++j) acc[i][j] = mfma32x32x16(fa[cur][i], fb[cur][j], acc[i][j]);
+      // fence: nothing of step s + 1 (its fragment reads for s + 2) moves up
+      // into this step, so each step's reads overlap exactly one step of MFMAs
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
+  wait_vmcnt0();
 
   // ---- epilogue -----------------------------------------------------------
   // Accumulator element r of block (i, j) in lane L is output row
