@@ -9,9 +9,9 @@
 // Both operands are contiguous along k (X row-major, W in nn.Linear layout), so
 // every MFMA operand of a lane is 16 contiguous bytes of one row.
 //
-// Tiling: 256 x 256 output tile per workgroup of 4 waves, each wave a
-// 128 x 128 sub-tile of 4 x 4 v_mfma_f32_32x32x16_bf16 blocks (256 float32
-// accumulators per lane).  k advances BK at a time through an NSTAGE-deep LDS
+// Tiling: 256 x 256 output tile per workgroup of 8 waves (two per SIMD), each
+// wave a 64 x 128 sub-tile of 2 x 4 v_mfma_f32_32x32x16_bf16 blocks (128
+// float32 accumulators per lane).  k advances BK at a time through an NSTAGE-deep LDS
 // ring; tiles are fetched with 16-byte buffer loads that write LDS directly (no
 // register staging), NSTAGE - 1 k-steps ahead of the MFMAs.  Out-of-range rows
 // and the k tail are fetched as zeros by the buffer's range check.  Each LDS
@@ -25,7 +25,10 @@ namespace {
 
 constexpr int BM = 256;
 constexpr int BN = 256;
-constexpr int NT = 256;
+#ifndef TP_GEMM_NW
+#define TP_GEMM_NW 8
+#endif
+constexpr int GEMM_NW = TP_GEMM_NW;             // waves per workgroup (4 or 8)
 #ifndef TP_GEMM_BK
 #define TP_GEMM_BK 64
 #endif
@@ -80,8 +83,15 @@ __device__ __forceinline__ void tile_coords(int id, int nb, int num_bm, int num_
   bn = inner / gs;
 }
 
-template <int EPI>
-__global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(Args args) {
+// NW waves per workgroup laid out (NW / 2) x 2 over the 256 x 256 tile: each
+// wave owns 512/NW rows x 128 columns, i.e. MI = 16/NW row blocks of 32 and
+// 4 column blocks.  With NW = 8 two waves share each SIMD, so one can issue
+// MFMAs while the other waits on memory or the barrier.
+template <int EPI, int NW>
+__global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(Args args) {
+  constexpr int MI = 16 / NW;              // 32-row MFMA blocks per wave
+  constexpr int WROWS = 32 * MI;           // rows per wave
+  constexpr int LPW = LPT * 4 / NW;        // loads per thread per operand per stage
   __shared__ __attribute__((aligned(1024))) char smem[SMEM_BYTES];
 
   const int lane = lane_id();
@@ -110,13 +120,13 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(Args args) {
     rsrc_b = make_rsrc(args.w + n0 * K, (uint32_t)n_valid * row_bytes);
   }
 
-  // Slot s = (j * 4 + wave) * 64 + lane of a stage holds tile row s / CH,
+  // Slot s = (j * NW + wave) * 64 + lane of a stage holds tile row s / CH,
   // physical chunk s % CH, i.e. logical chunk (s % CH) ^ swz(row).
-  uint32_t a_off[LPT], b_off[LPT];
-  int a_k[LPT];  // element offset of the chunk within the k-block
+  uint32_t a_off[LPW], b_off[LPW];
+  int a_k[LPW];  // element offset of the chunk within the k-block
 #pragma unroll
-  for (int j = 0; j < LPT; ++j) {
-    const int slot = (j * 4 + wave) * 64 + lane;
+  for (int j = 0; j < LPW; ++j) {
+    const int slot = (j * NW + wave) * 64 + lane;
     const int r = slot / CH;
     const int c = (slot % CH) ^ swz(r);
     a_k[j] = c * 8;
@@ -131,76 +141,83 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(Args args) {
     }
   }
 
-  // load j (0 .. LPT-1) of both operands of the stage at k0
+  // load j (0 .. LPW-1) of both operands of the stage at k0
   auto load_one = [&](char* stage, int j, int64_t k0) {
     const uint32_t kb = (uint32_t)(k0 * 2);
     const bool kin = (k0 + a_k[j]) < K;
-    buffer_load_lds16(rsrc_a, stage + (j * 4 + wave) * 1024, kin ? a_off[j] + kb : TP_OOB_OFFSET);
-    buffer_load_lds16(rsrc_b, stage + TILE_BYTES + (j * 4 + wave) * 1024,
+    buffer_load_lds16(rsrc_a, stage + (j * NW + wave) * 1024, kin ? a_off[j] + kb : TP_OOB_OFFSET);
+    buffer_load_lds16(rsrc_b, stage + TILE_BYTES + (j * NW + wave) * 1024,
                       (kin && b_off[j] != TP_OOB_OFFSET) ? b_off[j] + kb : TP_OOB_OFFSET);
   };
 
   // ---- LDS -> registers addressing ----------------------------------------
   const int wm = wave >> 1, wn = wave & 1;
   const int l31 = lane & 31, hk = lane >> 5;
-  uint32_t ra[4][KSUB], rb[4][KSUB];  // [i or j][s] byte offsets within a tile
+  uint32_t ra[MI][KSUB], rb[4][KSUB];  // [block][s] byte offsets within a tile
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r_a = wm * 128 + i * 32 + l31;
-    const int r_b = wn * 128 + i * 32 + l31;
+  for (int i = 0; i < MI; ++i) {
+    const int r_a = wm * WROWS + i * 32 + l31;
 #pragma unroll
     for (int s = 0; s < KSUB; ++s) {
       const int c = 2 * s + hk;
       ra[i][s] = (uint32_t)(r_a * ROWB + ((c ^ swz(r_a)) << 4));
-      rb[i][s] = (uint32_t)(r_b * ROWB + ((c ^ swz(r_b)) << 4));
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int r_b = wn * 128 + j * 32 + l31;
+#pragma unroll
+    for (int s = 0; s < KSUB; ++s) {
+      const int c = 2 * s + hk;
+      rb[j][s] = (uint32_t)(r_b * ROWB + ((c ^ swz(r_b)) << 4));
     }
   }
 
-  f32x16 acc[4][4];
+  f32x16 acc[MI][4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
 
   // Fragments are double-buffered in registers: while the 16 MFMAs of k-step
   // s run, the 8 fragment reads of step s + 1 are in flight, so LDS latency
   // does not stall the matrix pipe inside a stage.
-  u32x4 fa[2][4], fb[2][4];
+  u32x4 fa[2][MI], fb[2][4];
   const int nk = (int)((K + BK - 1) / BK);
 #pragma unroll
   for (int st = 0; st < NSTAGE - 1; ++st)
 #pragma unroll
-    for (int j = 0; j < LPT; ++j) load_one(smem + st * STAGE_BYTES, j, (int64_t)st * BK);
+    for (int j = 0; j < LPW; ++j) load_one(smem + st * STAGE_BYTES, j, (int64_t)st * BK);
   for (int kt = 0; kt < nk; ++kt) {
     // this wave's loads of stage kt have landed once at most the later
     // NSTAGE - 2 stages' loads are outstanding; the barrier extends that to
     // every wave, and retires all reads of the buffer about to be refilled
-    wait_vmcnt<2 * LPT * (NSTAGE - 2)>();
+    wait_vmcnt<2 * LPW * (NSTAGE - 2)>();
     __syncthreads();
     const char* sa = smem + (kt % NSTAGE) * STAGE_BYTES;
     const char* sb = sa + TILE_BYTES;
     char* nstage = smem + ((kt + NSTAGE - 1) % NSTAGE) * STAGE_BYTES;
     const int64_t kn = (int64_t)(kt + NSTAGE - 1) * BK;  // beyond K at the end: loads read zeros
 #pragma unroll
-    for (int i = 0; i < 4; ++i) fa[0][i] = lds_read16(sa + ra[i][0]);
+    for (int i = 0; i < MI; ++i) fa[0][i] = lds_read16(sa + ra[i][0]);
 #pragma unroll
     for (int j = 0; j < 4; ++j) fb[0][j] = lds_read16(sb + rb[j][0]);
     // every load of the stage NSTAGE - 1 ahead goes out at once: the vector
     // memory path sustains its throughput only with many requests in flight
 #pragma unroll
-    for (int j = 0; j < LPT; ++j) load_one(nstage, j, kn);
+    for (int j = 0; j < LPW; ++j) load_one(nstage, j, kn);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int s = 0; s < KSUB; ++s) {
       const int cur = s & 1, nxt = cur ^ 1;
       if (s + 1 < KSUB) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) fa[nxt][i] = lds_read16(sa + ra[i][s + 1]);
+        for (int i = 0; i < MI; ++i) fa[nxt][i] = lds_read16(sa + ra[i][s + 1]);
 #pragma unroll
         for (int j = 0; j < 4; ++j) fb[nxt][j] = lds_read16(sb + rb[j][s + 1]);
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < MI; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = mfma32x32x16(fa[cur][i], fb[cur][j], acc[i][j]);
       // fence: nothing of step s + 1 (its fragment reads for s + 2) moves up
@@ -213,12 +230,12 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(Args args) {
   // ---- epilogue -----------------------------------------------------------
   // Accumulator element r of block (i, j) in lane L is output row
   // 32 i + 8 (r / 4) + 4 (L / 32) + r % 4 and column 32 j + L % 32 of the
-  // wave's 128 x 128 sub-tile.
-  const int64_t row_base = m0 + wm * 128 + 4 * hk;
+  // wave's WROWS x 128 sub-tile.
+  const int64_t row_base = m0 + wm * WROWS + 4 * hk;
   if (EPI == EPI_F32 || EPI == EPI_BF16 || EPI == EPI_GELU) {
     const int64_t col_base = (int64_t)bn * BN + wn * 128 + l31;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int64_t col = col_base + j * 32;
@@ -239,7 +256,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(Args args) {
   } else if (EPI == EPI_SWIGLU) {
     const int64_t col_base = (int64_t)bn * (BN / 2) + wn * 64 + l31;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const int64_t col = col_base + j * 32;
@@ -274,7 +291,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(Args args) {
         tpp[j] = exp2(-(double)(2 * (j * 32 + l31)) * (1.0 / 128.0) * (double)o.log2_base) *
                  0.15915494309189533577;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < MI; ++i)
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
           const int64_t row0 = row_base + i * 32 + 8 * g4;
@@ -303,7 +320,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(Args args) {
       bf16_t* vt = reinterpret_cast<bf16_t*>(o.vt);
       const bool vec = (seq & 3u) == 0;  // groups of 4 never straddle sequences
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < MI; ++i)
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
           const int64_t row0 = row_base + i * 32 + 8 * g4;
@@ -363,12 +380,13 @@ hipError_t launch_gemm_bf16(int epi, int64_t M, int64_t N, int64_t K, const void
   if (qkv) a.qkv = *qkv; else a.qkv = QkvOut{};
   const int nb = a.num_bm * a.num_bn;
   if (nb == 0) return hipSuccess;
-  dim3 grid(nb), block(NT);
+  constexpr int NW = GEMM_NW;
+  dim3 grid(nb), block(NW * 64);
   switch (epi) {
-    case EPI_F32: hipLaunchKernelGGL(gemm_bf16_kernel<EPI_F32>, grid, block, 0, s, a); break;
-    case EPI_BF16: hipLaunchKernelGGL(gemm_bf16_kernel<EPI_BF16>, grid, block, 0, s, a); break;
-    case EPI_GELU: hipLaunchKernelGGL(gemm_bf16_kernel<EPI_GELU>, grid, block, 0, s, a); break;
-    case EPI_SWIGLU: hipLaunchKernelGGL(gemm_bf16_kernel<EPI_SWIGLU>, grid, block, 0, s, a); break;
+    case EPI_F32: hipLaunchKernelGGL((gemm_bf16_kernel<EPI_F32, NW>), grid, block, 0, s, a); break;
+    case EPI_BF16: hipLaunchKernelGGL((gemm_bf16_kernel<EPI_BF16, NW>), grid, block, 0, s, a); break;
+    case EPI_GELU: hipLaunchKernelGGL((gemm_bf16_kernel<EPI_GELU, NW>), grid, block, 0, s, a); break;
+    case EPI_SWIGLU: hipLaunchKernelGGL((gemm_bf16_kernel<EPI_SWIGLU, NW>), grid, block, 0, s, a); break;
     case EPI_QKV: {
       if (a.qkv.seq_pad > a.qkv.seq) {
         const int64_t rows = (M / a.qkv.seq) * a.qkv.hkv * 128;
@@ -377,7 +395,7 @@ hipError_t launch_gemm_bf16(int epi, int64_t M, int64_t N, int64_t K, const void
         hipLaunchKernelGGL(vt_pad_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
                            reinterpret_cast<bf16_t*>(a.qkv.vt), rows, a.qkv.seq, a.qkv.seq_pad);
       }
-      hipLaunchKernelGGL(gemm_bf16_kernel<EPI_QKV>, grid, block, 0, s, a);
+      hipLaunchKernelGGL((gemm_bf16_kernel<EPI_QKV, NW>), grid, block, 0, s, a);
       break;
     }
     default: return hipErrorInvalidValue;
