@@ -193,6 +193,16 @@ tp_status tp_shard_sum(int32_t t, int64_t n, const float* const* partials, const
 tp_status tp_rmsnorm(tp_dtype in_dt, int64_t m, int64_t h, const void* x, const float* gain,
                      float eps, void* y, void* stream);
 
+/* --------------------------------------------------------------------------
+ * Introspection: how the bf16 GEMM behind tp_colwise / tp_rowwise /
+ * tp_qkv_rope tiles an m x n output (n = output columns; swiglu != 0 for the
+ * SwiGLU colwise GEMM, whose tiles cover 128 output columns instead of 256).
+ * Tile columns [0, split) run at tile height bm_main and the remaining ones at
+ * bm_tail (heights 256, 192 or 128 rows).  Host-only; launches nothing.
+ * ------------------------------------------------------------------------ */
+tp_status tp_gemm_plan(int64_t m, int64_t n, int32_t swiglu, int32_t* bm_main, int32_t* split,
+                       int32_t* bm_tail);
+
 /* Message for the calling thread's last error ("" if none). */
 const char* tp_last_error(void);
 

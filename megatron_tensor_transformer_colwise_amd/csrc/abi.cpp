@@ -145,6 +145,18 @@ extern "C" {
 
 const char* tp_last_error(void) { return g_err; }
 
+tp_status tp_gemm_plan(int64_t m, int64_t n, int32_t swiglu, int32_t* bm_main, int32_t* split,
+                       int32_t* bm_tail) {
+  if (m <= 0 || n <= 0) return fail(TP_ERR_SHAPE, "m and n must be positive");
+  if (!bm_main || !split || !bm_tail) return fail(TP_ERR_INVALID_ARG, "NULL output pointer");
+  int a, b, c;
+  tpk::gemm_plan(m, n, swiglu != 0, &a, &b, &c);
+  *bm_main = a;
+  *split = b;
+  *bm_tail = c;
+  return ok();
+}
+
 tp_status tp_device_check(void) {
   TRY(device_check());
   return ok();

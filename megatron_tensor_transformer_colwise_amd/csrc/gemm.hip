@@ -9,59 +9,67 @@
 // Both operands are contiguous along k (X row-major, W in nn.Linear layout), so
 // every MFMA operand of a lane is 16 contiguous bytes of one row.
 //
-// Tiling: 256 x 256 output tile per workgroup of 8 waves (two per SIMD), each
-// wave a 64 x 128 sub-tile of 2 x 4 v_mfma_f32_32x32x16_bf16 blocks (128
-// float32 accumulators per lane).  k advances BK at a time through an NSTAGE-deep LDS
-// ring; tiles are fetched with 16-byte buffer loads that write LDS directly (no
-// register staging), NSTAGE - 1 k-steps ahead of the MFMAs.  Out-of-range rows
-// and the k tail are fetched as zeros by the buffer's range check.  Each LDS
-// row holds BK bf16; its 16-byte chunks are XOR-permuted by swz(row) so the 32
-// rows one fragment read touches spread over all banks.
+// Tiling: BMT x 256 output tiles, BMT in {256, 192, 128}, worked by BMT / 32
+// waves laid out (BMT / 64) x 2; every wave owns a 64 x 128 sub-tile of 2 x 4
+// v_mfma_f32_32x32x16_bf16 blocks (128 float32 accumulators per lane).  With
+// 8 waves two share each SIMD, so one issues MFMAs while the other waits on
+// memory or the barrier.  k advances 64 at a time through a two-stage LDS
+// ring; tiles are fetched with 16-byte buffer loads that write LDS directly
+// (no register staging), all of a stage's loads issued together one k-step
+// ahead.  Out-of-range rows and the k tail are fetched as zeros by the
+// buffer's range check.  Each LDS row holds 64 bf16; its eight 16-byte chunks
+// are XOR-permuted by swz(row) so the 32 rows one fragment read touches hit
+// distinct banks (measured: no bank conflicts).
+//
+// The host picks the tile height per launch, and may split the tile columns
+// into a main range and a tail range of lower height, to minimise
+// rounds-of-256-workgroups x (BMT + 256): the loads of a tile scale with
+// BMT + 256 and the kernel is close to its load bound, while a partly filled
+// last round costs a whole round.
 #include "common.h"
 #include "kernels.h"
 
 namespace tpk {
 namespace {
 
-constexpr int BM = 256;
-constexpr int BN = 256;
-#ifndef TP_GEMM_NW
-#define TP_GEMM_NW 8
-#endif
-constexpr int GEMM_NW = TP_GEMM_NW;             // waves per workgroup (4 or 8)
-#ifndef TP_GEMM_BK
-#define TP_GEMM_BK 64
-#endif
-#ifndef TP_GEMM_NSTAGE
-#define TP_GEMM_NSTAGE 2
-#endif
-constexpr int BK = TP_GEMM_BK;                  // k per stage (32 or 64)
-constexpr int NSTAGE = TP_GEMM_NSTAGE;          // LDS ring depth
+constexpr int BN = 256;                         // tile columns (weight rows)
+constexpr int BK = 64;                          // k per stage
+constexpr int NSTAGE = 2;                       // LDS ring depth
 constexpr int CH = BK / 8;                      // 16-byte chunks per tile row
 constexpr int ROWB = BK * 2;                    // bytes per tile row
 constexpr int KSUB = BK / 16;                   // MFMA k-steps per stage
-constexpr int LPT = CH;                         // loads per thread per operand per stage
-constexpr int TILE_BYTES = 256 * ROWB;          // one operand, one stage
-constexpr int STAGE_BYTES = 2 * TILE_BYTES;     // A then B
-constexpr int SMEM_BYTES = NSTAGE * STAGE_BYTES;
-static_assert(BK == 32 || BK == 64, "BK");
-static_assert(SMEM_BYTES <= 160 * 1024, "LDS");
+constexpr int MI = 2;                           // 32-row MFMA blocks per wave
+constexpr int WROWS = 32 * MI;                  // rows per wave
+constexpr int B_TILE = BN * ROWB;               // one stage of weight rows
+constexpr int B_INSTR = BN * CH / 64;           // wave-instructions per B stage
+
+template <int BMT>
+struct Cfg {
+  static constexpr int NW = BMT / 32;                         // waves
+  static constexpr int A_TILE = BMT * ROWB;
+  static constexpr int STAGE = A_TILE + B_TILE;
+  static constexpr int SMEM = NSTAGE * STAGE;
+  static constexpr int A_INSTR = BMT * CH / 64;               // wave-instructions per A stage
+  static constexpr int LA = (A_INSTR + NW - 1) / NW;          // per wave, A
+  static constexpr int LB = (B_INSTR + NW - 1) / NW;          // per wave, B
+  static_assert(SMEM <= 160 * 1024, "LDS");
+};
 
 struct Args {
   const bf16_t* x;
   const bf16_t* w;
   void* out;
   int64_t M, N, K;
-  int num_bm, num_bn;
+  int num_bm;  // tile rows of this launch (height BMT)
+  int num_bn;  // tile columns of this launch
+  int bn0;     // first tile column of this launch
   QkvOut qkv;
 };
 
 // Chunk permutation of tile row r.  Reads of one fragment touch 32 consecutive
 // rows at one logical chunk; the permutation makes every 8-row group (128-byte
 // bank window) and every 16-row group (256-byte window) hit distinct banks.
-__device__ __forceinline__ int swz(int r) {
-  return BK == 64 ? ((r ^ (r >> 3)) & 7) : (((r >> 1) ^ (r >> 3)) & 3);
-}
+__device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
 
 // Launch index -> output tile.  Workgroups are dealt to the 8 XCDs round-robin;
 // first undo that so each XCD owns a contiguous range of logical tiles, then
@@ -83,30 +91,25 @@ __device__ __forceinline__ void tile_coords(int id, int nb, int num_bm, int num_
   bn = inner / gs;
 }
 
-// NW waves per workgroup laid out (NW / 2) x 2 over the 256 x 256 tile: each
-// wave owns 512/NW rows x 128 columns, i.e. MI = 16/NW row blocks of 32 and
-// 4 column blocks.  With NW = 8 two waves share each SIMD, so one can issue
-// MFMAs while the other waits on memory or the barrier.
-template <int EPI, int NW>
-__global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(Args args) {
-  constexpr int MI = 16 / NW;              // 32-row MFMA blocks per wave
-  constexpr int WROWS = 32 * MI;           // rows per wave
-  constexpr int LPW = LPT * 4 / NW;        // loads per thread per operand per stage
-  __shared__ __attribute__((aligned(1024))) char smem[SMEM_BYTES];
+template <int EPI, int BMT>
+__global__ __launch_bounds__(BMT * 2, 1) void gemm_bf16_kernel(Args args) {
+  using C = Cfg<BMT>;
+  constexpr int NW = C::NW;
+  __shared__ __attribute__((aligned(1024))) char smem[C::SMEM];
 
   const int lane = lane_id();
   const int wave = wave_id();
   int bm, bn;
   tile_coords(blockIdx.x, gridDim.x, args.num_bm, args.num_bn, bm, bn);
+  bn += args.bn0;
 
   const int64_t M = args.M, N = args.N, K = args.K;
-  const int64_t m0 = (int64_t)bm * BM;
+  const int64_t m0 = (int64_t)bm * BMT;
   const uint32_t row_bytes = (uint32_t)(K * 2);
 
   // ---- global -> LDS addressing -------------------------------------------
-  const int m_rows = (int)min<int64_t>(BM, M - m0);
-  __amdgpu_buffer_rsrc_t rsrc_a =
-      make_rsrc(args.x + m0 * K, (uint32_t)m_rows * row_bytes);
+  const int m_rows = (int)min<int64_t>(BMT, M - m0);
+  __amdgpu_buffer_rsrc_t rsrc_a = make_rsrc(args.x + m0 * K, (uint32_t)m_rows * row_bytes);
 
   __amdgpu_buffer_rsrc_t rsrc_b;
   int n_valid;  // valid weight rows (plain) or valid output columns (SwiGLU)
@@ -120,17 +123,25 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(Args args) {
     rsrc_b = make_rsrc(args.w + n0 * K, (uint32_t)n_valid * row_bytes);
   }
 
-  // Slot s = (j * NW + wave) * 64 + lane of a stage holds tile row s / CH,
-  // physical chunk s % CH, i.e. logical chunk (s % CH) ^ swz(row).
-  uint32_t a_off[LPW], b_off[LPW];
-  int a_k[LPW];  // element offset of the chunk within the k-block
+  // Wave-instruction blk of a stage fills slots blk * 64 + lane: tile row
+  // slot / CH, physical chunk slot % CH, i.e. logical chunk (slot % CH) ^
+  // swz(row).  Wave w issues blocks j * NW + w.
+  uint32_t a_off[C::LA], b_off[C::LB];
+  int a_k[C::LA], b_k[C::LB];  // element offset of the chunk within the k-block
 #pragma unroll
-  for (int j = 0; j < LPW; ++j) {
+  for (int j = 0; j < C::LA; ++j) {
     const int slot = (j * NW + wave) * 64 + lane;
     const int r = slot / CH;
     const int c = (slot % CH) ^ swz(r);
     a_k[j] = c * 8;
     a_off[j] = (uint32_t)r * row_bytes + (uint32_t)c * 16;
+  }
+#pragma unroll
+  for (int j = 0; j < C::LB; ++j) {
+    const int slot = (j * NW + wave) * 64 + lane;
+    const int r = slot / CH;
+    const int c = (slot % CH) ^ swz(r);
+    b_k[j] = c * 8;
     if (EPI == EPI_SWIGLU) {
       const int wn = r >> 7, qq = r & 127;
       const int o_rel = wn * 64 + (qq & 63);
@@ -141,13 +152,25 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(Args args) {
     }
   }
 
-  // load j (0 .. LPW-1) of both operands of the stage at k0
-  auto load_one = [&](char* stage, int j, int64_t k0) {
+  // all loads of one stage at k0 (blocks past the tile are skipped wave-uniformly)
+  auto load_stage = [&](char* stage, int64_t k0) {
     const uint32_t kb = (uint32_t)(k0 * 2);
-    const bool kin = (k0 + a_k[j]) < K;
-    buffer_load_lds16(rsrc_a, stage + (j * NW + wave) * 1024, kin ? a_off[j] + kb : TP_OOB_OFFSET);
-    buffer_load_lds16(rsrc_b, stage + TILE_BYTES + (j * NW + wave) * 1024,
-                      (kin && b_off[j] != TP_OOB_OFFSET) ? b_off[j] + kb : TP_OOB_OFFSET);
+#pragma unroll
+    for (int j = 0; j < C::LA; ++j) {
+      const int blk = j * NW + wave;
+      if (C::A_INSTR % NW == 0 || blk < C::A_INSTR) {
+        const bool kin = (k0 + a_k[j]) < K;
+        buffer_load_lds16(rsrc_a, stage + blk * 1024, kin ? a_off[j] + kb : TP_OOB_OFFSET);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < C::LB; ++j) {
+      const int blk = j * NW + wave;
+      if (B_INSTR % NW == 0 || blk < B_INSTR) {
+        const bool kin = (k0 + b_k[j]) < K && b_off[j] != TP_OOB_OFFSET;
+        buffer_load_lds16(rsrc_b, stage + C::A_TILE + blk * 1024, kin ? b_off[j] + kb : TP_OOB_OFFSET);
+      }
+    }
   };
 
   // ---- LDS -> registers addressing ----------------------------------------
@@ -169,7 +192,7 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(Args args) {
 #pragma unroll
     for (int s = 0; s < KSUB; ++s) {
       const int c = 2 * s + hk;
-      rb[j][s] = (uint32_t)(r_b * ROWB + ((c ^ swz(r_b)) << 4));
+      rb[j][s] = (uint32_t)(C::A_TILE + r_b * ROWB + ((c ^ swz(r_b)) << 4));
     }
   }
 
@@ -179,42 +202,36 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(Args args) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
 
-  // Fragments are double-buffered in registers: while the 16 MFMAs of k-step
-  // s run, the 8 fragment reads of step s + 1 are in flight, so LDS latency
-  // does not stall the matrix pipe inside a stage.
+  // Fragments are double-buffered in registers: while the MFMAs of k-step s
+  // run, the fragment reads of step s + 1 are in flight, so LDS latency does
+  // not stall the matrix pipe inside a stage.
   u32x4 fa[2][MI], fb[2][4];
   const int nk = (int)((K + BK - 1) / BK);
-#pragma unroll
-  for (int st = 0; st < NSTAGE - 1; ++st)
-#pragma unroll
-    for (int j = 0; j < LPW; ++j) load_one(smem + st * STAGE_BYTES, j, (int64_t)st * BK);
+  load_stage(smem, 0);
   for (int kt = 0; kt < nk; ++kt) {
-    // this wave's loads of stage kt have landed once at most the later
-    // NSTAGE - 2 stages' loads are outstanding; the barrier extends that to
-    // every wave, and retires all reads of the buffer about to be refilled
-    wait_vmcnt<2 * LPW * (NSTAGE - 2)>();
+    // this wave's loads of stage kt have landed; the barrier extends that to
+    // every wave and retires all reads of the buffer about to be refilled
+    wait_vmcnt0();
     __syncthreads();
-    const char* sa = smem + (kt % NSTAGE) * STAGE_BYTES;
-    const char* sb = sa + TILE_BYTES;
-    char* nstage = smem + ((kt + NSTAGE - 1) % NSTAGE) * STAGE_BYTES;
-    const int64_t kn = (int64_t)(kt + NSTAGE - 1) * BK;  // beyond K at the end: loads read zeros
+    const char* st = smem + (kt & 1) * C::STAGE;
+    char* nst = smem + ((kt + 1) & 1) * C::STAGE;
 #pragma unroll
-    for (int i = 0; i < MI; ++i) fa[0][i] = lds_read16(sa + ra[i][0]);
+    for (int i = 0; i < MI; ++i) fa[0][i] = lds_read16(st + ra[i][0]);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) fb[0][j] = lds_read16(sb + rb[j][0]);
-    // every load of the stage NSTAGE - 1 ahead goes out at once: the vector
-    // memory path sustains its throughput only with many requests in flight
-#pragma unroll
-    for (int j = 0; j < LPW; ++j) load_one(nstage, j, kn);
+    for (int j = 0; j < 4; ++j) fb[0][j] = lds_read16(st + rb[j][0]);
+    // every load of the next stage goes out at once: the vector memory path
+    // sustains its throughput only with many requests in flight.  Beyond K
+    // on the last step the loads read zeros into the idle buffer.
+    load_stage(nst, (int64_t)(kt + 1) * BK);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int s = 0; s < KSUB; ++s) {
       const int cur = s & 1, nxt = cur ^ 1;
       if (s + 1 < KSUB) {
 #pragma unroll
-        for (int i = 0; i < MI; ++i) fa[nxt][i] = lds_read16(sa + ra[i][s + 1]);
+        for (int i = 0; i < MI; ++i) fa[nxt][i] = lds_read16(st + ra[i][s + 1]);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) fb[nxt][j] = lds_read16(sb + rb[j][s + 1]);
+        for (int j = 0; j < 4; ++j) fb[nxt][j] = lds_read16(st + rb[j][s + 1]);
       }
 #pragma unroll
       for (int i = 0; i < MI; ++i)
@@ -365,6 +382,81 @@ __global__ void vt_pad_zero_kernel(bf16_t* vt, int64_t rows, int64_t seq, int64_
 
 }  // namespace
 
+// ---- launch planning --------------------------------------------------------
+
+namespace {
+
+struct Plan {
+  int bm_main, split, bm_tail;  // columns [0, split) at bm_main, [split, nbn) at bm_tail
+};
+
+int64_t rounds_of(int64_t tiles) { return (tiles + 255) / 256; }
+
+// Cost of a launch ~ rounds of 256 workgroups x (BMT + 256): close to the
+// load bound, a tile's time scales with the rows it streams.
+int64_t cost(int64_t M, int64_t cols, int bmt) {
+  if (cols <= 0) return 0;
+  const int64_t tiles = ((M + bmt - 1) / bmt) * cols;
+  return rounds_of(tiles) * (bmt + 256);
+}
+
+Plan plan_for(int64_t M, int64_t nbn) {
+  static const int H[3] = {256, 192, 128};
+  Plan best{256, (int)nbn, 256};
+  int64_t best_cost = cost(M, nbn, 256);
+  for (int hm : H) {
+    const int64_t one = cost(M, nbn, hm);
+    if (one < best_cost) {
+      best_cost = one;
+      best = Plan{hm, (int)nbn, hm};
+    }
+    for (int64_t split = 1; split < nbn; ++split)
+      for (int ht : H) {
+        if (ht >= hm) continue;  // a tail only at a lower height
+        const int64_t c = cost(M, split, hm) + cost(M, nbn - split, ht);
+        if (c < best_cost) {
+          best_cost = c;
+          best = Plan{hm, (int)split, ht};
+        }
+      }
+  }
+  return best;
+}
+
+template <int EPI, int BMT>
+void launch_part(Args a, int bn0, int cols, hipStream_t s) {
+  a.bn0 = bn0;
+  a.num_bn = cols;
+  a.num_bm = (int)((a.M + BMT - 1) / BMT);
+  const int nb = a.num_bm * cols;
+  if (nb == 0) return;
+  hipLaunchKernelGGL((gemm_bf16_kernel<EPI, BMT>), dim3(nb), dim3(BMT * 2), 0, s, a);
+}
+
+template <int EPI>
+void launch_planned(const Args& a, int64_t nbn, hipStream_t s) {
+  const Plan p = plan_for(a.M, nbn);
+  auto part = [&](int bmt, int bn0, int cols) {
+    switch (bmt) {
+      case 256: launch_part<EPI, 256>(a, bn0, cols, s); break;
+      case 192: launch_part<EPI, 192>(a, bn0, cols, s); break;
+      default: launch_part<EPI, 128>(a, bn0, cols, s); break;
+    }
+  };
+  part(p.bm_main, 0, p.split);
+  if (p.split < nbn) part(p.bm_tail, p.split, (int)(nbn - p.split));
+}
+
+}  // namespace
+
+void gemm_plan(int64_t M, int64_t N, int swiglu, int* bm_main, int* split, int* bm_tail) {
+  const int64_t nbn = (N + (swiglu ? BN / 2 : BN) - 1) / (swiglu ? BN / 2 : BN);
+  const Plan p = plan_for(M, nbn);
+  *bm_main = p.bm_main;
+  *split = p.split;
+  *bm_tail = p.bm_tail;
+}
+
 hipError_t launch_gemm_bf16(int epi, int64_t M, int64_t N, int64_t K, const void* x, const void* w,
                             void* out, const QkvOut* qkv, hipStream_t s) {
   Args a;
@@ -374,19 +466,16 @@ hipError_t launch_gemm_bf16(int epi, int64_t M, int64_t N, int64_t K, const void
   a.M = M;
   a.N = N;
   a.K = K;
-  const int64_t bn_cols = (epi == EPI_SWIGLU) ? BN / 2 : BN;
-  a.num_bm = (int)((M + BM - 1) / BM);
-  a.num_bn = (int)((N + bn_cols - 1) / bn_cols);
+  a.num_bm = a.num_bn = a.bn0 = 0;
   if (qkv) a.qkv = *qkv; else a.qkv = QkvOut{};
-  const int nb = a.num_bm * a.num_bn;
-  if (nb == 0) return hipSuccess;
-  constexpr int NW = GEMM_NW;
-  dim3 grid(nb), block(NW * 64);
+  const int64_t bn_cols = (epi == EPI_SWIGLU) ? BN / 2 : BN;
+  const int64_t nbn = (N + bn_cols - 1) / bn_cols;
+  if (M == 0 || nbn == 0) return hipSuccess;
   switch (epi) {
-    case EPI_F32: hipLaunchKernelGGL((gemm_bf16_kernel<EPI_F32, NW>), grid, block, 0, s, a); break;
-    case EPI_BF16: hipLaunchKernelGGL((gemm_bf16_kernel<EPI_BF16, NW>), grid, block, 0, s, a); break;
-    case EPI_GELU: hipLaunchKernelGGL((gemm_bf16_kernel<EPI_GELU, NW>), grid, block, 0, s, a); break;
-    case EPI_SWIGLU: hipLaunchKernelGGL((gemm_bf16_kernel<EPI_SWIGLU, NW>), grid, block, 0, s, a); break;
+    case EPI_F32: launch_planned<EPI_F32>(a, nbn, s); break;
+    case EPI_BF16: launch_planned<EPI_BF16>(a, nbn, s); break;
+    case EPI_GELU: launch_planned<EPI_GELU>(a, nbn, s); break;
+    case EPI_SWIGLU: launch_planned<EPI_SWIGLU>(a, nbn, s); break;
     case EPI_QKV: {
       if (a.qkv.seq_pad > a.qkv.seq) {
         const int64_t rows = (M / a.qkv.seq) * a.qkv.hkv * 128;
@@ -395,7 +484,7 @@ hipError_t launch_gemm_bf16(int epi, int64_t M, int64_t N, int64_t K, const void
         hipLaunchKernelGGL(vt_pad_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
                            reinterpret_cast<bf16_t*>(a.qkv.vt), rows, a.qkv.seq, a.qkv.seq_pad);
       }
-      hipLaunchKernelGGL((gemm_bf16_kernel<EPI_QKV, NW>), grid, block, 0, s, a);
+      launch_planned<EPI_QKV>(a, nbn, s);
       break;
     }
     default: return hipErrorInvalidValue;

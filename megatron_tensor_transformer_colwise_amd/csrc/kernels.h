@@ -30,6 +30,10 @@ struct QkvOut {
 hipError_t launch_gemm_bf16(int epi, int64_t M, int64_t N, int64_t K, const void* x, const void* w,
                             void* out, const QkvOut* qkv, hipStream_t s);
 
+// Tile heights the bf16 GEMM launches for an M x N output (N = output
+// columns): columns [0, split) at height bm_main, the rest at bm_tail.
+void gemm_plan(int64_t M, int64_t N, int swiglu, int* bm_main, int* split, int* bm_tail);
+
 // Same contraction in float32 throughout (EPI_F32 / EPI_BF16 meaning "no
 // nonlinearity, float32 out", EPI_GELU, EPI_SWIGLU).
 hipError_t launch_gemm_f32(int epi, int64_t M, int64_t N, int64_t K, const float* x, const float* w,

@@ -52,6 +52,7 @@ _SIGS = {
                       ctypes.c_size_t, _vp, _vp],
     "tp_shard_sum": [_i32, _i64, ctypes.POINTER(_vp), _vp, _i32, _vp, _vp],
     "tp_rmsnorm": [_i32, _i64, _i64, _vp, _vp, _f32, _vp, _vp],
+    "tp_gemm_plan": [_i64, _i64, _i32, ctypes.POINTER(_i32), ctypes.POINTER(_i32), ctypes.POINTER(_i32)],
     "tp_last_error": [],
     "tp_device_check": [],
 }
@@ -109,6 +110,13 @@ def _check(status: int) -> None:
 
 def tp_last_error() -> str:
     return lib().tp_last_error().decode()
+
+
+def tp_gemm_plan(m, n, swiglu=False) -> tuple[int, int, int]:
+    """(bm_main, split, bm_tail) of the bf16 GEMM for an m x n output."""
+    a, b, c = _i32(), _i32(), _i32()
+    _check(lib().tp_gemm_plan(m, n, int(bool(swiglu)), ctypes.byref(a), ctypes.byref(b), ctypes.byref(c)))
+    return a.value, b.value, c.value
 
 
 def tp_device_check() -> None:

@@ -118,6 +118,18 @@ def test_rmsnorm_validation(L):
     assert status("tp_rmsnorm", 1, 4, 16, A16, MIS, 1e-5, A16, None) == tp.TP_ERR_INVALID_ARG
 
 
+def test_gemm_plans(L):
+    """Tile-height plans of the workload shapes (host-only call)."""
+    assert tp.tp_gemm_plan(8192, 3584, True) == (256, 24, 128)    # SwiGLU, 70B t=8: tail at 128
+    assert tp.tp_gemm_plan(8192, 8192) == (256, 32, 256)          # down proj / o_proj
+    assert tp.tp_gemm_plan(8192, 1280) == (192, 5, 192)           # QKV, 70B t=8
+    assert tp.tp_gemm_plan(8192, 768) == (128, 3, 128)            # QKV, 70B t=16
+    assert tp.tp_gemm_plan(4096, 3584, True) == (256, 28, 256)    # SwiGLU, Llama-8B
+    assert tp.tp_gemm_plan(2048, 1024) == (128, 4, 128)           # GPT MLP
+    with pytest.raises(tp.TpError):
+        tp.tp_gemm_plan(0, 16)
+
+
 def test_binding_raises_with_message(L):
     with pytest.raises(tp.TpError) as e:
         tp.tp_colwise("gelu", "bf16", 4, 12, 16, A16, A16, A16, stream=0)

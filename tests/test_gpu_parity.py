@@ -97,6 +97,24 @@ def test_rowwise_gemm_integer_bit_exact(device, m, k, n):
     assert np.array_equal(host(out), ref)
 
 
+@pytest.mark.parametrize("m,k,n,plan", [
+    (4096, 64, 4096, (256, 16, 256)),     # 256-row tiles
+    (8192, 72, 1280, (192, 5, 192)),      # 192-row tiles, k tail of 8
+    (8192, 64, 7168, (256, 24, 128)),     # main range at 256, tail columns at 128
+    (1000, 136, 776, (128, 4, 128)),      # 128-row tiles, ragged m and n
+])
+def test_rowwise_gemm_plans_bit_exact(device, m, k, n, plan):
+    """Every tile height and the split launch, bit-exact on integer inputs."""
+    say(f"case rowwise plan m={m} k={k} n={n} plan={plan}")
+    assert tp.tp_gemm_plan(m, n) == plan
+    y = inputs.integers(9, 0, (m, k), -2, 2)
+    w = inputs.integers(9, 1, (n, k), -2, 2)
+    out = torch.empty(m, n, dtype=torch.float32, device=device)
+    tp.tp_rowwise("bf16", m, k, n, to_dev(y, device), to_dev(w, device), out)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(out), y.f64() @ w.f64().T)
+
+
 @pytest.mark.parametrize("m,k,n", [(300, 40, 264), (64, 48, 512)])
 def test_colwise_none_integer_bit_exact(device, m, k, n):
     """Plain colwise projection, integers small enough (|sum| <= 2*2*48 < 256)
