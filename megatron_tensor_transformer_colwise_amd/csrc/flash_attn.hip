@@ -13,8 +13,10 @@
 // product is O^T = V^T P^T: P^T is the B operand straight from the score
 // registers (after rounding to bf16 and one v_permlane32_swap that makes each
 // lane's 8 keys contiguous), and V^T is read from LDS as rows of the
-// transposed-V layout the projection writes.  Exponentials are exp2 with the
-// 1/sqrt(d) * log2(e) scale folded in; accumulation is float32.
+// transposed-V layout the projection writes.  Exponentials are exp2 of one
+// FMA (the 1/sqrt(d) * log2(e) scale folded in); the running max moves, and
+// O is rescaled, only when a score exceeds it by more than 2^8; accumulation
+// is float32.
 #include "common.h"
 #include "kernels.h"
 
@@ -28,6 +30,7 @@ constexpr int NT = 256;
 constexpr int K_TILE = BKV * D * 2;            // [64 keys][128 d], 256-byte rows
 constexpr int V_TILE = D * BKV * 2;            // [128 d][64 keys], 128-byte rows
 constexpr int STAGE = K_TILE + V_TILE;
+constexpr float TAU = 8.0f;                    // lazy-rescale threshold, log2 units
 
 struct FaArgs {
   const bf16_t* q;
@@ -128,7 +131,7 @@ __global__ __launch_bounds__(NT, 2) void flash_attn_kernel(FaArgs a) {
   f32x16 oacc[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db) oacc[db] = f32x16{};
-  float m_run = -INFINITY, l_run = 0.0f;
+  float m_use = -INFINITY, l_run = 0.0f;
 
   const int64_t last_q = min<int64_t>((int64_t)q0 + BQ - 1, seq - 1);
   const int n_kv = a.causal ? (int)(last_q / BKV) + 1 : (int)((seq + BKV - 1) / BKV);
@@ -141,52 +144,85 @@ __global__ __launch_bounds__(NT, 2) void flash_attn_kernel(FaArgs a) {
     const char* sk = smem + (t & 1) * STAGE;
     const char* sv = sk + K_TILE;
 
-    // S^T for 64 keys: two 32 x 32 blocks
+    // S^T for 64 keys: two 32 x 32 blocks.  All K fragments are read before
+    // the first MFMA, and all V^T fragments right after the last one, so LDS
+    // latency hides under the score MFMAs and under the softmax.
+    u32x4 kf[2][8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) kf[kb][s] = lds_read16(sk + kr[kb][s]);
+    __builtin_amdgcn_sched_barrier(0);
     f32x16 sacc[2] = {f32x16{}, f32x16{}};
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) sacc[kb] = mfma32x32x16(lds_read16(sk + kr[kb][s]), qf[s], sacc[kb]);
+      for (int kb = 0; kb < 2; ++kb) sacc[kb] = mfma32x32x16(kf[kb][s], qf[s], sacc[kb]);
     }
+    u32x4 vf[4][4];  // [key step u][d block]
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int db = 0; db < 4; ++db) vf[u][db] = lds_read16(sv + vr[db][u]);
+    __builtin_amdgcn_sched_barrier(0);
 
-    // scale, mask, running max
+    // mask, then the running max in raw score units.  The max used for the
+    // exponentials (m_use) only moves when some score exceeds it by more than
+    // 2^TAU after scaling; until then probabilities may reach 2^TAU, which
+    // float32 sums and bf16 P hold exactly enough, and O / l are rescaled only
+    // on the tiles where the max actually moves.
     const int key0 = t * BKV;
     const bool need_mask = (a.causal && key0 + BKV - 1 > q0) || (key0 + BKV > seq);
-    float mt = -INFINITY;
+    if (need_mask) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float v = sacc[kb][r] * a.scale_log2;
-        if (need_mask) {
+        for (int r = 0; r < 16; ++r) {
           const int key = key0 + kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-          if (key >= seq || (a.causal && key > qpos)) v = -INFINITY;
+          if (key >= seq || (a.causal && key > qpos)) sacc[kb][r] = -INFINITY;
         }
-        sacc[kb][r] = v;
-        mt = fmaxf(mt, v);
-      }
-    mt = fmaxf(mt, other_half(mt));
-    const float m_new = fmaxf(m_run, mt);
-    const float alpha = exp2f(m_run - m_new);
-    m_run = m_new;
+    }
+    // pairwise (tree) max: depth 5 instead of a 32-long dependency chain
+    float mx[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx[r] = fmaxf(sacc[0][r], sacc[1][r]);
+#pragma unroll
+    for (int w = 8; w >= 1; w >>= 1)
+#pragma unroll
+      for (int r = 0; r < w; ++r) mx[r] = fmaxf(mx[r], mx[r + w]);
+    const float mt = fmaxf(mx[0], other_half(mx[0]));
+    const bool grow = (mt - m_use) * a.scale_log2 > TAU;  // also true on the first tile
+    if (__builtin_amdgcn_ballot_w64(grow)) {
+      const float m_new = grow ? mt : m_use;
+      const float alpha = exp2f((m_use - m_new) * a.scale_log2);
+      m_use = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+    }
+    // (a lane whose keys are all masked so far keeps p = 0: exp2(-inf))
+    const float mc = m_use == -INFINITY ? 0.0f : -m_use * a.scale_log2;
 
-    // probabilities, rounded to bf16 in pairs of consecutive keys
+    // probabilities exp2(s * c - m * c), rounded to bf16 in pairs of keys
     uint32_t pk[2][8];
-    float psum = 0.0f;
+    float ps[16];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; r += 2) {
-        const float p0 = exp2f(sacc[kb][r] - m_new);
-        const float p1 = exp2f(sacc[kb][r + 1] - m_new);
-        psum += p0 + p1;
+        const float p0 = exp2f(fmaf(sacc[kb][r], a.scale_log2, mc));
+        const float p1 = exp2f(fmaf(sacc[kb][r + 1], a.scale_log2, mc));
+        ps[kb * 8 + (r >> 1)] = p0 + p1;
         pk[kb][r >> 1] = pack_bf16x2(p0, p1);
       }
-    l_run = l_run * alpha + psum;
+    // pairwise (tree) sum
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+    for (int w = 8; w >= 1; w >>= 1)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+      for (int r = 0; r < w; ++r) ps[r] += ps[r + w];
+    l_run += ps[0];
 
     // O^T += V^T P^T over four 16-key steps
 #pragma unroll
@@ -199,7 +235,7 @@ __global__ __launch_bounds__(NT, 2) void flash_attn_kernel(FaArgs a) {
       // lanes 0-31 now hold keys 16u+0..7, lanes 32-63 keys 16u+8..15
       const u32x4 pb = {s0[0], s1[0], s0[1], s1[1]};
 #pragma unroll
-      for (int db = 0; db < 4; ++db) oacc[db] = mfma32x32x16(lds_read16(sv + vr[db][u]), pb, oacc[db]);
+      for (int db = 0; db < 4; ++db) oacc[db] = mfma32x32x16(vf[u][db], pb, oacc[db]);
     }
   }
 
