@@ -114,6 +114,97 @@ def cpu_baseline(case, w_host, budget_s: float = 20.0) -> dict:
     }
 
 
+def _time(fn, reps=10, warm=2):
+    """Median milliseconds of fn over reps, each bracketed by events."""
+    import statistics
+
+    import torch
+
+    for _ in range(warm):
+        fn()
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        b.synchronize()
+        ts.append(a.elapsed_time(b))
+    return statistics.median(ts)
+
+
+def per_config_report(dev):
+    """Per-call time and rate of every workload (one rank's call unless noted)."""
+    from megatron_tensor_transformer_colwise_amd import inputs, shard
+
+    def emit(rec):
+        print(json.dumps(rec), flush=True)
+
+    def sum_rate(mod, t, n, res_bytes):
+        ms = _time(lambda: mod.reduce(residual=None))
+        return ms, (t + 1) * 4 * n / ms / 1e6
+
+    # GPT-style GeLU MLP and Llama-8B SwiGLU MLP
+    for name in ("gpt_gelu_mlp", "llama8b_swiglu_mlp"):
+        case = inputs.CONFIGS[name]
+        log(f"configs: {name}")
+        dw = {k: v.torch().to(dev) for k, v in inputs.gen_mlp(case).items()}
+        mlp = shard.MLPShards(dw["X"], dw, case.t, case.act)
+        fl = 2.0 * case.tokens * case.hidden * case.f_shard * (3 if case.act == "swiglu" else 2)
+        ms = _time(lambda: mlp.rank(0))
+        rec = {"workload": name, "call": "tp_shard_mlp (one rank)", "ms": round(ms, 4),
+               "tflops": round(fl / ms / 1e9, 1), "pct_mfma_peak": round(fl / ms / 1e9 / 25, 2)}
+        msg = _time(lambda: mlp.all_ranks_grouped())
+        rec["grouped_all_ranks_ms"] = round(msg, 4)
+        rec["grouped_tflops"] = round(case.t * fl / msg / 1e9, 1)
+        sms, gbs = sum_rate(mlp, case.t, case.tokens * case.hidden, 0)
+        rec.update({"shard_sum_ms": round(sms, 4), "shard_sum_gbs": round(gbs, 1)})
+        emit(rec)
+        del mlp, dw
+
+    # Llama-8B attention
+    case = inputs.CONFIGS["llama8b_attn"]
+    log("configs: llama8b_attn")
+    dw = {k: v.torch().to(dev) for k, v in inputs.gen_attn(case).items()}
+    at = shard.AttnShards(dw["X"], dw, case)
+    rk = at.ranks[0]
+    fl = block_flops(inputs.BlockCase("a", case.batch, case.seq, case.hidden, case.heads, case.kv_heads,
+                                      case.head_dim, case.hidden, case.t, case.rope_base, 0), case.t)
+    afl = fl["qkv"] + fl["attn_core"] + fl["o_proj"]
+    ms = _time(lambda: at.rank(0))
+    sms, gbs = sum_rate(at, case.t, case.tokens * case.hidden, 0)
+    emit({"workload": "llama8b_attn", "call": "tp_shard_attn (one rank)", "ms": round(ms, 4),
+          "tflops": round(afl / ms / 1e9, 1), "pct_mfma_peak": round(afl / ms / 1e9 / 25, 2),
+          "shard_sum_ms": round(sms, 4), "shard_sum_gbs": round(gbs, 1)})
+    del at, dw
+
+    # 70B block at t = 8 and t = 16
+    for name in ("llama70b_block_t8", "llama70b_block_t16"):
+        case = inputs.CONFIGS[name]
+        log(f"configs: {name}")
+        dw = {k: v.torch().to(dev) for k, v in inputs.gen_block(case).items()}
+        blk = shard.BlockShards(dw["X"], dw, case)
+        fl = block_flops(case, case.t)
+        afl = fl["qkv"] + fl["attn_core"] + fl["o_proj"]
+        mfl = fl["swiglu_gemm"] + fl["down_gemm"]
+        blk.norm_attn()
+        blk.norm_mlp()
+        ams = _time(lambda: blk.attn.rank(0))
+        mms = _time(lambda: blk.mlp.rank(0))
+        sms = _time(lambda: blk.mlp.reduce(residual=blk.attn.out, residual_dt="f32"))
+        step = _time(lambda: blk.forward(), reps=5)
+        emit({"workload": name, "attn_call_ms": round(ams, 4), "attn_tflops": round(afl / ams / 1e9, 1),
+              "mlp_call_ms": round(mms, 4), "mlp_tflops": round(mfl / mms / 1e9, 1),
+              "shard_aggregate_tflops": round((afl + mfl) / (ams + mms) / 1e9, 1),
+              "shard_sum_ms": round(sms, 4),
+              "shard_sum_gbs": round((case.t + 2) * 4 * case.tokens * case.hidden / sms / 1e6, 1),
+              "block_step_ms": round(step, 3),
+              "block_step_tflops": round(case.t * (afl + mfl) / step / 1e9, 1)})
+        del blk, dw
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -122,6 +213,8 @@ def main():
     ap.add_argument("--config", default="llama70b_block_t8")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--configs", action="store_true",
+                    help="per-call report for every workload (one JSON line each) instead of the step")
     ap.add_argument("--pmc-pass", action="store_true",
                     help="launch only a 256 MiB copy and the SwiGLU GEMM (for counter runs)")
     args = ap.parse_args()
@@ -142,6 +235,10 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     tp.tp_device_check()
+
+    if args.configs:
+        per_config_report(dev)
+        return
 
     case = inputs.CONFIGS[args.config]
     t = case.t

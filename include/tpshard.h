@@ -119,6 +119,23 @@ tp_status tp_shard_mlp(tp_act act, tp_dtype dt, int64_t m, int64_t h, int64_t f_
                        void* act_ws, float* partial, void* stream);
 
 /* --------------------------------------------------------------------------
+ * All t ranks' MLP shards of one layer in one pair of launches (the rank is
+ * the second grid dimension), for shapes whose per-rank GEMMs are too small
+ * to fill the device.  A one-device helper: on a real tensor-parallel group
+ * every rank calls tp_shard_mlp on its own GPU.  Results are bitwise equal
+ * to t calls of tp_shard_mlp with the same operands.
+ *
+ *   t                  1 .. 16
+ *   x                  [m, h], shared by every rank
+ *   w_in, w_out,       HOST arrays of t device pointers, each as in
+ *   act_ws, partial    tp_shard_mlp for rank i
+ * ------------------------------------------------------------------------ */
+tp_status tp_shard_mlp_group(tp_act act, tp_dtype dt, int32_t t, int64_t m, int64_t h,
+                             int64_t f_shard, const void* x, const void* const* w_in,
+                             const void* const* w_out, void* const* act_ws,
+                             float* const* partial, void* stream);
+
+/* --------------------------------------------------------------------------
  * Column-parallel Q/K/V projection of one rank with rotary embedding
  * ("Self-attention" section), bf16 only.
  *

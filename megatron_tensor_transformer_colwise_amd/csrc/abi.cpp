@@ -150,7 +150,7 @@ tp_status tp_gemm_plan(int64_t m, int64_t n, int32_t swiglu, int32_t* bm_main, i
   if (m <= 0 || n <= 0) return fail(TP_ERR_SHAPE, "m and n must be positive");
   if (!bm_main || !split || !bm_tail) return fail(TP_ERR_INVALID_ARG, "NULL output pointer");
   int a, b, c;
-  tpk::gemm_plan(m, n, swiglu != 0, &a, &b, &c);
+  tpk::gemm_plan(m, n, swiglu != 0, 1, &a, &b, &c);
   *bm_main = a;
   *split = b;
   *bm_tail = c;
@@ -199,6 +199,38 @@ tp_status tp_shard_mlp(tp_act act, tp_dtype dt, int64_t m, int64_t h, int64_t f_
   TRY(check_gemm(TP_ACT_NONE, dt, m, f_shard, h, act_ws, w_out, partial, "act_ws", "w_out", "partial"));
   TRY(tp_colwise(act, dt, m, h, f_shard, x, w_in, act_ws, stream));
   return tp_rowwise(dt, m, f_shard, h, act_ws, w_out, partial, stream);
+}
+
+tp_status tp_shard_mlp_group(tp_act act, tp_dtype dt, int32_t t, int64_t m, int64_t h,
+                             int64_t f_shard, const void* x, const void* const* w_in,
+                             const void* const* w_out, void* const* act_ws,
+                             float* const* partial, void* stream) {
+  if (act != TP_ACT_GELU && act != TP_ACT_SWIGLU)
+    return fail(TP_ERR_INVALID_ARG, "tp_shard_mlp_group needs GELU or SWIGLU, got %d", (int)act);
+  if (t < 1 || t > TP_MAX_SHARDS) return fail(TP_ERR_SHAPE, "t = %d outside 1..%d", t, TP_MAX_SHARDS);
+  if (m > 0 && (!w_in || !w_out || !act_ws || !partial))
+    return fail(TP_ERR_INVALID_ARG, "a pointer array is NULL");
+  for (int i = 0; i < t && m > 0; ++i) {
+    TRY(check_gemm(act, dt, m, h, f_shard, x, w_in[i], act_ws[i], "x", "w_in[i]", "act_ws[i]"));
+    TRY(check_gemm(TP_ACT_NONE, dt, m, f_shard, h, act_ws[i], w_out[i], partial[i], "act_ws[i]",
+                   "w_out[i]", "partial[i]"));
+  }
+  TRY(check_gemm(act, dt, m, h, f_shard, x, x, x, "x", "x", "x"));
+  if (m == 0) return ok();
+  if (dt == TP_F32) {
+    for (int i = 0; i < t; ++i)
+      TRY(tp_shard_mlp(act, dt, m, h, f_shard, x, w_in[i], w_out[i], act_ws[i], partial[i], stream));
+    return ok();
+  }
+  TRY(device_check());
+  const void* xs[TP_MAX_SHARDS];
+  for (int i = 0; i < t; ++i) xs[i] = x;
+  hipError_t e = tpk::launch_gemm_bf16_group(epi_of(act), t, m, f_shard, h, xs, w_in, act_ws, nullptr,
+                                             as_stream(stream));
+  if (e != hipSuccess) return launched(e, "tp_shard_mlp_group");
+  e = tpk::launch_gemm_bf16_group(tpk::EPI_F32, t, m, h, f_shard, act_ws, w_out,
+                                  reinterpret_cast<void* const*>(partial), nullptr, as_stream(stream));
+  return launched(e, "tp_shard_mlp_group");
 }
 
 tp_status tp_qkv_rope(int64_t batch, int64_t seq, int64_t h, int32_t hq, int32_t hkv,

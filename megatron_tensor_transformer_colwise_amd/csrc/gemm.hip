@@ -55,10 +55,14 @@ struct Cfg {
   static_assert(SMEM <= 160 * 1024, "LDS");
 };
 
+constexpr int MAX_GROUP = 16;
+
+// Operands of one launch.  A launch may carry G independent GEMMs of equal
+// shape (one per tensor-parallel rank): blockIdx.y selects x[g], w[g], out[g].
 struct Args {
-  const bf16_t* x;
-  const bf16_t* w;
-  void* out;
+  const bf16_t* x[MAX_GROUP];
+  const bf16_t* w[MAX_GROUP];
+  void* out[MAX_GROUP];
   int64_t M, N, K;
   int num_bm;  // tile rows of this launch (height BMT)
   int num_bn;  // tile columns of this launch
@@ -99,6 +103,9 @@ __global__ __launch_bounds__(BMT * 2, 1) void gemm_bf16_kernel(Args args) {
 
   const int lane = lane_id();
   const int wave = wave_id();
+  const bf16_t* const xg = args.x[blockIdx.y];
+  const bf16_t* const wg = args.w[blockIdx.y];
+  void* const outg = args.out[blockIdx.y];
   int bm, bn;
   tile_coords(blockIdx.x, gridDim.x, args.num_bm, args.num_bn, bm, bn);
   bn += args.bn0;
@@ -109,18 +116,18 @@ __global__ __launch_bounds__(BMT * 2, 1) void gemm_bf16_kernel(Args args) {
 
   // ---- global -> LDS addressing -------------------------------------------
   const int m_rows = (int)min<int64_t>(BMT, M - m0);
-  __amdgpu_buffer_rsrc_t rsrc_a = make_rsrc(args.x + m0 * K, (uint32_t)m_rows * row_bytes);
+  __amdgpu_buffer_rsrc_t rsrc_a = make_rsrc(xg + m0 * K, (uint32_t)m_rows * row_bytes);
 
   __amdgpu_buffer_rsrc_t rsrc_b;
   int n_valid;  // valid weight rows (plain) or valid output columns (SwiGLU)
   if (EPI == EPI_SWIGLU) {
     const int64_t o0 = (int64_t)bn * (BN / 2);
     n_valid = (int)min<int64_t>(BN / 2, N - o0);
-    rsrc_b = make_rsrc(args.w + o0 * K, (uint32_t)((N + n_valid) * K * 2));
+    rsrc_b = make_rsrc(wg + o0 * K, (uint32_t)((N + n_valid) * K * 2));
   } else {
     const int64_t n0 = (int64_t)bn * BN;
     n_valid = (int)min<int64_t>(BN, N - n0);
-    rsrc_b = make_rsrc(args.w + n0 * K, (uint32_t)n_valid * row_bytes);
+    rsrc_b = make_rsrc(wg + n0 * K, (uint32_t)n_valid * row_bytes);
   }
 
   // Wave-instruction blk of a stage fills slots blk * 64 + lane: tile row
@@ -263,10 +270,10 @@ __global__ __launch_bounds__(BMT * 2, 1) void gemm_bf16_kernel(Args args) {
           if (row >= M) continue;
           float v = acc[i][j][r];
           if (EPI == EPI_F32) {
-            reinterpret_cast<float*>(args.out)[row * N + col] = v;
+            reinterpret_cast<float*>(outg)[row * N + col] = v;
           } else {
             if (EPI == EPI_GELU) v = gelu_erf(v);
-            reinterpret_cast<bf16_t*>(args.out)[row * N + col] = f32_to_bf16(v);
+            reinterpret_cast<bf16_t*>(outg)[row * N + col] = f32_to_bf16(v);
           }
         }
       }
@@ -283,7 +290,7 @@ __global__ __launch_bounds__(BMT * 2, 1) void gemm_bf16_kernel(Args args) {
           const int64_t row = row_base + i * 32 + 8 * (r >> 2) + (r & 3);
           if (row >= M) continue;
           const float g = acc[i][j][r], u = acc[i][j + 2][r];
-          reinterpret_cast<bf16_t*>(args.out)[row * N + col] = f32_to_bf16(silu(g) * u);
+          reinterpret_cast<bf16_t*>(outg)[row * N + col] = f32_to_bf16(silu(g) * u);
         }
       }
   } else {  // EPI_QKV: this wave's 128 columns are exactly one head
@@ -394,18 +401,18 @@ int64_t rounds_of(int64_t tiles) { return (tiles + 255) / 256; }
 
 // Cost of a launch ~ rounds of 256 workgroups x (BMT + 256): close to the
 // load bound, a tile's time scales with the rows it streams.
-int64_t cost(int64_t M, int64_t cols, int bmt) {
+int64_t cost(int64_t M, int64_t cols, int bmt, int groups) {
   if (cols <= 0) return 0;
-  const int64_t tiles = ((M + bmt - 1) / bmt) * cols;
+  const int64_t tiles = ((M + bmt - 1) / bmt) * cols * groups;
   return rounds_of(tiles) * (bmt + 256);
 }
 
-Plan plan_for(int64_t M, int64_t nbn) {
+Plan plan_for(int64_t M, int64_t nbn, int groups) {
   static const int H[3] = {256, 192, 128};
   Plan best{256, (int)nbn, 256};
-  int64_t best_cost = cost(M, nbn, 256);
+  int64_t best_cost = cost(M, nbn, 256, groups);
   for (int hm : H) {
-    const int64_t one = cost(M, nbn, hm);
+    const int64_t one = cost(M, nbn, hm, groups);
     if (one < best_cost) {
       best_cost = one;
       best = Plan{hm, (int)nbn, hm};
@@ -413,7 +420,7 @@ Plan plan_for(int64_t M, int64_t nbn) {
     for (int64_t split = 1; split < nbn; ++split)
       for (int ht : H) {
         if (ht >= hm) continue;  // a tail only at a lower height
-        const int64_t c = cost(M, split, hm) + cost(M, nbn - split, ht);
+        const int64_t c = cost(M, split, hm, groups) + cost(M, nbn - split, ht, groups);
         if (c < best_cost) {
           best_cost = c;
           best = Plan{hm, (int)split, ht};
@@ -424,23 +431,23 @@ Plan plan_for(int64_t M, int64_t nbn) {
 }
 
 template <int EPI, int BMT>
-void launch_part(Args a, int bn0, int cols, hipStream_t s) {
+void launch_part(Args a, int bn0, int cols, int groups, hipStream_t s) {
   a.bn0 = bn0;
   a.num_bn = cols;
   a.num_bm = (int)((a.M + BMT - 1) / BMT);
   const int nb = a.num_bm * cols;
   if (nb == 0) return;
-  hipLaunchKernelGGL((gemm_bf16_kernel<EPI, BMT>), dim3(nb), dim3(BMT * 2), 0, s, a);
+  hipLaunchKernelGGL((gemm_bf16_kernel<EPI, BMT>), dim3(nb, groups), dim3(BMT * 2), 0, s, a);
 }
 
 template <int EPI>
-void launch_planned(const Args& a, int64_t nbn, hipStream_t s) {
-  const Plan p = plan_for(a.M, nbn);
+void launch_planned(const Args& a, int64_t nbn, int groups, hipStream_t s) {
+  const Plan p = plan_for(a.M, nbn, groups);
   auto part = [&](int bmt, int bn0, int cols) {
     switch (bmt) {
-      case 256: launch_part<EPI, 256>(a, bn0, cols, s); break;
-      case 192: launch_part<EPI, 192>(a, bn0, cols, s); break;
-      default: launch_part<EPI, 128>(a, bn0, cols, s); break;
+      case 256: launch_part<EPI, 256>(a, bn0, cols, groups, s); break;
+      case 192: launch_part<EPI, 192>(a, bn0, cols, groups, s); break;
+      default: launch_part<EPI, 128>(a, bn0, cols, groups, s); break;
     }
   };
   part(p.bm_main, 0, p.split);
@@ -449,20 +456,26 @@ void launch_planned(const Args& a, int64_t nbn, hipStream_t s) {
 
 }  // namespace
 
-void gemm_plan(int64_t M, int64_t N, int swiglu, int* bm_main, int* split, int* bm_tail) {
+void gemm_plan(int64_t M, int64_t N, int swiglu, int groups, int* bm_main, int* split,
+               int* bm_tail) {
   const int64_t nbn = (N + (swiglu ? BN / 2 : BN) - 1) / (swiglu ? BN / 2 : BN);
-  const Plan p = plan_for(M, nbn);
+  const Plan p = plan_for(M, nbn, groups);
   *bm_main = p.bm_main;
   *split = p.split;
   *bm_tail = p.bm_tail;
 }
 
-hipError_t launch_gemm_bf16(int epi, int64_t M, int64_t N, int64_t K, const void* x, const void* w,
-                            void* out, const QkvOut* qkv, hipStream_t s) {
+hipError_t launch_gemm_bf16_group(int epi, int groups, int64_t M, int64_t N, int64_t K,
+                                  const void* const* x, const void* const* w, void* const* out,
+                                  const QkvOut* qkv, hipStream_t s) {
+  if (groups < 1 || groups > MAX_GROUP) return hipErrorInvalidValue;
   Args a;
-  a.x = reinterpret_cast<const bf16_t*>(x);
-  a.w = reinterpret_cast<const bf16_t*>(w);
-  a.out = out;
+  for (int g = 0; g < MAX_GROUP; ++g) {
+    const int src = g < groups ? g : 0;
+    a.x[g] = reinterpret_cast<const bf16_t*>(x[src]);
+    a.w[g] = reinterpret_cast<const bf16_t*>(w[src]);
+    a.out[g] = out[src];
+  }
   a.M = M;
   a.N = N;
   a.K = K;
@@ -472,11 +485,12 @@ hipError_t launch_gemm_bf16(int epi, int64_t M, int64_t N, int64_t K, const void
   const int64_t nbn = (N + bn_cols - 1) / bn_cols;
   if (M == 0 || nbn == 0) return hipSuccess;
   switch (epi) {
-    case EPI_F32: launch_planned<EPI_F32>(a, nbn, s); break;
-    case EPI_BF16: launch_planned<EPI_BF16>(a, nbn, s); break;
-    case EPI_GELU: launch_planned<EPI_GELU>(a, nbn, s); break;
-    case EPI_SWIGLU: launch_planned<EPI_SWIGLU>(a, nbn, s); break;
+    case EPI_F32: launch_planned<EPI_F32>(a, nbn, groups, s); break;
+    case EPI_BF16: launch_planned<EPI_BF16>(a, nbn, groups, s); break;
+    case EPI_GELU: launch_planned<EPI_GELU>(a, nbn, groups, s); break;
+    case EPI_SWIGLU: launch_planned<EPI_SWIGLU>(a, nbn, groups, s); break;
     case EPI_QKV: {
+      if (groups != 1) return hipErrorInvalidValue;
       if (a.qkv.seq_pad > a.qkv.seq) {
         const int64_t rows = (M / a.qkv.seq) * a.qkv.hkv * 128;
         const int64_t total = rows * (a.qkv.seq_pad - a.qkv.seq);
@@ -484,12 +498,20 @@ hipError_t launch_gemm_bf16(int epi, int64_t M, int64_t N, int64_t K, const void
         hipLaunchKernelGGL(vt_pad_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
                            reinterpret_cast<bf16_t*>(a.qkv.vt), rows, a.qkv.seq, a.qkv.seq_pad);
       }
-      launch_planned<EPI_QKV>(a, nbn, s);
+      launch_planned<EPI_QKV>(a, nbn, 1, s);
       break;
     }
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+hipError_t launch_gemm_bf16(int epi, int64_t M, int64_t N, int64_t K, const void* x, const void* w,
+                            void* out, const QkvOut* qkv, hipStream_t s) {
+  const void* xs[1] = {x};
+  const void* ws[1] = {w};
+  void* os[1] = {out};
+  return launch_gemm_bf16_group(epi, 1, M, N, K, xs, ws, os, qkv, s);
 }
 
 }  // namespace tpk

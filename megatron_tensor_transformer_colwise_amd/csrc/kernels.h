@@ -32,7 +32,14 @@ hipError_t launch_gemm_bf16(int epi, int64_t M, int64_t N, int64_t K, const void
 
 // Tile heights the bf16 GEMM launches for an M x N output (N = output
 // columns): columns [0, split) at height bm_main, the rest at bm_tail.
-void gemm_plan(int64_t M, int64_t N, int swiglu, int* bm_main, int* split, int* bm_tail);
+// groups: independent GEMMs of the same shape launched together.
+void gemm_plan(int64_t M, int64_t N, int swiglu, int groups, int* bm_main, int* split,
+               int* bm_tail);
+
+// G (<= 16) GEMMs of the same shape in one launch: out[g] = epi(x[g] . w[g]^T).
+hipError_t launch_gemm_bf16_group(int epi, int groups, int64_t M, int64_t N, int64_t K,
+                                  const void* const* x, const void* const* w, void* const* out,
+                                  const QkvOut* qkv, hipStream_t s);
 
 // Same contraction in float32 throughout (EPI_F32 / EPI_BF16 meaning "no
 // nonlinearity, float32 out", EPI_GELU, EPI_SWIGLU).

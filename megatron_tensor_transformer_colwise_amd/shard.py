@@ -111,6 +111,7 @@ class MLPShards:
         self.f_shard = self.w_out[0].shape[1]
         tdt = torch.float32 if dtype == "f32" else torch.bfloat16
         self.act_ws = torch.empty(self.m, self.f_shard, dtype=tdt, device=x.device)
+        self.group_ws = None
         self.partials = torch.empty(t, self.m, self.h, dtype=torch.float32, device=x.device)
         self.out = torch.empty(self.m, self.h, dtype=torch.float32, device=x.device)
 
@@ -126,12 +127,24 @@ class MLPShards:
         tp.tp_rowwise(self.dt, self.m, self.f_shard, self.h, self.act_ws, self.w_out[r],
                       self.partials[r], stream)
 
+    def all_ranks_grouped(self, x=None, stream=None) -> None:
+        """Every rank's MLP in one pair of launches (one workspace per rank)."""
+        if self.group_ws is None:
+            self.group_ws = torch.empty(self.t, self.m, self.f_shard, dtype=self.act_ws.dtype,
+                                        device=self.act_ws.device)
+        tp.tp_shard_mlp_group(self.act, self.dt, self.t, self.m, self.h, self.f_shard,
+                              self.x if x is None else x, self.w_in, self.w_out,
+                              list(self.group_ws), list(self.partials), stream)
+
     def reduce(self, residual=None, residual_dt="f32", stream=None) -> None:
         tp.tp_shard_sum(self.t, self.m * self.h, list(self.partials), residual, residual_dt, self.out, stream)
 
-    def forward(self, x=None, residual=None, residual_dt="f32", stream=None):
-        for r in range(self.t):
-            self.rank(r, x, stream)
+    def forward(self, x=None, residual=None, residual_dt="f32", stream=None, grouped=False):
+        if grouped:
+            self.all_ranks_grouped(x, stream)
+        else:
+            for r in range(self.t):
+                self.rank(r, x, stream)
         self.reduce(residual, residual_dt, stream)
         return self.out
 

@@ -45,6 +45,8 @@ _SIGS = {
     "tp_colwise": [_i32, _i32, _i64, _i64, _i64, _vp, _vp, _vp, _vp],
     "tp_rowwise": [_i32, _i64, _i64, _i64, _vp, _vp, _vp, _vp],
     "tp_shard_mlp": [_i32, _i32, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp],
+    "tp_shard_mlp_group": [_i32, _i32, _i32, _i64, _i64, _i64, _vp, ctypes.POINTER(_vp),
+                           ctypes.POINTER(_vp), ctypes.POINTER(_vp), ctypes.POINTER(_vp), _vp],
     "tp_qkv_rope": [_i64, _i64, _i64, _i32, _i32, _i32, _f32, _vp, _vp, _vp, _vp, _vp, _vp],
     "tp_flash_attn": [_i64, _i64, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp],
     "tp_shard_attn_workspace_bytes": [_i64, _i64, _i32, _i32, _i32],
@@ -134,6 +136,15 @@ def tp_rowwise(dt, m, k, n, y, w, partial, stream=None) -> None:
 def tp_shard_mlp(act, dt, m, h, f_shard, x, w_in, w_out, act_ws, partial, stream=None) -> None:
     _check(lib().tp_shard_mlp(_e(act, ACTS), _e(dt, DTYPES), m, h, f_shard, _p(x), _p(w_in),
                               _p(w_out), _p(act_ws), _p(partial), _s(stream)))
+
+
+def _arr(ptrs):
+    return (_vp * max(len(ptrs), 1))(*[_p(q) for q in ptrs])
+
+
+def tp_shard_mlp_group(act, dt, t, m, h, f_shard, x, w_in, w_out, act_ws, partial, stream=None) -> None:
+    _check(lib().tp_shard_mlp_group(_e(act, ACTS), _e(dt, DTYPES), t, m, h, f_shard, _p(x),
+                                    _arr(w_in), _arr(w_out), _arr(act_ws), _arr(partial), _s(stream)))
 
 
 def tp_qkv_rope(batch, seq, h, hq, hkv, head_dim, rope_base, x, w_qkv, q, k, vt, stream=None) -> None:

@@ -154,6 +154,33 @@ def test_mlp_small(device, act, m, h, inter, t):
     assert rel_err(host(out), full) <= BF16_TOL
 
 
+@pytest.mark.parametrize("act,dt,m,h,inter,t", [("gelu", "bf16", 2048, 1024, 4096, 4),
+                                                ("swiglu", "bf16", 300, 256, 1024, 8),
+                                                ("gelu", "f32", 4, 16, 64, 4)])
+def test_mlp_group_bitwise_equals_single_calls(device, act, dt, m, h, inter, t):
+    """tp_shard_mlp_group: every partial bitwise equal to the per-rank call."""
+    say(f"case mlp group {act} {dt} m={m} h={h} inter={inter} t={t}")
+    case = inputs.MLPCase("group", m, h, inter, t, act, dt, seed=23,
+                          draw="torch" if dt == "f32" else "counter", w_std=1.0 if dt == "f32" else 0.02)
+    w = inputs.gen_mlp(case)
+    dw = {k: to_dev(v, device) for k, v in w.items()}
+    mlp = shard.MLPShards(dw["X"], dw, t, act, dt)
+    single = []
+    for r in range(t):
+        mlp.rank(r)
+        single.append(mlp.partials[r].clone())
+    mlp.partials.zero_()
+    mlp.all_ranks_grouped()
+    torch.cuda.synchronize()
+    for r in range(t):
+        assert torch.equal(mlp.partials[r], single[r]), r
+    if act == "gelu" and dt == "bf16":
+        W = {k: v.f64() for k, v in w.items()}
+        parts = oracle.mlp_gelu_partials(W["X"], W["A"], W["B"], t)
+        for r in range(t):
+            assert rel_err(host(mlp.partials[r]), parts[r]) <= BF16_TOL
+
+
 def test_colwise_activation_slices(device):
     """The colwise output Y_i itself (bf16) against the oracle's activation."""
     say("case colwise slices")
