@@ -8,8 +8,12 @@ counter is scaled by bytes_known / counter_reading_of_the_copy.  Writes the
 per-launch traffic of the measured kernel, with the hash of the source it was
 taken on, to a JSON file that bench.py reports while the source is unchanged.
 
+A call of the measured entry point may be several dispatches (a main range
+and a tail range of tiles); every dispatch whose name contains
+KERNEL_SUBSTRING is summed and divided by CALLS.
+
 Usage: python -m megatron_tensor_transformer_colwise_amd.pmc_traffic \\
-           FETCH_DB WRITE_DB COPY_BYTES KERNEL_SUBSTRING SOURCE_FILE OUT_JSON
+           FETCH_DB WRITE_DB COPY_BYTES KERNEL_SUBSTRING CALLS SOURCE_FILE OUT_JSON
 """
 import hashlib
 import json
@@ -30,8 +34,9 @@ def source_hash(path: str) -> str:
     return hashlib.sha256(Path(path).read_bytes()).hexdigest()[:16]
 
 
-def main(fetch_db, write_db, copy_bytes, kernel_sub, source, out_json):
+def main(fetch_db, write_db, copy_bytes, kernel_sub, calls, source, out_json):
     copy_bytes = float(copy_bytes)
+    calls = int(calls)
     res = {}
     for counter, db in (("FETCH_SIZE", fetch_db), ("WRITE_SIZE", write_db)):
         d = per_dispatch(db, counter)
@@ -41,9 +46,10 @@ def main(fetch_db, write_db, copy_bytes, kernel_sub, source, out_json):
             raise SystemExit(f"{counter}: no copy or no '{kernel_sub}' dispatches in {db}")
         copy_kib = sorted(copy)[len(copy) // 2]
         scale = copy_bytes / (copy_kib * 1024.0)
-        kern_kib = sorted(kern)[len(kern) // 2]
-        res[counter] = {"copy_kib": copy_kib, "scale": scale, "kernel_kib": kern_kib,
-                        "kernel_bytes": kern_kib * 1024.0 * scale, "dispatches": len(kern)}
+        kern_kib = sum(kern) / calls
+        res[counter] = {"copy_kib": copy_kib, "scale": scale, "kernel_kib_per_call": kern_kib,
+                        "kernel_bytes": kern_kib * 1024.0 * scale, "dispatches": len(kern),
+                        "calls": calls}
     out = {
         "kernel": kernel_sub,
         "source": Path(source).name,
@@ -58,4 +64,4 @@ def main(fetch_db, write_db, copy_bytes, kernel_sub, source, out_json):
 
 
 if __name__ == "__main__":
-    main(*sys.argv[1:7])
+    main(*sys.argv[1:8])

@@ -43,7 +43,9 @@ def rel_err(got, ref):
     ref = np.asarray(ref, dtype=np.float64)
     assert got.shape == ref.shape, (got.shape, ref.shape)
     assert np.all(np.isfinite(got)), "non-finite GPU output"
-    return float(np.max(np.abs(got - ref)) / max(np.max(np.abs(ref)), 1e-30))
+    e = float(np.max(np.abs(got - ref)) / max(np.max(np.abs(ref)), 1e-30))
+    say(f"  max|gpu-oracle|/max|oracle| = {e:.3e}")
+    return e
 
 
 def to_dev(ht, dev):
@@ -75,6 +77,7 @@ def test_tiny_mlp_f32_worked_example(device):
     for r in range(case.t):
         assert np.max(np.abs(host(mlp.partials[r]) - parts[r])) <= F32_ATOL
     got = host(out)
+    say(f"  max|gpu-oracle| = {np.max(np.abs(got - ref)):.3e}")
     assert np.max(np.abs(got - ref)) <= F32_ATOL
     assert np.allclose(got, ref, atol=1e-4, rtol=1e-5)
 
