@@ -51,6 +51,14 @@ __device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t rsrc, v
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, LDS_PTR(lds_wave_base), 16, voffset, 0, 0, 0);
 }
 
+// Same, with a wave-uniform byte offset added from a scalar register.  Lanes
+// that must read zeros keep voffset itself out of range; for the others
+// voffset + soffset must stay inside the buffer.
+__device__ __forceinline__ void buffer_load_lds16_so(__amdgpu_buffer_rsrc_t rsrc, void* lds_wave_base,
+                                                     uint32_t voffset, uint32_t soffset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, LDS_PTR(lds_wave_base), 16, voffset, (int)soffset, 0, 0);
+}
+
 __device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voffset) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, voffset, 0, 0));
 }

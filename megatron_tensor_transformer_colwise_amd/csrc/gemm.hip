@@ -21,11 +21,20 @@
 // are XOR-permuted by swz(row) so the 32 rows one fragment read touches hit
 // distinct banks (measured: no bank conflicts).
 //
+// The inner loop carries almost no address arithmetic: LDS holds the two A
+// stages, then the two B stages, so a fragment's address is a fixed per-lane
+// register plus an immediate that selects the stage (the k loop is unrolled
+// by the two stages), and a global load's k advance is a scalar offset on a
+// fixed per-lane offset.  Only a partial last k-step takes the per-lane
+// k-range checks.
+//
 // The host picks the tile height per launch, and may split the tile columns
 // into a main range and a tail range of lower height, to minimise
 // rounds-of-256-workgroups x (BMT + 256): the loads of a tile scale with
 // BMT + 256 and the kernel is close to its load bound, while a partly filled
 // last round costs a whole round.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -47,8 +56,8 @@ template <int BMT>
 struct Cfg {
   static constexpr int NW = BMT / 32;                         // waves
   static constexpr int A_TILE = BMT * ROWB;
-  static constexpr int STAGE = A_TILE + B_TILE;
-  static constexpr int SMEM = NSTAGE * STAGE;
+  static constexpr int SMEM = NSTAGE * (A_TILE + B_TILE);  // A stages, then B stages
+  static constexpr int B_BASE = NSTAGE * A_TILE;
   static constexpr int A_INSTR = BMT * CH / 64;               // wave-instructions per A stage
   static constexpr int LA = (A_INSTR + NW - 1) / NW;          // per wave, A
   static constexpr int LB = (B_INSTR + NW - 1) / NW;          // per wave, B
@@ -159,23 +168,39 @@ __global__ __launch_bounds__(BMT * 2, 1) void gemm_bf16_kernel(Args args) {
     }
   }
 
-  // all loads of one stage at k0 (blocks past the tile are skipped wave-uniformly)
-  auto load_stage = [&](char* stage, int64_t k0) {
-    const uint32_t kb = (uint32_t)(k0 * 2);
+  // All loads of stage S for k-step kn (blocks past the tile are skipped
+  // wave-uniformly).  FULL: a whole k-step, whose k offset is a scalar added
+  // to fixed per-lane offsets.  Otherwise each chunk beyond K is sent out of
+  // the buffer, so it reads zeros.
+  auto load_stage = [&](auto stage_tag, auto full_tag, int kn) {
+    constexpr int S = decltype(stage_tag)::value;
+    constexpr bool FULL = decltype(full_tag)::value;
+    char* const a_dst = smem + S * C::A_TILE;
+    char* const b_dst = smem + C::B_BASE + S * B_TILE;
+    const uint32_t kb = (uint32_t)kn * (uint32_t)(BK * 2);
+    const int64_t k0 = (int64_t)kn * BK;
 #pragma unroll
     for (int j = 0; j < C::LA; ++j) {
       const int blk = j * NW + wave;
       if (C::A_INSTR % NW == 0 || blk < C::A_INSTR) {
-        const bool kin = (k0 + a_k[j]) < K;
-        buffer_load_lds16(rsrc_a, stage + blk * 1024, kin ? a_off[j] + kb : TP_OOB_OFFSET);
+        if (FULL) {
+          buffer_load_lds16_so(rsrc_a, a_dst + blk * 1024, a_off[j], kb);
+        } else {
+          const bool kin = (k0 + a_k[j]) < K;
+          buffer_load_lds16(rsrc_a, a_dst + blk * 1024, kin ? a_off[j] + kb : TP_OOB_OFFSET);
+        }
       }
     }
 #pragma unroll
     for (int j = 0; j < C::LB; ++j) {
       const int blk = j * NW + wave;
       if (B_INSTR % NW == 0 || blk < B_INSTR) {
-        const bool kin = (k0 + b_k[j]) < K && b_off[j] != TP_OOB_OFFSET;
-        buffer_load_lds16(rsrc_b, stage + C::A_TILE + blk * 1024, kin ? b_off[j] + kb : TP_OOB_OFFSET);
+        if (FULL) {
+          buffer_load_lds16_so(rsrc_b, b_dst + blk * 1024, b_off[j], kb);
+        } else {
+          const bool kin = (k0 + b_k[j]) < K && b_off[j] != TP_OOB_OFFSET;
+          buffer_load_lds16(rsrc_b, b_dst + blk * 1024, kin ? b_off[j] + kb : TP_OOB_OFFSET);
+        }
       }
     }
   };
@@ -199,7 +224,7 @@ __global__ __launch_bounds__(BMT * 2, 1) void gemm_bf16_kernel(Args args) {
 #pragma unroll
     for (int s = 0; s < KSUB; ++s) {
       const int c = 2 * s + hk;
-      rb[j][s] = (uint32_t)(C::A_TILE + r_b * ROWB + ((c ^ swz(r_b)) << 4));
+      rb[j][s] = (uint32_t)(C::B_BASE + r_b * ROWB + ((c ^ swz(r_b)) << 4));
     }
   }
 
@@ -214,31 +239,43 @@ __global__ __launch_bounds__(BMT * 2, 1) void gemm_bf16_kernel(Args args) {
   // not stall the matrix pipe inside a stage.
   u32x4 fa[2][MI], fb[2][4];
   const int nk = (int)((K + BK - 1) / BK);
-  load_stage(smem, 0);
-  for (int kt = 0; kt < nk; ++kt) {
+  const int nfull = (int)(K / BK);
+  using Full = std::true_type;
+  using Partial = std::false_type;
+  // One k-step on stage S.  MAIN: the next stage is a whole k-step.
+  // Otherwise the next stage may be partial, or absent after the last step.
+  auto kstep = [&](auto stage_tag, auto main_tag, int kt) {
+    constexpr int S = decltype(stage_tag)::value;
+    constexpr bool MAIN = decltype(main_tag)::value;
     // this wave's loads of stage kt have landed; the barrier extends that to
     // every wave and retires all reads of the buffer about to be refilled
     wait_vmcnt0();
     __syncthreads();
-    const char* st = smem + (kt & 1) * C::STAGE;
-    char* nst = smem + ((kt + 1) & 1) * C::STAGE;
+    const char* const a_st = smem + S * C::A_TILE;
+    const char* const b_st = smem + S * B_TILE;  // rb[][] holds the B base
 #pragma unroll
-    for (int i = 0; i < MI; ++i) fa[0][i] = lds_read16(st + ra[i][0]);
+    for (int i = 0; i < MI; ++i) fa[0][i] = lds_read16(a_st + ra[i][0]);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) fb[0][j] = lds_read16(st + rb[j][0]);
+    for (int j = 0; j < 4; ++j) fb[0][j] = lds_read16(b_st + rb[j][0]);
     // every load of the next stage goes out at once: the vector memory path
-    // sustains its throughput only with many requests in flight.  Beyond K
-    // on the last step the loads read zeros into the idle buffer.
-    load_stage(nst, (int64_t)(kt + 1) * BK);
+    // sustains its throughput only with many requests in flight
+    constexpr std::integral_constant<int, 1 - S> next{};
+    if (MAIN) {
+      load_stage(next, Full{}, kt + 1);
+    } else if (kt + 1 < nfull) {
+      load_stage(next, Full{}, kt + 1);
+    } else if (kt + 1 < nk) {
+      load_stage(next, Partial{}, kt + 1);
+    }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int s = 0; s < KSUB; ++s) {
       const int cur = s & 1, nxt = cur ^ 1;
       if (s + 1 < KSUB) {
 #pragma unroll
-        for (int i = 0; i < MI; ++i) fa[nxt][i] = lds_read16(st + ra[i][s + 1]);
+        for (int i = 0; i < MI; ++i) fa[nxt][i] = lds_read16(a_st + ra[i][s + 1]);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) fb[nxt][j] = lds_read16(st + rb[j][s + 1]);
+        for (int j = 0; j < 4; ++j) fb[nxt][j] = lds_read16(b_st + rb[j][s + 1]);
       }
 #pragma unroll
       for (int i = 0; i < MI; ++i)
@@ -248,6 +285,20 @@ __global__ __launch_bounds__(BMT * 2, 1) void gemm_bf16_kernel(Args args) {
       // into this step, so each step's reads overlap exactly one step of MFMAs
       __builtin_amdgcn_sched_barrier(0);
     }
+  };
+  constexpr std::integral_constant<int, 0> st0{};
+  constexpr std::integral_constant<int, 1> st1{};
+  if (nfull > 0) load_stage(st0, Full{}, 0);
+  else load_stage(st0, Partial{}, 0);
+  int kt = 0;
+  // pairs of steps whose next stages are both whole k-steps
+  for (; kt + 2 < nfull; kt += 2) {
+    kstep(st0, Full{}, kt);
+    kstep(st1, Full{}, kt + 1);
+  }
+  for (; kt < nk; kt += 2) {
+    kstep(st0, Partial{}, kt);
+    if (kt + 1 < nk) kstep(st1, Partial{}, kt + 1);
   }
   wait_vmcnt0();
 
