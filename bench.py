@@ -114,8 +114,9 @@ def cpu_baseline(case, w_host, budget_s: float = 20.0) -> dict:
     }
 
 
-def _time(fn, reps=10, warm=2):
-    """Median milliseconds of fn over reps, each bracketed by events."""
+def _time(fn, reps=20, warm=5, before=None):
+    """(median, min) milliseconds of fn over reps, each bracketed by events on
+    the current stream; before() (e.g. a cache flush) runs outside the bracket."""
     import statistics
 
     import torch
@@ -125,6 +126,8 @@ def _time(fn, reps=10, warm=2):
     torch.cuda.synchronize()
     ts = []
     for _ in range(reps):
+        if before is not None:
+            before()
         a = torch.cuda.Event(enable_timing=True)
         b = torch.cuda.Event(enable_timing=True)
         a.record()
@@ -132,19 +135,34 @@ def _time(fn, reps=10, warm=2):
         b.record()
         b.synchronize()
         ts.append(a.elapsed_time(b))
-    return statistics.median(ts)
+    return statistics.median(ts), min(ts)
 
 
 def per_config_report(dev):
-    """Per-call time and rate of every workload (one rank's call unless noted)."""
+    """Per-call time and rate of every workload (one rank's call unless noted):
+    median and minimum of 20 event-bracketed reps after 5 warm-ups.  Shard-sum
+    reps are preceded by a 512 MiB write so the 256 MiB Infinity Cache holds
+    none of their inputs."""
+    import torch
+
     from megatron_tensor_transformer_colwise_amd import inputs, shard
+
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+
+    def flush():
+        scratch.zero_()
 
     def emit(rec):
         print(json.dumps(rec), flush=True)
 
-    def sum_rate(mod, t, n, res_bytes):
-        ms = _time(lambda: mod.reduce(residual=None))
-        return ms, (t + 1) * 4 * n / ms / 1e6
+    def rate(fl, ms):
+        return round(fl / ms / 1e9, 1)
+
+    def sum_rec(fn, nbytes):
+        med, mn = _time(fn, before=flush)
+        return {"shard_sum_ms": round(med, 4), "shard_sum_min_ms": round(mn, 4),
+                "shard_sum_gbs": round(nbytes / med / 1e6, 1),
+                "shard_sum_pct_hbm": round(100.0 * nbytes / med / 1e6 / HBM_PEAK_GBS, 1)}
 
     # GPT-style GeLU MLP and Llama-8B SwiGLU MLP
     for name in ("gpt_gelu_mlp", "llama8b_swiglu_mlp"):
@@ -153,14 +171,15 @@ def per_config_report(dev):
         dw = {k: v.torch().to(dev) for k, v in inputs.gen_mlp(case).items()}
         mlp = shard.MLPShards(dw["X"], dw, case.t, case.act)
         fl = 2.0 * case.tokens * case.hidden * case.f_shard * (3 if case.act == "swiglu" else 2)
-        ms = _time(lambda: mlp.rank(0))
-        rec = {"workload": name, "call": "tp_shard_mlp (one rank)", "ms": round(ms, 4),
-               "tflops": round(fl / ms / 1e9, 1), "pct_mfma_peak": round(fl / ms / 1e9 / 25, 2)}
-        msg = _time(lambda: mlp.all_ranks_grouped())
-        rec["grouped_all_ranks_ms"] = round(msg, 4)
-        rec["grouped_tflops"] = round(case.t * fl / msg / 1e9, 1)
-        sms, gbs = sum_rate(mlp, case.t, case.tokens * case.hidden, 0)
-        rec.update({"shard_sum_ms": round(sms, 4), "shard_sum_gbs": round(gbs, 1)})
+        med, mn = _time(lambda: mlp.rank(0))
+        rec = {"workload": name, "call": "tp_shard_mlp (one rank)", "ms": round(med, 4),
+               "min_ms": round(mn, 4), "tflops": rate(fl, med),
+               "pct_mfma_peak": round(100.0 * fl / med / 1e9 / MFMA_BF16_PEAK_TFLOPS, 2)}
+        gmed, gmn = _time(lambda: mlp.all_ranks_grouped())
+        rec.update({"grouped_all_ranks_ms": round(gmed, 4), "grouped_min_ms": round(gmn, 4),
+                    "grouped_tflops": rate(case.t * fl, gmed)})
+        n = case.tokens * case.hidden
+        rec.update(sum_rec(lambda: mlp.reduce(residual=None), (case.t + 1) * 4 * n))
         emit(rec)
         del mlp, dw
 
@@ -169,15 +188,16 @@ def per_config_report(dev):
     log("configs: llama8b_attn")
     dw = {k: v.torch().to(dev) for k, v in inputs.gen_attn(case).items()}
     at = shard.AttnShards(dw["X"], dw, case)
-    rk = at.ranks[0]
     fl = block_flops(inputs.BlockCase("a", case.batch, case.seq, case.hidden, case.heads, case.kv_heads,
                                       case.head_dim, case.hidden, case.t, case.rope_base, 0), case.t)
     afl = fl["qkv"] + fl["attn_core"] + fl["o_proj"]
-    ms = _time(lambda: at.rank(0))
-    sms, gbs = sum_rate(at, case.t, case.tokens * case.hidden, 0)
-    emit({"workload": "llama8b_attn", "call": "tp_shard_attn (one rank)", "ms": round(ms, 4),
-          "tflops": round(afl / ms / 1e9, 1), "pct_mfma_peak": round(afl / ms / 1e9 / 25, 2),
-          "shard_sum_ms": round(sms, 4), "shard_sum_gbs": round(gbs, 1)})
+    med, mn = _time(lambda: at.rank(0))
+    rec = {"workload": "llama8b_attn", "call": "tp_shard_attn (one rank)", "ms": round(med, 4),
+           "min_ms": round(mn, 4), "tflops": rate(afl, med),
+           "pct_mfma_peak": round(100.0 * afl / med / 1e9 / MFMA_BF16_PEAK_TFLOPS, 2)}
+    n = case.tokens * case.hidden
+    rec.update(sum_rec(lambda: at.reduce(residual=None), (case.t + 1) * 4 * n))
+    emit(rec)
     del at, dw
 
     # 70B block at t = 8 and t = 16
@@ -191,18 +211,24 @@ def per_config_report(dev):
         mfl = fl["swiglu_gemm"] + fl["down_gemm"]
         blk.norm_attn()
         blk.norm_mlp()
-        ams = _time(lambda: blk.attn.rank(0))
-        mms = _time(lambda: blk.mlp.rank(0))
-        sms = _time(lambda: blk.mlp.reduce(residual=blk.attn.out, residual_dt="f32"))
-        step = _time(lambda: blk.forward(), reps=5)
-        emit({"workload": name, "attn_call_ms": round(ams, 4), "attn_tflops": round(afl / ams / 1e9, 1),
-              "mlp_call_ms": round(mms, 4), "mlp_tflops": round(mfl / mms / 1e9, 1),
-              "shard_aggregate_tflops": round((afl + mfl) / (ams + mms) / 1e9, 1),
-              "shard_sum_ms": round(sms, 4),
-              "shard_sum_gbs": round((case.t + 2) * 4 * case.tokens * case.hidden / sms / 1e6, 1),
-              "block_step_ms": round(step, 3),
-              "block_step_tflops": round(case.t * (afl + mfl) / step / 1e9, 1)})
+        ams, amn = _time(lambda: blk.attn.rank(0))
+        mms, mmn = _time(lambda: blk.mlp.rank(0))
+        n = case.tokens * case.hidden
+        srec = sum_rec(lambda: blk.mlp.reduce(residual=blk.attn.out, residual_dt="f32"),
+                       (case.t + 2) * 4 * n)
+        step, step_min = _time(lambda: blk.forward(), reps=5, warm=2)
+        rec = {"workload": name, "attn_call_ms": round(ams, 4), "attn_min_ms": round(amn, 4),
+               "attn_tflops": rate(afl, ams),
+               "attn_pct_mfma_peak": round(100.0 * afl / ams / 1e9 / MFMA_BF16_PEAK_TFLOPS, 2),
+               "mlp_call_ms": round(mms, 4), "mlp_min_ms": round(mmn, 4), "mlp_tflops": rate(mfl, mms),
+               "mlp_pct_mfma_peak": round(100.0 * mfl / mms / 1e9 / MFMA_BF16_PEAK_TFLOPS, 2),
+               "shard_aggregate_tflops": rate(afl + mfl, ams + mms)}
+        rec.update(srec)
+        rec.update({"block_step_ms": round(step, 3), "block_step_min_ms": round(step_min, 3),
+                    "block_step_tflops": rate(case.t * (afl + mfl), step)})
+        emit(rec)
         del blk, dw
+    del scratch
 
 
 def main():
