@@ -9,11 +9,13 @@
 // Both operands are contiguous along k (X row-major, W in nn.Linear layout), so
 // every MFMA operand of a lane is 16 contiguous bytes of one row.
 //
-// Tiling: BMT x 256 output tiles, BMT in {256, 192, 128}, worked by BMT / 32
-// waves laid out (BMT / 64) x 2; every wave owns a 64 x 128 sub-tile of 2 x 4
-// v_mfma_f32_32x32x16_bf16 blocks (128 float32 accumulators per lane).  With
-// 8 waves two share each SIMD, so one issues MFMAs while the other waits on
-// memory or the barrier.  k advances 64 at a time through a two-stage LDS
+// Tiling: BMT x 256 output tiles, BMT in {256, 192, 128}.  The waves are laid
+// out (rows) x 2 (column halves of 128); a wave owns MI x 4 blocks of
+// v_mfma_f32_32x32x16_bf16: 8 waves of 64 x 128 at BMT 256 (128 float32
+// accumulators per lane), 4 waves of 96 x 128 at 192, 8 waves of 32 x 128 at
+// 128.  The wave count is a multiple of the 4 SIMDs so they share the MFMA
+// work evenly; with two waves per SIMD one issues MFMAs while the other
+// waits on memory or the barrier.  k advances 64 at a time through a two-stage LDS
 // ring; tiles are fetched with 16-byte buffer loads that write LDS directly
 // (no register staging), all of a stage's loads issued together one k-step
 // ahead.  Out-of-range rows and the k tail are fetched as zeros by the
@@ -47,14 +49,22 @@ constexpr int NSTAGE = 2;                       // LDS ring depth
 constexpr int CH = BK / 8;                      // 16-byte chunks per tile row
 constexpr int ROWB = BK * 2;                    // bytes per tile row
 constexpr int KSUB = BK / 16;                   // MFMA k-steps per stage
-constexpr int MI = 2;                           // 32-row MFMA blocks per wave
-constexpr int WROWS = 32 * MI;                  // rows per wave
 constexpr int B_TILE = BN * ROWB;               // one stage of weight rows
 constexpr int B_INSTR = BN * CH / 64;           // wave-instructions per B stage
 
+// 32-row MFMA blocks per wave for a tile height.  The waves split the tile
+// rows evenly and the tile's two 128-column halves, and their count is a
+// multiple of the 4 SIMDs so every SIMD carries the same MFMA work:
+// 256 -> 8 waves of 64 rows, 192 -> 4 waves of 96, 128 -> 8 waves of 32
+// (two waves per SIMD where the registers allow it).
+constexpr int wave_blocks(int bmt) { return bmt == 256 ? 2 : bmt == 192 ? 3 : 1; }
+
 template <int BMT>
 struct Cfg {
-  static constexpr int NW = BMT / 32;                         // waves
+  static constexpr int MI = wave_blocks(BMT);                 // 32-row MFMA blocks per wave
+  static constexpr int WROWS = 32 * MI;                       // rows per wave
+  static constexpr int NW = BMT / WROWS * 2;                  // waves
+  static_assert(NW % 4 == 0 && BMT % WROWS == 0, "waves must cover the tile and the SIMDs");
   static constexpr int A_TILE = BMT * ROWB;
   static constexpr int SMEM = NSTAGE * (A_TILE + B_TILE);  // A stages, then B stages
   static constexpr int B_BASE = NSTAGE * A_TILE;
@@ -105,9 +115,11 @@ __device__ __forceinline__ void tile_coords(int id, int nb, int num_bm, int num_
 }
 
 template <int EPI, int BMT>
-__global__ __launch_bounds__(BMT * 2, 1) void gemm_bf16_kernel(Args args) {
+__global__ __launch_bounds__(Cfg<BMT>::NW * 64, 1) void gemm_bf16_kernel(Args args) {
   using C = Cfg<BMT>;
   constexpr int NW = C::NW;
+  constexpr int MI = C::MI;
+  constexpr int WROWS = C::WROWS;
   __shared__ __attribute__((aligned(1024))) char smem[C::SMEM];
 
   const int lane = lane_id();
@@ -488,7 +500,7 @@ void launch_part(Args a, int bn0, int cols, int groups, hipStream_t s) {
   a.num_bm = (int)((a.M + BMT - 1) / BMT);
   const int nb = a.num_bm * cols;
   if (nb == 0) return;
-  hipLaunchKernelGGL((gemm_bf16_kernel<EPI, BMT>), dim3(nb, groups), dim3(BMT * 2), 0, s, a);
+  hipLaunchKernelGGL((gemm_bf16_kernel<EPI, BMT>), dim3(nb, groups), dim3(Cfg<BMT>::NW * 64), 0, s, a);
 }
 
 template <int EPI>
