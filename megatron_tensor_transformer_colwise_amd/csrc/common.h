@@ -88,6 +88,30 @@ __device__ __forceinline__ f32x16 mfma32x32x16(u32x4 a, u32x4 b, f32x16 c) {
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+// Transpose of a 4 x 4 block held by a quad of lanes (q = lane & 3): on
+// entry a[e] is element (row e, column q); on exit a[c] is element (row q,
+// column c).  Two butterfly rounds over lane bit 0 and lane bit 1, each a
+// DPP quad permutation plus selects.
+__device__ __forceinline__ float quad_xor1(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float quad_xor2(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));
+}
+__device__ __forceinline__ void quad_transpose(float (&a)[4], int q) {
+  const bool b0 = (q & 1) != 0, b1 = (q & 2) != 0;
+#pragma unroll
+  for (int e = 0; e < 4; e += 2) {  // rows/columns differing in bit 0
+    const float r = quad_xor1(b0 ? a[e] : a[e + 1]);
+    if (b0) a[e] = r; else a[e + 1] = r;
+  }
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {  // rows/columns differing in bit 1
+    const float r = quad_xor2(b1 ? a[e] : a[e + 2]);
+    if (b1) a[e] = r; else a[e + 2] = r;
+  }
+}
+
 __device__ __forceinline__ float gelu_erf(float x) {
   return 0.5f * x * (1.0f + erff(x * 0.70710678118654752440f));
 }

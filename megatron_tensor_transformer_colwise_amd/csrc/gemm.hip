@@ -317,9 +317,18 @@ __global__ __launch_bounds__(Cfg<BMT>::NW * 64, 1) void gemm_bf16_kernel(Args ar
   // ---- epilogue -----------------------------------------------------------
   // Accumulator element r of block (i, j) in lane L is output row
   // 32 i + 8 (r / 4) + 4 (L / 32) + r % 4 and column 32 j + L % 32 of the
-  // wave's WROWS x 128 sub-tile.
+  // wave's WROWS x 128 sub-tile.  For bf16 outputs each group of 4
+  // consecutive rows is transposed across the 4 lanes of a quad, so a lane
+  // ends up with 4 consecutive columns of one row and writes them as one
+  // 8-byte store instead of four 2-byte ones.  The transposes run in every
+  // lane (they exchange data between lanes); only the stores are masked by
+  // the output bounds.  float32 partials are stored as they lie, one 4-byte
+  // store per element (measured: no slower than 16-byte stores after a
+  // transpose, which costs VALU time the tile holds its CU for).
   const int64_t row_base = m0 + wm * WROWS + 4 * hk;
-  if (EPI == EPI_F32 || EPI == EPI_BF16 || EPI == EPI_GELU) {
+  const int q = l31 & 3;             // row within a group after the transpose
+  const int cq = 4 * (l31 >> 2);     // first of the lane's 4 columns after it
+  if (EPI == EPI_F32) {
     const int64_t col_base = (int64_t)bn * BN + wn * 128 + l31;
 #pragma unroll
     for (int i = 0; i < MI; ++i)
@@ -330,30 +339,48 @@ __global__ __launch_bounds__(Cfg<BMT>::NW * 64, 1) void gemm_bf16_kernel(Args ar
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int64_t row = row_base + i * 32 + 8 * (r >> 2) + (r & 3);
-          if (row >= M) continue;
-          float v = acc[i][j][r];
-          if (EPI == EPI_F32) {
-            reinterpret_cast<float*>(outg)[row * N + col] = v;
-          } else {
-            if (EPI == EPI_GELU) v = gelu_erf(v);
-            reinterpret_cast<bf16_t*>(outg)[row * N + col] = f32_to_bf16(v);
+          if (row < M) reinterpret_cast<float*>(outg)[row * N + col] = acc[i][j][r];
+        }
+      }
+  } else if (EPI == EPI_BF16 || EPI == EPI_GELU) {
+    const int64_t col_base = (int64_t)bn * BN + wn * 128 + cq;
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int64_t col = col_base + j * 32;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          float v[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            v[e] = acc[i][j][4 * g + e];
+            if (EPI == EPI_GELU) v[e] = gelu_erf(v[e]);
           }
+          quad_transpose(v, q);
+          const int64_t row = row_base + i * 32 + 8 * g + q;
+          if (row < M && col < N)
+            *reinterpret_cast<u32x2*>(reinterpret_cast<bf16_t*>(outg) + row * N + col) =
+                u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
         }
       }
   } else if (EPI == EPI_SWIGLU) {
-    const int64_t col_base = (int64_t)bn * (BN / 2) + wn * 64 + l31;
+    const int64_t col_base = (int64_t)bn * (BN / 2) + wn * 64 + cq;
 #pragma unroll
     for (int i = 0; i < MI; ++i)
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const int64_t col = col_base + j * 32;
-        if (col >= N) continue;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int64_t row = row_base + i * 32 + 8 * (r >> 2) + (r & 3);
-          if (row >= M) continue;
-          const float g = acc[i][j][r], u = acc[i][j + 2][r];
-          reinterpret_cast<bf16_t*>(outg)[row * N + col] = f32_to_bf16(silu(g) * u);
+        for (int g = 0; g < 4; ++g) {
+          float v[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = silu(acc[i][j][4 * g + e]) * acc[i][j + 2][4 * g + e];
+          quad_transpose(v, q);
+          const int64_t row = row_base + i * 32 + 8 * g + q;
+          if (row < M && col < N)
+            *reinterpret_cast<u32x2*>(reinterpret_cast<bf16_t*>(outg) + row * N + col) =
+                u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
         }
       }
   } else {  // EPI_QKV: this wave's 128 columns are exactly one head
@@ -382,23 +409,29 @@ __global__ __launch_bounds__(Cfg<BMT>::NW * 64, 1) void gemm_bf16_kernel(Args ar
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
           const int64_t row0 = row_base + i * 32 + 8 * g4;
-          if (row0 >= M) continue;
           const uint32_t p0 = (uint32_t)row0 % seq;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int64_t row = row0 + e;
-            if (row >= M) continue;
-            uint32_t pos = p0 + e;
-            if (pos >= seq) pos -= seq;
+          for (int j = 0; j < 2; ++j) {
+            float y1[4], y2[4];
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-              const int c1 = j * 32 + l31;
+            for (int e = 0; e < 4; ++e) {
+              uint32_t pos = p0 + e;
+              if (pos >= seq) pos -= seq;
               const double turns = (double)pos * tpp[j];
               const float frac = (float)(turns - floor(turns));
               const float sn = __builtin_amdgcn_sinf(frac), cs = __builtin_amdgcn_cosf(frac);
               const float x1 = acc[i][j][4 * g4 + e], x2 = acc[i][j + 2][4 * g4 + e];
-              dst[row * ld + c1] = f32_to_bf16(x1 * cs - x2 * sn);
-              dst[row * ld + c1 + 64] = f32_to_bf16(x2 * cs + x1 * sn);
+              y1[e] = x1 * cs - x2 * sn;
+              y2[e] = x2 * cs + x1 * sn;
+            }
+            quad_transpose(y1, q);
+            quad_transpose(y2, q);
+            const int64_t row = row0 + q;
+            if (row < M) {
+              bf16_t* line = dst + row * ld + j * 32 + cq;
+              *reinterpret_cast<u32x2*>(line) = u32x2{pack_bf16x2(y1[0], y1[1]), pack_bf16x2(y1[2], y1[3])};
+              *reinterpret_cast<u32x2*>(line + 64) =
+                  u32x2{pack_bf16x2(y2[0], y2[1]), pack_bf16x2(y2[2], y2[3])};
             }
           }
         }
