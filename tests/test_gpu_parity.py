@@ -105,6 +105,8 @@ def test_rowwise_gemm_integer_bit_exact(device, m, k, n):
     (8192, 72, 1280, (192, 5, 192)),      # 192-row tiles, k tail of 8
     (8192, 64, 7168, (256, 24, 128)),     # main range at 256, tail columns at 128
     (1000, 136, 776, (128, 4, 128)),      # 128-row tiles, ragged m and n
+    (7777, 72, 1280, (192, 5, 192)),      # 192-row tiles (96-row waves), ragged m
+    (5000, 64, 3584, (192, 8, 128)),      # 192-row main range, 128-row tail, ragged m
 ])
 def test_rowwise_gemm_plans_bit_exact(device, m, k, n, plan):
     """Every tile height and the split launch, bit-exact on integer inputs."""
@@ -205,6 +207,23 @@ def test_colwise_activation_slices(device):
             assert rel_err(host(mlp.act_ws), ref) <= BF16_TOL
 
 
+@pytest.mark.parametrize("m,h,f,plan", [(3000, 64, 1536, (192, 12, 192)), (5000, 64, 1792, (192, 8, 128))])
+def test_swiglu_colwise_tile_heights(device, m, h, f, plan):
+    """SwiGLU epilogue (gate/up pairing, 4-column stores) at 192-row tiles and a
+    192/128 split, ragged m, against the oracle's activation."""
+    say(f"case swiglu colwise m={m} h={h} f={f} plan={plan}")
+    assert tp.tp_gemm_plan(m, f, True) == plan
+    case = inputs.MLPCase("heights", m, h, f, 1, "swiglu", "bf16", seed=24)
+    w = inputs.gen_mlp(case)
+    dw = {k: to_dev(v, device) for k, v in w.items()}
+    mlp = shard.MLPShards(dw["X"], dw, 1, "swiglu")
+    mlp.colwise(0)
+    torch.cuda.synchronize()
+    W = {k: v.f64() for k, v in w.items()}
+    ref = oracle.colwise_act(W["X"], None, "swiglu", (W["W1"], W["W3"]))
+    assert rel_err(host(mlp.act_ws), ref) <= BF16_TOL
+
+
 # ---------------------------------------------------------------- attention, small
 
 
@@ -214,6 +233,7 @@ def test_colwise_activation_slices(device):
     (2, 96, 256, 8, 2, 8, True),      # kv < t: each KV head replicated on 4 ranks
     (3, 64, 256, 4, 4, 1, True),      # MHA, one rank
     (1, 1, 128, 2, 1, 1, True),       # a single token
+    (5, 1400, 128, 8, 2, 1, True),    # Q/K/V projection on 192-row tiles, ragged m and seq
 ])
 def test_attention_small(device, batch, seq, h, heads, kv, t, causal):
     say(f"case attn b={batch} s={seq} h={h} heads={heads} kv={kv} t={t} causal={causal}")
