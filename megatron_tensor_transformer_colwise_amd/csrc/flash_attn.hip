@@ -13,10 +13,14 @@
 // product is O^T = V^T P^T: P^T is the B operand straight from the score
 // registers (after rounding to bf16 and one v_permlane32_swap that makes each
 // lane's 8 keys contiguous), and V^T is read from LDS as rows of the
-// transposed-V layout the projection writes.  Exponentials are exp2 of one
-// FMA (the 1/sqrt(d) * log2(e) scale folded in); the running max moves, and
+// transposed-V layout the projection writes.  Exponentials are the hardware
+// exp2 of one FMA (the 1/sqrt(d) * log2(e) scale folded in; probabilities
+// below 2^-126 may flush to zero, far below the bf16 P they feed and the
+// float32 sum they join); the running max moves, and
 // O is rescaled, only when a score exceeds it by more than 2^8; accumulation
 // is float32.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -99,8 +103,8 @@ __global__ __launch_bounds__(NT, 2) void flash_attn_kernel(FaArgs a) {
     const int d = s >> 3, cv = (s & 7) ^ swz_v(d);
     v_off[i] = (uint32_t)((int64_t)d * a.seq_pad * 2 + cv * 16);
   }
-  auto load_tile = [&](int stage, int t) {
-    char* sk = smem + stage * STAGE;
+  auto load_tile = [&](auto stage_tag, int t) {
+    char* sk = smem + decltype(stage_tag)::value * STAGE;
     char* sv = sk + K_TILE;
     const int kb = t * BKV;
 #pragma unroll
@@ -136,12 +140,16 @@ __global__ __launch_bounds__(NT, 2) void flash_attn_kernel(FaArgs a) {
   const int64_t last_q = min<int64_t>((int64_t)q0 + BQ - 1, seq - 1);
   const int n_kv = a.causal ? (int)(last_q / BKV) + 1 : (int)((seq + BKV - 1) / BKV);
 
-  load_tile(0, 0);
-  for (int t = 0; t < n_kv; ++t) {
+  constexpr std::integral_constant<int, 0> st0{};
+  constexpr std::integral_constant<int, 1> st1{};
+  // One key tile on LDS stage S (a compile-time constant, so fragment
+  // addresses are fixed registers plus an immediate).
+  auto kv_tile = [&](auto stage_tag, int t) {
+    constexpr int S = decltype(stage_tag)::value;
     wait_vmcnt0();
     __syncthreads();
-    if (t + 1 < n_kv) load_tile((t + 1) & 1, t + 1);
-    const char* sk = smem + (t & 1) * STAGE;
+    if (t + 1 < n_kv) load_tile(std::integral_constant<int, 1 - S>{}, t + 1);
+    const char* sk = smem + S * STAGE;
     const char* sv = sk + K_TILE;
 
     // S^T for 64 keys: two 32 x 32 blocks.  All K fragments are read before
@@ -174,12 +182,14 @@ __global__ __launch_bounds__(NT, 2) void flash_attn_kernel(FaArgs a) {
     const int key0 = t * BKV;
     const bool need_mask = (a.causal && key0 + BKV - 1 > q0) || (key0 + BKV > seq);
     if (need_mask) {
+      // keys beyond the sequence or after the query (seq < 2^31, checked by the caller)
+      const int key_lim = a.causal ? min(qpos, (int)seq - 1) : (int)seq - 1;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = key0 + kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-          if (key >= seq || (a.causal && key > qpos)) sacc[kb][r] = -INFINITY;
+          if (key > key_lim) sacc[kb][r] = -INFINITY;
         }
     }
     // pairwise (tree) max: depth 5 instead of a 32-long dependency chain
@@ -194,7 +204,7 @@ __global__ __launch_bounds__(NT, 2) void flash_attn_kernel(FaArgs a) {
     const bool grow = (mt - m_use) * a.scale_log2 > TAU;  // also true on the first tile
     if (__builtin_amdgcn_ballot_w64(grow)) {
       const float m_new = grow ? mt : m_use;
-      const float alpha = exp2f((m_use - m_new) * a.scale_log2);
+      const float alpha = __builtin_amdgcn_exp2f((m_use - m_new) * a.scale_log2);
       m_use = m_new;
       l_run *= alpha;
 #pragma unroll
@@ -212,8 +222,8 @@ __global__ __launch_bounds__(NT, 2) void flash_attn_kernel(FaArgs a) {
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; r += 2) {
-        const float p0 = exp2f(fmaf(sacc[kb][r], a.scale_log2, mc));
-        const float p1 = exp2f(fmaf(sacc[kb][r + 1], a.scale_log2, mc));
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r], a.scale_log2, mc));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r + 1], a.scale_log2, mc));
         ps[kb * 8 + (r >> 1)] = p0 + p1;
         pk[kb][r >> 1] = pack_bf16x2(p0, p1);
       }
@@ -237,6 +247,11 @@ __global__ __launch_bounds__(NT, 2) void flash_attn_kernel(FaArgs a) {
 #pragma unroll
       for (int db = 0; db < 4; ++db) oacc[db] = mfma32x32x16(vf[u][db], pb, oacc[db]);
     }
+  };
+  load_tile(st0, 0);
+  for (int t = 0; t < n_kv; t += 2) {
+    kv_tile(st0, t);
+    if (t + 1 < n_kv) kv_tile(st1, t + 1);
   }
 
   // ---- normalise and store: O^T block db, register r -> d = 32 db + 8 (r/4) + 4 h + r%4
