@@ -117,3 +117,8 @@ __device__ __forceinline__ float gelu_erf(float x) {
 }
 
 __device__ __forceinline__ float silu(float x) { return x / (1.0f + __expf(-x)); }
+// For bf16 outputs: the hardware reciprocal (about 1 ulp) instead of a
+// correctly rounded division.  x -> -inf gives -0, x -> +inf gives x.
+__device__ __forceinline__ float silu_fast(float x) {
+  return x * __builtin_amdgcn_rcpf(1.0f + __expf(-x));
+}

@@ -375,7 +375,7 @@ __global__ __launch_bounds__(Cfg<BMT>::NW * 64, 1) void gemm_bf16_kernel(Args ar
         for (int g = 0; g < 4; ++g) {
           float v[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = silu(acc[i][j][4 * g + e]) * acc[i][j + 2][4 * g + e];
+          for (int e = 0; e < 4; ++e) v[e] = silu_fast(acc[i][j][4 * g + e]) * acc[i][j + 2][4 * g + e];
           quad_transpose(v, q);
           const int64_t row = row_base + i * 32 + 8 * g + q;
           if (row < M && col < N)
@@ -399,30 +399,57 @@ __global__ __launch_bounds__(Cfg<BMT>::NW * 64, 1) void gemm_bf16_kernel(Args ar
       // angle = pos * base^(-2 c1 / 128) radians for the pair (c1, c1 + 64),
       // taken in turns (1 turn = 2 pi) in float64 so only the fraction of a
       // turn is rounded to float32; v_sin/v_cos take their argument in turns.
+      // The 4 rows of a group are consecutive positions: the first angle is
+      // evaluated that way and the next three follow by rotating it by one
+      // position's angle (angle addition), unless the group crosses into the
+      // next sequence.
       double tpp[2];
+      float c1p[2], s1p[2];  // cos / sin of one position's angle
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < 2; ++j) {
         tpp[j] = exp2(-(double)(2 * (j * 32 + l31)) * (1.0 / 128.0) * (double)o.log2_base) *
                  0.15915494309189533577;
+        const float fr = (float)(tpp[j] - floor(tpp[j]));
+        c1p[j] = __builtin_amdgcn_cosf(fr);
+        s1p[j] = __builtin_amdgcn_sinf(fr);
+      }
+      auto angle = [&](uint32_t pos, int j, float& cs, float& sn) {
+        const double turns = (double)pos * tpp[j];
+        const float frac = (float)(turns - floor(turns));
+        sn = __builtin_amdgcn_sinf(frac);
+        cs = __builtin_amdgcn_cosf(frac);
+      };
 #pragma unroll
       for (int i = 0; i < MI; ++i)
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
           const int64_t row0 = row_base + i * 32 + 8 * g4;
           const uint32_t p0 = (uint32_t)row0 % seq;
+          const bool run = p0 + 3 < seq;  // the group stays inside one sequence
 #pragma unroll
           for (int j = 0; j < 2; ++j) {
+            float cs[4], sn[4];
+            angle(p0, j, cs[0], sn[0]);
+            if (run) {
+#pragma unroll
+              for (int e = 1; e < 4; ++e) {
+                cs[e] = cs[e - 1] * c1p[j] - sn[e - 1] * s1p[j];
+                sn[e] = sn[e - 1] * c1p[j] + cs[e - 1] * s1p[j];
+              }
+            } else {
+#pragma unroll
+              for (int e = 1; e < 4; ++e) {
+                uint32_t pos = p0 + e;
+                if (pos >= seq) pos -= seq;
+                angle(pos, j, cs[e], sn[e]);
+              }
+            }
             float y1[4], y2[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              uint32_t pos = p0 + e;
-              if (pos >= seq) pos -= seq;
-              const double turns = (double)pos * tpp[j];
-              const float frac = (float)(turns - floor(turns));
-              const float sn = __builtin_amdgcn_sinf(frac), cs = __builtin_amdgcn_cosf(frac);
               const float x1 = acc[i][j][4 * g4 + e], x2 = acc[i][j + 2][4 * g4 + e];
-              y1[e] = x1 * cs - x2 * sn;
-              y2[e] = x2 * cs + x1 * sn;
+              y1[e] = x1 * cs[e] - x2 * sn[e];
+              y2[e] = x2 * cs[e] + x1 * sn[e];
             }
             quad_transpose(y1, q);
             quad_transpose(y2, q);

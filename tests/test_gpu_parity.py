@@ -229,6 +229,7 @@ def test_swiglu_colwise_tile_heights(device, m, h, f, plan):
 
 @pytest.mark.parametrize("batch,seq,h,heads,kv,t,causal", [
     (2, 200, 256, 8, 2, 2, True),     # ragged seq (not a multiple of 64 or 128)
+    (3, 203, 256, 8, 2, 2, True),     # seq not a multiple of 4: row groups straddle sequences
     (1, 128, 128, 4, 1, 4, True),     # one head per rank
     (2, 96, 256, 8, 2, 8, True),      # kv < t: each KV head replicated on 4 ranks
     (3, 64, 256, 4, 4, 1, True),      # MHA, one rank
