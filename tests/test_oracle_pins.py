@@ -159,6 +159,30 @@ def test_swiglu_mlp_split_identity_and_brute_force():
                 assert abs(parts[i][row, col] - acc) < 1e-12
 
 
+def test_colwise_activation_slices_brute_force():
+    """Y_i, the rank's colwise output: scalar loops for GeLU and SwiGLU, and the
+    rank slices side by side are the unsharded activation (column split)."""
+    r = _rng(13)
+    m, h, f, t = 3, 5, 8, 2
+    x = r.standard_normal((m, h))
+    a, w1, w3 = (r.standard_normal((h, f)) for _ in range(3))
+    fs = f // t
+    ya = [oracle.colwise_act(x, oracle.split_columns(a, t)[i], "gelu") for i in range(t)]
+    ys = [oracle.colwise_act(x, None, "swiglu", (oracle.split_columns(w1, t)[i],
+                                                 oracle.split_columns(w3, t)[i])) for i in range(t)]
+    for i in range(t):
+        for row in range(m):
+            for j in range(fs):
+                u = sum(x[row, k] * a[k, i * fs + j] for k in range(h))
+                assert abs(ya[i][row, j] - 0.5 * u * (1 + math.erf(u / math.sqrt(2)))) < 1e-12
+                g = sum(x[row, k] * w1[k, i * fs + j] for k in range(h))
+                v = sum(x[row, k] * w3[k, i * fs + j] for k in range(h))
+                assert abs(ys[i][row, j] - g / (1 + math.exp(-g)) * v) < 1e-12
+    assert np.max(np.abs(np.concatenate(ya, axis=1) - oracle.colwise_act(x, a, "gelu"))) < 1e-13
+    assert np.max(np.abs(np.concatenate(ys, axis=1)
+                         - oracle.colwise_act(x, None, "swiglu", (w1, w3)))) < 1e-13
+
+
 def test_shard_sum_orders_and_precision():
     r = _rng(3)
     ints = [r.integers(-1000, 1000, size=257).astype(np.float32) for _ in range(16)]
