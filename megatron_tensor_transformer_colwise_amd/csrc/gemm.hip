@@ -280,22 +280,23 @@ __global__ __launch_bounds__(Cfg<BMT>::NW * 64, 1) void gemm_bf16_kernel(Args ar
       load_stage(next, Partial{}, kt + 1);
     }
     __builtin_amdgcn_sched_barrier(0);
+    // Within a k-step s the fragment reads of step s + 1 are slotted one after
+    // each MFMA (fenced so the compiler keeps that order), so every read has
+    // the rest of the step's MFMAs to land (measured 1-5% faster than issuing
+    // them together).
+    constexpr int NQ = MI * 4 > MI + 4 ? MI * 4 : MI + 4;
 #pragma unroll
     for (int s = 0; s < KSUB; ++s) {
       const int cur = s & 1, nxt = cur ^ 1;
-      if (s + 1 < KSUB) {
 #pragma unroll
-        for (int i = 0; i < MI; ++i) fa[nxt][i] = lds_read16(a_st + ra[i][s + 1]);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) fb[nxt][j] = lds_read16(b_st + rb[j][s + 1]);
+      for (int q = 0; q < NQ; ++q) {
+        if (q < MI * 4) acc[q >> 2][q & 3] = mfma32x32x16(fa[cur][q >> 2], fb[cur][q & 3], acc[q >> 2][q & 3]);
+        if (s + 1 < KSUB) {
+          if (q < MI) fa[nxt][q] = lds_read16(a_st + ra[q][s + 1]);
+          else if (q < MI + 4) fb[nxt][q - MI] = lds_read16(b_st + rb[q - MI][s + 1]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
-#pragma unroll
-      for (int i = 0; i < MI; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = mfma32x32x16(fa[cur][i], fb[cur][j], acc[i][j]);
-      // fence: nothing of step s + 1 (its fragment reads for s + 2) moves up
-      // into this step, so each step's reads overlap exactly one step of MFMAs
-      __builtin_amdgcn_sched_barrier(0);
     }
   };
   constexpr std::integral_constant<int, 0> st0{};
