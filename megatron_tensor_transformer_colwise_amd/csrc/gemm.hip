@@ -254,58 +254,74 @@ __global__ __launch_bounds__(Cfg<BMT>::NW * 64, 1) void gemm_bf16_kernel(Args ar
   const int nfull = (int)(K / BK);
   using Full = std::true_type;
   using Partial = std::false_type;
-  // One k-step on stage S.  MAIN: the next stage is a whole k-step.
-  // Otherwise the next stage may be partial, or absent after the last step.
+  constexpr std::integral_constant<int, 0> st0{};
+  constexpr std::integral_constant<int, 1> st1{};
+  constexpr int NQ = MI * 4 > MI + 4 ? MI * 4 : MI + 4;
+  constexpr int MID = MI * 2;  // the hand-over point inside the last k-substep
+  static_assert(C::A_INSTR % NW == 0 && B_INSTR % NW == 0, "every wave issues LA + LB loads per stage");
+  // One k-step on stage S (resident, its first fragments already in
+  // registers).  Two stages are in flight: halfway through the last substep
+  // the barrier retires every read of stage S and makes stage kt + 1
+  // visible; stage kt + 2 is then fetched into S while the remaining MFMAs
+  // of this step cover the first fragment reads of stage kt + 1.
   auto kstep = [&](auto stage_tag, auto main_tag, int kt) {
     constexpr int S = decltype(stage_tag)::value;
     constexpr bool MAIN = decltype(main_tag)::value;
-    // this wave's loads of stage kt have landed; the barrier extends that to
-    // every wave and retires all reads of the buffer about to be refilled
-    wait_vmcnt0();
-    __syncthreads();
     const char* const a_st = smem + S * C::A_TILE;
     const char* const b_st = smem + S * B_TILE;  // rb[][] holds the B base
-#pragma unroll
-    for (int i = 0; i < MI; ++i) fa[0][i] = lds_read16(a_st + ra[i][0]);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) fb[0][j] = lds_read16(b_st + rb[j][0]);
-    // every load of the next stage goes out at once: the vector memory path
-    // sustains its throughput only with many requests in flight
-    constexpr std::integral_constant<int, 1 - S> next{};
-    if (MAIN) {
-      load_stage(next, Full{}, kt + 1);
-    } else if (kt + 1 < nfull) {
-      load_stage(next, Full{}, kt + 1);
-    } else if (kt + 1 < nk) {
-      load_stage(next, Partial{}, kt + 1);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    // Within a k-step s the fragment reads of step s + 1 are slotted one after
-    // each MFMA (fenced so the compiler keeps that order), so every read has
-    // the rest of the step's MFMAs to land (measured 1-5% faster than issuing
-    // them together).
-    constexpr int NQ = MI * 4 > MI + 4 ? MI * 4 : MI + 4;
+    const char* const a_nx = smem + (1 - S) * C::A_TILE;
+    const char* const b_nx = smem + (1 - S) * B_TILE;
 #pragma unroll
     for (int s = 0; s < KSUB; ++s) {
       const int cur = s & 1, nxt = cur ^ 1;
 #pragma unroll
       for (int q = 0; q < NQ; ++q) {
+        if (s == KSUB - 1 && q == MID) {
+          wait_vmcnt0();
+          __syncthreads();
+          if (MAIN) load_stage(stage_tag, Full{}, kt + 2);
+          else if (kt + 2 < nfull) load_stage(stage_tag, Full{}, kt + 2);
+          else if (kt + 2 < nk) load_stage(stage_tag, Partial{}, kt + 2);
+        }
         if (q < MI * 4) acc[q >> 2][q & 3] = mfma32x32x16(fa[cur][q >> 2], fb[cur][q & 3], acc[q >> 2][q & 3]);
         if (s + 1 < KSUB) {
           if (q < MI) fa[nxt][q] = lds_read16(a_st + ra[q][s + 1]);
           else if (q < MI + 4) fb[nxt][q - MI] = lds_read16(b_st + rb[q - MI][s + 1]);
+        } else if (q >= MID) {
+          // first fragments of stage kt + 1 (beyond K: zeros or unused data)
+          const int r = q - MID;
+          if (r < MI) fa[nxt][r] = lds_read16(a_nx + ra[r][0]);
+          else if (r < MI + 4) fb[nxt][r - MI] = lds_read16(b_nx + rb[r - MI][0]);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
+      if (s == KSUB - 1) {
+        // fragment reads that did not fit beside the MFMAs after the barrier
+#pragma unroll
+        for (int r = NQ - MID; r < MI + 4; ++r) {
+          if (r < MI) fa[nxt][r] = lds_read16(a_nx + ra[r][0]);
+          else fb[nxt][r - MI] = lds_read16(b_nx + rb[r - MI][0]);
+        }
+      }
     }
   };
-  constexpr std::integral_constant<int, 0> st0{};
-  constexpr std::integral_constant<int, 1> st1{};
   if (nfull > 0) load_stage(st0, Full{}, 0);
   else load_stage(st0, Partial{}, 0);
+  if (nk > 1) {
+    if (nfull > 1) load_stage(st1, Full{}, 1);
+    else load_stage(st1, Partial{}, 1);
+    wait_vmcnt<C::LA + C::LB>();  // stage 0 landed, stage 1 may still be in flight
+  } else {
+    wait_vmcnt0();
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < MI; ++i) fa[0][i] = lds_read16(smem + ra[i][0]);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) fb[0][j] = lds_read16(smem + rb[j][0]);
   int kt = 0;
-  // pairs of steps whose next stages are both whole k-steps
-  for (; kt + 2 < nfull; kt += 2) {
+  // pairs of steps whose stage-after-next is a whole k-step
+  for (; kt + 3 < nfull; kt += 2) {
     kstep(st0, Full{}, kt);
     kstep(st1, Full{}, kt + 1);
   }
