@@ -15,10 +15,14 @@
 // accumulators per lane), 4 waves of 96 x 128 at 192, 8 waves of 32 x 128 at
 // 128.  The wave count is a multiple of the 4 SIMDs so they share the MFMA
 // work evenly; with two waves per SIMD one issues MFMAs while the other
-// waits on memory or the barrier.  k advances 64 at a time through a two-stage LDS
-// ring; tiles are fetched with 16-byte buffer loads that write LDS directly
-// (no register staging), all of a stage's loads issued together one k-step
-// ahead.  Out-of-range rows and the k tail are fetched as zeros by the
+// waits on memory or the barrier.  k advances 64 at a time through a
+// two-stage LDS ring; tiles are fetched with 16-byte buffer loads that write
+// LDS directly (no register staging), all of a stage's loads issued
+// together.  The one barrier of a k-step sits halfway through its last
+// 16-deep substep: it makes the next stage visible and frees the current
+// one, whose refill (two stages ahead) goes out at once while the step's
+// remaining MFMAs cover the next stage's first fragment reads; within a
+// substep one fragment read follows each MFMA.  Out-of-range rows and the k tail are fetched as zeros by the
 // buffer's range check.  Each LDS row holds 64 bf16; its eight 16-byte chunks
 // are XOR-permuted by swz(row) so the 32 rows one fragment read touches hit
 // distinct banks (measured: no bank conflicts).
