@@ -9,13 +9,14 @@
 // Both operands are contiguous along k (X row-major, W in nn.Linear layout), so
 // every MFMA operand of a lane is 16 contiguous bytes of one row.
 //
-// Tiling: BMT x 256 output tiles, BMT in {256, 192, 128}.  The waves are laid
-// out (rows) x 2 (column halves of 128); a wave owns MI x 4 blocks of
-// v_mfma_f32_32x32x16_bf16: 8 waves of 64 x 128 at BMT 256 (128 float32
-// accumulators per lane), 4 waves of 96 x 128 at 192, 8 waves of 32 x 128 at
-// 128.  The wave count is a multiple of the 4 SIMDs so they share the MFMA
-// work evenly; with two waves per SIMD one issues MFMAs while the other
-// waits on memory or the barrier.  k advances 64 at a time through a
+// Tiling: BMT x 256 output tiles, BMT in {256, 192, 128}, always 8 waves (two
+// per SIMD, so one issues MFMAs while the other waits on memory or the
+// barrier).  A wave owns MI x NJ blocks of v_mfma_f32_32x32x16_bf16: 64 x 128
+// at BMT 256 (128 float32 accumulators per lane), 96 x 64 at 192, 64 x 64 at
+// 128.  At 192 rows, 4 waves of 96 x 128 read less from LDS but leave each
+// SIMD one wave and nothing to cover its waits (13% slower on a QKV
+// projection); at 128 rows, 32 x 128 waves would read 5 fragments per 4
+// MFMAs instead of 4.  k advances 64 at a time through a
 // two-stage LDS ring; tiles are fetched with 16-byte buffer loads that write
 // LDS directly (no register staging), all of a stage's loads issued
 // together.  The one barrier of a k-step sits halfway through its last
@@ -57,17 +58,28 @@ constexpr int B_TILE = BN * ROWB;               // one stage of weight rows
 constexpr int B_INSTR = BN * CH / 64;           // wave-instructions per B stage
 
 // 32-row MFMA blocks per wave for a tile height.  The waves split the tile
-// rows evenly and the tile's two 128-column halves, and their count is a
-// multiple of the 4 SIMDs so every SIMD carries the same MFMA work:
-// 256 -> 8 waves of 64 rows, 192 -> 4 waves of 96, 128 -> 8 waves of 32
-// (two waves per SIMD where the registers allow it).
-constexpr int wave_blocks(int bmt) { return bmt == 256 ? 2 : bmt == 192 ? 3 : 1; }
+// rows and columns evenly into 8 waves, so every SIMD carries the same MFMA
+// work (rows x columns of waves): 256 -> 4 x 2 waves of 64 x 128, 192 -> 2 x 4
+// of 96 x 64, 128 -> 2 x 4 of 64 x 64 (no spills at any height).
+constexpr int wave_blocks(int bmt) { return bmt == 256 ? 2 : bmt == 192 ? 3 : 2; }
+// 32-column MFMA blocks per wave: 4 (a 128-column half of the tile) or 2.
+constexpr int wave_cols(int bmt) { return bmt == 256 ? 4 : 2; }
+
+// Tile column block (0..7, 32 columns each) of a wave's block jj.  A wave
+// always holds blocks jj and jj + NJ / 2 exactly 64 columns apart, so the
+// SwiGLU gate/up pair and the RoPE pair (c, c + 64) meet in one lane.
+template <int NJ>
+__device__ __forceinline__ int col_block(int wn, int jj) {
+  return NJ == 4 ? 4 * wn + jj : 4 * (wn >> 1) + (wn & 1) + 2 * jj;
+}
 
 template <int BMT>
 struct Cfg {
   static constexpr int MI = wave_blocks(BMT);                 // 32-row MFMA blocks per wave
+  static constexpr int NJ = wave_cols(BMT);                   // 32-column MFMA blocks per wave
   static constexpr int WROWS = 32 * MI;                       // rows per wave
-  static constexpr int NW = BMT / WROWS * 2;                  // waves
+  static constexpr int WC = 8 / NJ;                           // wave columns
+  static constexpr int NW = BMT / WROWS * WC;                 // waves
   static_assert(NW % 4 == 0 && BMT % WROWS == 0, "waves must cover the tile and the SIMDs");
   static constexpr int A_TILE = BMT * ROWB;
   static constexpr int SMEM = NSTAGE * (A_TILE + B_TILE);  // A stages, then B stages
@@ -124,6 +136,8 @@ __global__ __launch_bounds__(Cfg<BMT>::NW * 64, 1) void gemm_bf16_kernel(Args ar
   constexpr int NW = C::NW;
   constexpr int MI = C::MI;
   constexpr int WROWS = C::WROWS;
+  constexpr int NJ = C::NJ;
+  constexpr int NP = NJ / 2;  // (first, second) block pairs 64 columns apart
   __shared__ __attribute__((aligned(1024))) char smem[C::SMEM];
 
   const int lane = lane_id();
@@ -222,9 +236,9 @@ __global__ __launch_bounds__(Cfg<BMT>::NW * 64, 1) void gemm_bf16_kernel(Args ar
   };
 
   // ---- LDS -> registers addressing ----------------------------------------
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / C::WC, wn = wave % C::WC;
   const int l31 = lane & 31, hk = lane >> 5;
-  uint32_t ra[MI][KSUB], rb[4][KSUB];  // [block][s] byte offsets within a tile
+  uint32_t ra[MI][KSUB], rb[NJ][KSUB];  // [block][s] byte offsets within a tile
 #pragma unroll
   for (int i = 0; i < MI; ++i) {
     const int r_a = wm * WROWS + i * 32 + l31;
@@ -235,8 +249,8 @@ __global__ __launch_bounds__(Cfg<BMT>::NW * 64, 1) void gemm_bf16_kernel(Args ar
     }
   }
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int r_b = wn * 128 + j * 32 + l31;
+  for (int j = 0; j < NJ; ++j) {
+    const int r_b = col_block<NJ>(wn, j) * 32 + l31;
 #pragma unroll
     for (int s = 0; s < KSUB; ++s) {
       const int c = 2 * s + hk;
@@ -244,24 +258,24 @@ __global__ __launch_bounds__(Cfg<BMT>::NW * 64, 1) void gemm_bf16_kernel(Args ar
     }
   }
 
-  f32x16 acc[MI][4];
+  f32x16 acc[MI][NJ];
 #pragma unroll
   for (int i = 0; i < MI; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+    for (int j = 0; j < NJ; ++j) acc[i][j] = f32x16{};
 
   // Fragments are double-buffered in registers: while the MFMAs of k-step s
   // run, the fragment reads of step s + 1 are in flight, so LDS latency does
   // not stall the matrix pipe inside a stage.
-  u32x4 fa[2][MI], fb[2][4];
+  u32x4 fa[2][MI], fb[2][NJ];
   const int nk = (int)((K + BK - 1) / BK);
   const int nfull = (int)(K / BK);
   using Full = std::true_type;
   using Partial = std::false_type;
   constexpr std::integral_constant<int, 0> st0{};
   constexpr std::integral_constant<int, 1> st1{};
-  constexpr int NQ = MI * 4 > MI + 4 ? MI * 4 : MI + 4;
-  constexpr int MID = MI * 2;  // the hand-over point inside the last k-substep
+  constexpr int NQ = MI * NJ > MI + NJ ? MI * NJ : MI + NJ;
+  constexpr int MID = MI * NJ / 2;  // the hand-over point inside the last k-substep
   static_assert(C::A_INSTR % NW == 0 && B_INSTR % NW == 0, "every wave issues LA + LB loads per stage");
   // One k-step on stage S (resident, its first fragments already in
   // registers).  Two stages are in flight: halfway through the last substep
@@ -287,22 +301,23 @@ __global__ __launch_bounds__(Cfg<BMT>::NW * 64, 1) void gemm_bf16_kernel(Args ar
           else if (kt + 2 < nfull) load_stage(stage_tag, Full{}, kt + 2);
           else if (kt + 2 < nk) load_stage(stage_tag, Partial{}, kt + 2);
         }
-        if (q < MI * 4) acc[q >> 2][q & 3] = mfma32x32x16(fa[cur][q >> 2], fb[cur][q & 3], acc[q >> 2][q & 3]);
+        if (q < MI * NJ)
+          acc[q / NJ][q % NJ] = mfma32x32x16(fa[cur][q / NJ], fb[cur][q % NJ], acc[q / NJ][q % NJ]);
         if (s + 1 < KSUB) {
           if (q < MI) fa[nxt][q] = lds_read16(a_st + ra[q][s + 1]);
-          else if (q < MI + 4) fb[nxt][q - MI] = lds_read16(b_st + rb[q - MI][s + 1]);
+          else if (q < MI + NJ) fb[nxt][q - MI] = lds_read16(b_st + rb[q - MI][s + 1]);
         } else if (q >= MID) {
           // first fragments of stage kt + 1 (beyond K: zeros or unused data)
           const int r = q - MID;
           if (r < MI) fa[nxt][r] = lds_read16(a_nx + ra[r][0]);
-          else if (r < MI + 4) fb[nxt][r - MI] = lds_read16(b_nx + rb[r - MI][0]);
+          else if (r < MI + NJ) fb[nxt][r - MI] = lds_read16(b_nx + rb[r - MI][0]);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
       if (s == KSUB - 1) {
         // fragment reads that did not fit beside the MFMAs after the barrier
 #pragma unroll
-        for (int r = NQ - MID; r < MI + 4; ++r) {
+        for (int r = NQ - MID; r < MI + NJ; ++r) {
           if (r < MI) fa[nxt][r] = lds_read16(a_nx + ra[r][0]);
           else fb[nxt][r - MI] = lds_read16(b_nx + rb[r - MI][0]);
         }
@@ -322,7 +337,7 @@ __global__ __launch_bounds__(Cfg<BMT>::NW * 64, 1) void gemm_bf16_kernel(Args ar
 #pragma unroll
   for (int i = 0; i < MI; ++i) fa[0][i] = lds_read16(smem + ra[i][0]);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) fb[0][j] = lds_read16(smem + rb[j][0]);
+  for (int j = 0; j < NJ; ++j) fb[0][j] = lds_read16(smem + rb[j][0]);
   int kt = 0;
   // pairs of steps whose stage-after-next is a whole k-step
   for (; kt + 3 < nfull; kt += 2) {
@@ -337,8 +352,8 @@ __global__ __launch_bounds__(Cfg<BMT>::NW * 64, 1) void gemm_bf16_kernel(Args ar
 
   // ---- epilogue -----------------------------------------------------------
   // Accumulator element r of block (i, j) in lane L is output row
-  // 32 i + 8 (r / 4) + 4 (L / 32) + r % 4 and column 32 j + L % 32 of the
-  // wave's WROWS x 128 sub-tile.  For bf16 outputs each group of 4
+  // 32 i + 8 (r / 4) + 4 (L / 32) + r % 4 of the wave's rows and column
+  // 32 col_block(wn, j) + L % 32 of the tile.  For bf16 outputs each group of 4
   // consecutive rows is transposed across the 4 lanes of a quad, so a lane
   // ends up with 4 consecutive columns of one row and writes them as one
   // 8-byte store instead of four 2-byte ones.  The transposes run in every
@@ -349,13 +364,16 @@ __global__ __launch_bounds__(Cfg<BMT>::NW * 64, 1) void gemm_bf16_kernel(Args ar
   const int64_t row_base = m0 + wm * WROWS + 4 * hk;
   const int q = l31 & 3;             // row within a group after the transpose
   const int cq = 4 * (l31 >> 2);     // first of the lane's 4 columns after it
+  const int hg = NJ == 4 ? wn : wn >> 1;  // the wave's 128-column group of the tile
+  // column offset, within the first 64 of its group, of pair jp's first block
+  auto pair_col = [&](int jp) { return 32 * (NJ == 4 ? jp : (wn & 1)); };
   if (EPI == EPI_F32) {
-    const int64_t col_base = (int64_t)bn * BN + wn * 128 + l31;
+    const int64_t col_base = (int64_t)bn * BN + l31;
 #pragma unroll
     for (int i = 0; i < MI; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int64_t col = col_base + j * 32;
+      for (int j = 0; j < NJ; ++j) {
+        const int64_t col = col_base + col_block<NJ>(wn, j) * 32;
         if (col >= N) continue;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -364,12 +382,12 @@ __global__ __launch_bounds__(Cfg<BMT>::NW * 64, 1) void gemm_bf16_kernel(Args ar
         }
       }
   } else if (EPI == EPI_BF16 || EPI == EPI_GELU) {
-    const int64_t col_base = (int64_t)bn * BN + wn * 128 + cq;
+    const int64_t col_base = (int64_t)bn * BN + cq;
 #pragma unroll
     for (int i = 0; i < MI; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int64_t col = col_base + j * 32;
+      for (int j = 0; j < NJ; ++j) {
+        const int64_t col = col_base + col_block<NJ>(wn, j) * 32;
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           float v[4];
@@ -386,17 +404,17 @@ __global__ __launch_bounds__(Cfg<BMT>::NW * 64, 1) void gemm_bf16_kernel(Args ar
         }
       }
   } else if (EPI == EPI_SWIGLU) {
-    const int64_t col_base = (int64_t)bn * (BN / 2) + wn * 64 + cq;
+    const int64_t col_base = (int64_t)bn * (BN / 2) + hg * 64 + cq;
 #pragma unroll
     for (int i = 0; i < MI; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int64_t col = col_base + j * 32;
+      for (int j = 0; j < NP; ++j) {
+        const int64_t col = col_base + pair_col(j);
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           float v[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = silu_fast(acc[i][j][4 * g + e]) * acc[i][j + 2][4 * g + e];
+          for (int e = 0; e < 4; ++e) v[e] = silu_fast(acc[i][j][4 * g + e]) * acc[i][j + NP][4 * g + e];
           quad_transpose(v, q);
           const int64_t row = row_base + i * 32 + 8 * g + q;
           if (row < M && col < N)
@@ -404,9 +422,9 @@ __global__ __launch_bounds__(Cfg<BMT>::NW * 64, 1) void gemm_bf16_kernel(Args ar
                 u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
         }
       }
-  } else {  // EPI_QKV: this wave's 128 columns are exactly one head
+  } else {  // EPI_QKV: each 128-column group of the tile is exactly one head
     const QkvOut& o = args.qkv;
-    const int hd = bn * 2 + wn;
+    const int hd = bn * 2 + hg;
     const int nheads = o.hq + 2 * o.hkv;
     if (hd >= nheads) return;
     const uint32_t seq = (uint32_t)o.seq;
@@ -424,11 +442,11 @@ __global__ __launch_bounds__(Cfg<BMT>::NW * 64, 1) void gemm_bf16_kernel(Args ar
       // evaluated that way and the next three follow by rotating it by one
       // position's angle (angle addition), unless the group crosses into the
       // next sequence.
-      double tpp[2];
-      float c1p[2], s1p[2];  // cos / sin of one position's angle
+      double tpp[NP];
+      float c1p[NP], s1p[NP];  // cos / sin of one position's angle
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        tpp[j] = exp2(-(double)(2 * (j * 32 + l31)) * (1.0 / 128.0) * (double)o.log2_base) *
+      for (int j = 0; j < NP; ++j) {
+        tpp[j] = exp2(-(double)(2 * (pair_col(j) + l31)) * (1.0 / 128.0) * (double)o.log2_base) *
                  0.15915494309189533577;
         const float fr = (float)(tpp[j] - floor(tpp[j]));
         c1p[j] = __builtin_amdgcn_cosf(fr);
@@ -448,7 +466,7 @@ __global__ __launch_bounds__(Cfg<BMT>::NW * 64, 1) void gemm_bf16_kernel(Args ar
           const uint32_t p0 = (uint32_t)row0 % seq;
           const bool run = p0 + 3 < seq;  // the group stays inside one sequence
 #pragma unroll
-          for (int j = 0; j < 2; ++j) {
+          for (int j = 0; j < NP; ++j) {
             float cs[4], sn[4];
             angle(p0, j, cs[0], sn[0]);
             if (run) {
@@ -468,7 +486,7 @@ __global__ __launch_bounds__(Cfg<BMT>::NW * 64, 1) void gemm_bf16_kernel(Args ar
             float y1[4], y2[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              const float x1 = acc[i][j][4 * g4 + e], x2 = acc[i][j + 2][4 * g4 + e];
+              const float x1 = acc[i][j][4 * g4 + e], x2 = acc[i][j + NP][4 * g4 + e];
               y1[e] = x1 * cs[e] - x2 * sn[e];
               y2[e] = x2 * cs[e] + x1 * sn[e];
             }
@@ -476,7 +494,7 @@ __global__ __launch_bounds__(Cfg<BMT>::NW * 64, 1) void gemm_bf16_kernel(Args ar
             quad_transpose(y2, q);
             const int64_t row = row0 + q;
             if (row < M) {
-              bf16_t* line = dst + row * ld + j * 32 + cq;
+              bf16_t* line = dst + row * ld + pair_col(j) + cq;
               *reinterpret_cast<u32x2*>(line) = u32x2{pack_bf16x2(y1[0], y1[1]), pack_bf16x2(y1[2], y1[3])};
               *reinterpret_cast<u32x2*>(line + 64) =
                   u32x2{pack_bf16x2(y2[0], y2[1]), pack_bf16x2(y2[2], y2[3])};
@@ -495,8 +513,8 @@ __global__ __launch_bounds__(Cfg<BMT>::NW * 64, 1) void gemm_bf16_kernel(Args ar
           if (row0 >= M) continue;
           const uint32_t b0 = (uint32_t)row0 / seq, p0 = (uint32_t)row0 - b0 * seq;
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int c = j * 32 + l31;
+          for (int j = 0; j < NJ; ++j) {
+            const int c = (col_block<NJ>(wn, j) & 3) * 32 + l31;
             if (vec && row0 + 3 < M) {
               bf16_t* line = vt + (((int64_t)b0 * o.hkv + g) * 128 + c) * o.seq_pad;
               const u32x2 pr = {pack_bf16x2(acc[i][j][4 * g4 + 0], acc[i][j][4 * g4 + 1]),
