@@ -73,10 +73,12 @@ __device__ __forceinline__ int col_block(int wn, int jj) {
   return NJ == 4 ? 4 * wn + jj : 4 * (wn >> 1) + (wn & 1) + 2 * jj;
 }
 
-template <int BMT>
+// W4: a 256-row tile worked by four waves of 128 x 128 (one per SIMD).
+template <int BMT, bool W4 = false>
 struct Cfg {
-  static constexpr int MI = wave_blocks(BMT);                 // 32-row MFMA blocks per wave
-  static constexpr int NJ = wave_cols(BMT);                   // 32-column MFMA blocks per wave
+  static_assert(!W4 || BMT == 256, "four-wave layout is for 256-row tiles");
+  static constexpr int MI = W4 ? 4 : wave_blocks(BMT);        // 32-row MFMA blocks per wave
+  static constexpr int NJ = W4 ? 4 : wave_cols(BMT);          // 32-column MFMA blocks per wave
   static constexpr int WROWS = 32 * MI;                       // rows per wave
   static constexpr int WC = 8 / NJ;                           // wave columns
   static constexpr int NW = BMT / WROWS * WC;                 // waves
@@ -130,9 +132,9 @@ __device__ __forceinline__ void tile_coords(int id, int nb, int num_bm, int num_
   bn = inner / gs;
 }
 
-template <int EPI, int BMT>
-__global__ __launch_bounds__(Cfg<BMT>::NW * 64, 1) void gemm_bf16_kernel(Args args) {
-  using C = Cfg<BMT>;
+template <int EPI, int BMT, bool W4>
+__global__ __launch_bounds__((Cfg<BMT, W4>::NW * 64), 1) void gemm_bf16_kernel(Args args) {
+  using C = Cfg<BMT, W4>;
   constexpr int NW = C::NW;
   constexpr int MI = C::MI;
   constexpr int WROWS = C::WROWS;
@@ -235,6 +237,27 @@ __global__ __launch_bounds__(Cfg<BMT>::NW * 64, 1) void gemm_bf16_kernel(Args ar
     }
   };
 
+  // Load j (0 .. LA + LB - 1) of stage S for k-step kn: the A loads, then the B loads.
+  auto load_one = [&](auto stage_tag, auto full_tag, int kn, int j) {
+    constexpr int S = decltype(stage_tag)::value;
+    constexpr bool FULL = decltype(full_tag)::value;
+    const uint32_t kb = (uint32_t)kn * (uint32_t)(BK * 2);
+    const int64_t k0 = (int64_t)kn * BK;
+    if (j < C::LA) {
+      char* const a_dst = smem + S * C::A_TILE + (j * NW + wave) * 1024;
+      if (FULL) buffer_load_lds16_so(rsrc_a, a_dst, a_off[j], kb);
+      else buffer_load_lds16(rsrc_a, a_dst, ((k0 + a_k[j]) < K) ? a_off[j] + kb : TP_OOB_OFFSET);
+    } else {
+      const int jb = j - C::LA;
+      char* const b_dst = smem + C::B_BASE + S * B_TILE + (jb * NW + wave) * 1024;
+      if (FULL) buffer_load_lds16_so(rsrc_b, b_dst, b_off[jb], kb);
+      else {
+        const bool kin = (k0 + b_k[jb]) < K && b_off[jb] != TP_OOB_OFFSET;
+        buffer_load_lds16(rsrc_b, b_dst, kin ? b_off[jb] + kb : TP_OOB_OFFSET);
+      }
+    }
+  };
+
   // ---- LDS -> registers addressing ----------------------------------------
   const int wm = wave / C::WC, wn = wave % C::WC;
   const int l31 = lane & 31, hk = lane >> 5;
@@ -282,6 +305,67 @@ __global__ __launch_bounds__(Cfg<BMT>::NW * 64, 1) void gemm_bf16_kernel(Args ar
   // the barrier retires every read of stage S and makes stage kt + 1
   // visible; stage kt + 2 is then fetched into S while the remaining MFMAs
   // of this step cover the first fragment reads of stage kt + 1.
+  // Four waves (one per SIMD, 128 x 128 each): a k-step is 4 substeps of 16
+  // MFMAs.  With a single wave per SIMD every non-MFMA instruction delays the
+  // matrix pipe, so the schedule spreads them out: the 8 fragment reads of
+  // the next substep follow the first 8 MFMAs of a substep (A0, B0..B3,
+  // A1..A3, the order the MFMAs consume them), and the 16 loads of the stage
+  // after next go out one per second MFMA over the three substeps after the
+  // barrier that frees its buffer (4 after it in this step, 6 + 6 in the first
+  // two substeps of the next), leaving a substep and a half for the last to
+  // land.  The k-step's one barrier sits after the 8th MFMA of its last
+  // substep: every read of this stage is done and the next stage has landed,
+  // so the remaining 8 MFMAs carry the next stage's first fragment reads.
+  // Issuing a stage's loads in one burst instead doubled their average L2
+  // latency (counter-measured) and cost 8% of the k loop.
+  auto kstep4 = [&](auto stage_tag, auto main_tag, int kt) {
+    constexpr int S = decltype(stage_tag)::value;
+    constexpr bool MAIN = decltype(main_tag)::value;
+    constexpr std::integral_constant<int, 1 - S> other_tag{};
+    const char* const a_st = smem + S * C::A_TILE;
+    const char* const b_st = smem + S * B_TILE;
+    const char* const a_nx = smem + (1 - S) * C::A_TILE;
+    const char* const b_nx = smem + (1 - S) * B_TILE;
+    const bool cont = MAIN || (kt >= 1 && kt + 1 < nk);  // rest of step kt + 1's loads
+    const bool cont_full = MAIN || kt + 1 < nfull;
+    const bool start = MAIN || kt + 2 < nk;               // first loads of step kt + 2
+    const bool start_full = MAIN || kt + 2 < nfull;
+    auto rd = [&](const char* a, const char* b, int sub, int r) {
+      const int ia = r == 0 ? 0 : (r >= 5 ? r - 4 : -1);
+      if (ia >= 0) fa[(sub & 1)][ia] = lds_read16(a + ra[ia][sub]);
+      else fb[(sub & 1)][r - 1] = lds_read16(b + rb[r - 1][sub]);
+    };
+#pragma unroll
+    for (int s = 0; s < KSUB; ++s) {
+      const int cur = s & 1;
+#pragma unroll
+      for (int q = 0; q < MI * NJ; ++q) {
+        if (s == KSUB - 1 && q == 8) {
+          wait_vmcnt0();
+          wait_lgkmcnt0();
+          __builtin_amdgcn_s_barrier();
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        acc[q / NJ][q % NJ] = mfma32x32x16(fa[cur][q / NJ], fb[cur][q % NJ], acc[q / NJ][q % NJ]);
+        if (s + 1 < KSUB) {
+          if (q < 8) rd(a_st, b_st, s + 1, q);
+        } else if (q >= 8) {
+          rd(a_nx, b_nx, 0, q - 8);
+        }
+        if (s < 2 && (q & 1) && q < 12 && cont) {
+          const int j = 4 + s * 6 + (q >> 1);
+          if (cont_full) load_one(other_tag, Full{}, kt + 1, j);
+          else load_one(other_tag, Partial{}, kt + 1, j);
+        }
+        if (s == KSUB - 1 && q >= 9 && (q & 1) && start) {
+          const int j = (q - 9) >> 1;
+          if (start_full) load_one(stage_tag, Full{}, kt + 2, j);
+          else load_one(stage_tag, Partial{}, kt + 2, j);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
   auto kstep = [&](auto stage_tag, auto main_tag, int kt) {
     constexpr int S = decltype(stage_tag)::value;
     constexpr bool MAIN = decltype(main_tag)::value;
@@ -340,6 +424,20 @@ __global__ __launch_bounds__(Cfg<BMT>::NW * 64, 1) void gemm_bf16_kernel(Args ar
   for (int j = 0; j < NJ; ++j) fb[0][j] = lds_read16(smem + rb[j][0]);
   int kt = 0;
   // pairs of steps whose stage-after-next is a whole k-step
+  if constexpr (NW == 4) {
+    static_assert(MI * NJ == 16 && C::LA + C::LB == 16, "four-wave schedule");
+    kstep4(st0, Partial{}, 0);
+    if (nk > 1) kstep4(st1, Partial{}, 1);
+    kt = 2;
+    for (; kt + 3 < nfull; kt += 2) {
+      kstep4(st0, Full{}, kt);
+      kstep4(st1, Full{}, kt + 1);
+    }
+    for (; kt < nk; kt += 2) {
+      kstep4(st0, Partial{}, kt);
+      if (kt + 1 < nk) kstep4(st1, Partial{}, kt + 1);
+    }
+  } else {
   for (; kt + 3 < nfull; kt += 2) {
     kstep(st0, Full{}, kt);
     kstep(st1, Full{}, kt + 1);
@@ -347,6 +445,7 @@ __global__ __launch_bounds__(Cfg<BMT>::NW * 64, 1) void gemm_bf16_kernel(Args ar
   for (; kt < nk; kt += 2) {
     kstep(st0, Partial{}, kt);
     if (kt + 1 < nk) kstep(st1, Partial{}, kt + 1);
+  }
   }
   wait_vmcnt0();
 
@@ -367,7 +466,27 @@ __global__ __launch_bounds__(Cfg<BMT>::NW * 64, 1) void gemm_bf16_kernel(Args ar
   const int hg = NJ == 4 ? wn : wn >> 1;  // the wave's 128-column group of the tile
   // column offset, within the first 64 of its group, of pair jp's first block
   auto pair_col = [&](int jp) { return 32 * (NJ == 4 ? jp : (wn & 1)); };
-  if (EPI == EPI_F32) {
+  if (EPI == EPI_F32 && NW == 4) {
+    // four waves: 16-byte stores of 4 consecutive columns after a quad transpose
+    const int64_t col_base = (int64_t)bn * BN + cq;
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int64_t col = col_base + col_block<NJ>(wn, j) * 32;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          float v[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * g + e];
+          quad_transpose(v, q);
+          const int64_t row = row_base + i * 32 + 8 * g + q;
+          if (row < M && col < N)
+            *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(outg) + row * N + col) =
+                f32x4{v[0], v[1], v[2], v[3]};
+        }
+      }
+  } else if (EPI == EPI_F32) {
     const int64_t col_base = (int64_t)bn * BN + l31;
 #pragma unroll
     for (int i = 0; i < MI; ++i)
@@ -559,6 +678,12 @@ struct Plan {
   int bm_main, split, bm_tail;  // columns [0, split) at bm_main, [split, nbn) at bm_tail
 };
 
+// 256-row tiles switch from eight waves to four (one per SIMD) from this
+// depth on: a short k loop leaves the four-wave tile's prologue and epilogue
+// exposed (an o_proj of k = 1024 runs 6% slower on four waves, a down
+// projection of k = 3584 as fast, k = 8192 5-7% faster).
+constexpr int64_t W4_MIN_K = 2048;
+
 int64_t rounds_of(int64_t tiles) { return (tiles + 255) / 256; }
 
 // Cost of a launch ~ rounds of 256 workgroups x (BMT + 256): close to the
@@ -599,7 +724,13 @@ void launch_part(Args a, int bn0, int cols, int groups, hipStream_t s) {
   a.num_bm = (int)((a.M + BMT - 1) / BMT);
   const int nb = a.num_bm * cols;
   if (nb == 0) return;
-  hipLaunchKernelGGL((gemm_bf16_kernel<EPI, BMT>), dim3(nb, groups), dim3(Cfg<BMT>::NW * 64), 0, s, a);
+  if constexpr (BMT == 256) {
+    if (a.K >= W4_MIN_K) {
+      hipLaunchKernelGGL((gemm_bf16_kernel<EPI, 256, true>), dim3(nb, groups), dim3(Cfg<256, true>::NW * 64), 0, s, a);
+      return;
+    }
+  }
+  hipLaunchKernelGGL((gemm_bf16_kernel<EPI, BMT, false>), dim3(nb, groups), dim3(Cfg<BMT>::NW * 64), 0, s, a);
 }
 
 template <int EPI>

@@ -107,6 +107,9 @@ def test_rowwise_gemm_integer_bit_exact(device, m, k, n):
     (1000, 136, 776, (128, 4, 128)),      # 128-row tiles, ragged m and n
     (7777, 72, 1280, (192, 5, 192)),      # 192-row tiles (96-row waves), ragged m
     (5000, 64, 3584, (192, 8, 128)),      # 192-row main range, 128-row tail, ragged m
+    (4000, 2056, 4000, (256, 16, 256)),   # four-wave 256-row tiles: ragged m and n, k tail of 8
+    (4096, 2048, 4096, (256, 16, 256)),   # four-wave 256-row tiles, whole k-steps only
+    (300, 4104, 264, (128, 2, 128)),      # deep k on 128-row tiles
 ])
 def test_rowwise_gemm_plans_bit_exact(device, m, k, n, plan):
     """Every tile height and the split launch, bit-exact on integer inputs."""
@@ -207,20 +210,28 @@ def test_colwise_activation_slices(device):
             assert rel_err(host(mlp.act_ws), ref) <= BF16_TOL
 
 
-@pytest.mark.parametrize("m,h,f,plan", [(3000, 64, 1536, (192, 12, 192)), (5000, 64, 1792, (192, 8, 128))])
-def test_swiglu_colwise_tile_heights(device, m, h, f, plan):
-    """SwiGLU epilogue (gate/up pairing, 4-column stores) at 192-row tiles and a
-    192/128 split, ragged m, against the oracle's activation."""
-    say(f"case swiglu colwise m={m} h={h} f={f} plan={plan}")
-    assert tp.tp_gemm_plan(m, f, True) == plan
-    case = inputs.MLPCase("heights", m, h, f, 1, "swiglu", "bf16", seed=24)
+@pytest.mark.parametrize("act,m,h,f,plan", [
+    ("swiglu", 3000, 64, 1536, (192, 12, 192)),
+    ("swiglu", 5000, 64, 1792, (192, 8, 128)),
+    ("swiglu", 4000, 2056, 2048, (256, 16, 256)),   # four-wave tiles, ragged m, k tail
+    ("gelu", 4000, 2056, 4000, (256, 16, 256)),     # four-wave tiles, ragged m and n
+])
+def test_colwise_activation_tile_heights(device, act, m, h, f, plan):
+    """GeLU and SwiGLU epilogues (gate/up pairing, 4-column stores) at every
+    tile layout, ragged m, against the oracle's activation."""
+    say(f"case {act} colwise m={m} h={h} f={f} plan={plan}")
+    assert tp.tp_gemm_plan(m, f, act == "swiglu") == plan
+    case = inputs.MLPCase("heights", m, h, f, 1, act, "bf16", seed=24)
     w = inputs.gen_mlp(case)
     dw = {k: to_dev(v, device) for k, v in w.items()}
-    mlp = shard.MLPShards(dw["X"], dw, 1, "swiglu")
+    mlp = shard.MLPShards(dw["X"], dw, 1, act)
     mlp.colwise(0)
     torch.cuda.synchronize()
     W = {k: v.f64() for k, v in w.items()}
-    ref = oracle.colwise_act(W["X"], None, "swiglu", (W["W1"], W["W3"]))
+    if act == "swiglu":
+        ref = oracle.colwise_act(W["X"], None, "swiglu", (W["W1"], W["W3"]))
+    else:
+        ref = oracle.colwise_act(W["X"], W["A"], "gelu")
     assert rel_err(host(mlp.act_ws), ref) <= BF16_TOL
 
 
@@ -235,6 +246,7 @@ def test_swiglu_colwise_tile_heights(device, m, h, f, plan):
     (3, 64, 256, 4, 4, 1, True),      # MHA, one rank
     (1, 1, 128, 2, 1, 1, True),       # a single token
     (5, 1400, 128, 8, 2, 1, True),    # Q/K/V projection on 192-row tiles, ragged m and seq
+    (2, 2000, 2056, 20, 4, 1, True),  # Q/K/V projection on four-wave 256-row tiles, k tail
 ])
 def test_attention_small(device, batch, seq, h, heads, kv, t, causal):
     say(f"case attn b={batch} s={seq} h={h} heads={heads} kv={kv} t={t} causal={causal}")
