@@ -73,11 +73,11 @@ __device__ __forceinline__ int col_block(int wn, int jj) {
   return NJ == 4 ? 4 * wn + jj : 4 * (wn >> 1) + (wn & 1) + 2 * jj;
 }
 
-// W4: a 256-row tile worked by four waves of 128 x 128 (one per SIMD).
+// W4: the tile worked by four waves (one per SIMD) in a 2 x 2 grid of
+// (BMT / 2) x 128 each.
 template <int BMT, bool W4 = false>
 struct Cfg {
-  static_assert(!W4 || BMT == 256, "four-wave layout is for 256-row tiles");
-  static constexpr int MI = W4 ? 4 : wave_blocks(BMT);        // 32-row MFMA blocks per wave
+  static constexpr int MI = W4 ? BMT / 64 : wave_blocks(BMT);  // 32-row MFMA blocks per wave
   static constexpr int NJ = W4 ? 4 : wave_cols(BMT);          // 32-column MFMA blocks per wave
   static constexpr int WROWS = 32 * MI;                       // rows per wave
   static constexpr int WC = 8 / NJ;                           // wave columns
@@ -149,7 +149,12 @@ __global__ __launch_bounds__((Cfg<BMT, W4>::NW * 64), 1) void gemm_bf16_kernel(A
   void* const outg = args.out[blockIdx.y];
   int bm, bn;
   tile_coords(blockIdx.x, gridDim.x, args.num_bm, args.num_bn, bm, bn);
-  bn += args.bn0;
+  // The tile coordinates come out of VALU divisions; marking them uniform
+  // keeps the buffer descriptors built from them in scalar registers (the
+  // compiler otherwise wrapped every global load of some epilogue variants
+  // in a loop over the wave's distinct descriptor values).
+  bm = __builtin_amdgcn_readfirstlane(bm);
+  bn = __builtin_amdgcn_readfirstlane(bn + args.bn0);
 
   const int64_t M = args.M, N = args.N, K = args.K;
   const int64_t m0 = (int64_t)bm * BMT;
@@ -322,6 +327,14 @@ __global__ __launch_bounds__((Cfg<BMT, W4>::NW * 64), 1) void gemm_bf16_kernel(A
     constexpr int S = decltype(stage_tag)::value;
     constexpr bool MAIN = decltype(main_tag)::value;
     constexpr std::integral_constant<int, 1 - S> other_tag{};
+    constexpr int NMF = MI * NJ;            // MFMAs per substep
+    constexpr int NRD = MI + NJ;            // fragment reads per substep
+    constexpr int BPOS = NMF - NRD;         // the barrier follows this many MFMAs of the last substep
+    constexpr int NLD = C::LA + C::LB;      // loads per wave per stage
+    constexpr int NST = NRD / 2;            // loads after the barrier, one per second MFMA
+    constexpr int NC0 = (NLD - NST + 1) / 2, NC1 = NLD - NST - NC0;  // in substeps 0 and 1
+    constexpr int SP0 = NMF / NC0, SP1 = NMF / NC1;                 // their spacing in MFMAs
+    static_assert(NJ == 4 && BPOS > 0 && SP0 >= 1 && SP1 >= 1, "four-wave schedule");
     const char* const a_st = smem + S * C::A_TILE;
     const char* const b_st = smem + S * B_TILE;
     const char* const a_nx = smem + (1 - S) * C::A_TILE;
@@ -330,6 +343,7 @@ __global__ __launch_bounds__((Cfg<BMT, W4>::NW * 64), 1) void gemm_bf16_kernel(A
     const bool cont_full = MAIN || kt + 1 < nfull;
     const bool start = MAIN || kt + 2 < nk;               // first loads of step kt + 2
     const bool start_full = MAIN || kt + 2 < nfull;
+    // fragment read r: A0, B0..B3, A1.. (the order the MFMAs use them)
     auto rd = [&](const char* a, const char* b, int sub, int r) {
       const int ia = r == 0 ? 0 : (r >= 5 ? r - 4 : -1);
       if (ia >= 0) fa[(sub & 1)][ia] = lds_read16(a + ra[ia][sub]);
@@ -339,8 +353,8 @@ __global__ __launch_bounds__((Cfg<BMT, W4>::NW * 64), 1) void gemm_bf16_kernel(A
     for (int s = 0; s < KSUB; ++s) {
       const int cur = s & 1;
 #pragma unroll
-      for (int q = 0; q < MI * NJ; ++q) {
-        if (s == KSUB - 1 && q == 8) {
+      for (int q = 0; q < NMF; ++q) {
+        if (s == KSUB - 1 && q == BPOS) {
           wait_vmcnt0();
           wait_lgkmcnt0();
           __builtin_amdgcn_s_barrier();
@@ -348,17 +362,21 @@ __global__ __launch_bounds__((Cfg<BMT, W4>::NW * 64), 1) void gemm_bf16_kernel(A
         }
         acc[q / NJ][q % NJ] = mfma32x32x16(fa[cur][q / NJ], fb[cur][q % NJ], acc[q / NJ][q % NJ]);
         if (s + 1 < KSUB) {
-          if (q < 8) rd(a_st, b_st, s + 1, q);
-        } else if (q >= 8) {
-          rd(a_nx, b_nx, 0, q - 8);
+          if (q < NRD) rd(a_st, b_st, s + 1, q);
+        } else if (q >= BPOS) {
+          rd(a_nx, b_nx, 0, q - BPOS);
         }
-        if (s < 2 && (q & 1) && q < 12 && cont) {
-          const int j = 4 + s * 6 + (q >> 1);
-          if (cont_full) load_one(other_tag, Full{}, kt + 1, j);
-          else load_one(other_tag, Partial{}, kt + 1, j);
+        if (s < 2 && cont) {
+          const int sp = s == 0 ? SP0 : SP1;
+          const int i = (q + 1) / sp - 1;
+          if ((q + 1) % sp == 0 && i < (s == 0 ? NC0 : NC1)) {
+            const int j = NST + (s == 0 ? 0 : NC0) + i;
+            if (cont_full) load_one(other_tag, Full{}, kt + 1, j);
+            else load_one(other_tag, Partial{}, kt + 1, j);
+          }
         }
-        if (s == KSUB - 1 && q >= 9 && (q & 1) && start) {
-          const int j = (q - 9) >> 1;
+        if (s == KSUB - 1 && q > BPOS && ((q - BPOS) & 1) && start) {
+          const int j = (q - BPOS) >> 1;
           if (start_full) load_one(stage_tag, Full{}, kt + 2, j);
           else load_one(stage_tag, Partial{}, kt + 2, j);
         }
@@ -425,7 +443,6 @@ __global__ __launch_bounds__((Cfg<BMT, W4>::NW * 64), 1) void gemm_bf16_kernel(A
   int kt = 0;
   // pairs of steps whose stage-after-next is a whole k-step
   if constexpr (NW == 4) {
-    static_assert(MI * NJ == 16 && C::LA + C::LB == 16, "four-wave schedule");
     kstep4(st0, Partial{}, 0);
     if (nk > 1) kstep4(st1, Partial{}, 1);
     kt = 2;
@@ -542,38 +559,63 @@ __global__ __launch_bounds__((Cfg<BMT, W4>::NW * 64), 1) void gemm_bf16_kernel(A
         }
       }
   } else {  // EPI_QKV: each 128-column group of the tile is exactly one head
-    const QkvOut& o = args.qkv;
+    const QkvOut o = args.qkv;
     const int hd = bn * 2 + hg;
     const int nheads = o.hq + 2 * o.hkv;
+    // V heads are transposed through LDS; every wave of the tile passes this
+    // barrier (before any returns) so no wave still reads the k loop's stages
+    __syncthreads();
     if (hd >= nheads) return;
     const uint32_t seq = (uint32_t)o.seq;
-    // Rows 8 g4 + e, e = 0..3, of block i are 4 consecutive tokens; one
-    // division per group gives (sequence, position) of its first token.
+    // Rows 8 g4 + e, e = 0..3, of block i are 4 consecutive tokens.  One
+    // division per lane gives (sequence, position) of the lane's first row;
+    // a group's first token is that plus its row offset, wrapped.
+    const uint32_t b_base = (uint32_t)(row_base / seq);
+    const uint32_t p_base = (uint32_t)(row_base - (int64_t)b_base * seq);
+    auto split_pos = [&](int off, uint32_t& b, uint32_t& p) {
+      p = p_base + (uint32_t)off;
+      b = b_base;
+      if (p >= seq) {
+        if ((uint32_t)off < seq) {
+          p -= seq;
+          ++b;
+        } else {
+          b += p / seq;
+          p %= seq;
+        }
+      }
+    };
     if (hd < o.hq + o.hkv) {
       const bool is_q = hd < o.hq;
       bf16_t* dst = reinterpret_cast<bf16_t*>(is_q ? o.q : o.k);
       const int64_t ld = (int64_t)(is_q ? o.hq : o.hkv) * 128;
       dst += (int64_t)(is_q ? hd : hd - o.hq) * 128;
       // angle = pos * base^(-2 c1 / 128) radians for the pair (c1, c1 + 64),
-      // taken in turns (1 turn = 2 pi) in float64 so only the fraction of a
-      // turn is rounded to float32; v_sin/v_cos take their argument in turns.
-      // The 4 rows of a group are consecutive positions: the first angle is
-      // evaluated that way and the next three follow by rotating it by one
-      // position's angle (angle addition), unless the group crosses into the
-      // next sequence.
-      double tpp[NP];
+      // taken in turns (1 turn = 2 pi): v_sin/v_cos take turns.  The turns
+      // per position are held as an unevaluated float sum f_hi + f_lo
+      // (evaluated once per lane in float64), and pos * f_hi is split into
+      // its rounded value and exact error by an FMA, so only the fraction of
+      // a turn is rounded to float32, as if the product were taken in
+      // float64.  The 4 rows of a group are consecutive positions: the
+      // first angle is evaluated that way and the next three follow by
+      // rotating it by one position's angle (angle addition), unless the
+      // group crosses into the next sequence.
+      float f_hi[NP], f_lo[NP];
       float c1p[NP], s1p[NP];  // cos / sin of one position's angle
 #pragma unroll
       for (int j = 0; j < NP; ++j) {
-        tpp[j] = exp2(-(double)(2 * (pair_col(j) + l31)) * (1.0 / 128.0) * (double)o.log2_base) *
-                 0.15915494309189533577;
-        const float fr = (float)(tpp[j] - floor(tpp[j]));
-        c1p[j] = __builtin_amdgcn_cosf(fr);
-        s1p[j] = __builtin_amdgcn_sinf(fr);
+        const double fd = exp2(-(double)(2 * (pair_col(j) + l31)) * (1.0 / 128.0) * (double)o.log2_base) *
+                          0.15915494309189533577;
+        f_hi[j] = (float)fd;
+        f_lo[j] = (float)(fd - (double)f_hi[j]);
+        c1p[j] = __builtin_amdgcn_cosf(f_hi[j]);
+        s1p[j] = __builtin_amdgcn_sinf(f_hi[j]);
       }
       auto angle = [&](uint32_t pos, int j, float& cs, float& sn) {
-        const double turns = (double)pos * tpp[j];
-        const float frac = (float)(turns - floor(turns));
+        const float pf = (float)pos;  // exact: positions are below 2^24
+        const float a = pf * f_hi[j];
+        const float err = fmaf(pf, f_hi[j], -a);
+        const float frac = (a - floorf(a)) + fmaf(pf, f_lo[j], err);
         sn = __builtin_amdgcn_sinf(frac);
         cs = __builtin_amdgcn_cosf(frac);
       };
@@ -582,7 +624,8 @@ __global__ __launch_bounds__((Cfg<BMT, W4>::NW * 64), 1) void gemm_bf16_kernel(A
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
           const int64_t row0 = row_base + i * 32 + 8 * g4;
-          const uint32_t p0 = (uint32_t)row0 % seq;
+          uint32_t b0, p0;
+          split_pos(i * 32 + 8 * g4, b0, p0);
           const bool run = p0 + 3 < seq;  // the group stays inside one sequence
 #pragma unroll
           for (int j = 0; j < NP; ++j) {
@@ -597,8 +640,8 @@ __global__ __launch_bounds__((Cfg<BMT, W4>::NW * 64), 1) void gemm_bf16_kernel(A
             } else {
 #pragma unroll
               for (int e = 1; e < 4; ++e) {
-                uint32_t pos = p0 + e;
-                if (pos >= seq) pos -= seq;
+                uint32_t bb, pos;
+                split_pos(i * 32 + 8 * g4 + e, bb, pos);
                 angle(pos, j, cs[e], sn[e]);
               }
             }
@@ -620,6 +663,58 @@ __global__ __launch_bounds__((Cfg<BMT, W4>::NW * 64), 1) void gemm_bf16_kernel(A
             }
           }
         }
+    } else if ((seq & 7u) == 0) {
+      // V head, stored transposed per sequence: Vt[b][g][c][p].  A lane holds
+      // 4-row runs of one channel; written straight out that is one 8-byte
+      // store per run, 64 channels apart across the wave.  Instead the wave's
+      // block goes through its own LDS region as [channel][row] (rows padded
+      // by 8 against bank conflicts), and is read back 8 rows of one channel
+      // per lane, so each 16-byte store extends a contiguous run of a channel
+      // row of Vt.  With seq a multiple of 8 (and tile rows at multiples of
+      // 32) an 8-row chunk never straddles two sequences.  Passes of PI
+      // 32-row blocks keep every wave's region inside the tile's LDS.
+      constexpr int CH_W = NJ * 32;  // channels of the wave
+      constexpr int PI = (NW * CH_W * (MI * 32 + 8) * 2 <= C::SMEM) ? MI
+                         : (MI % 2 == 0 && NW * CH_W * (MI * 16 + 8) * 2 <= C::SMEM) ? MI / 2 : 1;
+      constexpr int RP = PI * 32 + 8;  // padded row length of a channel in LDS
+      static_assert(NW * CH_W * RP * 2 <= C::SMEM, "V staging region");
+      constexpr int CPC = PI * 4;      // 8-row chunks per channel per pass
+      const int g = hd - o.hq - o.hkv;
+      bf16_t* vt = reinterpret_cast<bf16_t*>(o.vt);
+      bf16_t* reg = reinterpret_cast<bf16_t*>(smem) + wave * CH_W * RP;
+      const int64_t wrow0 = m0 + wm * WROWS;  // the wave's first row (a multiple of 32)
+      const uint32_t vb0 = (uint32_t)(wrow0 / seq), vp0 = (uint32_t)(wrow0 - (int64_t)vb0 * seq);
+#pragma unroll
+      for (int i0 = 0; i0 < MI; i0 += PI) {
+        if (i0 > 0) wait_lgkmcnt0();  // the previous pass's reads are done
+#pragma unroll
+        for (int ii = 0; ii < PI; ++ii)
+#pragma unroll
+          for (int j = 0; j < NJ; ++j)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+              const u32x2 pr = {pack_bf16x2(acc[i0 + ii][j][4 * g4 + 0], acc[i0 + ii][j][4 * g4 + 1]),
+                                pack_bf16x2(acc[i0 + ii][j][4 * g4 + 2], acc[i0 + ii][j][4 * g4 + 3])};
+              *reinterpret_cast<u32x2*>(reg + (j * 32 + l31) * RP + ii * 32 + 8 * g4 + 4 * hk) = pr;
+            }
+        wait_lgkmcnt0();
+#pragma unroll
+        for (int it = 0; it < CH_W * CPC / 64; ++it) {
+          const int idx = it * 64 + lane;
+          const int cl = idx / CPC, k = idx % CPC;
+          const u32x4 v = lds_read16(reg + cl * RP + 8 * k);
+          const int off = (i0 * 32) + 8 * k;  // row offset within the wave
+          if (wrow0 + off < M) {
+            uint32_t b = vb0, p = vp0 + (uint32_t)off;
+            if (p >= seq) {
+              b += p / seq;
+              p %= seq;
+            }
+            const int c = (col_block<NJ>(wn, cl >> 5) & 3) * 32 + (cl & 31);
+            *reinterpret_cast<u32x4*>(vt + (((int64_t)b * o.hkv + g) * 128 + c) * o.seq_pad + p) = v;
+          }
+        }
+      }
     } else {
       const int g = hd - o.hq - o.hkv;
       bf16_t* vt = reinterpret_cast<bf16_t*>(o.vt);
@@ -630,7 +725,8 @@ __global__ __launch_bounds__((Cfg<BMT, W4>::NW * 64), 1) void gemm_bf16_kernel(A
         for (int g4 = 0; g4 < 4; ++g4) {
           const int64_t row0 = row_base + i * 32 + 8 * g4;
           if (row0 >= M) continue;
-          const uint32_t b0 = (uint32_t)row0 / seq, p0 = (uint32_t)row0 - b0 * seq;
+          uint32_t b0, p0;
+          split_pos(i * 32 + 8 * g4, b0, p0);
 #pragma unroll
           for (int j = 0; j < NJ; ++j) {
             const int c = (col_block<NJ>(wn, j) & 3) * 32 + l31;
@@ -724,11 +820,9 @@ void launch_part(Args a, int bn0, int cols, int groups, hipStream_t s) {
   a.num_bm = (int)((a.M + BMT - 1) / BMT);
   const int nb = a.num_bm * cols;
   if (nb == 0) return;
-  if constexpr (BMT == 256) {
-    if (a.K >= W4_MIN_K) {
-      hipLaunchKernelGGL((gemm_bf16_kernel<EPI, 256, true>), dim3(nb, groups), dim3(Cfg<256, true>::NW * 64), 0, s, a);
-      return;
-    }
+  if (a.K >= W4_MIN_K) {
+    hipLaunchKernelGGL((gemm_bf16_kernel<EPI, BMT, true>), dim3(nb, groups), dim3(Cfg<BMT, true>::NW * 64), 0, s, a);
+    return;
   }
   hipLaunchKernelGGL((gemm_bf16_kernel<EPI, BMT, false>), dim3(nb, groups), dim3(Cfg<BMT>::NW * 64), 0, s, a);
 }

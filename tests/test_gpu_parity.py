@@ -109,7 +109,9 @@ def test_rowwise_gemm_integer_bit_exact(device, m, k, n):
     (5000, 64, 3584, (192, 8, 128)),      # 192-row main range, 128-row tail, ragged m
     (4000, 2056, 4000, (256, 16, 256)),   # four-wave 256-row tiles: ragged m and n, k tail of 8
     (4096, 2048, 4096, (256, 16, 256)),   # four-wave 256-row tiles, whole k-steps only
-    (300, 4104, 264, (128, 2, 128)),      # deep k on 128-row tiles
+    (300, 4104, 264, (128, 2, 128)),      # four-wave 128-row tiles, deep k
+    (4000, 2056, 2560, (192, 10, 192)),   # four-wave 192-row tiles, ragged m, k tail
+    (5000, 2056, 3584, (192, 8, 128)),    # four-wave 192/128 split launch, ragged m, k tail
 ])
 def test_rowwise_gemm_plans_bit_exact(device, m, k, n, plan):
     """Every tile height and the split launch, bit-exact on integer inputs."""
@@ -215,6 +217,7 @@ def test_colwise_activation_slices(device):
     ("swiglu", 5000, 64, 1792, (192, 8, 128)),
     ("swiglu", 4000, 2056, 2048, (256, 16, 256)),   # four-wave tiles, ragged m, k tail
     ("gelu", 4000, 2056, 4000, (256, 16, 256)),     # four-wave tiles, ragged m and n
+    ("swiglu", 5000, 2056, 1792, (192, 8, 128)),    # four-wave 192/128 split, ragged m, k tail
 ])
 def test_colwise_activation_tile_heights(device, act, m, h, f, plan):
     """GeLU and SwiGLU epilogues (gate/up pairing, 4-column stores) at every
