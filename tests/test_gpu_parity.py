@@ -125,6 +125,40 @@ def test_rowwise_gemm_plans_bit_exact(device, m, k, n, plan):
     assert np.array_equal(host(out), y.f64() @ w.f64().T)
 
 
+@pytest.mark.parametrize("m,k,n,plan", [
+    (6100, 1096, 5904, (192, 24, 192)),   # eight-wave tiles, k tail of 8
+    (6100, 2120, 5904, (192, 24, 192)),   # four-wave tiles, k tail of 8
+    (8000, 2048, 4400, (192, 18, 192)),   # four-wave tiles, whole k-steps only
+])
+def test_rowwise_gemm_many_tiles_bit_exact(device, m, k, n, plan):
+    """Several rounds of tiles per launch (more tiles than compute units),
+    ragged m and n, with and without a k tail: bit-exact on integer inputs."""
+    say(f"case rowwise many tiles m={m} k={k} n={n} plan={plan}")
+    assert tp.tp_gemm_plan(m, n) == plan
+    y = inputs.integers(10, 0, (m, k), -2, 2)
+    w = inputs.integers(10, 1, (n, k), -2, 2)
+    out = torch.full((m, n), float("nan"), dtype=torch.float32, device=device)
+    tp.tp_rowwise("bf16", m, k, n, to_dev(y, device), to_dev(w, device), out)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(out), y.f64() @ w.f64().T)
+
+
+@pytest.mark.parametrize("m,k,n", [(6100, 128, 5904), (6100, 2048, 5904)])
+def test_colwise_none_many_tiles_bit_exact(device, m, k, n):
+    """bf16 outputs of a launch with more tiles than compute units (eight- and
+    four-wave tiles).  Inputs in {-1, 0, 1}: the seeded sums stay within
+    +-256, where bf16 holds every integer."""
+    say(f"case colwise many tiles m={m} k={k} n={n}")
+    x = inputs.integers(11, 0, (m, k), -1, 1)
+    w = inputs.integers(11, 1, (n, k), -1, 1)
+    ref = x.f64() @ w.f64().T
+    assert np.max(np.abs(ref)) <= 256
+    out = torch.empty(m, n, dtype=torch.bfloat16, device=device)
+    tp.tp_colwise("none", "bf16", m, k, n, to_dev(x, device), to_dev(w, device), out)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(out), ref)
+
+
 @pytest.mark.parametrize("m,k,n", [(300, 40, 264), (64, 48, 512)])
 def test_colwise_none_integer_bit_exact(device, m, k, n):
     """Plain colwise projection, integers small enough (|sum| <= 2*2*48 < 256)
