@@ -5,8 +5,12 @@ A step is one forward pass of a 70B-shaped pre-norm block (h=8192, 64 query /
 at t=8, with every rank's work run on this GPU one after another:
 
   RMSNorm(X) -> for each rank: QKV+RoPE GEMM, flash attention, o_proj GEMM
-  -> shard-sum (+X) -> RMSNorm(h1) -> for each rank: SwiGLU GEMM, down GEMM
-  -> shard-sum (+h1).
+  -> shard-sum (+X) and RMSNorm(h1) in one pass -> for each rank: SwiGLU
+  GEMM, down GEMM -> shard-sum (+h1).
+
+The detail also times the sequence-parallel form of the same step (norms on
+each rank's slice of every sequence, the sums as reduce-scatters onto those
+slices), which computes the same result.
 
 ``value`` is the algorithmic bf16 flop rate of the step (2 flops per
 multiply-add of every GEMM, causal attention counting only unmasked pairs)
@@ -217,6 +221,7 @@ def per_config_report(dev):
         srec = sum_rec(lambda: blk.mlp.reduce(residual=blk.attn.out, residual_dt="f32"),
                        (case.t + 2) * 4 * n)
         step, step_min = _time(lambda: blk.forward(), reps=5, warm=2)
+        sp_step, sp_min = _time(lambda: blk.forward_sp(), reps=5, warm=2)
         rec = {"workload": name, "attn_call_ms": round(ams, 4), "attn_min_ms": round(amn, 4),
                "attn_tflops": rate(afl, ams),
                "attn_pct_mfma_peak": round(100.0 * afl / ams / 1e9 / MFMA_BF16_PEAK_TFLOPS, 2),
@@ -225,7 +230,9 @@ def per_config_report(dev):
                "shard_aggregate_tflops": rate(afl + mfl, ams + mms)}
         rec.update(srec)
         rec.update({"block_step_ms": round(step, 3), "block_step_min_ms": round(step_min, 3),
-                    "block_step_tflops": rate(case.t * (afl + mfl), step)})
+                    "block_step_tflops": rate(case.t * (afl + mfl), step),
+                    "sequence_parallel_step_ms": round(sp_step, 3),
+                    "sequence_parallel_step_tflops": rate(case.t * (afl + mfl), sp_step)})
         emit(rec)
         del blk, dw
     del scratch
@@ -298,8 +305,9 @@ def main():
 
     def step(record: bool):
         blk.norm_attn()
-        attn.forward(residual=blk.x, residual_dt="bf16")
-        blk.norm_mlp()
+        for r in range(t):
+            attn.rank(r)
+        blk.sum_norm_mlp()
         for r in range(t):
             if record:
                 e0 = torch.cuda.Event(enable_timing=True)
@@ -353,7 +361,9 @@ def main():
     attn_ms = time_call(lambda: attn.rank(0))
     mlp_ms = time_call(lambda: mlp.rank(0))
     sum_ms = time_call(lambda: mlp.reduce(residual=attn.out, residual_dt="f32"))
+    sum_norm_ms = time_call(lambda: blk.sum_norm_mlp())
     norm_ms = time_call(lambda: blk.norm_mlp())
+    sp_ms = time_call(lambda: blk.forward_sp(), reps=3)
     n = case.tokens * case.hidden
     detail = {
         "attn_call_ms": round(attn_ms, 4),
@@ -362,8 +372,12 @@ def main():
         "mlp_call_tflops": round((fl["swiglu_gemm"] + fl["down_gemm"]) / mlp_ms / 1e9, 1),
         "shard_sum_ms": round(sum_ms, 4),
         "shard_sum_gbs": round((t + 2) * 4 * n / sum_ms / 1e6, 1),
+        "sum_rmsnorm_ms": round(sum_norm_ms, 4),
+        "sum_rmsnorm_gbs": round((4 * t + 8) * n / sum_norm_ms / 1e6, 1),
         "rmsnorm_f32_ms": round(norm_ms, 4),
         "rmsnorm_gbs": round(6 * n / norm_ms / 1e6, 1),
+        "sequence_parallel_step_ms": round(sp_ms, 4),
+        "sequence_parallel_tflops": round(step_flops / (sp_ms * 1e-3) / 1e12, 1),
     }
     log(f"detail {detail}")
 

@@ -211,6 +211,45 @@ tp_status tp_rmsnorm(tp_dtype in_dt, int64_t m, int64_t h, const void* x, const 
                      float eps, void* y, void* stream);
 
 /* --------------------------------------------------------------------------
+ * The sum that ends a sublayer and the norm that opens the next one, in one
+ * pass over rows of h:
+ *   x   = ((partials[0] + partials[1]) + ... + partials[t-1]) + residual
+ *         (t = 0: the residual alone)
+ *   out = x                                                 (float32, if out)
+ *   y   = bf16( x / sqrt(mean_c x^2 + eps) * gain )  per row   (if y)
+ * with tp_shard_sum's and tp_rmsnorm's arithmetic exactly, so the results
+ * are bitwise those of those calls, and without reading out back.
+ *
+ * The rows are nrun runs of run_rows consecutive rows, the first rows of
+ * consecutive runs run_stride rows apart (run_stride is ignored for one
+ * run); every pointer addresses the first row of the first run.  This is
+ * the sequence-parallel form ("Tensor parallelism" page, section "Sequence
+ * parallelism": a norm acts on every token alone, so each rank normalises
+ * only its slice of the sequence, and the sum after a row-parallel layer is
+ * a reduce-scatter that leaves each rank the sum over its slice; section
+ * "Writing it in PyTorch": the slice is Shard(1), the sequence dimension of
+ * (batch, sequence, hidden)).  Rank r of t, with batch sequences of S tokens
+ * stored token-major, passes its positions [r S/t, (r+1) S/t) of every
+ * sequence as nrun = batch runs of run_rows = S/t, run_stride = S, pointers
+ * offset by r S/t rows:
+ *   its norm of X:                  t = 0, residual = X, out = NULL, y
+ *   reduce-scatter + X, then norm:  t partials, residual = X, out = h1, y
+ *   reduce-scatter + h1:            t partials, residual = h1, out = Z, y = NULL
+ * (on one device, or over peer pointers).  One run of all rows gives the
+ * replicated form.
+ *
+ *   t          0 .. 16
+ *   partials   HOST array of t device pointers, float32 rows
+ *   residual   rows of residual_dt (TP_F32 or TP_BF16), or NULL (t >= 1)
+ *   out        float32 rows or NULL; may alias a float32 residual, not a partial
+ *   gain       [h] float32 or NULL (all ones); y bf16 rows or NULL
+ *   out and y may not both be NULL.
+ * ------------------------------------------------------------------------ */
+tp_status tp_shard_sum_rmsnorm(int32_t t, int64_t nrun, int64_t run_rows, int64_t run_stride, int64_t h,
+                               const float* const* partials, const void* residual, tp_dtype residual_dt,
+                               float* out, const float* gain, float eps, void* y, void* stream);
+
+/* --------------------------------------------------------------------------
  * Introspection: how the bf16 GEMM behind tp_colwise / tp_rowwise /
  * tp_qkv_rope tiles an m x n output (n = output columns; swiglu != 0 for the
  * SwiGLU colwise GEMM, whose tiles cover 128 output columns instead of 256).

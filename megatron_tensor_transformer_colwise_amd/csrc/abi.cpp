@@ -342,4 +342,42 @@ tp_status tp_rmsnorm(tp_dtype in_dt, int64_t m, int64_t h, const void* x, const 
                   "tp_rmsnorm");
 }
 
+tp_status tp_shard_sum_rmsnorm(int32_t t, int64_t nrun, int64_t run_rows, int64_t run_stride, int64_t h,
+                               const float* const* partials, const void* residual, tp_dtype residual_dt,
+                               float* out, const float* gain, float eps, void* y, void* stream) {
+  if (t < 0 || t > TP_MAX_SHARDS) return fail(TP_ERR_SHAPE, "t = %d outside 0..%d", t, TP_MAX_SHARDS);
+  if (nrun < 0 || run_rows < 0)
+    return fail(TP_ERR_SHAPE, "nrun = %lld, run_rows = %lld: negative", (long long)nrun, (long long)run_rows);
+  if (nrun > 1 && run_stride < run_rows)
+    return fail(TP_ERR_SHAPE, "run_stride = %lld is below run_rows = %lld", (long long)run_stride,
+                (long long)run_rows);
+  TRY(check_dim8(h, "h"));
+  if (residual && residual_dt != TP_F32 && residual_dt != TP_BF16)
+    return fail(TP_ERR_INVALID_ARG, "unknown residual dtype %d", (int)residual_dt);
+  if (!(eps >= 0.0f)) return fail(TP_ERR_INVALID_ARG, "eps must be >= 0");
+  if (t == 0 && !residual) return fail(TP_ERR_INVALID_ARG, "t = 0 needs a residual");
+  if (!out && !y) return fail(TP_ERR_INVALID_ARG, "out and y are both NULL");
+  if (nrun == 0 || run_rows == 0) return ok();
+  if (nrun > 0x7FFFFFFF / run_rows) return fail(TP_ERR_SHAPE, "nrun * run_rows too large");
+  if (t > 0 && !partials) return fail(TP_ERR_INVALID_ARG, "partials is NULL");
+  for (int i = 0; i < t; ++i) {
+    char name[32];
+    snprintf(name, sizeof(name), "partials[%d]", i);
+    TRY(check_ptr(partials[i], name));
+    if (out && partials[i] == out) return fail(TP_ERR_INVALID_ARG, "out aliases partials[%d]", i);
+  }
+  if (residual) {
+    TRY(check_ptr(residual, "residual"));
+    if (residual == out && residual_dt != TP_F32)
+      return fail(TP_ERR_INVALID_ARG, "out may alias residual only for a float32 residual");
+  }
+  if (out) TRY(check_ptr(out, "out"));
+  if (gain) TRY(check_ptr(gain, "gain"));
+  if (y) TRY(check_ptr(y, "y"));
+  TRY(device_check());
+  return launched(tpk::launch_sum_rmsnorm(t, nrun, run_rows, run_stride, h, partials, residual,
+                                          residual_dt == TP_BF16, out, gain, eps, y, as_stream(stream)),
+                  "tp_shard_sum_rmsnorm");
+}
+
 }  // extern "C"

@@ -56,4 +56,11 @@ hipError_t launch_shard_sum(int t, int64_t n, const float* const* partials, cons
 hipError_t launch_rmsnorm(int in_bf16, int64_t m, int64_t h, const void* x, const float* gain,
                           float eps, void* y, hipStream_t s);
 
+// x = shard-sum of t (0..16) partials (+ residual) over nrun runs of run_rows
+// rows of h (runs run_stride rows apart); out = x if out, y = RMSNorm(x)
+// (bf16) if y; one pass.
+hipError_t launch_sum_rmsnorm(int t, int64_t nrun, int64_t run_rows, int64_t run_stride, int64_t h,
+                              const float* const* partials, const void* residual, int residual_bf16,
+                              float* out, const float* gain, float eps, void* y, hipStream_t s);
+
 }  // namespace tpk

@@ -187,7 +187,16 @@ class AttnShards:
 
 class BlockShards:
     """Pre-norm block, every rank on one device:
-    h1 = X + sum_i Attn_i(RMSNorm(X)); Z = h1 + sum_i MLP_i(RMSNorm(h1))."""
+    h1 = X + sum_i Attn_i(RMSNorm(X)); Z = h1 + sum_i MLP_i(RMSNorm(h1)).
+
+    ``forward`` is the replicated form ("f and g": every rank sums and
+    normalises the whole activation; the sum after attention and the norm
+    before the MLP run as one pass).  ``forward_sp`` is the sequence-parallel
+    form ("Sequence parallelism"): rank r normalises only its Shard(1) slice
+    of every sequence, the sums after each sublayer are reduce-scatters onto
+    those slices, and the slices are gathered before the tensor-parallel
+    layers.  On one device every rank's slice lands in the one shared buffer,
+    which is the all-gather."""
 
     def __init__(self, x, weights: dict, case, t: int | None = None):
         self.case = case
@@ -208,9 +217,59 @@ class BlockShards:
     def norm_mlp(self, stream=None):
         tp.tp_rmsnorm("f32", self.m, self.h, self.attn.out, self.g_mlp, self.case.eps, self.hn, stream)
 
-    def forward(self, stream=None):
+    def sum_norm_mlp(self, stream=None):
+        """h1 = X + sum of the attention partials, and RMSNorm(h1), in one pass."""
+        tp.tp_shard_sum_rmsnorm(self.t, self.m, self.h, list(self.attn.partials), self.x, "bf16",
+                                self.attn.out, self.g_mlp, self.case.eps, self.hn, stream)
+
+    def forward(self, stream=None, fused=True):
         self.norm_attn(stream)
-        self.attn.forward(residual=self.x, residual_dt="bf16", stream=stream)
-        self.norm_mlp(stream)
+        if fused:
+            for r in range(self.t):
+                self.attn.rank(r, stream=stream)
+            self.sum_norm_mlp(stream)
+        else:
+            self.attn.forward(residual=self.x, residual_dt="bf16", stream=stream)
+            self.norm_mlp(stream)
         self.mlp.forward(residual=self.attn.out, residual_dt="f32", stream=stream)
+        return self.mlp.out
+
+    def sp_runs(self) -> tuple[int, int, int]:
+        """(nrun, run_rows, run_stride) of one rank's slice: positions
+        [r S/t, (r+1) S/t) of each of the batch sequences (Shard(1) of
+        (batch, seq, h)); rank r's runs start at row r S/t."""
+        seq, t = self.case.seq, self.t
+        if seq % t:
+            raise ValueError(f"sequence parallelism needs t = {t} to divide the sequence length {seq}")
+        return self.case.batch, seq // t, seq
+
+    def sp_slices(self) -> list[list[tuple[int, int]]]:
+        """Rank r's token rows as (first row, count) runs, one per sequence."""
+        nrun, n, stride = self.sp_runs()
+        return [[(b * stride + r * n, n) for b in range(nrun)] for r in range(self.t)]
+
+    def forward_sp(self, stream=None):
+        t, h, eps = self.t, self.h, self.case.eps
+        runs = self.sp_runs()
+        n = runs[1]
+        ap, mp = self.attn.partials, self.mlp.partials
+        # rank r: the norm of its slice of X, into the shared (gathered) input
+        for r in range(t):
+            o = r * n
+            tp.tp_shard_sum_rmsnorm(0, 0, h, [], self.x[o:], "bf16", None, self.g_attn, eps, self.xn[o:],
+                                    stream, runs=runs)
+        for r in range(t):
+            self.attn.rank(r, stream=stream)
+        # rank r: reduce-scatter onto its slice, + X, and the MLP norm of the slice
+        for r in range(t):
+            o = r * n
+            tp.tp_shard_sum_rmsnorm(t, 0, h, [ap[i][o:] for i in range(t)], self.x[o:], "bf16",
+                                    self.attn.out[o:], self.g_mlp, eps, self.hn[o:], stream, runs=runs)
+        for r in range(t):
+            self.mlp.rank(r, stream=stream)
+        # rank r: reduce-scatter onto its slice, + h1
+        for r in range(t):
+            o = r * n
+            tp.tp_shard_sum_rmsnorm(t, 0, h, [mp[i][o:] for i in range(t)], self.attn.out[o:], "f32",
+                                    self.mlp.out[o:], None, eps, None, stream, runs=runs)
         return self.mlp.out

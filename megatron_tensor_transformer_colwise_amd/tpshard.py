@@ -54,6 +54,8 @@ _SIGS = {
                       ctypes.c_size_t, _vp, _vp],
     "tp_shard_sum": [_i32, _i64, ctypes.POINTER(_vp), _vp, _i32, _vp, _vp],
     "tp_rmsnorm": [_i32, _i64, _i64, _vp, _vp, _f32, _vp, _vp],
+    "tp_shard_sum_rmsnorm": [_i32, _i64, _i64, _i64, _i64, ctypes.POINTER(_vp), _vp, _i32, _vp, _vp, _f32,
+                             _vp, _vp],
     "tp_gemm_plan": [_i64, _i64, _i32, ctypes.POINTER(_i32), ctypes.POINTER(_i32), ctypes.POINTER(_i32)],
     "tp_last_error": [],
     "tp_device_check": [],
@@ -174,3 +176,12 @@ def tp_shard_sum(t, n, partials, residual, residual_dt, out, stream=None) -> Non
 
 def tp_rmsnorm(in_dt, m, h, x, gain, eps, y, stream=None) -> None:
     _check(lib().tp_rmsnorm(_e(in_dt, DTYPES), m, h, _p(x), _p(gain), eps, _p(y), _s(stream)))
+
+
+def tp_shard_sum_rmsnorm(t, m, h, partials, residual, residual_dt, out, gain, eps, y, stream=None,
+                         runs=None) -> None:
+    """m rows (one run), or ``runs = (nrun, run_rows, run_stride)``."""
+    nrun, run_rows, run_stride = runs if runs is not None else (1, m, m)
+    arr = (_vp * max(len(partials), 1))(*[_p(p) for p in partials])
+    _check(lib().tp_shard_sum_rmsnorm(t, nrun, run_rows, run_stride, h, arr, _p(residual),
+                                      _e(residual_dt, DTYPES), _p(out), _p(gain), eps, _p(y), _s(stream)))

@@ -27,6 +27,12 @@ Sources (the "Tensor parallelism" page of itwiki, by section):
   replicated across ranks when there are fewer KV heads than t.
 * "f and g": norms and residual connections are replicated on every rank; a
   block has one sum after attention and one after the MLP.
+* "Sequence parallelism": the norms act on every token alone, so each rank
+  can hold and normalise only its slice of the sequence; the sequence is
+  gathered (all-gather) on entering the tensor-parallel region and, on
+  leaving it, the sum over ranks is taken as a reduce-scatter that leaves
+  each rank the sum for its own slice.  "Writing it in PyTorch": the slice is
+  Shard(1) of a (batch, sequence, hidden) activation, the sequence dimension.
 
 Readings where the pages say nothing (each stated where it is used):
 erf GeLU (the page's example uses PyTorch's default GeLU, which is the erf
@@ -290,3 +296,60 @@ def block(x, w: dict, case, t: int | None = None, rows=None) -> dict:
     mlp_parts = mlp_swiglu_partials(hn, w["W1"], w["W3"], w["W2"], t)
     z = h1 + shard_sum(mlp_parts)
     return {"h1": h1, "z": z, "attn_partials": attn_parts, "mlp_partials": mlp_parts}
+
+
+# --------------------------------------------------------------------------
+# sequence-parallel form ("Sequence parallelism"; "Writing it in PyTorch")
+# --------------------------------------------------------------------------
+
+
+def seq_slices(batch: int, seq: int, t: int) -> list[np.ndarray]:
+    """Token rows (row = b * seq + p) that rank r holds: positions
+    [r seq/t, (r+1) seq/t) of every sequence, the Shard(1) split of a
+    (batch, sequence, hidden) tensor.  Reading: t divides seq, so the slices
+    are equal (the pages give no rule for a remainder)."""
+    if seq % t:
+        raise ValueError(f"sequence length {seq} is not divisible by t = {t}")
+    n = seq // t
+    return [np.concatenate([b * seq + np.arange(r * n, (r + 1) * n) for b in range(batch)])
+            for r in range(t)]
+
+
+def reduce_scatter(partials, slices) -> list[np.ndarray]:
+    """Rank r receives the sum over ranks (ascending) of every partial's rows
+    in its slice."""
+    return [shard_sum([np.asarray(p)[rows] for p in partials]) for rows in slices]
+
+
+def all_gather(pieces, slices, m: int) -> np.ndarray:
+    """Every rank receives the full activation: the ranks' slices put back at
+    their rows."""
+    first = np.asarray(pieces[0])
+    out = np.empty((m,) + first.shape[1:], dtype=np.float64)
+    for rows, piece in zip(slices, pieces):
+        out[rows] = piece
+    return out
+
+
+def sp_block(x, w: dict, case, t: int | None = None) -> dict:
+    """The block with sequence parallelism, rank by rank:
+
+    xn_r = RMSNorm(X[slice_r]);  xn = all-gather(xn_r)
+    h1_r = X[slice_r] + reduce-scatter_r(Attn_i(xn))
+    hn_r = RMSNorm(h1_r);        hn = all-gather(hn_r)
+    Z_r  = h1_r + reduce-scatter_r(MLP_i(hn))
+
+    Returns each rank's slices and the gathered h1 and Z."""
+    t = case.t if t is None else t
+    m = case.tokens
+    x = np.asarray(x, dtype=np.float64)
+    slices = seq_slices(case.batch, case.seq, t)
+    xn = all_gather([rmsnorm(x[rows], w.get("g_attn"), case.eps) for rows in slices], slices, m)
+    attn_parts = [attn_partial(xn, w, case, r, t) for r in range(t)]
+    h1_r = [x[rows] + red for rows, red in zip(slices, reduce_scatter(attn_parts, slices))]
+    hn = all_gather([rmsnorm(h, w.get("g_mlp"), case.eps) for h in h1_r], slices, m)
+    mlp_parts = mlp_swiglu_partials(hn, w["W1"], w["W3"], w["W2"], t)
+    z_r = [h + red for h, red in zip(h1_r, reduce_scatter(mlp_parts, slices))]
+    return {"slices": slices, "h1_slices": h1_r, "z_slices": z_r,
+            "h1": all_gather(h1_r, slices, m), "z": all_gather(z_r, slices, m)}
+

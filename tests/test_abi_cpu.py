@@ -111,6 +111,34 @@ def test_shard_sum_validation(L):
     assert status("tp_shard_sum", 2, 16, ptrs, A16 + 4096, 5, A16 + 8192, None) == tp.TP_ERR_INVALID_ARG
 
 
+def test_shard_sum_rmsnorm_validation(L):
+    ptrs = (ctypes.c_void_p * 17)(*([A16 + 64 * i for i in range(17)]))
+    out, y = A16 + 8192, A16 + 16384
+
+    def call(t, h=16, res=None, rdt=0, o=out, g=None, eps=1e-5, yy=y, runs=(1, 4, 4), arr=ptrs):
+        return status("tp_shard_sum_rmsnorm", t, runs[0], runs[1], runs[2], h, arr, res, rdt, o, g, eps, yy, None)
+
+    assert call(-1) == tp.TP_ERR_SHAPE
+    assert call(17) == tp.TP_ERR_SHAPE
+    assert call(2, runs=(-1, 4, 4)) == tp.TP_ERR_SHAPE
+    assert call(2, runs=(2, 4, 3)) == tp.TP_ERR_SHAPE                # runs overlap
+    assert "run_stride" in tp.tp_last_error()
+    assert call(2, h=12) == tp.TP_ERR_SHAPE                          # h not a multiple of 8
+    assert call(2, eps=-1.0) == tp.TP_ERR_INVALID_ARG
+    assert call(2, o=A16) == tp.TP_ERR_INVALID_ARG                   # out aliases partials[0]
+    assert "aliases partials[0]" in tp.tp_last_error()
+    assert call(2, res=out, rdt=1) == tp.TP_ERR_INVALID_ARG          # bf16 residual aliased by out
+    assert call(2, res=A16 + 4096, rdt=7) == tp.TP_ERR_INVALID_ARG    # unknown residual dtype
+    assert call(2, g=MIS) == tp.TP_ERR_INVALID_ARG                   # misaligned gain
+    assert call(0) == tp.TP_ERR_INVALID_ARG                          # no partials and no residual
+    assert "needs a residual" in tp.tp_last_error()
+    assert call(2, o=None, yy=None) == tp.TP_ERR_INVALID_ARG         # nothing to write
+    assert call(2, arr=None) == tp.TP_ERR_INVALID_ARG
+    # nothing to do: OK without touching pointers or the device
+    assert call(2, runs=(0, 4, 4), o=None, yy=y, arr=None) == tp.TP_OK
+    assert call(2, runs=(3, 0, 4), arr=None) == tp.TP_OK
+
+
 def test_rmsnorm_validation(L):
     assert status("tp_rmsnorm", 1, 4, 12, A16, None, 1e-5, A16, None) == tp.TP_ERR_SHAPE
     assert status("tp_rmsnorm", 3, 4, 16, A16, None, 1e-5, A16, None) == tp.TP_ERR_INVALID_ARG
@@ -174,3 +202,21 @@ def test_sharding_layouts():
     assert torch.equal(r.w_qkv[2 * d:3 * d], wk[:, d:2 * d].t())
     assert torch.equal(r.w_qkv[3 * d:], wv[:, d:2 * d].t())
     assert torch.equal(r.w_o, wo[6 * d:8 * d].t())
+
+
+def test_sequence_parallel_slices_host():
+    """Rank r's runs are positions [r S/t, (r+1) S/t) of every sequence; a
+    sequence length that t does not divide is refused (host-only)."""
+    from megatron_tensor_transformer_colwise_amd import inputs
+
+    case = inputs.BlockCase("sp_host", batch=3, seq=8, hidden=16, heads=4, kv_heads=2, head_dim=128,
+                            inter=32, t=4, rope_base=500000.0, seed=1)
+    w = {k: v.torch() for k, v in inputs.gen_block(case).items()}
+    blk = shard.BlockShards(w["X"], w, case)
+    assert blk.sp_slices()[1] == [(2, 2), (10, 2), (18, 2)]
+    blk2 = shard.BlockShards(w["X"], w, inputs.BlockCase("sp_host2", batch=1, seq=6, hidden=16, heads=4,
+                                                         kv_heads=2, head_dim=128, inter=32, t=4,
+                                                         rope_base=500000.0, seed=1))
+    with pytest.raises(ValueError):
+        blk2.sp_slices()
+

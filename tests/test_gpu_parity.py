@@ -384,6 +384,122 @@ def test_rmsnorm(device, in_dt, m, h, gain):
     assert np.all(np.abs(got - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-6)
 
 
+@pytest.mark.parametrize("t,m,h,res,gain", [(8, 37, 8192, "bf16", True), (1, 5, 136, None, False),
+                                             (3, 300, 4096, "f32", True), (16, 3, 16392, "f32", False),
+                                             (2, 1, 24, "bf16", False)])
+def test_shard_sum_rmsnorm(device, t, m, h, res, gain):
+    """The fused sum + norm: the sum is bit-exact to the oracle's float32
+    shard-sum, the normed rows bitwise those of tp_shard_sum then tp_rmsnorm
+    (and within one bf16 rounding of the float64 norm of that sum); h beyond
+    8192 reads back the stored sums."""
+    say(f"case shard_sum_rmsnorm t={t} m={m} h={h} res={res} gain={gain}")
+    parts = [inputs.normal(53, s, (m, h), 1.0, "f32").data for s in range(t)]
+    dparts = [torch.from_numpy(p).to(device) for p in parts]
+    r_host = r_dev = None
+    if res is not None:
+        rt = inputs.normal(53, 99, (m, h), 1.0, res)
+        r_host, r_dev = rt.f32(), to_dev(rt, device)
+    gv = (inputs.normal(53, 100, (h,), 0.1, "f32").data + np.float32(1)) if gain else None
+    g_dev = None if gv is None else torch.from_numpy(gv).to(device)
+    out = torch.empty(m, h, dtype=torch.float32, device=device)
+    y = torch.empty(m, h, dtype=torch.bfloat16, device=device)
+    tp.tp_shard_sum_rmsnorm(t, m, h, dparts, r_dev, res or "f32", out, g_dev, 1e-5, y)
+    out2 = torch.empty_like(out)
+    y2 = torch.empty_like(y)
+    tp.tp_shard_sum(t, m * h, dparts, r_dev, res or "f32", out2)
+    tp.tp_rmsnorm("f32", m, h, out2, g_dev, 1e-5, y2)
+    torch.cuda.synchronize()
+    ref_sum = oracle.shard_sum_f32(parts, r_host)
+    assert np.array_equal(out.cpu().numpy(), ref_sum)
+    assert torch.equal(y, y2)
+    ref = oracle.rmsnorm(ref_sum.astype(np.float64), None if gv is None else gv.astype(np.float64), 1e-5)
+    assert np.all(np.abs(host(y) - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-6)
+
+
+def test_shard_sum_rmsnorm_in_place_residual(device):
+    """out may be the float32 residual itself (the residual stream updated in place)."""
+    say("case shard_sum_rmsnorm in place")
+    t, m, h = 4, 64, 1024
+    parts = [inputs.normal(54, s, (m, h), 1.0, "f32").data for s in range(t)]
+    dparts = [torch.from_numpy(p).to(device) for p in parts]
+    r = inputs.normal(54, 99, (m, h), 1.0, "f32").data
+    acc = torch.from_numpy(r.copy()).to(device)
+    y = torch.empty(m, h, dtype=torch.bfloat16, device=device)
+    tp.tp_shard_sum_rmsnorm(t, m, h, dparts, acc, "f32", acc, None, 1e-5, y)
+    torch.cuda.synchronize()
+    assert np.array_equal(acc.cpu().numpy(), oracle.shard_sum_f32(parts, r))
+
+
+@pytest.mark.parametrize("t", [4, 12])
+def test_shard_sum_rmsnorm_runs(device, t):
+    """Rank slices as runs (positions [r S/t, (r+1) S/t) of every sequence): the
+    norm alone (t = 0), the reduce-scatter with norm, and the reduce-scatter
+    alone each write exactly their rows, bitwise equal to the whole-matrix
+    calls, and leave every other row alone."""
+    say(f"case shard_sum_rmsnorm runs t={t}")
+    batch, seq, h = 3, 48, 264
+    m, n = batch * seq, seq // t
+    parts = torch.stack([torch.from_numpy(inputs.normal(55, s, (m, h), 1.0, "f32").data) for s in range(t)]).to(device)
+    x = to_dev(inputs.normal(55, 99, (m, h), 1.0, "bf16"), device)
+    g = torch.from_numpy(inputs.normal(55, 100, (h,), 0.1, "f32").data + np.float32(1)).to(device)
+    # whole-matrix references
+    xn_ref = torch.empty(m, h, dtype=torch.bfloat16, device=device)
+    tp.tp_rmsnorm("bf16", m, h, x, g, 1e-5, xn_ref)
+    h1_ref = torch.empty(m, h, device=device)
+    hn_ref = torch.empty(m, h, dtype=torch.bfloat16, device=device)
+    tp.tp_shard_sum_rmsnorm(t, m, h, list(parts), x, "bf16", h1_ref, g, 1e-5, hn_ref)
+    z_ref = torch.empty(m, h, device=device)
+    tp.tp_shard_sum(t, m * h, list(parts), h1_ref, "f32", z_ref)
+    # per-rank runs, into buffers prefilled with a sentinel
+    sent = float("nan")
+    xn = torch.full((m, h), sent, dtype=torch.bfloat16, device=device)
+    h1 = torch.full((m, h), sent, device=device)
+    hn = torch.full((m, h), sent, dtype=torch.bfloat16, device=device)
+    z = torch.full((m, h), sent, device=device)
+    runs = (batch, n, seq)
+    for r in range(t):
+        o = r * n
+        tp.tp_shard_sum_rmsnorm(0, 0, h, [], x[o:], "bf16", None, g, 1e-5, xn[o:], runs=runs)
+        tp.tp_shard_sum_rmsnorm(t, 0, h, [parts[i][o:] for i in range(t)], x[o:], "bf16", h1[o:], g, 1e-5,
+                                hn[o:], runs=runs)
+        tp.tp_shard_sum_rmsnorm(t, 0, h, [parts[i][o:] for i in range(t)], h1[o:], "f32", z[o:], None, 1e-5,
+                                None, runs=runs)
+        if r == 0:  # after rank 0 alone, only its rows are written
+            torch.cuda.synchronize()
+            rows0 = np.concatenate([b * seq + np.arange(n) for b in range(batch)])
+            others = np.setdiff1d(np.arange(m), rows0)
+            assert torch.isnan(xn[others].float()).all() and torch.isnan(z[others]).all()
+            assert not torch.isnan(xn[rows0].float()).any() and not torch.isnan(z[rows0]).any()
+    torch.cuda.synchronize()
+    assert torch.equal(xn, xn_ref) and torch.equal(h1, h1_ref) and torch.equal(hn, hn_ref)
+    assert torch.equal(z, z_ref)
+    assert np.array_equal(h1.cpu().numpy(), oracle.shard_sum_f32([p.cpu().numpy() for p in parts],
+                                                                 inputs.normal(55, 99, (m, h), 1.0, "bf16").f32()))
+
+
+def test_sequence_parallel_block(device):
+    """The sequence-parallel block (norms on each rank's Shard(1) slices,
+    reduce-scatter + norm per slice, shared gathered inputs) against the
+    oracle's sequence-parallel block, and bitwise equal to the replicated
+    forms (fused and two-pass)."""
+    case = inputs.BlockCase("sp_block", batch=2, seq=192, hidden=512, heads=8, kv_heads=2,
+                            head_dim=128, inter=1024, t=4, rope_base=500000.0, seed=71, gain_std=0.1)
+    say(f"case sequence-parallel block {case}")
+    w = inputs.gen_block(case)
+    dw = {k: to_dev(v, device) for k, v in w.items()}
+    blk = shard.BlockShards(dw["X"], dw, case)
+    z_sp = blk.forward_sp().clone()
+    h1_sp = blk.attn.out.clone()
+    z_rep = blk.forward().clone()
+    z_two = blk.forward(fused=False).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(z_sp, z_rep) and torch.equal(z_rep, z_two)
+    W = {k: v.f64() for k, v in w.items()}
+    ref = oracle.sp_block(W["X"], W, case)
+    assert rel_err(host(h1_sp), ref["h1"]) <= BF16_TOL
+    assert rel_err(host(z_sp), ref["z"]) <= BF16_TOL
+
+
 # ---------------------------------------------------------------- determinism
 
 
@@ -485,10 +601,12 @@ def test_config_70b_block(device, block70b, t):
     t0 = time.time()
     dw = {k: to_dev(v, device) for k, v in w.items()}
     blk = shard.BlockShards(dw["X"], dw, case, t=t)
-    z = blk.forward()
+    z = blk.forward().clone()
     torch.cuda.synchronize()
     assert rel_err(host(blk.attn.out, rows), ref["h1"]) <= BF16_TOL
     assert rel_err(host(z, rows), ref["z"]) <= BF16_TOL
+    # the sequence-parallel form of the same block: bitwise the same result
+    assert torch.equal(blk.forward_sp(), z)
     say(f"  done in {time.time() - t0:.1f}s")
 
 

@@ -351,6 +351,55 @@ def test_block_is_t_invariant():
     assert np.max(np.abs(zs - ref[rows])) < 1e-12
 
 
+def test_sequence_slices_are_shard1():
+    """Rank r's rows are positions [r S/t, (r+1) S/t) of every sequence (Shard(1)
+    of (batch, sequence, hidden)); the slices partition the tokens; with one
+    sequence they are contiguous row ranges."""
+    for batch, seq, t in [(1, 16, 4), (3, 8, 2), (2, 12, 3), (4, 2048, 8)]:
+        sl = oracle.seq_slices(batch, seq, t)
+        assert len(sl) == t
+        assert np.array_equal(np.sort(np.concatenate(sl)), np.arange(batch * seq))
+        n = seq // t
+        for r, rows in enumerate(sl):
+            assert len(rows) == batch * n
+            assert np.array_equal(rows // seq, np.repeat(np.arange(batch), n))
+            assert np.array_equal(rows % seq, np.tile(np.arange(r * n, (r + 1) * n), batch))
+    assert np.array_equal(oracle.seq_slices(1, 16, 4)[2], np.arange(8, 12))
+    with pytest.raises(ValueError):
+        oracle.seq_slices(2, 10, 4)
+
+
+def test_reduce_scatter_then_all_gather_is_the_all_reduce():
+    """All-reduce = reduce-scatter + all-gather: gathering the per-rank sums of
+    the slices gives the full ascending-rank sum exactly."""
+    r = np.random.default_rng(5)
+    batch, seq, h, t = 3, 8, 16, 4
+    parts = [r.standard_normal((batch * seq, h)) for _ in range(t)]
+    sl = oracle.seq_slices(batch, seq, t)
+    pieces = oracle.reduce_scatter(parts, sl)
+    for rows, piece in zip(sl, pieces):
+        assert np.array_equal(piece, oracle.shard_sum(parts)[rows])
+    assert np.array_equal(oracle.all_gather(pieces, sl, batch * seq), oracle.shard_sum(parts))
+
+
+@pytest.mark.parametrize("t", [2, 4, 8])
+def test_sequence_parallel_block_equals_replicated(t):
+    """The sequence-parallel block (norms on slices, reduce-scatter, all-gather)
+    gives exactly the replicated block's h1 and Z: every step it changes acts
+    row by row, and the gathered inputs of the tensor-parallel layers are the
+    replicated ones bit for bit."""
+    case = inputs.BlockCase("tinyblock_sp", batch=2, seq=8, hidden=32, heads=8, kv_heads=2,
+                            head_dim=4, inter=64, t=t, rope_base=10000.0, seed=17, gain_std=0.1,
+                            dtype="f32", w_std=0.2)
+    w = {k: v.f64() for k, v in inputs.gen_block(case).items()}
+    ref = oracle.block(w["X"], w, case, t=t)
+    sp = oracle.sp_block(w["X"], w, case, t=t)
+    assert np.array_equal(sp["h1"], ref["h1"])
+    assert np.array_equal(sp["z"], ref["z"])
+    for rows, z in zip(sp["slices"], sp["z_slices"]):
+        assert np.array_equal(z, ref["z"][rows])
+
+
 # ---------------------------------------------------------------- inputs
 
 
