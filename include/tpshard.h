@@ -85,13 +85,18 @@ typedef enum tp_act {
  *   w  [n, k]      rank i's weight A_i^T                     (act NONE, GELU)
  *      [2n, k]     [W1_i^T ; W3_i^T]: the rank's gate rows then its up rows,
  *                  each block sliced from its own tensor   (act SWIGLU)
- *   y  [m, n]      rank i's output slice Y_i (dt)
+ *   bias [n] float32, or [2n] (the gate biases then the up biases, SWIGLU),
+ *                  or NULL: rank i's slice of the layer's bias, added before
+ *                  the nonlinearity (a column-parallel layer shards its bias
+ *                  with its output features: transformers "Tensor
+ *                  parallelism" page, partitioning table and DTensor example)
+ *   y  [m, n]      rank i's output slice Y_i = act(x A_i + b_i) (dt)
  *
  * dt is TP_BF16 (bf16 in and out, float32 accumulate) or TP_F32 (float32 in,
  * out and arithmetic; meant for small checks).
  * ------------------------------------------------------------------------ */
 tp_status tp_colwise(tp_act act, tp_dtype dt, int64_t m, int64_t k, int64_t n,
-                     const void* x, const void* w, void* y, void* stream);
+                     const void* x, const void* w, const float* bias, void* y, void* stream);
 
 /* --------------------------------------------------------------------------
  * Row-parallel linear to a float32 partial sum ("Matmul split").
@@ -103,6 +108,21 @@ tp_status tp_colwise(tp_act act, tp_dtype dt, int64_t m, int64_t k, int64_t n,
  * ------------------------------------------------------------------------ */
 tp_status tp_rowwise(tp_dtype dt, int64_t m, int64_t k, int64_t n,
                      const void* y, const void* w, float* partial, void* stream);
+
+/* --------------------------------------------------------------------------
+ * Row-parallel linear over a replicated input ("rowwise_split_input" of the
+ * diffusers tensor-parallel guide, style table: the weight is split along
+ * its input features and each rank computes its partial sum from its own
+ * slice of the replicated input; the sum over ranks is the layer output).
+ *
+ *   x        [m, k]      the replicated input (dt); rank r reads its columns
+ *                        [r k/t, (r+1) k/t) in place (no copy)
+ *   w        [n, k/t]    the rank's weight columns (nn.Linear dim 1 sliced)
+ *   partial  [m, n]      float32, overwritten with the rank's share
+ * k / t must be a multiple of 8.
+ * ------------------------------------------------------------------------ */
+tp_status tp_rowwise_split_input(tp_dtype dt, int64_t m, int64_t k, int64_t n, int32_t t, int32_t rank,
+                                 const void* x, const void* w, float* partial, void* stream);
 
 /* --------------------------------------------------------------------------
  * One rank's MLP: tp_colwise(act) then tp_rowwise ("MLP" section).
@@ -149,12 +169,14 @@ tp_status tp_shard_mlp_group(tp_act act, tp_dtype dt, int32_t t, int64_t m, int6
  *   vt     [batch, hkv, d, seq_pad]  (x Wv_i) transposed per sequence and
  *                           head, seq_pad = seq rounded up to 64; columns
  *                           >= seq are written as zero
+ *   bias   [(hq + 2 hkv) * d] float32 or NULL: the rank's q, k, v biases in
+ *                           the order of w_qkv's rows, added before RoPE
  * RoPE rotates the pair (c, c + d/2) of every head by the angle
  * pos * rope_base^(-2c/d) (rotate-half form).  d must be 128.
  * ------------------------------------------------------------------------ */
 tp_status tp_qkv_rope(int64_t batch, int64_t seq, int64_t h, int32_t hq, int32_t hkv,
                       int32_t head_dim, float rope_base, const void* x, const void* w_qkv,
-                      void* q, void* k, void* vt, void* stream);
+                      const float* bias, void* q, void* k, void* vt, void* stream);
 
 /* --------------------------------------------------------------------------
  * Attention of one rank's heads ("Self-attention" section), bf16 only.
@@ -213,12 +235,15 @@ tp_status tp_rmsnorm(tp_dtype in_dt, int64_t m, int64_t h, const void* x, const 
 /* --------------------------------------------------------------------------
  * The sum that ends a sublayer and the norm that opens the next one, in one
  * pass over rows of h:
- *   x   = ((partials[0] + partials[1]) + ... + partials[t-1]) + residual
- *         (t = 0: the residual alone)
+ *   x   = (((partials[0] + partials[1]) + ... + partials[t-1]) + bias) + residual
+ *         (t = 0: the residual alone; bias, when given, is the row-parallel
+ *         layer's bias, added once after the sum: transformers "Tensor
+ *         parallelism" page, RowwiseParallel replicates the bias and adds it
+ *         after the reduction)
  *   out = x                                                 (float32, if out)
  *   y   = bf16( x / sqrt(mean_c x^2 + eps) * gain )  per row   (if y)
- * with tp_shard_sum's and tp_rmsnorm's arithmetic exactly, so the results
- * are bitwise those of those calls, and without reading out back.
+ * with tp_shard_sum's and tp_rmsnorm's arithmetic exactly (with no bias the
+ * results are bitwise those of those calls), and without reading out back.
  *
  * The rows are nrun runs of run_rows consecutive rows, the first rows of
  * consecutive runs run_stride rows apart (run_stride is ignored for one
@@ -240,14 +265,16 @@ tp_status tp_rmsnorm(tp_dtype in_dt, int64_t m, int64_t h, const void* x, const 
  *
  *   t          0 .. 16
  *   partials   HOST array of t device pointers, float32 rows
+ *   bias       [h] float32 or NULL (t >= 1)
  *   residual   rows of residual_dt (TP_F32 or TP_BF16), or NULL (t >= 1)
  *   out        float32 rows or NULL; may alias a float32 residual, not a partial
  *   gain       [h] float32 or NULL (all ones); y bf16 rows or NULL
  *   out and y may not both be NULL.
  * ------------------------------------------------------------------------ */
 tp_status tp_shard_sum_rmsnorm(int32_t t, int64_t nrun, int64_t run_rows, int64_t run_stride, int64_t h,
-                               const float* const* partials, const void* residual, tp_dtype residual_dt,
-                               float* out, const float* gain, float eps, void* y, void* stream);
+                               const float* const* partials, const float* bias, const void* residual,
+                               tp_dtype residual_dt, float* out, const float* gain, float eps, void* y,
+                               void* stream);
 
 /* --------------------------------------------------------------------------
  * Introspection: how the bf16 GEMM behind tp_colwise / tp_rowwise /

@@ -163,16 +163,17 @@ tp_status tp_device_check(void) {
 }
 
 tp_status tp_colwise(tp_act act, tp_dtype dt, int64_t m, int64_t k, int64_t n, const void* x,
-                     const void* w, void* y, void* stream) {
+                     const void* w, const float* bias, void* y, void* stream) {
   TRY(check_gemm(act, dt, m, k, n, x, w, y, "x", "w", "y"));
   if (m == 0) return ok();
+  if (bias) TRY(check_ptr(bias, "bias"));
   TRY(device_check());
   hipError_t e;
   if (dt == TP_BF16)
-    e = tpk::launch_gemm_bf16(epi_of(act), m, n, k, x, w, y, nullptr, as_stream(stream));
+    e = tpk::launch_gemm_bf16(epi_of(act), m, n, k, x, w, y, nullptr, as_stream(stream), bias);
   else
     e = tpk::launch_gemm_f32(epi_of(act), m, n, k, static_cast<const float*>(x),
-                             static_cast<const float*>(w), static_cast<float*>(y), as_stream(stream));
+                             static_cast<const float*>(w), static_cast<float*>(y), as_stream(stream), bias);
   return launched(e, "tp_colwise");
 }
 
@@ -190,6 +191,29 @@ tp_status tp_rowwise(tp_dtype dt, int64_t m, int64_t k, int64_t n, const void* y
   return launched(e, "tp_rowwise");
 }
 
+tp_status tp_rowwise_split_input(tp_dtype dt, int64_t m, int64_t k, int64_t n, int32_t t, int32_t rank,
+                                 const void* x, const void* w, float* partial, void* stream) {
+  if (t < 1 || t > TP_MAX_SHARDS) return fail(TP_ERR_SHAPE, "t = %d outside 1..%d", t, TP_MAX_SHARDS);
+  if (rank < 0 || rank >= t) return fail(TP_ERR_SHAPE, "rank = %d outside 0..%d", rank, t - 1);
+  TRY(check_dim8(k, "k"));
+  if (k % t != 0 || (k / t) % 8 != 0)
+    return fail(TP_ERR_SHAPE, "k / t = %lld / %d must be a whole multiple of 8", (long long)k, t);
+  const int64_t ks = k / t;
+  TRY(check_gemm(TP_ACT_NONE, dt, m, ks, n, x, w, partial, "x", "w", "partial"));
+  const int64_t esz = dt == TP_BF16 ? 2 : 4;
+  if (dt == TP_BF16 && 256 * k * esz >= kMaxOffset) return fail(TP_ERR_SHAPE, "k = %lld too large", (long long)k);
+  if (m == 0) return ok();
+  TRY(device_check());
+  const char* xs = static_cast<const char*>(x) + rank * ks * esz;  // the rank's input columns
+  hipError_t e;
+  if (dt == TP_BF16)
+    e = tpk::launch_gemm_bf16(tpk::EPI_F32, m, n, ks, xs, w, partial, nullptr, as_stream(stream), nullptr, k);
+  else
+    e = tpk::launch_gemm_f32(tpk::EPI_F32, m, n, ks, reinterpret_cast<const float*>(xs),
+                             static_cast<const float*>(w), partial, as_stream(stream), nullptr, k);
+  return launched(e, "tp_rowwise_split_input");
+}
+
 tp_status tp_shard_mlp(tp_act act, tp_dtype dt, int64_t m, int64_t h, int64_t f_shard,
                        const void* x, const void* w_in, const void* w_out, void* act_ws,
                        float* partial, void* stream) {
@@ -197,7 +221,7 @@ tp_status tp_shard_mlp(tp_act act, tp_dtype dt, int64_t m, int64_t h, int64_t f_
     return fail(TP_ERR_INVALID_ARG, "tp_shard_mlp needs GELU or SWIGLU, got %d", (int)act);
   TRY(check_gemm(act, dt, m, h, f_shard, x, w_in, act_ws, "x", "w_in", "act_ws"));
   TRY(check_gemm(TP_ACT_NONE, dt, m, f_shard, h, act_ws, w_out, partial, "act_ws", "w_out", "partial"));
-  TRY(tp_colwise(act, dt, m, h, f_shard, x, w_in, act_ws, stream));
+  TRY(tp_colwise(act, dt, m, h, f_shard, x, w_in, nullptr, act_ws, stream));
   return tp_rowwise(dt, m, f_shard, h, act_ws, w_out, partial, stream);
 }
 
@@ -234,8 +258,8 @@ tp_status tp_shard_mlp_group(tp_act act, tp_dtype dt, int32_t t, int64_t m, int6
 }
 
 tp_status tp_qkv_rope(int64_t batch, int64_t seq, int64_t h, int32_t hq, int32_t hkv,
-                      int32_t head_dim, float rope_base, const void* x, const void* w_qkv, void* q,
-                      void* k, void* vt, void* stream) {
+                      int32_t head_dim, float rope_base, const void* x, const void* w_qkv,
+                      const float* bias, void* q, void* k, void* vt, void* stream) {
   TRY(check_attn_shape(batch, seq, hq, hkv, head_dim));
   if (!(rope_base > 1.0f)) return fail(TP_ERR_INVALID_ARG, "rope_base must be > 1");
   const int64_t n = (int64_t)(hq + 2 * hkv) * head_dim;
@@ -244,6 +268,7 @@ tp_status tp_qkv_rope(int64_t batch, int64_t seq, int64_t h, int32_t hq, int32_t
   if (m == 0) return ok();
   TRY(check_ptr(k, "k"));
   TRY(check_ptr(vt, "vt"));
+  if (bias) TRY(check_ptr(bias, "bias"));
   TRY(device_check());
   tpk::QkvOut o;
   o.q = q;
@@ -254,7 +279,7 @@ tp_status tp_qkv_rope(int64_t batch, int64_t seq, int64_t h, int32_t hq, int32_t
   o.hq = hq;
   o.hkv = hkv;
   o.log2_base = log2f(rope_base);
-  return launched(tpk::launch_gemm_bf16(tpk::EPI_QKV, m, n, h, x, w_qkv, nullptr, &o, as_stream(stream)),
+  return launched(tpk::launch_gemm_bf16(tpk::EPI_QKV, m, n, h, x, w_qkv, nullptr, &o, as_stream(stream), bias),
                   "tp_qkv_rope");
 }
 
@@ -293,7 +318,7 @@ tp_status tp_shard_attn(int64_t batch, int64_t seq, int64_t h, int32_t hq, int32
   if (ws_bytes < L.total)
     return fail(TP_ERR_WORKSPACE, "workspace of %zu bytes < %zu needed", ws_bytes, L.total);
   char* base = static_cast<char*>(ws);
-  TRY(tp_qkv_rope(batch, seq, h, hq, hkv, head_dim, rope_base, x, w_qkv, base + L.q, base + L.k,
+  TRY(tp_qkv_rope(batch, seq, h, hq, hkv, head_dim, rope_base, x, w_qkv, nullptr, base + L.q, base + L.k,
                   base + L.vt, stream));
   TRY(tp_flash_attn(batch, seq, hq, hkv, head_dim, causal, base + L.q, base + L.k, base + L.vt,
                     base + L.o, stream));
@@ -343,8 +368,9 @@ tp_status tp_rmsnorm(tp_dtype in_dt, int64_t m, int64_t h, const void* x, const 
 }
 
 tp_status tp_shard_sum_rmsnorm(int32_t t, int64_t nrun, int64_t run_rows, int64_t run_stride, int64_t h,
-                               const float* const* partials, const void* residual, tp_dtype residual_dt,
-                               float* out, const float* gain, float eps, void* y, void* stream) {
+                               const float* const* partials, const float* bias, const void* residual,
+                               tp_dtype residual_dt, float* out, const float* gain, float eps, void* y,
+                               void* stream) {
   if (t < 0 || t > TP_MAX_SHARDS) return fail(TP_ERR_SHAPE, "t = %d outside 0..%d", t, TP_MAX_SHARDS);
   if (nrun < 0 || run_rows < 0)
     return fail(TP_ERR_SHAPE, "nrun = %lld, run_rows = %lld: negative", (long long)nrun, (long long)run_rows);
@@ -356,6 +382,7 @@ tp_status tp_shard_sum_rmsnorm(int32_t t, int64_t nrun, int64_t run_rows, int64_
     return fail(TP_ERR_INVALID_ARG, "unknown residual dtype %d", (int)residual_dt);
   if (!(eps >= 0.0f)) return fail(TP_ERR_INVALID_ARG, "eps must be >= 0");
   if (t == 0 && !residual) return fail(TP_ERR_INVALID_ARG, "t = 0 needs a residual");
+  if (t == 0 && bias) return fail(TP_ERR_INVALID_ARG, "a bias needs partials to follow");
   if (!out && !y) return fail(TP_ERR_INVALID_ARG, "out and y are both NULL");
   if (nrun == 0 || run_rows == 0) return ok();
   if (nrun > 0x7FFFFFFF / run_rows) return fail(TP_ERR_SHAPE, "nrun * run_rows too large");
@@ -372,10 +399,11 @@ tp_status tp_shard_sum_rmsnorm(int32_t t, int64_t nrun, int64_t run_rows, int64_
       return fail(TP_ERR_INVALID_ARG, "out may alias residual only for a float32 residual");
   }
   if (out) TRY(check_ptr(out, "out"));
+  if (bias) TRY(check_ptr(bias, "bias"));
   if (gain) TRY(check_ptr(gain, "gain"));
   if (y) TRY(check_ptr(y, "y"));
   TRY(device_check());
-  return launched(tpk::launch_sum_rmsnorm(t, nrun, run_rows, run_stride, h, partials, residual,
+  return launched(tpk::launch_sum_rmsnorm(t, nrun, run_rows, run_stride, h, partials, bias, residual,
                                           residual_dt == TP_BF16, out, gain, eps, y, as_stream(stream)),
                   "tp_shard_sum_rmsnorm");
 }

@@ -101,6 +101,8 @@ struct Args {
   const bf16_t* w[MAX_GROUP];
   void* out[MAX_GROUP];
   int64_t M, N, K;
+  int64_t lda;        // row stride of x in elements (>= K; a column slice when > K)
+  const float* bias;  // per output column, added before the epilogue's nonlinearity, or NULL
   int num_bm;  // tile rows of this launch (height BMT)
   int num_bn;  // tile columns of this launch
   int bn0;     // first tile column of this launch
@@ -156,13 +158,14 @@ __global__ __launch_bounds__((Cfg<BMT, W4>::NW * 64), 1) void gemm_bf16_kernel(A
   bm = __builtin_amdgcn_readfirstlane(bm);
   bn = __builtin_amdgcn_readfirstlane(bn + args.bn0);
 
-  const int64_t M = args.M, N = args.N, K = args.K;
+  const int64_t M = args.M, N = args.N, K = args.K, lda = args.lda;
   const int64_t m0 = (int64_t)bm * BMT;
-  const uint32_t row_bytes = (uint32_t)(K * 2);
+  const uint32_t row_bytes = (uint32_t)(K * 2);     // a weight row
+  const uint32_t a_row_bytes = (uint32_t)(lda * 2);  // an x row (its first K columns are read)
 
   // ---- global -> LDS addressing -------------------------------------------
   const int m_rows = (int)min<int64_t>(BMT, M - m0);
-  __amdgpu_buffer_rsrc_t rsrc_a = make_rsrc(xg + m0 * K, (uint32_t)m_rows * row_bytes);
+  __amdgpu_buffer_rsrc_t rsrc_a = make_rsrc(xg + m0 * lda, (uint32_t)m_rows * a_row_bytes);
 
   __amdgpu_buffer_rsrc_t rsrc_b;
   int n_valid;  // valid weight rows (plain) or valid output columns (SwiGLU)
@@ -187,7 +190,7 @@ __global__ __launch_bounds__((Cfg<BMT, W4>::NW * 64), 1) void gemm_bf16_kernel(A
     const int r = slot / CH;
     const int c = (slot % CH) ^ swz(r);
     a_k[j] = c * 8;
-    a_off[j] = (uint32_t)r * row_bytes + (uint32_t)c * 16;
+    a_off[j] = (uint32_t)r * a_row_bytes + (uint32_t)c * 16;
   }
 #pragma unroll
   for (int j = 0; j < C::LB; ++j) {
@@ -519,6 +522,14 @@ __global__ __launch_bounds__((Cfg<BMT, W4>::NW * 64), 1) void gemm_bf16_kernel(A
       }
   } else if (EPI == EPI_BF16 || EPI == EPI_GELU) {
     const int64_t col_base = (int64_t)bn * BN + cq;
+    // the bias of each block's column of this lane (before the transpose);
+    // -0 is the identity of the float add, so no bias leaves results as they were
+    float bcol[NJ];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int64_t c = (int64_t)bn * BN + col_block<NJ>(wn, j) * 32 + l31;
+      bcol[j] = (args.bias && c < N) ? args.bias[c] : -0.0f;
+    }
 #pragma unroll
     for (int i = 0; i < MI; ++i)
 #pragma unroll
@@ -529,7 +540,7 @@ __global__ __launch_bounds__((Cfg<BMT, W4>::NW * 64), 1) void gemm_bf16_kernel(A
           float v[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            v[e] = acc[i][j][4 * g + e];
+            v[e] = acc[i][j][4 * g + e] + bcol[j];
             if (EPI == EPI_GELU) v[e] = gelu_erf(v[e]);
           }
           quad_transpose(v, q);
@@ -541,6 +552,15 @@ __global__ __launch_bounds__((Cfg<BMT, W4>::NW * 64), 1) void gemm_bf16_kernel(A
       }
   } else if (EPI == EPI_SWIGLU) {
     const int64_t col_base = (int64_t)bn * (BN / 2) + hg * 64 + cq;
+    // gate and up biases of this lane's output column of each pair (bias
+    // holds the N gate biases, then the N up biases); -0 when there is none
+    float bg[NP], bu[NP];
+#pragma unroll
+    for (int j = 0; j < NP; ++j) {
+      const int64_t o = (int64_t)bn * (BN / 2) + hg * 64 + pair_col(j) + l31;
+      bg[j] = (args.bias && o < N) ? args.bias[o] : -0.0f;
+      bu[j] = (args.bias && o < N) ? args.bias[N + o] : -0.0f;
+    }
 #pragma unroll
     for (int i = 0; i < MI; ++i)
 #pragma unroll
@@ -550,7 +570,8 @@ __global__ __launch_bounds__((Cfg<BMT, W4>::NW * 64), 1) void gemm_bf16_kernel(A
         for (int g = 0; g < 4; ++g) {
           float v[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = silu_fast(acc[i][j][4 * g + e]) * acc[i][j + NP][4 * g + e];
+          for (int e = 0; e < 4; ++e)
+            v[e] = silu_fast(acc[i][j][4 * g + e] + bg[j]) * (acc[i][j + NP][4 * g + e] + bu[j]);
           quad_transpose(v, q);
           const int64_t row = row_base + i * 32 + 8 * g + q;
           if (row < M && col < N)
@@ -600,6 +621,14 @@ __global__ __launch_bounds__((Cfg<BMT, W4>::NW * 64), 1) void gemm_bf16_kernel(A
       // first angle is evaluated that way and the next three follow by
       // rotating it by one position's angle (angle addition), unless the
       // group crosses into the next sequence.
+      // biases of the pair (c1, c1 + 64) of this lane, added before the rotation
+      float hb1[NP], hb2[NP];
+#pragma unroll
+      for (int j = 0; j < NP; ++j) {
+        const int64_t c = (int64_t)hd * 128 + pair_col(j) + l31;
+        hb1[j] = args.bias ? args.bias[c] : -0.0f;
+        hb2[j] = args.bias ? args.bias[c + 64] : -0.0f;
+      }
       float f_hi[NP], f_lo[NP];
       float c1p[NP], s1p[NP];  // cos / sin of one position's angle
 #pragma unroll
@@ -648,7 +677,7 @@ __global__ __launch_bounds__((Cfg<BMT, W4>::NW * 64), 1) void gemm_bf16_kernel(A
             float y1[4], y2[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              const float x1 = acc[i][j][4 * g4 + e], x2 = acc[i][j + NP][4 * g4 + e];
+              const float x1 = acc[i][j][4 * g4 + e] + hb1[j], x2 = acc[i][j + NP][4 * g4 + e] + hb2[j];
               y1[e] = x1 * cs[e] - x2 * sn[e];
               y2[e] = x2 * cs[e] + x1 * sn[e];
             }
@@ -682,6 +711,10 @@ __global__ __launch_bounds__((Cfg<BMT, W4>::NW * 64), 1) void gemm_bf16_kernel(A
       const int g = hd - o.hq - o.hkv;
       bf16_t* vt = reinterpret_cast<bf16_t*>(o.vt);
       bf16_t* reg = reinterpret_cast<bf16_t*>(smem) + wave * CH_W * RP;
+      float vb[NJ];  // bias of this lane's channel of each block
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+        vb[j] = args.bias ? args.bias[(int64_t)hd * 128 + (col_block<NJ>(wn, j) & 3) * 32 + l31] : -0.0f;
       const int64_t wrow0 = m0 + wm * WROWS;  // the wave's first row (a multiple of 32)
       const uint32_t vb0 = (uint32_t)(wrow0 / seq), vp0 = (uint32_t)(wrow0 - (int64_t)vb0 * seq);
 #pragma unroll
@@ -693,8 +726,8 @@ __global__ __launch_bounds__((Cfg<BMT, W4>::NW * 64), 1) void gemm_bf16_kernel(A
           for (int j = 0; j < NJ; ++j)
 #pragma unroll
             for (int g4 = 0; g4 < 4; ++g4) {
-              const u32x2 pr = {pack_bf16x2(acc[i0 + ii][j][4 * g4 + 0], acc[i0 + ii][j][4 * g4 + 1]),
-                                pack_bf16x2(acc[i0 + ii][j][4 * g4 + 2], acc[i0 + ii][j][4 * g4 + 3])};
+              const u32x2 pr = {pack_bf16x2(acc[i0 + ii][j][4 * g4 + 0] + vb[j], acc[i0 + ii][j][4 * g4 + 1] + vb[j]),
+                                pack_bf16x2(acc[i0 + ii][j][4 * g4 + 2] + vb[j], acc[i0 + ii][j][4 * g4 + 3] + vb[j])};
               *reinterpret_cast<u32x2*>(reg + (j * 32 + l31) * RP + ii * 32 + 8 * g4 + 4 * hk) = pr;
             }
         wait_lgkmcnt0();
@@ -719,6 +752,10 @@ __global__ __launch_bounds__((Cfg<BMT, W4>::NW * 64), 1) void gemm_bf16_kernel(A
       const int g = hd - o.hq - o.hkv;
       bf16_t* vt = reinterpret_cast<bf16_t*>(o.vt);
       const bool vec = (seq & 3u) == 0;  // groups of 4 never straddle sequences
+      float vb[NJ];  // bias of this lane's channel of each block
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+        vb[j] = args.bias ? args.bias[(int64_t)hd * 128 + (col_block<NJ>(wn, j) & 3) * 32 + l31] : -0.0f;
 #pragma unroll
       for (int i = 0; i < MI; ++i)
 #pragma unroll
@@ -732,8 +769,8 @@ __global__ __launch_bounds__((Cfg<BMT, W4>::NW * 64), 1) void gemm_bf16_kernel(A
             const int c = (col_block<NJ>(wn, j) & 3) * 32 + l31;
             if (vec && row0 + 3 < M) {
               bf16_t* line = vt + (((int64_t)b0 * o.hkv + g) * 128 + c) * o.seq_pad;
-              const u32x2 pr = {pack_bf16x2(acc[i][j][4 * g4 + 0], acc[i][j][4 * g4 + 1]),
-                                pack_bf16x2(acc[i][j][4 * g4 + 2], acc[i][j][4 * g4 + 3])};
+              const u32x2 pr = {pack_bf16x2(acc[i][j][4 * g4 + 0] + vb[j], acc[i][j][4 * g4 + 1] + vb[j]),
+                                pack_bf16x2(acc[i][j][4 * g4 + 2] + vb[j], acc[i][j][4 * g4 + 3] + vb[j])};
               *reinterpret_cast<u32x2*>(line + p0) = pr;
             } else {
 #pragma unroll
@@ -745,7 +782,7 @@ __global__ __launch_bounds__((Cfg<BMT, W4>::NW * 64), 1) void gemm_bf16_kernel(A
                   ++b;
                 }
                 vt[(((int64_t)b * o.hkv + g) * 128 + c) * o.seq_pad + pos] =
-                    f32_to_bf16(acc[i][j][4 * g4 + e]);
+                    f32_to_bf16(acc[i][j][4 * g4 + e] + vb[j]);
               }
             }
           }
@@ -854,7 +891,7 @@ void gemm_plan(int64_t M, int64_t N, int swiglu, int groups, int* bm_main, int* 
 
 hipError_t launch_gemm_bf16_group(int epi, int groups, int64_t M, int64_t N, int64_t K,
                                   const void* const* x, const void* const* w, void* const* out,
-                                  const QkvOut* qkv, hipStream_t s) {
+                                  const QkvOut* qkv, hipStream_t s, const float* bias, int64_t lda) {
   if (groups < 1 || groups > MAX_GROUP) return hipErrorInvalidValue;
   Args a;
   for (int g = 0; g < MAX_GROUP; ++g) {
@@ -866,6 +903,8 @@ hipError_t launch_gemm_bf16_group(int epi, int groups, int64_t M, int64_t N, int
   a.M = M;
   a.N = N;
   a.K = K;
+  a.lda = lda > 0 ? lda : K;
+  a.bias = bias;
   a.num_bm = a.num_bn = a.bn0 = 0;
   if (qkv) a.qkv = *qkv; else a.qkv = QkvOut{};
   const int64_t bn_cols = (epi == EPI_SWIGLU) ? BN / 2 : BN;
@@ -894,11 +933,11 @@ hipError_t launch_gemm_bf16_group(int epi, int groups, int64_t M, int64_t N, int
 }
 
 hipError_t launch_gemm_bf16(int epi, int64_t M, int64_t N, int64_t K, const void* x, const void* w,
-                            void* out, const QkvOut* qkv, hipStream_t s) {
+                            void* out, const QkvOut* qkv, hipStream_t s, const float* bias, int64_t lda) {
   const void* xs[1] = {x};
   const void* ws[1] = {w};
   void* os[1] = {out};
-  return launch_gemm_bf16_group(epi, 1, M, N, K, xs, ws, os, qkv, s);
+  return launch_gemm_bf16_group(epi, 1, M, N, K, xs, ws, os, qkv, s, bias, lda);
 }
 
 }  // namespace tpk

@@ -19,7 +19,8 @@ constexpr int NT = 256;
 
 template <int EPI>
 __global__ __launch_bounds__(NT) void gemm_f32_kernel(const float* x, const float* w, float* out,
-                                                      int64_t M, int64_t N, int64_t K) {
+                                                      int64_t M, int64_t N, int64_t K, int64_t lda,
+                                                      const float* bias) {
   constexpr bool DUAL = EPI == EPI_SWIGLU;
   __shared__ float xs[TK][T + 1];
   __shared__ float ws[DUAL ? 2 : 1][TK][T + 1];
@@ -32,7 +33,7 @@ __global__ __launch_bounds__(NT) void gemm_f32_kernel(const float* x, const floa
       const int idx = threadIdx.x + e * NT;
       const int r = idx >> 4, c = idx & 15;
       const bool kin = k0 + c < K;
-      xs[c][r] = (kin && m0 + r < M) ? x[(m0 + r) * K + k0 + c] : 0.0f;
+      xs[c][r] = (kin && m0 + r < M) ? x[(m0 + r) * lda + k0 + c] : 0.0f;
       ws[0][c][r] = (kin && n0 + r < N) ? w[(n0 + r) * K + k0 + c] : 0.0f;
       if (DUAL) ws[DUAL ? 1 : 0][c][r] = (kin && n0 + r < N) ? w[(N + n0 + r) * K + k0 + c] : 0.0f;
     }
@@ -64,8 +65,9 @@ __global__ __launch_bounds__(NT) void gemm_f32_kernel(const float* x, const floa
       const int64_t col = n0 + tx * 4 + j;
       if (col >= N) continue;
       float v = acc[0][i][j];
+      if (bias) v += bias[col];
       if (EPI == EPI_GELU) v = gelu_erf(v);
-      if (EPI == EPI_SWIGLU) v = silu(v) * acc[DUAL ? 1 : 0][i][j];
+      if (EPI == EPI_SWIGLU) v = silu(v) * (acc[DUAL ? 1 : 0][i][j] + (bias ? bias[N + col] : 0.0f));
       out[row * N + col] = v;
     }
   }
@@ -74,14 +76,21 @@ __global__ __launch_bounds__(NT) void gemm_f32_kernel(const float* x, const floa
 }  // namespace
 
 hipError_t launch_gemm_f32(int epi, int64_t M, int64_t N, int64_t K, const float* x, const float* w,
-                           float* out, hipStream_t s) {
+                           float* out, hipStream_t s, const float* bias, int64_t lda) {
   if (M == 0 || N == 0) return hipSuccess;
+  if (lda <= 0) lda = K;
   dim3 grid((unsigned)((N + T - 1) / T), (unsigned)((M + T - 1) / T)), block(NT);
   switch (epi) {
     case EPI_F32:
-    case EPI_BF16: hipLaunchKernelGGL(gemm_f32_kernel<EPI_F32>, grid, block, 0, s, x, w, out, M, N, K); break;
-    case EPI_GELU: hipLaunchKernelGGL(gemm_f32_kernel<EPI_GELU>, grid, block, 0, s, x, w, out, M, N, K); break;
-    case EPI_SWIGLU: hipLaunchKernelGGL(gemm_f32_kernel<EPI_SWIGLU>, grid, block, 0, s, x, w, out, M, N, K); break;
+    case EPI_BF16:
+      hipLaunchKernelGGL(gemm_f32_kernel<EPI_F32>, grid, block, 0, s, x, w, out, M, N, K, lda, bias);
+      break;
+    case EPI_GELU:
+      hipLaunchKernelGGL(gemm_f32_kernel<EPI_GELU>, grid, block, 0, s, x, w, out, M, N, K, lda, bias);
+      break;
+    case EPI_SWIGLU:
+      hipLaunchKernelGGL(gemm_f32_kernel<EPI_SWIGLU>, grid, block, 0, s, x, w, out, M, N, K, lda, bias);
+      break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

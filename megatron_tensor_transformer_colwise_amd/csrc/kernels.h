@@ -26,9 +26,14 @@ struct QkvOut {
   float log2_base;
 };
 
-// out[m, n] = epi( sum_k x[m, k] * w[row(n), k] ), bf16 operands, float32 accumulate.
+// out[m, n] = epi( sum_k x[m, k] * w[row(n), k] + bias[n] ), bf16 operands,
+// float32 accumulate.  bias (float32, or NULL) is added before the
+// nonlinearity (SwiGLU: N gate biases then N up biases; QKV: before RoPE;
+// not for EPI_F32).  x rows are lda elements apart (lda = 0: K), of which
+// the first K are read.
 hipError_t launch_gemm_bf16(int epi, int64_t M, int64_t N, int64_t K, const void* x, const void* w,
-                            void* out, const QkvOut* qkv, hipStream_t s);
+                            void* out, const QkvOut* qkv, hipStream_t s, const float* bias = nullptr,
+                            int64_t lda = 0);
 
 // Tile heights the bf16 GEMM launches for an M x N output (N = output
 // columns): columns [0, split) at height bm_main, the rest at bm_tail.
@@ -39,12 +44,13 @@ void gemm_plan(int64_t M, int64_t N, int swiglu, int groups, int* bm_main, int* 
 // G (<= 16) GEMMs of the same shape in one launch: out[g] = epi(x[g] . w[g]^T).
 hipError_t launch_gemm_bf16_group(int epi, int groups, int64_t M, int64_t N, int64_t K,
                                   const void* const* x, const void* const* w, void* const* out,
-                                  const QkvOut* qkv, hipStream_t s);
+                                  const QkvOut* qkv, hipStream_t s, const float* bias = nullptr,
+                                  int64_t lda = 0);
 
 // Same contraction in float32 throughout (EPI_F32 / EPI_BF16 meaning "no
 // nonlinearity, float32 out", EPI_GELU, EPI_SWIGLU).
 hipError_t launch_gemm_f32(int epi, int64_t M, int64_t N, int64_t K, const float* x, const float* w,
-                           float* out, hipStream_t s);
+                           float* out, hipStream_t s, const float* bias = nullptr, int64_t lda = 0);
 
 hipError_t launch_flash_attn(int64_t batch, int64_t seq, int64_t seq_pad, int hq, int hkv,
                              int causal, const void* q, const void* k, const void* vt, void* o,
@@ -56,11 +62,12 @@ hipError_t launch_shard_sum(int t, int64_t n, const float* const* partials, cons
 hipError_t launch_rmsnorm(int in_bf16, int64_t m, int64_t h, const void* x, const float* gain,
                           float eps, void* y, hipStream_t s);
 
-// x = shard-sum of t (0..16) partials (+ residual) over nrun runs of run_rows
+// x = shard-sum of t (0..16) partials (+ bias[h]) (+ residual) over nrun runs of run_rows
 // rows of h (runs run_stride rows apart); out = x if out, y = RMSNorm(x)
 // (bf16) if y; one pass.
 hipError_t launch_sum_rmsnorm(int t, int64_t nrun, int64_t run_rows, int64_t run_stride, int64_t h,
-                              const float* const* partials, const void* residual, int residual_bf16,
-                              float* out, const float* gain, float eps, void* y, hipStream_t s);
+                              const float* const* partials, const float* bias, const void* residual,
+                              int residual_bf16, float* out, const float* gain, float eps, void* y,
+                              hipStream_t s);
 
 }  // namespace tpk

@@ -118,6 +118,7 @@ __global__ __launch_bounds__(NT) void rmsnorm_kernel(const void* x, const float*
 
 struct SumNormArgs {
   const float* p[16];  // the t partials, at the first row of the first run
+  const float* bias;   // [h], added to the sum of the partials, or NULL
   const void* res;     // residual rows (float32 or bf16) or NULL
   float* out;          // sum rows, float32 (may be the float32 residual), or NULL
   const float* gain;
@@ -132,14 +133,15 @@ __device__ __forceinline__ f32x4 ld_nt4(const float* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
 }
 
-// For G groups of 8 elements at e[0..G): x = ((p_0 + p_1) + ... + p_{T-1})
-// + residual (T = 0: the residual alone), stored to out when there is one
+// For G groups of 8 elements at e[0..G) (columns c[0..G)): x = (((p_0 + p_1)
+// + ... + p_{T-1}) + bias) + residual (T = 0: the residual alone; the
+// row-parallel bias is added once, after the sum), stored to out when there is one
 // (non-temporal: it is next read a sublayer later).  Every load of the G
 // groups is issued before the first add and store (the compiler cannot
 // reorder loads past a store to a pointer it cannot tell apart).
 template <int T, int G>
-__device__ __forceinline__ void sum_groups(const SumNormArgs& a, const int64_t (&e)[G], const bool (&ok)[G],
-                                           float (&x)[G][8]) {
+__device__ __forceinline__ void sum_groups(const SumNormArgs& a, const int64_t (&e)[G], const int64_t (&c)[G],
+                                           const bool (&ok)[G], float (&x)[G][8]) {
   constexpr int TL = T > 0 ? T : 1;
   f32x4 lo[G][TL], hi[G][TL], rl[G], rh[G];
 #pragma unroll
@@ -180,6 +182,10 @@ __device__ __forceinline__ void sum_groups(const SumNormArgs& a, const int64_t (
         sl += lo[g][s];
         sh += hi[g][s];
       }
+      if (a.bias) {
+        sl += *reinterpret_cast<const f32x4*>(a.bias + c[g]);
+        sh += *reinterpret_cast<const f32x4*>(a.bias + c[g] + 4);
+      }
       if (a.res) {
         sl += rl[g];
         sh += rh[g];
@@ -212,16 +218,17 @@ __global__ __launch_bounds__(NT) void sum_rmsnorm_kernel(SumNormArgs a) {
   float ss = 0.0f;
 #pragma unroll
   for (int i0 = 0; i0 < MAX_CACHED; i0 += G) {
-    int64_t e[G];
+    int64_t e[G], c[G];
     bool ok[G];
     float x[G][8];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       const int64_t gi = threadIdx.x + (int64_t)(i0 + g) * NT;
       ok[g] = gi < groups;
-      e[g] = base + gi * 8;
+      c[g] = gi * 8;
+      e[g] = base + c[g];
     }
-    sum_groups<T, G>(a, e, ok, x);
+    sum_groups<T, G>(a, e, c, ok, x);
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       if (!ok[g]) continue;
@@ -233,10 +240,10 @@ __global__ __launch_bounds__(NT) void sum_rmsnorm_kernel(SumNormArgs a) {
     }
   }
   for (int64_t gi = threadIdx.x + (int64_t)MAX_CACHED * NT; gi < groups; gi += NT) {
-    const int64_t e[1] = {base + gi * 8};
+    const int64_t e[1] = {base + gi * 8}, c[1] = {gi * 8};
     const bool ok[1] = {true};
     float x[1][8];
-    sum_groups<T, 1>(a, e, ok, x);
+    sum_groups<T, 1>(a, e, c, ok, x);
 #pragma unroll
     for (int k = 0; k < 8; ++k) ss += x[0][k] * x[0][k];
   }
@@ -255,10 +262,10 @@ __global__ __launch_bounds__(NT) void sum_rmsnorm_kernel(SumNormArgs a) {
     if (a.out) {
       load8<false>(a.out, base + gi * 8, v);
     } else {
-      const int64_t e[1] = {base + gi * 8};
+      const int64_t e[1] = {base + gi * 8}, c[1] = {gi * 8};
       const bool ok[1] = {true};
       float x[1][8];
-      sum_groups<T, 1>(a, e, ok, x);
+      sum_groups<T, 1>(a, e, c, ok, x);
 #pragma unroll
       for (int k = 0; k < 8; ++k) v[k] = x[0][k];
     }
@@ -280,12 +287,14 @@ hipError_t launch_rmsnorm(int in_bf16, int64_t m, int64_t h, const void* x, cons
 }
 
 hipError_t launch_sum_rmsnorm(int t, int64_t nrun, int64_t run_rows, int64_t run_stride, int64_t h,
-                              const float* const* partials, const void* residual, int residual_bf16,
-                              float* out, const float* gain, float eps, void* y, hipStream_t s) {
+                              const float* const* partials, const float* bias, const void* residual,
+                              int residual_bf16, float* out, const float* gain, float eps, void* y,
+                              hipStream_t s) {
   const int64_t m = nrun * run_rows;
   if (m == 0) return hipSuccess;
   SumNormArgs a;
   for (int i = 0; i < 16; ++i) a.p[i] = i < t ? partials[i] : nullptr;
+  a.bias = bias;
   a.res = residual;
   a.out = out;
   a.gain = gain;

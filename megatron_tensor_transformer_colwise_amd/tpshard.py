@@ -42,20 +42,21 @@ _lib = None
 
 _i64, _i32, _f32, _vp = ctypes.c_int64, ctypes.c_int32, ctypes.c_float, ctypes.c_void_p
 _SIGS = {
-    "tp_colwise": [_i32, _i32, _i64, _i64, _i64, _vp, _vp, _vp, _vp],
+    "tp_colwise": [_i32, _i32, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp],
     "tp_rowwise": [_i32, _i64, _i64, _i64, _vp, _vp, _vp, _vp],
+    "tp_rowwise_split_input": [_i32, _i64, _i64, _i64, _i32, _i32, _vp, _vp, _vp, _vp],
     "tp_shard_mlp": [_i32, _i32, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp],
     "tp_shard_mlp_group": [_i32, _i32, _i32, _i64, _i64, _i64, _vp, ctypes.POINTER(_vp),
                            ctypes.POINTER(_vp), ctypes.POINTER(_vp), ctypes.POINTER(_vp), _vp],
-    "tp_qkv_rope": [_i64, _i64, _i64, _i32, _i32, _i32, _f32, _vp, _vp, _vp, _vp, _vp, _vp],
+    "tp_qkv_rope": [_i64, _i64, _i64, _i32, _i32, _i32, _f32, _vp, _vp, _vp, _vp, _vp, _vp, _vp],
     "tp_flash_attn": [_i64, _i64, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp],
     "tp_shard_attn_workspace_bytes": [_i64, _i64, _i32, _i32, _i32],
     "tp_shard_attn": [_i64, _i64, _i64, _i32, _i32, _i32, _f32, _i32, _vp, _vp, _vp, _vp,
                       ctypes.c_size_t, _vp, _vp],
     "tp_shard_sum": [_i32, _i64, ctypes.POINTER(_vp), _vp, _i32, _vp, _vp],
     "tp_rmsnorm": [_i32, _i64, _i64, _vp, _vp, _f32, _vp, _vp],
-    "tp_shard_sum_rmsnorm": [_i32, _i64, _i64, _i64, _i64, ctypes.POINTER(_vp), _vp, _i32, _vp, _vp, _f32,
-                             _vp, _vp],
+    "tp_shard_sum_rmsnorm": [_i32, _i64, _i64, _i64, _i64, ctypes.POINTER(_vp), _vp, _vp, _i32, _vp, _vp,
+                             _f32, _vp, _vp],
     "tp_gemm_plan": [_i64, _i64, _i32, ctypes.POINTER(_i32), ctypes.POINTER(_i32), ctypes.POINTER(_i32)],
     "tp_last_error": [],
     "tp_device_check": [],
@@ -127,12 +128,18 @@ def tp_device_check() -> None:
     _check(lib().tp_device_check())
 
 
-def tp_colwise(act, dt, m, k, n, x, w, y, stream=None) -> None:
-    _check(lib().tp_colwise(_e(act, ACTS), _e(dt, DTYPES), m, k, n, _p(x), _p(w), _p(y), _s(stream)))
+def tp_colwise(act, dt, m, k, n, x, w, y, stream=None, bias=None) -> None:
+    _check(lib().tp_colwise(_e(act, ACTS), _e(dt, DTYPES), m, k, n, _p(x), _p(w), _p(bias), _p(y),
+                            _s(stream)))
 
 
 def tp_rowwise(dt, m, k, n, y, w, partial, stream=None) -> None:
     _check(lib().tp_rowwise(_e(dt, DTYPES), m, k, n, _p(y), _p(w), _p(partial), _s(stream)))
+
+
+def tp_rowwise_split_input(dt, m, k, n, t, rank, x, w, partial, stream=None) -> None:
+    _check(lib().tp_rowwise_split_input(_e(dt, DTYPES), m, k, n, t, rank, _p(x), _p(w), _p(partial),
+                                        _s(stream)))
 
 
 def tp_shard_mlp(act, dt, m, h, f_shard, x, w_in, w_out, act_ws, partial, stream=None) -> None:
@@ -149,9 +156,10 @@ def tp_shard_mlp_group(act, dt, t, m, h, f_shard, x, w_in, w_out, act_ws, partia
                                     _arr(w_in), _arr(w_out), _arr(act_ws), _arr(partial), _s(stream)))
 
 
-def tp_qkv_rope(batch, seq, h, hq, hkv, head_dim, rope_base, x, w_qkv, q, k, vt, stream=None) -> None:
-    _check(lib().tp_qkv_rope(batch, seq, h, hq, hkv, head_dim, rope_base, _p(x), _p(w_qkv), _p(q),
-                             _p(k), _p(vt), _s(stream)))
+def tp_qkv_rope(batch, seq, h, hq, hkv, head_dim, rope_base, x, w_qkv, q, k, vt, stream=None,
+                bias=None) -> None:
+    _check(lib().tp_qkv_rope(batch, seq, h, hq, hkv, head_dim, rope_base, _p(x), _p(w_qkv), _p(bias),
+                             _p(q), _p(k), _p(vt), _s(stream)))
 
 
 def tp_flash_attn(batch, seq, hq, hkv, head_dim, causal, q, k, vt, o, stream=None) -> None:
@@ -179,9 +187,9 @@ def tp_rmsnorm(in_dt, m, h, x, gain, eps, y, stream=None) -> None:
 
 
 def tp_shard_sum_rmsnorm(t, m, h, partials, residual, residual_dt, out, gain, eps, y, stream=None,
-                         runs=None) -> None:
+                         runs=None, bias=None) -> None:
     """m rows (one run), or ``runs = (nrun, run_rows, run_stride)``."""
     nrun, run_rows, run_stride = runs if runs is not None else (1, m, m)
     arr = (_vp * max(len(partials), 1))(*[_p(p) for p in partials])
-    _check(lib().tp_shard_sum_rmsnorm(t, nrun, run_rows, run_stride, h, arr, _p(residual),
+    _check(lib().tp_shard_sum_rmsnorm(t, nrun, run_rows, run_stride, h, arr, _p(bias), _p(residual),
                                       _e(residual_dt, DTYPES), _p(out), _p(gain), eps, _p(y), _s(stream)))

@@ -27,6 +27,12 @@ Sources (the "Tensor parallelism" page of itwiki, by section):
   replicated across ranks when there are fewer KV heads than t.
 * "f and g": norms and residual connections are replicated on every rank; a
   block has one sum after attention and one after the MLP.
+* transformers "Tensor parallelism" page (partitioning table, DTensor
+  example): a column-parallel layer shards its bias with its output features;
+  a row-parallel layer's bias is replicated and added once, after the sum.
+* diffusers tensor-parallel guide (style table), "rowwise_split_input": a
+  row-parallel layer over a replicated input, each rank taking its own slice
+  of the input features.
 * "Sequence parallelism": the norms act on every token alone, so each rank
   can hold and normalise only its slice of the sequence; the sequence is
   gathered (all-gather) on entering the tensor-parallel region and, on
@@ -136,16 +142,73 @@ def mlp_gelu_row_split(x, a, t: int) -> tuple[np.ndarray, np.ndarray]:
     return gelu(shard_sum(pre)), shard_sum([gelu(p) for p in pre])
 
 
-def colwise_act(x, w_in, act: str, w_gate_up=None) -> np.ndarray:
-    """Rank-local colwise output Y_i: GeLU(X A_i), or SiLU(X W1_i) * (X W3_i)."""
+def linear(x, a, bias=None) -> np.ndarray:
+    """X A (+ bias on every row)."""
+    y = x @ a
+    return y if bias is None else y + np.asarray(bias, dtype=np.float64)
+
+
+def colwise_act(x, w_in, act: str, w_gate_up=None, bias=None, bias_gate_up=None) -> np.ndarray:
+    """Rank-local colwise output Y_i: GeLU(X A_i + b_i), or
+    SiLU(X W1_i + b1_i) * (X W3_i + b3_i); biases optional."""
     if act == "gelu":
-        return gelu(x @ w_in)
+        return gelu(linear(x, w_in, bias))
     if act == "swiglu":
         w1, w3 = w_gate_up
-        return silu(x @ w1) * (x @ w3)
+        b1, b3 = bias_gate_up if bias_gate_up is not None else (None, None)
+        return silu(linear(x, w1, b1)) * linear(x, w3, b3)
     if act == "none":
-        return x @ w_in
+        return linear(x, w_in, bias)
     raise ValueError(act)
+
+
+# Biases (transformers "Tensor parallelism" page, partitioning table and its
+# DTensor example): a column-parallel layer shards its bias with its output
+# features, so rank i adds b_i before its nonlinearity; a row-parallel layer
+# replicates its bias and it is added once, after the sum over ranks.
+
+
+def split_vector(b, t: int) -> list[np.ndarray]:
+    """Rank i's contiguous 1/t of a bias over output features."""
+    b = np.asarray(b)
+    if b.shape[0] % t:
+        raise ValueError(f"{b.shape[0]} features are not divisible by t = {t}")
+    n = b.shape[0] // t
+    return [b[i * n:(i + 1) * n] for i in range(t)]
+
+
+def mlp_gelu_bias(x, a, ba, b, bb) -> np.ndarray:
+    """Z = GeLU(X A + ba) B + bb, the unsharded layer with biases."""
+    return linear(gelu(linear(x, a, ba)), b, bb)
+
+
+def mlp_gelu_bias_partials(x, a, ba, b, t: int) -> list[np.ndarray]:
+    """partial_i = GeLU(X A_i + ba_i) B_i; the layer output is their sum plus bb once."""
+    return [gelu(linear(x, ai, bai)) @ bi
+            for ai, bai, bi in zip(split_columns(a, t), split_vector(ba, t), split_rows(b, t))]
+
+
+def mlp_swiglu_bias(x, w1, b1, w3, b3, w2, b2) -> np.ndarray:
+    """Z = (SiLU(X W1 + b1) * (X W3 + b3)) W2 + b2."""
+    return linear(silu(linear(x, w1, b1)) * linear(x, w3, b3), w2, b2)
+
+
+def mlp_swiglu_bias_partials(x, w1, b1, w3, b3, w2, t: int) -> list[np.ndarray]:
+    """partial_i = (SiLU(X W1_i + b1_i) * (X W3_i + b3_i)) W2_i."""
+    return [(silu(linear(x, a, ba)) * linear(x, c, bc)) @ bw
+            for a, ba, c, bc, bw in zip(split_columns(w1, t), split_vector(b1, t), split_columns(w3, t),
+                                        split_vector(b3, t), split_rows(w2, t))]
+
+
+# "rowwise_split_input" (diffusers tensor-parallel guide, style table): a
+# row-parallel layer whose input is replicated; each rank multiplies its own
+# slice of the input features by its rows of the weight.
+
+
+def rowwise_split_input_partials(x, w, t: int) -> list[np.ndarray]:
+    """partial_r = X[:, cols_r] W[cols_r, :] with cols_r the r-th 1/t of the input
+    features; their sum is X W."""
+    return [xr @ wr for xr, wr in zip(split_columns(x, t), split_rows(w, t))]
 
 
 def mlp_swiglu(x, w1, w3, w2) -> np.ndarray:
@@ -220,13 +283,18 @@ def causal_attention(q, k, v, q_pos=None) -> np.ndarray:
 
 def attn_heads_output(x, wq, wk, wv, heads: int, kv_heads: int, head_dim: int,
                       batch: int, seq: int, rope_base: float, q_heads: list[int],
-                      rows=None) -> np.ndarray:
+                      rows=None, bq=None, bk=None, bv=None) -> np.ndarray:
     """Concatenated outputs of the given query heads, [len(rows), len(q_heads)*d].
 
-    x [batch*seq, h]; wq [h, heads*d]; wk, wv [h, kv_heads*d] (math convention).
+    x [batch*seq, h]; wq [h, heads*d]; wk, wv [h, kv_heads*d] (math convention);
+    optional biases bq [heads*d], bk, bv [kv_heads*d], added before RoPE.
     ``rows`` selects output token rows (default: all); K and V are still
     computed for every token, since a row sees its whole causal prefix."""
     d = head_dim
+
+    def proj(xx, w, b, j):
+        return linear(xx, w[:, j * d:(j + 1) * d], None if b is None else b[j * d:(j + 1) * d])
+
     m = batch * seq
     rows = np.arange(m) if rows is None else np.asarray(rows)
     out = np.zeros((len(rows), len(q_heads) * d))
@@ -240,12 +308,12 @@ def attn_heads_output(x, wq, wk, wv, heads: int, kv_heads: int, head_dim: int,
         qpos = rows[sel] - b * seq
         kv = {}
         for g in kv_needed:
-            kh = rope(xb @ wk[:, g * d:(g + 1) * d], pos_all, rope_base)
-            vh = xb @ wv[:, g * d:(g + 1) * d]
+            kh = rope(proj(xb, wk, bk, g), pos_all, rope_base)
+            vh = proj(xb, wv, bv, g)
             kv[g] = (kh, vh)
         xq = xb[qpos]
         for c, j in enumerate(q_heads):
-            qh = rope(xq @ wq[:, j * d:(j + 1) * d], qpos, rope_base)
+            qh = rope(proj(xq, wq, bq, j), qpos, rope_base)
             kh, vh = kv[kv_head_of(j, heads, kv_heads)]
             out[sel, c * d:(c + 1) * d] = causal_attention(qh, kh, vh, qpos)
     return out
@@ -257,7 +325,8 @@ def attn_partial(x, w: dict, case, rank: int, t: int | None = None, rows=None) -
     t = case.t if t is None else t
     q_heads = rank_query_heads(rank, case.heads, t)
     o = attn_heads_output(x, w["Wq"], w["Wk"], w["Wv"], case.heads, case.kv_heads,
-                          case.head_dim, case.batch, case.seq, case.rope_base, q_heads, rows)
+                          case.head_dim, case.batch, case.seq, case.rope_base, q_heads, rows,
+                          w.get("bq"), w.get("bk"), w.get("bv"))
     d = case.head_dim
     wo_rows = w["Wo"][q_heads[0] * d:(q_heads[-1] + 1) * d]
     return o @ wo_rows

@@ -39,27 +39,27 @@ def status(fn, *args):
 
 def test_colwise_rowwise_validation(L):
     # k not a multiple of 8
-    assert status("tp_colwise", 1, 1, 4, 12, 16, A16, A16, A16, None) == tp.TP_ERR_SHAPE
+    assert status("tp_colwise", 1, 1, 4, 12, 16, A16, A16, None, A16, None) == tp.TP_ERR_SHAPE
     assert "k = 12" in tp.tp_last_error()
     # n not positive
-    assert status("tp_colwise", 1, 1, 4, 16, 0, A16, A16, A16, None) == tp.TP_ERR_SHAPE
+    assert status("tp_colwise", 1, 1, 4, 16, 0, A16, A16, None, A16, None) == tp.TP_ERR_SHAPE
     # negative m
     assert status("tp_rowwise", 1, -1, 16, 16, A16, A16, A16, None) == tp.TP_ERR_SHAPE
     # unknown dtype / activation
-    assert status("tp_colwise", 1, 7, 4, 16, 16, A16, A16, A16, None) == tp.TP_ERR_INVALID_ARG
-    assert status("tp_colwise", 9, 1, 4, 16, 16, A16, A16, A16, None) == tp.TP_ERR_INVALID_ARG
+    assert status("tp_colwise", 1, 7, 4, 16, 16, A16, A16, None, A16, None) == tp.TP_ERR_INVALID_ARG
+    assert status("tp_colwise", 9, 1, 4, 16, 16, A16, A16, None, A16, None) == tp.TP_ERR_INVALID_ARG
     # null and misaligned pointers
-    assert status("tp_colwise", 1, 1, 4, 16, 16, None, A16, A16, None) == tp.TP_ERR_INVALID_ARG
+    assert status("tp_colwise", 1, 1, 4, 16, 16, None, A16, None, A16, None) == tp.TP_ERR_INVALID_ARG
     assert "x is NULL" in tp.tp_last_error()
     assert status("tp_rowwise", 1, 4, 16, 16, A16, MIS, A16, None) == tp.TP_ERR_INVALID_ARG
     assert "w is not 16-byte aligned" in tp.tp_last_error()
     # weight over the 2 GiB operand limit
-    assert status("tp_colwise", 2, 1, 4, 65536, 65536, A16, A16, A16, None) == tp.TP_ERR_SHAPE
+    assert status("tp_colwise", 2, 1, 4, 65536, 65536, A16, A16, None, A16, None) == tp.TP_ERR_SHAPE
 
 
 def test_m_zero_is_a_noop(L):
     # nothing to do: OK without touching pointers or the device
-    assert status("tp_colwise", 1, 1, 0, 16, 16, None, None, None, None) == tp.TP_OK
+    assert status("tp_colwise", 1, 1, 0, 16, 16, None, None, None, None, None) == tp.TP_OK
     assert status("tp_rowwise", 1, 0, 16, 16, None, None, None, None) == tp.TP_OK
     assert status("tp_shard_mlp", 2, 1, 0, 16, 16, None, None, None, None, None, None) == tp.TP_OK
     arr = (ctypes.c_void_p * 1)(None)
@@ -91,7 +91,7 @@ def test_attention_validation(L):
     st = status("tp_shard_attn", 2, 64, 256, 4, 2, 128, 500000.0, 1, A16, A16, A16, A16, ws_need - 1,
                 A16, None)
     assert st == tp.TP_ERR_WORKSPACE
-    assert status("tp_qkv_rope", 2, 64, 256, 4, 2, 128, 0.5, A16, A16, A16, A16, A16, None) == tp.TP_ERR_INVALID_ARG
+    assert status("tp_qkv_rope", 2, 64, 256, 4, 2, 128, 0.5, A16, A16, None, A16, A16, A16, None) == tp.TP_ERR_INVALID_ARG
     assert status("tp_flash_attn", 2, 64, 4, 2, 128, 1, A16, A16, None, A16, None) == tp.TP_ERR_INVALID_ARG
     # seq padding to 64 in the transposed-V region
     assert tp.tp_shard_attn_workspace_bytes(1, 65, 1, 1, 128) >= 128 * 128 * 2
@@ -115,8 +115,9 @@ def test_shard_sum_rmsnorm_validation(L):
     ptrs = (ctypes.c_void_p * 17)(*([A16 + 64 * i for i in range(17)]))
     out, y = A16 + 8192, A16 + 16384
 
-    def call(t, h=16, res=None, rdt=0, o=out, g=None, eps=1e-5, yy=y, runs=(1, 4, 4), arr=ptrs):
-        return status("tp_shard_sum_rmsnorm", t, runs[0], runs[1], runs[2], h, arr, res, rdt, o, g, eps, yy, None)
+    def call(t, h=16, res=None, rdt=0, o=out, g=None, eps=1e-5, yy=y, runs=(1, 4, 4), arr=ptrs, bias=None):
+        return status("tp_shard_sum_rmsnorm", t, runs[0], runs[1], runs[2], h, arr, bias, res, rdt, o, g, eps, yy,
+                      None)
 
     assert call(-1) == tp.TP_ERR_SHAPE
     assert call(17) == tp.TP_ERR_SHAPE
@@ -134,6 +135,8 @@ def test_shard_sum_rmsnorm_validation(L):
     assert "needs a residual" in tp.tp_last_error()
     assert call(2, o=None, yy=None) == tp.TP_ERR_INVALID_ARG         # nothing to write
     assert call(2, arr=None) == tp.TP_ERR_INVALID_ARG
+    assert call(2, bias=MIS) == tp.TP_ERR_INVALID_ARG                 # misaligned bias
+    assert call(0, res=A16 + 4096, rdt=0, bias=A16 + 4096) == tp.TP_ERR_INVALID_ARG  # bias without partials
     # nothing to do: OK without touching pointers or the device
     assert call(2, runs=(0, 4, 4), o=None, yy=y, arr=None) == tp.TP_OK
     assert call(2, runs=(3, 0, 4), arr=None) == tp.TP_OK
@@ -219,4 +222,23 @@ def test_sequence_parallel_slices_host():
                                                          rope_base=500000.0, seed=1))
     with pytest.raises(ValueError):
         blk2.sp_slices()
+
+
+def test_rowwise_split_input_validation(L):
+    f = lambda t, r, k=64, n=16, x=A16, w=A16, o=A16 + 8192, dt=1: status(  # noqa: E731
+        "tp_rowwise_split_input", dt, 4, k, n, t, r, x, w, o, None)
+    assert f(0, 0) == tp.TP_ERR_SHAPE
+    assert f(17, 0) == tp.TP_ERR_SHAPE
+    assert f(4, 4) == tp.TP_ERR_SHAPE and "rank = 4" in tp.tp_last_error()
+    assert f(4, -1) == tp.TP_ERR_SHAPE
+    assert f(3, 0, k=64) == tp.TP_ERR_SHAPE      # 64 / 3 is not whole
+    assert f(4, 0, k=48) == tp.TP_ERR_SHAPE      # 48 / 4 = 12: not a multiple of 8
+    assert f(4, 0, x=MIS) == tp.TP_ERR_INVALID_ARG
+    assert f(4, 0, dt=5) == tp.TP_ERR_INVALID_ARG
+    assert status("tp_rowwise_split_input", 1, 0, 64, 16, 4, 0, None, None, None, None) == tp.TP_OK
+
+
+def test_bias_pointer_checked(L):
+    assert status("tp_colwise", 1, 1, 4, 16, 16, A16, A16, MIS, A16, None) == tp.TP_ERR_INVALID_ARG
+    assert "bias" in tp.tp_last_error()
 

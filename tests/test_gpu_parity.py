@@ -172,6 +172,146 @@ def test_colwise_none_integer_bit_exact(device, m, k, n):
     assert np.array_equal(host(out), x.f64() @ w.f64().T)
 
 
+# ---------------------------------------------------------------- projection variants
+
+
+@pytest.mark.parametrize("m,k,n", [(300, 40, 264), (6100, 128, 5904), (777, 2056, 520)])
+def test_colwise_bias_integer_bit_exact(device, m, k, n):
+    """A column-parallel bias added in the epilogue: integer inputs and bias keep
+    every sum within +-256, so the bf16 output is exact (eight- and four-wave
+    tiles, several rounds of tiles, ragged m and n)."""
+    say(f"case colwise bias int m={m} k={k} n={n}")
+    x = inputs.integers(12, 0, (m, k), -1, 1)
+    w = inputs.integers(12, 1, (n, k), -1, 1)
+    b = inputs.integers(12, 2, (n,), -4, 4, "f32").data
+    ref = x.f64() @ w.f64().T + b.astype(np.float64)
+    assert np.max(np.abs(ref)) <= 256
+    out = torch.empty(m, n, dtype=torch.bfloat16, device=device)
+    tp.tp_colwise("none", "bf16", m, k, n, to_dev(x, device), to_dev(w, device), out,
+                  bias=torch.from_numpy(b).to(device))
+    torch.cuda.synchronize()
+    assert np.array_equal(host(out), ref)
+
+
+@pytest.mark.parametrize("act,dt,m,k,f", [("gelu", "bf16", 333, 256, 264), ("swiglu", "bf16", 333, 256, 264),
+                                          ("swiglu", "bf16", 5000, 2056, 1792), ("gelu", "f32", 37, 64, 72),
+                                          ("swiglu", "f32", 37, 64, 72)])
+def test_colwise_bias_activations(device, act, dt, m, k, f):
+    """GeLU(X A_i + b_i) and SiLU(X W1_i + b1_i) * (X W3_i + b3_i) against the oracle."""
+    say(f"case colwise bias {act} {dt} m={m} k={k} f={f}")
+    x = inputs.normal(13, 0, (m, k), 1.0, dt)
+    rows = 2 * f if act == "swiglu" else f
+    w = inputs.normal(13, 1, (rows, k), 0.05, dt)
+    b = inputs.normal(13, 2, (rows,), 0.5, "f32").data
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    out = torch.empty(m, f, dtype=tdt, device=device)
+    tp.tp_colwise(act, dt, m, k, f, to_dev(x, device), to_dev(w, device), out, bias=torch.from_numpy(b).to(device))
+    torch.cuda.synchronize()
+    X, W, B = x.f64(), w.f64(), b.astype(np.float64)
+    if act == "gelu":
+        ref = oracle.colwise_act(X, W.T, "gelu", bias=B)
+    else:
+        ref = oracle.colwise_act(X, None, "swiglu", (W[:f].T, W[f:].T), bias_gate_up=(B[:f], B[f:]))
+    if dt == "f32":
+        assert np.max(np.abs(host(out) - ref)) <= F32_ATOL
+    else:
+        assert rel_err(host(out), ref) <= BF16_TOL
+
+
+def test_qkv_rope_bias(device):
+    """Q/K/V biases added before RoPE (Q, K) and before the transposed store (V),
+    against the oracle's projections; sequence 100 leaves a ragged last key tile."""
+    batch, seq, h, hq, hkv, d = 2, 100, 256, 4, 2, 128
+    say(f"case qkv_rope bias batch={batch} seq={seq}")
+    m, n = batch * seq, (hq + 2 * hkv) * d
+    x = inputs.normal(14, 0, (m, h), 1.0, "bf16")
+    w = inputs.normal(14, 1, (n, h), 0.05, "bf16")
+    b = inputs.normal(14, 2, (n,), 0.5, "f32").data
+    seq_pad = (seq + 63) // 64 * 64
+    q = torch.empty(m, hq * d, dtype=torch.bfloat16, device=device)
+    k = torch.empty(m, hkv * d, dtype=torch.bfloat16, device=device)
+    vt = torch.empty(batch, hkv, d, seq_pad, dtype=torch.bfloat16, device=device)
+    tp.tp_qkv_rope(batch, seq, h, hq, hkv, d, 500000.0, to_dev(x, device), to_dev(w, device), q, k, vt,
+                   bias=torch.from_numpy(b).to(device))
+    torch.cuda.synchronize()
+    X, W, B = x.f64(), w.f64(), b.astype(np.float64)
+    pos = np.tile(np.arange(seq), batch)
+    for j in range(hq):
+        ref = oracle.rope(oracle.linear(X, W[j * d:(j + 1) * d].T, B[j * d:(j + 1) * d]), pos, 500000.0)
+        assert rel_err(host(q[:, j * d:(j + 1) * d]), ref) <= BF16_TOL
+    for g in range(hkv):
+        r0 = (hq + g) * d
+        ref = oracle.rope(oracle.linear(X, W[r0:r0 + d].T, B[r0:r0 + d]), pos, 500000.0)
+        assert rel_err(host(k[:, g * d:(g + 1) * d]), ref) <= BF16_TOL
+        r0 = (hq + hkv + g) * d
+        refv = oracle.linear(X, W[r0:r0 + d].T, B[r0:r0 + d])
+        got = vt[:, g, :, :seq].permute(0, 2, 1).reshape(m, d)
+        assert rel_err(host(got), refv) <= BF16_TOL
+        assert not vt[:, g, :, seq:].any()
+
+
+@pytest.mark.parametrize("dt,m,k,n,t", [("bf16", 300, 4096, 264, 4), ("bf16", 6100, 1024, 5904, 2),
+                                        ("f32", 37, 64, 40, 2)])
+def test_rowwise_split_input_bit_exact(device, dt, m, k, n, t):
+    """Each rank reads its own columns of the replicated input in place; the
+    partials are bit-exact on integer inputs and sum to X W."""
+    say(f"case rowwise split input {dt} m={m} k={k} n={n} t={t}")
+    x = inputs.integers(15, 0, (m, k), -2, 2, dt)
+    w_lin = inputs.integers(15, 1, (n, k), -2, 2, dt)          # nn.Linear layout [out, in]
+    X, WL = x.f64(), w_lin.f64()
+    parts = oracle.rowwise_split_input_partials(X, WL.T, t)
+    dx = to_dev(x, device)
+    dwl = to_dev(w_lin, device)
+    ks = k // t
+    total = np.zeros((m, n))
+    for r in range(t):
+        wr = dwl[:, r * ks:(r + 1) * ks].contiguous()
+        out = torch.empty(m, n, dtype=torch.float32, device=device)
+        tp.tp_rowwise_split_input(dt, m, k, n, t, r, dx, wr, out)
+        torch.cuda.synchronize()
+        got = out.cpu().double().numpy()
+        assert np.array_equal(got, parts[r])
+        total += got
+    assert np.array_equal(total, X @ WL.T)
+
+
+def test_mlp_with_biases(device):
+    """A biased GeLU MLP sharded over 4 ranks: column biases in the colwise
+    epilogue, the row bias added once after the sum (bit-exact to a float32
+    sum of the GPU partials, then the bias), against the unsharded oracle."""
+    m, h, f, t = 512, 512, 2048, 4
+    say(f"case biased mlp m={m} h={h} f={f} t={t}")
+    x = inputs.normal(16, 0, (m, h), 1.0, "bf16")
+    a = inputs.normal(16, 1, (h, f), 0.02, "bf16")     # math convention [in, out]
+    b = inputs.normal(16, 2, (f, h), 0.02, "bf16")
+    ba = inputs.normal(16, 3, (f,), 0.5, "f32").data
+    bb = inputs.normal(16, 4, (h,), 0.5, "f32").data
+    A, Bm = a.torch(), b.torch()
+    dx = to_dev(x, device)
+    fs = f // t
+    act = torch.empty(m, fs, dtype=torch.bfloat16, device=device)
+    parts = torch.empty(t, m, h, dtype=torch.float32, device=device)
+    for r in range(t):
+        w_in = A[:, r * fs:(r + 1) * fs].T.contiguous().to(device)
+        w_out = Bm[r * fs:(r + 1) * fs, :].T.contiguous().to(device)
+        tp.tp_colwise("gelu", "bf16", m, h, fs, dx, w_in, act, bias=torch.from_numpy(ba[r * fs:(r + 1) * fs].copy()).to(device))
+        tp.tp_rowwise("bf16", m, fs, h, act, w_out, parts[r])
+    z = torch.empty(m, h, dtype=torch.float32, device=device)
+    y = torch.empty(m, h, dtype=torch.bfloat16, device=device)
+    tp.tp_shard_sum_rmsnorm(t, m, h, list(parts), None, "f32", z, None, 1e-5, y, bias=torch.from_numpy(bb).to(device))
+    torch.cuda.synchronize()
+    p_host = [p.cpu().numpy() for p in parts]
+    acc = p_host[0].copy()
+    for p in p_host[1:]:
+        acc = (acc + p).astype(np.float32)
+    acc = (acc + bb).astype(np.float32)
+    assert np.array_equal(z.cpu().numpy(), acc)
+    ref = oracle.mlp_gelu_bias(x.f64(), a.f64(), ba.astype(np.float64), b.f64(), bb.astype(np.float64))
+    assert rel_err(host(z), ref) <= BF16_TOL
+    refn = oracle.rmsnorm(acc.astype(np.float64), None, 1e-5)
+    assert np.all(np.abs(host(y) - refn) <= 2.0 ** -8 * np.abs(refn) + 1e-6)
+
+
 # ---------------------------------------------------------------- MLP, small
 
 

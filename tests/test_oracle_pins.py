@@ -400,6 +400,81 @@ def test_sequence_parallel_block_equals_replicated(t):
         assert np.array_equal(z, ref["z"][rows])
 
 
+# ---------------------------------------------------------------- projection variants
+
+
+@pytest.mark.parametrize("t", [1, 2, 4, 8])
+def test_bias_sharding_identity_and_negative_control(t):
+    """Column-parallel biases sharded with the output features and the row-parallel
+    bias added once after the sum reproduce the unsharded biased MLP (GeLU and
+    SwiGLU); adding the row-parallel bias on every rank instead is off by (t-1) b."""
+    r = np.random.default_rng(31)
+    m, h, f = 6, 16, 64
+    x = r.standard_normal((m, h))
+    a, b = r.standard_normal((h, f)) * 0.3, r.standard_normal((f, h)) * 0.3
+    ba, bb = r.standard_normal(f), r.standard_normal(h)
+    ref = oracle.mlp_gelu_bias(x, a, ba, b, bb)
+    parts = oracle.mlp_gelu_bias_partials(x, a, ba, b, t)
+    z = oracle.shard_sum(parts) + bb
+    assert np.max(np.abs(z - ref)) <= 1e-12 * np.max(np.abs(ref))
+    wrong = oracle.shard_sum([p + bb for p in parts])
+    assert np.allclose(wrong - ref, (t - 1) * bb[None, :], atol=1e-12)
+    # brute force of one element with the bias inside the GeLU
+    i, c = 2, 5
+    pre = [sum(x[i, k] * a[k, j] for k in range(h)) + ba[j] for j in range(f)]
+    assert abs(sum(oracle.gelu(pre[j]) * b[j, c] for j in range(f)) + bb[c] - ref[i, c]) < 1e-12
+    w1, w3, w2 = (r.standard_normal((h, f)) * 0.3, r.standard_normal((h, f)) * 0.3,
+                  r.standard_normal((f, h)) * 0.3)
+    b1, b3, b2 = r.standard_normal(f), r.standard_normal(f), r.standard_normal(h)
+    ref = oracle.mlp_swiglu_bias(x, w1, b1, w3, b3, w2, b2)
+    z = oracle.shard_sum(oracle.mlp_swiglu_bias_partials(x, w1, b1, w3, b3, w2, t)) + b2
+    assert np.max(np.abs(z - ref)) <= 1e-12 * np.max(np.abs(ref))
+    # swapping the gate and up biases changes the result
+    assert np.max(np.abs(oracle.mlp_swiglu_bias(x, w1, b3, w3, b1, w2, b2) - ref)) > 1e-3
+
+
+def test_attention_bias_identity_and_brute_force():
+    """Q/K/V biases (before RoPE): the sum over ranks equals the unsharded
+    biased attention (with KV replication at t = 8), and one head matches a
+    direct evaluation."""
+    case = inputs.AttnCase("bias_attn", 2, 5, 32, 8, 2, 4, 4, 10000.0, seed=3)
+    r = np.random.default_rng(7)
+    w = {k: v.f64() for k, v in inputs.gen_attn(case).items()}
+    w["bq"] = r.standard_normal(8 * 4)
+    w["bk"] = r.standard_normal(2 * 4)
+    w["bv"] = r.standard_normal(2 * 4)
+    full = oracle.attn_partial(w["X"], w, case, 0, t=1)
+    for t in (2, 4, 8):
+        z = oracle.shard_sum([oracle.attn_partial(w["X"], w, case, rk, t) for rk in range(t)])
+        assert np.max(np.abs(z - full)) <= 1e-12 * np.max(np.abs(full))
+    # head 5 (KV head 1), sequence 1, direct
+    d, j, g, b = 4, 5, 1, 1
+    xb = w["X"][b * 5:(b + 1) * 5]
+    pos = np.arange(5)
+    q = oracle.rope(xb @ w["Wq"][:, j * d:(j + 1) * d] + w["bq"][j * d:(j + 1) * d], pos, 10000.0)
+    k = oracle.rope(xb @ w["Wk"][:, g * d:(g + 1) * d] + w["bk"][g * d:(g + 1) * d], pos, 10000.0)
+    v = xb @ w["Wv"][:, g * d:(g + 1) * d] + w["bv"][g * d:(g + 1) * d]
+    o = oracle.attn_heads_output(w["X"], w["Wq"], w["Wk"], w["Wv"], 8, 2, 4, 2, 5, 10000.0, [j],
+                                 bq=w["bq"], bk=w["bk"], bv=w["bv"])[b * 5:(b + 1) * 5]
+    for p in range(5):
+        s_ = np.array([q[p] @ k[pp] for pp in range(p + 1)]) / 2.0
+        e = np.exp(s_ - s_.max())
+        assert np.allclose(o[p], (e / e.sum()) @ v[:p + 1], atol=1e-12)
+
+
+@pytest.mark.parametrize("t", [1, 2, 4])
+def test_rowwise_split_input_identity(t):
+    """Each rank multiplies its slice of the replicated input's features by its
+    rows of the weight; the sum over ranks is the full product."""
+    r = np.random.default_rng(11)
+    x, w = r.standard_normal((7, 32)), r.standard_normal((32, 12))
+    parts = oracle.rowwise_split_input_partials(x, w, t)
+    assert np.max(np.abs(oracle.shard_sum(parts) - x @ w)) < 1e-12
+    k = 32 // t
+    for rk, p in enumerate(parts):
+        assert np.array_equal(p, x[:, rk * k:(rk + 1) * k] @ w[rk * k:(rk + 1) * k])
+
+
 # ---------------------------------------------------------------- inputs
 
 
