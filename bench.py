@@ -235,6 +235,26 @@ def per_config_report(dev):
                     "sequence_parallel_step_tflops": rate(case.t * (afl + mfl), sp_step)})
         emit(rec)
         del blk, dw
+
+    # packed single-stream block (the guide's [1, 1, 1, 3, 3] example, mlp
+    # ratio 3): h = 3072, 24 heads of 128, 4608 tokens, no mask, t = 4
+    h, heads, d, seq, t = 3072, 24, 128, 4608, 4
+    log("configs: packed_single_stream")
+    x = inputs.normal(81, 0, (seq, h), 1.0, "bf16").torch().to(dev)
+    w_in = inputs.normal(81, 1, (9 * h, h), 0.02, "bf16").torch().to(dev)
+    w_out = inputs.normal(81, 2, (h, 4 * h), 0.02, "bf16").torch().to(dev)
+    ss = shard.SingleStreamShards(x, w_in, w_out, heads, d, 1, seq, t, 500000.0, causal=False)
+    hr, mr, m = h // t, 3 * h // t, seq
+    rfl = (2.0 * m * h * 3 * hr + 4.0 * d * seq * seq * (heads // t) + 2.0 * m * h * 2 * mr
+           + 2.0 * m * (hr + mr) * h)
+    rms, rmn = _time(lambda: ss.rank(0))
+    fms, fmn = _time(lambda: ss.forward(), reps=10, warm=2)
+    emit({"workload": "packed_single_stream", "call": "one rank: Q, K, V + RoPE and SwiGLU GEMMs from one packed "
+          "buffer, attention, two out-projection partials", "ms": round(rms, 4), "min_ms": round(rmn, 4),
+          "tflops": rate(rfl, rms), "pct_mfma_peak": round(100.0 * rfl / rms / 1e9 / MFMA_BF16_PEAK_TFLOPS, 2),
+          "all_ranks_and_sum_ms": round(fms, 4), "all_ranks_tflops": rate(t * rfl, fms),
+          "shape": f"h={h}, {heads} heads of {d}, mlp {3 * h}, {seq} tokens, t={t}, no mask"})
+    del ss, x, w_in, w_out
     del scratch
 
 

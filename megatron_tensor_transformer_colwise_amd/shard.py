@@ -273,3 +273,91 @@ class BlockShards:
             tp.tp_shard_sum_rmsnorm(t, 0, h, [mp[i][o:] for i in range(t)], self.attn.out[o:], "f32",
                                     self.mlp.out[o:], None, eps, None, stream, runs=runs)
         return self.mlp.out
+
+
+# ---------------------------------------------------------------- packed (fused) projections
+
+
+def _packed_ranges(n: int, blocks, t: int, rank: int) -> list[tuple[int, int]]:
+    """(start, stop) of rank ``rank``'s 1/t of every packed block of a
+    dimension of n; blocks are proportions whose sum divides n, and each block
+    must be divisible by t on its own (diffusers guide, "Fused projections",
+    "Constraints and validation")."""
+    total = sum(blocks)
+    if n % total:
+        raise ValueError(f"packed dimension {n} is not divisible by sum(blocks) = {total}")
+    unit, out, start = n // total, [], 0
+    for b in blocks:
+        size = b * unit
+        if size % t:
+            raise ValueError(f"packed block of {size} is not divisible by t = {t}")
+        out.append((start + rank * (size // t), start + (rank + 1) * (size // t)))
+        start += size
+    return out
+
+
+def packed_colwise_weight(w: torch.Tensor, blocks, t: int, rank: int) -> torch.Tensor:
+    """Rank's rows of an nn.Linear weight [out, in] whose output features pack
+    several tensors: its 1/t of every block, in packed order (contiguous)."""
+    return torch.cat([w[a:b] for a, b in _packed_ranges(w.shape[0], blocks, t, rank)]).contiguous()
+
+
+def packed_rowwise_weights(w: torch.Tensor, blocks, t: int, rank: int) -> list[torch.Tensor]:
+    """Rank's columns of an nn.Linear weight [out, in] whose input features pack
+    several tensors, one contiguous [out, in_block / t] weight per block."""
+    return [w[:, a:b].contiguous() for a, b in _packed_ranges(w.shape[1], blocks, t, rank)]
+
+
+class SingleStreamShards:
+    """A packed single-stream block, every rank on one device: one Linear
+    projects X to [Q | K | V | gate | up] (output blocks [1, 1, 1, 3, 3], the
+    guide's mlp_ratio = 3 example), attention runs on Q, K, V per head (no
+    mask by default), SiLU(gate) * up is the MLP, and one Linear projects
+    [attention | MLP] back (input blocks [1, 3]).  Rank r holds one buffer
+    with its rows of every in-projection block; its Q|K|V rows feed the
+    Q/K/V + RoPE GEMM and its gate|up rows the SwiGLU GEMM, in place.  Its
+    out-projection share is two row-parallel partials, one per input block,
+    and the sum runs over all 2t of them."""
+
+    def __init__(self, x, w_in: torch.Tensor, w_out: torch.Tensor, heads: int, head_dim: int, batch: int,
+                 seq: int, t: int, rope_base: float, causal: bool = False):
+        self.x, self.t, self.d = x, t, head_dim
+        self.m, self.h = x.shape
+        if heads % t:
+            raise ValueError(f"t = {t} does not divide the {heads} heads")
+        if 2 * t > tp.TP_MAX_SHARDS:
+            raise ValueError(f"t = {t}: the sum takes 2 t <= {tp.TP_MAX_SHARDS} partials")
+        self.batch, self.seq, self.base, self.causal = batch, seq, rope_base, causal
+        self.nh = heads // t
+        self.hr, self.mr = self.h // t, 3 * self.h // t
+        if self.hr != self.nh * head_dim:
+            raise ValueError("hidden size must be heads x head_dim")
+        self.w_in = [packed_colwise_weight(w_in, [1, 1, 1, 3, 3], t, r) for r in range(t)]
+        self.w_out = [packed_rowwise_weights(w_out, [1, 3], t, r) for r in range(t)]
+        dev, m = x.device, self.m
+        seq_pad = (seq + 63) // 64 * 64
+        bf = torch.bfloat16
+        self.q = torch.empty(m, self.hr, dtype=bf, device=dev)
+        self.k = torch.empty(m, self.hr, dtype=bf, device=dev)
+        self.vt = torch.empty(batch, self.nh, head_dim, seq_pad, dtype=bf, device=dev)
+        self.o = torch.empty(m, self.hr, dtype=bf, device=dev)
+        self.y = torch.empty(m, self.mr, dtype=bf, device=dev)
+        self.partials = torch.empty(2 * t, m, self.h, dtype=torch.float32, device=dev)
+        self.out = torch.empty(m, self.h, dtype=torch.float32, device=dev)
+
+    def rank(self, r: int, stream=None) -> None:
+        w, (wo_a, wo_m) = self.w_in[r], self.w_out[r]
+        hr, mr, nh, d = self.hr, self.mr, self.nh, self.d
+        tp.tp_qkv_rope(self.batch, self.seq, self.h, nh, nh, d, self.base, self.x, w[:3 * hr], self.q, self.k,
+                       self.vt, stream)
+        tp.tp_flash_attn(self.batch, self.seq, nh, nh, d, self.causal, self.q, self.k, self.vt, self.o, stream)
+        tp.tp_colwise("swiglu", "bf16", self.m, self.h, mr, self.x, w[3 * hr:], self.y, stream)
+        tp.tp_rowwise("bf16", self.m, hr, self.h, self.o, wo_a, self.partials[2 * r], stream)
+        tp.tp_rowwise("bf16", self.m, mr, self.h, self.y, wo_m, self.partials[2 * r + 1], stream)
+
+    def forward(self, stream=None):
+        for r in range(self.t):
+            self.rank(r, stream)
+        tp.tp_shard_sum(2 * self.t, self.m * self.h, list(self.partials), None, "f32", self.out, stream)
+        return self.out
+

@@ -33,6 +33,11 @@ Sources (the "Tensor parallelism" page of itwiki, by section):
 * diffusers tensor-parallel guide (style table), "rowwise_split_input": a
   row-parallel layer over a replicated input, each rank taking its own slice
   of the input features.
+* diffusers tensor-parallel guide, "Fused projections" and "Constraints and
+  validation": a Linear that packs several logical tensors along the sharded
+  dimension is sharded block by block (blocks given as proportions whose sum
+  divides the packed dimension, each block divisible by t on its own), since
+  a plain slice would cut across the packed parts.
 * "Sequence parallelism": the norms act on every token alone, so each rank
   can hold and normalise only its slice of the sequence; the sequence is
   gathered (all-gather) on entering the tensor-parallel region and, on
@@ -421,4 +426,85 @@ def sp_block(x, w: dict, case, t: int | None = None) -> dict:
     z_r = [h + red for h, red in zip(h1_r, reduce_scatter(mlp_parts, slices))]
     return {"slices": slices, "h1_slices": h1_r, "z_slices": z_r,
             "h1": all_gather(h1_r, slices, m), "z": all_gather(z_r, slices, m)}
+
+
+# --------------------------------------------------------------------------
+# packed (fused) projections (diffusers guide, "Fused projections")
+# --------------------------------------------------------------------------
+
+
+def packed_blocks(dim: int, blocks, t: int) -> list[tuple[int, int]]:
+    """(start, size) of each packed block of a dimension of ``dim``, from the
+    proportions ``blocks``; each block must be divisible by t on its own."""
+    total = sum(blocks)
+    if dim % total:
+        raise ValueError(f"packed dimension {dim} is not divisible by sum(blocks) = {total}")
+    unit = dim // total
+    out, start = [], 0
+    for b in blocks:
+        size = b * unit
+        if size % t:
+            raise ValueError(f"packed block of {size} is not divisible by t = {t}")
+        out.append((start, size))
+        start += size
+    return out
+
+
+def packed_rank_index(dim: int, blocks, t: int, rank: int) -> np.ndarray:
+    """Indices of the packed dimension rank ``rank`` holds: its 1/t of every
+    block, blocks in their packed order."""
+    return np.concatenate([np.arange(s + rank * (n // t), s + (rank + 1) * (n // t))
+                           for s, n in packed_blocks(dim, blocks, t)])
+
+
+def full_attention(q, k, v) -> np.ndarray:
+    """softmax(q k^T / sqrt(d)) v over every key (no mask)."""
+    s = (q @ k.T) / math.sqrt(q.shape[-1])
+    s = s - s.max(axis=1, keepdims=True)
+    p = np.exp(s)
+    return (p / p.sum(axis=1, keepdims=True)) @ v
+
+
+def single_stream_partial(x, w_in, w_out, heads: int, head_dim: int, batch: int, seq: int,
+                          rope_base: float, t: int = 1, rank: int = 0, causal: bool = False,
+                          naive: bool = False) -> np.ndarray:
+    """Rank ``rank``'s partial of a packed single-stream block (t = 1: the
+    whole layer):
+
+    [Q | K | V | G | U] = X W_in   (W_in [h, 9h] in math convention, blocks
+                                    [1, 1, 1, 3, 3]: the guide's mlp_ratio = 3)
+    A = attention(RoPE(Q), RoPE(K), V) per head (every head its own K, V)
+    M = SiLU(G) * U
+    out = [A | M] W_out           (W_out [4h, h], input blocks [1, 3])
+
+    The rank takes its 1/t of every block of W_in's columns (its heads and
+    its slice of the MLP) and the matching rows of each block of W_out.
+    ``naive`` instead slices both packed dimensions as plain contiguous
+    ranges, the cut the guide warns against."""
+    h = x.shape[1]
+    d = head_dim
+    if naive:
+        n_in, n_out = w_in.shape[1] // t, w_out.shape[0] // t
+        cols = np.arange(rank * n_in, (rank + 1) * n_in)
+        rows = np.arange(rank * n_out, (rank + 1) * n_out)
+    else:
+        cols = packed_rank_index(w_in.shape[1], [1, 1, 1, 3, 3], t, rank)
+        rows = packed_rank_index(w_out.shape[0], [1, 3], t, rank)
+    w = w_in[:, cols]
+    hr, mr = h // t, 3 * h // t
+    wq, wk, wv = w[:, :hr], w[:, hr:2 * hr], w[:, 2 * hr:3 * hr]
+    wg, wu = w[:, 3 * hr:3 * hr + mr], w[:, 3 * hr + mr:]
+    nh = hr // d
+    attn = np.zeros((x.shape[0], hr))
+    pos = np.arange(seq)
+    for b in range(batch):
+        xb = x[b * seq:(b + 1) * seq]
+        for j in range(nh):
+            sl = slice(j * d, (j + 1) * d)
+            q = rope(xb @ wq[:, sl], pos, rope_base)
+            k = rope(xb @ wk[:, sl], pos, rope_base)
+            v = xb @ wv[:, sl]
+            attn[b * seq:(b + 1) * seq, sl] = causal_attention(q, k, v) if causal else full_attention(q, k, v)
+    mlp = silu(x @ wg) * (x @ wu)
+    return np.concatenate([attn, mlp], axis=1) @ w_out[rows]
 

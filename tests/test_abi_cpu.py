@@ -242,3 +242,25 @@ def test_bias_pointer_checked(L):
     assert status("tp_colwise", 1, 1, 4, 16, 16, A16, A16, MIS, A16, None) == tp.TP_ERR_INVALID_ARG
     assert "bias" in tp.tp_last_error()
 
+
+def test_packed_weight_slices_match_oracle_indices():
+    """The packed-weight helpers take exactly the oracle's per-rank indices of
+    every block (host-only), and refuse blocks t does not divide."""
+    import numpy as np
+
+    import oracle
+
+    w = torch.arange(36 * 5, dtype=torch.float32).reshape(36, 5)
+    for t in (1, 2, 4):
+        for r in range(t):
+            rows = shard.packed_colwise_weight(w, [1, 1, 1, 3, 3], t, r)
+            idx = oracle.packed_rank_index(36, [1, 1, 1, 3, 3], t, r)
+            assert torch.equal(rows, w[torch.from_numpy(idx)])
+    wo = torch.arange(5 * 16, dtype=torch.float32).reshape(5, 16)
+    a, b = shard.packed_rowwise_weights(wo, [1, 3], 2, 1)
+    idx = oracle.packed_rank_index(16, [1, 3], 2, 1)
+    assert torch.equal(torch.cat([a, b], dim=1), wo[:, torch.from_numpy(idx)])
+    with pytest.raises(ValueError):
+        shard.packed_colwise_weight(w, [1, 1, 1, 3, 3], 8, 0)   # blocks of 4 rows are not divisible by 8
+    assert np.array_equal(oracle.packed_rank_index(36, [1, 1, 1, 3, 3], 2, 0)[:2], [0, 1])
+

@@ -312,6 +312,31 @@ def test_mlp_with_biases(device):
     assert np.all(np.abs(host(y) - refn) <= 2.0 ** -8 * np.abs(refn) + 1e-6)
 
 
+@pytest.mark.parametrize("t,causal", [(2, False), (4, True)])
+def test_packed_single_stream(device, t, causal):
+    """Packed single-stream block: one [1, 1, 1, 3, 3] in-projection buffer per
+    rank feeding the Q/K/V + RoPE and SwiGLU GEMMs in place, attention, and
+    the [1, 3] out-projection as two partials per rank; each rank's share and
+    the sum over ranks against the oracle."""
+    h, heads, d, batch, seq = 512, 4, 128, 2, 96
+    say(f"case packed single stream t={t} causal={causal}")
+    m = batch * seq
+    x = inputs.normal(17, 0, (m, h), 1.0, "bf16")
+    w_in = inputs.normal(17, 1, (9 * h, h), 0.02, "bf16")      # nn.Linear [out, in]
+    w_out = inputs.normal(17, 2, (h, 4 * h), 0.02, "bf16")
+    blk = shard.SingleStreamShards(to_dev(x, device), to_dev(w_in, device), to_dev(w_out, device), heads, d,
+                                   batch, seq, t, 500000.0, causal)
+    z = blk.forward()
+    torch.cuda.synchronize()
+    X, WI, WO = x.f64(), w_in.f64().T, w_out.f64().T              # math convention
+    for r in range(t):
+        ref_r = oracle.single_stream_partial(X, WI, WO, heads, d, batch, seq, 500000.0, t, r, causal)
+        got_r = host(blk.partials[2 * r]) + host(blk.partials[2 * r + 1])
+        assert rel_err(got_r, ref_r) <= BF16_TOL
+    ref = oracle.single_stream_partial(X, WI, WO, heads, d, batch, seq, 500000.0, 1, 0, causal)
+    assert rel_err(host(z), ref) <= BF16_TOL
+
+
 # ---------------------------------------------------------------- MLP, small
 
 

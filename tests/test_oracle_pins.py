@@ -475,6 +475,48 @@ def test_rowwise_split_input_identity(t):
         assert np.array_equal(p, x[:, rk * k:(rk + 1) * k] @ w[rk * k:(rk + 1) * k])
 
 
+def test_packed_blocks_rules():
+    """Blocks are proportions whose sum divides the packed dimension, each
+    block divisible by t on its own; rank r holds its 1/t of every block."""
+    assert oracle.packed_blocks(18, [1, 1, 1, 3, 3], 2) == [(0, 2), (2, 2), (4, 2), (6, 6), (12, 6)]
+    assert np.array_equal(oracle.packed_rank_index(18, [1, 1, 1, 3, 3], 2, 1),
+                          [1, 3, 5, 9, 10, 11, 15, 16, 17])
+    # [1, 1]: the SwiGLU gate/up packing, rank r = [gate_r ; up_r]
+    assert np.array_equal(oracle.packed_rank_index(16, [1, 1], 4, 2), [4, 5, 12, 13])
+    with pytest.raises(ValueError):
+        oracle.packed_blocks(20, [1, 1, 1, 3, 3], 2)          # 9 does not divide 20
+    with pytest.raises(ValueError):
+        oracle.packed_blocks(9, [1, 1, 1, 3, 3], 2)           # blocks of 1 are not divisible by 2
+    # every index of the packed dimension is held by exactly one rank
+    idx = np.concatenate([oracle.packed_rank_index(36, [1, 1, 1, 3, 3], 4, r) for r in range(4)])
+    assert np.array_equal(np.sort(idx), np.arange(36))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_packed_single_stream_identity_and_naive_cut(causal):
+    """Sharding the packed [1, 1, 1, 3, 3] in-projection and the [1, 3]
+    out-projection block by block reproduces the unsharded block (t = 2, 4);
+    cutting the packed dimensions as plain ranges does not."""
+    r = np.random.default_rng(19)
+    h, d, heads, batch, seq = 32, 4, 8, 2, 5
+    x = r.standard_normal((batch * seq, h))
+    w_in = r.standard_normal((h, 9 * h)) * 0.2
+    w_out = r.standard_normal((4 * h, h)) * 0.2
+    ref = oracle.single_stream_partial(x, w_in, w_out, heads, d, batch, seq, 10000.0, causal=causal)
+    for t in (2, 4):
+        z = oracle.shard_sum([oracle.single_stream_partial(x, w_in, w_out, heads, d, batch, seq, 10000.0, t, rk,
+                                                           causal) for rk in range(t)])
+        assert np.max(np.abs(z - ref)) <= 1e-12 * np.max(np.abs(ref))
+        bad = oracle.shard_sum([oracle.single_stream_partial(x, w_in, w_out, heads, d, batch, seq, 10000.0, t,
+                                                             rk, causal, naive=True) for rk in range(t)])
+        assert np.max(np.abs(bad - ref)) > 0.1 * np.max(np.abs(ref))
+    # the unmasked attention against PyTorch's SDPA on one head
+    q, k, v = (r.standard_normal((6, 4)) for _ in range(3))
+    import torch
+    sd = torch.nn.functional.scaled_dot_product_attention(*(torch.from_numpy(a)[None] for a in (q, k, v)))[0]
+    assert np.max(np.abs(oracle.full_attention(q, k, v) - sd.numpy())) < 1e-12
+
+
 # ---------------------------------------------------------------- inputs
 
 
