@@ -149,7 +149,7 @@ def per_config_report(dev):
     none of their inputs."""
     import torch
 
-    from megatron_tensor_transformer_colwise_amd import inputs, shard
+    from megatron_tensor_transformer_colwise_amd import inputs, shard, tpshard as tp
 
     scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
 
@@ -255,6 +255,29 @@ def per_config_report(dev):
           "all_ranks_and_sum_ms": round(fms, 4), "all_ranks_tflops": rate(t * rfl, fms),
           "shape": f"h={h}, {heads} heads of {d}, mlp {3 * h}, {seq} tokens, t={t}, no mask"})
     del ss, x, w_in, w_out
+
+    # vocabulary-parallel output layer + cross-entropy: h = 4096, vocabulary
+    # 128256 over t = 4 ranks, 4096 tokens (the Llama-8B shapes of the other
+    # workloads), labels seeded uniform
+    h, v, m, t = 4096, 128256, 4096, 4
+    log("configs: vocab_parallel_ce")
+    x = inputs.normal(82, 0, (m, h), 1.0, "bf16").torch().to(dev)
+    w = inputs.normal(82, 1, (v, h), 0.02, "bf16").torch().to(dev)
+    import numpy as _np
+    labels = torch.from_numpy(_np.random.default_rng(82).integers(0, v, m).astype(_np.int32)).to(dev)
+    ce = shard.VocabParallelCE(x, w, t)
+    n = v // t
+    gfl = 2.0 * m * h * n
+    rms, rmn = _time(lambda: ce.rank(0, labels))
+    sms, smn = _time(lambda: tp.tp_ce_stats(m, n, 0, ce.logits, labels, ce.stats[0]))
+    fms, fmn = _time(lambda: ce.forward(labels), reps=10, warm=2)
+    emit({"workload": "vocab_parallel_ce", "call": "one rank: logits GEMM (float32) + max/sum/label statistics",
+          "ms": round(rms, 4), "min_ms": round(rmn, 4), "tflops": rate(gfl, rms),
+          "pct_mfma_peak": round(100.0 * gfl / rms / 1e9 / MFMA_BF16_PEAK_TFLOPS, 2),
+          "stats_ms": round(sms, 4), "stats_gbs": round(4.0 * m * n / sms / 1e6, 1),
+          "all_ranks_and_combine_ms": round(fms, 4), "all_ranks_tflops": rate(t * gfl, fms),
+          "shape": f"h={h}, vocabulary {v} over t={t}, {m} tokens"})
+    del ce, x, w
     del scratch
 
 

@@ -277,6 +277,49 @@ tp_status tp_shard_sum_rmsnorm(int32_t t, int64_t nrun, int64_t run_rows, int64_
                                void* stream);
 
 /* --------------------------------------------------------------------------
+ * Vocabulary-parallel embedding and cross-entropy ("Tensor parallelism"
+ * page, section "Embedding and output layer": the embedding matrix is split
+ * along the vocabulary; rather than gathering the b x s x v output logits,
+ * each rank computes from its own slice the maximum and the sum the
+ * cross-entropy needs, and only b x s values cross between ranks;
+ * transformers "Tensor parallelism" page, EmbeddingParallel).
+ *
+ * tp_embedding: out[i, 0:w] = table[ids[i] - v_start, 0:w] for ids in
+ * [v_start, v_start + v_rows), zeros otherwise (float32 out, rows ld apart).
+ *   vocabulary-sharded lookup (embedding_rowwise): rank r passes its rows
+ *     [r v/t, (r+1) v/t) of the [v, h] table, w = ld = h, and out is its
+ *     partial: the sum over ranks (tp_shard_sum) is the lookup, exactly;
+ *   hidden-sharded lookup (embedding_colwise): rank r passes its columns
+ *     [v, h/t] of the table, v_start = 0, v_rows = v, w = h/t, ld = h, out at
+ *     column r h/t of the gathered [m, h] buffer.
+ *   ids      [m] int32; table [v_rows, w] bf16; out float32
+ *
+ * tp_vocab_logits: logits[m, v_shard] = x [m, h] . w[v_shard, h]^T, float32
+ * (bf16 operands): the rank's slice of the output layer (its vocabulary rows).
+ *
+ * tp_ce_stats: for each token i, stats[i] = { max_j x_j, sum_j exp(x_j - max),
+ * x at the label if the label is in [v_start, v_start + v_shard) else 0,
+ * 1 if it is else 0 } over the rank's logits x = logits[i, 0:v_shard).
+ *   labels [m] int32 (a label outside [0, v) marks an ignored token);
+ *   stats [m, 4] float32.
+ *
+ * tp_ce_combine: the exchange's result: for each token, with M = max_r max_r
+ * and S = sum_r sum_r exp(max_r - M) (ranks in ascending order),
+ *   loss[i] = log S + M - x_label    (0 for an ignored token)
+ * and, if mean is not NULL, mean[0] = the average over non-ignored tokens.
+ *   stats  HOST array of t device pointers [m, 4] (rank r's statistics; on
+ *          one device, rows of one [t, m, 4] buffer)
+ * ------------------------------------------------------------------------ */
+tp_status tp_embedding(int64_t m, int64_t w, int64_t v_start, int64_t v_rows, const int32_t* ids,
+                       const void* table, float* out, int64_t ld, void* stream);
+tp_status tp_vocab_logits(int64_t m, int64_t h, int64_t v_shard, const void* x, const void* w, float* logits,
+                          void* stream);
+tp_status tp_ce_stats(int64_t m, int64_t v_shard, int64_t v_start, const float* logits, const int32_t* labels,
+                      float* stats, void* stream);
+tp_status tp_ce_combine(int32_t t, int64_t m, int64_t v, const float* const* stats, const int32_t* labels,
+                        float* loss, float* mean, void* stream);
+
+/* --------------------------------------------------------------------------
  * Introspection: how the bf16 GEMM behind tp_colwise / tp_rowwise /
  * tp_qkv_rope tiles an m x n output (n = output columns; swiglu != 0 for the
  * SwiGLU colwise GEMM, whose tiles cover 128 output columns instead of 256).

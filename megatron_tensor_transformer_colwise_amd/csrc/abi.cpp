@@ -408,4 +408,63 @@ tp_status tp_shard_sum_rmsnorm(int32_t t, int64_t nrun, int64_t run_rows, int64_
                   "tp_shard_sum_rmsnorm");
 }
 
+tp_status tp_embedding(int64_t m, int64_t w, int64_t v_start, int64_t v_rows, const int32_t* ids,
+                       const void* table, float* out, int64_t ld, void* stream) {
+  if (m < 0) return fail(TP_ERR_SHAPE, "m = %lld is negative", (long long)m);
+  TRY(check_dim8(w, "w"));
+  if (v_start < 0 || v_rows < 0) return fail(TP_ERR_SHAPE, "v_start and v_rows must be >= 0");
+  if (ld < w || ld % 8 != 0) return fail(TP_ERR_SHAPE, "ld = %lld must be >= w and a multiple of 8", (long long)ld);
+  if (m == 0) return ok();
+  if (m > 0x7FFFFFFF) return fail(TP_ERR_SHAPE, "m too large");
+  TRY(check_ptr(ids, "ids"));
+  if (v_rows > 0) TRY(check_ptr(table, "table"));
+  TRY(check_ptr(out, "out"));
+  TRY(device_check());
+  return launched(tpk::launch_embedding(m, w, v_start, v_rows, ids, table, out, ld, as_stream(stream)),
+                  "tp_embedding");
+}
+
+tp_status tp_vocab_logits(int64_t m, int64_t h, int64_t v_shard, const void* x, const void* w, float* logits,
+                          void* stream) {
+  TRY(check_gemm(TP_ACT_NONE, TP_BF16, m, h, v_shard, x, w, logits, "x", "w", "logits"));
+  if (m == 0) return ok();
+  TRY(device_check());
+  return launched(tpk::launch_gemm_bf16(tpk::EPI_F32, m, v_shard, h, x, w, logits, nullptr, as_stream(stream)),
+                  "tp_vocab_logits");
+}
+
+tp_status tp_ce_stats(int64_t m, int64_t v_shard, int64_t v_start, const float* logits, const int32_t* labels,
+                      float* stats, void* stream) {
+  if (m < 0) return fail(TP_ERR_SHAPE, "m = %lld is negative", (long long)m);
+  TRY(check_dim8(v_shard, "v_shard"));
+  if (v_start < 0) return fail(TP_ERR_SHAPE, "v_start must be >= 0");
+  if (m == 0) return ok();
+  if (m > 0x7FFFFFFF) return fail(TP_ERR_SHAPE, "m too large");
+  TRY(check_ptr(logits, "logits"));
+  TRY(check_ptr(labels, "labels"));
+  TRY(check_ptr(stats, "stats"));
+  TRY(device_check());
+  return launched(tpk::launch_ce_stats(m, v_shard, v_start, logits, labels, stats, as_stream(stream)),
+                  "tp_ce_stats");
+}
+
+tp_status tp_ce_combine(int32_t t, int64_t m, int64_t v, const float* const* stats, const int32_t* labels,
+                        float* loss, float* mean, void* stream) {
+  if (t < 1 || t > TP_MAX_SHARDS) return fail(TP_ERR_SHAPE, "t = %d outside 1..%d", t, TP_MAX_SHARDS);
+  if (m < 0) return fail(TP_ERR_SHAPE, "m = %lld is negative", (long long)m);
+  if (v < 1) return fail(TP_ERR_SHAPE, "v = %lld must be >= 1", (long long)v);
+  if (m == 0) return ok();
+  if (!stats) return fail(TP_ERR_INVALID_ARG, "stats is NULL");
+  for (int r = 0; r < t; ++r) {
+    char name[32];
+    snprintf(name, sizeof(name), "stats[%d]", r);
+    TRY(check_ptr(stats[r], name));
+  }
+  TRY(check_ptr(labels, "labels"));
+  TRY(check_ptr(loss, "loss"));
+  if (mean) TRY(check_ptr(mean, "mean"));
+  TRY(device_check());
+  return launched(tpk::launch_ce_combine(t, m, stats, loss, labels, v, mean, as_stream(stream)), "tp_ce_combine");
+}
+
 }  // extern "C"

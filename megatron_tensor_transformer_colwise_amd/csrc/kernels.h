@@ -70,4 +70,19 @@ hipError_t launch_sum_rmsnorm(int t, int64_t nrun, int64_t run_rows, int64_t run
                               int residual_bf16, float* out, const float* gain, float eps, void* y,
                               hipStream_t s);
 
+// out[i, 0:w] (rows ld apart, float32) = table[ids[i] - v_start] (bf16) for
+// ids in [v_start, v_start + v_rows), else zeros.
+hipError_t launch_embedding(int64_t m, int64_t w, int64_t v_start, int64_t v_rows, const int32_t* ids,
+                            const void* table, float* out, int64_t ld, hipStream_t s);
+
+// stats[i] = {max, sum of exp(x - max), x_label or 0, 1 if the label is the
+// rank's} over logits[i, 0:n) (float32), the rank's vocabulary [v_start, v_start + n).
+hipError_t launch_ce_stats(int64_t m, int64_t n, int64_t v_start, const float* logits, const int32_t* labels,
+                           float* stats, hipStream_t s);
+
+// Per-token loss from the t ranks' statistics, and (if mean) the mean over
+// tokens whose label is in [0, v).
+hipError_t launch_ce_combine(int t, int64_t m, const float* const* stats, float* loss, const int32_t* labels,
+                             int64_t v, float* mean, hipStream_t s);
+
 }  // namespace tpk

@@ -361,3 +361,67 @@ class SingleStreamShards:
         tp.tp_shard_sum(2 * self.t, self.m * self.h, list(self.partials), None, "f32", self.out, stream)
         return self.out
 
+
+# ---------------------------------------------------------------- vocabulary-parallel embedding and loss
+
+
+def embedding_rowwise(ids, table: torch.Tensor, t: int, partials=None, out=None, stream=None):
+    """Vocabulary-sharded lookup, every rank on one device: rank r holds rows
+    [r v/t, (r+1) v/t) of the [v, h] table, looks up the ids it holds (zeros
+    for the others), and the ranks' partials are summed."""
+    v, h = table.shape
+    if v % t:
+        raise ValueError(f"vocabulary {v} is not divisible by t = {t}")
+    n, m = v // t, ids.shape[0]
+    partials = torch.empty(t, m, h, dtype=torch.float32, device=table.device) if partials is None else partials
+    out = torch.empty(m, h, dtype=torch.float32, device=table.device) if out is None else out
+    for r in range(t):
+        tp.tp_embedding(m, h, r * n, n, ids, table[r * n:(r + 1) * n], partials[r], h, stream)
+    tp.tp_shard_sum(t, m * h, list(partials), None, "f32", out, stream)
+    return out
+
+
+def embedding_colwise(ids, table: torch.Tensor, t: int, out=None, stream=None):
+    """Hidden-sharded lookup: rank r holds columns [r h/t, (r+1) h/t) of every
+    row and writes its slice into the gathered [m, h] output."""
+    v, h = table.shape
+    if h % t or (h // t) % 8:
+        raise ValueError(f"hidden {h} is not a multiple of 8 t (t = {t})")
+    hs, m = h // t, ids.shape[0]
+    out = torch.empty(m, h, dtype=torch.float32, device=table.device) if out is None else out
+    for r in range(t):
+        tp.tp_embedding(m, hs, 0, v, ids, table[:, r * hs:(r + 1) * hs].contiguous(), out[:, r * hs:], h, stream)
+    return out
+
+
+class VocabParallelCE:
+    """Output layer and cross-entropy with the vocabulary split over t ranks,
+    every rank on one device: rank r computes its [m, v/t] logits and, from
+    them, per token the max, the sum of exponentials and the label's logit
+    (if it holds the label); combining the ranks' statistics gives the loss
+    without ever gathering the [m, v] logits."""
+
+    def __init__(self, x, w: torch.Tensor, t: int):
+        v, h = w.shape                                  # nn.Linear layout [vocab, hidden]
+        if v % t or (v // t) % 8:
+            raise ValueError(f"vocabulary {v} must split into t = {t} slices of a multiple of 8")
+        self.x, self.t, self.v, self.h = x, t, v, h
+        self.n = v // t
+        self.m = x.shape[0]
+        self.w = [w[r * self.n:(r + 1) * self.n] for r in range(t)]
+        dev = x.device
+        self.logits = torch.empty(self.m, self.n, dtype=torch.float32, device=dev)
+        self.stats = torch.empty(t, self.m, 4, dtype=torch.float32, device=dev)
+        self.loss = torch.empty(self.m, dtype=torch.float32, device=dev)
+        self.mean = torch.empty(1, dtype=torch.float32, device=dev)
+
+    def rank(self, r: int, labels, stream=None) -> None:
+        tp.tp_vocab_logits(self.m, self.h, self.n, self.x, self.w[r], self.logits, stream)
+        tp.tp_ce_stats(self.m, self.n, r * self.n, self.logits, labels, self.stats[r], stream)
+
+    def forward(self, labels, stream=None):
+        for r in range(self.t):
+            self.rank(r, labels, stream)
+        tp.tp_ce_combine(self.t, self.m, self.v, list(self.stats), labels, self.loss, self.mean, stream)
+        return self.loss, self.mean
+

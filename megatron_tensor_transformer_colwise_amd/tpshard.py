@@ -58,6 +58,10 @@ _SIGS = {
     "tp_shard_sum_rmsnorm": [_i32, _i64, _i64, _i64, _i64, ctypes.POINTER(_vp), _vp, _vp, _i32, _vp, _vp,
                              _f32, _vp, _vp],
     "tp_gemm_plan": [_i64, _i64, _i32, ctypes.POINTER(_i32), ctypes.POINTER(_i32), ctypes.POINTER(_i32)],
+    "tp_embedding": [_i64, _i64, _i64, _i64, _vp, _vp, _vp, _i64, _vp],
+    "tp_vocab_logits": [_i64, _i64, _i64, _vp, _vp, _vp, _vp],
+    "tp_ce_stats": [_i64, _i64, _i64, _vp, _vp, _vp, _vp],
+    "tp_ce_combine": [_i32, _i64, _i64, ctypes.POINTER(_vp), _vp, _vp, _vp, _vp],
     "tp_last_error": [],
     "tp_device_check": [],
 }
@@ -193,3 +197,21 @@ def tp_shard_sum_rmsnorm(t, m, h, partials, residual, residual_dt, out, gain, ep
     arr = (_vp * max(len(partials), 1))(*[_p(p) for p in partials])
     _check(lib().tp_shard_sum_rmsnorm(t, nrun, run_rows, run_stride, h, arr, _p(bias), _p(residual),
                                       _e(residual_dt, DTYPES), _p(out), _p(gain), eps, _p(y), _s(stream)))
+
+
+def tp_embedding(m, w, v_start, v_rows, ids, table, out, ld, stream=None) -> None:
+    _check(lib().tp_embedding(m, w, v_start, v_rows, _p(ids), _p(table), _p(out), ld, _s(stream)))
+
+
+def tp_vocab_logits(m, h, v_shard, x, w, logits, stream=None) -> None:
+    _check(lib().tp_vocab_logits(m, h, v_shard, _p(x), _p(w), _p(logits), _s(stream)))
+
+
+def tp_ce_stats(m, v_shard, v_start, logits, labels, stats, stream=None) -> None:
+    _check(lib().tp_ce_stats(m, v_shard, v_start, _p(logits), _p(labels), _p(stats), _s(stream)))
+
+
+def tp_ce_combine(t, m, v, stats, labels, loss, mean, stream=None) -> None:
+    arr = (_vp * max(len(stats), 1))(*[_p(p) for p in stats])
+    _check(lib().tp_ce_combine(t, m, v, arr, _p(labels), _p(loss), _p(mean), _s(stream)))
+

@@ -38,6 +38,12 @@ Sources (the "Tensor parallelism" page of itwiki, by section):
   dimension is sharded block by block (blocks given as proportions whose sum
   divides the packed dimension, each block divisible by t on its own), since
   a plain slice would cut across the packed parts.
+* "Embedding and output layer": the embedding matrix is split along the
+  vocabulary; instead of gathering the b x s x v logits, each rank computes
+  from its own slice the maximum and the sum the cross-entropy needs, so only
+  b x s values are exchanged.  transformers "Tensor parallelism" page,
+  EmbeddingParallel: a vocabulary-sharded lookup sums the ranks' partial
+  lookups; a hidden-sharded one gathers their column slices.
 * "Sequence parallelism": the norms act on every token alone, so each rank
   can hold and normalise only its slice of the sequence; the sequence is
   gathered (all-gather) on entering the tensor-parallel region and, on
@@ -507,4 +513,89 @@ def single_stream_partial(x, w_in, w_out, heads: int, head_dim: int, batch: int,
             attn[b * seq:(b + 1) * seq, sl] = causal_attention(q, k, v) if causal else full_attention(q, k, v)
     mlp = silu(x @ wg) * (x @ wu)
     return np.concatenate([attn, mlp], axis=1) @ w_out[rows]
+
+
+# --------------------------------------------------------------------------
+# vocabulary-parallel embedding and cross-entropy ("Embedding and output layer")
+# --------------------------------------------------------------------------
+
+
+def embedding_lookup(table, ids) -> np.ndarray:
+    """Row ids[i] of the [v, h] table for every token (nn.Embedding layout;
+    the page writes E in R^{h x v}, the same matrix transposed)."""
+    return np.asarray(table, dtype=np.float64)[np.asarray(ids)]
+
+
+def embedding_rowwise_partials(table, ids, t: int) -> list[np.ndarray]:
+    """Rank r holds vocabulary rows [r v/t, (r+1) v/t): its partial is the row
+    for the ids it holds and zero for the others; the sum is the lookup."""
+    table = np.asarray(table, dtype=np.float64)
+    ids = np.asarray(ids)
+    v = table.shape[0]
+    if v % t:
+        raise ValueError(f"vocabulary {v} is not divisible by t = {t}")
+    n = v // t
+    out = []
+    for r in range(t):
+        mine = (ids >= r * n) & (ids < (r + 1) * n)
+        p = np.zeros((len(ids), table.shape[1]))
+        p[mine] = table[ids[mine]]
+        out.append(p)
+    return out
+
+
+def embedding_colwise_slices(table, ids, t: int) -> list[np.ndarray]:
+    """Rank r holds hidden columns [r h/t, (r+1) h/t) of every row; gathering
+    the slices side by side gives the lookup."""
+    return [embedding_lookup(c, ids) for c in split_columns(np.asarray(table, dtype=np.float64), t)]
+
+
+def cross_entropy(logits, labels, v: int | None = None) -> tuple[np.ndarray, float]:
+    """Per-token loss log(sum_j exp x_j) - x_label and the mean over tokens
+    whose label lies in [0, v) (others are ignored: loss 0)."""
+    x = np.asarray(logits, dtype=np.float64)
+    labels = np.asarray(labels)
+    v = x.shape[1] if v is None else v
+    ok = (labels >= 0) & (labels < v)
+    mx = x.max(axis=1)
+    lse = np.log(np.exp(x - mx[:, None]).sum(axis=1)) + mx
+    loss = np.where(ok, lse - x[np.arange(len(labels)), np.where(ok, labels, 0)], 0.0)
+    return loss, (float(loss[ok].mean()) if ok.any() else 0.0)
+
+
+def vocab_ce_stats(logits_r, labels, v_start: int) -> np.ndarray:
+    """One rank's statistics per token from its slice of the logits (its
+    vocabulary [v_start, v_start + n)): max, sum of exp(x - max), the label's
+    logit if the rank holds the label (else 0), and 1 if it does (else 0)."""
+    x = np.asarray(logits_r, dtype=np.float64)
+    labels = np.asarray(labels)
+    n = x.shape[1]
+    mx = x.max(axis=1)
+    s = np.exp(x - mx[:, None]).sum(axis=1)
+    mine = (labels >= v_start) & (labels < v_start + n)
+    z = np.where(mine, x[np.arange(len(labels)), np.clip(labels - v_start, 0, n - 1)], 0.0)
+    return np.stack([mx, s, z, mine.astype(np.float64)], axis=1)
+
+
+def vocab_ce_combine(stats) -> np.ndarray:
+    """Per-token loss from every rank's statistics (the b x s exchange):
+    M = max_r max_r, S = sum_r sum_r exp(max_r - M), loss = log S + M - x_label;
+    a token no rank holds the label of is ignored (loss 0)."""
+    st = np.stack([np.asarray(s, dtype=np.float64) for s in stats])   # [t, m, 4]
+    mx = st[:, :, 0].max(axis=0)
+    s = (st[:, :, 1] * np.exp(st[:, :, 0] - mx[None, :])).sum(axis=0)
+    z = st[:, :, 2].sum(axis=0)
+    owners = st[:, :, 3].sum(axis=0)
+    return np.where(owners == 1, np.log(s) + mx - z, 0.0)
+
+
+def vocab_parallel_ce(x, w_out, labels, t: int) -> np.ndarray:
+    """Per-token loss of the output layer X W_out (W_out [h, v]) with the
+    vocabulary split over t ranks: each rank's logits, its statistics, then
+    the combination."""
+    v = w_out.shape[1]
+    if v % t:
+        raise ValueError(f"vocabulary {v} is not divisible by t = {t}")
+    n = v // t
+    return vocab_ce_combine([vocab_ce_stats(x @ w_out[:, r * n:(r + 1) * n], labels, r * n) for r in range(t)])
 

@@ -264,3 +264,19 @@ def test_packed_weight_slices_match_oracle_indices():
         shard.packed_colwise_weight(w, [1, 1, 1, 3, 3], 8, 0)   # blocks of 4 rows are not divisible by 8
     assert np.array_equal(oracle.packed_rank_index(36, [1, 1, 1, 3, 3], 2, 0)[:2], [0, 1])
 
+
+def test_vocab_parallel_validation(L):
+    assert status("tp_embedding", 4, 12, 0, 10, A16, A16, A16, 16, None) == tp.TP_ERR_SHAPE     # w not x8
+    assert status("tp_embedding", 4, 16, 0, 10, A16, A16, A16, 8, None) == tp.TP_ERR_SHAPE      # ld < w
+    assert status("tp_embedding", 4, 16, -1, 10, A16, A16, A16, 16, None) == tp.TP_ERR_SHAPE
+    assert status("tp_embedding", 4, 16, 0, 10, MIS, A16, A16, 16, None) == tp.TP_ERR_INVALID_ARG
+    assert status("tp_embedding", 0, 16, 0, 10, None, None, None, 16, None) == tp.TP_OK
+    assert status("tp_vocab_logits", 4, 16, 12, A16, A16, A16, None) == tp.TP_ERR_SHAPE           # v_shard not x8
+    assert status("tp_ce_stats", 4, 12, 0, A16, A16, A16, None) == tp.TP_ERR_SHAPE
+    assert status("tp_ce_stats", 4, 16, 0, A16, None, A16, None) == tp.TP_ERR_INVALID_ARG
+    arr = (ctypes.c_void_p * 2)(A16, MIS)
+    assert status("tp_ce_combine", 0, 4, 16, arr, A16, A16, None, None) == tp.TP_ERR_SHAPE
+    assert status("tp_ce_combine", 2, 4, 0, arr, A16, A16, None, None) == tp.TP_ERR_SHAPE
+    assert status("tp_ce_combine", 2, 4, 16, arr, A16, A16, None, None) == tp.TP_ERR_INVALID_ARG
+    assert "stats[1]" in tp.tp_last_error()
+

@@ -337,6 +337,60 @@ def test_packed_single_stream(device, t, causal):
     assert rel_err(host(z), ref) <= BF16_TOL
 
 
+# ---------------------------------------------------------------- vocabulary parallel
+
+
+@pytest.mark.parametrize("t", [1, 4])
+def test_vocab_parallel_embedding(device, t):
+    """Vocabulary-sharded lookup (partials summed) and hidden-sharded lookup
+    (slices gathered): exactly the table's rows, ids on every shard boundary."""
+    v, h, m = 1000, 264, 333
+    say(f"case embedding t={t}")
+    table = inputs.normal(61, 0, (v, h), 1.0, "bf16")
+    n = v // t
+    ids = np.concatenate([np.array([0, v - 1] + [r * n for r in range(t)] + [r * n - 1 for r in range(1, t)]),
+                          np.random.default_rng(5).integers(0, v, m)]).astype(np.int32)[:m]
+    d_ids = torch.from_numpy(ids).to(device)
+    dt = to_dev(table, device)
+    ref = oracle.embedding_lookup(table.f64(), ids)
+    got = shard.embedding_rowwise(d_ids, dt, t)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(got), ref)
+    if h % (8 * t) == 0:
+        got = shard.embedding_colwise(d_ids, dt, t)
+        torch.cuda.synchronize()
+        assert np.array_equal(host(got), ref)
+
+
+@pytest.mark.parametrize("t,m,h,v", [(1, 300, 512, 1000), (4, 300, 512, 4096), (8, 1000, 256, 32768)])
+def test_vocab_parallel_cross_entropy(device, t, m, h, v):
+    """Per-token loss and mean from the ranks' statistics, against the oracle
+    (float64, same bf16 inputs); the statistics themselves against the
+    oracle's on the GPU's own logits; ignored labels give 0."""
+    say(f"case vocab-parallel CE t={t} m={m} h={h} v={v}")
+    x = inputs.normal(62, 0, (m, h), 1.0, "bf16")
+    w = inputs.normal(62, 1, (v, h), 0.05, "bf16")            # nn.Linear [vocab, hidden]
+    labels = np.random.default_rng(6).integers(0, v, m).astype(np.int32)
+    labels[[3, 17]] = -100
+    d_lab = torch.from_numpy(labels).to(device)
+    ce = shard.VocabParallelCE(to_dev(x, device), to_dev(w, device), t)
+    loss, mean = ce.forward(d_lab)
+    torch.cuda.synchronize()
+    X, W = x.f64(), w.f64()
+    ref = oracle.vocab_parallel_ce(X, W.T, labels, t)
+    got = host(loss)
+    assert got[3] == 0 and got[17] == 0
+    assert np.max(np.abs(got - ref)) <= 1e-3 * max(1.0, np.max(np.abs(ref)))
+    ok = labels >= 0
+    assert abs(float(mean.item()) - ref[ok].mean()) <= 1e-3 * max(1.0, abs(ref[ok].mean()))
+    # the last rank's statistics against the oracle's on the same float32 logits
+    n = v // t
+    st = oracle.vocab_ce_stats(host(ce.logits), labels, (t - 1) * n)
+    gs = host(ce.stats[t - 1])
+    assert np.array_equal(gs[:, 0], st[:, 0]) and np.array_equal(gs[:, 2:], st[:, 2:])
+    assert np.max(np.abs(gs[:, 1] / st[:, 1] - 1)) <= 1e-5
+
+
 # ---------------------------------------------------------------- MLP, small
 
 

@@ -517,6 +517,75 @@ def test_packed_single_stream_identity_and_naive_cut(causal):
     assert np.max(np.abs(oracle.full_attention(q, k, v) - sd.numpy())) < 1e-12
 
 
+# ---------------------------------------------------------------- vocabulary parallel
+
+
+def test_vocab_parallel_embedding_exact():
+    """Partial lookups over vocabulary shards sum to the lookup exactly, ids at
+    every shard boundary included; hidden-sharded slices side by side are the
+    lookup."""
+    r = np.random.default_rng(23)
+    v, h = 48, 12
+    table = r.standard_normal((v, h))
+    ids = np.array([0, 11, 12, 23, 24, 47, 5, 30, 12, 0])
+    for t in (1, 2, 4, 6):
+        parts = oracle.embedding_rowwise_partials(table, ids, t)
+        assert np.array_equal(oracle.shard_sum(parts), table[ids])
+        assert all(np.count_nonzero(np.any(p != 0, axis=1)) <= len(ids) for p in parts)
+    for t in (1, 2, 3, 4):
+        assert np.array_equal(np.concatenate(oracle.embedding_colwise_slices(table, ids, t), axis=1), table[ids])
+
+
+def test_cross_entropy_closed_forms_and_library():
+    """Uniform logits give log v; a label logit far above the rest gives ~0;
+    shifting all logits changes nothing; PyTorch cross_entropy in float64;
+    ignored labels give 0 and leave the mean."""
+    import torch
+    import torch.nn.functional as F
+
+    v = 37
+    loss, mean = oracle.cross_entropy(np.zeros((3, v)), [0, 5, 36])
+    assert np.allclose(loss, np.log(v), atol=1e-15) and abs(mean - np.log(v)) < 1e-15
+    x = np.zeros((1, v))
+    x[0, 7] = 60.0
+    assert oracle.cross_entropy(x, [7])[0][0] < 1e-24
+    r = np.random.default_rng(29)
+    x = r.standard_normal((9, v)) * 4
+    labels = r.integers(0, v, 9)
+    loss, mean = oracle.cross_entropy(x, labels)
+    assert np.max(np.abs(oracle.cross_entropy(x + 1e4, labels)[0] - loss)) < 1e-9
+    ref = F.cross_entropy(torch.from_numpy(x), torch.from_numpy(labels), reduction="none").numpy()
+    assert np.max(np.abs(loss - ref)) < 1e-13
+    labels2 = labels.copy()
+    labels2[[1, 4]] = -100
+    loss2, mean2 = oracle.cross_entropy(x, labels2, v)
+    assert loss2[1] == 0 and loss2[4] == 0
+    ok = np.ones(9, bool)
+    ok[[1, 4]] = False
+    assert abs(mean2 - loss[ok].mean()) < 1e-13
+
+
+@pytest.mark.parametrize("t", [1, 2, 4, 8])
+def test_vocab_parallel_ce_identity(t):
+    """Combining the ranks' (max, sum, label logit) statistics gives the
+    unsharded cross-entropy of X W_out for every token; an ignored label is 0
+    on every split."""
+    r = np.random.default_rng(37)
+    m, h, v = 10, 16, 64
+    x, w = r.standard_normal((m, h)), r.standard_normal((h, v))
+    labels = r.integers(0, v, m)
+    labels[3] = -100
+    ref, _ = oracle.cross_entropy(x @ w, labels, v)
+    got = oracle.vocab_parallel_ce(x, w, labels, t)
+    assert np.max(np.abs(got - ref)) <= 1e-12 * max(1.0, np.max(np.abs(ref)))
+    assert got[3] == 0
+    # the statistics of the rank holding a label carry its logit
+    n = v // t
+    owner = labels[0] // n
+    st = oracle.vocab_ce_stats((x @ w)[:, owner * n:(owner + 1) * n], labels, owner * n)
+    assert st[0, 3] == 1 and abs(st[0, 2] - (x @ w)[0, labels[0]]) < 1e-12
+
+
 # ---------------------------------------------------------------- inputs
 
 
