@@ -278,6 +278,23 @@ def per_config_report(dev):
           "all_ranks_and_combine_ms": round(fms, 4), "all_ranks_tflops": rate(t * gfl, fms),
           "shape": f"h={h}, vocabulary {v} over t={t}, {m} tokens"})
     del ce, x, w
+
+    # backward of one rank's SwiGLU MLP at the 70B block's shape (t = 8)
+    case = inputs.MLPCase("llama70b_mlp_t8", 8192, 8192, 28672, 8, "swiglu", "bf16", seed=83)
+    log("configs: llama70b_mlp_backward_t8")
+    dw = {k: v.torch().to(dev) for k, v in inputs.gen_mlp(case).items()}
+    dz = inputs.normal(83, 9, (case.tokens, case.hidden), 1.0, "bf16").torch().to(dev)
+    mlp = shard.MLPShards(dw["X"], dw, case.t, "swiglu")
+    m, h, f = case.tokens, case.hidden, case.f_shard
+    bwd_fl = 2.0 * m * h * f * (1 + 2 + 1 + 2)      # dY, dX (2f), dW_out, dW_in (2f)
+    rec_fl = 2.0 * m * h * 2 * f                    # the recomputed pre-activation
+    bms, bmn = _time(lambda: mlp.backward_rank(0, dz), reps=10, warm=3)
+    emit({"workload": "llama70b_mlp_backward_t8", "call": "tp_shard_mlp_backward (one rank, SwiGLU)",
+          "ms": round(bms, 4), "min_ms": round(bmn, 4), "tflops": rate(bwd_fl + rec_fl, bms),
+          "pct_mfma_peak": round(100.0 * (bwd_fl + rec_fl) / bms / 1e9 / MFMA_BF16_PEAK_TFLOPS, 2),
+          "backward_only_tflops": rate(bwd_fl, bms),
+          "shape": f"m={m}, h={h}, f_shard={f} (t=8), weight gradients float32"})
+    del mlp, dw, dz
     del scratch
 
 
@@ -293,6 +310,8 @@ def main():
                     help="per-call report for every workload (one JSON line each) instead of the step")
     ap.add_argument("--pmc-pass", action="store_true",
                     help="launch only a 256 MiB copy and the SwiGLU GEMM (for counter runs)")
+    ap.add_argument("--bwd-pass", action="store_true",
+                    help="run one rank's SwiGLU MLP backward at the 70B t=8 shape four times (for a kernel trace)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -314,6 +333,17 @@ def main():
 
     if args.configs:
         per_config_report(dev)
+        return
+
+    if args.bwd_pass:
+        case = inputs.MLPCase("llama70b_mlp_t8", 8192, 8192, 28672, 8, "swiglu", "bf16", seed=83)
+        dw = {k: v.torch().to(dev) for k, v in inputs.gen_mlp(case).items()}
+        dz = inputs.normal(83, 9, (case.tokens, case.hidden), 1.0, "bf16").torch().to(dev)
+        mlp = shard.MLPShards(dw["X"], dw, case.t, "swiglu")
+        for _ in range(4):
+            mlp.backward_rank(0, dz)
+        torch.cuda.synchronize()
+        log("backward pass done")
         return
 
     case = inputs.CONFIGS[args.config]

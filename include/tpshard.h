@@ -320,6 +320,39 @@ tp_status tp_ce_combine(int32_t t, int64_t m, int64_t v, const float* const* sta
                         float* loss, float* mean, void* stream);
 
 /* --------------------------------------------------------------------------
+ * Backward pass of one rank's MLP ("Tensor parallelism" page, section "f and
+ * g": g's backward is the identity, so every rank receives the whole output
+ * gradient dZ; f's backward sums the ranks' input-gradient partials, one
+ * all-reduce; a block's backward has two).  bf16 operands, float32
+ * accumulation; weights as in tp_shard_mlp.
+ *
+ *   pre  = x w_in^T                          (recomputed pre-activation, [m, F])
+ *   dY   = dZ w_out                          [m, f]
+ *   dPre = dY * act'(pre)                    (GeLU; or [dY u SiLU'(g) | dY SiLU(g)]
+ *                                             for pre = [g | u], SwiGLU)
+ *   dx_partial = dPre w_in                   [m, h] float32 (the rank's share of dX)
+ *   dw_out = dZ^T act(pre)                   [h, f] float32
+ *   dw_in  = dPre^T x                        [F, h] float32
+ * with F = f (GeLU) or 2 f (SwiGLU, rows [W1_i^T ; W3_i^T] as in the forward).
+ *
+ *   x, dz       [m, h] bf16; m must be a multiple of 8
+ *   xt, dzt     [h, m] bf16 transposes of x and dz, or NULL (then the call
+ *               makes them in ws; on one device the ranks may share them)
+ *   ws          workspace of tp_shard_mlp_backward_workspace_bytes bytes
+ *
+ * tp_transpose: dst [cols, rows] = src [rows, cols]^T (bf16).
+ * tp_mlp_act_backward: the dPre step alone (and Y if y is not NULL).
+ * ------------------------------------------------------------------------ */
+size_t tp_shard_mlp_backward_workspace_bytes(tp_act act, int64_t m, int64_t h, int64_t f_shard);
+tp_status tp_shard_mlp_backward(tp_act act, int64_t m, int64_t h, int64_t f_shard, const void* x,
+                                const void* w_in, const void* w_out, const void* dz, const void* xt,
+                                const void* dzt, void* ws, size_t ws_bytes, float* dx_partial, float* dw_in,
+                                float* dw_out, void* stream);
+tp_status tp_transpose(int64_t rows, int64_t cols, const void* src, void* dst, void* stream);
+tp_status tp_mlp_act_backward(tp_act act, int64_t m, int64_t n, const void* pre, const void* dy, void* dpre,
+                              void* y, void* stream);
+
+/* --------------------------------------------------------------------------
  * Introspection: how the bf16 GEMM behind tp_colwise / tp_rowwise /
  * tp_qkv_rope tiles an m x n output (n = output columns; swiglu != 0 for the
  * SwiGLU colwise GEMM, whose tiles cover 128 output columns instead of 256).

@@ -97,6 +97,29 @@ AttnLayout attn_layout(int64_t batch, int64_t seq, int32_t hq, int32_t hkv, int3
   return L;
 }
 
+// Workspace of one rank's MLP backward (F = f or 2 f rows of w_in).
+struct MlpBwdLayout {
+  size_t pre, wout_t, dy, dpre, y, win_t, y_t, dpre_t, xt, dzt, total;
+};
+
+MlpBwdLayout mlp_bwd_layout(tp_act act, int64_t m, int64_t h, int64_t f) {
+  const size_t F = act == TP_ACT_SWIGLU ? 2 * (size_t)f : (size_t)f;
+  const size_t M = (size_t)m, H = (size_t)h, Fs = (size_t)f;
+  MlpBwdLayout L;
+  L.pre = 0;
+  L.wout_t = L.pre + align256(M * F * 2);
+  L.dy = L.wout_t + align256(Fs * H * 2);
+  L.dpre = L.dy + align256(M * Fs * 2);
+  L.y = L.dpre + align256(M * F * 2);
+  L.win_t = L.y + align256(M * Fs * 2);
+  L.y_t = L.win_t + align256(H * F * 2);
+  L.dpre_t = L.y_t + align256(Fs * M * 2);
+  L.xt = L.dpre_t + align256(F * M * 2);
+  L.dzt = L.xt + align256(H * M * 2);
+  L.total = L.dzt + align256(H * M * 2);
+  return L;
+}
+
 // Shared checks of one GEMM call: sizes, pointers, 32-bit offset ranges.
 tp_status check_gemm(tp_act act, tp_dtype dt, int64_t m, int64_t k, int64_t n, const void* x,
                      const void* w, const void* out, const char* xn, const char* wn, const char* on) {
@@ -465,6 +488,98 @@ tp_status tp_ce_combine(int32_t t, int64_t m, int64_t v, const float* const* sta
   if (mean) TRY(check_ptr(mean, "mean"));
   TRY(device_check());
   return launched(tpk::launch_ce_combine(t, m, stats, loss, labels, v, mean, as_stream(stream)), "tp_ce_combine");
+}
+
+tp_status tp_transpose(int64_t rows, int64_t cols, const void* src, void* dst, void* stream) {
+  if (rows < 0 || cols < 0) return fail(TP_ERR_SHAPE, "rows and cols must be >= 0");
+  if (rows == 0 || cols == 0) return ok();
+  if (rows > (int64_t)65535 * 64 || cols > ((int64_t)1 << 31) * 64)
+    return fail(TP_ERR_SHAPE, "rows = %lld too large", (long long)rows);
+  TRY(check_ptr(src, "src"));
+  TRY(check_ptr(dst, "dst"));
+  if (src == dst) return fail(TP_ERR_INVALID_ARG, "dst aliases src");
+  TRY(device_check());
+  return launched(tpk::launch_transpose(rows, cols, src, dst, as_stream(stream)), "tp_transpose");
+}
+
+tp_status tp_mlp_act_backward(tp_act act, int64_t m, int64_t n, const void* pre, const void* dy, void* dpre,
+                              void* y, void* stream) {
+  if (act != TP_ACT_GELU && act != TP_ACT_SWIGLU)
+    return fail(TP_ERR_INVALID_ARG, "tp_mlp_act_backward needs GELU or SWIGLU, got %d", (int)act);
+  if (m < 0) return fail(TP_ERR_SHAPE, "m = %lld is negative", (long long)m);
+  TRY(check_dim8(n, "n"));
+  if (m == 0) return ok();
+  TRY(check_ptr(pre, "pre"));
+  TRY(check_ptr(dy, "dy"));
+  TRY(check_ptr(dpre, "dpre"));
+  if (y) TRY(check_ptr(y, "y"));
+  TRY(device_check());
+  return launched(tpk::launch_act_backward(act == TP_ACT_SWIGLU, m, n, pre, dy, dpre, y, as_stream(stream)),
+                  "tp_mlp_act_backward");
+}
+
+size_t tp_shard_mlp_backward_workspace_bytes(tp_act act, int64_t m, int64_t h, int64_t f_shard) {
+  if (m < 0 || h <= 0 || f_shard <= 0) return 0;
+  return mlp_bwd_layout(act, m, h, f_shard).total;
+}
+
+tp_status tp_shard_mlp_backward(tp_act act, int64_t m, int64_t h, int64_t f_shard, const void* x,
+                                const void* w_in, const void* w_out, const void* dz, const void* xt,
+                                const void* dzt, void* ws, size_t ws_bytes, float* dx_partial, float* dw_in,
+                                float* dw_out, void* stream) {
+  if (act != TP_ACT_GELU && act != TP_ACT_SWIGLU)
+    return fail(TP_ERR_INVALID_ARG, "tp_shard_mlp_backward needs GELU or SWIGLU, got %d", (int)act);
+  if (m % 8 != 0) return fail(TP_ERR_SHAPE, "m = %lld must be a multiple of 8 (the weight gradients reduce over tokens)",
+                              (long long)m);
+  const int64_t F = act == TP_ACT_SWIGLU ? 2 * f_shard : f_shard;
+  // the forward's two GEMMs and the backward's six, with their operand sizes
+  TRY(check_gemm(TP_ACT_NONE, TP_BF16, m, h, F, x, w_in, ws, "x", "w_in", "ws"));
+  TRY(check_gemm(TP_ACT_NONE, TP_BF16, m, h, f_shard, dz, w_out, ws, "dz", "w_out", "ws"));
+  TRY(check_gemm(TP_ACT_NONE, TP_BF16, m, F, h, ws, ws, dx_partial, "ws", "ws", "dx_partial"));
+  if (m == 0) return ok();
+  TRY(check_gemm(TP_ACT_NONE, TP_BF16, h, m, f_shard, ws, ws, dw_out, "ws", "ws", "dw_out"));
+  TRY(check_gemm(TP_ACT_NONE, TP_BF16, F, m, h, ws, ws, dw_in, "ws", "ws", "dw_in"));
+  if (xt) TRY(check_ptr(xt, "xt"));
+  if (dzt) TRY(check_ptr(dzt, "dzt"));
+  TRY(check_ptr(ws, "ws"));
+  const MlpBwdLayout L = mlp_bwd_layout(act, m, h, f_shard);
+  if (ws_bytes < L.total) return fail(TP_ERR_WORKSPACE, "workspace of %zu bytes < %zu needed", ws_bytes, L.total);
+  TRY(device_check());
+  hipStream_t s = as_stream(stream);
+  char* b = static_cast<char*>(ws);
+  auto gemm = [&](int epi, int64_t M, int64_t N, int64_t K, const void* a, const void* w, void* c) {
+    return tpk::launch_gemm_bf16(epi, M, N, K, a, w, c, nullptr, s);
+  };
+  hipError_t e;
+#define TP_BWD_STEP(call, what) \
+  if ((e = (call)) != hipSuccess) return launched(e, what);
+  // recompute the pre-activation; dY = dZ W_out (W_out transposed to [f, h])
+  TP_BWD_STEP(gemm(tpk::EPI_BF16, m, F, h, x, w_in, b + L.pre), "tp_shard_mlp_backward (pre-activation)");
+  TP_BWD_STEP(tpk::launch_transpose(h, f_shard, w_out, b + L.wout_t, s), "tp_shard_mlp_backward (w_out^T)");
+  TP_BWD_STEP(gemm(tpk::EPI_BF16, m, f_shard, h, dz, b + L.wout_t, b + L.dy), "tp_shard_mlp_backward (dY)");
+  // dPre (and the activation Y again, for the output layer's weight gradient)
+  TP_BWD_STEP(tpk::launch_act_backward(act == TP_ACT_SWIGLU, m, f_shard, b + L.pre, b + L.dy, b + L.dpre, b + L.y, s),
+              "tp_shard_mlp_backward (activation)");
+  // dX partial = dPre W_in (W_in transposed to [h, F]); f's backward sums these over ranks
+  TP_BWD_STEP(tpk::launch_transpose(F, h, w_in, b + L.win_t, s), "tp_shard_mlp_backward (w_in^T)");
+  TP_BWD_STEP(gemm(tpk::EPI_F32, m, h, F, b + L.dpre, b + L.win_t, dx_partial), "tp_shard_mlp_backward (dX)");
+  // dW_out = dZ^T Y and dW_in = dPre^T X, reducing over the tokens
+  const void* dzt_p = dzt;
+  if (!dzt_p) {
+    TP_BWD_STEP(tpk::launch_transpose(m, h, dz, b + L.dzt, s), "tp_shard_mlp_backward (dZ^T)");
+    dzt_p = b + L.dzt;
+  }
+  const void* xt_p = xt;
+  if (!xt_p) {
+    TP_BWD_STEP(tpk::launch_transpose(m, h, x, b + L.xt, s), "tp_shard_mlp_backward (X^T)");
+    xt_p = b + L.xt;
+  }
+  TP_BWD_STEP(tpk::launch_transpose(m, f_shard, b + L.y, b + L.y_t, s), "tp_shard_mlp_backward (Y^T)");
+  TP_BWD_STEP(gemm(tpk::EPI_F32, h, f_shard, m, dzt_p, b + L.y_t, dw_out), "tp_shard_mlp_backward (dW_out)");
+  TP_BWD_STEP(tpk::launch_transpose(m, F, b + L.dpre, b + L.dpre_t, s), "tp_shard_mlp_backward (dPre^T)");
+  TP_BWD_STEP(gemm(tpk::EPI_F32, F, h, m, b + L.dpre_t, xt_p, dw_in), "tp_shard_mlp_backward (dW_in)");
+#undef TP_BWD_STEP
+  return ok();
 }
 
 }  // extern "C"

@@ -85,4 +85,12 @@ hipError_t launch_ce_stats(int64_t m, int64_t n, int64_t v_start, const float* l
 hipError_t launch_ce_combine(int t, int64_t m, const float* const* stats, float* loss, const int32_t* labels,
                              int64_t v, float* mean, hipStream_t s);
 
+// dst [cols, rows] = src [rows, cols]^T, bf16.
+hipError_t launch_transpose(int64_t rows, int64_t cols, const void* src, void* dst, hipStream_t s);
+
+// From the pre-activation and dY (n columns): dPre and, if y, the activation
+// Y.  GeLU: pre [m, n]; SwiGLU: pre [m, 2n] = [gate | up], dPre likewise.
+hipError_t launch_act_backward(int swiglu, int64_t m, int64_t n, const void* pre, const void* dy, void* dpre,
+                               void* y, hipStream_t s);
+
 }  // namespace tpk

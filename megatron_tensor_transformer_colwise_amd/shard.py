@@ -148,6 +148,32 @@ class MLPShards:
         self.reduce(residual, residual_dt, stream)
         return self.out
 
+    # ---- backward ("f and g": every rank gets the whole dZ; the dX partials are summed)
+
+    def _bwd_buffers(self):
+        if getattr(self, "bwd_ws", None) is None:
+            dev, m, h, f = self.x.device, self.m, self.h, self.f_shard
+            fin = 2 * f if self.act == "swiglu" else f
+            self.bwd_ws_bytes = tp.tp_shard_mlp_backward_workspace_bytes(self.act, m, h, f)
+            self.bwd_ws = torch.empty(self.bwd_ws_bytes, dtype=torch.uint8, device=dev)
+            self.dx_partials = torch.empty(self.t, m, h, dtype=torch.float32, device=dev)
+            self.dw_in = [torch.empty(fin, h, dtype=torch.float32, device=dev) for _ in range(self.t)]
+            self.dw_out = [torch.empty(h, f, dtype=torch.float32, device=dev) for _ in range(self.t)]
+            self.dx = torch.empty(m, h, dtype=torch.float32, device=dev)
+
+    def backward_rank(self, r: int, dz, stream=None) -> None:
+        """Rank r's gradients: its dX partial and its weight shards' gradients."""
+        self._bwd_buffers()
+        tp.tp_shard_mlp_backward(self.act, self.m, self.h, self.f_shard, self.x, self.w_in[r], self.w_out[r], dz,
+                                 None, None, self.bwd_ws, self.bwd_ws_bytes, self.dx_partials[r], self.dw_in[r],
+                                 self.dw_out[r], stream)
+
+    def backward(self, dz, stream=None):
+        for r in range(self.t):
+            self.backward_rank(r, dz, stream)
+        tp.tp_shard_sum(self.t, self.m * self.h, list(self.dx_partials), None, "f32", self.dx, stream)
+        return self.dx
+
 
 class AttnShards:
     """All t ranks of an attention layer on one device, run one after another."""

@@ -59,6 +59,11 @@ _SIGS = {
                              _f32, _vp, _vp],
     "tp_gemm_plan": [_i64, _i64, _i32, ctypes.POINTER(_i32), ctypes.POINTER(_i32), ctypes.POINTER(_i32)],
     "tp_embedding": [_i64, _i64, _i64, _i64, _vp, _vp, _vp, _i64, _vp],
+    "tp_shard_mlp_backward_workspace_bytes": [_i32, _i64, _i64, _i64],
+    "tp_shard_mlp_backward": [_i32, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp,
+                              _vp, _vp, _vp],
+    "tp_transpose": [_i64, _i64, _vp, _vp, _vp],
+    "tp_mlp_act_backward": [_i32, _i64, _i64, _vp, _vp, _vp, _vp, _vp],
     "tp_vocab_logits": [_i64, _i64, _i64, _vp, _vp, _vp, _vp],
     "tp_ce_stats": [_i64, _i64, _i64, _vp, _vp, _vp, _vp],
     "tp_ce_combine": [_i32, _i64, _i64, ctypes.POINTER(_vp), _vp, _vp, _vp, _vp],
@@ -80,6 +85,7 @@ def lib() -> ctypes.CDLL:
             fn.restype = ctypes.c_int
         L.tp_last_error.restype = ctypes.c_char_p
         L.tp_shard_attn_workspace_bytes.restype = ctypes.c_size_t
+        L.tp_shard_mlp_backward_workspace_bytes.restype = ctypes.c_size_t
         _lib = L
     return _lib
 
@@ -214,4 +220,23 @@ def tp_ce_stats(m, v_shard, v_start, logits, labels, stats, stream=None) -> None
 def tp_ce_combine(t, m, v, stats, labels, loss, mean, stream=None) -> None:
     arr = (_vp * max(len(stats), 1))(*[_p(p) for p in stats])
     _check(lib().tp_ce_combine(t, m, v, arr, _p(labels), _p(loss), _p(mean), _s(stream)))
+
+
+def tp_shard_mlp_backward_workspace_bytes(act, m, h, f_shard) -> int:
+    return int(lib().tp_shard_mlp_backward_workspace_bytes(_e(act, ACTS), m, h, f_shard))
+
+
+def tp_shard_mlp_backward(act, m, h, f_shard, x, w_in, w_out, dz, xt, dzt, ws, ws_bytes, dx_partial, dw_in,
+                          dw_out, stream=None) -> None:
+    _check(lib().tp_shard_mlp_backward(_e(act, ACTS), m, h, f_shard, _p(x), _p(w_in), _p(w_out), _p(dz), _p(xt),
+                                       _p(dzt), _p(ws), ws_bytes, _p(dx_partial), _p(dw_in), _p(dw_out),
+                                       _s(stream)))
+
+
+def tp_transpose(rows, cols, src, dst, stream=None) -> None:
+    _check(lib().tp_transpose(rows, cols, _p(src), _p(dst), _s(stream)))
+
+
+def tp_mlp_act_backward(act, m, n, pre, dy, dpre, y, stream=None) -> None:
+    _check(lib().tp_mlp_act_backward(_e(act, ACTS), m, n, _p(pre), _p(dy), _p(dpre), _p(y), _s(stream)))
 

@@ -44,6 +44,9 @@ Sources (the "Tensor parallelism" page of itwiki, by section):
   b x s values are exchanged.  transformers "Tensor parallelism" page,
   EmbeddingParallel: a vocabulary-sharded lookup sums the ranks' partial
   lookups; a hidden-sharded one gathers their column slices.
+* "f and g" (backward): g's backward is the identity (every rank gets the whole
+  output gradient), f's backward is the all-reduce of the ranks' input-gradient
+  partials; each rank's weight gradients are the gradients of its own shards.
 * "Sequence parallelism": the norms act on every token alone, so each rank
   can hold and normalise only its slice of the sequence; the sequence is
   gathered (all-gather) on entering the tensor-parallel region and, on
@@ -598,4 +601,53 @@ def vocab_parallel_ce(x, w_out, labels, t: int) -> np.ndarray:
         raise ValueError(f"vocabulary {v} is not divisible by t = {t}")
     n = v // t
     return vocab_ce_combine([vocab_ce_stats(x @ w_out[:, r * n:(r + 1) * n], labels, r * n) for r in range(t)])
+
+
+# --------------------------------------------------------------------------
+# backward of the MLP shard ("f and g": g's backward is the identity, f's is
+# the all-reduce of the input-gradient partials)
+# --------------------------------------------------------------------------
+
+
+def gelu_grad(x):
+    """d/dx [x Phi(x)] = Phi(x) + x phi(x)."""
+    x = np.asarray(x, dtype=np.float64)
+    return 0.5 * (1.0 + _erf(x / math.sqrt(2.0))) + x * np.exp(-0.5 * x * x) / math.sqrt(2.0 * math.pi)
+
+
+def silu_grad(x):
+    """d/dx [x sigma(x)] = sigma(x) (1 + x (1 - sigma(x)))."""
+    x = np.asarray(x, dtype=np.float64)
+    sg = 1.0 / (1.0 + np.exp(-x))
+    return sg * (1.0 + x * (1.0 - sg))
+
+
+def mlp_gelu_backward(x, a, b, dz) -> dict:
+    """Gradients of Z = GeLU(X A) B for the output gradient dZ (full A, B: the
+    unsharded layer; A_i, B_i: rank i's share, whose dX is its partial)."""
+    pre = x @ a
+    dy = dz @ b.T
+    dpre = dy * gelu_grad(pre)
+    return {"dx": dpre @ a.T, "da": x.T @ dpre, "db": gelu(pre).T @ dz}
+
+
+def mlp_gelu_backward_partials(x, a, b, dz, t: int) -> list[dict]:
+    """Rank i's gradients from its column shard of A and row shard of B; the
+    sum of the dX partials is dX (f's backward), the weight gradients are the
+    shards of the full ones."""
+    return [mlp_gelu_backward(x, ai, bi, dz) for ai, bi in zip(split_columns(a, t), split_rows(b, t))]
+
+
+def mlp_swiglu_backward(x, w1, w3, w2, dz) -> dict:
+    """Gradients of Z = (SiLU(X W1) * (X W3)) W2 for dZ."""
+    g, u = x @ w1, x @ w3
+    dy = dz @ w2.T
+    dg = dy * u * silu_grad(g)
+    du = dy * silu(g)
+    return {"dx": dg @ w1.T + du @ w3.T, "dw1": x.T @ dg, "dw3": x.T @ du, "dw2": (silu(g) * u).T @ dz}
+
+
+def mlp_swiglu_backward_partials(x, w1, w3, w2, dz, t: int) -> list[dict]:
+    return [mlp_swiglu_backward(x, a, c, b, dz)
+            for a, c, b in zip(split_columns(w1, t), split_columns(w3, t), split_rows(w2, t))]
 

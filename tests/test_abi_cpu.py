@@ -280,3 +280,18 @@ def test_vocab_parallel_validation(L):
     assert status("tp_ce_combine", 2, 4, 16, arr, A16, A16, None, None) == tp.TP_ERR_INVALID_ARG
     assert "stats[1]" in tp.tp_last_error()
 
+
+def test_mlp_backward_validation(L):
+    ws = tp.tp_shard_mlp_backward_workspace_bytes("gelu", 16, 16, 32)
+    assert ws > 0
+    args = lambda act, m, wsb=ws, x=A16: status(  # noqa: E731
+        "tp_shard_mlp_backward", act, m, 16, 32, x, A16, A16, A16, None, None, A16, wsb, A16, A16, A16, None)
+    assert args(0, 16) == tp.TP_ERR_INVALID_ARG          # needs an activation
+    assert args(1, 12) == tp.TP_ERR_SHAPE                # m not a multiple of 8
+    assert args(1, 16, wsb=ws - 1) == tp.TP_ERR_WORKSPACE
+    assert args(1, 16, x=MIS) == tp.TP_ERR_INVALID_ARG
+    assert status("tp_transpose", 4, 4, A16, A16, None) == tp.TP_ERR_INVALID_ARG    # in place
+    assert status("tp_transpose", 0, 4, None, None, None) == tp.TP_OK
+    assert status("tp_mlp_act_backward", 0, 4, 16, A16, A16, A16, None, None) == tp.TP_ERR_INVALID_ARG
+    assert status("tp_mlp_act_backward", 1, 4, 12, A16, A16, A16, None, None) == tp.TP_ERR_SHAPE
+

@@ -337,6 +337,79 @@ def test_packed_single_stream(device, t, causal):
     assert rel_err(host(z), ref) <= BF16_TOL
 
 
+# ---------------------------------------------------------------- backward
+
+
+def test_transpose_exact(device):
+    say("case transpose")
+    for rows, cols in [(1, 8), (65, 130), (1000, 264), (4096, 1024)]:
+        a = inputs.normal(71, rows, (rows, cols), 1.0, "bf16")
+        src = to_dev(a, device)
+        dst = torch.empty(cols, rows, dtype=torch.bfloat16, device=device)
+        tp.tp_transpose(rows, cols, src, dst)
+        torch.cuda.synchronize()
+        assert torch.equal(dst, src.T.contiguous())
+
+
+@pytest.mark.parametrize("act", ["gelu", "swiglu"])
+def test_mlp_act_backward(device, act):
+    """dPre and the recomputed activation against the oracle's derivatives."""
+    m, n = 300, 264
+    say(f"case act backward {act}")
+    pw = 2 * n if act == "swiglu" else n
+    pre = inputs.normal(72, 0, (m, pw), 2.0, "bf16")
+    dy = inputs.normal(72, 1, (m, n), 1.0, "bf16")
+    dpre = torch.empty(m, pw, dtype=torch.bfloat16, device=device)
+    y = torch.empty(m, n, dtype=torch.bfloat16, device=device)
+    tp.tp_mlp_act_backward(act, m, n, to_dev(pre, device), to_dev(dy, device), dpre, y)
+    torch.cuda.synchronize()
+    P, D = pre.f64(), dy.f64()
+    if act == "gelu":
+        ref_d, ref_y = D * oracle.gelu_grad(P), oracle.gelu(P)
+    else:
+        g, u = P[:, :n], P[:, n:]
+        ref_d = np.concatenate([D * u * oracle.silu_grad(g), D * oracle.silu(g)], axis=1)
+        ref_y = oracle.silu(g) * u
+    # one bf16 rounding of each output plus float32 arithmetic
+    assert np.all(np.abs(host(dpre) - ref_d) <= 2.0 ** -8 * np.abs(ref_d) + 1e-5 * np.max(np.abs(ref_d)))
+    assert np.all(np.abs(host(y) - ref_y) <= 2.0 ** -8 * np.abs(ref_y) + 1e-5 * np.max(np.abs(ref_y)))
+
+
+@pytest.mark.parametrize("act,m,h,f,t", [("gelu", 256, 256, 1024, 2), ("swiglu", 264, 512, 1024, 4),
+                                         ("swiglu", 2048, 1024, 4096, 4)])
+def test_mlp_backward(device, act, m, h, f, t):
+    """Each rank's dX partial and weight gradients against the oracle's, and
+    the summed dX (f's backward) against the unsharded layer's."""
+    say(f"case mlp backward {act} m={m} h={h} f={f} t={t}")
+    case = inputs.MLPCase("bwd", m, h, f, t, act, "bf16", seed=73)
+    w = inputs.gen_mlp(case)
+    dz = inputs.normal(73, 9, (m, h), 1.0, "bf16")
+    dw = {k: to_dev(v, device) for k, v in w.items()}
+    mlp = shard.MLPShards(dw["X"], dw, t, act)
+    dx = mlp.backward(to_dev(dz, device))
+    torch.cuda.synchronize()
+    W = {k: v.f64() for k, v in w.items()}
+    DZ = dz.f64()
+    fs = f // t
+    if act == "gelu":
+        parts = oracle.mlp_gelu_backward_partials(W["X"], W["A"], W["B"], DZ, t)
+        full = oracle.mlp_gelu_backward(W["X"], W["A"], W["B"], DZ)
+        for r in range(t):
+            assert rel_err(host(mlp.dx_partials[r]), parts[r]["dx"]) <= BF16_TOL
+            assert rel_err(host(mlp.dw_in[r]), parts[r]["da"].T) <= BF16_TOL       # [f_shard, h]
+            assert rel_err(host(mlp.dw_out[r]), parts[r]["db"].T) <= BF16_TOL      # [h, f_shard]
+    else:
+        parts = oracle.mlp_swiglu_backward_partials(W["X"], W["W1"], W["W3"], W["W2"], DZ, t)
+        full = oracle.mlp_swiglu_backward(W["X"], W["W1"], W["W3"], W["W2"], DZ)
+        for r in range(t):
+            assert rel_err(host(mlp.dx_partials[r]), parts[r]["dx"]) <= BF16_TOL
+            g = host(mlp.dw_in[r])                                                 # [2 f_shard, h]
+            assert rel_err(g[:fs], parts[r]["dw1"].T) <= BF16_TOL
+            assert rel_err(g[fs:], parts[r]["dw3"].T) <= BF16_TOL
+            assert rel_err(host(mlp.dw_out[r]), parts[r]["dw2"].T) <= BF16_TOL
+    assert rel_err(host(dx), full["dx"]) <= BF16_TOL
+
+
 # ---------------------------------------------------------------- vocabulary parallel
 
 

@@ -586,6 +586,55 @@ def test_vocab_parallel_ce_identity(t):
     assert st[0, 3] == 1 and abs(st[0, 2] - (x @ w)[0, labels[0]]) < 1e-12
 
 
+# ---------------------------------------------------------------- backward
+
+
+def test_activation_gradients_against_autograd():
+    import torch
+    import torch.nn.functional as F
+
+    xs = torch.linspace(-6, 6, 241, dtype=torch.float64, requires_grad=True)
+    F.gelu(xs).sum().backward()
+    assert np.max(np.abs(oracle.gelu_grad(xs.detach().numpy()) - xs.grad.numpy())) < 1e-14
+    xs.grad = None
+    F.silu(xs).sum().backward()
+    assert np.max(np.abs(oracle.silu_grad(xs.detach().numpy()) - xs.grad.numpy())) < 1e-14
+
+
+@pytest.mark.parametrize("t", [1, 2, 4])
+def test_mlp_backward_against_autograd_and_sharding(t):
+    """The hand-written gradients equal PyTorch autograd's (float64) for the GeLU
+    and SwiGLU MLPs; the ranks' dX partials sum to dX and their weight
+    gradients are the shards of the full ones."""
+    import torch
+    import torch.nn.functional as F
+
+    r = np.random.default_rng(41)
+    m, h, f = 6, 8, 16
+    x, dz = r.standard_normal((m, h)), r.standard_normal((m, h))
+    a, b = r.standard_normal((h, f)) * 0.5, r.standard_normal((f, h)) * 0.5
+    T = lambda v: torch.from_numpy(v).requires_grad_(True)  # noqa: E731
+    tx, ta, tb = T(x), T(a), T(b)
+    (F.gelu(tx @ ta) @ tb).backward(torch.from_numpy(dz))
+    full = oracle.mlp_gelu_backward(x, a, b, dz)
+    for k, g in (("dx", tx.grad), ("da", ta.grad), ("db", tb.grad)):
+        assert np.max(np.abs(full[k] - g.numpy())) < 1e-12, k
+    parts = oracle.mlp_gelu_backward_partials(x, a, b, dz, t)
+    assert np.max(np.abs(oracle.shard_sum([p["dx"] for p in parts]) - full["dx"])) < 1e-12
+    assert np.max(np.abs(np.concatenate([p["da"] for p in parts], axis=1) - full["da"])) < 1e-12
+    assert np.max(np.abs(np.concatenate([p["db"] for p in parts], axis=0) - full["db"])) < 1e-12
+    w1, w3, w2 = r.standard_normal((h, f)) * 0.5, r.standard_normal((h, f)) * 0.5, r.standard_normal((f, h)) * 0.5
+    tx, t1, t3, t2 = T(x), T(w1), T(w3), T(w2)
+    ((F.silu(tx @ t1) * (tx @ t3)) @ t2).backward(torch.from_numpy(dz))
+    full = oracle.mlp_swiglu_backward(x, w1, w3, w2, dz)
+    for k, g in (("dx", tx.grad), ("dw1", t1.grad), ("dw3", t3.grad), ("dw2", t2.grad)):
+        assert np.max(np.abs(full[k] - g.numpy())) < 1e-12, k
+    parts = oracle.mlp_swiglu_backward_partials(x, w1, w3, w2, dz, t)
+    assert np.max(np.abs(oracle.shard_sum([p["dx"] for p in parts]) - full["dx"])) < 1e-12
+    assert np.max(np.abs(np.concatenate([p["dw1"] for p in parts], axis=1) - full["dw1"])) < 1e-12
+    assert np.max(np.abs(np.concatenate([p["dw2"] for p in parts], axis=0) - full["dw2"])) < 1e-12
+
+
 # ---------------------------------------------------------------- inputs
 
 
