@@ -47,6 +47,11 @@ Sources (the "Tensor parallelism" page of itwiki, by section):
 * "f and g" (backward): g's backward is the identity (every rank gets the whole
   output gradient), f's backward is the all-reduce of the ranks' input-gradient
   partials; each rank's weight gradients are the gradients of its own shards.
+* "Self-attention" with "f and g" (backward): a rank's attention gradients
+  are those of its own heads; its dX partial sums over them, and a KV head
+  replicated on several ranks gets one weight-gradient share per rank.  The
+  softmax and rotation gradients are their plain definitions (the Jacobian
+  of the row softmax; the transpose of the RoPE rotation).
 * "Sequence parallelism": the norms act on every token alone, so each rank
   can hold and normalise only its slice of the sequence; the sequence is
   gathered (all-gather) on entering the tensor-parallel region and, on
@@ -651,3 +656,99 @@ def mlp_swiglu_backward_partials(x, w1, w3, w2, dz, t: int) -> list[dict]:
     return [mlp_swiglu_backward(x, a, c, b, dz)
             for a, c, b in zip(split_columns(w1, t), split_columns(w3, t), split_rows(w2, t))]
 
+
+
+# --------------------------------------------------------------------------
+# backward of the attention shard ("f and g": the same rule as the MLP; the
+# "Self-attention" split makes each rank's gradients those of its own heads)
+# --------------------------------------------------------------------------
+
+
+def rope_backward(g: np.ndarray, pos: np.ndarray, base: float) -> np.ndarray:
+    """Gradient through ``rope``: each pair (k, k + d/2) is rotated by the
+    angle's negative (the transpose of the rotation)."""
+    d = g.shape[-1]
+    half = d // 2
+    k = np.arange(half, dtype=np.float64)
+    theta = base ** (-2.0 * k / d)
+    ang = np.asarray(pos, dtype=np.float64)[:, None] * theta[None, :]
+    c, s = np.cos(ang), np.sin(ang)
+    g1, g2 = g[..., :half], g[..., half:]
+    return np.concatenate([g1 * c + g2 * s, g2 * c - g1 * s], axis=-1)
+
+
+def causal_attention_backward(q, k, v, do):
+    """Gradients (dq, dk, dv) of O = softmax(q k^T / sqrt(d), causal) v for dO.
+
+    With P the probabilities: dV = P^T dO, dP = dO V^T, and the softmax
+    Jacobian gives dS = P * (dP - rowsum(dP * P)); the scale carries through to
+    dq = dS k / sqrt(d) and dk = dS^T q / sqrt(d)."""
+    d = q.shape[-1]
+    n = q.shape[0]
+    s = (q @ k.T) / math.sqrt(d)
+    s = np.where(np.arange(k.shape[0])[None, :] > np.arange(n)[:, None], -np.inf, s)
+    p = np.exp(s - s.max(axis=1, keepdims=True))
+    p = p / p.sum(axis=1, keepdims=True)
+    dv = p.T @ do
+    dp = do @ v.T
+    ds = p * (dp - np.sum(dp * p, axis=1, keepdims=True))
+    return ds @ k / math.sqrt(d), ds.T @ q / math.sqrt(d), dv
+
+
+def attn_backward(x, wq, wk, wv, wo, dz, heads: int, kv_heads: int, head_dim: int, batch: int,
+                  seq: int, rope_base: float, q_heads: list[int] | None = None) -> dict:
+    """Gradients of the attention sublayer Z = concat_j(attn_j) Wo restricted to
+    the query heads ``q_heads`` (default all) and the KV heads they read, for
+    the output gradient dZ.  Weights in math convention: wq [h, heads*d],
+    wk, wv [h, kv_heads*d], wo [heads*d, h_out].
+
+    Returns dx [m, h] (a rank's input-gradient partial), dwq [h, nq*d],
+    dwk, dwv [h, nkv*d] (a KV head shared with other ranks gets only this
+    rank's share), dwo [nq*d, h_out] and dqkv [m, (nq + 2 nkv) d], the
+    gradient of the projections before RoPE packed as Q heads, K heads, V
+    heads (what a rank feeds its weight-gradient products)."""
+    d = head_dim
+    q_heads = list(range(heads)) if q_heads is None else list(q_heads)
+    kv_list = sorted({kv_head_of(j, heads, kv_heads) for j in q_heads})
+    nq, nkv = len(q_heads), len(kv_list)
+    m = batch * seq
+    pos = np.arange(seq)
+    wo_rows = np.concatenate([wo[j * d:(j + 1) * d] for j in q_heads], axis=0)
+    do_all = dz @ wo_rows.T
+    o_all = np.zeros((m, nq * d))
+    dqkv = np.zeros((m, (nq + 2 * nkv) * d))
+    for b in range(batch):
+        rows = slice(b * seq, (b + 1) * seq)
+        xb = x[rows]
+        kv = {}
+        for g in kv_list:
+            kv[g] = (rope(xb @ wk[:, g * d:(g + 1) * d], pos, rope_base), xb @ wv[:, g * d:(g + 1) * d])
+        dk = {g: np.zeros((seq, d)) for g in kv_list}
+        dv = {g: np.zeros((seq, d)) for g in kv_list}
+        for c, j in enumerate(q_heads):
+            g = kv_head_of(j, heads, kv_heads)
+            qh = rope(xb @ wq[:, j * d:(j + 1) * d], pos, rope_base)
+            kh, vh = kv[g]
+            o_all[rows, c * d:(c + 1) * d] = causal_attention(qh, kh, vh)
+            dq_h, dk_h, dv_h = causal_attention_backward(qh, kh, vh, do_all[rows, c * d:(c + 1) * d])
+            dqkv[rows, c * d:(c + 1) * d] = rope_backward(dq_h, pos, rope_base)
+            dk[g] += dk_h
+            dv[g] += dv_h
+        for e, g in enumerate(kv_list):
+            dqkv[rows, (nq + e) * d:(nq + e + 1) * d] = rope_backward(dk[g], pos, rope_base)
+            dqkv[rows, (nq + nkv + e) * d:(nq + nkv + e + 1) * d] = dv[g]
+    wq_r = np.concatenate([wq[:, j * d:(j + 1) * d] for j in q_heads], axis=1)
+    wk_r = np.concatenate([wk[:, g * d:(g + 1) * d] for g in kv_list], axis=1)
+    wv_r = np.concatenate([wv[:, g * d:(g + 1) * d] for g in kv_list], axis=1)
+    w_r = np.concatenate([wq_r, wk_r, wv_r], axis=1)
+    dw = x.T @ dqkv
+    return {"dx": dqkv @ w_r.T, "dwq": dw[:, :nq * d], "dwk": dw[:, nq * d:(nq + nkv) * d],
+            "dwv": dw[:, (nq + nkv) * d:], "dwo": o_all.T @ dz, "dqkv": dqkv, "o": o_all}
+
+
+def attn_backward_partials(x, w: dict, dz, case, t: int | None = None) -> list[dict]:
+    """Every rank's ``attn_backward`` over its a/t query heads."""
+    t = case.t if t is None else t
+    return [attn_backward(x, w["Wq"], w["Wk"], w["Wv"], w["Wo"], dz, case.heads, case.kv_heads,
+                          case.head_dim, case.batch, case.seq, case.rope_base,
+                          rank_query_heads(r, case.heads, t)) for r in range(t)]

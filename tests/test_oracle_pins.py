@@ -635,6 +635,86 @@ def test_mlp_backward_against_autograd_and_sharding(t):
     assert np.max(np.abs(np.concatenate([p["dw2"] for p in parts], axis=0) - full["dw2"])) < 1e-12
 
 
+def _torch_rope(x, base):
+    """RoPE as complex multiplication: the pair (k, k + d/2) is the complex
+    number x_k + i x_{k+d/2}, multiplied by exp(i pos base^(-2k/d)).  x is
+    [batch, heads, seq, d]."""
+    d = x.shape[-1]
+    half = d // 2
+    ang = torch.arange(x.shape[-2], dtype=torch.float64)[:, None] * \
+        (base ** (-torch.arange(0, d, 2, dtype=torch.float64) / d))[None, :]
+    z = torch.complex(x[..., :half], x[..., half:]) * torch.polar(torch.ones_like(ang), ang)
+    return torch.cat([z.real, z.imag], dim=-1)
+
+
+def test_rope_backward_is_the_adjoint():
+    """<rope(x), g> = <x, rope_backward(g)> for every x, g: the gradient of a
+    rotation is its transpose; and rope_backward undoes rope."""
+    r = _rng(43)
+    x, g = r.standard_normal((7, 16)), r.standard_normal((7, 16))
+    pos = np.arange(3, 10)
+    assert abs(np.sum(oracle.rope(x, pos, 50.0) * g) - np.sum(x * oracle.rope_backward(g, pos, 50.0))) < 1e-12
+    assert np.max(np.abs(oracle.rope_backward(oracle.rope(x, pos, 50.0), pos, 50.0) - x)) < 1e-13
+
+
+@pytest.mark.parametrize("t", [1, 2, 4])
+def test_attention_backward_against_autograd_and_sharding(t):
+    """The hand-written attention gradients equal PyTorch autograd's (float64)
+    through projections, RoPE (written as complex rotation), causal GQA
+    scaled_dot_product_attention and o_proj; the ranks' dX partials sum to
+    dX, their dWq / dWo are the column / row shards of the full ones, and the
+    ranks sharing a replicated KV head (t = 4 > kv_heads = 2) sum to its
+    gradient."""
+    case = inputs.AttnCase("bwd", batch=2, seq=7, hidden=16, heads=4, kv_heads=2, head_dim=8,
+                           t=t, rope_base=100.0, seed=44, dtype="f32", w_std=0.4)
+    w = {k: v.f64() for k, v in inputs.gen_attn(case).items()}
+    x = w["X"]
+    b, s, hd, d = case.batch, case.seq, case.heads, case.head_dim
+    dz = _rng(45).standard_normal((b * s, case.hidden))
+    T = lambda v: torch.from_numpy(v).requires_grad_(True)  # noqa: E731
+    tx, tq, tk, tv, to = T(x), T(w["Wq"]), T(w["Wk"]), T(w["Wv"]), T(w["Wo"])
+
+    def heads_of(y, n):
+        return y.reshape(b, s, n, d).transpose(1, 2)
+
+    q = _torch_rope(heads_of(tx @ tq, hd), case.rope_base)
+    k = _torch_rope(heads_of(tx @ tk, case.kv_heads), case.rope_base)
+    v = heads_of(tx @ tv, case.kv_heads)
+    o = F.scaled_dot_product_attention(q, k, v, is_causal=True, enable_gqa=True)
+    (o.transpose(1, 2).reshape(b * s, hd * d) @ to).backward(torch.from_numpy(dz))
+    full = oracle.attn_backward(x, w["Wq"], w["Wk"], w["Wv"], w["Wo"], dz, hd, case.kv_heads, d, b, s,
+                                case.rope_base)
+    for key, g in (("dx", tx.grad), ("dwq", tq.grad), ("dwk", tk.grad), ("dwv", tv.grad), ("dwo", to.grad)):
+        assert np.max(np.abs(full[key] - g.numpy())) < 1e-12 * max(1.0, np.max(np.abs(g.numpy()))), key
+    parts = oracle.attn_backward_partials(x, w, dz, case, t)
+    assert np.max(np.abs(oracle.shard_sum([p["dx"] for p in parts]) - full["dx"])) < 1e-12
+    assert np.max(np.abs(np.concatenate([p["dwq"] for p in parts], axis=1) - full["dwq"])) < 1e-12
+    assert np.max(np.abs(np.concatenate([p["dwo"] for p in parts], axis=0) - full["dwo"])) < 1e-12
+    for g in range(case.kv_heads):
+        owners = [r for r in range(t) if g in oracle.rank_kv_heads(r, hd, case.kv_heads, t)]
+        got = sum(parts[r]["dwk"][:, oracle.rank_kv_heads(r, hd, case.kv_heads, t).index(g) * d:][:, :d]
+                  for r in owners)
+        assert np.max(np.abs(got - full["dwk"][:, g * d:(g + 1) * d])) < 1e-12
+    if t == 4:
+        assert oracle.rank_kv_heads(0, 4, 2, 4) == oracle.rank_kv_heads(1, 4, 2, 4) == [0]
+
+
+def test_attention_backward_single_token_and_uniform_keys():
+    """Closed forms: with one token the softmax is 1, so dV = dO and dq = dk = 0;
+    with zero queries the probabilities are uniform over the causal prefix,
+    dV[j] = sum_{i >= j} dO[i] / (i + 1)."""
+    r = _rng(46)
+    d = 8
+    q, k, v, do = (r.standard_normal((1, d)) for _ in range(4))
+    dq, dk, dv = oracle.causal_attention_backward(q, k, v, do)
+    assert np.max(np.abs(dv - do)) < 1e-15 and np.max(np.abs(dq)) < 1e-15 and np.max(np.abs(dk)) < 1e-15
+    n = 6
+    k, v, do = (r.standard_normal((n, d)) for _ in range(3))
+    _, _, dv = oracle.causal_attention_backward(np.zeros((n, d)), k, v, do)
+    want = np.array([sum(do[i] / (i + 1) for i in range(j, n)) for j in range(n)])
+    assert np.max(np.abs(dv - want)) < 1e-14
+
+
 # ---------------------------------------------------------------- inputs
 
 
