@@ -353,6 +353,60 @@ tp_status tp_mlp_act_backward(tp_act act, int64_t m, int64_t n, const void* pre,
                               void* y, void* stream);
 
 /* --------------------------------------------------------------------------
+ * Backward pass of one rank's attention ("Tensor parallelism" page, sections
+ * "Self-attention" and "f and g": the rank differentiates its own heads with
+ * no exchange; a KV head read by several of its query heads gets the sum of
+ * their gradients; the dX partials are summed over ranks by f's backward).
+ * bf16 operands, float32 accumulation; d must be 128.
+ *
+ * tp_flash_attn_lse: tp_flash_attn that also writes
+ *   lse   [batch, hq, seq_pad] float32 (seq_pad = seq rounded up to 64;
+ *         entries past seq are left as they are): the log-sum-exp of each
+ *         query row's scores in log2 units, so P = exp2(s log2(e)/sqrt(d) - lse).
+ *
+ * tp_flash_attn_backward: from the forward's q, k, vt, o, lse and the output
+ * gradient dout [batch*seq, hq*d], with P the probabilities and
+ * D = rowsum(dO * O):
+ *   dV = P^T dO,  dS = P * (dO V^T - D),  dQ = dS K / sqrt(d),  dK = dS^T Q / sqrt(d)
+ * (dK, dV summed over the query heads sharing a KV head, in ascending order).
+ * Writes bf16 rows of dqkv (row stride ld >= (hq + 2 hkv) d, a multiple of
+ * 8): dQ in columns [0, hq d), dK in [hq d, (hq + hkv) d), dV after them, the
+ * layout of tp_qkv_rope's projection output.  rope_base > 1 rotates dQ and dK
+ * back through RoPE (the transpose of the forward rotation), giving the
+ * gradient of the projection before RoPE; rope_base = 0 leaves them as the
+ * gradients of the rotated q and k.  ws: at least
+ * tp_flash_attn_backward_workspace_bytes bytes.  batch * hq <= 65535.
+ *
+ * tp_shard_attn_backward: the whole sublayer for the output gradient dZ
+ * (weights as in tp_shard_attn):
+ *   recompute q, k, vt (tp_qkv_rope), o and lse (tp_flash_attn_lse);
+ *   dO = dZ w_o;  dQKV = tp_flash_attn_backward(...) before RoPE;
+ *   dx_partial = dQKV w_qkv       [batch*seq, h] float32 (the rank's share of dX)
+ *   dw_qkv     = dQKV^T x         [(hq + 2 hkv) d, h] float32
+ *   dw_o       = dZ^T O           [h, hq d] float32
+ *   x, dz      [batch*seq, h] bf16; batch*seq must be a multiple of 8
+ *   xt, dzt    [h, batch*seq] bf16 transposes of x and dz, or NULL (then the
+ *              call makes them in ws)
+ *   ws         at least tp_shard_attn_backward_workspace_bytes bytes
+ * Biases are not differentiated here.
+ * ------------------------------------------------------------------------ */
+tp_status tp_flash_attn_lse(int64_t batch, int64_t seq, int32_t hq, int32_t hkv, int32_t head_dim,
+                            int32_t causal, const void* q, const void* k, const void* vt, void* o, float* lse,
+                            void* stream);
+size_t tp_flash_attn_backward_workspace_bytes(int64_t batch, int64_t seq, int32_t hq, int32_t hkv,
+                                              int32_t head_dim);
+tp_status tp_flash_attn_backward(int64_t batch, int64_t seq, int32_t hq, int32_t hkv, int32_t head_dim,
+                                 float rope_base, int32_t causal, const void* q, const void* k, const void* vt,
+                                 const void* o, const float* lse, const void* dout, void* ws, size_t ws_bytes,
+                                 void* dqkv, int64_t ld, void* stream);
+size_t tp_shard_attn_backward_workspace_bytes(int64_t batch, int64_t seq, int64_t h, int32_t hq, int32_t hkv,
+                                              int32_t head_dim);
+tp_status tp_shard_attn_backward(int64_t batch, int64_t seq, int64_t h, int32_t hq, int32_t hkv, int32_t head_dim,
+                                 float rope_base, int32_t causal, const void* x, const void* w_qkv, const void* w_o,
+                                 const void* dz, const void* xt, const void* dzt, void* ws, size_t ws_bytes,
+                                 float* dx_partial, float* dw_qkv, float* dw_o, void* stream);
+
+/* --------------------------------------------------------------------------
  * Introspection: how the bf16 GEMM behind tp_colwise / tp_rowwise /
  * tp_qkv_rope tiles an m x n output (n = output columns; swiglu != 0 for the
  * SwiGLU colwise GEMM, whose tiles cover 128 output columns instead of 256).

@@ -97,6 +97,66 @@ AttnLayout attn_layout(int64_t batch, int64_t seq, int32_t hq, int32_t hkv, int3
   return L;
 }
 
+// Heads of a KV group one dK/dV workgroup of the attention backward walks:
+// the whole group when that already gives the chip 512 workgroups, else the
+// group is split (the smallest divisor of its size reaching 512, or all of
+// them); each split adds a float32 partial of dK and dV summed afterwards.
+int attn_bwd_nsplit(int64_t batch, int64_t seq, int32_t hq, int32_t hkv) {
+  const int gs = hq / hkv;
+  const int64_t base = batch * hkv * ((seq + 127) / 128);
+  int n = 1;
+  while (base * n < 512) {
+    int m = n + 1;
+    while (m <= gs && gs % m != 0) ++m;
+    if (m > gs) break;
+    n = m;
+  }
+  return n;
+}
+
+struct AttnBwdLayout {
+  size_t dvec, kt, vtok, qt, dot, part, total;
+};
+
+AttnBwdLayout attn_bwd_layout(int64_t batch, int64_t seq, int32_t hq, int32_t hkv, int32_t d) {
+  const size_t B = (size_t)batch, sp = (size_t)seq_pad_of(seq), D = (size_t)d;
+  AttnBwdLayout L;
+  L.dvec = 0;
+  L.kt = L.dvec + align256(B * hq * sp * 4);
+  L.vtok = L.kt + align256(B * hkv * D * sp * 2);
+  L.qt = L.vtok + align256(B * hkv * sp * D * 2);
+  L.dot = L.qt + align256(B * hq * D * sp * 2);
+  L.part = L.dot + align256(B * hq * D * sp * 2);
+  L.total = L.part + align256(B * hkv * (size_t)attn_bwd_nsplit(batch, seq, hq, hkv) * 2 * sp * D * 4);
+  return L;
+}
+
+// Workspace of one rank's attention backward: the recomputed forward (Q, K,
+// V^T, O and the log-sum-exp), dO, the packed dQKV and the transposed
+// operands of the weight-gradient products, then the attention core's own.
+struct AttnShardBwdLayout {
+  size_t fwd, lse, dout, wo_t, dqkv, wqkv_t, dzt, o_t, dqkv_t, xt, core, total;
+};
+
+AttnShardBwdLayout attn_shard_bwd_layout(int64_t batch, int64_t seq, int64_t h, int32_t hq, int32_t hkv,
+                                         int32_t d) {
+  const size_t M = (size_t)(batch * seq), H = (size_t)h, QD = (size_t)hq * d, N = (size_t)(hq + 2 * hkv) * d;
+  AttnShardBwdLayout L;
+  L.fwd = 0;
+  L.lse = L.fwd + attn_layout(batch, seq, hq, hkv, d).total;
+  L.dout = L.lse + align256((size_t)batch * hq * (size_t)seq_pad_of(seq) * 4);
+  L.wo_t = L.dout + align256(M * QD * 2);
+  L.dqkv = L.wo_t + align256(QD * H * 2);
+  L.wqkv_t = L.dqkv + align256(M * N * 2);
+  L.dzt = L.wqkv_t + align256(H * N * 2);
+  L.o_t = L.dzt + align256(H * M * 2);
+  L.dqkv_t = L.o_t + align256(QD * M * 2);
+  L.xt = L.dqkv_t + align256(N * M * 2);
+  L.core = L.xt + align256(H * M * 2);
+  L.total = L.core + attn_bwd_layout(batch, seq, hq, hkv, d).total;
+  return L;
+}
+
 // Workspace of one rank's MLP backward (F = f or 2 f rows of w_in).
 struct MlpBwdLayout {
   size_t pre, wout_t, dy, dpre, y, win_t, y_t, dpre_t, xt, dzt, total;
@@ -319,6 +379,160 @@ tp_status tp_flash_attn(int64_t batch, int64_t seq, int32_t hq, int32_t hkv, int
   return launched(tpk::launch_flash_attn(batch, seq, seq_pad_of(seq), hq, hkv, causal, q, k, vt, o,
                                          as_stream(stream)),
                   "tp_flash_attn");
+}
+
+tp_status tp_flash_attn_lse(int64_t batch, int64_t seq, int32_t hq, int32_t hkv, int32_t head_dim,
+                            int32_t causal, const void* q, const void* k, const void* vt, void* o, float* lse,
+                            void* stream) {
+  TRY(check_attn_shape(batch, seq, hq, hkv, head_dim));
+  if (batch * seq == 0) return ok();
+  TRY(check_ptr(q, "q"));
+  TRY(check_ptr(k, "k"));
+  TRY(check_ptr(vt, "vt"));
+  TRY(check_ptr(o, "o"));
+  TRY(check_ptr(lse, "lse"));
+  TRY(device_check());
+  return launched(tpk::launch_flash_attn(batch, seq, seq_pad_of(seq), hq, hkv, causal, q, k, vt, o,
+                                         as_stream(stream), lse),
+                  "tp_flash_attn_lse");
+}
+
+size_t tp_flash_attn_backward_workspace_bytes(int64_t batch, int64_t seq, int32_t hq, int32_t hkv,
+                                              int32_t head_dim) {
+  if (batch < 0 || seq < 0 || hq <= 0 || hkv <= 0 || head_dim <= 0 || hq % hkv != 0) return 0;
+  return attn_bwd_layout(batch, seq, hq, hkv, head_dim).total;
+}
+
+tp_status tp_flash_attn_backward(int64_t batch, int64_t seq, int32_t hq, int32_t hkv, int32_t head_dim,
+                                 float rope_base, int32_t causal, const void* q, const void* k, const void* vt,
+                                 const void* o, const float* lse, const void* dout, void* ws, size_t ws_bytes,
+                                 void* dqkv, int64_t ld, void* stream) {
+  TRY(check_attn_shape(batch, seq, hq, hkv, head_dim));
+  if (!(rope_base == 0.0f || rope_base > 1.0f))
+    return fail(TP_ERR_INVALID_ARG, "rope_base must be 0 (no rotation) or > 1");
+  const int64_t n = (int64_t)(hq + 2 * hkv) * head_dim;
+  if (ld < n || ld % 8 != 0)
+    return fail(TP_ERR_SHAPE, "ld = %lld must be a multiple of 8 and >= (hq + 2 hkv) * head_dim = %lld",
+                (long long)ld, (long long)n);
+  if (seq * ld * 2 >= kMaxOffset) return fail(TP_ERR_SHAPE, "one sequence of dqkv exceeds 2 GiB");
+  if (batch * (int64_t)hq > 65535) return fail(TP_ERR_SHAPE, "batch * hq must be at most 65535");
+  if (batch * seq == 0) return ok();
+  const void* ptrs[] = {q, k, vt, o, lse, dout, ws, dqkv};
+  const char* names[] = {"q", "k", "vt", "o", "lse", "dout", "ws", "dqkv"};
+  for (int i = 0; i < 8; ++i) TRY(check_ptr(ptrs[i], names[i]));
+  const AttnBwdLayout L = attn_bwd_layout(batch, seq, hq, hkv, head_dim);
+  if (ws_bytes < L.total) return fail(TP_ERR_WORKSPACE, "workspace of %zu bytes < %zu needed", ws_bytes, L.total);
+  TRY(device_check());
+  hipStream_t s = as_stream(stream);
+  char* w = static_cast<char*>(ws);
+  const int64_t sp = seq_pad_of(seq), D = head_dim;
+  hipError_t e;
+#define TP_STEP(call, what) \
+  if ((e = (call)) != hipSuccess) return launched(e, what);
+  TP_STEP(tpk::launch_attn_dvec(batch, seq, sp, hq, o, dout, reinterpret_cast<float*>(w + L.dvec), s),
+          "tp_flash_attn_backward (D)");
+  // K^T and Q^T, dO^T per head, zero-padded to seq_pad; V token-major from V^T
+  TP_STEP(tpk::launch_transpose_batched(batch, hkv, seq, sp, D, hkv * D, sp, seq * hkv * D, D, hkv * D * sp, D * sp,
+                                        k, w + L.kt, s),
+          "tp_flash_attn_backward (K^T)");
+  TP_STEP(tpk::launch_transpose_batched(batch * hkv, 1, D, D, sp, sp, D, D * sp, 0, sp * D, 0, vt, w + L.vtok, s),
+          "tp_flash_attn_backward (V)");
+  TP_STEP(tpk::launch_transpose_batched(batch, hq, seq, sp, D, hq * D, sp, seq * hq * D, D, hq * D * sp, D * sp, q,
+                                        w + L.qt, s),
+          "tp_flash_attn_backward (Q^T)");
+  TP_STEP(tpk::launch_transpose_batched(batch, hq, seq, sp, D, hq * D, sp, seq * hq * D, D, hq * D * sp, D * sp,
+                                        dout, w + L.dot, s),
+          "tp_flash_attn_backward (dO^T)");
+  tpk::AttnBwdIn in;
+  in.q = q;
+  in.k = k;
+  in.vtok = w + L.vtok;
+  in.kt = w + L.kt;
+  in.qt = w + L.qt;
+  in.dout = dout;
+  in.dot = w + L.dot;
+  in.lse = lse;
+  in.dvec = reinterpret_cast<const float*>(w + L.dvec);
+  TP_STEP(tpk::launch_flash_attn_bwd(batch, seq, sp, hq, hkv, causal, rope_base > 0.0f ? log2((double)rope_base) : 0.0,
+                                     in, reinterpret_cast<float*>(w + L.part), attn_bwd_nsplit(batch, seq, hq, hkv),
+                                     dqkv, ld, s),
+          "tp_flash_attn_backward");
+#undef TP_STEP
+  return ok();
+}
+
+size_t tp_shard_attn_backward_workspace_bytes(int64_t batch, int64_t seq, int64_t h, int32_t hq, int32_t hkv,
+                                              int32_t head_dim) {
+  if (batch < 0 || seq < 0 || h <= 0 || hq <= 0 || hkv <= 0 || head_dim <= 0 || hq % hkv != 0) return 0;
+  return attn_shard_bwd_layout(batch, seq, h, hq, hkv, head_dim).total;
+}
+
+tp_status tp_shard_attn_backward(int64_t batch, int64_t seq, int64_t h, int32_t hq, int32_t hkv, int32_t head_dim,
+                                 float rope_base, int32_t causal, const void* x, const void* w_qkv, const void* w_o,
+                                 const void* dz, const void* xt, const void* dzt, void* ws, size_t ws_bytes,
+                                 float* dx_partial, float* dw_qkv, float* dw_o, void* stream) {
+  TRY(check_attn_shape(batch, seq, hq, hkv, head_dim));
+  if (!(rope_base > 1.0f)) return fail(TP_ERR_INVALID_ARG, "rope_base must be > 1");
+  const int64_t m = batch * seq;
+  if (m % 8 != 0)
+    return fail(TP_ERR_SHAPE, "batch * seq = %lld must be a multiple of 8 (the weight gradients reduce over tokens)",
+                (long long)m);
+  const int64_t qd = (int64_t)hq * head_dim, n = (int64_t)(hq + 2 * hkv) * head_dim;
+  // the forward's projection and the backward's five products, with their operand sizes
+  TRY(check_gemm(TP_ACT_NONE, TP_BF16, m, h, n, x, w_qkv, ws, "x", "w_qkv", "ws"));
+  TRY(check_gemm(TP_ACT_NONE, TP_BF16, m, h, qd, dz, ws, ws, "dz", "ws", "ws"));
+  TRY(check_gemm(TP_ACT_NONE, TP_BF16, m, n, h, ws, ws, dx_partial, "ws", "ws", "dx_partial"));
+  if (m == 0) return ok();
+  TRY(check_ptr(w_o, "w_o"));
+  TRY(check_gemm(TP_ACT_NONE, TP_BF16, h, m, qd, ws, ws, dw_o, "ws", "ws", "dw_o"));
+  TRY(check_gemm(TP_ACT_NONE, TP_BF16, n, m, h, ws, ws, dw_qkv, "ws", "ws", "dw_qkv"));
+  if (xt) TRY(check_ptr(xt, "xt"));
+  if (dzt) TRY(check_ptr(dzt, "dzt"));
+  const AttnShardBwdLayout L = attn_shard_bwd_layout(batch, seq, h, hq, hkv, head_dim);
+  if (ws_bytes < L.total) return fail(TP_ERR_WORKSPACE, "workspace of %zu bytes < %zu needed", ws_bytes, L.total);
+  TRY(device_check());
+  hipStream_t s = as_stream(stream);
+  char* b = static_cast<char*>(ws);
+  const AttnLayout F = attn_layout(batch, seq, hq, hkv, head_dim);
+  char* f = b + L.fwd;
+  auto gemm = [&](int epi, int64_t M, int64_t N, int64_t K, const void* a, const void* w, void* c) {
+    return tpk::launch_gemm_bf16(epi, M, N, K, a, w, c, nullptr, s);
+  };
+  hipError_t e;
+#define TP_STEP(call, what) \
+  if ((e = (call)) != hipSuccess) return launched(e, what);
+  // recompute the forward: Q, K, V^T (RoPE applied), O and the log-sum-exp
+  TRY(tp_qkv_rope(batch, seq, h, hq, hkv, head_dim, rope_base, x, w_qkv, nullptr, f + F.q, f + F.k, f + F.vt,
+                  stream));
+  TRY(tp_flash_attn_lse(batch, seq, hq, hkv, head_dim, causal, f + F.q, f + F.k, f + F.vt, f + F.o,
+                        reinterpret_cast<float*>(b + L.lse), stream));
+  // dO = dZ W_o (W_o [h, hq d] transposed to [hq d, h])
+  TP_STEP(tpk::launch_transpose(h, qd, w_o, b + L.wo_t, s), "tp_shard_attn_backward (w_o^T)");
+  TP_STEP(gemm(tpk::EPI_BF16, m, qd, h, dz, b + L.wo_t, b + L.dout), "tp_shard_attn_backward (dO)");
+  // the attention core: dQKV before RoPE, packed like the projection's output
+  TRY(tp_flash_attn_backward(batch, seq, hq, hkv, head_dim, rope_base, causal, f + F.q, f + F.k, f + F.vt, f + F.o,
+                             reinterpret_cast<const float*>(b + L.lse), b + L.dout, b + L.core, L.total - L.core,
+                             b + L.dqkv, n, stream));
+  // dX partial = dQKV W_qkv (W_qkv transposed to [h, n]); f's backward sums these over ranks
+  TP_STEP(tpk::launch_transpose(n, h, w_qkv, b + L.wqkv_t, s), "tp_shard_attn_backward (w_qkv^T)");
+  TP_STEP(gemm(tpk::EPI_F32, m, h, n, b + L.dqkv, b + L.wqkv_t, dx_partial), "tp_shard_attn_backward (dX)");
+  // dW_o = dZ^T O and dW_qkv = dQKV^T X, reducing over the tokens
+  const void* dzt_p = dzt;
+  if (!dzt_p) {
+    TP_STEP(tpk::launch_transpose(m, h, dz, b + L.dzt, s), "tp_shard_attn_backward (dZ^T)");
+    dzt_p = b + L.dzt;
+  }
+  const void* xt_p = xt;
+  if (!xt_p) {
+    TP_STEP(tpk::launch_transpose(m, h, x, b + L.xt, s), "tp_shard_attn_backward (X^T)");
+    xt_p = b + L.xt;
+  }
+  TP_STEP(tpk::launch_transpose(m, qd, f + F.o, b + L.o_t, s), "tp_shard_attn_backward (O^T)");
+  TP_STEP(gemm(tpk::EPI_F32, h, qd, m, dzt_p, b + L.o_t, dw_o), "tp_shard_attn_backward (dW_o)");
+  TP_STEP(tpk::launch_transpose(m, n, b + L.dqkv, b + L.dqkv_t, s), "tp_shard_attn_backward (dQKV^T)");
+  TP_STEP(gemm(tpk::EPI_F32, n, h, m, b + L.dqkv_t, xt_p, dw_qkv), "tp_shard_attn_backward (dW_qkv)");
+#undef TP_STEP
+  return ok();
 }
 
 size_t tp_shard_attn_workspace_bytes(int64_t batch, int64_t seq, int32_t hq, int32_t hkv,

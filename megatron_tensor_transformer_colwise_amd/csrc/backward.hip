@@ -44,21 +44,32 @@ __global__ __launch_bounds__(NT) void transpose_kernel(const bf16_t* src, bf16_t
   }
 }
 
-// The same with 16-byte accesses (rows and cols multiples of 8): a thread
-// reads 8 consecutive elements of a source row into LDS (rows padded by 8
-// elements, so the column reads below spread over the banks) and writes 8
+// The same with 16-byte accesses, generalised for the attention backward's
+// layouts.  Per batch z = z1 * n2 + z2 (blockIdx.z; src starts at
+// z1 * src_bs1 + z2 * src_bs2, dst at z1 * dst_bs1 + z2 * dst_bs2):
+//   dst[c * ldd + r] = r < rows_in ? src[r * lds + c] : 0,  r < rows_out, c < cols
+// A thread reads 8 consecutive elements of a source row into LDS (rows padded
+// by 8 elements, so the column reads spread over the banks) and writes 8
 // consecutive elements of a destination row, gathered down an LDS column.
-__global__ __launch_bounds__(NT) void transpose16_kernel(const bf16_t* src, bf16_t* dst, int64_t rows,
-                                                         int64_t cols) {
+// rows_out must be a multiple of 8; a source row is read in chunks of 8 from
+// c = 0, so up to 7 elements past cols are read (the caller keeps them in
+// bounds: cols a multiple of 8, or padding after each row).
+__global__ __launch_bounds__(NT) void transpose16_kernel(const bf16_t* src, bf16_t* dst, int64_t rows_in,
+                                                         int64_t rows_out, int64_t cols, int64_t lds, int64_t ldd,
+                                                         int n2, int64_t src_bs1, int64_t src_bs2, int64_t dst_bs1,
+                                                         int64_t dst_bs2) {
   constexpr int PAD = TT + 8;
   __shared__ bf16_t tile[TT][PAD];
+  const int64_t z1 = blockIdx.z / n2, z2 = blockIdx.z % n2;
+  src += z1 * src_bs1 + z2 * src_bs2;
+  dst += z1 * dst_bs1 + z2 * dst_bs2;
   const int64_t r0 = (int64_t)blockIdx.y * TT, c0 = (int64_t)blockIdx.x * TT;
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
     const int idx = threadIdx.x + k * NT;  // 512 chunks of 8: 64 rows x 8 chunks
     const int r = idx >> 3, ch = (idx & 7) * 8;
     u32x4 v = {0, 0, 0, 0};
-    if (r0 + r < rows && c0 + ch < cols) v = *reinterpret_cast<const u32x4*>(src + (r0 + r) * cols + c0 + ch);
+    if (r0 + r < rows_in && c0 + ch < cols) v = *reinterpret_cast<const u32x4*>(src + (r0 + r) * lds + c0 + ch);
     *reinterpret_cast<u32x4*>(&tile[r][ch]) = v;
   }
   __syncthreads();
@@ -66,12 +77,12 @@ __global__ __launch_bounds__(NT) void transpose16_kernel(const bf16_t* src, bf16
   for (int k = 0; k < 2; ++k) {
     const int idx = threadIdx.x + k * NT;  // destination: 64 rows (source columns) x 8 chunks
     const int c = idx >> 3, rr = (idx & 7) * 8;
-    if (c0 + c < cols && r0 + rr < rows) {
+    if (c0 + c < cols && r0 + rr < rows_out) {
       uint32_t w[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e)
         w[e] = (uint32_t)tile[rr + 2 * e][c] | ((uint32_t)tile[rr + 2 * e + 1][c] << 16);
-      *reinterpret_cast<u32x4*>(dst + (c0 + c) * rows + r0 + rr) = u32x4{w[0], w[1], w[2], w[3]};
+      *reinterpret_cast<u32x4*>(dst + (c0 + c) * ldd + r0 + rr) = u32x4{w[0], w[1], w[2], w[3]};
     }
   }
 }
@@ -139,7 +150,8 @@ hipError_t launch_transpose(int64_t rows, int64_t cols, const void* src, void* d
   const dim3 grid((unsigned)((cols + TT - 1) / TT), (unsigned)((rows + TT - 1) / TT));
   if (rows % 8 == 0 && cols % 8 == 0)
     hipLaunchKernelGGL(transpose16_kernel, grid, dim3(NT), 0, s, reinterpret_cast<const bf16_t*>(src),
-                       reinterpret_cast<bf16_t*>(dst), rows, cols);
+                       reinterpret_cast<bf16_t*>(dst), rows, rows, cols, cols, rows, 1, (int64_t)0, (int64_t)0,
+                       (int64_t)0, (int64_t)0);
   else
     hipLaunchKernelGGL(transpose_kernel, grid, dim3(NT), 0, s, reinterpret_cast<const bf16_t*>(src),
                        reinterpret_cast<bf16_t*>(dst), rows, cols);
@@ -157,6 +169,18 @@ hipError_t launch_act_backward(int swiglu, int64_t m, int64_t n, const void* pre
     hipLaunchKernelGGL(act_backward_kernel<true>, grid, dim3(NT), 0, s, P(pre), P(dy), Q(dpre), Q(y), m, n);
   else
     hipLaunchKernelGGL(act_backward_kernel<false>, grid, dim3(NT), 0, s, P(pre), P(dy), Q(dpre), Q(y), m, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_transpose_batched(int64_t n1, int64_t n2, int64_t rows_in, int64_t rows_out, int64_t cols,
+                                    int64_t lds, int64_t ldd, int64_t src_bs1, int64_t src_bs2, int64_t dst_bs1,
+                                    int64_t dst_bs2, const void* src, void* dst, hipStream_t s) {
+  if (n1 == 0 || n2 == 0 || rows_out == 0 || cols == 0) return hipSuccess;
+  if (rows_out % 8 != 0 || rows_in > rows_out || n1 * n2 > 65535) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)((cols + TT - 1) / TT), (unsigned)((rows_out + TT - 1) / TT), (unsigned)(n1 * n2));
+  hipLaunchKernelGGL(transpose16_kernel, grid, dim3(NT), 0, s, reinterpret_cast<const bf16_t*>(src),
+                     reinterpret_cast<bf16_t*>(dst), rows_in, rows_out, cols, lds, ldd, (int)n2, src_bs1, src_bs2,
+                     dst_bs1, dst_bs2);
   return hipGetLastError();
 }
 

@@ -41,6 +41,7 @@ struct FaArgs {
   const bf16_t* k;
   const bf16_t* vt;
   bf16_t* o;
+  float* lse;  // [batch, hq, seq_pad] log2-domain log-sum-exp of the scaled scores, or NULL
   int64_t seq, seq_pad;
   int hq, hkv, batch, nqb, causal;
   float scale_log2;
@@ -257,6 +258,9 @@ __global__ __launch_bounds__(NT, 2) void flash_attn_kernel(FaArgs a) {
   // ---- normalise and store: O^T block db, register r -> d = 32 db + 8 (r/4) + 4 h + r%4
   const float l_tot = l_run + other_half(l_run);
   const float inv = 1.0f / l_tot;
+  // for the backward pass: P = exp2(s * scale_log2 - lse), lse = m * scale_log2 + log2(l)
+  if (a.lse && h == 0 && qpos < seq)
+    a.lse[((int64_t)b * a.hq + j) * a.seq_pad + qpos] = m_use * a.scale_log2 + __builtin_amdgcn_logf(l_tot);
   if (qpos < seq) {
     bf16_t* orow = a.o + ((int64_t)b * seq + qpos) * ldq + (int64_t)j * D;
 #pragma unroll
@@ -275,12 +279,13 @@ __global__ __launch_bounds__(NT, 2) void flash_attn_kernel(FaArgs a) {
 
 hipError_t launch_flash_attn(int64_t batch, int64_t seq, int64_t seq_pad, int hq, int hkv,
                              int causal, const void* q, const void* k, const void* vt, void* o,
-                             hipStream_t s) {
+                             hipStream_t s, float* lse) {
   FaArgs a;
   a.q = reinterpret_cast<const bf16_t*>(q);
   a.k = reinterpret_cast<const bf16_t*>(k);
   a.vt = reinterpret_cast<const bf16_t*>(vt);
   a.o = reinterpret_cast<bf16_t*>(o);
+  a.lse = lse;
   a.seq = seq;
   a.seq_pad = seq_pad;
   a.hq = hq;

@@ -52,9 +52,40 @@ hipError_t launch_gemm_bf16_group(int epi, int groups, int64_t M, int64_t N, int
 hipError_t launch_gemm_f32(int epi, int64_t M, int64_t N, int64_t K, const float* x, const float* w,
                            float* out, hipStream_t s, const float* bias = nullptr, int64_t lda = 0);
 
+// lse (optional): [batch, hq, seq_pad] float32 (entries past seq untouched),
+// the log-sum-exp of the scores scaled to log2 units:
+// P = exp2(s * log2(e) / sqrt(d) - lse).
 hipError_t launch_flash_attn(int64_t batch, int64_t seq, int64_t seq_pad, int hq, int hkv,
                              int causal, const void* q, const void* k, const void* vt, void* o,
-                             hipStream_t s);
+                             hipStream_t s, float* lse = nullptr);
+
+// Backward of launch_flash_attn for head_dim 128.  Inputs as the forward's
+// (q, k token-major, vt per head transposed, seq_pad columns) plus kt
+// [batch, hkv, 128, seq_pad] and vtok [batch, hkv, seq_pad, 128] (K
+// transposed, V token-major, zero past seq), qt, dot [batch, hq, 128, seq_pad]
+// (Q and dO transposed), dout [batch*seq, hq*128], lse and dvec
+// [batch, hq, seq_pad] (dvec = rowsum(dO * O)).  Writes dQ into columns
+// [0, hq*128) of dqkv rows (row stride ld), and dK, dV after it; with
+// log2_base != 0 dQ and dK are rotated back through RoPE (base 2^log2_base).
+// part: float32 scratch [batch, hkv, nsplit, 2, seq_pad, 128]; nsplit divides
+// hq / hkv.
+struct AttnBwdIn {
+  const void* q;
+  const void* k;
+  const void* vtok;
+  const void* kt;
+  const void* qt;
+  const void* dout;
+  const void* dot;
+  const float* lse;
+  const float* dvec;
+};
+hipError_t launch_flash_attn_bwd(int64_t batch, int64_t seq, int64_t seq_pad, int hq, int hkv, int causal,
+                                 double log2_base, const AttnBwdIn& in, float* part, int nsplit, void* dqkv,
+                                 int64_t ld, hipStream_t s);
+// dvec[b, j, p] = sum_c dout[b*seq + p, j*128 + c] * o[...] (rows past seq untouched).
+hipError_t launch_attn_dvec(int64_t batch, int64_t seq, int64_t seq_pad, int hq, const void* o, const void* dout,
+                            float* dvec, hipStream_t s);
 
 hipError_t launch_shard_sum(int t, int64_t n, const float* const* partials, const void* residual,
                             int residual_bf16, float* out, hipStream_t s);
@@ -87,6 +118,14 @@ hipError_t launch_ce_combine(int t, int64_t m, const float* const* stats, float*
 
 // dst [cols, rows] = src [rows, cols]^T, bf16.
 hipError_t launch_transpose(int64_t rows, int64_t cols, const void* src, void* dst, hipStream_t s);
+
+// Per batch z = z1 * n2 + z2 (z1 < n1): with src and dst advanced by
+// z1 * bs1 + z2 * bs2 of their own, dst[c * ldd + r] = r < rows_in ?
+// src[r * lds + c] : 0 for r < rows_out (a multiple of 8), c < cols; reads up
+// to 7 elements past cols in each source row (the caller keeps them in bounds).
+hipError_t launch_transpose_batched(int64_t n1, int64_t n2, int64_t rows_in, int64_t rows_out, int64_t cols,
+                                    int64_t lds, int64_t ldd, int64_t src_bs1, int64_t src_bs2, int64_t dst_bs1,
+                                    int64_t dst_bs2, const void* src, void* dst, hipStream_t s);
 
 // From the pre-activation and dY (n columns): dPre and, if y, the activation
 // Y.  GeLU: pre [m, n]; SwiGLU: pre [m, 2n] = [gate | up], dPre likewise.

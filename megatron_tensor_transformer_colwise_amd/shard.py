@@ -210,6 +210,38 @@ class AttnShards:
         self.reduce(residual, residual_dt, stream)
         return self.out
 
+    # ---- backward ("Self-attention" + "f and g": each rank differentiates its
+    # own heads from the whole dZ; the dX partials are summed)
+
+    def _bwd_buffers(self):
+        if getattr(self, "bwd_ws", None) is None:
+            dev, m, h, d = self.x.device, self.batch * self.seq, self.h, self.d
+            hq, hkv = self.ranks[0].hq, max(rk.hkv for rk in self.ranks)
+            self.bwd_ws_bytes = tp.tp_shard_attn_backward_workspace_bytes(self.batch, self.seq, h, hq, hkv, d)
+            self.bwd_ws = torch.empty(self.bwd_ws_bytes, dtype=torch.uint8, device=dev)
+            self.dx_partials = torch.empty(self.t, m, h, dtype=torch.float32, device=dev)
+            self.dw_qkv = [torch.empty((rk.hq + 2 * rk.hkv) * d, h, dtype=torch.float32, device=dev)
+                           for rk in self.ranks]
+            self.dw_o = [torch.empty(h, rk.hq * d, dtype=torch.float32, device=dev) for rk in self.ranks]
+            self.dx = torch.empty(m, h, dtype=torch.float32, device=dev)
+
+    def backward_rank(self, r: int, dz, x=None, stream=None) -> None:
+        """Rank r's gradients: its dX partial and the gradients of its W_qkv
+        rows and W_o columns."""
+        self._bwd_buffers()
+        rk = self.ranks[r]
+        tp.tp_shard_attn_backward(self.batch, self.seq, self.h, rk.hq, rk.hkv, self.d, self.case.rope_base,
+                                  self.causal, self.x if x is None else x, rk.w_qkv, rk.w_o, dz, None, None,
+                                  self.bwd_ws, self.bwd_ws_bytes, self.dx_partials[r], self.dw_qkv[r],
+                                  self.dw_o[r], stream)
+
+    def backward(self, dz, x=None, stream=None):
+        for r in range(self.t):
+            self.backward_rank(r, dz, x, stream)
+        m = self.batch * self.seq
+        tp.tp_shard_sum(self.t, m * self.h, list(self.dx_partials), None, "f32", self.dx, stream)
+        return self.dx
+
 
 class BlockShards:
     """Pre-norm block, every rank on one device:

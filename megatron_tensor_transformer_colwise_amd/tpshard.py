@@ -64,6 +64,13 @@ _SIGS = {
                               _vp, _vp, _vp],
     "tp_transpose": [_i64, _i64, _vp, _vp, _vp],
     "tp_mlp_act_backward": [_i32, _i64, _i64, _vp, _vp, _vp, _vp, _vp],
+    "tp_flash_attn_lse": [_i64, _i64, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp],
+    "tp_flash_attn_backward_workspace_bytes": [_i64, _i64, _i32, _i32, _i32],
+    "tp_flash_attn_backward": [_i64, _i64, _i32, _i32, _i32, _f32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                               ctypes.c_size_t, _vp, _i64, _vp],
+    "tp_shard_attn_backward_workspace_bytes": [_i64, _i64, _i64, _i32, _i32, _i32],
+    "tp_shard_attn_backward": [_i64, _i64, _i64, _i32, _i32, _i32, _f32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                               ctypes.c_size_t, _vp, _vp, _vp, _vp],
     "tp_vocab_logits": [_i64, _i64, _i64, _vp, _vp, _vp, _vp],
     "tp_ce_stats": [_i64, _i64, _i64, _vp, _vp, _vp, _vp],
     "tp_ce_combine": [_i32, _i64, _i64, ctypes.POINTER(_vp), _vp, _vp, _vp, _vp],
@@ -86,6 +93,8 @@ def lib() -> ctypes.CDLL:
         L.tp_last_error.restype = ctypes.c_char_p
         L.tp_shard_attn_workspace_bytes.restype = ctypes.c_size_t
         L.tp_shard_mlp_backward_workspace_bytes.restype = ctypes.c_size_t
+        L.tp_flash_attn_backward_workspace_bytes.restype = ctypes.c_size_t
+        L.tp_shard_attn_backward_workspace_bytes.restype = ctypes.c_size_t
         _lib = L
     return _lib
 
@@ -231,6 +240,32 @@ def tp_shard_mlp_backward(act, m, h, f_shard, x, w_in, w_out, dz, xt, dzt, ws, w
     _check(lib().tp_shard_mlp_backward(_e(act, ACTS), m, h, f_shard, _p(x), _p(w_in), _p(w_out), _p(dz), _p(xt),
                                        _p(dzt), _p(ws), ws_bytes, _p(dx_partial), _p(dw_in), _p(dw_out),
                                        _s(stream)))
+
+
+def tp_flash_attn_lse(batch, seq, hq, hkv, head_dim, causal, q, k, vt, o, lse, stream=None) -> None:
+    _check(lib().tp_flash_attn_lse(batch, seq, hq, hkv, head_dim, int(causal), _p(q), _p(k), _p(vt), _p(o),
+                                   _p(lse), _s(stream)))
+
+
+def tp_flash_attn_backward_workspace_bytes(batch, seq, hq, hkv, head_dim) -> int:
+    return int(lib().tp_flash_attn_backward_workspace_bytes(batch, seq, hq, hkv, head_dim))
+
+
+def tp_flash_attn_backward(batch, seq, hq, hkv, head_dim, rope_base, causal, q, k, vt, o, lse, dout, ws, ws_bytes,
+                           dqkv, ld, stream=None) -> None:
+    _check(lib().tp_flash_attn_backward(batch, seq, hq, hkv, head_dim, rope_base, int(causal), _p(q), _p(k), _p(vt),
+                                        _p(o), _p(lse), _p(dout), _p(ws), ws_bytes, _p(dqkv), ld, _s(stream)))
+
+
+def tp_shard_attn_backward_workspace_bytes(batch, seq, h, hq, hkv, head_dim) -> int:
+    return int(lib().tp_shard_attn_backward_workspace_bytes(batch, seq, h, hq, hkv, head_dim))
+
+
+def tp_shard_attn_backward(batch, seq, h, hq, hkv, head_dim, rope_base, causal, x, w_qkv, w_o, dz, xt, dzt, ws,
+                           ws_bytes, dx_partial, dw_qkv, dw_o, stream=None) -> None:
+    _check(lib().tp_shard_attn_backward(batch, seq, h, hq, hkv, head_dim, rope_base, int(causal), _p(x), _p(w_qkv),
+                                        _p(w_o), _p(dz), _p(xt), _p(dzt), _p(ws), ws_bytes, _p(dx_partial),
+                                        _p(dw_qkv), _p(dw_o), _s(stream)))
 
 
 def tp_transpose(rows, cols, src, dst, stream=None) -> None:

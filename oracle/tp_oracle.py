@@ -677,8 +677,20 @@ def rope_backward(g: np.ndarray, pos: np.ndarray, base: float) -> np.ndarray:
     return np.concatenate([g1 * c + g2 * s, g2 * c - g1 * s], axis=-1)
 
 
-def causal_attention_backward(q, k, v, do):
-    """Gradients (dq, dk, dv) of O = softmax(q k^T / sqrt(d), causal) v for dO.
+def attention_lse(q, k, causal: bool = True) -> np.ndarray:
+    """Per query row, log(sum_j exp(q k_j / sqrt(d))) over the visible keys
+    (the softmax's normaliser in log form), natural log."""
+    d = q.shape[-1]
+    s = (q @ k.T) / math.sqrt(d)
+    if causal:
+        s = np.where(np.arange(k.shape[0])[None, :] > np.arange(q.shape[0])[:, None], -np.inf, s)
+    mx = s.max(axis=1, keepdims=True)
+    return (mx + np.log(np.exp(s - mx).sum(axis=1, keepdims=True)))[:, 0]
+
+
+def causal_attention_backward(q, k, v, do, causal: bool = True):
+    """Gradients (dq, dk, dv) of O = softmax(q k^T / sqrt(d), causal) v for dO
+    (``causal=False``: every key visible).
 
     With P the probabilities: dV = P^T dO, dP = dO V^T, and the softmax
     Jacobian gives dS = P * (dP - rowsum(dP * P)); the scale carries through to
@@ -686,7 +698,8 @@ def causal_attention_backward(q, k, v, do):
     d = q.shape[-1]
     n = q.shape[0]
     s = (q @ k.T) / math.sqrt(d)
-    s = np.where(np.arange(k.shape[0])[None, :] > np.arange(n)[:, None], -np.inf, s)
+    if causal:
+        s = np.where(np.arange(k.shape[0])[None, :] > np.arange(n)[:, None], -np.inf, s)
     p = np.exp(s - s.max(axis=1, keepdims=True))
     p = p / p.sum(axis=1, keepdims=True)
     dv = p.T @ do

@@ -295,3 +295,29 @@ def test_mlp_backward_validation(L):
     assert status("tp_mlp_act_backward", 0, 4, 16, A16, A16, A16, None, None) == tp.TP_ERR_INVALID_ARG
     assert status("tp_mlp_act_backward", 1, 4, 12, A16, A16, A16, None, None) == tp.TP_ERR_SHAPE
 
+
+
+def test_attention_backward_validation(L):
+    ws = tp.tp_flash_attn_backward_workspace_bytes(2, 64, 4, 2, 128)
+    assert ws > 0 and tp.tp_flash_attn_backward_workspace_bytes(2, 64, 4, 3, 128) == 0
+    core = lambda d=128, rope=500000.0, ld=1024, wsb=ws, hq=4, hkv=2, q=A16: status(  # noqa: E731
+        "tp_flash_attn_backward", 2, 64, hq, hkv, d, rope, 1, q, A16, A16, A16, A16, A16, A16, wsb, A16, ld, None)
+    assert core(d=64) == tp.TP_ERR_UNSUPPORTED
+    assert core(rope=0.5) == tp.TP_ERR_INVALID_ARG        # neither 0 nor > 1
+    assert core(ld=1016) == tp.TP_ERR_SHAPE               # < (hq + 2 hkv) d
+    assert core(ld=1028) == tp.TP_ERR_SHAPE               # not a multiple of 8
+    assert core(hq=4, hkv=3) == tp.TP_ERR_SHAPE
+    assert core(wsb=ws - 1) == tp.TP_ERR_WORKSPACE
+    assert core(q=MIS) == tp.TP_ERR_INVALID_ARG
+    assert status("tp_flash_attn_lse", 2, 64, 4, 2, 128, 1, A16, A16, A16, A16, None, None) == tp.TP_ERR_INVALID_ARG
+    sws = tp.tp_shard_attn_backward_workspace_bytes(2, 64, 256, 4, 2, 128)
+    assert sws > ws
+    shard_bwd = lambda seq=64, wsb=sws, rope=500000.0, x=A16: status(  # noqa: E731
+        "tp_shard_attn_backward", 2, seq, 256, 4, 2, 128, rope, 1, x, A16, A16, A16, None, None, A16, wsb,
+        A16, A16, A16, None)
+    assert shard_bwd(seq=63) == tp.TP_ERR_SHAPE           # batch * seq not a multiple of 8
+    assert shard_bwd(rope=0.0) == tp.TP_ERR_INVALID_ARG
+    assert shard_bwd(wsb=sws - 1) == tp.TP_ERR_WORKSPACE
+    assert shard_bwd(x=MIS) == tp.TP_ERR_INVALID_ARG
+    assert status("tp_flash_attn_backward", 0, 64, 4, 2, 128, 0.0, 1, None, None, None, None, None, None, None, 0,
+                  None, 1024, None) == tp.TP_OK

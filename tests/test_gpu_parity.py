@@ -10,6 +10,8 @@ need only K and V, which the oracle computes for every token).
 """
 import time
 
+import math
+
 import numpy as np
 import pytest
 import torch
@@ -408,6 +410,177 @@ def test_mlp_backward(device, act, m, h, f, t):
             assert rel_err(g[fs:], parts[r]["dw3"].T) <= BF16_TOL
             assert rel_err(host(mlp.dw_out[r]), parts[r]["dw2"].T) <= BF16_TOL
     assert rel_err(host(dx), full["dx"]) <= BF16_TOL
+
+
+def _attn_core_inputs(device, batch, seq, hq, hkv, seed, d=128):
+    """Seeded bf16 q, k, v, dO (token-major) and the per-head transposed V the
+    forward reads (zero past seq)."""
+    m = batch * seq
+    q = inputs.normal(seed, 1, (m, hq * d), 1.0, "bf16").torch()
+    k = inputs.normal(seed, 2, (m, hkv * d), 1.0, "bf16").torch()
+    v = inputs.normal(seed, 3, (m, hkv * d), 1.0, "bf16").torch()
+    do = inputs.normal(seed, 4, (m, hq * d), 1.0, "bf16").torch()
+    seq_pad = (seq + 63) // 64 * 64
+    vt = torch.zeros(batch, hkv, d, seq_pad, dtype=torch.bfloat16)
+    vt[..., :seq] = v.view(batch, seq, hkv, d).permute(0, 2, 3, 1)
+    return {"q": q, "k": k, "v": v, "do": do, "vt": vt, "seq_pad": seq_pad}
+
+
+def _attn_core_backward(device, batch, seq, hq, hkv, causal, rope_base, t_in):
+    """Forward with LSE, then the core backward, through the C ABI."""
+    d = 128
+    m = batch * seq
+    dev = {k: v.to(device) for k, v in t_in.items() if torch.is_tensor(v)}
+    o = torch.empty(m, hq * d, dtype=torch.bfloat16, device=device)
+    lse = torch.full((batch, hq, t_in["seq_pad"]), float("nan"), dtype=torch.float32, device=device)
+    tp.tp_flash_attn_lse(batch, seq, hq, hkv, d, causal, dev["q"], dev["k"], dev["vt"], o, lse)
+    n = (hq + 2 * hkv) * d
+    ws_bytes = tp.tp_flash_attn_backward_workspace_bytes(batch, seq, hq, hkv, d)
+    # NaN-filled workspace: any read of a padding entry that is not masked shows up
+    ws = torch.full((ws_bytes // 4,), float("nan"), dtype=torch.float32, device=device)
+    dqkv = torch.full((m, n + 8), float("nan"), dtype=torch.bfloat16, device=device)
+    tp.tp_flash_attn_backward(batch, seq, hq, hkv, d, rope_base, causal, dev["q"], dev["k"], dev["vt"], o, lse,
+                              dev["do"], ws, ws_bytes, dqkv, n + 8)
+    torch.cuda.synchronize()
+    return o, lse, dqkv
+
+
+@pytest.mark.parametrize("batch,seq,hq,hkv,causal", [(2, 130, 4, 2, True), (1, 300, 4, 1, True),
+                                                     (2, 64, 2, 2, True), (1, 200, 4, 2, False),
+                                                     (1, 1, 2, 1, True)])
+def test_flash_attn_lse(device, batch, seq, hq, hkv, causal):
+    """The forward's log-sum-exp (log2 units) against the oracle's natural-log
+    normaliser times log2(e); the output is the forward's own."""
+    say(f"case flash lse b={batch} s={seq} hq={hq} hkv={hkv} causal={causal}")
+    d = 128
+    t_in = _attn_core_inputs(device, batch, seq, hq, hkv, 81)
+    m = batch * seq
+    o = torch.empty(m, hq * d, dtype=torch.bfloat16, device=device)
+    lse = torch.full((batch, hq, t_in["seq_pad"]), -7.0, dtype=torch.float32, device=device)
+    tp.tp_flash_attn_lse(batch, seq, hq, hkv, d, causal, t_in["q"].to(device), t_in["k"].to(device),
+                         t_in["vt"].to(device), o, lse)
+    o2 = torch.empty_like(o)
+    tp.tp_flash_attn(batch, seq, hq, hkv, d, causal, t_in["q"].to(device), t_in["k"].to(device),
+                     t_in["vt"].to(device), o2)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2)
+    got = lse.cpu().double().numpy()
+    assert np.all(got[:, :, seq:] == -7.0)  # padding untouched
+    qh, kh = t_in["q"].double().numpy(), t_in["k"].double().numpy()
+    worst = 0.0
+    for b in range(batch):
+        rows = slice(b * seq, (b + 1) * seq)
+        for j in range(hq):
+            g = j // (hq // hkv)
+            ref = oracle.attention_lse(qh[rows, j * d:(j + 1) * d], kh[rows, g * d:(g + 1) * d], causal)
+            worst = max(worst, float(np.max(np.abs(got[b, j, :seq] - ref / math.log(2.0)))))
+    say(f"  max|lse gpu - oracle| = {worst:.3e} (log2 units)")
+    # the scores are float32 sums of bf16 products; |s| / sqrt(d) stays below ~6 here
+    assert worst <= 1e-3
+
+
+@pytest.mark.parametrize("batch,seq,hq,hkv,causal,rope", [
+    (2, 130, 4, 2, True, 0.0), (1, 300, 4, 1, True, 500000.0), (2, 64, 2, 2, True, 10000.0),
+    (1, 200, 4, 2, False, 0.0), (1, 1, 2, 1, True, 500000.0), (1, 257, 8, 1, True, 500000.0)])
+def test_flash_attn_backward_core(device, batch, seq, hq, hkv, causal, rope):
+    """dQ, dK, dV of the attention core (GQA groups summed, RoPE rotated back
+    when rope > 0) against the oracle's, from the same bf16 q, k, v, dO;
+    ragged sequences, a single token, several query tiles per key block and a
+    head group split over workgroups; bitwise equal on a second run."""
+    say(f"case flash backward b={batch} s={seq} hq={hq} hkv={hkv} causal={causal} rope={rope}")
+    d = 128
+    t_in = _attn_core_inputs(device, batch, seq, hq, hkv, 82)
+    o, lse, dqkv = _attn_core_backward(device, batch, seq, hq, hkv, causal, rope, t_in)
+    _, _, dqkv2 = _attn_core_backward(device, batch, seq, hq, hkv, causal, rope, t_in)
+    n = (hq + 2 * hkv) * d
+    assert torch.equal(dqkv[:, :n].view(torch.int16), dqkv2[:, :n].view(torch.int16))
+    got = host(dqkv)
+    assert np.all(np.isnan(got[:, n:]))  # the row padding is not written
+    got = got[:, :n]
+    qh, kh, vh, doh = (t_in[x].double().numpy() for x in ("q", "k", "v", "do"))
+    ref = np.zeros_like(got)
+    pos = np.arange(seq)
+    for b in range(batch):
+        rows = slice(b * seq, (b + 1) * seq)
+        for j in range(hq):
+            g = j // (hq // hkv)
+            dq, dk, dv = oracle.causal_attention_backward(
+                qh[rows, j * d:(j + 1) * d], kh[rows, g * d:(g + 1) * d], vh[rows, g * d:(g + 1) * d],
+                doh[rows, j * d:(j + 1) * d], causal)
+            ref[rows, j * d:(j + 1) * d] = dq
+            ref[rows, (hq + g) * d:(hq + g + 1) * d] += dk
+            ref[rows, (hq + hkv + g) * d:(hq + hkv + g + 1) * d] += dv
+        if rope > 0:
+            for c in range(hq + hkv):
+                ref[rows, c * d:(c + 1) * d] = oracle.rope_backward(ref[rows, c * d:(c + 1) * d], pos, rope)
+    for name, cols in (("dq", slice(0, hq * d)), ("dk", slice(hq * d, (hq + hkv) * d)),
+                       ("dv", slice((hq + hkv) * d, n))):
+        say(f"  {name}")
+        if np.max(np.abs(ref[:, cols])) == 0.0:
+            # one token: the softmax is constant, dq = dk = 0 exactly; the GPU
+            # keeps only the rounding of dP - D (float32 sums in two orders)
+            assert np.max(np.abs(got[:, cols])) <= 1e-5 * np.max(np.abs(ref)), name
+        else:
+            assert rel_err(got[:, cols], ref[:, cols]) <= BF16_TOL, name
+
+
+@pytest.mark.parametrize("batch,seq,h,heads,kv,t", [(2, 72, 256, 8, 2, 2), (1, 136, 384, 8, 2, 4),
+                                                    (2, 64, 256, 4, 4, 1)])
+def test_attention_backward(device, batch, seq, h, heads, kv, t):
+    """Each rank's dX partial and weight gradients (W_qkv rows, W_o columns)
+    against the oracle's; the summed dX (f's backward) against the unsharded
+    layer's; t = 4 > kv = 2 replicates a KV head on two ranks."""
+    say(f"case attn backward b={batch} s={seq} h={h} heads={heads} kv={kv} t={t}")
+    case = inputs.AttnCase("bwd", batch, seq, h, heads, kv, 128, t, 500000.0, seed=75)
+    w = inputs.gen_attn(case)
+    m = batch * seq
+    dz = inputs.normal(75, 9, (m, h), 1.0, "bf16")
+    dw = {k: to_dev(v, device) for k, v in w.items()}
+    at = shard.AttnShards(dw["X"], dw, case)
+    dx = at.backward(to_dev(dz, device))
+    torch.cuda.synchronize()
+    W = {k: v.f64() for k, v in w.items()}
+    DZ = dz.f64()
+    parts = oracle.attn_backward_partials(W["X"], W, DZ, case, t)
+    for r in range(t):
+        say(f"  rank {r}")
+        p = parts[r]
+        assert rel_err(host(at.dx_partials[r]), p["dx"]) <= BF16_TOL
+        ref_qkv = np.concatenate([p["dwq"].T, p["dwk"].T, p["dwv"].T], axis=0)
+        assert rel_err(host(at.dw_qkv[r]), ref_qkv) <= BF16_TOL
+        assert rel_err(host(at.dw_o[r]), p["dwo"].T) <= BF16_TOL
+    full = oracle.attn_backward(W["X"], W["Wq"], W["Wk"], W["Wv"], W["Wo"], DZ, heads, kv, 128, batch, seq,
+                                case.rope_base)
+    assert rel_err(host(dx), full["dx"]) <= BF16_TOL
+
+
+def test_flash_attn_backward_full_size_sampled(device):
+    """The core backward at the 70B t = 8 rank's shape (4 sequences of 2048,
+    8 query heads, 1 KV head, RoPE base 500000) in the configuration the
+    benchmark times: for the last sequence, dQ of 64 sampled rows per head and
+    dK, dV of 64 sampled rows (summed over the 8 heads) against the oracle."""
+    batch, seq, hq, hkv, d, rope = 4, 2048, 8, 1, 128, 500000.0
+    say(f"case flash backward full size b={batch} s={seq} hq={hq} hkv={hkv}")
+    t_in = _attn_core_inputs(device, batch, seq, hq, hkv, 83)
+    _, _, dqkv = _attn_core_backward(device, batch, seq, hq, hkv, True, rope, t_in)
+    b = batch - 1
+    rows = slice(b * seq, (b + 1) * seq)
+    got = host(dqkv[b * seq:(b + 1) * seq])
+    sample = np.sort(np.random.default_rng(7).choice(seq, 64, replace=False))
+    sample[0], sample[-1] = 0, seq - 1
+    qh, kh, vh, doh = (t_in[x][rows].double().numpy() for x in ("q", "k", "v", "do"))
+    dk_sum = np.zeros((seq, d))
+    dv_sum = np.zeros((seq, d))
+    pos = np.arange(seq)
+    for j in range(hq):
+        dq, dk, dv = oracle.causal_attention_backward(qh[:, j * d:(j + 1) * d], kh, vh, doh[:, j * d:(j + 1) * d])
+        dk_sum += dk
+        dv_sum += dv
+        ref = oracle.rope_backward(dq, pos, rope)[sample]
+        assert rel_err(got[sample, j * d:(j + 1) * d], ref) <= BF16_TOL, j
+    say("  dk, dv")
+    assert rel_err(got[sample, hq * d:(hq + 1) * d], oracle.rope_backward(dk_sum, pos, rope)[sample]) <= BF16_TOL
+    assert rel_err(got[sample, (hq + 1) * d:(hq + 2) * d], dv_sum[sample]) <= BF16_TOL
 
 
 # ---------------------------------------------------------------- vocabulary parallel

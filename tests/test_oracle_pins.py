@@ -699,6 +699,27 @@ def test_attention_backward_against_autograd_and_sharding(t):
         assert oracle.rank_kv_heads(0, 4, 2, 4) == oracle.rank_kv_heads(1, 4, 2, 4) == [0]
 
 
+@pytest.mark.parametrize("causal", [True, False])
+def test_attention_core_backward_and_lse_against_autograd(causal):
+    """The core's gradients (dq, dk, dv) equal autograd's through
+    scaled_dot_product_attention, masked and unmasked; the log-sum-exp equals
+    torch.logsumexp of the masked scaled scores."""
+    r = _rng(47)
+    n, d = 9, 8
+    q, k, v, do = (r.standard_normal((n, d)) for _ in range(4))
+    T = lambda a: torch.from_numpy(a).requires_grad_(True)  # noqa: E731
+    tq, tk, tv = T(q), T(k), T(v)
+    F.scaled_dot_product_attention(tq[None, None], tk[None, None], tv[None, None],
+                                   is_causal=causal)[0, 0].backward(torch.from_numpy(do))
+    got = oracle.causal_attention_backward(q, k, v, do, causal)
+    for a, g in zip(got, (tq.grad, tk.grad, tv.grad)):
+        assert np.max(np.abs(a - g.numpy())) < 1e-13
+    s = torch.from_numpy(q @ k.T / math.sqrt(d))
+    if causal:
+        s = s.masked_fill(torch.ones(n, n, dtype=torch.bool).triu(1), float("-inf"))
+    assert np.max(np.abs(oracle.attention_lse(q, k, causal) - torch.logsumexp(s, 1).numpy())) < 1e-13
+
+
 def test_attention_backward_single_token_and_uniform_keys():
     """Closed forms: with one token the softmax is 1, so dV = dO and dq = dk = 0;
     with zero queries the probabilities are uniform over the causal prefix,
