@@ -295,7 +295,85 @@ def per_config_report(dev):
           "backward_only_tflops": rate(bwd_fl, bms),
           "shape": f"m={m}, h={h}, f_shard={f} (t=8), weight gradients float32"})
     del mlp, dw, dz
+
+    # backward of one rank's attention at the 70B block's shape (t = 8: 8 query
+    # heads, 1 KV head of 128, h = 8192, 4 sequences of 2048, causal); a
+    # one-rank layer of that shape stands for the rank
+    case, dw, dz, at = attn_backward_case(inputs, shard, dev)
+    log("configs: llama70b_attn_backward_t8")
+    fl = attn_backward_flops(case)
+    bms, bmn = _time(lambda: at.backward_rank(0, dz), reps=10, warm=3)
+    rk = at.ranks[0]
+    core_in = attn_core_buffers(tp, at, case, dev, dz)
+    cms, cmn = _time(lambda: core_in["run"](), reps=10, warm=3)
+    emit({"workload": "llama70b_attn_backward_t8",
+          "call": "tp_shard_attn_backward (one rank: forward recomputed, dO, core backward, dX, dW_qkv, dW_o)",
+          "ms": round(bms, 4), "min_ms": round(bmn, 4), "tflops": rate(fl["total"], bms),
+          "pct_mfma_peak": round(100.0 * fl["total"] / bms / 1e9 / MFMA_BF16_PEAK_TFLOPS, 2),
+          "backward_only_tflops": rate(fl["backward"], bms),
+          "core_call": "tp_flash_attn_backward (D, transposes, dQ, dK/dV, sum)", "core_ms": round(cms, 4),
+          "core_min_ms": round(cmn, 4), "core_tflops": rate(fl["core_backward"], cms),
+          "core_pct_mfma_peak": round(100.0 * fl["core_backward"] / cms / 1e9 / MFMA_BF16_PEAK_TFLOPS, 2),
+          "shape": f"batch={case.batch}, seq={case.seq}, h={case.hidden}, hq={rk.hq}, hkv={rk.hkv}, d=128, "
+                   "causal, weight gradients float32"})
+    del at, dw, dz, core_in
     del scratch
+
+
+def attn_backward_case(inputs, shard, dev):
+    """One rank of the 70B attention at t = 8 (8 query heads, 1 KV head,
+    h = 8192, 4 x 2048 tokens) with a seeded output gradient."""
+    case = inputs.AttnCase("llama70b_attn_rank_t8", 4, 2048, 8192, 8, 1, 128, 1, 500000.0, seed=84)
+    dw = {k: v.torch().to(dev) for k, v in inputs.gen_attn(case).items()}
+    dz = inputs.normal(84, 9, (case.tokens, case.hidden), 1.0, "bf16").torch().to(dev)
+    return case, dw, dz, shard.AttnShards(dw["X"], dw, case)
+
+
+def attn_backward_flops(case) -> dict:
+    """Algorithmic flops of one rank's attention backward: the recomputed
+    forward (QKV GEMM, attention core), the dO GEMM, the core backward
+    (dP, dV, dQ, dK over the causal pairs, plus the recomputed scores: 5
+    products of 2 d flops per pair) and the dX, dW_qkv, dW_o GEMMs."""
+    m, h, d = case.tokens, case.hidden, case.head_dim
+    hq, hkv = case.heads // case.t, max(1, case.kv_heads // case.t)
+    n = (hq + 2 * hkv) * d
+    pairs = case.seq * (case.seq + 1) / 2 * case.batch * hq
+    fwd = 2.0 * m * h * n + 4.0 * d * pairs
+    core = 10.0 * d * pairs
+    bwd = 2.0 * m * h * hq * d + core + 2.0 * m * n * h + 2.0 * m * h * n + 2.0 * m * h * hq * d
+    return {"total": fwd + bwd, "backward": bwd, "core_backward": core}
+
+
+def attn_core_buffers(tp, at, case, dev, dz):
+    """The core backward alone on the rank's recomputed forward (run the
+    sublayer backward once first so Q, K, V^T, O, LSE and dO are in its
+    workspace)."""
+    import torch
+
+    rk = at.ranks[0]
+    b, s, d = case.batch, case.seq, case.head_dim
+    m = b * s
+    n = (rk.hq + 2 * rk.hkv) * d
+    sp = (s + 63) // 64 * 64
+    core_bytes = tp.tp_flash_attn_backward_workspace_bytes(b, s, rk.hq, rk.hkv, d)
+    q = torch.empty(m, rk.hq * d, dtype=torch.bfloat16, device=dev)
+    k = torch.empty(m, rk.hkv * d, dtype=torch.bfloat16, device=dev)
+    vt = torch.zeros(b, rk.hkv, d, sp, dtype=torch.bfloat16, device=dev)
+    o = torch.empty(m, rk.hq * d, dtype=torch.bfloat16, device=dev)
+    lse = torch.empty(b, rk.hq, sp, dtype=torch.float32, device=dev)
+    do = torch.empty(m, rk.hq * d, dtype=torch.bfloat16, device=dev)
+    tp.tp_qkv_rope(b, s, case.hidden, rk.hq, rk.hkv, d, case.rope_base, at.x, rk.w_qkv, q, k, vt)
+    tp.tp_flash_attn_lse(b, s, rk.hq, rk.hkv, d, True, q, k, vt, o, lse)
+    wo_t = torch.empty(rk.hq * d, case.hidden, dtype=torch.bfloat16, device=dev)
+    tp.tp_transpose(case.hidden, rk.hq * d, rk.w_o, wo_t)
+    tp.tp_colwise("none", "bf16", m, case.hidden, rk.hq * d, dz, wo_t, do)
+    ws = torch.empty(core_bytes, dtype=torch.uint8, device=dev)
+    dqkv = torch.empty(m, n, dtype=torch.bfloat16, device=dev)
+
+    def run():
+        tp.tp_flash_attn_backward(b, s, rk.hq, rk.hkv, d, case.rope_base, True, q, k, vt, o, lse, do, ws,
+                                  core_bytes, dqkv, n)
+    return {"run": run, "keep": (q, k, vt, o, lse, do, ws, dqkv, wo_t)}
 
 
 def main():
@@ -311,7 +389,8 @@ def main():
     ap.add_argument("--pmc-pass", action="store_true",
                     help="launch only a 256 MiB copy and the SwiGLU GEMM (for counter runs)")
     ap.add_argument("--bwd-pass", action="store_true",
-                    help="run one rank's SwiGLU MLP backward at the 70B t=8 shape four times (for a kernel trace)")
+                    help="run one rank's SwiGLU MLP backward and attention backward at the 70B t=8 shape four "
+                         "times each (for a kernel trace)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -343,7 +422,13 @@ def main():
         for _ in range(4):
             mlp.backward_rank(0, dz)
         torch.cuda.synchronize()
-        log("backward pass done")
+        log("MLP backward pass done")
+        del mlp, dw, dz
+        _, dw, dz, at = attn_backward_case(inputs, shard, dev)
+        for _ in range(4):
+            at.backward_rank(0, dz)
+        torch.cuda.synchronize()
+        log("attention backward pass done")
         return
 
     case = inputs.CONFIGS[args.config]
