@@ -765,3 +765,46 @@ def attn_backward_partials(x, w: dict, dz, case, t: int | None = None) -> list[d
     return [attn_backward(x, w["Wq"], w["Wk"], w["Wv"], w["Wo"], dz, case.heads, case.kv_heads,
                           case.head_dim, case.batch, case.seq, case.rope_base,
                           rank_query_heads(r, case.heads, t)) for r in range(t)]
+
+
+# --------------------------------------------------------------------------
+# backward of the block ("f and g": a block's backward has the two sums of
+# the sublayers' dX partials; norms and residuals are replicated, so their
+# gradients are taken on every rank after the sum)
+# --------------------------------------------------------------------------
+
+
+def rmsnorm_backward(x, gain, dy, eps: float = 1e-5) -> tuple[np.ndarray, np.ndarray]:
+    """Gradients (dx, dgain) of y = x r gain, r = 1 / sqrt(mean(x^2) + eps), per
+    row, for dy.  With g = gain * dy and x_hat = x r, differentiating r gives
+    dx = r (g - x_hat mean(g x_hat)); dgain sums dy x_hat over the rows."""
+    x = np.asarray(x, dtype=np.float64)
+    dy = np.asarray(dy, dtype=np.float64)
+    gn = np.ones(x.shape[-1]) if gain is None else np.asarray(gain, dtype=np.float64)
+    r = 1.0 / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)
+    xh = x * r
+    g = dy * gn
+    dx = r * (g - xh * np.mean(g * xh, axis=-1, keepdims=True))
+    return dx, np.sum(dy * xh, axis=0)
+
+
+def block_backward(x, w: dict, case, dz, t: int | None = None) -> dict:
+    """Gradients of the pre-norm block of ``block`` for the output gradient dZ,
+    rank by rank: the MLP ranks' dX partials are summed (f's backward) into the
+    gradient of the MLP's normed input, taken through the norm and added to dZ
+    (the residual) to give dh1; the attention ranks' dX partials for dh1 are
+    summed and taken through the first norm, plus dh1, to give dX.  Returns
+    dx, dh1, the gains' gradients and every rank's weight gradients."""
+    t = case.t if t is None else t
+    xn = rmsnorm(x, w.get("g_attn"), case.eps)
+    h1 = x + shard_sum([attn_partial(xn, w, case, r, t) for r in range(t)])
+    hn = rmsnorm(h1, w.get("g_mlp"), case.eps)
+    mlp = mlp_swiglu_backward_partials(hn, w["W1"], w["W3"], w["W2"], dz, t)
+    d_hn = shard_sum([p["dx"] for p in mlp])
+    d1, dg_mlp = rmsnorm_backward(h1, w.get("g_mlp"), d_hn, case.eps)
+    dh1 = dz + d1
+    attn = attn_backward_partials(xn, w, dh1, case, t)
+    d_xn = shard_sum([p["dx"] for p in attn])
+    d0, dg_attn = rmsnorm_backward(x, w.get("g_attn"), d_xn, case.eps)
+    return {"dx": dh1 + d0, "dh1": dh1, "dg_attn": dg_attn, "dg_mlp": dg_mlp, "mlp": mlp, "attn": attn}
+

@@ -736,6 +736,62 @@ def test_attention_backward_single_token_and_uniform_keys():
     assert np.max(np.abs(dv - want)) < 1e-14
 
 
+def test_rmsnorm_backward_against_autograd():
+    """rmsnorm_backward equals autograd through PyTorch's own rms_norm (float64),
+    with and without a gain; a gradient along y itself is mapped to a multiple
+    of x only through the gain."""
+    r = _rng(48)
+    x, dy, g = r.standard_normal((5, 12)), r.standard_normal((5, 12)), 1.0 + 0.3 * r.standard_normal(12)
+    for gain in (None, g):
+        tx = torch.from_numpy(x).requires_grad_(True)
+        tg = None if gain is None else torch.from_numpy(gain).requires_grad_(True)
+        F.rms_norm(tx, (12,), tg, eps=1e-5).backward(torch.from_numpy(dy))
+        dx, dgn = oracle.rmsnorm_backward(x, gain, dy, 1e-5)
+        assert np.max(np.abs(dx - tx.grad.numpy())) < 1e-13
+        if gain is not None:
+            assert np.max(np.abs(dgn - tg.grad.numpy())) < 1e-13
+    # the norm is scale invariant, so dx is orthogonal to x when eps = 0
+    dx, _ = oracle.rmsnorm_backward(x, g, dy, 0.0)
+    assert np.max(np.abs(np.sum(dx * x, axis=1))) < 1e-12
+
+
+@pytest.mark.parametrize("t", [1, 2])
+def test_block_backward_against_autograd(t):
+    """block_backward equals autograd (float64) through the whole pre-norm block
+    written with torch ops (rms_norm, complex-rotation RoPE, GQA SDPA, SwiGLU)
+    for dX and both gains; the ranks' weight gradients are the shards of the
+    full ones."""
+    case = inputs.BlockCase("bwd", batch=2, seq=5, hidden=16, heads=4, kv_heads=2, head_dim=8, inter=24, t=t,
+                            rope_base=100.0, seed=49, dtype="f32", w_std=0.3, gain_std=0.2)
+    w = {k: v.f64() for k, v in inputs.gen_block(case).items()}
+    x = w["X"]
+    b, s, hd, d, hid = case.batch, case.seq, case.heads, case.head_dim, case.hidden
+    dz = _rng(50).standard_normal((b * s, hid))
+    T = lambda v: torch.from_numpy(v).requires_grad_(True)  # noqa: E731
+    tw = {k: T(v) for k, v in w.items()}
+
+    def heads_of(y, n):
+        return y.reshape(b, s, n, d).transpose(1, 2)
+
+    xn = F.rms_norm(tw["X"], (hid,), tw["g_attn"], eps=case.eps)
+    q = _torch_rope(heads_of(xn @ tw["Wq"], hd), case.rope_base)
+    k = _torch_rope(heads_of(xn @ tw["Wk"], case.kv_heads), case.rope_base)
+    v = heads_of(xn @ tw["Wv"], case.kv_heads)
+    o = F.scaled_dot_product_attention(q, k, v, is_causal=True, enable_gqa=True)
+    h1 = tw["X"] + o.transpose(1, 2).reshape(b * s, hd * d) @ tw["Wo"]
+    hn = F.rms_norm(h1, (hid,), tw["g_mlp"], eps=case.eps)
+    z = h1 + (F.silu(hn @ tw["W1"]) * (hn @ tw["W3"])) @ tw["W2"]
+    z.backward(torch.from_numpy(dz))
+    got = oracle.block_backward(x, w, case, dz, t)
+    scale = lambda g: max(1.0, float(np.max(np.abs(g))))  # noqa: E731
+    for key, g in (("dx", tw["X"].grad), ("dg_attn", tw["g_attn"].grad), ("dg_mlp", tw["g_mlp"].grad)):
+        assert np.max(np.abs(got[key] - g.numpy())) < 1e-11 * scale(g.numpy()), key
+    w1 = np.concatenate([p["dw1"] for p in got["mlp"]], axis=1)
+    assert np.max(np.abs(w1 - tw["W1"].grad.numpy())) < 1e-11 * scale(w1)
+    wq = np.concatenate([p["dwq"] for p in got["attn"]], axis=1)
+    assert np.max(np.abs(wq - tw["Wq"].grad.numpy())) < 1e-11 * scale(wq)
+
+
 # ---------------------------------------------------------------- inputs
 
 
