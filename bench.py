@@ -58,6 +58,17 @@ def block_flops(case, t: int) -> dict:
     }
 
 
+def block_backward_flops(case, t: int) -> float:
+    """Algorithmic flops of one rank's share of the block's backward: the MLP's
+    recomputed gate/up GEMM and its four backward GEMMs (16 m h f_t), the
+    attention's recomputed forward (Q/K/V GEMM, core), dO, the core backward
+    (2.5 times the core forward), dX, dW_qkv and dW_o."""
+    f = block_flops(case, t)
+    mlp = 16.0 * case.tokens * case.hidden * (case.inter // t)
+    attn = 3.0 * f["qkv"] + 2.0 * f["o_proj"] + 3.5 * f["attn_core"]
+    return mlp + attn
+
+
 TRAFFIC_FILE = REPO / "profiles" / "swiglu_gemm_traffic.json"
 GEMM_SOURCE = REPO / "megatron_tensor_transformer_colwise_amd" / "csrc" / "gemm.hip"
 
@@ -233,8 +244,22 @@ def per_config_report(dev):
                     "block_step_tflops": rate(case.t * (afl + mfl), step),
                     "sequence_parallel_step_ms": round(sp_step, 3),
                     "sequence_parallel_step_tflops": rate(case.t * (afl + mfl), sp_step)})
+        # the block's backward (after its forward), all ranks and both norm backwards
+        dz = inputs.normal(93, 20, (case.tokens, case.hidden), 1.0, "bf16").torch().to(dev)
+        blk.forward()
+        blk.backward(dz)
+        bstep, bmin = _time(lambda: blk.backward(dz), reps=3, warm=1)
+        m, h = case.tokens, case.hidden
+        nms, nmn = _time(lambda: tp.tp_shard_sum_rmsnorm_backward(
+            case.t, m, h, list(blk.mlp.dx_partials), blk.attn.out, "f32", blk.g_mlp, case.eps, dz, "bf16", blk.dh1,
+            blk.dh1_bf16, blk.dg_mlp, blk.norm_ws, blk.norm_ws_bytes))
+        nbytes = (case.t * 4 + 4 + 2 + 4 + 2) * m * h
+        bfl = case.t * block_backward_flops(case, case.t)
+        rec.update({"block_backward_step_ms": round(bstep, 3), "block_backward_step_min_ms": round(bmin, 3),
+                    "block_backward_step_tflops": rate(bfl, bstep),
+                    "norm_backward_ms": round(nms, 4), "norm_backward_gbs": round(nbytes / nms / 1e6, 1)})
         emit(rec)
-        del blk, dw
+        del blk, dw, dz
 
     # packed single-stream block (the guide's [1, 1, 1, 3, 3] example, mlp
     # ratio 3): h = 3072, 24 heads of 128, 4608 tokens, no mask, t = 4

@@ -390,6 +390,30 @@ tp_status tp_mlp_act_backward(tp_act act, int64_t m, int64_t n, const void* pre,
  *   ws         at least tp_shard_attn_backward_workspace_bytes bytes
  * Biases are not differentiated here.
  * ------------------------------------------------------------------------ */
+/* --------------------------------------------------------------------------
+ * Backward of the fused shard-sum + RMSNorm (tp_shard_sum_rmsnorm): f's
+ * backward sums the ranks' dX partials of the sublayer the norm feeds
+ * ("Tensor parallelism" page, "f and g"), then the replicated norm's gradient
+ * is taken, per row, and the gradient arriving through the residual added:
+ *   dy = ((partials[0] + partials[1]) + ...)        (ascending rank order)
+ *   r  = 1 / sqrt(mean(x^2) + eps),  g = gain * dy
+ *   dx = r g - x r^3 sum(g x) / h  (+ residual_grad)
+ *   dgain = sum over the m rows of dy x r          (ascending-order partials)
+ *   partials      t (1..16) float32 [m, h] device pointers (host array)
+ *   x             [m, h] the norm's input (x_dt float32 or bf16)
+ *   gain          [h] float32 or NULL (gain 1)
+ *   residual_grad [m, h] (residual_dt) or NULL; dx may overwrite it if float32
+ *   dx            [m, h] float32 or NULL;  dx_bf16 [m, h] bf16 or NULL (not both)
+ *   dgain         [h] float32 or NULL; then ws needs
+ *                 tp_shard_sum_rmsnorm_backward_workspace_bytes(m, h) bytes
+ * h must be a multiple of 8 and at most 8192.
+ * ------------------------------------------------------------------------ */
+size_t tp_shard_sum_rmsnorm_backward_workspace_bytes(int64_t m, int64_t h);
+tp_status tp_shard_sum_rmsnorm_backward(int32_t t, int64_t m, int64_t h, const float* const* partials, const void* x,
+                                        tp_dtype x_dt, const float* gain, float eps, const void* residual_grad,
+                                        tp_dtype residual_dt, float* dx, void* dx_bf16, float* dgain, void* ws,
+                                        size_t ws_bytes, void* stream);
+
 tp_status tp_flash_attn_lse(int64_t batch, int64_t seq, int32_t hq, int32_t hkv, int32_t head_dim,
                             int32_t causal, const void* q, const void* k, const void* vt, void* o, float* lse,
                             void* stream);

@@ -535,6 +535,56 @@ tp_status tp_shard_attn_backward(int64_t batch, int64_t seq, int64_t h, int32_t 
   return ok();
 }
 
+size_t tp_shard_sum_rmsnorm_backward_workspace_bytes(int64_t m, int64_t h) {
+  if (m <= 0 || h <= 0) return 0;
+  return align256((size_t)tpk::norm_bwd_blocks(m) * (size_t)h * 4);
+}
+
+tp_status tp_shard_sum_rmsnorm_backward(int32_t t, int64_t m, int64_t h, const float* const* partials, const void* x,
+                                        tp_dtype x_dt, const float* gain, float eps, const void* residual_grad,
+                                        tp_dtype residual_dt, float* dx, void* dx_bf16, float* dgain, void* ws,
+                                        size_t ws_bytes, void* stream) {
+  if (t < 1 || t > TP_MAX_SHARDS) return fail(TP_ERR_SHAPE, "t = %d outside 1..%d", t, TP_MAX_SHARDS);
+  if (m < 0) return fail(TP_ERR_SHAPE, "m = %lld is negative", (long long)m);
+  TRY(check_dim8(h, "h"));
+  if (h > 8192) return fail(TP_ERR_SHAPE, "h = %lld: the norm backward keeps rows of at most 8192 in registers",
+                            (long long)h);
+  if (x_dt != TP_F32 && x_dt != TP_BF16) return fail(TP_ERR_INVALID_ARG, "unknown x dtype %d", (int)x_dt);
+  if (residual_grad && residual_dt != TP_F32 && residual_dt != TP_BF16)
+    return fail(TP_ERR_INVALID_ARG, "unknown residual dtype %d", (int)residual_dt);
+  if (!(eps >= 0.0f) || eps > 1.0f) return fail(TP_ERR_INVALID_ARG, "eps must be in [0, 1]");
+  if (m == 0) return ok();
+  if (!partials) return fail(TP_ERR_INVALID_ARG, "partials is NULL");
+  for (int i = 0; i < t; ++i) {
+    char name[32];
+    snprintf(name, sizeof name, "partials[%d]", i);
+    TRY(check_ptr(partials[i], name));
+    if (partials[i] == dx) return fail(TP_ERR_INVALID_ARG, "dx aliases %s", name);
+  }
+  TRY(check_ptr(x, "x"));
+  if (!dx && !dx_bf16) return fail(TP_ERR_INVALID_ARG, "dx and dx_bf16 are both NULL");
+  if (dx) TRY(check_ptr(dx, "dx"));
+  if (dx_bf16) TRY(check_ptr(dx_bf16, "dx_bf16"));
+  if (x == dx || x == dx_bf16) return fail(TP_ERR_INVALID_ARG, "an output aliases x");
+  if (residual_grad) {
+    TRY(check_ptr(residual_grad, "residual_grad"));
+    if (residual_grad == dx_bf16 || (residual_grad == dx && residual_dt != TP_F32))
+      return fail(TP_ERR_INVALID_ARG, "only a float32 residual_grad may be overwritten by dx");
+  }
+  if (gain) TRY(check_ptr(gain, "gain"));
+  if (dgain) {
+    TRY(check_ptr(dgain, "dgain"));
+    TRY(check_ptr(ws, "ws"));
+    const size_t need = tp_shard_sum_rmsnorm_backward_workspace_bytes(m, h);
+    if (ws_bytes < need) return fail(TP_ERR_WORKSPACE, "workspace of %zu bytes < %zu needed", ws_bytes, need);
+  }
+  TRY(device_check());
+  return launched(tpk::launch_sum_rmsnorm_bwd(t, m, h, partials, x, x_dt == TP_BF16, gain, eps, residual_grad,
+                                              residual_dt == TP_BF16, dx, dx_bf16, dgain, static_cast<float*>(ws),
+                                              as_stream(stream)),
+                  "tp_shard_sum_rmsnorm_backward");
+}
+
 size_t tp_shard_attn_workspace_bytes(int64_t batch, int64_t seq, int32_t hq, int32_t hkv,
                                      int32_t head_dim) {
   if (batch < 0 || seq < 0 || hq <= 0 || hkv <= 0 || head_dim <= 0) return 0;

@@ -280,6 +280,41 @@ class BlockShards:
         tp.tp_shard_sum_rmsnorm(self.t, self.m, self.h, list(self.attn.partials), self.x, "bf16",
                                 self.attn.out, self.g_mlp, self.case.eps, self.hn, stream)
 
+    # ---- backward ("f and g": each sublayer's dX partials are summed, then the
+    # replicated norm's gradient is taken and the residual's gradient added)
+
+    def _bwd_buffers(self):
+        if getattr(self, "d_x", None) is None:
+            dev, m, h = self.x.device, self.m, self.h
+            self.dh1 = torch.empty(m, h, dtype=torch.float32, device=dev)
+            self.dh1_bf16 = torch.empty(m, h, dtype=torch.bfloat16, device=dev)
+            self.d_x = torch.empty(m, h, dtype=torch.float32, device=dev)
+            self.dg_attn = torch.empty(h, dtype=torch.float32, device=dev)
+            self.dg_mlp = torch.empty(h, dtype=torch.float32, device=dev)
+            self.norm_ws_bytes = tp.tp_shard_sum_rmsnorm_backward_workspace_bytes(m, h)
+            self.norm_ws = torch.empty(max(self.norm_ws_bytes, 256), dtype=torch.uint8, device=dev)
+
+    def backward(self, dz, stream=None):
+        """Gradients of the block for the bf16 output gradient dZ, after
+        ``forward`` (its normed inputs and h1 are the saved activations):
+        every MLP rank's backward, their dX partials summed through the MLP
+        norm's backward plus dZ (dh1); every attention rank's backward for
+        dh1, their partials summed through the first norm's backward plus dh1
+        (dX).  Weight gradients stay in the sublayers' per-rank buffers."""
+        self._bwd_buffers()
+        m, h, eps = self.m, self.h, self.case.eps
+        for r in range(self.t):
+            self.mlp.backward_rank(r, dz, stream)
+        tp.tp_shard_sum_rmsnorm_backward(self.t, m, h, list(self.mlp.dx_partials), self.attn.out, "f32", self.g_mlp,
+                                         eps, dz, "bf16", self.dh1, self.dh1_bf16, self.dg_mlp, self.norm_ws,
+                                         self.norm_ws_bytes, stream)
+        for r in range(self.t):
+            self.attn.backward_rank(r, self.dh1_bf16, stream=stream)
+        tp.tp_shard_sum_rmsnorm_backward(self.t, m, h, list(self.attn.dx_partials), self.x, "bf16", self.g_attn,
+                                         eps, self.dh1, "f32", self.d_x, None, self.dg_attn, self.norm_ws,
+                                         self.norm_ws_bytes, stream)
+        return self.d_x
+
     def forward(self, stream=None, fused=True):
         self.norm_attn(stream)
         if fused:

@@ -64,6 +64,9 @@ _SIGS = {
                               _vp, _vp, _vp],
     "tp_transpose": [_i64, _i64, _vp, _vp, _vp],
     "tp_mlp_act_backward": [_i32, _i64, _i64, _vp, _vp, _vp, _vp, _vp],
+    "tp_shard_sum_rmsnorm_backward_workspace_bytes": [_i64, _i64],
+    "tp_shard_sum_rmsnorm_backward": [_i32, _i64, _i64, ctypes.POINTER(_vp), _vp, _i32, _vp, _f32, _vp, _i32, _vp,
+                                      _vp, _vp, _vp, ctypes.c_size_t, _vp],
     "tp_flash_attn_lse": [_i64, _i64, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp],
     "tp_flash_attn_backward_workspace_bytes": [_i64, _i64, _i32, _i32, _i32],
     "tp_flash_attn_backward": [_i64, _i64, _i32, _i32, _i32, _f32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
@@ -94,6 +97,7 @@ def lib() -> ctypes.CDLL:
         L.tp_shard_attn_workspace_bytes.restype = ctypes.c_size_t
         L.tp_shard_mlp_backward_workspace_bytes.restype = ctypes.c_size_t
         L.tp_flash_attn_backward_workspace_bytes.restype = ctypes.c_size_t
+        L.tp_shard_sum_rmsnorm_backward_workspace_bytes.restype = ctypes.c_size_t
         L.tp_shard_attn_backward_workspace_bytes.restype = ctypes.c_size_t
         _lib = L
     return _lib
@@ -212,6 +216,18 @@ def tp_shard_sum_rmsnorm(t, m, h, partials, residual, residual_dt, out, gain, ep
     arr = (_vp * max(len(partials), 1))(*[_p(p) for p in partials])
     _check(lib().tp_shard_sum_rmsnorm(t, nrun, run_rows, run_stride, h, arr, _p(bias), _p(residual),
                                       _e(residual_dt, DTYPES), _p(out), _p(gain), eps, _p(y), _s(stream)))
+
+
+def tp_shard_sum_rmsnorm_backward_workspace_bytes(m, h) -> int:
+    return int(lib().tp_shard_sum_rmsnorm_backward_workspace_bytes(m, h))
+
+
+def tp_shard_sum_rmsnorm_backward(t, m, h, partials, x, x_dt, gain, eps, residual_grad, residual_dt, dx, dx_bf16,
+                                  dgain, ws, ws_bytes, stream=None) -> None:
+    arr = (_vp * max(len(partials), 1))(*[_p(p) for p in partials])
+    _check(lib().tp_shard_sum_rmsnorm_backward(t, m, h, arr, _p(x), _e(x_dt, DTYPES), _p(gain), eps,
+                                               _p(residual_grad), _e(residual_dt, DTYPES), _p(dx), _p(dx_bf16),
+                                               _p(dgain), _p(ws), ws_bytes, _s(stream)))
 
 
 def tp_embedding(m, w, v_start, v_rows, ids, table, out, ld, stream=None) -> None:

@@ -321,3 +321,25 @@ def test_attention_backward_validation(L):
     assert shard_bwd(x=MIS) == tp.TP_ERR_INVALID_ARG
     assert status("tp_flash_attn_backward", 0, 64, 4, 2, 128, 0.0, 1, None, None, None, None, None, None, None, 0,
                   None, 1024, None) == tp.TP_OK
+
+
+def test_norm_backward_validation(L):
+    ws = tp.tp_shard_sum_rmsnorm_backward_workspace_bytes(16, 64)
+    assert ws >= 16 * 64 * 4 or ws >= 64 * 4
+    arr = (ctypes.c_void_p * 2)(A16, A16 + 4096)
+    f = lambda t=2, m=16, h=64, x=A16 + 8192, xdt=1, eps=1e-5, res=None, rdt=0, dx=A16 + 12288, dxb=None, \
+        dg=None, w=None, wsb=0: status(  # noqa: E731
+        "tp_shard_sum_rmsnorm_backward", t, m, h, arr, x, xdt, None, eps, res, rdt, dx, dxb, dg, w, wsb, None)
+    assert f(t=0) == tp.TP_ERR_SHAPE
+    assert f(t=17) == tp.TP_ERR_SHAPE
+    assert f(h=60) == tp.TP_ERR_SHAPE
+    assert f(h=8200) == tp.TP_ERR_SHAPE                       # wider than the register-held row
+    assert f(xdt=7) == tp.TP_ERR_INVALID_ARG
+    assert f(eps=-1.0) == tp.TP_ERR_INVALID_ARG
+    assert f(dx=None) == tp.TP_ERR_INVALID_ARG                 # no output
+    assert f(dx=A16) == tp.TP_ERR_INVALID_ARG                  # aliases a partial
+    assert f(x=A16 + 12288) == tp.TP_ERR_INVALID_ARG           # output aliases x
+    assert f(res=A16 + 12288, rdt=1) == tp.TP_ERR_INVALID_ARG  # bf16 residual overwritten
+    assert f(dg=A16 + 16384, w=A16 + 20480, wsb=ws - 1) == tp.TP_ERR_WORKSPACE
+    assert f(x=MIS) == tp.TP_ERR_INVALID_ARG
+    assert f(m=0, x=None, dx=None) == tp.TP_OK

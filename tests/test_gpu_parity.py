@@ -583,6 +583,74 @@ def test_flash_attn_backward_full_size_sampled(device):
     assert rel_err(got[sample, (hq + 1) * d:(hq + 2) * d], dv_sum[sample]) <= BF16_TOL
 
 
+@pytest.mark.parametrize("t,m,h,xdt,res,gain", [(1, 7, 64, "f32", None, False), (4, 1000, 1024, "bf16", "f32", True),
+                                               (8, 3001, 8192, "f32", "bf16", True), (16, 130, 264, "bf16", "f32", True),
+                                               (3, 2048, 4096, "f32", "inplace", True)])
+def test_shard_sum_rmsnorm_backward(device, t, m, h, xdt, res, gain):
+    """f's backward sum (ascending), the RMSNorm gradient and the residual
+    gradient, and dgain summed over row runs, against the oracle's
+    rmsnorm_backward on the same partials and x; float32 arithmetic, so within
+    1e-5 of the float64 result (relative to its largest value); in place over
+    a float32 residual gradient; ragged row runs and column groups."""
+    say(f"case norm backward t={t} m={m} h={h} x={xdt} res={res} gain={gain}")
+    parts = [inputs.normal(91, s, (m, h), 1.0, "f32").torch() for s in range(t)]
+    x = inputs.normal(91, 40, (m, h), 1.0, xdt).torch()
+    g = (1.0 + 0.2 * inputs.normal(91, 41, (h,), 1.0, "f32").torch()) if gain else None
+    rgrad = None
+    if res is not None:
+        rgrad = inputs.normal(91, 42, (m, h), 1.0, "bf16" if res == "bf16" else "f32").torch()
+    dparts = [p.to(device) for p in parts]
+    dres = None if rgrad is None else rgrad.to(device)
+    dx = dres if res == "inplace" else torch.full((m, h), float("nan"), dtype=torch.float32, device=device)
+    dxb = torch.empty(m, h, dtype=torch.bfloat16, device=device)
+    dgn = torch.full((h,), float("nan"), dtype=torch.float32, device=device)
+    wsb = tp.tp_shard_sum_rmsnorm_backward_workspace_bytes(m, h)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=device)
+    tp.tp_shard_sum_rmsnorm_backward(t, m, h, dparts, x.to(device), xdt, None if g is None else g.to(device), 1e-5,
+                                     dres, "bf16" if res == "bf16" else "f32", dx, dxb, dgn, ws, wsb)
+    torch.cuda.synchronize()
+    dy = sum(p.double().numpy() for p in parts)
+    ref_dx, ref_dg = oracle.rmsnorm_backward(x.double().numpy(), None if g is None else g.double().numpy(), dy, 1e-5)
+    if rgrad is not None:
+        ref_dx = ref_dx + rgrad.double().numpy()
+    assert rel_err(host(dx), ref_dx) <= 1e-5
+    assert rel_err(host(dgn), ref_dg) <= 1e-5
+    assert torch.equal(dxb, dx.to(torch.bfloat16))
+
+
+@pytest.mark.parametrize("t", [1, 2])
+def test_block_backward(device, t):
+    """The whole pre-norm block's backward (after its forward): dX, dh1, both
+    gains' gradients and every rank's weight gradients against the oracle's
+    block_backward from the same bf16 inputs."""
+    case = inputs.BlockCase("bwd", 2, 64, 256, 4, 2, 128, 512, t, 500000.0, seed=92, gain_std=0.1)
+    say(f"case block backward t={t}")
+    w = inputs.gen_block(case)
+    dz = inputs.normal(92, 20, (case.tokens, case.hidden), 1.0, "bf16")
+    dw = {k: to_dev(v, device) for k, v in w.items()}
+    blk = shard.BlockShards(dw["X"], dw, case)
+    blk.forward()
+    dx = blk.backward(to_dev(dz, device))
+    torch.cuda.synchronize()
+    W = {k: v.f64() for k, v in w.items()}
+    ref = oracle.block_backward(W["X"], W, case, dz.f64(), t)
+    for name, got, want in (("dh1", blk.dh1, ref["dh1"]), ("dx", dx, ref["dx"]), ("dg_mlp", blk.dg_mlp, ref["dg_mlp"]),
+                            ("dg_attn", blk.dg_attn, ref["dg_attn"])):
+        say(f"  {name}")
+        assert rel_err(host(got), want) <= BF16_TOL, name
+    fs = case.inter // t
+    for r in range(t):
+        say(f"  rank {r} weights")
+        p = ref["mlp"][r]
+        gw = host(blk.mlp.dw_in[r])
+        assert rel_err(gw[:fs], p["dw1"].T) <= BF16_TOL
+        assert rel_err(gw[fs:], p["dw3"].T) <= BF16_TOL
+        assert rel_err(host(blk.mlp.dw_out[r]), p["dw2"].T) <= BF16_TOL
+        a = ref["attn"][r]
+        assert rel_err(host(blk.attn.dw_qkv[r]), np.concatenate([a["dwq"].T, a["dwk"].T, a["dwv"].T])) <= BF16_TOL
+        assert rel_err(host(blk.attn.dw_o[r]), a["dwo"].T) <= BF16_TOL
+
+
 # ---------------------------------------------------------------- vocabulary parallel
 
 
