@@ -398,7 +398,7 @@ tp_status tp_mlp_act_backward(tp_act act, int64_t m, int64_t n, const void* pre,
  *   dy = ((partials[0] + partials[1]) + ...)        (ascending rank order)
  *   r  = 1 / sqrt(mean(x^2) + eps),  g = gain * dy
  *   dx = r g - x r^3 sum(g x) / h  (+ residual_grad)
- *   dgain = sum over the m rows of dy x r          (ascending-order partials)
+ *   dgain = sum over the m rows of dy x r          (partials summed in a fixed order)
  *   partials      t (1..16) float32 [m, h] device pointers (host array)
  *   x             [m, h] the norm's input (x_dt float32 or bf16)
  *   gain          [h] float32 or NULL (gain 1)

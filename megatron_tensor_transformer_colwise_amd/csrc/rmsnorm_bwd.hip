@@ -11,7 +11,7 @@
 // One workgroup walks a run of consecutive rows, keeping each row's dy and x
 // in registers between the row's reduction and its output (h <= 8192), and
 // accumulating its columns' dgain terms across the run; a second kernel sums
-// the runs' dgain partials in ascending order.  No atomics.
+// the runs' dgain partials in a fixed order.  No atomics.
 // HBM-bound: t + 1 (+1 residual) float32 reads and one or two writes per element.
 #include "common.h"
 #include "kernels.h"
@@ -58,22 +58,34 @@ __device__ __forceinline__ void load8f(const void* p, int64_t e, bool bf16, floa
 template <int T>
 __global__ __launch_bounds__(NT) void sum_rmsnorm_bwd_kernel(NormBwdArgs a) {
   __shared__ float red[2][2][NT / 64];  // [row parity][sum][wave]
+  __shared__ __attribute__((aligned(16))) float sgain[MAXC * NT * 8];  // the gain, read back per row
   const int64_t h = a.h, groups = h >> 3;
   const int64_t r0 = (int64_t)blockIdx.x * a.rows_per_block;
   const int64_t r1 = min(r0 + a.rows_per_block, a.m);
-  float gn[MAXC][8], dg[MAXC][8];
+  float dg[MAXC][8];
 #pragma unroll
   for (int i = 0; i < MAXC; ++i) {
     const int64_t gi = threadIdx.x + (int64_t)i * NT;
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      gn[i][k] = (a.gain && gi < groups) ? a.gain[gi * 8 + k] : 1.0f;
+      // each thread reads back only the columns it wrote: no barrier needed
+      sgain[gi * 8 + k] = (a.gain && gi < groups) ? a.gain[gi * 8 + k] : 1.0f;
       dg[i][k] = 0.0f;
     }
   }
+  auto gain8 = [&](int i, float (&g)[8]) {
+    const int64_t gi = threadIdx.x + (int64_t)i * NT;
+    const f32x4 lo = *reinterpret_cast<const f32x4*>(&sgain[gi * 8]);
+    const f32x4 hi = *reinterpret_cast<const f32x4*>(&sgain[gi * 8 + 4]);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      g[k] = lo[k];
+      g[4 + k] = hi[k];
+    }
+  };
   for (int64_t r = r0; r < r1; ++r) {
     const int64_t base = r * h;
-    float dy[MAXC][8], xv[MAXC][8];
+    float dy[MAXC][8], xv[MAXC][8], rv[MAXC][8];
     float sxx = 0.0f, sgx = 0.0f;
 #pragma unroll
     for (int i = 0; i < MAXC; ++i) {
@@ -87,6 +99,11 @@ __global__ __launch_bounds__(NT) void sum_rmsnorm_bwd_kernel(NormBwdArgs a) {
         hi[s] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(a.p[s] + e + 4));
       }
       load8f(a.x, e, a.x_bf16 != 0, xv[i]);
+      // the residual gradient is loaded with the row's other inputs: one
+      // memory round trip per row
+#pragma unroll
+      for (int k = 0; k < 8; ++k) rv[i][k] = 0.0f;
+      if (a.res) load8f(a.res, e, a.res_bf16 != 0, rv[i]);
       f32x4 sl = lo[0], sh = hi[0];
 #pragma unroll
       for (int s = 1; s < T; ++s) {
@@ -98,10 +115,12 @@ __global__ __launch_bounds__(NT) void sum_rmsnorm_bwd_kernel(NormBwdArgs a) {
         dy[i][k] = sl[k];
         dy[i][4 + k] = sh[k];
       }
+      float gn[8];
+      gain8(i, gn);
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
         sxx += xv[i][k] * xv[i][k];
-        sgx += gn[i][k] * dy[i][k] * xv[i][k];
+        sgx += gn[k] * dy[i][k] * xv[i][k];
       }
     }
     // both row sums across the workgroup: the wave's butterfly, then the 4 waves
@@ -125,12 +144,11 @@ __global__ __launch_bounds__(NT) void sum_rmsnorm_bwd_kernel(NormBwdArgs a) {
       const int64_t gi = threadIdx.x + (int64_t)i * NT;
       if (gi >= groups) continue;
       const int64_t e = base + gi * 8;
-      float rv[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-      if (a.res) load8f(a.res, e, a.res_bf16 != 0, rv);
-      float o[8];
+      float o[8], gn[8];
+      gain8(i, gn);
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        o[k] = (rr * (gn[i][k] * dy[i][k]) - xv[i][k] * coef) + rv[k];
+        o[k] = (rr * (gn[k] * dy[i][k]) - xv[i][k] * coef) + rv[i][k];
         dg[i][k] += dy[i][k] * (xv[i][k] * rr);
       }
       if (a.dx) {
@@ -153,19 +171,43 @@ __global__ __launch_bounds__(NT) void sum_rmsnorm_bwd_kernel(NormBwdArgs a) {
   }
 }
 
-// dgain[c] = sum over the blocks' partials, ascending.
+// dgain[c] = the blocks' partials summed in a fixed order: 16 interleaved
+// slices (slice s takes blocks s, s + 16, ... in ascending order, 8 loads in
+// flight), then the 16 slice sums in slice order.  16 columns per workgroup.
 __global__ __launch_bounds__(NT) void dgain_sum_kernel(const float* part, int64_t blocks, int64_t h, float* dgain) {
-  const int64_t c = (int64_t)blockIdx.x * NT + threadIdx.x;
-  if (c >= h) return;
+  __shared__ float red[16][17];
+  const int cl = threadIdx.x & 15, sl = threadIdx.x >> 4;
+  const int64_t c = (int64_t)blockIdx.x * 16 + cl;
   float s = 0.0f;
-  for (int64_t b = 0; b < blocks; ++b) s += part[b * h + c];
-  dgain[c] = s;
+  if (c < h) {
+    int64_t b = sl;
+    for (; b + 16 * 7 < blocks; b += 16 * 8) {
+      float v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = part[(b + 16 * i) * h + c];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) s += v[i];
+    }
+    for (; b < blocks; b += 16) s += part[b * h + c];
+  }
+  red[sl][cl] = s;
+  __syncthreads();
+  if (sl == 0 && c < h) {
+    float tot = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) tot += red[k][cl];
+    dgain[c] = tot;
+  }
 }
 
 }  // namespace
 
+// Rows per workgroup: runs of ceil(m / 1024) rows when dgain is wanted (at
+// most 1024 dgain partials), else one row per workgroup.
+int64_t norm_bwd_rows_per_block(int64_t m, bool dgain) { return dgain ? (m + 1023) / 1024 : 1; }
+
 int64_t norm_bwd_blocks(int64_t m) {
-  const int64_t rpb = (m + 1023) / 1024;
+  const int64_t rpb = norm_bwd_rows_per_block(m, true);
   return (m + rpb - 1) / rpb;
 }
 
@@ -184,11 +226,11 @@ hipError_t launch_sum_rmsnorm_bwd(int t, int64_t m, int64_t h, const float* cons
   a.dg_part = dgain ? ws : nullptr;
   a.m = m;
   a.h = h;
-  a.rows_per_block = (m + 1023) / 1024;
+  a.rows_per_block = norm_bwd_rows_per_block(m, dgain != nullptr);
   a.eps = eps;
   a.x_bf16 = x_bf16;
   a.res_bf16 = res_bf16;
-  const int64_t blocks = norm_bwd_blocks(m);
+  const int64_t blocks = (m + a.rows_per_block - 1) / a.rows_per_block;
   const dim3 grid((unsigned)blocks), block(NT);
   switch (t) {
 #define TP_NORM_BWD_CASE(T) \
@@ -201,7 +243,7 @@ hipError_t launch_sum_rmsnorm_bwd(int t, int64_t m, int64_t h, const float* cons
     default: return hipErrorInvalidValue;
   }
   if (dgain)
-    hipLaunchKernelGGL(dgain_sum_kernel, dim3((unsigned)((h + NT - 1) / NT)), dim3(NT), 0, s, ws, blocks, h, dgain);
+    hipLaunchKernelGGL(dgain_sum_kernel, dim3((unsigned)((h + 15) / 16)), dim3(NT), 0, s, ws, blocks, h, dgain);
   return hipGetLastError();
 }
 
