@@ -5,7 +5,8 @@
 * ``synth/_synth.so`` -- the seeded synthetic-input generator (plain C, OpenMP).
 
 Every HIP translation unit is compiled with packed-fp32 instructions disabled
-(``-Xclang -target-feature -Xclang -packed-fp32-ops``).
+(``-Xclang -target-feature -Xclang -packed-fp32-ops``); ``FILE_FLAGS`` adds
+per-file code-generation options.
 """
 from __future__ import annotations
 
@@ -38,6 +39,16 @@ HIP_FLAGS = [
 ]
 
 
+# Per-file additions.  The attention backward's kernels post-process every
+# score and score-gradient accumulator with vector ALU code; left to its
+# default, the register allocator places those accumulators in AGPRs and
+# moves each value to a VGPR and back (hundreds of moves per tile), so its
+# MFMAs are told to write VGPRs.
+FILE_FLAGS = {
+    "flash_attn_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
+
 def _run(cmd: list[str]) -> None:
     proc = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
     out = "\n".join(
@@ -68,7 +79,7 @@ def build_hip(jobs: int | None = None) -> Path:
     def compile_one(pair):
         src, obj = pair
         lang = ["-x", "hip"] if src.suffix == ".hip" else []
-        _run([HIPCC, *HIP_FLAGS, *lang, "-c", str(src), "-o", str(obj)])
+        _run([HIPCC, *HIP_FLAGS, *FILE_FLAGS.get(src.name, []), *lang, "-c", str(src), "-o", str(obj)])
 
     jobs = jobs or min(len(srcs), os.cpu_count() or 4, 16)
     with ThreadPoolExecutor(jobs) as ex:

@@ -45,8 +45,17 @@ constexpr int NT = 256;
 constexpr int ROW_TILE = 64 * D * 2;  // [64 tokens][128 d], 256-byte rows
 constexpr int COL_TILE = D * 64 * 2;  // [128 d][64 tokens], 128-byte rows
 constexpr int VEC_TILE = 1024;        // 64 float32 values (+ the zeros of idle lanes)
-constexpr int DQ_STAGE = 2 * ROW_TILE + COL_TILE;                  // K, V, K^T
-constexpr int KV_STAGE = 2 * ROW_TILE + 2 * COL_TILE + 2 * VEC_TILE;  // Q, dO, Q^T, dO^T, lse, D
+// LDS layouts, two stages each.  The row tiles of both stages sit in the first
+// 64 KiB and the column tiles from 64 KiB on, so that every fragment read is
+// a per-lane register (the column-tile offsets carry the 64 KiB) plus an
+// immediate below 64 KiB.
+//   dQ:    K(s) = 32 KiB s, V(s) = 32 KiB s + 16 KiB, K^T(s) = 64 KiB + 16 KiB s
+//   dK/dV: Q(s) = 32 KiB s, dO(s) = 32 KiB s + 16 KiB, Q^T(s) = 64 KiB + 32 KiB s,
+//          dO^T(s) = Q^T(s) + 16 KiB, lse(s) = 128 KiB + 2 KiB s, D(s) = lse(s) + 1 KiB
+constexpr int COLS = 65536;
+constexpr int DQ_LDS = COLS + 2 * COL_TILE;
+constexpr int KV_LDS = COLS + 4 * COL_TILE + 4 * VEC_TILE;
+static_assert(4 * ROW_TILE == COLS && 2 * ROW_TILE + 2 * COL_TILE == 65536, "layout");
 
 struct BwdArgs {
   const bf16_t* q;     // [batch*seq, hq*D], RoPE applied
@@ -95,10 +104,19 @@ __device__ __forceinline__ u32x4 c_to_b(const uint32_t (&pk)[2][8], int u) {
   return u32x4{s0[0], s1[0], s0[1], s1[1]};
 }
 
+// The same for one 32-token block's packed pairs: half hf (0 or 1) gives
+// tokens 16 hf + 0..7 (lanes 0-31) and 16 hf + 8..15 (lanes 32-63).
+__device__ __forceinline__ u32x4 c_to_b1(const uint32_t (&pk)[8], int hf) {
+  const int r0 = hf * 4;
+  auto s0 = __builtin_amdgcn_permlane32_swap(pk[r0 + 0], pk[r0 + 2], false, false);
+  auto s1 = __builtin_amdgcn_permlane32_swap(pk[r0 + 1], pk[r0 + 3], false, false);
+  return u32x4{s0[0], s1[0], s0[1], s1[1]};
+}
+
 // ---------------------------------------------------------------- dQ
 
 __global__ __launch_bounds__(NT, 1) void attn_bwd_dq_kernel(BwdArgs a) {
-  __shared__ __attribute__((aligned(1024))) char smem[2 * DQ_STAGE];
+  __shared__ __attribute__((aligned(1024))) char smem[DQ_LDS];
   const int lane = lane_id(), wave = wave_id();
   const int l31 = lane & 31, h = lane >> 5;
 
@@ -150,9 +168,10 @@ __global__ __launch_bounds__(NT, 1) void attn_bwd_dq_kernel(BwdArgs a) {
     t_off[i] = (uint32_t)((int64_t)d * sp * 2 + cv * 16);
   }
   auto load_tile = [&](auto stage_tag, int t) {
-    char* sk = smem + decltype(stage_tag)::value * DQ_STAGE;
+    constexpr int S = decltype(stage_tag)::value;
+    char* sk = smem + S * 2 * ROW_TILE;
     char* sv = sk + ROW_TILE;
-    char* st = sv + ROW_TILE;
+    char* st = smem + COLS + S * COL_TILE;
     const int kb = t * 64;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -166,16 +185,17 @@ __global__ __launch_bounds__(NT, 1) void attn_bwd_dq_kernel(BwdArgs a) {
 
   // LDS read offsets.  Row tiles: token 32 blk + l31 at d step s is
   // rr[s] + blk * 8192 (the swizzle depends on the token mod 16 only).
-  // Column tiles: d = 32 db + l31 at token step u is cr[db & 1][u] +
-  // (db >> 1) * 8192 (the swizzle repeats every 64 rows).
-  uint32_t rr[8], cr[2][4];
+  // Column tiles: d = 32 db + l31 at token step u is crb[db & 1][u] - COLS +
+  // (db >> 1) * 8192 (the swizzle repeats every 64 rows; crb carries the
+  // column tiles' base).
+  uint32_t rr[8], crb[2][4];
 #pragma unroll
   for (int s = 0; s < 8; ++s) rr[s] = (uint32_t)(l31 * 256 + (((2 * s + h) ^ swz_row(l31)) << 4));
 #pragma unroll
   for (int db = 0; db < 2; ++db) {
     const int d = db * 32 + l31;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) cr[db][u] = (uint32_t)(d * 128 + (((2 * u + h) ^ swz_col(d)) << 4));
+    for (int u = 0; u < 4; ++u) crb[db][u] = (uint32_t)(COLS + d * 128 + (((2 * u + h) ^ swz_col(d)) << 4));
   }
 
   f32x16 acc[4];
@@ -192,70 +212,57 @@ __global__ __launch_bounds__(NT, 1) void attn_bwd_dq_kernel(BwdArgs a) {
     wait_vmcnt0();
     __syncthreads();
     if (t + 1 < n_kv) load_tile(std::integral_constant<int, 1 - S>{}, t + 1);
-    const char* sk = smem + S * DQ_STAGE;
+    const char* sk = smem + S * 2 * ROW_TILE;
     const char* sv = sk + ROW_TILE;
-    const char* st = sv + ROW_TILE;
+    const char* st = smem + S * COL_TILE;  // + COLS, carried by crb
 
-    // S^T = K Q^T and dP^T = V dO^T for 64 keys (two 32-key blocks)
-    f32x16 sacc[2] = {f32x16{}, f32x16{}}, pacc[2] = {f32x16{}, f32x16{}};
-    {
-      u32x4 kf[2][8];
-#pragma unroll
-      for (int s = 0; s < 8; ++s)
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) kf[kb][s] = lds_read16(sk + rr[s] + kb * 8192);
-#pragma unroll
-      for (int s = 0; s < 8; ++s)
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) sacc[kb] = mfma32x32x16(kf[kb][s], qf[s], sacc[kb]);
-    }
-    {
-      u32x4 vf[2][8];
-#pragma unroll
-      for (int s = 0; s < 8; ++s)
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) vf[kb][s] = lds_read16(sv + rr[s] + kb * 8192);
-#pragma unroll
-      for (int s = 0; s < 8; ++s)
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) pacc[kb] = mfma32x32x16(vf[kb][s], df[s], pacc[kb]);
-    }
-    u32x4 tf[4][4];  // [key step u][d block]
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-#pragma unroll
-      for (int db = 0; db < 4; ++db) tf[u][db] = lds_read16(st + cr[db & 1][u] + (db >> 1) * 8192);
-
-    // dS^T = P^T (dP^T - D), zero where the key is masked or past the sequence
+    // per 32-key block: S^T = K Q^T and dP^T = V dO^T (two interleaved MFMA
+    // chains, fragments read as they are used), dS^T = P^T (dP^T - D) rounded
+    // to bf16 pairs (zero where the key is masked or past the sequence), then
+    // dQ^T += K^T dS^T over the block's two 16-key steps
     const int key0 = t * 64;
-    const bool need_mask = (a.causal && key0 + 63 > q0) || (key0 + 64 > seq);
+    const bool live = t < n_kv;  // the odd tail's second tile is computed fully masked
+    const bool need_mask = !live || (a.causal && key0 + 63 > q0) || (key0 + 64 > seq);
+    const int klim = live ? key_lim : -1;
     uint32_t dsk[2][8];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < 2; ++kb) {
+      f32x16 sacc = f32x16{}, pacc = f32x16{};
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const u32x4 kf = lds_read16(sk + rr[s] + kb * 8192);
+        const u32x4 vf = lds_read16(sv + rr[s] + kb * 8192);
+        sacc = mfma32x32x16(kf, qf[s], sacc);
+        pacc = mfma32x32x16(vf, df[s], pacc);
+      }
 #pragma unroll
       for (int r = 0; r < 16; r += 2) {
-        const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r], a.scale_log2, -lse));
-        const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r + 1], a.scale_log2, -lse));
-        float d0 = p0 * (pacc[kb][r] - dd), d1 = p1 * (pacc[kb][r + 1] - dd);
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[r], a.scale_log2, -lse));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[r + 1], a.scale_log2, -lse));
+        float d0 = p0 * (pacc[r] - dd), d1 = p1 * (pacc[r + 1] - dd);
         if (need_mask) {
           const int key = key0 + kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-          d0 = key > key_lim ? 0.0f : d0;
-          d1 = key + 1 > key_lim ? 0.0f : d1;
+          d0 = key > klim ? 0.0f : d0;
+          d1 = key + 1 > klim ? 0.0f : d1;
         }
         dsk[kb][r >> 1] = pack_bf16x2(d0, d1);
       }
-    // dQ^T += K^T dS^T over four 16-key steps
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const u32x4 bs = c_to_b(dsk, u);
+      for (int u = 2 * kb; u < 2 * kb + 2; ++u) {
+        const u32x4 bs = c_to_b(dsk, u);
 #pragma unroll
-      for (int db = 0; db < 4; ++db) acc[db] = mfma32x32x16(tf[u][db], bs, acc[db]);
+        for (int db = 0; db < 4; ++db)
+          acc[db] = mfma32x32x16(lds_read16(st + crb[db & 1][u] + (db >> 1) * 8192), bs, acc[db]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
+  // tiles in pairs, both always run (see the dK/dV kernel)
   load_tile(st0, 0);
   for (int t = 0; t < n_kv; t += 2) {
     kv_tile(st0, t);
-    if (t + 1 < n_kv) kv_tile(st1, t + 1);
+    kv_tile(st1, t + 1);
   }
 
   // ---- scale, rotate back through RoPE, store: block db, register r ->
@@ -291,7 +298,7 @@ __global__ __launch_bounds__(NT, 1) void attn_bwd_dq_kernel(BwdArgs a) {
 // ---------------------------------------------------------------- dK, dV
 
 __global__ __launch_bounds__(NT, 1) void attn_bwd_dkdv_kernel(BwdArgs a) {
-  __shared__ __attribute__((aligned(1024))) char smem[2 * KV_STAGE];
+  __shared__ __attribute__((aligned(1024))) char smem[KV_LDS];
   const int lane = lane_id(), wave = wave_id();
   const int l31 = lane & 31, h = lane >> 5;
 
@@ -345,11 +352,12 @@ __global__ __launch_bounds__(NT, 1) void attn_bwd_dkdv_kernel(BwdArgs a) {
   const int n_it = per_head * hps;
 
   auto load_tile = [&](auto stage_tag, int it) {
-    char* sq = smem + decltype(stage_tag)::value * KV_STAGE;
+    constexpr int S = decltype(stage_tag)::value;
+    char* sq = smem + S * 2 * ROW_TILE;
     char* sdo = sq + ROW_TILE;
-    char* sqt = sdo + ROW_TILE;
+    char* sqt = smem + COLS + S * 2 * COL_TILE;
     char* sdot = sqt + COL_TILE;
-    char* sl = sdot + COL_TILE;
+    char* sl = smem + COLS + 4 * COL_TILE + S * 2 * VEC_TILE;
     char* sdv = sl + VEC_TILE;
     const int hi = it / per_head;
     const int jj = j0 + hi;
@@ -381,14 +389,14 @@ __global__ __launch_bounds__(NT, 1) void attn_bwd_dkdv_kernel(BwdArgs a) {
   };
 
   // LDS read offsets, as in the dQ kernel
-  uint32_t rr[8], cr[2][4];
+  uint32_t rr[8], crb[2][4];
 #pragma unroll
   for (int s = 0; s < 8; ++s) rr[s] = (uint32_t)(l31 * 256 + (((2 * s + h) ^ swz_row(l31)) << 4));
 #pragma unroll
   for (int db = 0; db < 2; ++db) {
     const int d = db * 32 + l31;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) cr[db][u] = (uint32_t)(d * 128 + (((2 * u + h) ^ swz_col(d)) << 4));
+    for (int u = 0; u < 4; ++u) crb[db][u] = (uint32_t)(COLS + d * 128 + (((2 * u + h) ^ swz_col(d)) << 4));
   }
 
   f32x16 dk[4], dv[4];
@@ -405,44 +413,39 @@ __global__ __launch_bounds__(NT, 1) void attn_bwd_dkdv_kernel(BwdArgs a) {
     wait_vmcnt0();
     __syncthreads();
     if (it + 1 < n_it) load_tile(std::integral_constant<int, 1 - S>{}, it + 1);
-    const char* sq = smem + S * KV_STAGE;
+    const char* sq = smem + S * 2 * ROW_TILE;
     const char* sdo = sq + ROW_TILE;
-    const char* sqt = sdo + ROW_TILE;
+    const char* sqt = smem + S * 2 * COL_TILE;  // + COLS, carried by crb
     const char* sdot = sqt + COL_TILE;
-    const char* sl = sdot + COL_TILE;
+    const char* sl = smem + COLS + 4 * COL_TILE + S * 2 * VEC_TILE;
     const char* sdv = sl + VEC_TILE;
     const int hi = it / per_head;
     const int q0 = (qt0 + it - hi * per_head) * 64;
+    const bool live = it < n_it;  // the odd tail's second tile is computed fully masked
 
-    // S = Q K^T and dP = dO V^T for 64 queries (two 32-query blocks)
-    f32x16 sacc[2] = {f32x16{}, f32x16{}}, pacc[2] = {f32x16{}, f32x16{}};
-    {
-      u32x4 qa[2][8];
+    // per 32-query block: S = Q K^T and dP = dO V^T (two interleaved MFMA
+    // chains, fragments read as they are used); P and dS rounded to bf16
+    // pairs; then the block's two 16-query steps of dV^T += dO^T P and
+    // dK^T += Q^T dS.  Register r of block qb is query
+    // q0 + 32 qb + 8 (r/4) + 4 h + r%4.  Kept: queries that exist and (causal)
+    // may see this lane's key; only P is masked, since dS = P (dP - D) and D
+    // is zero past the sequence.
+    const bool need_mask = !live || (a.causal && q0 < k0 + 127) || (q0 + 64 > seq);
+    const int q_hi = live ? (int)min<int64_t>(seq, (int64_t)q0 + 64) : 0;
+    const int q_lo = a.causal ? kw : 0;
+    const uint32_t span = (uint32_t)max(q_hi - q_lo, 0);
+    const int qbase = q0 + 4 * h - q_lo;
 #pragma unroll
-      for (int s = 0; s < 8; ++s)
+    for (int qb = 0; qb < 2; ++qb) {
+      f32x16 sacc = f32x16{}, pacc = f32x16{};
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) qa[qb][s] = lds_read16(sq + rr[s] + qb * 8192);
-#pragma unroll
-      for (int s = 0; s < 8; ++s)
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) sacc[qb] = mfma32x32x16(qa[qb][s], kf[s], sacc[qb]);
-    }
-    {
-      u32x4 da[2][8];
-#pragma unroll
-      for (int s = 0; s < 8; ++s)
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) da[qb][s] = lds_read16(sdo + rr[s] + qb * 8192);
-#pragma unroll
-      for (int s = 0; s < 8; ++s)
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) pacc[qb] = mfma32x32x16(da[qb][s], vf[s], pacc[qb]);
-    }
-    // P and dS; register r of block qb is query q0 + 32 qb + 8 (r/4) + 4 h + r%4
-    const bool need_mask = (a.causal && q0 < k0 + 127) || (q0 + 64 > seq);
-    uint32_t pk[2][8], sk[2][8];
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
+      for (int s = 0; s < 8; ++s) {
+        const u32x4 qa = lds_read16(sq + rr[s] + qb * 8192);
+        const u32x4 da = lds_read16(sdo + rr[s] + qb * 8192);
+        sacc = mfma32x32x16(qa, kf[s], sacc);
+        pacc = mfma32x32x16(da, vf[s], pacc);
+      }
+      uint32_t pk[8], sk[8];
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
         const int qr = qb * 32 + 8 * r4 + 4 * h;
@@ -451,42 +454,35 @@ __global__ __launch_bounds__(NT, 1) void attn_bwd_dkdv_kernel(BwdArgs a) {
         float p[4], ds[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          p[e] = __builtin_amdgcn_exp2f(fmaf(sacc[qb][4 * r4 + e], a.scale_log2, -L[e]));
-          ds[e] = p[e] * (pacc[qb][4 * r4 + e] - Dv[e]);
-          if (need_mask) {
-            const int q = q0 + qr + e;
-            const bool ok = q < seq && (!a.causal || q >= kw);
-            p[e] = ok ? p[e] : 0.0f;
-            ds[e] = ok ? ds[e] : 0.0f;
-          }
+          p[e] = __builtin_amdgcn_exp2f(fmaf(sacc[4 * r4 + e], a.scale_log2, -L[e]));
+          if (need_mask) p[e] = (uint32_t)(qbase + qb * 32 + 8 * r4 + e) < span ? p[e] : 0.0f;
+          ds[e] = p[e] * (pacc[4 * r4 + e] - Dv[e]);
         }
-        pk[qb][2 * r4] = pack_bf16x2(p[0], p[1]);
-        pk[qb][2 * r4 + 1] = pack_bf16x2(p[2], p[3]);
-        sk[qb][2 * r4] = pack_bf16x2(ds[0], ds[1]);
-        sk[qb][2 * r4 + 1] = pack_bf16x2(ds[2], ds[3]);
-      }
-    // dV^T += dO^T P and dK^T += Q^T dS over four 16-query steps
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const u32x4 pb = c_to_b(pk, u);
-      const u32x4 sb = c_to_b(sk, u);
-      u32x4 of[4], tf[4];
-#pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        of[db] = lds_read16(sdot + cr[db & 1][u] + (db >> 1) * 8192);
-        tf[db] = lds_read16(sqt + cr[db & 1][u] + (db >> 1) * 8192);
+        pk[2 * r4] = pack_bf16x2(p[0], p[1]);
+        pk[2 * r4 + 1] = pack_bf16x2(p[2], p[3]);
+        sk[2 * r4] = pack_bf16x2(ds[0], ds[1]);
+        sk[2 * r4 + 1] = pack_bf16x2(ds[2], ds[3]);
       }
 #pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        dv[db] = mfma32x32x16(of[db], pb, dv[db]);
-        dk[db] = mfma32x32x16(tf[db], sb, dk[db]);
+      for (int uu = 0; uu < 2; ++uu) {
+        const int u = 2 * qb + uu;  // query step within the tile
+        const u32x4 pb = c_to_b1(pk, uu);
+        const u32x4 sb = c_to_b1(sk, uu);
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+          const uint32_t off = crb[db & 1][u] + (db >> 1) * 8192;
+          dv[db] = mfma32x32x16(lds_read16(sdot + off), pb, dv[db]);
+          dk[db] = mfma32x32x16(lds_read16(sqt + off), sb, dk[db]);
+        }
       }
     }
   };
+  // tiles in pairs, both always run: a conditional second tile would make the
+  // compiler copy the accumulators between register files at the join
   load_tile(st0, 0);
   for (int it = 0; it < n_it; it += 2) {
     q_tile(st0, it);
-    if (it + 1 < n_it) q_tile(st1, it + 1);
+    q_tile(st1, it + 1);
   }
 
   // ---- partials: lane = key, block db register r -> d = 32 db + 8 (r/4) + 4 h + r%4
@@ -569,6 +565,10 @@ __global__ __launch_bounds__(NT) void attn_dvec_kernel(const bf16_t* o, const bf
     const int j = (int)(row % hq);
     const int64_t b = token / seq, p = token % seq;
     dvec[(b * hq + j) * sp + p] = acc;
+    // the row's padding past the sequence is zero (the dK/dV kernel's dS
+    // relies on it for rows it masks)
+    if (p == seq - 1)
+      for (int64_t q = seq; q < sp; ++q) dvec[(b * hq + j) * sp + q] = 0.0f;
   }
 }
 
