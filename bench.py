@@ -58,14 +58,15 @@ def block_flops(case, t: int) -> dict:
     }
 
 
-def block_backward_flops(case, t: int) -> float:
+def block_backward_flops(case, t: int, saved: bool = False) -> float:
     """Algorithmic flops of one rank's share of the block's backward: the MLP's
-    recomputed gate/up GEMM and its four backward GEMMs (16 m h f_t), the
-    attention's recomputed forward (Q/K/V GEMM, core), dO, the core backward
-    (2.5 times the core forward), dX, dW_qkv and dW_o."""
+    four backward GEMMs (12 m h f_t) and, unless the forward saved them, its
+    recomputed gate/up GEMM (4 m h f_t); the attention's dO, core backward
+    (2.5 times the core forward), dX, dW_qkv, dW_o and, unless saved, its
+    recomputed forward (Q/K/V GEMM, core)."""
     f = block_flops(case, t)
-    mlp = 16.0 * case.tokens * case.hidden * (case.inter // t)
-    attn = 3.0 * f["qkv"] + 2.0 * f["o_proj"] + 3.5 * f["attn_core"]
+    mlp = (12.0 if saved else 16.0) * case.tokens * case.hidden * (case.inter // t)
+    attn = (2.0 if saved else 3.0) * f["qkv"] + 2.0 * f["o_proj"] + (2.5 if saved else 3.5) * f["attn_core"]
     return mlp + attn
 
 
@@ -258,6 +259,14 @@ def per_config_report(dev):
         rec.update({"block_backward_step_ms": round(bstep, 3), "block_backward_step_min_ms": round(bmin, 3),
                     "block_backward_step_tflops": rate(bfl, bstep),
                     "norm_backward_ms": round(nms, 4), "norm_backward_gbs": round(nbytes / nms / 1e6, 1)})
+        # with the forward keeping its activations (no recomputation in the backward)
+        fsv, _ = _time(lambda: blk.forward(save=True), reps=3, warm=1)
+        blk.backward(dz)
+        sstep, smin = _time(lambda: blk.backward(dz), reps=3, warm=1)
+        sfl = case.t * block_backward_flops(case, case.t, saved=True)
+        rec.update({"saving_forward_step_ms": round(fsv, 3),
+                    "saved_backward_step_ms": round(sstep, 3), "saved_backward_step_min_ms": round(smin, 3),
+                    "saved_backward_step_tflops": rate(sfl, sstep)})
         emit(rec)
         del blk, dw, dz
 

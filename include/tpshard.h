@@ -320,6 +320,16 @@ tp_status tp_ce_combine(int32_t t, int64_t m, int64_t v, const float* const* sta
                         float* loss, float* mean, void* stream);
 
 /* --------------------------------------------------------------------------
+ * tp_colwise (bf16, GELU or SWIGLU) that also stores the pre-activation the
+ * backward pass needs ("f and g": the rank's backward differentiates its own
+ * nonlinearity), so it need not be recomputed:
+ *   pre  [m, n] bf16 (GELU: x w^T + bias) or [m, 2n] bf16 (SWIGLU: the n gate
+ *        columns x W1_i + b1, then the n up columns x W3_i + b3)
+ * ------------------------------------------------------------------------ */
+tp_status tp_colwise_save(tp_act act, int64_t m, int64_t k, int64_t n, const void* x, const void* w,
+                          const float* bias, void* y, void* pre, void* stream);
+
+/* --------------------------------------------------------------------------
  * Backward pass of one rank's MLP ("Tensor parallelism" page, section "f and
  * g": g's backward is the identity, so every rank receives the whole output
  * gradient dZ; f's backward sums the ranks' input-gradient partials, one
@@ -338,6 +348,8 @@ tp_status tp_ce_combine(int32_t t, int64_t m, int64_t v, const float* const* sta
  *   x, dz       [m, h] bf16; m must be a multiple of 8
  *   xt, dzt     [h, m] bf16 transposes of x and dz, or NULL (then the call
  *               makes them in ws; on one device the ranks may share them)
+ *   pre         [m, F] bf16 pre-activation saved by tp_colwise_save in the
+ *               forward, or NULL: then it is recomputed (x w_in^T)
  *   ws          workspace of tp_shard_mlp_backward_workspace_bytes bytes
  *
  * tp_transpose: dst [cols, rows] = src [rows, cols]^T (bf16).
@@ -346,8 +358,8 @@ tp_status tp_ce_combine(int32_t t, int64_t m, int64_t v, const float* const* sta
 size_t tp_shard_mlp_backward_workspace_bytes(tp_act act, int64_t m, int64_t h, int64_t f_shard);
 tp_status tp_shard_mlp_backward(tp_act act, int64_t m, int64_t h, int64_t f_shard, const void* x,
                                 const void* w_in, const void* w_out, const void* dz, const void* xt,
-                                const void* dzt, void* ws, size_t ws_bytes, float* dx_partial, float* dw_in,
-                                float* dw_out, void* stream);
+                                const void* dzt, const void* pre, void* ws, size_t ws_bytes, float* dx_partial,
+                                float* dw_in, float* dw_out, void* stream);
 tp_status tp_transpose(int64_t rows, int64_t cols, const void* src, void* dst, void* stream);
 tp_status tp_mlp_act_backward(tp_act act, int64_t m, int64_t n, const void* pre, const void* dy, void* dpre,
                               void* y, void* stream);
@@ -387,8 +399,14 @@ tp_status tp_mlp_act_backward(tp_act act, int64_t m, int64_t n, const void* pre,
  *   x, dz      [batch*seq, h] bf16; batch*seq must be a multiple of 8
  *   xt, dzt    [h, batch*seq] bf16 transposes of x and dz, or NULL (then the
  *              call makes them in ws)
+ *   saved_q, saved_k, saved_vt, saved_o, saved_lse: the forward's, as written
+ *              by tp_shard_attn_save, all five or none (then recomputed)
  *   ws         at least tp_shard_attn_backward_workspace_bytes bytes
  * Biases are not differentiated here.
+ *
+ * tp_shard_attn_save: tp_shard_attn that keeps what the backward needs in
+ * caller buffers instead of a workspace: q, k, vt (as tp_qkv_rope), o
+ * [batch*seq, hq d] and lse (as tp_flash_attn_lse).
  * ------------------------------------------------------------------------ */
 /* --------------------------------------------------------------------------
  * Backward of the fused shard-sum + RMSNorm (tp_shard_sum_rmsnorm): f's
@@ -425,10 +443,15 @@ tp_status tp_flash_attn_backward(int64_t batch, int64_t seq, int32_t hq, int32_t
                                  void* dqkv, int64_t ld, void* stream);
 size_t tp_shard_attn_backward_workspace_bytes(int64_t batch, int64_t seq, int64_t h, int32_t hq, int32_t hkv,
                                               int32_t head_dim);
+tp_status tp_shard_attn_save(int64_t batch, int64_t seq, int64_t h, int32_t hq, int32_t hkv, int32_t head_dim,
+                             float rope_base, int32_t causal, const void* x, const void* w_qkv, const void* w_o,
+                             void* q, void* k, void* vt, void* o, float* lse, float* partial, void* stream);
 tp_status tp_shard_attn_backward(int64_t batch, int64_t seq, int64_t h, int32_t hq, int32_t hkv, int32_t head_dim,
                                  float rope_base, int32_t causal, const void* x, const void* w_qkv, const void* w_o,
-                                 const void* dz, const void* xt, const void* dzt, void* ws, size_t ws_bytes,
-                                 float* dx_partial, float* dw_qkv, float* dw_o, void* stream);
+                                 const void* dz, const void* xt, const void* dzt, const void* saved_q,
+                                 const void* saved_k, const void* saved_vt, const void* saved_o,
+                                 const float* saved_lse, void* ws, size_t ws_bytes, float* dx_partial, float* dw_qkv,
+                                 float* dw_o, void* stream);
 
 /* --------------------------------------------------------------------------
  * Introspection: how the bf16 GEMM behind tp_colwise / tp_rowwise /

@@ -260,6 +260,23 @@ tp_status tp_colwise(tp_act act, tp_dtype dt, int64_t m, int64_t k, int64_t n, c
   return launched(e, "tp_colwise");
 }
 
+tp_status tp_colwise_save(tp_act act, int64_t m, int64_t k, int64_t n, const void* x, const void* w,
+                          const float* bias, void* y, void* pre, void* stream) {
+  if (act != TP_ACT_GELU && act != TP_ACT_SWIGLU)
+    return fail(TP_ERR_INVALID_ARG, "tp_colwise_save needs GELU or SWIGLU, got %d", (int)act);
+  TRY(check_gemm(act, TP_BF16, m, k, n, x, w, y, "x", "w", "y"));
+  if (m == 0) return ok();
+  TRY(check_ptr(pre, "pre"));
+  if (pre == y || pre == x) return fail(TP_ERR_INVALID_ARG, "pre aliases x or y");
+  const int64_t pw = act == TP_ACT_SWIGLU ? 2 * n : n;
+  if (m * pw * 2 >= ((int64_t)1 << 40)) return fail(TP_ERR_SHAPE, "pre too large");
+  if (bias) TRY(check_ptr(bias, "bias"));
+  TRY(device_check());
+  return launched(tpk::launch_gemm_bf16(act == TP_ACT_SWIGLU ? tpk::EPI_SWIGLU_SAVE : tpk::EPI_GELU_SAVE, m, n, k,
+                                        x, w, y, nullptr, as_stream(stream), bias, 0, pre),
+                  "tp_colwise_save");
+}
+
 tp_status tp_rowwise(tp_dtype dt, int64_t m, int64_t k, int64_t n, const void* y, const void* w,
                      float* partial, void* stream) {
   TRY(check_gemm(TP_ACT_NONE, dt, m, k, n, y, w, partial, "y", "w", "partial"));
@@ -467,10 +484,24 @@ size_t tp_shard_attn_backward_workspace_bytes(int64_t batch, int64_t seq, int64_
   return attn_shard_bwd_layout(batch, seq, h, hq, hkv, head_dim).total;
 }
 
+tp_status tp_shard_attn_save(int64_t batch, int64_t seq, int64_t h, int32_t hq, int32_t hkv, int32_t head_dim,
+                             float rope_base, int32_t causal, const void* x, const void* w_qkv, const void* w_o,
+                             void* q, void* k, void* vt, void* o, float* lse, float* partial, void* stream) {
+  TRY(check_attn_shape(batch, seq, hq, hkv, head_dim));
+  const int64_t m = batch * seq;
+  TRY(check_gemm(TP_ACT_NONE, TP_BF16, m, (int64_t)hq * head_dim, h, x, w_o, partial, "x", "w_o", "partial"));
+  if (m == 0) return ok();
+  TRY(tp_qkv_rope(batch, seq, h, hq, hkv, head_dim, rope_base, x, w_qkv, nullptr, q, k, vt, stream));
+  TRY(tp_flash_attn_lse(batch, seq, hq, hkv, head_dim, causal, q, k, vt, o, lse, stream));
+  return tp_rowwise(TP_BF16, m, (int64_t)hq * head_dim, h, o, w_o, partial, stream);
+}
+
 tp_status tp_shard_attn_backward(int64_t batch, int64_t seq, int64_t h, int32_t hq, int32_t hkv, int32_t head_dim,
                                  float rope_base, int32_t causal, const void* x, const void* w_qkv, const void* w_o,
-                                 const void* dz, const void* xt, const void* dzt, void* ws, size_t ws_bytes,
-                                 float* dx_partial, float* dw_qkv, float* dw_o, void* stream) {
+                                 const void* dz, const void* xt, const void* dzt, const void* saved_q,
+                                 const void* saved_k, const void* saved_vt, const void* saved_o,
+                                 const float* saved_lse, void* ws, size_t ws_bytes, float* dx_partial, float* dw_qkv,
+                                 float* dw_o, void* stream) {
   TRY(check_attn_shape(batch, seq, hq, hkv, head_dim));
   if (!(rope_base > 1.0f)) return fail(TP_ERR_INVALID_ARG, "rope_base must be > 1");
   const int64_t m = batch * seq;
@@ -488,6 +519,12 @@ tp_status tp_shard_attn_backward(int64_t batch, int64_t seq, int64_t h, int32_t 
   TRY(check_gemm(TP_ACT_NONE, TP_BF16, n, m, h, ws, ws, dw_qkv, "ws", "ws", "dw_qkv"));
   if (xt) TRY(check_ptr(xt, "xt"));
   if (dzt) TRY(check_ptr(dzt, "dzt"));
+  const void* sv[5] = {saved_q, saved_k, saved_vt, saved_o, saved_lse};
+  const int nsaved = (saved_q != nullptr) + (saved_k != nullptr) + (saved_vt != nullptr) + (saved_o != nullptr) +
+                     (saved_lse != nullptr);
+  if (nsaved != 0 && nsaved != 5)
+    return fail(TP_ERR_INVALID_ARG, "saved q, k, vt, o and lse come all together or not at all");
+  for (int i = 0; i < nsaved; ++i) TRY(check_ptr(sv[i], "a saved activation"));
   const AttnShardBwdLayout L = attn_shard_bwd_layout(batch, seq, h, hq, hkv, head_dim);
   if (ws_bytes < L.total) return fail(TP_ERR_WORKSPACE, "workspace of %zu bytes < %zu needed", ws_bytes, L.total);
   TRY(device_check());
@@ -501,18 +538,29 @@ tp_status tp_shard_attn_backward(int64_t batch, int64_t seq, int64_t h, int32_t 
   hipError_t e;
 #define TP_STEP(call, what) \
   if ((e = (call)) != hipSuccess) return launched(e, what);
-  // recompute the forward: Q, K, V^T (RoPE applied), O and the log-sum-exp
-  TRY(tp_qkv_rope(batch, seq, h, hq, hkv, head_dim, rope_base, x, w_qkv, nullptr, f + F.q, f + F.k, f + F.vt,
-                  stream));
-  TRY(tp_flash_attn_lse(batch, seq, hq, hkv, head_dim, causal, f + F.q, f + F.k, f + F.vt, f + F.o,
-                        reinterpret_cast<float*>(b + L.lse), stream));
+  // the forward's saved Q, K, V^T (RoPE applied), O and log-sum-exp, or them recomputed
+  const void* q = saved_q;
+  const void* k = saved_k;
+  const void* vt = saved_vt;
+  const void* o = saved_o;
+  const float* lse = saved_lse;
+  if (!nsaved) {
+    TRY(tp_qkv_rope(batch, seq, h, hq, hkv, head_dim, rope_base, x, w_qkv, nullptr, f + F.q, f + F.k, f + F.vt,
+                    stream));
+    TRY(tp_flash_attn_lse(batch, seq, hq, hkv, head_dim, causal, f + F.q, f + F.k, f + F.vt, f + F.o,
+                          reinterpret_cast<float*>(b + L.lse), stream));
+    q = f + F.q;
+    k = f + F.k;
+    vt = f + F.vt;
+    o = f + F.o;
+    lse = reinterpret_cast<const float*>(b + L.lse);
+  }
   // dO = dZ W_o (W_o [h, hq d] transposed to [hq d, h])
   TP_STEP(tpk::launch_transpose(h, qd, w_o, b + L.wo_t, s), "tp_shard_attn_backward (w_o^T)");
   TP_STEP(gemm(tpk::EPI_BF16, m, qd, h, dz, b + L.wo_t, b + L.dout), "tp_shard_attn_backward (dO)");
   // the attention core: dQKV before RoPE, packed like the projection's output
-  TRY(tp_flash_attn_backward(batch, seq, hq, hkv, head_dim, rope_base, causal, f + F.q, f + F.k, f + F.vt, f + F.o,
-                             reinterpret_cast<const float*>(b + L.lse), b + L.dout, b + L.core, L.total - L.core,
-                             b + L.dqkv, n, stream));
+  TRY(tp_flash_attn_backward(batch, seq, hq, hkv, head_dim, rope_base, causal, q, k, vt, o, lse, b + L.dout,
+                             b + L.core, L.total - L.core, b + L.dqkv, n, stream));
   // dX partial = dQKV W_qkv (W_qkv transposed to [h, n]); f's backward sums these over ranks
   TP_STEP(tpk::launch_transpose(n, h, w_qkv, b + L.wqkv_t, s), "tp_shard_attn_backward (w_qkv^T)");
   TP_STEP(gemm(tpk::EPI_F32, m, h, n, b + L.dqkv, b + L.wqkv_t, dx_partial), "tp_shard_attn_backward (dX)");
@@ -527,7 +575,7 @@ tp_status tp_shard_attn_backward(int64_t batch, int64_t seq, int64_t h, int32_t 
     TP_STEP(tpk::launch_transpose(m, h, x, b + L.xt, s), "tp_shard_attn_backward (X^T)");
     xt_p = b + L.xt;
   }
-  TP_STEP(tpk::launch_transpose(m, qd, f + F.o, b + L.o_t, s), "tp_shard_attn_backward (O^T)");
+  TP_STEP(tpk::launch_transpose(m, qd, o, b + L.o_t, s), "tp_shard_attn_backward (O^T)");
   TP_STEP(gemm(tpk::EPI_F32, h, qd, m, dzt_p, b + L.o_t, dw_o), "tp_shard_attn_backward (dW_o)");
   TP_STEP(tpk::launch_transpose(m, n, b + L.dqkv, b + L.dqkv_t, s), "tp_shard_attn_backward (dQKV^T)");
   TP_STEP(gemm(tpk::EPI_F32, n, h, m, b + L.dqkv_t, xt_p, dw_qkv), "tp_shard_attn_backward (dW_qkv)");
@@ -789,8 +837,8 @@ size_t tp_shard_mlp_backward_workspace_bytes(tp_act act, int64_t m, int64_t h, i
 
 tp_status tp_shard_mlp_backward(tp_act act, int64_t m, int64_t h, int64_t f_shard, const void* x,
                                 const void* w_in, const void* w_out, const void* dz, const void* xt,
-                                const void* dzt, void* ws, size_t ws_bytes, float* dx_partial, float* dw_in,
-                                float* dw_out, void* stream) {
+                                const void* dzt, const void* pre, void* ws, size_t ws_bytes, float* dx_partial,
+                                float* dw_in, float* dw_out, void* stream) {
   if (act != TP_ACT_GELU && act != TP_ACT_SWIGLU)
     return fail(TP_ERR_INVALID_ARG, "tp_shard_mlp_backward needs GELU or SWIGLU, got %d", (int)act);
   if (m % 8 != 0) return fail(TP_ERR_SHAPE, "m = %lld must be a multiple of 8 (the weight gradients reduce over tokens)",
@@ -805,6 +853,7 @@ tp_status tp_shard_mlp_backward(tp_act act, int64_t m, int64_t h, int64_t f_shar
   TRY(check_gemm(TP_ACT_NONE, TP_BF16, F, m, h, ws, ws, dw_in, "ws", "ws", "dw_in"));
   if (xt) TRY(check_ptr(xt, "xt"));
   if (dzt) TRY(check_ptr(dzt, "dzt"));
+  if (pre) TRY(check_ptr(pre, "pre"));
   TRY(check_ptr(ws, "ws"));
   const MlpBwdLayout L = mlp_bwd_layout(act, m, h, f_shard);
   if (ws_bytes < L.total) return fail(TP_ERR_WORKSPACE, "workspace of %zu bytes < %zu needed", ws_bytes, L.total);
@@ -817,12 +866,17 @@ tp_status tp_shard_mlp_backward(tp_act act, int64_t m, int64_t h, int64_t f_shar
   hipError_t e;
 #define TP_BWD_STEP(call, what) \
   if ((e = (call)) != hipSuccess) return launched(e, what);
-  // recompute the pre-activation; dY = dZ W_out (W_out transposed to [f, h])
-  TP_BWD_STEP(gemm(tpk::EPI_BF16, m, F, h, x, w_in, b + L.pre), "tp_shard_mlp_backward (pre-activation)");
+  // the forward's saved pre-activation, or it recomputed; dY = dZ W_out (W_out
+  // transposed to [f, h])
+  const void* pre_p = pre;
+  if (!pre_p) {
+    TP_BWD_STEP(gemm(tpk::EPI_BF16, m, F, h, x, w_in, b + L.pre), "tp_shard_mlp_backward (pre-activation)");
+    pre_p = b + L.pre;
+  }
   TP_BWD_STEP(tpk::launch_transpose(h, f_shard, w_out, b + L.wout_t, s), "tp_shard_mlp_backward (w_out^T)");
   TP_BWD_STEP(gemm(tpk::EPI_BF16, m, f_shard, h, dz, b + L.wout_t, b + L.dy), "tp_shard_mlp_backward (dY)");
   // dPre (and the activation Y again, for the output layer's weight gradient)
-  TP_BWD_STEP(tpk::launch_act_backward(act == TP_ACT_SWIGLU, m, f_shard, b + L.pre, b + L.dy, b + L.dpre, b + L.y, s),
+  TP_BWD_STEP(tpk::launch_act_backward(act == TP_ACT_SWIGLU, m, f_shard, pre_p, b + L.dy, b + L.dpre, b + L.y, s),
               "tp_shard_mlp_backward (activation)");
   // dX partial = dPre W_in (W_in transposed to [h, F]); f's backward sums these over ranks
   TP_BWD_STEP(tpk::launch_transpose(F, h, w_in, b + L.win_t, s), "tp_shard_mlp_backward (w_in^T)");

@@ -103,6 +103,7 @@ struct Args {
   int64_t M, N, K;
   int64_t lda;        // row stride of x in elements (>= K; a column slice when > K)
   const float* bias;  // per output column, added before the epilogue's nonlinearity, or NULL
+  void* pre[MAX_GROUP];  // _SAVE epilogues: bf16 pre-activation rows (GeLU N, SwiGLU 2 N wide)
   int num_bm;  // tile rows of this launch (height BMT)
   int num_bn;  // tile columns of this launch
   int bn0;     // first tile column of this launch
@@ -133,6 +134,10 @@ __device__ __forceinline__ void tile_coords(int id, int nb, int num_bm, int num_
   bm = first + inner % gs;
   bn = inner / gs;
 }
+
+constexpr bool is_swiglu(int epi) { return epi == EPI_SWIGLU || epi == EPI_SWIGLU_SAVE; }
+constexpr bool is_gelu(int epi) { return epi == EPI_GELU || epi == EPI_GELU_SAVE; }
+constexpr bool saves_pre(int epi) { return epi == EPI_GELU_SAVE || epi == EPI_SWIGLU_SAVE; }
 
 template <int EPI, int BMT, bool W4>
 __global__ __launch_bounds__((Cfg<BMT, W4>::NW * 64), 1) void gemm_bf16_kernel(Args args) {
@@ -169,7 +174,7 @@ __global__ __launch_bounds__((Cfg<BMT, W4>::NW * 64), 1) void gemm_bf16_kernel(A
 
   __amdgpu_buffer_rsrc_t rsrc_b;
   int n_valid;  // valid weight rows (plain) or valid output columns (SwiGLU)
-  if (EPI == EPI_SWIGLU) {
+  if (is_swiglu(EPI)) {
     const int64_t o0 = (int64_t)bn * (BN / 2);
     n_valid = (int)min<int64_t>(BN / 2, N - o0);
     rsrc_b = make_rsrc(wg + o0 * K, (uint32_t)((N + n_valid) * K * 2));
@@ -198,7 +203,7 @@ __global__ __launch_bounds__((Cfg<BMT, W4>::NW * 64), 1) void gemm_bf16_kernel(A
     const int r = slot / CH;
     const int c = (slot % CH) ^ swz(r);
     b_k[j] = c * 8;
-    if (EPI == EPI_SWIGLU) {
+    if (is_swiglu(EPI)) {
       const int wn = r >> 7, qq = r & 127;
       const int o_rel = wn * 64 + (qq & 63);
       const int64_t rel_row = (qq < 64) ? o_rel : N + o_rel;
@@ -520,7 +525,7 @@ __global__ __launch_bounds__((Cfg<BMT, W4>::NW * 64), 1) void gemm_bf16_kernel(A
           if (row < M) reinterpret_cast<float*>(outg)[row * N + col] = acc[i][j][r];
         }
       }
-  } else if (EPI == EPI_BF16 || EPI == EPI_GELU) {
+  } else if (EPI == EPI_BF16 || is_gelu(EPI)) {
     const int64_t col_base = (int64_t)bn * BN + cq;
     // the bias of each block's column of this lane (before the transpose);
     // -0 is the identity of the float add, so no bias leaves results as they were
@@ -537,20 +542,27 @@ __global__ __launch_bounds__((Cfg<BMT, W4>::NW * 64), 1) void gemm_bf16_kernel(A
         const int64_t col = col_base + col_block<NJ>(wn, j) * 32;
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          float v[4];
+          float v[4], pv[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             v[e] = acc[i][j][4 * g + e] + bcol[j];
-            if (EPI == EPI_GELU) v[e] = gelu_erf(v[e]);
+            if (saves_pre(EPI)) pv[e] = v[e];
+            if (is_gelu(EPI)) v[e] = gelu_erf(v[e]);
           }
           quad_transpose(v, q);
           const int64_t row = row_base + i * 32 + 8 * g + q;
           if (row < M && col < N)
             *reinterpret_cast<u32x2*>(reinterpret_cast<bf16_t*>(outg) + row * N + col) =
                 u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+          if (saves_pre(EPI)) {
+            quad_transpose(pv, q);
+            if (row < M && col < N)
+              *reinterpret_cast<u32x2*>(reinterpret_cast<bf16_t*>(args.pre[blockIdx.y]) + row * N + col) =
+                  u32x2{pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3])};
+          }
         }
       }
-  } else if (EPI == EPI_SWIGLU) {
+  } else if (is_swiglu(EPI)) {
     const int64_t col_base = (int64_t)bn * (BN / 2) + hg * 64 + cq;
     // gate and up biases of this lane's output column of each pair (bias
     // holds the N gate biases, then the N up biases); -0 when there is none
@@ -568,15 +580,29 @@ __global__ __launch_bounds__((Cfg<BMT, W4>::NW * 64), 1) void gemm_bf16_kernel(A
         const int64_t col = col_base + pair_col(j);
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          float v[4];
+          float v[4], pg[4], pu[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
+          for (int e = 0; e < 4; ++e) {
+            if (saves_pre(EPI)) {
+              pg[e] = acc[i][j][4 * g + e] + bg[j];
+              pu[e] = acc[i][j + NP][4 * g + e] + bu[j];
+            }
             v[e] = silu_fast(acc[i][j][4 * g + e] + bg[j]) * (acc[i][j + NP][4 * g + e] + bu[j]);
+          }
           quad_transpose(v, q);
           const int64_t row = row_base + i * 32 + 8 * g + q;
           if (row < M && col < N)
             *reinterpret_cast<u32x2*>(reinterpret_cast<bf16_t*>(outg) + row * N + col) =
                 u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+          if (saves_pre(EPI)) {
+            quad_transpose(pg, q);
+            quad_transpose(pu, q);
+            bf16_t* pr = reinterpret_cast<bf16_t*>(args.pre[blockIdx.y]) + row * 2 * N + col;
+            if (row < M && col < N) {
+              *reinterpret_cast<u32x2*>(pr) = u32x2{pack_bf16x2(pg[0], pg[1]), pack_bf16x2(pg[2], pg[3])};
+              *reinterpret_cast<u32x2*>(pr + N) = u32x2{pack_bf16x2(pu[0], pu[1]), pack_bf16x2(pu[2], pu[3])};
+            }
+          }
         }
       }
   } else {  // EPI_QKV: each 128-column group of the tile is exactly one head
@@ -891,14 +917,17 @@ void gemm_plan(int64_t M, int64_t N, int swiglu, int groups, int* bm_main, int* 
 
 hipError_t launch_gemm_bf16_group(int epi, int groups, int64_t M, int64_t N, int64_t K,
                                   const void* const* x, const void* const* w, void* const* out,
-                                  const QkvOut* qkv, hipStream_t s, const float* bias, int64_t lda) {
+                                  const QkvOut* qkv, hipStream_t s, const float* bias, int64_t lda,
+                                  void* const* pre) {
   if (groups < 1 || groups > MAX_GROUP) return hipErrorInvalidValue;
+  if ((epi == EPI_GELU_SAVE || epi == EPI_SWIGLU_SAVE) && !pre) return hipErrorInvalidValue;
   Args a;
   for (int g = 0; g < MAX_GROUP; ++g) {
     const int src = g < groups ? g : 0;
     a.x[g] = reinterpret_cast<const bf16_t*>(x[src]);
     a.w[g] = reinterpret_cast<const bf16_t*>(w[src]);
     a.out[g] = out[src];
+    a.pre[g] = pre ? pre[src] : nullptr;
   }
   a.M = M;
   a.N = N;
@@ -907,7 +936,7 @@ hipError_t launch_gemm_bf16_group(int epi, int groups, int64_t M, int64_t N, int
   a.bias = bias;
   a.num_bm = a.num_bn = a.bn0 = 0;
   if (qkv) a.qkv = *qkv; else a.qkv = QkvOut{};
-  const int64_t bn_cols = (epi == EPI_SWIGLU) ? BN / 2 : BN;
+  const int64_t bn_cols = is_swiglu(epi) ? BN / 2 : BN;
   const int64_t nbn = (N + bn_cols - 1) / bn_cols;
   if (M == 0 || nbn == 0) return hipSuccess;
   switch (epi) {
@@ -915,6 +944,8 @@ hipError_t launch_gemm_bf16_group(int epi, int groups, int64_t M, int64_t N, int
     case EPI_BF16: launch_planned<EPI_BF16>(a, nbn, groups, s); break;
     case EPI_GELU: launch_planned<EPI_GELU>(a, nbn, groups, s); break;
     case EPI_SWIGLU: launch_planned<EPI_SWIGLU>(a, nbn, groups, s); break;
+    case EPI_GELU_SAVE: launch_planned<EPI_GELU_SAVE>(a, nbn, groups, s); break;
+    case EPI_SWIGLU_SAVE: launch_planned<EPI_SWIGLU_SAVE>(a, nbn, groups, s); break;
     case EPI_QKV: {
       if (groups != 1) return hipErrorInvalidValue;
       if (a.qkv.seq_pad > a.qkv.seq) {
@@ -933,11 +964,13 @@ hipError_t launch_gemm_bf16_group(int epi, int groups, int64_t M, int64_t N, int
 }
 
 hipError_t launch_gemm_bf16(int epi, int64_t M, int64_t N, int64_t K, const void* x, const void* w,
-                            void* out, const QkvOut* qkv, hipStream_t s, const float* bias, int64_t lda) {
+                            void* out, const QkvOut* qkv, hipStream_t s, const float* bias, int64_t lda,
+                            void* pre) {
   const void* xs[1] = {x};
   const void* ws[1] = {w};
   void* os[1] = {out};
-  return launch_gemm_bf16_group(epi, 1, M, N, K, xs, ws, os, qkv, s, bias, lda);
+  void* ps[1] = {pre};
+  return launch_gemm_bf16_group(epi, 1, M, N, K, xs, ws, os, qkv, s, bias, lda, pre ? ps : nullptr);
 }
 
 }  // namespace tpk

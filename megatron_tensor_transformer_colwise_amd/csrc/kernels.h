@@ -12,7 +12,9 @@ enum Epi : int {
   EPI_BF16 = 1,    // bf16 output, no nonlinearity
   EPI_GELU = 2,    // bf16 GeLU(acc)
   EPI_SWIGLU = 3,  // bf16 SiLU(gate) * up, weight rows [gate block ; up block]
-  EPI_QKV = 4      // Q/K with RoPE, V transposed per sequence
+  EPI_QKV = 4,     // Q/K with RoPE, V transposed per sequence
+  EPI_GELU_SAVE = 5,    // EPI_GELU that also stores the bf16 pre-activation
+  EPI_SWIGLU_SAVE = 6   // EPI_SWIGLU that also stores the bf16 gate and up pre-activations
 };
 
 struct QkvOut {
@@ -26,6 +28,9 @@ struct QkvOut {
   float log2_base;
 };
 
+// The _SAVE epilogues also store the bf16 pre-activation to pre: [M, N]
+// (GeLU) or [M, 2N] (SwiGLU: the N gate columns, then the N up columns),
+// with the bias added, exactly the values the nonlinearity reads.
 // out[m, n] = epi( sum_k x[m, k] * w[row(n), k] + bias[n] ), bf16 operands,
 // float32 accumulate.  bias (float32, or NULL) is added before the
 // nonlinearity (SwiGLU: N gate biases then N up biases; QKV: before RoPE;
@@ -33,7 +38,7 @@ struct QkvOut {
 // the first K are read.
 hipError_t launch_gemm_bf16(int epi, int64_t M, int64_t N, int64_t K, const void* x, const void* w,
                             void* out, const QkvOut* qkv, hipStream_t s, const float* bias = nullptr,
-                            int64_t lda = 0);
+                            int64_t lda = 0, void* pre = nullptr);
 
 // Tile heights the bf16 GEMM launches for an M x N output (N = output
 // columns): columns [0, split) at height bm_main, the rest at bm_tail.
@@ -45,7 +50,7 @@ void gemm_plan(int64_t M, int64_t N, int swiglu, int groups, int* bm_main, int* 
 hipError_t launch_gemm_bf16_group(int epi, int groups, int64_t M, int64_t N, int64_t K,
                                   const void* const* x, const void* const* w, void* const* out,
                                   const QkvOut* qkv, hipStream_t s, const float* bias = nullptr,
-                                  int64_t lda = 0);
+                                  int64_t lda = 0, void* const* pre = nullptr);
 
 // Same contraction in float32 throughout (EPI_F32 / EPI_BF16 meaning "no
 // nonlinearity, float32 out", EPI_GELU, EPI_SWIGLU).

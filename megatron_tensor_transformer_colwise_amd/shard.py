@@ -139,8 +139,25 @@ class MLPShards:
     def reduce(self, residual=None, residual_dt="f32", stream=None) -> None:
         tp.tp_shard_sum(self.t, self.m * self.h, list(self.partials), residual, residual_dt, self.out, stream)
 
-    def forward(self, x=None, residual=None, residual_dt="f32", stream=None, grouped=False):
-        if grouped:
+    def rank_save(self, r: int, x=None, stream=None) -> None:
+        """Rank r's forward that also keeps its pre-activation for the backward
+        (bf16 [m, f] for GeLU, [m, 2 f] = [gate | up] for SwiGLU)."""
+        if getattr(self, "pre", None) is None:
+            fin = 2 * self.f_shard if self.act == "swiglu" else self.f_shard
+            self.pre = [torch.empty(self.m, fin, dtype=torch.bfloat16, device=self.x.device)
+                        for _ in range(self.t)]
+        tp.tp_colwise_save(self.act, self.m, self.h, self.f_shard, self.x if x is None else x, self.w_in[r],
+                           self.act_ws, self.pre[r], stream)
+        self.rowwise(r, stream)
+
+    def forward(self, x=None, residual=None, residual_dt="f32", stream=None, grouped=False, save=False):
+        """All ranks and the sum; ``save`` keeps every rank's pre-activation so
+        the backward does not recompute it."""
+        self.saved = save
+        if save:
+            for r in range(self.t):
+                self.rank_save(r, x, stream)
+        elif grouped:
             self.all_ranks_grouped(x, stream)
         else:
             for r in range(self.t):
@@ -162,11 +179,13 @@ class MLPShards:
             self.dx = torch.empty(m, h, dtype=torch.float32, device=dev)
 
     def backward_rank(self, r: int, dz, stream=None) -> None:
-        """Rank r's gradients: its dX partial and its weight shards' gradients."""
+        """Rank r's gradients: its dX partial and its weight shards' gradients
+        (from the saved pre-activation after a saving forward, else recomputing it)."""
         self._bwd_buffers()
+        pre = self.pre[r] if getattr(self, "saved", False) else None
         tp.tp_shard_mlp_backward(self.act, self.m, self.h, self.f_shard, self.x, self.w_in[r], self.w_out[r], dz,
                                  None, None, self.bwd_ws, self.bwd_ws_bytes, self.dx_partials[r], self.dw_in[r],
-                                 self.dw_out[r], stream)
+                                 self.dw_out[r], stream, pre=pre)
 
     def backward(self, dz, stream=None):
         for r in range(self.t):
@@ -204,9 +223,31 @@ class AttnShards:
         m = self.batch * self.seq
         tp.tp_shard_sum(self.t, m * self.h, list(self.partials), residual, residual_dt, self.out, stream)
 
-    def forward(self, x=None, residual=None, residual_dt="f32", stream=None):
+    def rank_save(self, r: int, x=None, stream=None) -> None:
+        """Rank r's forward keeping Q, K, V^T, O and the log-sum-exp for the backward."""
+        rk = self.ranks[r]
+        if getattr(self, "saved_acts", None) is None:
+            dev, m, d = self.x.device, self.batch * self.seq, self.d
+            sp = (self.seq + 63) // 64 * 64
+            self.saved_acts = [(torch.empty(m, q.hq * d, dtype=torch.bfloat16, device=dev),
+                                torch.empty(m, q.hkv * d, dtype=torch.bfloat16, device=dev),
+                                torch.empty(self.batch, q.hkv, d, sp, dtype=torch.bfloat16, device=dev),
+                                torch.empty(m, q.hq * d, dtype=torch.bfloat16, device=dev),
+                                torch.empty(self.batch, q.hq, sp, dtype=torch.float32, device=dev))
+                               for q in self.ranks]
+        q, k, vt, o, lse = self.saved_acts[r]
+        tp.tp_shard_attn_save(self.batch, self.seq, self.h, rk.hq, rk.hkv, self.d, self.case.rope_base, self.causal,
+                              self.x if x is None else x, rk.w_qkv, rk.w_o, q, k, vt, o, lse, self.partials[r], stream)
+
+    def forward(self, x=None, residual=None, residual_dt="f32", stream=None, save=False):
+        """All ranks and the sum; ``save`` keeps every rank's activations so the
+        backward does not recompute the forward."""
+        self.saved = save
         for r in range(self.t):
-            self.rank(r, x, stream)
+            if save:
+                self.rank_save(r, x, stream)
+            else:
+                self.rank(r, x, stream)
         self.reduce(residual, residual_dt, stream)
         return self.out
 
@@ -230,10 +271,11 @@ class AttnShards:
         rows and W_o columns."""
         self._bwd_buffers()
         rk = self.ranks[r]
+        saved = self.saved_acts[r] if getattr(self, "saved", False) else None
         tp.tp_shard_attn_backward(self.batch, self.seq, self.h, rk.hq, rk.hkv, self.d, self.case.rope_base,
                                   self.causal, self.x if x is None else x, rk.w_qkv, rk.w_o, dz, None, None,
                                   self.bwd_ws, self.bwd_ws_bytes, self.dx_partials[r], self.dw_qkv[r],
-                                  self.dw_o[r], stream)
+                                  self.dw_o[r], stream, saved=saved)
 
     def backward(self, dz, x=None, stream=None):
         for r in range(self.t):
@@ -315,16 +357,22 @@ class BlockShards:
                                          self.norm_ws_bytes, stream)
         return self.d_x
 
-    def forward(self, stream=None, fused=True):
+    def forward(self, stream=None, fused=True, save=False):
+        """``save`` keeps every rank's activations for ``backward`` (no
+        recomputation there)."""
         self.norm_attn(stream)
         if fused:
+            self.attn.saved = save
             for r in range(self.t):
-                self.attn.rank(r, stream=stream)
+                if save:
+                    self.attn.rank_save(r, stream=stream)
+                else:
+                    self.attn.rank(r, stream=stream)
             self.sum_norm_mlp(stream)
         else:
-            self.attn.forward(residual=self.x, residual_dt="bf16", stream=stream)
+            self.attn.forward(residual=self.x, residual_dt="bf16", stream=stream, save=save)
             self.norm_mlp(stream)
-        self.mlp.forward(residual=self.attn.out, residual_dt="f32", stream=stream)
+        self.mlp.forward(residual=self.attn.out, residual_dt="f32", stream=stream, save=save)
         return self.mlp.out
 
     def sp_runs(self) -> tuple[int, int, int]:

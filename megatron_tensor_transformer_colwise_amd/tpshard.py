@@ -60,8 +60,9 @@ _SIGS = {
     "tp_gemm_plan": [_i64, _i64, _i32, ctypes.POINTER(_i32), ctypes.POINTER(_i32), ctypes.POINTER(_i32)],
     "tp_embedding": [_i64, _i64, _i64, _i64, _vp, _vp, _vp, _i64, _vp],
     "tp_shard_mlp_backward_workspace_bytes": [_i32, _i64, _i64, _i64],
-    "tp_shard_mlp_backward": [_i32, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp,
-                              _vp, _vp, _vp],
+    "tp_shard_mlp_backward": [_i32, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t,
+                              _vp, _vp, _vp, _vp],
+    "tp_colwise_save": [_i32, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp],
     "tp_transpose": [_i64, _i64, _vp, _vp, _vp],
     "tp_mlp_act_backward": [_i32, _i64, _i64, _vp, _vp, _vp, _vp, _vp],
     "tp_shard_sum_rmsnorm_backward_workspace_bytes": [_i64, _i64],
@@ -73,7 +74,9 @@ _SIGS = {
                                ctypes.c_size_t, _vp, _i64, _vp],
     "tp_shard_attn_backward_workspace_bytes": [_i64, _i64, _i64, _i32, _i32, _i32],
     "tp_shard_attn_backward": [_i64, _i64, _i64, _i32, _i32, _i32, _f32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
-                               ctypes.c_size_t, _vp, _vp, _vp, _vp],
+                               _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp, _vp, _vp, _vp],
+    "tp_shard_attn_save": [_i64, _i64, _i64, _i32, _i32, _i32, _f32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                           _vp, _vp],
     "tp_vocab_logits": [_i64, _i64, _i64, _vp, _vp, _vp, _vp],
     "tp_ce_stats": [_i64, _i64, _i64, _vp, _vp, _vp, _vp],
     "tp_ce_combine": [_i32, _i64, _i64, ctypes.POINTER(_vp), _vp, _vp, _vp, _vp],
@@ -252,10 +255,14 @@ def tp_shard_mlp_backward_workspace_bytes(act, m, h, f_shard) -> int:
 
 
 def tp_shard_mlp_backward(act, m, h, f_shard, x, w_in, w_out, dz, xt, dzt, ws, ws_bytes, dx_partial, dw_in,
-                          dw_out, stream=None) -> None:
+                          dw_out, stream=None, pre=None) -> None:
     _check(lib().tp_shard_mlp_backward(_e(act, ACTS), m, h, f_shard, _p(x), _p(w_in), _p(w_out), _p(dz), _p(xt),
-                                       _p(dzt), _p(ws), ws_bytes, _p(dx_partial), _p(dw_in), _p(dw_out),
+                                       _p(dzt), _p(pre), _p(ws), ws_bytes, _p(dx_partial), _p(dw_in), _p(dw_out),
                                        _s(stream)))
+
+
+def tp_colwise_save(act, m, k, n, x, w, y, pre, stream=None, bias=None) -> None:
+    _check(lib().tp_colwise_save(_e(act, ACTS), m, k, n, _p(x), _p(w), _p(bias), _p(y), _p(pre), _s(stream)))
 
 
 def tp_flash_attn_lse(batch, seq, hq, hkv, head_dim, causal, q, k, vt, o, lse, stream=None) -> None:
@@ -278,10 +285,19 @@ def tp_shard_attn_backward_workspace_bytes(batch, seq, h, hq, hkv, head_dim) -> 
 
 
 def tp_shard_attn_backward(batch, seq, h, hq, hkv, head_dim, rope_base, causal, x, w_qkv, w_o, dz, xt, dzt, ws,
-                           ws_bytes, dx_partial, dw_qkv, dw_o, stream=None) -> None:
+                           ws_bytes, dx_partial, dw_qkv, dw_o, stream=None, saved=None) -> None:
+    """``saved``: (q, k, vt, o, lse) from tp_shard_attn_save, or None (recompute)."""
+    sq, sk, svt, so, slse = saved if saved is not None else (None,) * 5
     _check(lib().tp_shard_attn_backward(batch, seq, h, hq, hkv, head_dim, rope_base, int(causal), _p(x), _p(w_qkv),
-                                        _p(w_o), _p(dz), _p(xt), _p(dzt), _p(ws), ws_bytes, _p(dx_partial),
-                                        _p(dw_qkv), _p(dw_o), _s(stream)))
+                                        _p(w_o), _p(dz), _p(xt), _p(dzt), _p(sq), _p(sk), _p(svt), _p(so),
+                                        _p(slse), _p(ws), ws_bytes, _p(dx_partial), _p(dw_qkv), _p(dw_o),
+                                        _s(stream)))
+
+
+def tp_shard_attn_save(batch, seq, h, hq, hkv, head_dim, rope_base, causal, x, w_qkv, w_o, q, k, vt, o, lse,
+                       partial, stream=None) -> None:
+    _check(lib().tp_shard_attn_save(batch, seq, h, hq, hkv, head_dim, rope_base, int(causal), _p(x), _p(w_qkv),
+                                    _p(w_o), _p(q), _p(k), _p(vt), _p(o), _p(lse), _p(partial), _s(stream)))
 
 
 def tp_transpose(rows, cols, src, dst, stream=None) -> None:

@@ -285,11 +285,19 @@ def test_mlp_backward_validation(L):
     ws = tp.tp_shard_mlp_backward_workspace_bytes("gelu", 16, 16, 32)
     assert ws > 0
     args = lambda act, m, wsb=ws, x=A16: status(  # noqa: E731
-        "tp_shard_mlp_backward", act, m, 16, 32, x, A16, A16, A16, None, None, A16, wsb, A16, A16, A16, None)
+        "tp_shard_mlp_backward", act, m, 16, 32, x, A16, A16, A16, None, None, None, A16, wsb, A16, A16, A16, None)
     assert args(0, 16) == tp.TP_ERR_INVALID_ARG          # needs an activation
     assert args(1, 12) == tp.TP_ERR_SHAPE                # m not a multiple of 8
     assert args(1, 16, wsb=ws - 1) == tp.TP_ERR_WORKSPACE
     assert args(1, 16, x=MIS) == tp.TP_ERR_INVALID_ARG
+    assert status("tp_shard_mlp_backward", 1, 16, 16, 32, A16, A16, A16, A16, None, None, MIS, A16, ws, A16, A16,
+                  A16, None) == tp.TP_ERR_INVALID_ARG                                 # misaligned saved pre
+    save = lambda act, n=16, pre=A16 + 8192, y=A16 + 4096: status(  # noqa: E731
+        "tp_colwise_save", act, 4, 16, n, A16, A16 + 12288, None, y, pre, None)
+    assert save(0) == tp.TP_ERR_INVALID_ARG                                           # needs a nonlinearity
+    assert save(1, pre=None) == tp.TP_ERR_INVALID_ARG
+    assert save(2, pre=A16 + 4096) == tp.TP_ERR_INVALID_ARG                          # pre aliases y
+    assert save(1, n=12) == tp.TP_ERR_SHAPE
     assert status("tp_transpose", 4, 4, A16, A16, None) == tp.TP_ERR_INVALID_ARG    # in place
     assert status("tp_transpose", 0, 4, None, None, None) == tp.TP_OK
     assert status("tp_mlp_act_backward", 0, 4, 16, A16, A16, A16, None, None) == tp.TP_ERR_INVALID_ARG
@@ -313,12 +321,16 @@ def test_attention_backward_validation(L):
     sws = tp.tp_shard_attn_backward_workspace_bytes(2, 64, 256, 4, 2, 128)
     assert sws > ws
     shard_bwd = lambda seq=64, wsb=sws, rope=500000.0, x=A16: status(  # noqa: E731
-        "tp_shard_attn_backward", 2, seq, 256, 4, 2, 128, rope, 1, x, A16, A16, A16, None, None, A16, wsb,
-        A16, A16, A16, None)
+        "tp_shard_attn_backward", 2, seq, 256, 4, 2, 128, rope, 1, x, A16, A16, A16, None, None, None, None, None,
+        None, None, A16, wsb, A16, A16, A16, None)
     assert shard_bwd(seq=63) == tp.TP_ERR_SHAPE           # batch * seq not a multiple of 8
     assert shard_bwd(rope=0.0) == tp.TP_ERR_INVALID_ARG
     assert shard_bwd(wsb=sws - 1) == tp.TP_ERR_WORKSPACE
     assert shard_bwd(x=MIS) == tp.TP_ERR_INVALID_ARG
+    assert status("tp_shard_attn_backward", 2, 64, 256, 4, 2, 128, 500000.0, 1, A16, A16, A16, A16, None, None,
+                  A16, A16, None, A16, A16, A16, sws, A16, A16, A16, None) == tp.TP_ERR_INVALID_ARG  # vt missing
+    assert status("tp_shard_attn_save", 2, 64, 256, 4, 2, 64, 500000.0, 1, A16, A16, A16, A16, A16, A16, A16, A16,
+                  A16, None) == tp.TP_ERR_UNSUPPORTED
     assert status("tp_flash_attn_backward", 0, 64, 4, 2, 128, 0.0, 1, None, None, None, None, None, None, None, 0,
                   None, 1024, None) == tp.TP_OK
 

@@ -554,6 +554,39 @@ def test_attention_backward(device, batch, seq, h, heads, kv, t):
     assert rel_err(host(dx), full["dx"]) <= BF16_TOL
 
 
+def test_saved_activation_backward_matches_recompute(device):
+    """The block backward after a forward that keeps every rank's activations
+    (the MLP's pre-activation from the GEMM epilogue, attention's Q, K, V^T, O
+    and log-sum-exp) is bitwise the backward that recomputes them; the saved
+    pre-activation is bitwise the recomputed one."""
+    case = inputs.BlockCase("saved", 2, 72, 256, 4, 2, 128, 512, 2, 500000.0, seed=94, gain_std=0.1)
+    say("case saved-activation block backward t=2")
+    w = inputs.gen_block(case)
+    dz = to_dev(inputs.normal(94, 20, (case.tokens, case.hidden), 1.0, "bf16"), device)
+    dw = {k: to_dev(v, device) for k, v in w.items()}
+    blk = shard.BlockShards(dw["X"], dw, case)
+    blk.forward()
+    z_plain = blk.mlp.out.clone()
+    blk.backward(dz)
+    ref = {"dx": blk.d_x.clone(), "dh1": blk.dh1.clone(), "dgm": blk.dg_mlp.clone(), "dga": blk.dg_attn.clone(),
+           "dwi": [t.clone() for t in blk.mlp.dw_in], "dwq": [t.clone() for t in blk.attn.dw_qkv],
+           "dwo": [t.clone() for t in blk.attn.dw_o]}
+    blk.forward(save=True)
+    assert torch.equal(blk.mlp.out, z_plain)  # the saving forward computes the same block
+    recomputed = torch.empty_like(blk.mlp.pre[1])
+    tp.tp_colwise("none", "bf16", case.tokens, case.hidden, 2 * blk.mlp.f_shard, blk.hn, blk.mlp.w_in[1], recomputed)
+    blk.backward(dz)
+    torch.cuda.synchronize()
+    assert torch.equal(blk.mlp.pre[1].view(torch.int16), recomputed.view(torch.int16))
+    for name, got, want in (("dx", blk.d_x, ref["dx"]), ("dh1", blk.dh1, ref["dh1"]), ("dg_mlp", blk.dg_mlp, ref["dgm"]),
+                            ("dg_attn", blk.dg_attn, ref["dga"])):
+        assert torch.equal(got, want), name
+    for r in range(case.t):
+        assert torch.equal(blk.mlp.dw_in[r], ref["dwi"][r])
+        assert torch.equal(blk.attn.dw_qkv[r], ref["dwq"][r])
+        assert torch.equal(blk.attn.dw_o[r], ref["dwo"][r])
+
+
 def test_flash_attn_backward_full_size_sampled(device):
     """The core backward at the 70B t = 8 rank's shape (4 sequences of 2048,
     8 query heads, 1 KV head, RoPE base 500000) in the configuration the
