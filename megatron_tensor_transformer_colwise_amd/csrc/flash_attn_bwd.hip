@@ -70,7 +70,7 @@ struct BwdArgs {
   bf16_t* dq;          // row r of dQ at dq + r * ld_dq, head j at column j*D
   float* part;         // [batch, hkv, nsplit, 2, seq_pad, D]
   int64_t ld_dq, seq, seq_pad;
-  int hq, hkv, batch, nqb, nsplit, causal;
+  int hq, hkv, batch, nsplit, causal;
   float scale_log2, scale;
   double log2_base;  // 0: no RoPE rotation
 };
@@ -115,21 +115,29 @@ __device__ __forceinline__ u32x4 c_to_b1(const uint32_t (&pk)[8], int hf) {
 
 // ---------------------------------------------------------------- dQ
 
-__global__ __launch_bounds__(NT, 1) void attn_bwd_dq_kernel(BwdArgs a) {
+// DQW waves of 32 queries per workgroup.  4 is launched: 8 (two waves per
+// SIMD, one wave's vector work beside the other's MFMAs) measured slower at
+// the 70B t = 8 shape (111 against 104 us), its 256 workgroups of 256
+// queries leaving the causal imbalance between query blocks uncovered.
+template <int DQW>
+__global__ __launch_bounds__(DQW * 64, 1) void attn_bwd_dq_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(1024))) char smem[DQ_LDS];
   const int lane = lane_id(), wave = wave_id();
   const int l31 = lane & 31, h = lane >> 5;
+  constexpr int QB = DQW * 32;     // queries per workgroup
+  constexpr int LI = 16 / DQW;     // 16 KiB tile loads per wave
 
   // heaviest query blocks first
   const int per_qb = a.hq * a.batch;
-  const int qb = a.nqb - 1 - (int)(blockIdx.x / per_qb);
+  const int nqb = (int)((a.seq + QB - 1) / QB);
+  const int qb = nqb - 1 - (int)(blockIdx.x / per_qb);
   const int rest = (int)(blockIdx.x % per_qb);
   const int j = rest % a.hq;
   const int b = rest / a.hq;
   const int g = j / (a.hq / a.hkv);
   const int64_t seq = a.seq, sp = a.seq_pad;
   const int64_t ldq = (int64_t)a.hq * D, ldk = (int64_t)a.hkv * D;
-  const int q0 = qb * 128;
+  const int q0 = qb * QB;
   const int qpos = q0 + wave * 32 + l31;
   const bool qok = qpos < seq;
 
@@ -153,13 +161,13 @@ __global__ __launch_bounds__(NT, 1) void attn_bwd_dq_kernel(BwdArgs a) {
       make_rsrc(a.k + (int64_t)b * seq * ldk + (int64_t)g * D, (uint32_t)(seq * ldk * 2));
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.vtok + ((int64_t)b * a.hkv + g) * sp * D, (uint32_t)(sp * D * 2));
   const __amdgpu_buffer_rsrc_t rkt = make_rsrc(a.kt + ((int64_t)b * a.hkv + g) * D * sp, (uint32_t)(D * sp * 2));
-  // load slots: s = (i*4 + wave)*64 + lane; row tiles: token s/16, physical
+  // load slots: s = (i*DQW + wave)*64 + lane; row tiles: token s/16, physical
   // chunk s%16; column tile: row d = s/8, physical chunk s%8
-  uint32_t k_off[4], v_off[4], t_off[4];
-  int row_of[4];
+  uint32_t k_off[LI], v_off[LI], t_off[LI];
+  int row_of[LI];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int s = (i * 4 + wave) * 64 + lane;
+  for (int i = 0; i < LI; ++i) {
+    const int s = (i * DQW + wave) * 64 + lane;
     const int row = s >> 4, ck = (s & 15) ^ swz_row(row);
     row_of[i] = row;
     k_off[i] = (uint32_t)((int64_t)row * ldk * 2 + ck * 16);
@@ -174,9 +182,9 @@ __global__ __launch_bounds__(NT, 1) void attn_bwd_dq_kernel(BwdArgs a) {
     char* st = smem + COLS + S * COL_TILE;
     const int kb = t * 64;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < LI; ++i) {
       const bool ok = kb + row_of[i] < seq;
-      const int slot = (i * 4 + wave) * 1024;
+      const int slot = (i * DQW + wave) * 1024;
       buffer_load_lds16(rk, sk + slot, ok ? k_off[i] + (uint32_t)((int64_t)kb * ldk * 2) : TP_OOB_OFFSET);
       buffer_load_lds16(rv, sv + slot, ok ? v_off[i] + (uint32_t)(kb * D * 2) : TP_OOB_OFFSET);
       buffer_load_lds16(rkt, st + slot, t_off[i] + (uint32_t)(kb * 2));
@@ -201,7 +209,7 @@ __global__ __launch_bounds__(NT, 1) void attn_bwd_dq_kernel(BwdArgs a) {
   f32x16 acc[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db) acc[db] = f32x16{};
-  const int64_t last_q = min<int64_t>((int64_t)q0 + 127, seq - 1);
+  const int64_t last_q = min<int64_t>((int64_t)q0 + QB - 1, seq - 1);
   const int n_kv = a.causal ? (int)(last_q / 64) + 1 : (int)((seq + 63) / 64);
   const int key_lim = a.causal ? min(qpos, (int)seq - 1) : (int)seq - 1;
 
@@ -609,14 +617,15 @@ hipError_t launch_flash_attn_bwd(int64_t batch, int64_t seq, int64_t seq_pad, in
   a.hq = hq;
   a.hkv = hkv;
   a.batch = (int)batch;
-  a.nqb = (int)((seq + 127) / 128);
   a.nsplit = nsplit;
   a.causal = causal ? 1 : 0;
   a.scale = 1.0f / sqrtf((float)D);
   a.scale_log2 = 1.4426950408889634f * a.scale;
   a.log2_base = log2_base;
   const int64_t nkb = (seq + 127) / 128;
-  hipLaunchKernelGGL(attn_bwd_dq_kernel, dim3((unsigned)((int64_t)a.nqb * hq * batch)), dim3(NT), 0, s, a);
+  constexpr int DQW = 4;
+  const int64_t nqb_dq = (seq + DQW * 32 - 1) / (DQW * 32);
+  hipLaunchKernelGGL(attn_bwd_dq_kernel<DQW>, dim3((unsigned)(nqb_dq * hq * batch)), dim3(DQW * 64), 0, s, a);
   hipLaunchKernelGGL(attn_bwd_dkdv_kernel, dim3((unsigned)(nkb * nsplit * hkv * batch)), dim3(NT), 0, s, a);
   const int64_t rows = batch * hkv * seq;
   bf16_t* base = reinterpret_cast<bf16_t*>(dqkv);
