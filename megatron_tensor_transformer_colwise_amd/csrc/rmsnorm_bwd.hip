@@ -151,9 +151,9 @@ __global__ __launch_bounds__(NT) void sum_rmsnorm_bwd_kernel(NormBwdArgs a) {
         o[k] = (rr * (gn[k] * dy[i][k]) - xv[i][k] * coef) + rv[i][k];
         dg[i][k] += dy[i][k] * (xv[i][k] * rr);
       }
-      if (a.dx) {
-        *reinterpret_cast<f32x4*>(a.dx + e) = f32x4{o[0], o[1], o[2], o[3]};
-        *reinterpret_cast<f32x4*>(a.dx + e + 4) = f32x4{o[4], o[5], o[6], o[7]};
+      if (a.dx) {  // the residual stream's gradient, next read a sublayer later: non-temporal
+        __builtin_nontemporal_store(f32x4{o[0], o[1], o[2], o[3]}, reinterpret_cast<f32x4*>(a.dx + e));
+        __builtin_nontemporal_store(f32x4{o[4], o[5], o[6], o[7]}, reinterpret_cast<f32x4*>(a.dx + e + 4));
       }
       if (a.dx_bf16)
         *reinterpret_cast<u32x4*>(a.dx_bf16 + e) =
