@@ -587,6 +587,44 @@ def test_saved_activation_backward_matches_recompute(device):
         assert torch.equal(blk.attn.dw_o[r], ref["dwo"][r])
 
 
+@pytest.mark.parametrize("act,m,h,f", [("gelu", 1000, 256, 1024), ("swiglu", 520, 384, 768)])
+def test_colwise_save_and_mlp_backward_from_it(device, act, m, h, f):
+    """tp_colwise_save's output equals tp_colwise's and its pre-activation the
+    plain GEMM's, bitwise, with and without a bias (ragged m, two rounds of
+    tiles); the MLP backward from the saved pre-activation equals the
+    recomputing backward bitwise."""
+    say(f"case colwise save {act} m={m} h={h} f={f}")
+    t = 2
+    case = inputs.MLPCase("save", m, h, f, t, act, "bf16", seed=95)
+    w = inputs.gen_mlp(case)
+    dw = {k: to_dev(v, device) for k, v in w.items()}
+    mlp = shard.MLPShards(dw["X"], dw, t, act)
+    fs = mlp.f_shard
+    fin = 2 * fs if act == "swiglu" else fs
+    for bias in (None, (0.1 * inputs.normal(95, 30, (fin,), 1.0, "f32").torch()).to(device)):
+        y0 = torch.empty(m, fs, dtype=torch.bfloat16, device=device)
+        y1 = torch.empty_like(y0)
+        pre = torch.empty(m, fin, dtype=torch.bfloat16, device=device)
+        tp.tp_colwise(act, "bf16", m, h, fs, dw["X"], mlp.w_in[0], y0, bias=bias)
+        tp.tp_colwise_save(act, m, h, fs, dw["X"], mlp.w_in[0], y1, pre, bias=bias)
+        plain = torch.empty(m, fin, dtype=torch.bfloat16, device=device)
+        tp.tp_colwise("none", "bf16", m, h, fin, dw["X"], mlp.w_in[0], plain,
+                      bias=None if bias is None else bias)
+        torch.cuda.synchronize()
+        assert torch.equal(y0.view(torch.int16), y1.view(torch.int16))
+        assert torch.equal(pre.view(torch.int16), plain.view(torch.int16))
+    dz = to_dev(inputs.normal(95, 9, (m, h), 1.0, "bf16"), device)
+    mlp.forward()
+    mlp.backward(dz)
+    ref = (mlp.dx.clone(), [a.clone() for a in mlp.dw_in], [a.clone() for a in mlp.dw_out])
+    mlp.forward(save=True)
+    mlp.backward(dz)
+    torch.cuda.synchronize()
+    assert torch.equal(mlp.dx, ref[0])
+    for r in range(t):
+        assert torch.equal(mlp.dw_in[r], ref[1][r]) and torch.equal(mlp.dw_out[r], ref[2][r])
+
+
 def test_flash_attn_backward_full_size_sampled(device):
     """The core backward at the 70B t = 8 rank's shape (4 sequences of 2048,
     8 query heads, 1 KV head, RoPE base 500000) in the configuration the
