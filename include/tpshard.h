@@ -424,13 +424,19 @@ tp_status tp_mlp_act_backward(tp_act act, int64_t m, int64_t n, const void* pre,
  *   dx            [m, h] float32 or NULL;  dx_bf16 [m, h] bf16 or NULL (not both)
  *   dgain         [h] float32 or NULL; then ws needs
  *                 tp_shard_sum_rmsnorm_backward_workspace_bytes(m, h) bytes
+ * The m = nrun * run_rows rows come in runs of run_rows rows, run_stride rows
+ * apart (row k of run j is row j * run_stride + k of every [., h] operand), as
+ * in tp_shard_sum_rmsnorm: a rank's slice of every sequence in the
+ * sequence-parallel form ("Sequence parallelism": the backward of the
+ * all-gather before the colwise GEMMs is a reduce-scatter onto the slices);
+ * then dgain covers those rows only.  nrun = 1, run_rows = m: all rows.
  * h must be a multiple of 8 and at most 8192.
  * ------------------------------------------------------------------------ */
 size_t tp_shard_sum_rmsnorm_backward_workspace_bytes(int64_t m, int64_t h);
-tp_status tp_shard_sum_rmsnorm_backward(int32_t t, int64_t m, int64_t h, const float* const* partials, const void* x,
-                                        tp_dtype x_dt, const float* gain, float eps, const void* residual_grad,
-                                        tp_dtype residual_dt, float* dx, void* dx_bf16, float* dgain, void* ws,
-                                        size_t ws_bytes, void* stream);
+tp_status tp_shard_sum_rmsnorm_backward(int32_t t, int64_t nrun, int64_t run_rows, int64_t run_stride, int64_t h,
+                                        const float* const* partials, const void* x, tp_dtype x_dt, const float* gain,
+                                        float eps, const void* residual_grad, tp_dtype residual_dt, float* dx,
+                                        void* dx_bf16, float* dgain, void* ws, size_t ws_bytes, void* stream);
 
 tp_status tp_flash_attn_lse(int64_t batch, int64_t seq, int32_t hq, int32_t hkv, int32_t head_dim,
                             int32_t causal, const void* q, const void* k, const void* vt, void* o, float* lse,

@@ -588,12 +588,15 @@ size_t tp_shard_sum_rmsnorm_backward_workspace_bytes(int64_t m, int64_t h) {
   return align256((size_t)tpk::norm_bwd_blocks(m) * (size_t)h * 4);
 }
 
-tp_status tp_shard_sum_rmsnorm_backward(int32_t t, int64_t m, int64_t h, const float* const* partials, const void* x,
-                                        tp_dtype x_dt, const float* gain, float eps, const void* residual_grad,
-                                        tp_dtype residual_dt, float* dx, void* dx_bf16, float* dgain, void* ws,
-                                        size_t ws_bytes, void* stream) {
+tp_status tp_shard_sum_rmsnorm_backward(int32_t t, int64_t nrun, int64_t run_rows, int64_t run_stride, int64_t h,
+                                        const float* const* partials, const void* x, tp_dtype x_dt, const float* gain,
+                                        float eps, const void* residual_grad, tp_dtype residual_dt, float* dx,
+                                        void* dx_bf16, float* dgain, void* ws, size_t ws_bytes, void* stream) {
   if (t < 1 || t > TP_MAX_SHARDS) return fail(TP_ERR_SHAPE, "t = %d outside 1..%d", t, TP_MAX_SHARDS);
-  if (m < 0) return fail(TP_ERR_SHAPE, "m = %lld is negative", (long long)m);
+  if (nrun < 0 || run_rows < 0) return fail(TP_ERR_SHAPE, "nrun and run_rows must be >= 0");
+  if (nrun > 1 && run_stride < run_rows)
+    return fail(TP_ERR_SHAPE, "run_stride = %lld < run_rows = %lld", (long long)run_stride, (long long)run_rows);
+  const int64_t m = nrun * run_rows;
   TRY(check_dim8(h, "h"));
   if (h > 8192) return fail(TP_ERR_SHAPE, "h = %lld: the norm backward keeps rows of at most 8192 in registers",
                             (long long)h);
@@ -627,9 +630,9 @@ tp_status tp_shard_sum_rmsnorm_backward(int32_t t, int64_t m, int64_t h, const f
     if (ws_bytes < need) return fail(TP_ERR_WORKSPACE, "workspace of %zu bytes < %zu needed", ws_bytes, need);
   }
   TRY(device_check());
-  return launched(tpk::launch_sum_rmsnorm_bwd(t, m, h, partials, x, x_dt == TP_BF16, gain, eps, residual_grad,
-                                              residual_dt == TP_BF16, dx, dx_bf16, dgain, static_cast<float*>(ws),
-                                              as_stream(stream)),
+  return launched(tpk::launch_sum_rmsnorm_bwd(t, nrun, run_rows, run_stride, h, partials, x, x_dt == TP_BF16, gain,
+                                              eps, residual_grad, residual_dt == TP_BF16, dx, dx_bf16, dgain,
+                                              static_cast<float*>(ws), as_stream(stream)),
                   "tp_shard_sum_rmsnorm_backward");
 }
 

@@ -135,10 +135,12 @@ hipError_t launch_transpose_batched(int64_t n1, int64_t n2, int64_t rows_in, int
 // Backward of the fused sum + RMSNorm: dy = sum of the t partials (ascending),
 // dx = r gain dy - x r^3 sum(gain dy x) / h (+ res), per row; dgain = sum over
 // rows of dy x r (ws: norm_bwd_blocks(m) * h float32 partials).  h <= 8192.
+// m = nrun * run_rows rows, in runs of run_rows run_stride apart.
 int64_t norm_bwd_blocks(int64_t m);
-hipError_t launch_sum_rmsnorm_bwd(int t, int64_t m, int64_t h, const float* const* partials, const void* x,
-                                  int x_bf16, const float* gain, float eps, const void* res, int res_bf16, float* dx,
-                                  void* dx_bf16, float* dgain, float* ws, hipStream_t s);
+hipError_t launch_sum_rmsnorm_bwd(int t, int64_t nrun, int64_t run_rows, int64_t run_stride, int64_t h,
+                                  const float* const* partials, const void* x, int x_bf16, const float* gain,
+                                  float eps, const void* res, int res_bf16, float* dx, void* dx_bf16, float* dgain,
+                                  float* ws, hipStream_t s);
 
 // From the pre-activation and dY (n columns): dPre and, if y, the activation
 // Y.  GeLU: pre [m, n]; SwiGLU: pre [m, 2n] = [gate | up], dPre likewise.

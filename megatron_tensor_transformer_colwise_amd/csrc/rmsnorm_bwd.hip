@@ -8,6 +8,8 @@
 //   dx = r g - x r^3 (sum_c g x) / h  (+ the gradient arriving through the
 //        residual path)
 //   dgain = sum over rows of dy * x * r
+// Rows may come as runs (run_rows rows, run_stride apart: a rank's slice of
+// every sequence in the sequence-parallel form), as in the forward.
 // One workgroup walks a run of consecutive rows, keeping each row's dy and x
 // in registers between the row's reduction and its output (h <= 8192), and
 // accumulating its columns' dgain terms across the run; a second kernel sums
@@ -31,6 +33,7 @@ struct NormBwdArgs {
   bf16_t* dx_bf16;     // bf16 rows, or NULL
   float* dg_part;      // [blocks, h] dgain partials, or NULL
   int64_t m, h, rows_per_block;
+  int64_t run_rows, run_stride;  // logical row r is row (r / run_rows) * run_stride + r % run_rows
   float eps;
   int x_bf16, res_bf16;
 };
@@ -84,7 +87,7 @@ __global__ __launch_bounds__(NT) void sum_rmsnorm_bwd_kernel(NormBwdArgs a) {
     }
   };
   for (int64_t r = r0; r < r1; ++r) {
-    const int64_t base = r * h;
+    const int64_t base = ((r / a.run_rows) * a.run_stride + r % a.run_rows) * h;
     float dy[MAXC][8], xv[MAXC][8], rv[MAXC][8];
     float sxx = 0.0f, sgx = 0.0f;
 #pragma unroll
@@ -211,9 +214,11 @@ int64_t norm_bwd_blocks(int64_t m) {
   return (m + rpb - 1) / rpb;
 }
 
-hipError_t launch_sum_rmsnorm_bwd(int t, int64_t m, int64_t h, const float* const* partials, const void* x,
-                                  int x_bf16, const float* gain, float eps, const void* res, int res_bf16, float* dx,
-                                  void* dx_bf16, float* dgain, float* ws, hipStream_t s) {
+hipError_t launch_sum_rmsnorm_bwd(int t, int64_t nrun, int64_t run_rows, int64_t run_stride, int64_t h,
+                                  const float* const* partials, const void* x, int x_bf16, const float* gain,
+                                  float eps, const void* res, int res_bf16, float* dx, void* dx_bf16, float* dgain,
+                                  float* ws, hipStream_t s) {
+  const int64_t m = nrun * run_rows;
   if (m == 0) return hipSuccess;
   if (t < 1 || t > 16 || h % 8 != 0 || h > (int64_t)MAXC * NT * 8) return hipErrorInvalidValue;
   NormBwdArgs a;
@@ -227,6 +232,8 @@ hipError_t launch_sum_rmsnorm_bwd(int t, int64_t m, int64_t h, const float* cons
   a.m = m;
   a.h = h;
   a.rows_per_block = norm_bwd_rows_per_block(m, dgain != nullptr);
+  a.run_rows = run_rows;
+  a.run_stride = nrun > 1 ? run_stride : run_rows;
   a.eps = eps;
   a.x_bf16 = x_bf16;
   a.res_bf16 = res_bf16;

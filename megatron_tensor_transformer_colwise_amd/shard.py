@@ -415,6 +415,44 @@ class BlockShards:
                                     self.mlp.out[o:], None, eps, None, stream, runs=runs)
         return self.mlp.out
 
+    def backward_sp(self, dz, stream=None):
+        """The sequence-parallel form's backward ("Sequence parallelism": the
+        backward of the all-gather before the colwise GEMMs is a reduce-scatter
+        onto the slices, that of the reduce-scatter after the rowwise GEMMs an
+        all-gather).  Every rank reads the whole dZ (the gathered slices; one
+        shared buffer on one device); per rank, one launch sums the MLP ranks'
+        dX partials over its slice, takes the MLP norm's gradient there and
+        adds dZ (its slice of dh1, written into the shared, gathered dh1); the
+        attention ranks' backward for dh1; one launch per rank for its slice of
+        dX.  dX and dh1 are bitwise those of ``backward`` (row-local steps);
+        each gain's gradient is the sum over the ranks' slices (an all-reduce
+        in ascending rank order)."""
+        self._bwd_buffers()
+        t, h, eps = self.t, self.h, self.case.eps
+        runs = self.sp_runs()
+        n = runs[1]
+        ms = runs[0] * n
+        if getattr(self, "dg_sp", None) is None:
+            self.dg_sp = torch.empty(2, t, h, dtype=torch.float32, device=self.x.device)
+        for r in range(t):
+            self.mlp.backward_rank(r, dz, stream)
+        mp, ap = self.mlp.dx_partials, self.attn.dx_partials
+        for r in range(t):
+            o = r * n
+            tp.tp_shard_sum_rmsnorm_backward(t, ms, h, [mp[i][o:] for i in range(t)], self.attn.out[o:], "f32",
+                                             self.g_mlp, eps, dz[o:], "bf16", self.dh1[o:], self.dh1_bf16[o:],
+                                             self.dg_sp[0, r], self.norm_ws, self.norm_ws_bytes, stream, runs=runs)
+        for r in range(t):
+            self.attn.backward_rank(r, self.dh1_bf16, stream=stream)
+        for r in range(t):
+            o = r * n
+            tp.tp_shard_sum_rmsnorm_backward(t, ms, h, [ap[i][o:] for i in range(t)], self.x[o:], "bf16",
+                                             self.g_attn, eps, self.dh1[o:], "f32", self.d_x[o:], None,
+                                             self.dg_sp[1, r], self.norm_ws, self.norm_ws_bytes, stream, runs=runs)
+        tp.tp_shard_sum(t, h, list(self.dg_sp[0]), None, "f32", self.dg_mlp, stream)
+        tp.tp_shard_sum(t, h, list(self.dg_sp[1]), None, "f32", self.dg_attn, stream)
+        return self.d_x
+
 
 # ---------------------------------------------------------------- packed (fused) projections
 

@@ -66,8 +66,8 @@ _SIGS = {
     "tp_transpose": [_i64, _i64, _vp, _vp, _vp],
     "tp_mlp_act_backward": [_i32, _i64, _i64, _vp, _vp, _vp, _vp, _vp],
     "tp_shard_sum_rmsnorm_backward_workspace_bytes": [_i64, _i64],
-    "tp_shard_sum_rmsnorm_backward": [_i32, _i64, _i64, ctypes.POINTER(_vp), _vp, _i32, _vp, _f32, _vp, _i32, _vp,
-                                      _vp, _vp, _vp, ctypes.c_size_t, _vp],
+    "tp_shard_sum_rmsnorm_backward": [_i32, _i64, _i64, _i64, _i64, ctypes.POINTER(_vp), _vp, _i32, _vp, _f32, _vp,
+                                      _i32, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp],
     "tp_flash_attn_lse": [_i64, _i64, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp],
     "tp_flash_attn_backward_workspace_bytes": [_i64, _i64, _i32, _i32, _i32],
     "tp_flash_attn_backward": [_i64, _i64, _i32, _i32, _i32, _f32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
@@ -226,11 +226,13 @@ def tp_shard_sum_rmsnorm_backward_workspace_bytes(m, h) -> int:
 
 
 def tp_shard_sum_rmsnorm_backward(t, m, h, partials, x, x_dt, gain, eps, residual_grad, residual_dt, dx, dx_bf16,
-                                  dgain, ws, ws_bytes, stream=None) -> None:
+                                  dgain, ws, ws_bytes, stream=None, runs=None) -> None:
+    """m rows (one run), or ``runs = (nrun, run_rows, run_stride)``."""
+    nrun, run_rows, run_stride = runs if runs is not None else (1, m, m)
     arr = (_vp * max(len(partials), 1))(*[_p(p) for p in partials])
-    _check(lib().tp_shard_sum_rmsnorm_backward(t, m, h, arr, _p(x), _e(x_dt, DTYPES), _p(gain), eps,
-                                               _p(residual_grad), _e(residual_dt, DTYPES), _p(dx), _p(dx_bf16),
-                                               _p(dgain), _p(ws), ws_bytes, _s(stream)))
+    _check(lib().tp_shard_sum_rmsnorm_backward(t, nrun, run_rows, run_stride, h, arr, _p(x), _e(x_dt, DTYPES),
+                                               _p(gain), eps, _p(residual_grad), _e(residual_dt, DTYPES), _p(dx),
+                                               _p(dx_bf16), _p(dgain), _p(ws), ws_bytes, _s(stream)))
 
 
 def tp_embedding(m, w, v_start, v_rows, ids, table, out, ld, stream=None) -> None:

@@ -341,7 +341,7 @@ def test_norm_backward_validation(L):
     arr = (ctypes.c_void_p * 2)(A16, A16 + 4096)
     f = lambda t=2, m=16, h=64, x=A16 + 8192, xdt=1, eps=1e-5, res=None, rdt=0, dx=A16 + 12288, dxb=None, \
         dg=None, w=None, wsb=0: status(  # noqa: E731
-        "tp_shard_sum_rmsnorm_backward", t, m, h, arr, x, xdt, None, eps, res, rdt, dx, dxb, dg, w, wsb, None)
+        "tp_shard_sum_rmsnorm_backward", t, 1, m, m, h, arr, x, xdt, None, eps, res, rdt, dx, dxb, dg, w, wsb, None)
     assert f(t=0) == tp.TP_ERR_SHAPE
     assert f(t=17) == tp.TP_ERR_SHAPE
     assert f(h=60) == tp.TP_ERR_SHAPE
@@ -355,3 +355,5 @@ def test_norm_backward_validation(L):
     assert f(dg=A16 + 16384, w=A16 + 20480, wsb=ws - 1) == tp.TP_ERR_WORKSPACE
     assert f(x=MIS) == tp.TP_ERR_INVALID_ARG
     assert f(m=0, x=None, dx=None) == tp.TP_OK
+    assert status("tp_shard_sum_rmsnorm_backward", 2, 4, 8, 4, 64, arr, A16 + 8192, 1, None, 1e-5, None, 0,
+                  A16 + 12288, None, None, None, 0, None) == tp.TP_ERR_SHAPE  # run_stride < run_rows

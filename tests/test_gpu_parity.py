@@ -625,6 +625,30 @@ def test_colwise_save_and_mlp_backward_from_it(device, act, m, h, f):
         assert torch.equal(mlp.dw_in[r], ref[1][r]) and torch.equal(mlp.dw_out[r], ref[2][r])
 
 
+@pytest.mark.parametrize("t", [2, 4])
+def test_sequence_parallel_backward(device, t):
+    """The sequence-parallel backward (per-rank norm backwards over each rank's
+    slice of every sequence) gives dX and dh1 bitwise equal to the replicated
+    backward, and the gains' gradients (summed over the ranks' slices) within
+    float32 rounding of it."""
+    case = inputs.BlockCase("spbwd", 2, 128, 256, 4, 2, 128, 512, t, 500000.0, seed=96, gain_std=0.1)
+    say(f"case sequence-parallel backward t={t}")
+    w = inputs.gen_block(case)
+    dz = to_dev(inputs.normal(96, 20, (case.tokens, case.hidden), 1.0, "bf16"), device)
+    dw = {k: to_dev(v, device) for k, v in w.items()}
+    blk = shard.BlockShards(dw["X"], dw, case)
+    blk.forward()
+    blk.backward(dz)
+    ref = (blk.d_x.clone(), blk.dh1.clone(), blk.dh1_bf16.clone(), blk.dg_mlp.clone(), blk.dg_attn.clone())
+    blk.d_x.fill_(float("nan"))
+    blk.dh1.fill_(float("nan"))
+    blk.backward_sp(dz)
+    torch.cuda.synchronize()
+    assert torch.equal(blk.d_x, ref[0]) and torch.equal(blk.dh1, ref[1]) and torch.equal(blk.dh1_bf16, ref[2])
+    assert rel_err(host(blk.dg_mlp), host(ref[3])) <= 1e-5
+    assert rel_err(host(blk.dg_attn), host(ref[4])) <= 1e-5
+
+
 def test_flash_attn_backward_full_size_sampled(device):
     """The core backward at the 70B t = 8 rank's shape (4 sequences of 2048,
     8 query heads, 1 KV head, RoPE base 500000) in the configuration the
