@@ -264,6 +264,11 @@ def per_config_report(dev):
         blk.backward(dz)
         sstep, smin = _time(lambda: blk.backward(dz), reps=3, warm=1)
         sfl = case.t * block_backward_flops(case, case.t, saved=True)
+        blk.forward()
+        blk.backward_sp(dz)
+        spb, _ = _time(lambda: blk.backward_sp(dz), reps=3, warm=1)
+        rec.update({"sequence_parallel_backward_step_ms": round(spb, 3),
+                    "sequence_parallel_backward_step_tflops": rate(bfl, spb)})
         rec.update({"saving_forward_step_ms": round(fsv, 3),
                     "saved_backward_step_ms": round(sstep, 3), "saved_backward_step_min_ms": round(smin, 3),
                     "saved_backward_step_tflops": rate(sfl, sstep)})
