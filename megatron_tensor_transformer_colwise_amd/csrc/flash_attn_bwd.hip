@@ -113,6 +113,13 @@ __device__ __forceinline__ u32x4 c_to_b1(const uint32_t (&pk)[8], int hf) {
   return u32x4{s0[0], s1[0], s0[1], s1[1]};
 }
 
+// Zeroes [off, off + bytes) of the workgroup's LDS (16 bytes per thread and step).
+template <int NTH>
+__device__ __forceinline__ void lds_zero(char* smem, int off, int bytes) {
+  for (int o = off + (int)threadIdx.x * 16; o < off + bytes; o += NTH * 16)
+    *reinterpret_cast<u32x4*>(smem + o) = u32x4{0, 0, 0, 0};
+}
+
 // ---------------------------------------------------------------- dQ
 
 // DQW waves of 32 queries per workgroup.  4 is launched: 8 (two waves per
@@ -266,7 +273,11 @@ __global__ __launch_bounds__(DQW * 64, 1) void attn_bwd_dq_kernel(BwdArgs a) {
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  // tiles in pairs, both always run (see the dK/dV kernel)
+  // tiles in pairs, both always run (see the dK/dV kernel).  Stage 1 starts
+  // zeroed: a one-tile walk runs its masked second tile there, and its zero
+  // dS must not meet stale non-finite LDS bits (0 x NaN is NaN).
+  lds_zero<DQW * 64>(smem, 2 * ROW_TILE, 2 * ROW_TILE);
+  lds_zero<DQW * 64>(smem, COLS + COL_TILE, COL_TILE);
   load_tile(st0, 0);
   for (int t = 0; t < n_kv; t += 2) {
     kv_tile(st0, t);
@@ -486,7 +497,12 @@ __global__ __launch_bounds__(NT, 1) void attn_bwd_dkdv_kernel(BwdArgs a) {
     }
   };
   // tiles in pairs, both always run: a conditional second tile would make the
-  // compiler copy the accumulators between register files at the join
+  // compiler copy the accumulators between register files at the join.
+  // Stage 1 starts zeroed: a one-tile walk runs its masked second tile there,
+  // and its zero P and dS must not meet stale non-finite LDS bits (0 x NaN).
+  lds_zero<NT>(smem, 2 * ROW_TILE, 2 * ROW_TILE);
+  lds_zero<NT>(smem, COLS + 2 * COL_TILE, 2 * COL_TILE);
+  lds_zero<NT>(smem, COLS + 4 * COL_TILE + 2 * VEC_TILE, 2 * VEC_TILE);
   load_tile(st0, 0);
   for (int it = 0; it < n_it; it += 2) {
     q_tile(st0, it);

@@ -649,6 +649,35 @@ def test_sequence_parallel_backward(device, t):
     assert rel_err(host(blk.dg_attn), host(ref[4])) <= 1e-5
 
 
+def test_flash_attn_backward_one_tile_after_nan_lds(device):
+    """Regression: workgroups that walk a single tile also run a fully masked
+    second tile on their second LDS stage.  A GEMM over NaN inputs first
+    leaves non-finite bits in every CU's LDS; a 64-token backward (one tile
+    per workgroup, one head per KV group) must still match the oracle."""
+    say("case flash backward after NaN-laden LDS")
+    m, k, n = 4096, 2048, 4096
+    xn = torch.full((m, k), float("nan"), dtype=torch.bfloat16, device=device)
+    wn = torch.full((n, k), float("nan"), dtype=torch.bfloat16, device=device)
+    yn = torch.empty(m, n, dtype=torch.bfloat16, device=device)
+    batch, seq, hq, hkv, d = 8, 64, 4, 4, 128
+    t_in = _attn_core_inputs(device, batch, seq, hq, hkv, 97)
+    tp.tp_colwise("none", "bf16", m, k, n, xn, wn, yn)
+    _, _, dqkv = _attn_core_backward(device, batch, seq, hq, hkv, True, 0.0, t_in)
+    got = host(dqkv)[:, :(hq + 2 * hkv) * d]
+    assert np.all(np.isfinite(got))
+    qh, kh, vh, doh = (t_in[x].double().numpy() for x in ("q", "k", "v", "do"))
+    ref = np.zeros_like(got)
+    for b in range(batch):
+        rows = slice(b * seq, (b + 1) * seq)
+        for j in range(hq):
+            dq, dk, dv = oracle.causal_attention_backward(qh[rows, j * d:(j + 1) * d], kh[rows, j * d:(j + 1) * d],
+                                                          vh[rows, j * d:(j + 1) * d], doh[rows, j * d:(j + 1) * d])
+            ref[rows, j * d:(j + 1) * d] = dq
+            ref[rows, (hq + j) * d:(hq + j + 1) * d] = dk
+            ref[rows, (2 * hq + j) * d:(2 * hq + j + 1) * d] = dv
+    assert rel_err(got, ref) <= BF16_TOL
+
+
 def test_flash_attn_backward_full_size_sampled(device):
     """The core backward at the 70B t = 8 rank's shape (4 sequences of 2048,
     8 query heads, 1 KV head, RoPE base 500000) in the configuration the
