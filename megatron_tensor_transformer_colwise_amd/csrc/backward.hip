@@ -48,9 +48,10 @@ __global__ __launch_bounds__(NT) void transpose_kernel(const bf16_t* src, bf16_t
 // layouts.  Per batch z = z1 * n2 + z2 (blockIdx.z; src starts at
 // z1 * src_bs1 + z2 * src_bs2, dst at z1 * dst_bs1 + z2 * dst_bs2):
 //   dst[c * ldd + r] = r < rows_in ? src[r * lds + c] : 0,  r < rows_out, c < cols
-// A thread reads 8 consecutive elements of a source row into LDS (rows padded
-// by 8 elements, so the column reads spread over the banks) and writes 8
+// A thread reads 8 consecutive elements of a source row into LDS and writes 8
 // consecutive elements of a destination row, gathered down an LDS column.
+// The 16-byte chunk k of tile row r sits at chunk position k ^ ((r / 8) % 8),
+// so the rows 8 apart that one column read touches fall in different banks.
 // rows_out must be a multiple of 8; a source row is read in chunks of 8 from
 // c = 0, so up to 7 elements past cols are read (the caller keeps them in
 // bounds: cols a multiple of 8, or padding after each row).
@@ -58,8 +59,7 @@ __global__ __launch_bounds__(NT) void transpose16_kernel(const bf16_t* src, bf16
                                                          int64_t rows_out, int64_t cols, int64_t lds, int64_t ldd,
                                                          int n2, int64_t src_bs1, int64_t src_bs2, int64_t dst_bs1,
                                                          int64_t dst_bs2) {
-  constexpr int PAD = TT + 8;
-  __shared__ bf16_t tile[TT][PAD];
+  __shared__ __attribute__((aligned(16))) bf16_t tile[TT][TT];
   const int64_t z1 = blockIdx.z / n2, z2 = blockIdx.z % n2;
   src += z1 * src_bs1 + z2 * src_bs2;
   dst += z1 * dst_bs1 + z2 * dst_bs2;
@@ -70,7 +70,7 @@ __global__ __launch_bounds__(NT) void transpose16_kernel(const bf16_t* src, bf16
     const int r = idx >> 3, ch = (idx & 7) * 8;
     u32x4 v = {0, 0, 0, 0};
     if (r0 + r < rows_in && c0 + ch < cols) v = *reinterpret_cast<const u32x4*>(src + (r0 + r) * lds + c0 + ch);
-    *reinterpret_cast<u32x4*>(&tile[r][ch]) = v;
+    *reinterpret_cast<u32x4*>(&tile[r][(((ch >> 3) ^ ((r >> 3) & 7)) << 3)]) = v;
   }
   __syncthreads();
 #pragma unroll
@@ -78,10 +78,12 @@ __global__ __launch_bounds__(NT) void transpose16_kernel(const bf16_t* src, bf16
     const int idx = threadIdx.x + k * NT;  // destination: 64 rows (source columns) x 8 chunks
     const int c = idx >> 3, rr = (idx & 7) * 8;
     if (c0 + c < cols && r0 + rr < rows_out) {
+      // rows rr .. rr + 7 share rr / 8, so one swizzled column position
+      const int cs = ((((c >> 3) ^ ((rr >> 3) & 7)) << 3) | (c & 7));
       uint32_t w[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        w[e] = (uint32_t)tile[rr + 2 * e][c] | ((uint32_t)tile[rr + 2 * e + 1][c] << 16);
+        w[e] = (uint32_t)tile[rr + 2 * e][cs] | ((uint32_t)tile[rr + 2 * e + 1][cs] << 16);
       *reinterpret_cast<u32x4*>(dst + (c0 + c) * ldd + r0 + rr) = u32x4{w[0], w[1], w[2], w[3]};
     }
   }
