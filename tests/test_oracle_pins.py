@@ -517,6 +517,46 @@ def test_packed_single_stream_identity_and_naive_cut(causal):
     assert np.max(np.abs(oracle.full_attention(q, k, v) - sd.numpy())) < 1e-12
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_packed_single_stream_against_named_blocks(causal):
+    """The packed single-stream block against a forward written in torch from
+    separately drawn Q, K, V, gate and up projections and separate attention
+    and MLP out-projections, packed in the guide's order ("Fused
+    projections": in-projection blocks [Q, K, V, gate, up] = [1, 1, 1, 3, 3],
+    out-projection inputs [attention, MLP] = [1, 3]).  A Q/K, K/V or
+    gate/up mix-up in the oracle's reading of the packed columns, or
+    attention and MLP rows read in the other order, fails here: the scores
+    q k^T are not symmetric in q and k, and SiLU(g) u is not SiLU(u) g."""
+    r = np.random.default_rng(29)
+    h, d, heads, batch, seq, base = 32, 8, 4, 2, 6, 1000.0
+    x = r.standard_normal((batch * seq, h))
+    wq, wk, wv = (r.standard_normal((h, h)) * 0.3 for _ in range(3))
+    wg, wu = (r.standard_normal((h, 3 * h)) * 0.3 for _ in range(2))
+    wo_attn, wo_mlp = r.standard_normal((h, h)) * 0.3, r.standard_normal((3 * h, h)) * 0.3
+    w_in = np.concatenate([wq, wk, wv, wg, wu], axis=1)
+    w_out = np.concatenate([wo_attn, wo_mlp], axis=0)
+
+    T = torch.from_numpy
+    tx = T(x)
+
+    def heads_of(y):
+        return y.reshape(batch, seq, heads, d).transpose(1, 2)
+
+    q = _torch_rope(heads_of(tx @ T(wq)), base)
+    k = _torch_rope(heads_of(tx @ T(wk)), base)
+    v = heads_of(tx @ T(wv))
+    o = F.scaled_dot_product_attention(q, k, v, is_causal=causal).transpose(1, 2).reshape(batch * seq, h)
+    mlp = F.silu(tx @ T(wg)) * (tx @ T(wu))
+    ref = (o @ T(wo_attn) + mlp @ T(wo_mlp)).numpy()
+
+    got = oracle.single_stream_partial(x, w_in, w_out, heads, d, batch, seq, base, causal=causal)
+    assert np.max(np.abs(got - ref)) < 1e-12 * np.max(np.abs(ref))
+    for t in (2, 4):
+        z = oracle.shard_sum([oracle.single_stream_partial(x, w_in, w_out, heads, d, batch, seq, base, t, rk,
+                                                           causal) for rk in range(t)])
+        assert np.max(np.abs(z - ref)) < 1e-12 * np.max(np.abs(ref))
+
+
 # ---------------------------------------------------------------- vocabulary parallel
 
 
@@ -781,6 +821,10 @@ def test_block_backward_against_autograd(t):
     h1 = tw["X"] + o.transpose(1, 2).reshape(b * s, hd * d) @ tw["Wo"]
     hn = F.rms_norm(h1, (hid,), tw["g_mlp"], eps=case.eps)
     z = h1 + (F.silu(hn @ tw["W1"]) * (hn @ tw["W3"])) @ tw["W2"]
+    # the oracle's forward of the same block, rank by rank, against the torch one
+    fwd = oracle.block(x, w, case, t)
+    assert np.max(np.abs(fwd["h1"] - h1.detach().numpy())) < 1e-12 * float(np.max(np.abs(fwd["h1"])))
+    assert np.max(np.abs(fwd["z"] - z.detach().numpy())) < 1e-12 * float(np.max(np.abs(fwd["z"])))
     z.backward(torch.from_numpy(dz))
     got = oracle.block_backward(x, w, case, dz, t)
     scale = lambda g: max(1.0, float(np.max(np.abs(g))))  # noqa: E731
