@@ -200,11 +200,13 @@ size_t tp_shard_attn_workspace_bytes(int64_t batch, int64_t seq, int32_t hq, int
  * One rank's attention sublayer: tp_qkv_rope, tp_flash_attn, then the
  * row-parallel o_proj to a float32 partial ("Self-attention" section).
  *
+ *   dt       TP_BF16 (the only attention built; TP_F32 returns
+ *            TP_ERR_UNSUPPORTED before anything is enqueued)
  *   w_o      [h, hq*d]   rows of Wo for this rank's heads, transposed
  *   ws       workspace of at least tp_shard_attn_workspace_bytes(...) bytes
  *   partial  [batch*seq, h] float32, overwritten
  * ------------------------------------------------------------------------ */
-tp_status tp_shard_attn(int64_t batch, int64_t seq, int64_t h, int32_t hq, int32_t hkv,
+tp_status tp_shard_attn(tp_dtype dt, int64_t batch, int64_t seq, int64_t h, int32_t hq, int32_t hkv,
                         int32_t head_dim, float rope_base, int32_t causal, const void* x,
                         const void* w_qkv, const void* w_o, void* ws, size_t ws_bytes,
                         float* partial, void* stream);

@@ -642,10 +642,12 @@ size_t tp_shard_attn_workspace_bytes(int64_t batch, int64_t seq, int32_t hq, int
   return attn_layout(batch, seq, hq, hkv, head_dim).total;
 }
 
-tp_status tp_shard_attn(int64_t batch, int64_t seq, int64_t h, int32_t hq, int32_t hkv,
+tp_status tp_shard_attn(tp_dtype dt, int64_t batch, int64_t seq, int64_t h, int32_t hq, int32_t hkv,
                         int32_t head_dim, float rope_base, int32_t causal, const void* x,
                         const void* w_qkv, const void* w_o, void* ws, size_t ws_bytes,
                         float* partial, void* stream) {
+  if (dt == TP_F32) return fail(TP_ERR_UNSUPPORTED, "tp_shard_attn: only bf16 attention is built");
+  if (dt != TP_BF16) return fail(TP_ERR_INVALID_ARG, "unknown dtype %d", (int)dt);
   TRY(check_attn_shape(batch, seq, hq, hkv, head_dim));
   const int64_t m = batch * seq;
   const int64_t qd = (int64_t)hq * head_dim;

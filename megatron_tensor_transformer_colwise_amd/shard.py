@@ -215,7 +215,7 @@ class AttnShards:
 
     def rank(self, r: int, x=None, stream=None) -> None:
         rk = self.ranks[r]
-        tp.tp_shard_attn(self.batch, self.seq, self.h, rk.hq, rk.hkv, self.d, self.case.rope_base,
+        tp.tp_shard_attn("bf16", self.batch, self.seq, self.h, rk.hq, rk.hkv, self.d, self.case.rope_base,
                          self.causal, self.x if x is None else x, rk.w_qkv, rk.w_o, self.ws,
                          self.ws_bytes, self.partials[r], stream)
 

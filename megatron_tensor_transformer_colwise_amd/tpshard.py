@@ -51,7 +51,7 @@ _SIGS = {
     "tp_qkv_rope": [_i64, _i64, _i64, _i32, _i32, _i32, _f32, _vp, _vp, _vp, _vp, _vp, _vp, _vp],
     "tp_flash_attn": [_i64, _i64, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp],
     "tp_shard_attn_workspace_bytes": [_i64, _i64, _i32, _i32, _i32],
-    "tp_shard_attn": [_i64, _i64, _i64, _i32, _i32, _i32, _f32, _i32, _vp, _vp, _vp, _vp,
+    "tp_shard_attn": [_i32, _i64, _i64, _i64, _i32, _i32, _i32, _f32, _i32, _vp, _vp, _vp, _vp,
                       ctypes.c_size_t, _vp, _vp],
     "tp_shard_sum": [_i32, _i64, ctypes.POINTER(_vp), _vp, _i32, _vp, _vp],
     "tp_rmsnorm": [_i32, _i64, _i64, _vp, _vp, _f32, _vp, _vp],
@@ -197,9 +197,9 @@ def tp_shard_attn_workspace_bytes(batch, seq, hq, hkv, head_dim) -> int:
     return int(lib().tp_shard_attn_workspace_bytes(batch, seq, hq, hkv, head_dim))
 
 
-def tp_shard_attn(batch, seq, h, hq, hkv, head_dim, rope_base, causal, x, w_qkv, w_o, ws, ws_bytes,
+def tp_shard_attn(dt, batch, seq, h, hq, hkv, head_dim, rope_base, causal, x, w_qkv, w_o, ws, ws_bytes,
                   partial, stream=None) -> None:
-    _check(lib().tp_shard_attn(batch, seq, h, hq, hkv, head_dim, rope_base, int(causal), _p(x),
+    _check(lib().tp_shard_attn(_e(dt, DTYPES), batch, seq, h, hq, hkv, head_dim, rope_base, int(causal), _p(x),
                                _p(w_qkv), _p(w_o), _p(ws), ws_bytes, _p(partial), _s(stream)))
 
 

@@ -74,11 +74,15 @@ def test_shard_mlp_needs_an_activation(L):
 def test_attention_validation(L):
     args = dict(batch=2, seq=64, h=256, hq=4, hkv=2, d=128)
 
-    def attn(**kw):
+    def attn(dt=tp.TP_BF16, **kw):
         a = {**args, **kw}
-        return status("tp_shard_attn", a["batch"], a["seq"], a["h"], a["hq"], a["hkv"], a["d"],
+        return status("tp_shard_attn", dt, a["batch"], a["seq"], a["h"], a["hq"], a["hkv"], a["d"],
                       500000.0, 1, A16, A16, A16, A16, 1 << 30, A16, None)
 
+    # the contract's dtype argument: only bf16 attention is built
+    assert attn(dt=tp.TP_F32) == tp.TP_ERR_UNSUPPORTED
+    assert "only bf16" in tp.tp_last_error()
+    assert attn(dt=7) == tp.TP_ERR_INVALID_ARG
     assert attn(d=64) == tp.TP_ERR_UNSUPPORTED
     assert attn(hq=3, hkv=2) == tp.TP_ERR_SHAPE
     assert "multiple of hkv" in tp.tp_last_error()
@@ -88,7 +92,7 @@ def test_attention_validation(L):
     m = 2 * 64
     expect = 4 * 128 * m * 2 + 2 * 128 * m * 2 + 2 * 2 * 128 * 64 * 2 + 4 * 128 * m * 2
     assert ws_need == expect
-    st = status("tp_shard_attn", 2, 64, 256, 4, 2, 128, 500000.0, 1, A16, A16, A16, A16, ws_need - 1,
+    st = status("tp_shard_attn", tp.TP_BF16, 2, 64, 256, 4, 2, 128, 500000.0, 1, A16, A16, A16, A16, ws_need - 1,
                 A16, None)
     assert st == tp.TP_ERR_WORKSPACE
     assert status("tp_qkv_rope", 2, 64, 256, 4, 2, 128, 0.5, A16, A16, None, A16, A16, A16, None) == tp.TP_ERR_INVALID_ARG
