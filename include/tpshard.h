@@ -212,6 +212,33 @@ tp_status tp_shard_attn(tp_dtype dt, int64_t batch, int64_t seq, int64_t h, int3
                         float* partial, void* stream);
 
 /* --------------------------------------------------------------------------
+ * tp_shard_attn without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, kernels and results as
+ * tp_shard_attn; the q, k, vt and o workspace is instead a static device
+ * array of the library holding 64 MiB (TP_STATIC_SCRATCH_BYTES) on every
+ * device it runs on, from the first call on that device until the process
+ * ends.  Nothing is allocated or freed by the call.
+ *
+ *   - A shape whose tp_shard_attn_workspace_bytes(...) exceeds 64 MiB returns
+ *     TP_ERR_WORKSPACE before anything is enqueued (every configuration of
+ *     this library's workloads fits: 36 MiB at batch 4 x seq 2048 with 8
+ *     query heads and 1 KV head).
+ *   - Every call on one device shares that device's array, which keeps the
+ *     last call's contents; each call writes every byte it later reads (the
+ *     transposed-V padding is zeroed by a kernel of the call), so no state
+ *     carries over.  Calls that overlap on one device (e.g. on two streams,
+ *     or from two threads before the first has drained) race on the array:
+ *     the caller must order them.
+ *   - The first call on a device looks up the array's device address
+ *     (TP_ERR_HIP if that fails).
+ * ------------------------------------------------------------------------ */
+#define TP_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+tp_status tp_shard_attn_noalloc(tp_dtype dt, int64_t batch, int64_t seq, int64_t h, int32_t hq, int32_t hkv,
+                                int32_t head_dim, float rope_base, int32_t causal, const void* x,
+                                const void* w_qkv, const void* w_o, float* partial, void* stream);
+
+/* --------------------------------------------------------------------------
  * Sum of the ranks' partials -- the forward all-reduce ("f and g" section),
  * computed inside one device:
  *

@@ -11,6 +11,8 @@
 #include "kernels.h"
 #include "tpshard.h"
 
+static_assert(TP_STATIC_SCRATCH_BYTES == tpk::kStaticScratchBytes, "static scratch size differs from the header");
+
 namespace {
 
 thread_local char g_err[512] = "";
@@ -663,6 +665,27 @@ tp_status tp_shard_attn(tp_dtype dt, int64_t batch, int64_t seq, int64_t h, int3
   TRY(tp_flash_attn(batch, seq, hq, hkv, head_dim, causal, base + L.q, base + L.k, base + L.vt,
                     base + L.o, stream));
   return tp_rowwise(TP_BF16, m, qd, h, base + L.o, w_o, partial, stream);
+}
+
+tp_status tp_shard_attn_noalloc(tp_dtype dt, int64_t batch, int64_t seq, int64_t h, int32_t hq, int32_t hkv,
+                                int32_t head_dim, float rope_base, int32_t causal, const void* x,
+                                const void* w_qkv, const void* w_o, float* partial, void* stream) {
+  if (dt == TP_F32) return fail(TP_ERR_UNSUPPORTED, "tp_shard_attn_noalloc: only bf16 attention is built");
+  if (dt != TP_BF16) return fail(TP_ERR_INVALID_ARG, "unknown dtype %d", (int)dt);
+  TRY(check_attn_shape(batch, seq, hq, hkv, head_dim));
+  const size_t need = attn_layout(batch, seq, hq, hkv, head_dim).total;
+  if (need > tpk::kStaticScratchBytes)
+    return fail(TP_ERR_WORKSPACE,
+                "tp_shard_attn_noalloc: this shape needs %zu bytes of workspace, beyond the %zu-byte static "
+                "scratch (use tp_shard_attn with a caller workspace)",
+                need, tpk::kStaticScratchBytes);
+  if (batch * seq == 0) return ok();
+  TRY(device_check());
+  void* ws = nullptr;
+  const hipError_t e = tpk::static_scratch(&ws);
+  if (e != hipSuccess) return fail(TP_ERR_HIP, "static scratch address lookup failed: %s", hipGetErrorString(e));
+  return tp_shard_attn(dt, batch, seq, h, hq, hkv, head_dim, rope_base, causal, x, w_qkv, w_o, ws,
+                       tpk::kStaticScratchBytes, partial, stream);
 }
 
 tp_status tp_shard_sum(int32_t t, int64_t n, const float* const* partials, const void* residual,

@@ -144,6 +144,12 @@ hipError_t launch_sum_rmsnorm_bwd(int t, int64_t nrun, int64_t run_rows, int64_t
 
 // From the pre-activation and dY (n columns): dPre and, if y, the activation
 // Y.  GeLU: pre [m, n]; SwiGLU: pre [m, 2n] = [gate | up], dPre likewise.
+// Size of the static device array tp_shard_attn_noalloc uses as its
+// workspace, and the lookup of its address on the current device (once per
+// device, then cached; no allocation).
+constexpr size_t kStaticScratchBytes = (size_t)64 << 20;
+hipError_t static_scratch(void** ptr);
+
 hipError_t launch_act_backward(int swiglu, int64_t m, int64_t n, const void* pre, const void* dy, void* dpre,
                                void* y, hipStream_t s);
 

@@ -53,6 +53,7 @@ _SIGS = {
     "tp_shard_attn_workspace_bytes": [_i64, _i64, _i32, _i32, _i32],
     "tp_shard_attn": [_i32, _i64, _i64, _i64, _i32, _i32, _i32, _f32, _i32, _vp, _vp, _vp, _vp,
                       ctypes.c_size_t, _vp, _vp],
+    "tp_shard_attn_noalloc": [_i32, _i64, _i64, _i64, _i32, _i32, _i32, _f32, _i32, _vp, _vp, _vp, _vp, _vp],
     "tp_shard_sum": [_i32, _i64, ctypes.POINTER(_vp), _vp, _i32, _vp, _vp],
     "tp_rmsnorm": [_i32, _i64, _i64, _vp, _vp, _f32, _vp, _vp],
     "tp_shard_sum_rmsnorm": [_i32, _i64, _i64, _i64, _i64, ctypes.POINTER(_vp), _vp, _vp, _i32, _vp, _vp,
@@ -201,6 +202,12 @@ def tp_shard_attn(dt, batch, seq, h, hq, hkv, head_dim, rope_base, causal, x, w_
                   partial, stream=None) -> None:
     _check(lib().tp_shard_attn(_e(dt, DTYPES), batch, seq, h, hq, hkv, head_dim, rope_base, int(causal), _p(x),
                                _p(w_qkv), _p(w_o), _p(ws), ws_bytes, _p(partial), _s(stream)))
+
+
+def tp_shard_attn_noalloc(dt, batch, seq, h, hq, hkv, head_dim, rope_base, causal, x, w_qkv, w_o, partial,
+                          stream=None) -> None:
+    _check(lib().tp_shard_attn_noalloc(_e(dt, DTYPES), batch, seq, h, hq, hkv, head_dim, rope_base, int(causal),
+                                       _p(x), _p(w_qkv), _p(w_o), _p(partial), _s(stream)))
 
 
 def tp_shard_sum(t, n, partials, residual, residual_dt, out, stream=None) -> None:

@@ -97,6 +97,17 @@ def test_attention_validation(L):
     assert st == tp.TP_ERR_WORKSPACE
     assert status("tp_qkv_rope", 2, 64, 256, 4, 2, 128, 0.5, A16, A16, None, A16, A16, A16, None) == tp.TP_ERR_INVALID_ARG
     assert status("tp_flash_attn", 2, 64, 4, 2, 128, 1, A16, A16, None, A16, None) == tp.TP_ERR_INVALID_ARG
+    # the variant on the library's static scratch: same checks, plus its size limit
+    assert status("tp_shard_attn_noalloc", tp.TP_F32, 2, 64, 256, 4, 2, 128, 500000.0, 1, A16, A16, A16, A16,
+                  None) == tp.TP_ERR_UNSUPPORTED
+    assert status("tp_shard_attn_noalloc", tp.TP_BF16, 2, 64, 256, 3, 2, 128, 500000.0, 1, A16, A16, A16, A16,
+                  None) == tp.TP_ERR_SHAPE
+    assert tp.tp_shard_attn_workspace_bytes(4, 8192, 16, 1, 128) > (64 << 20)
+    assert status("tp_shard_attn_noalloc", tp.TP_BF16, 4, 8192, 2048, 16, 1, 128, 500000.0, 1, A16, A16, A16,
+                  A16, None) == tp.TP_ERR_WORKSPACE
+    assert "static scratch" in tp.tp_last_error()
+    assert status("tp_shard_attn_noalloc", tp.TP_BF16, 0, 64, 256, 4, 2, 128, 500000.0, 1, None, None, None,
+                  None, None) == tp.TP_OK
     # seq padding to 64 in the transposed-V region
     assert tp.tp_shard_attn_workspace_bytes(1, 65, 1, 1, 128) >= 128 * 128 * 2
 
