@@ -39,12 +39,16 @@ HIP_FLAGS = [
 ]
 
 
-# Per-file additions.  The attention backward's kernels post-process every
-# score and score-gradient accumulator with vector ALU code; left to its
-# default, the register allocator places those accumulators in AGPRs and
-# moves each value to a VGPR and back (hundreds of moves per tile), so its
-# MFMAs are told to write VGPRs.
+# Per-file additions.  The attention kernels post-process every score (and
+# score-gradient) accumulator with vector ALU code; left to its default, the
+# register allocator places those accumulators in AGPRs and moves each value
+# to a VGPR and back (hundreds of moves per tile), so the backward's MFMAs are
+# told to write VGPRs (the forward, at two workgroups per CU, gets VGPR-form
+# MFMAs by default).  The forward's max trees assume no NaN scores (its inputs
+# are finite), so each fmax is one v_max/v_max3 without a quieting copy of its
+# operands.
 FILE_FLAGS = {
+    "flash_attn.hip": ["-fno-honor-nans"],
     "flash_attn_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 

@@ -63,10 +63,22 @@ __global__ __launch_bounds__(NT, 2) void flash_attn_kernel(FaArgs a) {
   const int lane = lane_id(), wave = wave_id();
   const int l31 = lane & 31, h = lane >> 5;
 
-  // heaviest query blocks first: id -> (qb descending, head, sequence)
+  // Query blocks by launch index: the first half of the launch takes the
+  // heavier half of the query blocks (heaviest first), the second half the
+  // lighter ones (lightest first), so launches i and i + nb/2 -- the two
+  // workgroups one CU holds when the launch fills every CU twice -- carry
+  // query blocks summing to nqb - 1: equal causal work per CU.
   const int per_qb = a.hq * a.batch;
-  const int qb = a.nqb - 1 - (int)(blockIdx.x / per_qb);
-  const int rest = (int)(blockIdx.x % per_qb);
+  int qb, rest;
+  const int half = (a.nqb / 2) * per_qb;
+  if ((a.nqb & 1) == 0 && (int)blockIdx.x >= half) {
+    const int i = (int)blockIdx.x - half;
+    qb = i / per_qb;
+    rest = i % per_qb;
+  } else {
+    qb = a.nqb - 1 - (int)(blockIdx.x / per_qb);
+    rest = (int)(blockIdx.x % per_qb);
+  }
   const int j = rest % a.hq;
   const int b = rest / a.hq;
   const int g = j / (a.hq / a.hkv);
