@@ -46,8 +46,13 @@ HIP_FLAGS = [
 # told to write VGPRs (the forward, at two workgroups per CU, gets VGPR-form
 # MFMAs by default).  The forward's max trees assume no NaN scores (its inputs
 # are finite), so each fmax is one v_max/v_max3 without a quieting copy of its
-# operands.
+# operands.  In the GEMM file, the scheduler's high-register-pressure
+# rescheduling pass otherwise splits the 16x16 kernel's 256 accumulator
+# registers between AGPRs and VGPRs and copies them around the k loop (one
+# move per MFMA); without it the loop is MFMAs, fragment reads and loads only
+# (the other GEMM kernels compile to the same code either way).
 FILE_FLAGS = {
+    "gemm.hip": ["-mllvm", "-amdgpu-disable-unclustered-high-rp-reschedule=1"],
     "flash_attn.hip": ["-fno-honor-nans"],
     "flash_attn_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }

@@ -822,6 +822,346 @@ __global__ __launch_bounds__((Cfg<BMT, W4>::NW * 64), 1) void gemm_bf16_kernel(A
   }
 }
 
+// ---- 16 x 16 x 32 MFMA variant for deep k ---------------------------------
+//
+// The same 256-column tiles, two-stage LDS ring and four waves (2 x 2, one
+// per SIMD, BMT / 2 x 128 each), but the wave's block is built from
+// v_mfma_f32_16x16x32_bf16 instead of 32x32x16.  Under sustained load the
+// board sits at its power limit and the clock is what the matrix work can
+// afford: a long MFMA stream with the GEMM's fragment reads holds 1.66 GHz
+// with 32x32x16 and 1.91 GHz with 16x16x32 on the same random bf16 data
+// (1.70 vs 1.89 PFLOP/s), since the smaller instruction moves less
+// accumulator data per flop.  The 16x16 stream costs a little more issue
+// time per flop, which deep k loops amortise: at k = 8192 the SwiGLU GEMM of
+// the 70B shard and an 8192^3 GEMM run 5-7% faster this way; at k = 3584 it
+// is 1% slower, so shorter k stays on the 32x32 kernel.  Accumulation order
+// and results are bitwise those of the 32x32 kernel.
+//
+// Fragment of a 16-row block for k-step s: lane l reads row l % 16, 16-byte
+// chunk 4 s + l / 16 of the 64-deep stage.  The LDS chunk permutation here
+// depends on the row within its 16-row group only (swz16), which keeps the 16
+// rows one read phase touches on distinct banks and makes block i's address
+// the block-0 address plus 2048 i, an immediate offset: two address
+// registers per operand instead of one per block.  A fragments are single
+// buffered (A_i of the next k-step is read into its registers right after
+// its last MFMA), B fragments double buffered.  Output block (i, j): lane l
+// holds column l % 16 of rows 4 (l / 16) + e, e = 0..3.
+constexpr int64_t MFMA16_MIN_K = 4096;
+
+__device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                 0, 0, 0);
+}
+
+__device__ __forceinline__ int swz16(int r) { return (r >> 1) & 7; }
+
+template <int EPI, int BMT>
+__global__ __launch_bounds__(256, 1) void gemm16_kernel(Args args) {
+  static_assert(EPI != EPI_QKV, "the QKV epilogue runs on the 32x32 kernel");
+  constexpr int NW = 4;
+  constexpr int WROWS = BMT / 2;  // 2 x 2 waves
+  constexpr int MI = WROWS / 16;  // 16-row blocks per wave
+  constexpr int NJ = 8;           // 16-column blocks per wave (128 columns)
+  constexpr int KS = BK / 32;     // MFMA k-steps per stage
+  constexpr int A_TILE = BMT * ROWB;
+  constexpr int SMEM = NSTAGE * (A_TILE + B_TILE);
+  constexpr int B_BASE = NSTAGE * A_TILE;
+  constexpr int A_INSTR = BMT * CH / 64;
+  constexpr int LA = A_INSTR / NW, LB = B_INSTR / NW;
+  static_assert(A_INSTR % NW == 0 && B_INSTR % NW == 0 && SMEM <= 160 * 1024, "tile");
+  __shared__ __attribute__((aligned(1024))) char smem[SMEM];
+
+  const int lane = lane_id();
+  const int wave = wave_id();
+  const bf16_t* const xg = args.x[blockIdx.y];
+  const bf16_t* const wg = args.w[blockIdx.y];
+  void* const outg = args.out[blockIdx.y];
+  int bm, bn;
+  tile_coords(blockIdx.x, gridDim.x, args.num_bm, args.num_bn, bm, bn);
+  bm = __builtin_amdgcn_readfirstlane(bm);
+  bn = __builtin_amdgcn_readfirstlane(bn + args.bn0);
+  const int64_t M = args.M, N = args.N, K = args.K, lda = args.lda;
+  const int64_t m0 = (int64_t)bm * BMT;
+  const uint32_t row_bytes = (uint32_t)(K * 2);
+  const uint32_t a_row_bytes = (uint32_t)(lda * 2);
+  const int m_rows = (int)min<int64_t>(BMT, M - m0);
+  __amdgpu_buffer_rsrc_t rsrc_a = make_rsrc(xg + m0 * lda, (uint32_t)m_rows * a_row_bytes);
+  __amdgpu_buffer_rsrc_t rsrc_b;
+  int n_valid;  // valid weight rows (plain) or valid output columns (SwiGLU)
+  if (is_swiglu(EPI)) {
+    const int64_t o0 = (int64_t)bn * (BN / 2);
+    n_valid = (int)min<int64_t>(BN / 2, N - o0);
+    rsrc_b = make_rsrc(wg + o0 * K, (uint32_t)((N + n_valid) * K * 2));
+  } else {
+    const int64_t n0 = (int64_t)bn * BN;
+    n_valid = (int)min<int64_t>(BN, N - n0);
+    rsrc_b = make_rsrc(wg + n0 * K, (uint32_t)n_valid * row_bytes);
+  }
+
+  // global -> LDS: wave-instruction blk of a stage fills tile row slot / CH,
+  // physical chunk slot % CH, from logical chunk (slot % CH) ^ swz16(row).
+  // SwiGLU tiles hold gate rows o .. o + 63, then the matching up rows, for
+  // each 64-output half (the same interleave as the 32x32 kernel).
+  uint32_t a_off[LA], b_off[LB];
+  int a_k[LA], b_k[LB];
+#pragma unroll
+  for (int j = 0; j < LA; ++j) {
+    const int slot = (j * NW + wave) * 64 + lane;
+    const int r = slot / CH;
+    const int c = (slot % CH) ^ swz16(r);
+    a_k[j] = c * 8;
+    a_off[j] = (uint32_t)r * a_row_bytes + (uint32_t)c * 16;
+  }
+#pragma unroll
+  for (int j = 0; j < LB; ++j) {
+    const int slot = (j * NW + wave) * 64 + lane;
+    const int r = slot / CH;
+    const int c = (slot % CH) ^ swz16(r);
+    b_k[j] = c * 8;
+    if (is_swiglu(EPI)) {
+      const int half = r >> 7, qq = r & 127;
+      const int o_rel = half * 64 + (qq & 63);
+      const int64_t rel_row = (qq < 64) ? o_rel : N + o_rel;
+      b_off[j] = (o_rel < n_valid) ? (uint32_t)(rel_row * K * 2) + (uint32_t)c * 16 : TP_OOB_OFFSET;
+    } else {
+      b_off[j] = (uint32_t)r * row_bytes + (uint32_t)c * 16;
+    }
+  }
+  auto load_a = [&](auto stage_tag, auto full_tag, int kn, int j) {
+    constexpr int S = decltype(stage_tag)::value;
+    char* const dst = smem + S * A_TILE + (j * NW + wave) * 1024;
+    const uint32_t kb = (uint32_t)kn * (uint32_t)(BK * 2);
+    if (decltype(full_tag)::value) buffer_load_lds16_so(rsrc_a, dst, a_off[j], kb);
+    else buffer_load_lds16(rsrc_a, dst, ((int64_t)kn * BK + a_k[j]) < K ? a_off[j] + kb : TP_OOB_OFFSET);
+  };
+  auto load_b = [&](auto stage_tag, auto full_tag, int kn, int j) {
+    constexpr int S = decltype(stage_tag)::value;
+    char* const dst = smem + B_BASE + S * B_TILE + (j * NW + wave) * 1024;
+    const uint32_t kb = (uint32_t)kn * (uint32_t)(BK * 2);
+    if (decltype(full_tag)::value) buffer_load_lds16_so(rsrc_b, dst, b_off[j], kb);
+    else
+      buffer_load_lds16(rsrc_b, dst,
+                        ((int64_t)kn * BK + b_k[j]) < K && b_off[j] != TP_OOB_OFFSET ? b_off[j] + kb : TP_OOB_OFFSET);
+  };
+  // load j (0 .. LA + LB - 1) of a stage: the A loads, then the B loads
+  auto load_one = [&](auto stage_tag, auto full_tag, int kn, int j) {
+    if (j < LA) load_a(stage_tag, full_tag, kn, j);
+    else load_b(stage_tag, full_tag, kn, j - LA);
+  };
+  auto load_stage = [&](auto stage_tag, auto full_tag, int kn) {
+#pragma unroll
+    for (int j = 0; j < LA + LB; ++j) load_one(stage_tag, full_tag, kn, j);
+  };
+
+  const int wm = wave >> 1, wn = wave & 1;
+  const int l15 = lane & 15, kq = lane >> 4;
+  uint32_t ra[KS], rb[KS];  // block 0's fragment address per k-step; block i at + 2048 i
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    const int c = 4 * s + kq;
+    const int r_a = wm * WROWS + l15, r_b = wn * 128 + l15;
+    ra[s] = (uint32_t)(r_a * ROWB + ((c ^ swz16(r_a)) << 4));
+    rb[s] = (uint32_t)(B_BASE + r_b * ROWB + ((c ^ swz16(r_b)) << 4));
+  }
+  f32x4 acc[MI][NJ];
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) acc[i][j] = f32x4{};
+  u32x4 fa[MI], fb[2][NJ];
+  auto rd_a = [&](const char* a, int s, int i) { fa[i] = lds_read16(a + ra[s] + 2048 * i); };
+  auto rd_b = [&](const char* b, int s, int j) { fb[s & 1][j] = lds_read16(b + rb[s] + 2048 * j); };
+
+  const int nk = (int)((K + BK - 1) / BK);
+  const int nfull = (int)(K / BK);
+  using Full = std::true_type;
+  using Partial = std::false_type;
+  constexpr std::integral_constant<int, 0> st0{};
+  constexpr std::integral_constant<int, 1> st1{};
+  // Per k-step of 64: KS substeps of MI x NJ MFMAs.  The one barrier sits
+  // NRD MFMAs before the end of the last substep: every read of this stage
+  // is done and the next stage has landed, so the remaining MFMAs carry the
+  // next stage's first fragment reads (A blocks already finished, then the
+  // B blocks, then each remaining A block after its last use).  The loads of
+  // the stage after next go out after the barrier that frees its buffer: a
+  // few spread over the rest of that substep, the others one every few MFMAs
+  // over the next step's first substep, leaving its second substep for the
+  // last of them to land.
+  constexpr int NMF = MI * NJ, NRD = MI + NJ, BPOS = NMF - NRD;
+  constexpr int NLD = LA + LB;
+  constexpr int NST = MI == 8 ? 4 : NRD / 2;       // loads after the barrier ...
+  constexpr int SPB = MI == 8 ? 4 : 2;             // ... one every SPB MFMAs
+  constexpr int NC0 = NLD - NST;                    // loads in the first substep ...
+  constexpr int SP0 = MI == 8 ? 5 : NMF / NC0;      // ... one every SP0 MFMAs
+  constexpr int IB = BPOS / NJ;                     // A blocks finished before the barrier
+  static_assert(KS == 2 && BPOS > 0 && NST * SPB <= NRD && NC0 > 0 && NC0 * SP0 <= NMF, "schedule");
+  auto kstep = [&](auto stage_tag, auto main_tag, int kt) {
+    constexpr int S = decltype(stage_tag)::value;
+    constexpr bool MAIN = decltype(main_tag)::value;
+    constexpr std::integral_constant<int, 1 - S> other_tag{};
+    const char* const a_st = smem + S * A_TILE;
+    const char* const b_st = smem + S * B_TILE;  // rb holds the B base
+    const char* const a_nx = smem + (1 - S) * A_TILE;
+    const char* const b_nx = smem + (1 - S) * B_TILE;
+    const bool cont = MAIN || (kt >= 1 && kt + 1 < nk);  // rest of step kt + 1's loads
+    const bool cont_full = MAIN || kt + 1 < nfull;
+    const bool start = MAIN || kt + 2 < nk;               // first loads of step kt + 2
+    const bool start_full = MAIN || kt + 2 < nfull;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+#pragma unroll
+      for (int q = 0; q < NMF; ++q) {
+        const int i = q / NJ, j = q % NJ;
+        if (s == KS - 1 && q == BPOS) {
+          wait_vmcnt0();
+          wait_lgkmcnt0();
+          __builtin_amdgcn_s_barrier();
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        acc[i][j] = mfma16x16x32(fa[i], fb[s][j], acc[i][j]);
+        if (s + 1 < KS) {
+          if (q % MI == MI / 2) rd_b(b_st, s + 1, q / MI);
+          if (j == NJ - 1) rd_a(a_st, s + 1, i);
+        } else if (q >= BPOS) {
+          const int r = q - BPOS;
+          if (r < IB) rd_a(a_nx, 0, r);
+          if (i >= IB && j == NJ - 1) rd_a(a_nx, 0, i);
+          if (r >= MI && r - MI < NJ) rd_b(b_nx, 0, r - MI);
+        }
+        if (s == 0 && cont && (q + 1) % SP0 == 0 && (q + 1) / SP0 - 1 < NC0) {
+          const int jj = NST + (q + 1) / SP0 - 1;
+          if (cont_full) load_one(other_tag, Full{}, kt + 1, jj);
+          else load_one(other_tag, Partial{}, kt + 1, jj);
+        }
+        if (s == KS - 1 && q >= BPOS && (q - BPOS) % SPB == SPB - 1 && (q - BPOS) / SPB < NST && start) {
+          const int jj = (q - BPOS) / SPB;
+          if (start_full) load_one(stage_tag, Full{}, kt + 2, jj);
+          else load_one(stage_tag, Partial{}, kt + 2, jj);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
+  if (nfull > 0) load_stage(st0, Full{}, 0);
+  else load_stage(st0, Partial{}, 0);
+  if (nk > 1) {
+    if (nfull > 1) load_stage(st1, Full{}, 1);
+    else load_stage(st1, Partial{}, 1);
+    wait_vmcnt<LA + LB>();  // stage 0 landed, stage 1 may still be in flight
+  } else {
+    wait_vmcnt0();
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < MI; ++i) rd_a(smem, 0, i);
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) rd_b(smem, 0, j);
+  kstep(st0, Partial{}, 0);
+  if (nk > 1) kstep(st1, Partial{}, 1);
+  int kt = 2;
+  for (; kt + 3 < nfull; kt += 2) {
+    kstep(st0, Full{}, kt);
+    kstep(st1, Full{}, kt + 1);
+  }
+  for (; kt < nk; kt += 2) {
+    kstep(st0, Partial{}, kt);
+    if (kt + 1 < nk) kstep(st1, Partial{}, kt + 1);
+  }
+  wait_vmcnt0();
+
+  // ---- epilogue: a quad transpose gives each lane 4 consecutive columns of
+  // one row (rows 4 kq + q of each block, q = lane & 3)
+  const int64_t row_base = m0 + wm * WROWS + 4 * kq;
+  const int q = lane & 3;
+  const int cq = 4 * (l15 >> 2);
+  if constexpr (EPI == EPI_F32) {
+    // float32 partials, stored non-temporally (next read by the shard-sum)
+    const int64_t col_base = (int64_t)bn * BN + wn * 128 + cq;
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        float v[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
+        quad_transpose(v, q);
+        const int64_t row = row_base + i * 16 + q;
+        const int64_t col = col_base + j * 16;
+        if (row < M && col < N)
+          __builtin_nontemporal_store(f32x4{v[0], v[1], v[2], v[3]},
+                                      reinterpret_cast<f32x4*>(reinterpret_cast<float*>(outg) + row * N + col));
+      }
+  } else if constexpr (EPI == EPI_BF16 || is_gelu(EPI)) {
+    const int64_t col_base = (int64_t)bn * BN + wn * 128 + cq;
+    float bcol[NJ];  // bias of the lane's column of each block (-0: none)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int64_t c = (int64_t)bn * BN + wn * 128 + 16 * j + l15;
+      bcol[j] = (args.bias && c < N) ? args.bias[c] : -0.0f;
+    }
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        float v[4], pv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          v[e] = acc[i][j][e] + bcol[j];
+          if (saves_pre(EPI)) pv[e] = v[e];
+          if (is_gelu(EPI)) v[e] = gelu_erf(v[e]);
+        }
+        quad_transpose(v, q);
+        const int64_t row = row_base + i * 16 + q;
+        const int64_t col = col_base + j * 16;
+        if (row < M && col < N)
+          *reinterpret_cast<u32x2*>(reinterpret_cast<bf16_t*>(outg) + row * N + col) =
+              u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+        if (saves_pre(EPI)) {
+          quad_transpose(pv, q);
+          if (row < M && col < N)
+            *reinterpret_cast<u32x2*>(reinterpret_cast<bf16_t*>(args.pre[blockIdx.y]) + row * N + col) =
+                u32x2{pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3])};
+        }
+      }
+  } else {  // SwiGLU: gate block j and up block j + 4 of a wave are the same 16 outputs
+    const int64_t ocol0 = (int64_t)bn * (BN / 2) + wn * 64;
+    float bg[4], bu[4];  // gate and up biases of the lane's output column (-0: none)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t o = ocol0 + 16 * j + l15;
+      bg[j] = (args.bias && o < N) ? args.bias[o] : -0.0f;
+      bu[j] = (args.bias && o < N) ? args.bias[N + o] : -0.0f;
+    }
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float v[4], pg[4], pu[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (saves_pre(EPI)) {
+            pg[e] = acc[i][j][e] + bg[j];
+            pu[e] = acc[i][j + 4][e] + bu[j];
+          }
+          v[e] = silu_fast(acc[i][j][e] + bg[j]) * (acc[i][j + 4][e] + bu[j]);
+        }
+        quad_transpose(v, q);
+        const int64_t row = row_base + i * 16 + q;
+        const int64_t col = ocol0 + 16 * j + cq;
+        if (row < M && col < N)
+          *reinterpret_cast<u32x2*>(reinterpret_cast<bf16_t*>(outg) + row * N + col) =
+              u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+        if (saves_pre(EPI)) {
+          quad_transpose(pg, q);
+          quad_transpose(pu, q);
+          bf16_t* pr = reinterpret_cast<bf16_t*>(args.pre[blockIdx.y]) + row * 2 * N + col;
+          if (row < M && col < N) {
+            *reinterpret_cast<u32x2*>(pr) = u32x2{pack_bf16x2(pg[0], pg[1]), pack_bf16x2(pg[2], pg[3])};
+            *reinterpret_cast<u32x2*>(pr + N) = u32x2{pack_bf16x2(pu[0], pu[1]), pack_bf16x2(pu[2], pu[3])};
+          }
+        }
+      }
+  }
+}
+
 // Zeroes the padding columns [seq, seq_pad) of every row of the transposed V,
 // so attention over a partial last key tile reads zeros there.
 __global__ void vt_pad_zero_kernel(bf16_t* vt, int64_t rows, int64_t seq, int64_t seq_pad) {
@@ -888,6 +1228,12 @@ void launch_part(Args a, int bn0, int cols, int groups, hipStream_t s) {
   a.num_bm = (int)((a.M + BMT - 1) / BMT);
   const int nb = a.num_bm * cols;
   if (nb == 0) return;
+  if constexpr (EPI != EPI_QKV) {
+    if (a.K >= MFMA16_MIN_K) {
+      hipLaunchKernelGGL((gemm16_kernel<EPI, BMT>), dim3(nb, groups), dim3(256), 0, s, a);
+      return;
+    }
+  }
   if (a.K >= W4_MIN_K) {
     hipLaunchKernelGGL((gemm_bf16_kernel<EPI, BMT, true>), dim3(nb, groups), dim3(Cfg<BMT, true>::NW * 64), 0, s, a);
     return;

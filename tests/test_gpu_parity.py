@@ -114,6 +114,10 @@ def test_rowwise_gemm_integer_bit_exact(device, m, k, n):
     (300, 4104, 264, (128, 2, 128)),      # four-wave 128-row tiles, deep k
     (4000, 2056, 2560, (192, 10, 192)),   # four-wave 192-row tiles, ragged m, k tail
     (5000, 2056, 3584, (192, 8, 128)),    # four-wave 192/128 split launch, ragged m, k tail
+    (4000, 4104, 4000, (256, 16, 256)),   # 16x16-MFMA 256-row tiles: ragged m and n, k tail of 8
+    (4096, 4096, 4096, (256, 16, 256)),   # 16x16-MFMA 256-row tiles, whole k-steps only
+    (4000, 4168, 2560, (192, 10, 192)),   # 16x16-MFMA 192-row tiles, ragged m, k tail of 8
+    (5000, 4104, 3584, (192, 8, 128)),    # 16x16-MFMA 192/128 split launch, ragged m, k tail
 ])
 def test_rowwise_gemm_plans_bit_exact(device, m, k, n, plan):
     """Every tile height and the split launch, bit-exact on integer inputs."""
@@ -131,6 +135,7 @@ def test_rowwise_gemm_plans_bit_exact(device, m, k, n, plan):
     (6100, 1096, 5904, (192, 24, 192)),   # eight-wave tiles, k tail of 8
     (6100, 2120, 5904, (192, 24, 192)),   # four-wave tiles, k tail of 8
     (8000, 2048, 4400, (192, 18, 192)),   # four-wave tiles, whole k-steps only
+    (6100, 4104, 5904, (192, 24, 192)),   # 16x16-MFMA tiles, k tail of 8
 ])
 def test_rowwise_gemm_many_tiles_bit_exact(device, m, k, n, plan):
     """Several rounds of tiles per launch (more tiles than compute units),
@@ -145,20 +150,27 @@ def test_rowwise_gemm_many_tiles_bit_exact(device, m, k, n, plan):
     assert np.array_equal(host(out), y.f64() @ w.f64().T)
 
 
-@pytest.mark.parametrize("m,k,n", [(6100, 128, 5904), (6100, 2048, 5904)])
+def _bf16_rne(v: np.ndarray) -> np.ndarray:
+    """float64 values that float32 holds exactly, rounded to bfloat16 (nearest,
+    ties to even) and widened back: the rounding of a bf16 store."""
+    bits = v.astype(np.float32).view(np.uint32).astype(np.uint64)
+    bits = (bits + 0x7FFF + ((bits >> 16) & 1)) >> 16 << 16
+    return bits.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
+@pytest.mark.parametrize("m,k,n", [(6100, 128, 5904), (6100, 2048, 5904), (6100, 4104, 5904)])
 def test_colwise_none_many_tiles_bit_exact(device, m, k, n):
-    """bf16 outputs of a launch with more tiles than compute units (eight- and
-    four-wave tiles).  Inputs in {-1, 0, 1}: the seeded sums stay within
-    +-256, where bf16 holds every integer."""
+    """bf16 outputs of a launch with more tiles than compute units (eight-wave,
+    four-wave and 16x16-MFMA tiles).  Inputs in {-1, 0, 1}: every sum is an
+    integer held exactly in float32, so the output is its bf16 rounding."""
     say(f"case colwise many tiles m={m} k={k} n={n}")
     x = inputs.integers(11, 0, (m, k), -1, 1)
     w = inputs.integers(11, 1, (n, k), -1, 1)
     ref = x.f64() @ w.f64().T
-    assert np.max(np.abs(ref)) <= 256
     out = torch.empty(m, n, dtype=torch.bfloat16, device=device)
     tp.tp_colwise("none", "bf16", m, k, n, to_dev(x, device), to_dev(w, device), out)
     torch.cuda.synchronize()
-    assert np.array_equal(host(out), ref)
+    assert np.array_equal(host(out), _bf16_rne(ref))
 
 
 @pytest.mark.parametrize("m,k,n", [(300, 40, 264), (64, 48, 512)])
@@ -197,7 +209,8 @@ def test_colwise_bias_integer_bit_exact(device, m, k, n):
 
 @pytest.mark.parametrize("act,dt,m,k,f", [("gelu", "bf16", 333, 256, 264), ("swiglu", "bf16", 333, 256, 264),
                                           ("swiglu", "bf16", 5000, 2056, 1792), ("gelu", "f32", 37, 64, 72),
-                                          ("swiglu", "f32", 37, 64, 72)])
+                                          ("swiglu", "f32", 37, 64, 72), ("swiglu", "bf16", 1000, 4104, 1792),
+                                          ("gelu", "bf16", 1000, 4104, 1000)])
 def test_colwise_bias_activations(device, act, dt, m, k, f):
     """GeLU(X A_i + b_i) and SiLU(X W1_i + b1_i) * (X W3_i + b3_i) against the oracle."""
     say(f"case colwise bias {act} {dt} m={m} k={k} f={f}")
@@ -587,7 +600,8 @@ def test_saved_activation_backward_matches_recompute(device):
         assert torch.equal(blk.attn.dw_o[r], ref["dwo"][r])
 
 
-@pytest.mark.parametrize("act,m,h,f", [("gelu", 1000, 256, 1024), ("swiglu", 520, 384, 768)])
+@pytest.mark.parametrize("act,m,h,f", [("gelu", 1000, 256, 1024), ("swiglu", 520, 384, 768),
+                                      ("swiglu", 520, 4104, 768), ("gelu", 600, 4104, 1024)])
 def test_colwise_save_and_mlp_backward_from_it(device, act, m, h, f):
     """tp_colwise_save's output equals tp_colwise's and its pre-activation the
     plain GEMM's, bitwise, with and without a bias (ragged m, two rounds of
@@ -909,6 +923,9 @@ def test_colwise_activation_slices(device):
     ("swiglu", 4000, 2056, 2048, (256, 16, 256)),   # four-wave tiles, ragged m, k tail
     ("gelu", 4000, 2056, 4000, (256, 16, 256)),     # four-wave tiles, ragged m and n
     ("swiglu", 5000, 2056, 1792, (192, 8, 128)),    # four-wave 192/128 split, ragged m, k tail
+    ("swiglu", 4000, 4104, 2048, (256, 16, 256)),   # 16x16-MFMA tiles, ragged m, k tail
+    ("gelu", 4000, 4104, 4000, (256, 16, 256)),     # 16x16-MFMA tiles, ragged m and n
+    ("swiglu", 5000, 4104, 1792, (192, 8, 128)),    # 16x16-MFMA 192/128 split, ragged m, k tail
 ])
 def test_colwise_activation_tile_heights(device, act, m, h, f, plan):
     """GeLU and SwiGLU epilogues (gate/up pairing, 4-column stores) at every
