@@ -110,20 +110,33 @@ def cpu_baseline(case, w_host, budget_s: float = 20.0) -> dict:
         Ws = dict(W)
         Ws["X"] = x_all.f32()[:s].astype(np.float64)
         t0 = time.perf_counter()
+        c0 = time.process_time()
         oracle.block(Ws["X"], Ws, sub)
         dt = time.perf_counter() - t0
+        cpu = time.process_time() - c0
         fl = sum(block_flops(sub, case.t).values()) * case.t
-        best = (s, dt, fl)
+        best = (s, dt, fl, cpu)
         log(f"cpu baseline: {s} tokens in {dt:.2f}s")
         if dt * 2.2 > budget_s or s >= case.seq:
             break
         s *= 2
-    s, dt, fl = best
+    s, dt, fl, cpu = best
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     return {
         "value": fl / dt / 1e12,
         "unit": "TFLOP/s",
         "cores": int(threads),
+        "effective_cores": round(cpu / dt, 1),
+        "host_cpus": len(os.sched_getaffinity(0)),
+        "cpu_model": model,
         "kind": "oracle",
         "sample": f"one sequence of {s} tokens through the same block (all {case.t} ranks, "
                   f"float64 numpy), {fl / 1e9:.1f} GFLOP in {dt:.2f} s",
@@ -152,6 +165,24 @@ def _time(fn, reps=20, warm=5, before=None):
         b.synchronize()
         ts.append(a.elapsed_time(b))
     return statistics.median(ts), min(ts)
+
+
+def _time_b2b(fn, reps=20, warm=5):
+    """Mean milliseconds of fn over reps calls issued back to back between two
+    events (no synchronisation between calls, as in a running model)."""
+    import torch
+
+    for _ in range(warm):
+        fn()
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        fn()
+    b.record()
+    b.synchronize()
+    return a.elapsed_time(b) / reps
 
 
 def per_config_report(dev):
@@ -188,9 +219,12 @@ def per_config_report(dev):
         mlp = shard.MLPShards(dw["X"], dw, case.t, case.act)
         fl = 2.0 * case.tokens * case.hidden * case.f_shard * (3 if case.act == "swiglu" else 2)
         med, mn = _time(lambda: mlp.rank(0))
+        b2b = _time_b2b(lambda: mlp.rank(0))
         rec = {"workload": name, "call": "tp_shard_mlp (one rank)", "ms": round(med, 4),
                "min_ms": round(mn, 4), "tflops": rate(fl, med),
-               "pct_mfma_peak": round(100.0 * fl / med / 1e9 / MFMA_BF16_PEAK_TFLOPS, 2)}
+               "pct_mfma_peak": round(100.0 * fl / med / 1e9 / MFMA_BF16_PEAK_TFLOPS, 2),
+               "b2b_ms": round(b2b, 4), "b2b_tflops": rate(fl, b2b),
+               "b2b_pct_mfma_peak": round(100.0 * fl / b2b / 1e9 / MFMA_BF16_PEAK_TFLOPS, 2)}
         gmed, gmn = _time(lambda: mlp.all_ranks_grouped())
         rec.update({"grouped_all_ranks_ms": round(gmed, 4), "grouped_min_ms": round(gmn, 4),
                     "grouped_tflops": rate(case.t * fl, gmed)})
@@ -208,9 +242,12 @@ def per_config_report(dev):
                                       case.head_dim, case.hidden, case.t, case.rope_base, 0), case.t)
     afl = fl["qkv"] + fl["attn_core"] + fl["o_proj"]
     med, mn = _time(lambda: at.rank(0))
+    b2b = _time_b2b(lambda: at.rank(0))
     rec = {"workload": "llama8b_attn", "call": "tp_shard_attn (one rank)", "ms": round(med, 4),
            "min_ms": round(mn, 4), "tflops": rate(afl, med),
-           "pct_mfma_peak": round(100.0 * afl / med / 1e9 / MFMA_BF16_PEAK_TFLOPS, 2)}
+           "pct_mfma_peak": round(100.0 * afl / med / 1e9 / MFMA_BF16_PEAK_TFLOPS, 2),
+           "b2b_ms": round(b2b, 4), "b2b_tflops": rate(afl, b2b),
+           "b2b_pct_mfma_peak": round(100.0 * afl / b2b / 1e9 / MFMA_BF16_PEAK_TFLOPS, 2)}
     n = case.tokens * case.hidden
     rec.update(sum_rec(lambda: at.reduce(residual=None), (case.t + 1) * 4 * n))
     emit(rec)
@@ -229,6 +266,8 @@ def per_config_report(dev):
         blk.norm_mlp()
         ams, amn = _time(lambda: blk.attn.rank(0))
         mms, mmn = _time(lambda: blk.mlp.rank(0))
+        ab2b = _time_b2b(lambda: blk.attn.rank(0))
+        mb2b = _time_b2b(lambda: blk.mlp.rank(0))
         n = case.tokens * case.hidden
         srec = sum_rec(lambda: blk.mlp.reduce(residual=blk.attn.out, residual_dt="f32"),
                        (case.t + 2) * 4 * n)
@@ -239,7 +278,10 @@ def per_config_report(dev):
                "attn_pct_mfma_peak": round(100.0 * afl / ams / 1e9 / MFMA_BF16_PEAK_TFLOPS, 2),
                "mlp_call_ms": round(mms, 4), "mlp_min_ms": round(mmn, 4), "mlp_tflops": rate(mfl, mms),
                "mlp_pct_mfma_peak": round(100.0 * mfl / mms / 1e9 / MFMA_BF16_PEAK_TFLOPS, 2),
-               "shard_aggregate_tflops": rate(afl + mfl, ams + mms)}
+               "shard_aggregate_tflops": rate(afl + mfl, ams + mms),
+               "attn_b2b_ms": round(ab2b, 4), "attn_b2b_tflops": rate(afl, ab2b),
+               "mlp_b2b_ms": round(mb2b, 4), "mlp_b2b_tflops": rate(mfl, mb2b),
+               "mlp_b2b_pct_mfma_peak": round(100.0 * mfl / mb2b / 1e9 / MFMA_BF16_PEAK_TFLOPS, 2)}
         rec.update(srec)
         rec.update({"block_step_ms": round(step, 3), "block_step_min_ms": round(step_min, 3),
                     "block_step_tflops": rate(case.t * (afl + mfl), step),
@@ -415,6 +457,63 @@ def attn_core_buffers(tp, at, case, dev, dz):
     return {"run": run, "keep": (q, k, vt, o, lse, do, ws, dqkv, wo_t)}
 
 
+def kernel_replay(blk, case, fl, stream, steps=3) -> dict:
+    """Per-kernel average duration and roofline fraction in a replay of the
+    step (after the timed region) in which every kernel launch is bracketed by
+    HIP events on the stream it runs on; attention runs as its three component
+    calls, the kernels tp_shard_attn launches.  GEMMs and attention are priced
+    against the bf16 MFMA peak, the norms and sums (HBM-bound) against HBM."""
+    import torch
+
+    t = case.t
+    n = case.tokens * case.hidden
+    work = {  # name -> (amount per launch, unit, peak)
+        "rmsnorm": (4 * n, "GB/s", HBM_PEAK_GBS),
+        "qkv_rope": (fl["qkv"], "TFLOP/s", MFMA_BF16_PEAK_TFLOPS),
+        "flash_attn": (fl["attn_core"], "TFLOP/s", MFMA_BF16_PEAK_TFLOPS),
+        "o_proj": (fl["o_proj"], "TFLOP/s", MFMA_BF16_PEAK_TFLOPS),
+        "sum_rmsnorm": ((4 * t + 8) * n, "GB/s", HBM_PEAK_GBS),
+        "swiglu_gemm": (fl["swiglu_gemm"], "TFLOP/s", MFMA_BF16_PEAK_TFLOPS),
+        "down_gemm": (fl["down_gemm"], "TFLOP/s", MFMA_BF16_PEAK_TFLOPS),
+        "shard_sum": ((t + 2) * 4 * n, "GB/s", HBM_PEAK_GBS),
+    }
+    evs = {k: [] for k in work}
+    open_ev = []
+
+    def mark(name):
+        e = torch.cuda.Event(enable_timing=True)
+        e.record(stream)
+        if name is not None:
+            open_ev.append((name, e))
+        else:
+            nm, e0 = open_ev.pop()
+            evs[nm].append((e0, e))
+
+    def timed(name, fn):
+        mark(name)
+        fn()
+        mark(None)
+
+    attn, mlp = blk.attn, blk.mlp
+    for _ in range(steps):
+        timed("rmsnorm", blk.norm_attn)
+        for r in range(t):
+            attn.rank_parts(r, mark=mark)
+        timed("sum_rmsnorm", blk.sum_norm_mlp)
+        for r in range(t):
+            timed("swiglu_gemm", lambda: mlp.colwise(r))
+            timed("down_gemm", lambda: mlp.rowwise(r))
+        timed("shard_sum", lambda: mlp.reduce(residual=attn.out, residual_dt="f32"))
+    torch.cuda.synchronize()
+    out = {}
+    for k, (amount, unit, peak) in work.items():
+        us = 1e3 * sum(a.elapsed_time(b) for a, b in evs[k]) / len(evs[k])
+        ach = amount / us / (1e6 if unit == "TFLOP/s" else 1e3)
+        out[k] = {"avg_us": round(us, 2), "achieved": round(ach, 1), "peak": peak, "unit": unit,
+                  "frac": round(ach / peak, 4), "launches": len(evs[k])}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -426,7 +525,7 @@ def main():
     ap.add_argument("--configs", action="store_true",
                     help="per-call report for every workload (one JSON line each) instead of the step")
     ap.add_argument("--pmc-pass", action="store_true",
-                    help="launch only a 256 MiB copy and the SwiGLU GEMM (for counter runs)")
+                    help="launch a 256 MiB copy, then one step of the block (for counter runs)")
     ap.add_argument("--bwd-pass", action="store_true",
                     help="run one rank's SwiGLU MLP backward and attention backward at the 70B t=8 shape four "
                          "times each (for a kernel trace)")
@@ -492,8 +591,7 @@ def main():
         for _ in range(3):
             tp.tp_shard_sum(1, n, [src], None, "f32", dst)
         torch.cuda.synchronize()
-        for r in range(3):
-            mlp.colwise(r)
+        blk.forward()  # one step: every kernel of the block, all ranks
         torch.cuda.synchronize()
         log("pmc pass done")
         return
@@ -577,6 +675,8 @@ def main():
         "sequence_parallel_tflops": round(step_flops / (sp_ms * 1e-3) / 1e12, 1),
     }
     log(f"detail {detail}")
+    kernels = kernel_replay(blk, case, fl, stream, steps=3)
+    log(f"kernels {kernels}")
 
     out = {
         "metric": "TFLOP/s per TP shard (MLP + attention, bf16) and % of MFMA bf16 peak",
@@ -615,6 +715,12 @@ def main():
                                                  + 2 * (case.inter // t) * case.hidden
                                                  + case.tokens * (case.inter // t)),
         },
+        "attention_roofline": {
+            "kernel": "flash_attn_kernel (causal GQA flash attention forward, one rank's heads)",
+            "bound": "mfma",
+            **{k: kernels["flash_attn"][k] for k in ("achieved", "peak", "unit", "frac", "avg_us")},
+        },
+        "kernels": kernels,
         "detail": detail,
     }
     if not args.no_cpu_baseline and int(os.environ.get("RANK", "0")) == 0:

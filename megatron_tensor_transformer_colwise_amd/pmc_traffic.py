@@ -3,7 +3,7 @@
 Reads the results databases of ``rocprofv3 --pmc FETCH_SIZE`` and
 ``rocprofv3 --pmc WRITE_SIZE`` runs of ``bench.py --pmc-pass``.  That mode
 launches a plain device copy of a known size (the shard-sum kernel with one
-partial: n float32 read, n written) before the measured kernel, so each
+partial, shard_sum_kernel<1>: n float32 read, n written) before the measured kernel, so each
 counter is scaled by bytes_known / counter_reading_of_the_copy.  Writes the
 per-launch traffic of the measured kernel, with the hash of the source it was
 taken on, to a JSON file that bench.py reports while the source is unchanged.
@@ -40,7 +40,7 @@ def main(fetch_db, write_db, copy_bytes, kernel_sub, calls, source, out_json):
     res = {}
     for counter, db in (("FETCH_SIZE", fetch_db), ("WRITE_SIZE", write_db)):
         d = per_dispatch(db, counter)
-        copy = [v for n, v in d if "shard_sum" in n]
+        copy = [v for n, v in d if "shard_sum_kernel<1>" in n]
         kern = [v for n, v in d if kernel_sub in n]
         if not copy or not kern:
             raise SystemExit(f"{counter}: no copy or no '{kernel_sub}' dispatches in {db}")

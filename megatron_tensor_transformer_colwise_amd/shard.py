@@ -223,6 +223,35 @@ class AttnShards:
         m = self.batch * self.seq
         tp.tp_shard_sum(self.t, m * self.h, list(self.partials), residual, residual_dt, self.out, stream)
 
+    def rank_parts(self, r: int, x=None, stream=None, mark=None) -> None:
+        """Rank r's attention as its three component calls (the kernels
+        tp_shard_attn launches, in the same order, on buffers of its own);
+        ``mark(name)`` runs before and ``mark(None)`` after each, e.g. to
+        bracket each kernel with events."""
+        rk = self.ranks[r]
+        if getattr(self, "part_bufs", None) is None:
+            dev, m, d = self.x.device, self.batch * self.seq, self.d
+            hq, hkv = self.ranks[0].hq, max(q.hkv for q in self.ranks)
+            sp = (self.seq + 63) // 64 * 64
+            bf = torch.bfloat16
+            self.part_bufs = (torch.empty(m, hq * d, dtype=bf, device=dev),
+                              torch.empty(m, hkv * d, dtype=bf, device=dev),
+                              torch.empty(self.batch * hkv * d * sp, dtype=bf, device=dev),
+                              torch.empty(m, hq * d, dtype=bf, device=dev))
+        q, k, vt, o = self.part_bufs
+        mark = mark or (lambda name: None)
+        m = self.batch * self.seq
+        mark("qkv_rope")
+        tp.tp_qkv_rope(self.batch, self.seq, self.h, rk.hq, rk.hkv, self.d, self.case.rope_base,
+                       self.x if x is None else x, rk.w_qkv, q, k, vt, stream)
+        mark(None)
+        mark("flash_attn")
+        tp.tp_flash_attn(self.batch, self.seq, rk.hq, rk.hkv, self.d, self.causal, q, k, vt, o, stream)
+        mark(None)
+        mark("o_proj")
+        tp.tp_rowwise("bf16", m, rk.hq * self.d, self.h, o, rk.w_o, self.partials[r], stream)
+        mark(None)
+
     def rank_save(self, r: int, x=None, stream=None) -> None:
         """Rank r's forward keeping Q, K, V^T, O and the log-sum-exp for the backward."""
         rk = self.ranks[r]
