@@ -91,8 +91,9 @@ def stored_traffic():
 
 def cpu_baseline(case, w_host, budget_s: float = 20.0) -> dict:
     """The float64 oracle on a bounded sample of the workload: the same block
-    (same weights, t ranks) over one sequence of S tokens, S doubled from 16
-    while the time stays within the budget."""
+    (same weights, t ranks) over the first S tokens of one sequence, S doubled
+    from 16 up to the sequence length, then over the first 2, 4, ... whole
+    sequences, while the time stays within the budget."""
     import numpy as np
     from threadpoolctl import threadpool_info
 
@@ -103,24 +104,30 @@ def cpu_baseline(case, w_host, budget_s: float = 20.0) -> dict:
     W = {k: v.f64() for k, v in w_host.items() if k != "X"}
     x_all = w_host["X"]
     best = None
-    s = 16
+    s, nseq = 16, 1
     while True:
-        sub = inputs.BlockCase(case.name + "-sample", 1, s, case.hidden, case.heads, case.kv_heads,
+        sub = inputs.BlockCase(case.name + "-sample", nseq, s, case.hidden, case.heads, case.kv_heads,
                                case.head_dim, case.inter, case.t, case.rope_base, case.seed)
         Ws = dict(W)
-        Ws["X"] = x_all.f32()[:s].astype(np.float64)
+        if nseq == 1:
+            Ws["X"] = x_all.f32()[:s].astype(np.float64)
+        else:  # the first nseq whole sequences
+            Ws["X"] = x_all.f32()[:nseq * s].astype(np.float64)
         t0 = time.perf_counter()
         c0 = time.process_time()
         oracle.block(Ws["X"], Ws, sub)
         dt = time.perf_counter() - t0
         cpu = time.process_time() - c0
         fl = sum(block_flops(sub, case.t).values()) * case.t
-        best = (s, dt, fl, cpu)
-        log(f"cpu baseline: {s} tokens in {dt:.2f}s")
-        if dt * 2.2 > budget_s or s >= case.seq:
+        best = (s, nseq, dt, fl, cpu)
+        log(f"cpu baseline: {nseq} x {s} tokens in {dt:.2f}s")
+        if dt * 2.2 > budget_s or (s >= case.seq and nseq >= case.batch):
             break
-        s *= 2
-    s, dt, fl, cpu = best
+        if s < case.seq:
+            s *= 2
+        else:
+            nseq *= 2
+    s, nseq, dt, fl, cpu = best
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     model = "unknown"
     try:
@@ -138,7 +145,7 @@ def cpu_baseline(case, w_host, budget_s: float = 20.0) -> dict:
         "host_cpus": len(os.sched_getaffinity(0)),
         "cpu_model": model,
         "kind": "oracle",
-        "sample": f"one sequence of {s} tokens through the same block (all {case.t} ranks, "
+        "sample": f"{nseq} sequence(s) of {s} tokens through the same block (all {case.t} ranks, "
                   f"float64 numpy), {fl / 1e9:.1f} GFLOP in {dt:.2f} s",
     }
 

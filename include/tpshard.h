@@ -490,13 +490,20 @@ tp_status tp_shard_attn_backward(int64_t batch, int64_t seq, int64_t h, int32_t 
 
 /* --------------------------------------------------------------------------
  * Introspection: how the bf16 GEMM behind tp_colwise / tp_rowwise /
- * tp_qkv_rope tiles an m x n output (n = output columns; swiglu != 0 for the
- * SwiGLU colwise GEMM, whose tiles cover 128 output columns instead of 256).
+ * tp_qkv_rope tiles an m x n output over depth k (n = output columns; the
+ * SwiGLU colwise GEMM's tiles cover 128 output columns instead of 256).
  * Tile columns [0, split) run at tile height bm_main and the remaining ones at
- * bm_tail (heights 256, 192 or 128 rows).  Host-only; launches nothing.
+ * bm_tail (heights 256, 192 or 128 rows); with *split_k = 2 the remaining
+ * columns run as 256-row tiles each summed by two workgroups over half of k
+ * (single bf16-output launches of depth k >= 4096, when that shortens the
+ * last round).  kind: TP_PLAN_ROWWISE (float32 partial), TP_PLAN_COLWISE
+ * (bf16, plain or GeLU), TP_PLAN_SWIGLU, TP_PLAN_QKV.  Host-only; launches
+ * nothing.  TP_ERR_SHAPE for non-positive sizes, TP_ERR_INVALID_ARG for an
+ * unknown kind or a NULL output.
  * ------------------------------------------------------------------------ */
-tp_status tp_gemm_plan(int64_t m, int64_t n, int32_t swiglu, int32_t* bm_main, int32_t* split,
-                       int32_t* bm_tail);
+enum { TP_PLAN_ROWWISE = 0, TP_PLAN_COLWISE = 1, TP_PLAN_SWIGLU = 2, TP_PLAN_QKV = 3 };
+tp_status tp_gemm_plan(int64_t m, int64_t n, int64_t k, int32_t kind, int32_t* bm_main, int32_t* split,
+                       int32_t* bm_tail, int32_t* split_k);
 
 /* Message for the calling thread's last error ("" if none). */
 const char* tp_last_error(void);

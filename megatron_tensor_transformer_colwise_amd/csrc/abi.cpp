@@ -230,15 +230,17 @@ extern "C" {
 
 const char* tp_last_error(void) { return g_err; }
 
-tp_status tp_gemm_plan(int64_t m, int64_t n, int32_t swiglu, int32_t* bm_main, int32_t* split,
-                       int32_t* bm_tail) {
-  if (m <= 0 || n <= 0) return fail(TP_ERR_SHAPE, "m and n must be positive");
-  if (!bm_main || !split || !bm_tail) return fail(TP_ERR_INVALID_ARG, "NULL output pointer");
-  int a, b, c;
-  tpk::gemm_plan(m, n, swiglu != 0, 1, &a, &b, &c);
+tp_status tp_gemm_plan(int64_t m, int64_t n, int64_t k, int32_t kind, int32_t* bm_main, int32_t* split,
+                       int32_t* bm_tail, int32_t* split_k) {
+  if (m <= 0 || n <= 0 || k <= 0) return fail(TP_ERR_SHAPE, "m, n and k must be positive");
+  if (kind < TP_PLAN_ROWWISE || kind > TP_PLAN_QKV) return fail(TP_ERR_INVALID_ARG, "unknown GEMM kind %d", (int)kind);
+  if (!bm_main || !split || !bm_tail || !split_k) return fail(TP_ERR_INVALID_ARG, "NULL output pointer");
+  int a, b, c, d;
+  tpk::gemm_plan(m, n, k, kind, 1, &a, &b, &c, &d);
   *bm_main = a;
   *split = b;
   *bm_tail = c;
+  *split_k = d;
   return ok();
 }
 

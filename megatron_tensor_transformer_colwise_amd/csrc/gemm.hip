@@ -40,7 +40,10 @@
 // rounds-of-256-workgroups x (BMT + 256): the loads of a tile scale with
 // BMT + 256 and the kernel is close to its load bound, while a partly filled
 // last round costs a whole round.
+#include <map>
+#include <mutex>
 #include <type_traits>
+#include <utility>
 
 #include "common.h"
 #include "kernels.h"
@@ -108,6 +111,14 @@ struct Args {
   int num_bn;  // tile columns of this launch
   int bn0;     // first tile column of this launch
   QkvOut qkv;
+  // Split-k launches of the 16x16 kernel (NULL sk_ws: none).  Two workgroups
+  // share each tile p: the producer sums k-steps [sk_half, nk) into sk_ws
+  // tile p and then raises sk_flag[p] to sk_epoch; the consumer sums k-steps
+  // [0, sk_half), waits for the flag, adds the partial and runs the epilogue.
+  float* sk_ws;
+  unsigned* sk_flag;
+  unsigned sk_epoch;
+  int sk_half;
 };
 
 // Chunk permutation of tile row r.  Reads of one fragment touch 32 consecutive
@@ -847,6 +858,7 @@ __global__ __launch_bounds__((Cfg<BMT, W4>::NW * 64), 1) void gemm_bf16_kernel(A
 // its last MFMA), B fragments double buffered.  Output block (i, j): lane l
 // holds column l % 16 of rows 4 (l / 16) + e, e = 0..3.
 constexpr int64_t MFMA16_MIN_K = 4096;
+constexpr int CPOL_SC0_SC1 = 1 | 16;  // cache policy bits of a system-coherent buffer access
 
 __device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
@@ -876,8 +888,18 @@ __global__ __launch_bounds__(256, 1) void gemm16_kernel(Args args) {
   const bf16_t* const xg = args.x[blockIdx.y];
   const bf16_t* const wg = args.w[blockIdx.y];
   void* const outg = args.out[blockIdx.y];
+  // Split launches: launch index b works on tile 8 (b / 16) + b % 8, the
+  // upper half of k when (b / 8) is even (the producer) and the lower half
+  // otherwise, so a tile's two workgroups sit on the same XCD (b and b + 8)
+  // and tile_coords sees tile ids in their XCD's order; the grid is 16 per 8
+  // tiles and the ids past the last tile have nothing to do.
+  const bool split = args.sk_ws != nullptr;
+  const bool producer = split && ((blockIdx.x >> 3) & 1) == 0;
+  const int ntiles = args.num_bm * args.num_bn;
+  const int tile_id = split ? (int)((blockIdx.x >> 4) * 8 + (blockIdx.x & 7)) : (int)blockIdx.x;
+  if (tile_id >= ntiles) return;
   int bm, bn;
-  tile_coords(blockIdx.x, gridDim.x, args.num_bm, args.num_bn, bm, bn);
+  tile_coords(tile_id, ntiles, args.num_bm, args.num_bn, bm, bn);
   bm = __builtin_amdgcn_readfirstlane(bm);
   bn = __builtin_amdgcn_readfirstlane(bn + args.bn0);
   const int64_t M = args.M, N = args.N, K = args.K, lda = args.lda;
@@ -972,8 +994,10 @@ __global__ __launch_bounds__(256, 1) void gemm16_kernel(Args args) {
   auto rd_a = [&](const char* a, int s, int i) { fa[i] = lds_read16(a + ra[s] + 2048 * i); };
   auto rd_b = [&](const char* b, int s, int j) { fb[s & 1][j] = lds_read16(b + rb[s] + 2048 * j); };
 
-  const int nk = (int)((K + BK - 1) / BK);
-  const int nfull = (int)(K / BK);
+  const int nfull = (int)(K / BK);  // k-steps without a k tail
+  // this workgroup's k-steps [kb, ke)
+  const int kb = split && producer ? args.sk_half : 0;
+  const int ke = split && !producer ? args.sk_half : (int)((K + BK - 1) / BK);
   using Full = std::true_type;
   using Partial = std::false_type;
   constexpr std::integral_constant<int, 0> st0{};
@@ -1003,9 +1027,9 @@ __global__ __launch_bounds__(256, 1) void gemm16_kernel(Args args) {
     const char* const b_st = smem + S * B_TILE;  // rb holds the B base
     const char* const a_nx = smem + (1 - S) * A_TILE;
     const char* const b_nx = smem + (1 - S) * B_TILE;
-    const bool cont = MAIN || (kt >= 1 && kt + 1 < nk);  // rest of step kt + 1's loads
+    const bool cont = MAIN || (kt > kb && kt + 1 < ke);  // rest of step kt + 1's loads
     const bool cont_full = MAIN || kt + 1 < nfull;
-    const bool start = MAIN || kt + 2 < nk;               // first loads of step kt + 2
+    const bool start = MAIN || kt + 2 < ke;              // first loads of step kt + 2
     const bool start_full = MAIN || kt + 2 < nfull;
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
@@ -1042,11 +1066,11 @@ __global__ __launch_bounds__(256, 1) void gemm16_kernel(Args args) {
       }
     }
   };
-  if (nfull > 0) load_stage(st0, Full{}, 0);
-  else load_stage(st0, Partial{}, 0);
-  if (nk > 1) {
-    if (nfull > 1) load_stage(st1, Full{}, 1);
-    else load_stage(st1, Partial{}, 1);
+  if (kb < nfull) load_stage(st0, Full{}, kb);
+  else load_stage(st0, Partial{}, kb);
+  if (kb + 1 < ke) {
+    if (kb + 1 < nfull) load_stage(st1, Full{}, kb + 1);
+    else load_stage(st1, Partial{}, kb + 1);
     wait_vmcnt<LA + LB>();  // stage 0 landed, stage 1 may still be in flight
   } else {
     wait_vmcnt0();
@@ -1056,18 +1080,66 @@ __global__ __launch_bounds__(256, 1) void gemm16_kernel(Args args) {
   for (int i = 0; i < MI; ++i) rd_a(smem, 0, i);
 #pragma unroll
   for (int j = 0; j < NJ; ++j) rd_b(smem, 0, j);
-  kstep(st0, Partial{}, 0);
-  if (nk > 1) kstep(st1, Partial{}, 1);
-  int kt = 2;
-  for (; kt + 3 < nfull; kt += 2) {
+  kstep(st0, Partial{}, kb);
+  if (kb + 1 < ke) kstep(st1, Partial{}, kb + 1);
+  int kt = kb + 2;
+  const int kmain = min(nfull, ke);
+  for (; kt + 3 < kmain; kt += 2) {
     kstep(st0, Full{}, kt);
     kstep(st1, Full{}, kt + 1);
   }
-  for (; kt < nk; kt += 2) {
+  for (; kt < ke; kt += 2) {
     kstep(st0, Partial{}, kt);
-    if (kt + 1 < nk) kstep(st1, Partial{}, kt + 1);
+    if (kt + 1 < ke) kstep(st1, Partial{}, kt + 1);
   }
   wait_vmcnt0();
+
+  if (split) {
+    // The partial of k-steps [sk_half, nk) crosses workgroups (and XCDs):
+    // it is written and read with system-coherent accesses (sc0 sc1: past
+    // the non-coherent L2s), lane by lane in accumulator order, and the flag
+    // goes up only after every wave's stores have completed.
+    constexpr int NBLK = MI * NJ;
+    __amdgpu_buffer_rsrc_t ws =
+        make_rsrc(args.sk_ws + (size_t)tile_id * (BMT * BN), (uint32_t)(BMT * BN * sizeof(float)));
+    unsigned* const flag = args.sk_flag + tile_id;
+    if (producer) {
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[i][j]), ws,
+                                                 (uint32_t)(((wave * NBLK + i * NJ + j) * 64 + lane) * 16), 0,
+                                                 CPOL_SC0_SC1);
+      wait_vmcnt0();
+      __syncthreads();
+      if (threadIdx.x == 0) __hip_atomic_store(flag, args.sk_epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return;
+    }
+    if (threadIdx.x == 0) {
+      // the producer has the lower launch index (b - 8), so it was dispatched
+      // first and never waits: this ends; the bound only guards against a
+      // broken launch (the result would then be wrong, not hung)
+      for (uint32_t n = 0; n < (1u << 22); ++n) {
+        if (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == args.sk_epoch) break;
+        __builtin_amdgcn_s_sleep(2);
+      }
+    }
+    __syncthreads();
+    // one row of blocks (NJ loads) in flight at a time: all of them at once
+    // would need 4 x MI x NJ more registers than the kernel has
+#pragma unroll
+    for (int i = 0; i < MI; ++i) {
+      u32x4 v[NJ];
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+        v[j] = __builtin_amdgcn_raw_buffer_load_b128(ws, (uint32_t)(((wave * NBLK + i * NJ + j) * 64 + lane) * 16), 0,
+                                                     CPOL_SC0_SC1);
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) acc[i][j] += __builtin_bit_cast(f32x4, v[j]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
 
   // ---- epilogue: a quad transpose gives each lane 4 consecutive columns of
   // one row (rows 4 kq + q of each block, q = lane & 3)
@@ -1180,6 +1252,8 @@ namespace {
 
 struct Plan {
   int bm_main, split, bm_tail;  // columns [0, split) at bm_main, [split, nbn) at bm_tail
+  int split_k;                  // 2: columns [split, nbn) as split-k pairs of 256-row tiles
+  int64_t cost;
 };
 
 // 256-row tiles switch from eight waves to four (one per SIMD) from this
@@ -1200,13 +1274,13 @@ int64_t cost(int64_t M, int64_t cols, int bmt, int groups) {
 
 Plan plan_for(int64_t M, int64_t nbn, int groups) {
   static const int H[3] = {256, 192, 128};
-  Plan best{256, (int)nbn, 256};
+  Plan best{256, (int)nbn, 256, 0, 0};
   int64_t best_cost = cost(M, nbn, 256, groups);
   for (int hm : H) {
     const int64_t one = cost(M, nbn, hm, groups);
     if (one < best_cost) {
       best_cost = one;
-      best = Plan{hm, (int)nbn, hm};
+      best = Plan{hm, (int)nbn, hm, 0, 0};
     }
     for (int64_t split = 1; split < nbn; ++split)
       for (int ht : H) {
@@ -1214,11 +1288,73 @@ Plan plan_for(int64_t M, int64_t nbn, int groups) {
         const int64_t c = cost(M, split, hm, groups) + cost(M, nbn - split, ht, groups);
         if (c < best_cost) {
           best_cost = c;
-          best = Plan{hm, (int)split, ht};
+          best = Plan{hm, (int)split, ht, 0, 0};
         }
       }
   }
+  best.cost = best_cost;
   return best;
+}
+
+// Split-k tail (single 16x16-kernel launches with bf16 outputs): the first
+// tile columns on whole rounds of 256-row tiles, the last ones as pairs of
+// workgroups that each sum half of k, when that round of half-depth
+// 256-row tiles (cost 256 + 256 per pair of halves, i.e. 256 per workgroup
+// round) beats the best plain plan.  At the 70B shard's SwiGLU GEMM (32 x 28
+// tiles): 768 tiles on 3 rounds, then 128 tiles as 256 half-k workgroups,
+// instead of the 4 tile columns as a round of 128-row tiles.
+constexpr int SK_MAX_TILES = 128;
+
+Plan plan_with_split(int64_t M, int64_t nbn, int64_t K, int groups, bool bf16_out) {
+  Plan p = plan_for(M, nbn, groups);
+  const int64_t nk = (K + BK - 1) / BK;
+  if (!bf16_out || groups != 1 || K < MFMA16_MIN_K || nk < 4) return p;
+  const int64_t nbm = (M + 255) / 256;
+  for (int64_t c = nbn - 1; c >= 0; --c) {
+    const int64_t main_t = nbm * c, tail_t = nbm * (nbn - c);
+    if (2 * tail_t > 2 * SK_MAX_TILES || 2 * tail_t > 256) break;  // fewer main columns only add tail tiles
+    if (main_t % 256 != 0) continue;
+    const int64_t c_split = rounds_of(main_t) * (256 + 256) + 256;
+    if (c_split < p.cost) p = Plan{256, (int)c, 256, 2, c_split};
+    break;
+  }
+  return p;
+}
+
+// Workspace of the split-k pairs: one float32 256 x 256 partial and one flag
+// per tile, per (device, stream), allocated at the first split launch on that
+// stream and kept until the process ends (calls on one stream are ordered;
+// calls on different streams use different workspaces).  A flag holds the
+// epoch of the launch that last raised it, so it is never cleared.
+struct SkSlot {
+  float* ws = nullptr;
+  unsigned* flag = nullptr;
+  unsigned epoch = 0;
+};
+std::mutex g_sk_mu;
+std::map<std::pair<int, hipStream_t>, SkSlot> g_sk;
+
+// The slot for this stream with its epoch advanced, or NULL when it cannot be
+// allocated (the caller then runs the plain plan).
+SkSlot* sk_acquire(hipStream_t s, unsigned* epoch) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return nullptr;
+  std::lock_guard<std::mutex> lock(g_sk_mu);
+  SkSlot& slot = g_sk[{dev, s}];
+  if (!slot.ws) {
+    constexpr size_t ws_bytes = (size_t)SK_MAX_TILES * 256 * BN * sizeof(float);
+    void* p = nullptr;
+    if (hipMalloc(&p, ws_bytes + SK_MAX_TILES * sizeof(unsigned)) != hipSuccess) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    slot.ws = static_cast<float*>(p);
+    slot.flag = reinterpret_cast<unsigned*>(static_cast<char*>(p) + ws_bytes);
+    if (hipMemsetAsync(slot.flag, 0, SK_MAX_TILES * sizeof(unsigned), s) != hipSuccess) return nullptr;
+  }
+  *epoch = ++slot.epoch;
+  if (*epoch == 0) *epoch = ++slot.epoch;  // 0 is the flags' initial value
+  return &slot;
 }
 
 template <int EPI, int BMT>
@@ -1230,7 +1366,8 @@ void launch_part(Args a, int bn0, int cols, int groups, hipStream_t s) {
   if (nb == 0) return;
   if constexpr (EPI != EPI_QKV) {
     if (a.K >= MFMA16_MIN_K) {
-      hipLaunchKernelGGL((gemm16_kernel<EPI, BMT>), dim3(nb, groups), dim3(256), 0, s, a);
+      hipLaunchKernelGGL((gemm16_kernel<EPI, BMT>), dim3(a.sk_ws ? 16 * ((nb + 7) / 8) : nb, groups), dim3(256), 0,
+                         s, a);
       return;
     }
   }
@@ -1243,7 +1380,22 @@ void launch_part(Args a, int bn0, int cols, int groups, hipStream_t s) {
 
 template <int EPI>
 void launch_planned(const Args& a, int64_t nbn, int groups, hipStream_t s) {
-  const Plan p = plan_for(a.M, nbn, groups);
+  constexpr bool BF16_OUT = EPI == EPI_BF16 || is_gelu(EPI) || is_swiglu(EPI);
+  const Plan p = plan_with_split(a.M, nbn, a.K, groups, BF16_OUT);
+  if constexpr (BF16_OUT) {
+    unsigned epoch = 0;
+    SkSlot* sk = p.split_k ? sk_acquire(s, &epoch) : nullptr;
+    if (sk) {
+      if (p.split > 0) launch_part<EPI, 256>(a, 0, p.split, 1, s);
+      Args b = a;
+      b.sk_ws = sk->ws;
+      b.sk_flag = sk->flag;
+      b.sk_epoch = epoch;
+      b.sk_half = (int)((a.K + BK - 1) / BK / 2);
+      launch_part<EPI, 256>(b, p.split, (int)(nbn - p.split), 1, s);
+      return;
+    }
+  }
   auto part = [&](int bmt, int bn0, int cols) {
     switch (bmt) {
       case 256: launch_part<EPI, 256>(a, bn0, cols, groups, s); break;
@@ -1251,19 +1403,28 @@ void launch_planned(const Args& a, int64_t nbn, int groups, hipStream_t s) {
       default: launch_part<EPI, 128>(a, bn0, cols, groups, s); break;
     }
   };
+  if (p.split_k) {  // no workspace: the plain plan
+    const Plan q = plan_for(a.M, nbn, groups);
+    part(q.bm_main, 0, q.split);
+    if (q.split < nbn) part(q.bm_tail, q.split, (int)(nbn - q.split));
+    return;
+  }
   part(p.bm_main, 0, p.split);
   if (p.split < nbn) part(p.bm_tail, p.split, (int)(nbn - p.split));
 }
 
 }  // namespace
 
-void gemm_plan(int64_t M, int64_t N, int swiglu, int groups, int* bm_main, int* split,
-               int* bm_tail) {
+void gemm_plan(int64_t M, int64_t N, int64_t K, int kind, int groups, int* bm_main, int* split, int* bm_tail,
+               int* split_k) {
+  const bool swiglu = kind == GEMM_PLAN_SWIGLU;
   const int64_t nbn = (N + (swiglu ? BN / 2 : BN) - 1) / (swiglu ? BN / 2 : BN);
-  const Plan p = plan_for(M, nbn, groups);
+  const bool bf16_out = kind == GEMM_PLAN_COLWISE || kind == GEMM_PLAN_SWIGLU;
+  const Plan p = plan_with_split(M, nbn, K, groups, bf16_out);
   *bm_main = p.bm_main;
   *split = p.split;
   *bm_tail = p.bm_tail;
+  *split_k = p.split_k;
 }
 
 hipError_t launch_gemm_bf16_group(int epi, int groups, int64_t M, int64_t N, int64_t K,
@@ -1286,6 +1447,10 @@ hipError_t launch_gemm_bf16_group(int epi, int groups, int64_t M, int64_t N, int
   a.lda = lda > 0 ? lda : K;
   a.bias = bias;
   a.num_bm = a.num_bn = a.bn0 = 0;
+  a.sk_ws = nullptr;
+  a.sk_flag = nullptr;
+  a.sk_epoch = 0;
+  a.sk_half = 0;
   if (qkv) a.qkv = *qkv; else a.qkv = QkvOut{};
   const int64_t bn_cols = is_swiglu(epi) ? BN / 2 : BN;
   const int64_t nbn = (N + bn_cols - 1) / bn_cols;

@@ -40,11 +40,14 @@ hipError_t launch_gemm_bf16(int epi, int64_t M, int64_t N, int64_t K, const void
                             void* out, const QkvOut* qkv, hipStream_t s, const float* bias = nullptr,
                             int64_t lda = 0, void* pre = nullptr);
 
-// Tile heights the bf16 GEMM launches for an M x N output (N = output
-// columns): columns [0, split) at height bm_main, the rest at bm_tail.
-// groups: independent GEMMs of the same shape launched together.
-void gemm_plan(int64_t M, int64_t N, int swiglu, int groups, int* bm_main, int* split,
-               int* bm_tail);
+// Tile heights the bf16 GEMM launches for an M x N x K GEMM of a kind
+// (N = output columns): columns [0, split) at height bm_main, the rest at
+// bm_tail, or, with split_k = 2, as pairs of workgroups that each sum half of
+// K over 256-row tiles.  groups: independent GEMMs of the same shape launched
+// together.
+enum { GEMM_PLAN_ROWWISE = 0, GEMM_PLAN_COLWISE = 1, GEMM_PLAN_SWIGLU = 2, GEMM_PLAN_QKV = 3 };
+void gemm_plan(int64_t M, int64_t N, int64_t K, int kind, int groups, int* bm_main, int* split, int* bm_tail,
+               int* split_k);
 
 // G (<= 16) GEMMs of the same shape in one launch: out[g] = epi(x[g] . w[g]^T).
 hipError_t launch_gemm_bf16_group(int epi, int groups, int64_t M, int64_t N, int64_t K,

@@ -58,7 +58,7 @@ _SIGS = {
     "tp_rmsnorm": [_i32, _i64, _i64, _vp, _vp, _f32, _vp, _vp],
     "tp_shard_sum_rmsnorm": [_i32, _i64, _i64, _i64, _i64, ctypes.POINTER(_vp), _vp, _vp, _i32, _vp, _vp,
                              _f32, _vp, _vp],
-    "tp_gemm_plan": [_i64, _i64, _i32, ctypes.POINTER(_i32), ctypes.POINTER(_i32), ctypes.POINTER(_i32)],
+    "tp_gemm_plan": [_i64, _i64, _i64, _i32] + [ctypes.POINTER(_i32)] * 4,
     "tp_embedding": [_i64, _i64, _i64, _i64, _vp, _vp, _vp, _i64, _vp],
     "tp_shard_mlp_backward_workspace_bytes": [_i32, _i64, _i64, _i64],
     "tp_shard_mlp_backward": [_i32, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t,
@@ -144,11 +144,16 @@ def tp_last_error() -> str:
     return lib().tp_last_error().decode()
 
 
-def tp_gemm_plan(m, n, swiglu=False) -> tuple[int, int, int]:
-    """(bm_main, split, bm_tail) of the bf16 GEMM for an m x n output."""
-    a, b, c = _i32(), _i32(), _i32()
-    _check(lib().tp_gemm_plan(m, n, int(bool(swiglu)), ctypes.byref(a), ctypes.byref(b), ctypes.byref(c)))
-    return a.value, b.value, c.value
+_PLAN_KIND = {"rowwise": 0, "colwise": 1, "swiglu": 2, "qkv": 3}
+
+
+def tp_gemm_plan(m, n, k=64, kind="rowwise") -> tuple[int, int, int, int]:
+    """(bm_main, split, bm_tail, split_k) of the bf16 GEMM for an m x n output
+    over depth k; kind is "rowwise", "colwise", "swiglu" or "qkv"."""
+    a, b, c, d = _i32(), _i32(), _i32(), _i32()
+    _check(lib().tp_gemm_plan(m, n, k, _PLAN_KIND[kind], ctypes.byref(a), ctypes.byref(b), ctypes.byref(c),
+                              ctypes.byref(d)))
+    return a.value, b.value, c.value, d.value
 
 
 def tp_device_check() -> None:

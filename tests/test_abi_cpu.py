@@ -165,15 +165,25 @@ def test_rmsnorm_validation(L):
 
 
 def test_gemm_plans(L):
-    """Tile-height plans of the workload shapes (host-only call)."""
-    assert tp.tp_gemm_plan(8192, 3584, True) == (256, 24, 128)    # SwiGLU, 70B t=8: tail at 128
-    assert tp.tp_gemm_plan(8192, 8192) == (256, 32, 256)          # down proj / o_proj
-    assert tp.tp_gemm_plan(8192, 1280) == (192, 5, 192)           # QKV, 70B t=8
-    assert tp.tp_gemm_plan(8192, 768) == (128, 3, 128)            # QKV, 70B t=16
-    assert tp.tp_gemm_plan(4096, 3584, True) == (256, 28, 256)    # SwiGLU, Llama-8B
-    assert tp.tp_gemm_plan(2048, 1024) == (128, 4, 128)           # GPT MLP
+    """Tile plans of the workload shapes (host-only call)."""
+    # SwiGLU, 70B t=8: 24 tile columns on 3 whole rounds, the last 4 as split-k pairs
+    assert tp.tp_gemm_plan(8192, 3584, 8192, "swiglu") == (256, 24, 256, 2)
+    assert tp.tp_gemm_plan(8192, 8192, 3584) == (256, 32, 256, 0)          # down proj
+    assert tp.tp_gemm_plan(8192, 8192, 1024) == (256, 32, 256, 0)          # o_proj
+    assert tp.tp_gemm_plan(8192, 1280, 8192, "qkv") == (192, 5, 192, 0)    # QKV, 70B t=8
+    assert tp.tp_gemm_plan(8192, 768, 8192, "qkv") == (128, 3, 128, 0)     # QKV, 70B t=16
+    assert tp.tp_gemm_plan(4096, 3584, 4096, "swiglu") == (256, 28, 256, 0)  # SwiGLU, Llama-8B
+    assert tp.tp_gemm_plan(2048, 1024, 1024, "colwise") == (128, 4, 128, 0)  # GPT MLP
+    # split-k only for bf16 outputs of depth >= 4096
+    assert tp.tp_gemm_plan(520, 768, 4104, "colwise") == (256, 0, 256, 2)
+    assert tp.tp_gemm_plan(520, 768, 4104, "rowwise")[3] == 0
+    assert tp.tp_gemm_plan(520, 768, 4032, "colwise")[3] == 0
+    assert tp.tp_gemm_plan(520, 1280, 8192, "qkv")[3] == 0
     with pytest.raises(tp.TpError):
         tp.tp_gemm_plan(0, 16)
+    with pytest.raises(tp.TpError):
+        tp.tp_gemm_plan(16, 16, 0)
+    assert L.tp_gemm_plan(16, 16, 16, 7, *[ctypes.byref(ctypes.c_int32()) for _ in range(4)]) == tp.TP_ERR_INVALID_ARG
 
 
 def test_binding_raises_with_message(L):

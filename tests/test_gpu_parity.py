@@ -122,7 +122,7 @@ def test_rowwise_gemm_integer_bit_exact(device, m, k, n):
 def test_rowwise_gemm_plans_bit_exact(device, m, k, n, plan):
     """Every tile height and the split launch, bit-exact on integer inputs."""
     say(f"case rowwise plan m={m} k={k} n={n} plan={plan}")
-    assert tp.tp_gemm_plan(m, n) == plan
+    assert tp.tp_gemm_plan(m, n, k) == (*plan, 0)
     y = inputs.integers(9, 0, (m, k), -2, 2)
     w = inputs.integers(9, 1, (n, k), -2, 2)
     out = torch.empty(m, n, dtype=torch.float32, device=device)
@@ -141,7 +141,7 @@ def test_rowwise_gemm_many_tiles_bit_exact(device, m, k, n, plan):
     """Several rounds of tiles per launch (more tiles than compute units),
     ragged m and n, with and without a k tail: bit-exact on integer inputs."""
     say(f"case rowwise many tiles m={m} k={k} n={n} plan={plan}")
-    assert tp.tp_gemm_plan(m, n) == plan
+    assert tp.tp_gemm_plan(m, n, k) == (*plan, 0)
     y = inputs.integers(10, 0, (m, k), -2, 2)
     w = inputs.integers(10, 1, (n, k), -2, 2)
     out = torch.full((m, n), float("nan"), dtype=torch.float32, device=device)
@@ -171,6 +171,39 @@ def test_colwise_none_many_tiles_bit_exact(device, m, k, n):
     tp.tp_colwise("none", "bf16", m, k, n, to_dev(x, device), to_dev(w, device), out)
     torch.cuda.synchronize()
     assert np.array_equal(host(out), _bf16_rne(ref))
+
+
+@pytest.mark.parametrize("m,k,n,plan", [
+    (2048, 4104, 12288, (256, 32, 256, 2)),   # a round of whole tiles, then 128 tiles as split-k pairs, k tail
+    (2000, 4096, 12288, (256, 32, 256, 2)),   # ragged m, whole k-steps
+    (520, 4104, 768, (256, 0, 256, 2)),       # split-k pairs only
+])
+def test_colwise_split_k_bit_exact(device, m, k, n, plan):
+    """Tiles summed by two workgroups (half of k each, the partial handed over
+    through the split workspace): bf16 outputs of integer inputs in {-1, 0, 1}
+    equal the rounding of the exact sums, twice in a row on one stream (the
+    flags' epoch advances) and once on a second stream (its own workspace)."""
+    say(f"case colwise split-k m={m} k={k} n={n} plan={plan}")
+    assert tp.tp_gemm_plan(m, n, k, "colwise") == plan
+    x = inputs.integers(12, 0, (m, k), -1, 1)
+    w = inputs.integers(12, 1, (n, k), -1, 1)
+    ref = _bf16_rne(x.f64() @ w.f64().T)
+    dx, dw = to_dev(x, device), to_dev(w, device)
+    outs = []
+    side = torch.cuda.Stream(device)
+    for stream in (None, None, side):
+        out = torch.full((m, n), float("nan"), dtype=torch.bfloat16, device=device)
+        if stream is None:
+            tp.tp_colwise("none", "bf16", m, k, n, dx, dw, out)
+        else:
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                tp.tp_colwise("none", "bf16", m, k, n, dx, dw, out, stream=side)
+            torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        outs.append(host(out))
+    for o in outs:
+        assert np.array_equal(o, ref)
 
 
 @pytest.mark.parametrize("m,k,n", [(300, 40, 264), (64, 48, 512)])
@@ -926,12 +959,14 @@ def test_colwise_activation_slices(device):
     ("swiglu", 4000, 4104, 2048, (256, 16, 256)),   # 16x16-MFMA tiles, ragged m, k tail
     ("gelu", 4000, 4104, 4000, (256, 16, 256)),     # 16x16-MFMA tiles, ragged m and n
     ("swiglu", 5000, 4104, 1792, (192, 8, 128)),    # 16x16-MFMA 192/128 split, ragged m, k tail
+    ("swiglu", 2048, 4104, 6144, (256, 32, 256, 2)),   # one round, then split-k pairs (k tail in the upper half)
+    ("gelu", 2000, 4104, 12288, (256, 32, 256, 2)),    # the same with GeLU, ragged m
 ])
 def test_colwise_activation_tile_heights(device, act, m, h, f, plan):
     """GeLU and SwiGLU epilogues (gate/up pairing, 4-column stores) at every
     tile layout, ragged m, against the oracle's activation."""
     say(f"case {act} colwise m={m} h={h} f={f} plan={plan}")
-    assert tp.tp_gemm_plan(m, f, act == "swiglu") == plan
+    assert tp.tp_gemm_plan(m, f, h, "swiglu" if act == "swiglu" else "colwise") == (plan + (0,))[:4]
     case = inputs.MLPCase("heights", m, h, f, 1, act, "bf16", seed=24)
     w = inputs.gen_mlp(case)
     dw = {k: to_dev(v, device) for k, v in w.items()}
