@@ -9,10 +9,16 @@ SQ_VALU_MFMA_BUSY_CYCLES were both collected, the matrix-core busy share
 SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs) and the
 mean graphics clock GRBM_GUI_ACTIVE / 8 / duration.
 
+Per-workload reports (``bench.py --configs`` JSON lines): one markdown table
+row per measured call, its synchronised median/minimum and, where measured,
+its back-to-back mean (calls issued without synchronisation, as in a model).
+
 Usage: python -m megatron_tensor_transformer_colwise_amd.profsummary RESULTS_DB
        python -m megatron_tensor_transformer_colwise_amd.profsummary --pmc RESULTS_DB
+       python -m megatron_tensor_transformer_colwise_amd.profsummary --configs JSONL
 """
 import collections
+import json
 import sqlite3
 import sys
 
@@ -67,8 +73,83 @@ def pmc_summary(db_path: str) -> str:
     return "\n".join(lines)
 
 
+def _pct(tflops) -> float:
+    return round(tflops / 25.0, 2)  # of the published 2500 TFLOP/s
+
+
+def configs_table(path: str) -> str:
+    rows = [json.loads(line) for line in open(path) if line.strip()]
+    out = ["| workload | call | median ms | min ms | TFLOP/s | % MFMA peak | back-to-back ms (TFLOP/s, % peak) "
+           "| shard-sum GB/s (% HBM) |",
+           "|---|---|---|---|---|---|---|---|"]
+
+    def row(w, call, ms="", mn="", tf="", pct="", b2b="", gbs=""):
+        out.append(f"| {w} | {call} | {ms} | {mn} | {tf} | {pct} | {b2b} | {gbs} |")
+
+    def b2b(r, prefix=""):
+        k = prefix + "b2b_ms"
+        if k not in r:
+            return ""
+        tf = r[prefix + "b2b_tflops"]
+        return f"{r[k]} ({tf}, {_pct(tf)})"
+
+    for r in rows:
+        w = r["workload"]
+        if w == "packed_single_stream":
+            row(f"{w} ({r['shape']})", r["call"], r["ms"], r["min_ms"], r["tflops"], r["pct_mfma_peak"])
+            row(w, "all 4 ranks + the sum of 8 partials", r["all_ranks_and_sum_ms"], "", r["all_ranks_tflops"],
+                _pct(r["all_ranks_tflops"]))
+        elif w == "llama70b_mlp_backward_t8":
+            row(f"{w} ({r['shape']})", f"{r['call']}: recomputed pre-activation + 5 GEMMs + transposes", r["ms"],
+                r["min_ms"], r["tflops"], r["pct_mfma_peak"])
+        elif w == "llama70b_attn_backward_t8":
+            row(f"{w} ({r['shape']})", r["call"], r["ms"], r["min_ms"], r["tflops"], r["pct_mfma_peak"])
+            row(w, r["core_call"], r["core_ms"], r["core_min_ms"], r["core_tflops"], r["core_pct_mfma_peak"])
+        elif w == "vocab_parallel_ce":
+            row(f"{w} ({r['shape']})", r["call"], r["ms"], r["min_ms"], r["tflops"], r["pct_mfma_peak"])
+            row(w, "statistics kernel alone (one rank's [m, v/t] float32 logits)", r["stats_ms"], gbs=
+                f"{r['stats_gbs']} ({round(r['stats_gbs'] / 80, 1)})")
+            row(w, "all 4 ranks + the combination", r["all_ranks_and_combine_ms"], "", r["all_ranks_tflops"],
+                _pct(r["all_ranks_tflops"]))
+        elif "call" in r:
+            row(w, r["call"], r["ms"], r["min_ms"], r["tflops"], r["pct_mfma_peak"], b2b(r),
+                f"{r['shard_sum_gbs']} ({r['shard_sum_pct_hbm']})")
+            if "grouped_all_ranks_ms" in r:
+                row(w, "tp_shard_mlp_group (all ranks, one launch pair)", r["grouped_all_ranks_ms"],
+                    r["grouped_min_ms"], r["grouped_tflops"], _pct(r["grouped_tflops"]))
+        else:
+            row(w, "tp_shard_attn (rank 0)", r["attn_call_ms"], r["attn_min_ms"], r["attn_tflops"],
+                r["attn_pct_mfma_peak"], b2b(r, "attn_"))
+            row(w, "tp_shard_mlp (rank 0)", r["mlp_call_ms"], r["mlp_min_ms"], r["mlp_tflops"],
+                r["mlp_pct_mfma_peak"], b2b(r, "mlp_"))
+            row(w, "shard-sum of the MLP partials + f32 residual", r["shard_sum_ms"], r["shard_sum_min_ms"],
+                gbs=f"{r['shard_sum_gbs']} ({r['shard_sum_pct_hbm']})")
+            row(w, "whole block, all ranks (forward)", r["block_step_ms"], r["block_step_min_ms"],
+                r["block_step_tflops"], _pct(r["block_step_tflops"]))
+            if "block_backward_step_ms" in r:
+                row(w, "whole block backward, all ranks (after the forward)", r["block_backward_step_ms"],
+                    r["block_backward_step_min_ms"], r["block_backward_step_tflops"],
+                    _pct(r["block_backward_step_tflops"]))
+                row(w, "sum of the MLP dX partials + RMSNorm backward + dZ (dh1, float32 and bf16, dgain)",
+                    r["norm_backward_ms"], gbs=f"{r['norm_backward_gbs']} ({round(r['norm_backward_gbs'] / 80, 1)})")
+            if "sequence_parallel_backward_step_ms" in r:
+                row(w, "whole block backward, sequence-parallel form", r["sequence_parallel_backward_step_ms"], "",
+                    r["sequence_parallel_backward_step_tflops"], _pct(r["sequence_parallel_backward_step_tflops"]))
+            if "saved_backward_step_ms" in r:
+                row(w, "whole block forward keeping its activations, all ranks", r["saving_forward_step_ms"])
+                row(w, "whole block backward from the saved activations, all ranks", r["saved_backward_step_ms"],
+                    r["saved_backward_step_min_ms"], r["saved_backward_step_tflops"],
+                    _pct(r["saved_backward_step_tflops"]))
+            if "sequence_parallel_step_ms" in r:
+                row(w, "whole block, sequence-parallel form", r["sequence_parallel_step_ms"], "",
+                    r["sequence_parallel_step_tflops"], _pct(r["sequence_parallel_step_tflops"]))
+    return "\n".join(out)
+
+
 if __name__ == "__main__":
     if sys.argv[1] == "--pmc":
         print(pmc_summary(sys.argv[2]))
+    elif sys.argv[1] == "--configs":
+        print(configs_table(sys.argv[2]))
     else:
         print(summary(sys.argv[1]))
