@@ -186,7 +186,12 @@ tp_status tp_qkv_rope(int64_t batch, int64_t seq, int64_t h, int32_t hq, int32_t
  *             query head j of the rank reading KV head j / (hq / hkv);
  *             causal != 0 lets position p see positions <= p of its own
  *             sequence, causal == 0 all positions of its sequence.
- * hq must be a multiple of hkv; d must be 128.
+ * hq must be a multiple of hkv; d must be 128.  When the launch cuts query
+ * blocks over workgroups (tp_flash_attn_plan), their float32 partials pass
+ * through a workspace of the library, one per (device, stream), allocated
+ * (about 34 MB) at the first such launch on a stream and kept until the
+ * process ends; if that allocation fails the launch runs uncut.  This also
+ * holds for tp_flash_attn_lse and tp_shard_attn.
  * ------------------------------------------------------------------------ */
 tp_status tp_flash_attn(int64_t batch, int64_t seq, int32_t hq, int32_t hkv, int32_t head_dim,
                         int32_t causal, const void* q, const void* k, const void* vt, void* o,
@@ -215,19 +220,24 @@ tp_status tp_shard_attn(tp_dtype dt, int64_t batch, int64_t seq, int64_t h, int3
  * tp_shard_attn without a workspace argument, for callers that cannot
  * allocate device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid hipMalloc).  Same arguments, kernels and results as
- * tp_shard_attn; the q, k, vt and o workspace is instead a static device
- * array of the library holding 64 MiB (TP_STATIC_SCRATCH_BYTES) on every
- * device it runs on, from the first call on that device until the process
- * ends.  Nothing is allocated or freed by the call.
+ * tp_shard_attn; the q, k, vt and o workspace, and the attention's cut-block
+ * partials and their flags, are instead a static device array of the
+ * library holding 64 MiB (TP_STATIC_SCRATCH_BYTES) on every device it runs
+ * on, from the first call on that device until the process ends.  Nothing
+ * is allocated or freed by the call.
  *
- *   - A shape whose tp_shard_attn_workspace_bytes(...) exceeds 64 MiB returns
- *     TP_ERR_WORKSPACE before anything is enqueued (every configuration of
- *     this library's workloads fits: 36 MiB at batch 4 x seq 2048 with 8
- *     query heads and 1 KV head).
+ *   - A shape whose tp_shard_attn_workspace_bytes(...), plus its cut-block
+ *     partials ((pieces - 1) x ceil(ceil(seq/128)/2) x batch x hq slots of
+ *     66560 bytes, pieces from tp_flash_attn_plan) and 2 KiB of flags,
+ *     exceeds 64 MiB returns TP_ERR_WORKSPACE before anything is enqueued
+ *     (every configuration of this library's workloads fits: 36 + 16.3 MiB
+ *     at batch 4 x seq 2048 with 8 query heads and 1 KV head).
  *   - Every call on one device shares that device's array, which keeps the
  *     last call's contents; each call writes every byte it later reads (the
- *     transposed-V padding is zeroed by a kernel of the call), so no state
- *     carries over.  Calls that overlap on one device (e.g. on two streams,
+ *     transposed-V padding is zeroed by a kernel of the call), except the
+ *     flags, which only ever hold the epoch of the call that raised them
+ *     (a per-device count, so a flag left by an earlier call never matches
+ *     a later one).  Calls that overlap on one device (e.g. on two streams,
  *     or from two threads before the first has drained) race on the array:
  *     the caller must order them.
  *   - The first call on a device looks up the array's device address
@@ -504,6 +514,21 @@ tp_status tp_shard_attn_backward(int64_t batch, int64_t seq, int64_t h, int32_t 
 enum { TP_PLAN_ROWWISE = 0, TP_PLAN_COLWISE = 1, TP_PLAN_SWIGLU = 2, TP_PLAN_QKV = 3 };
 tp_status tp_gemm_plan(int64_t m, int64_t n, int64_t k, int32_t kind, int32_t* bm_main, int32_t* split,
                        int32_t* bm_tail, int32_t* split_k);
+
+/* --------------------------------------------------------------------------
+ * Introspection: how tp_flash_attn, tp_flash_attn_lse and the attention
+ * sublayer calls share the attention of batch x hq heads over seq tokens
+ * among workgroups ("Self-attention" section: each head independent).
+ * Query blocks of 128 rows are taken in pairs (p, last - p), so every pair
+ * holds about the same causal work, and each pair's key tiles (64 keys) are
+ * cut into *pieces equal ranges, one workgroup each (1: every query block
+ * in one workgroup).  A block whose keys span pieces is completed by the
+ * piece holding its last key tile, which merges the float32 partials of
+ * the others (running max, sum and unnormalised output) in piece order.
+ * Host-only; launches nothing.  TP_ERR_SHAPE for a negative batch or seq or
+ * hq < 1, TP_ERR_INVALID_ARG for a NULL output.
+ * ------------------------------------------------------------------------ */
+tp_status tp_flash_attn_plan(int64_t batch, int64_t seq, int32_t hq, int32_t causal, int32_t* pieces);
 
 /* Message for the calling thread's last error ("" if none). */
 const char* tp_last_error(void);

@@ -230,6 +230,13 @@ extern "C" {
 
 const char* tp_last_error(void) { return g_err; }
 
+tp_status tp_flash_attn_plan(int64_t batch, int64_t seq, int32_t hq, int32_t causal, int32_t* pieces) {
+  if (batch < 0 || seq < 0 || hq < 1) return fail(TP_ERR_SHAPE, "batch and seq must be >= 0 and hq >= 1");
+  if (!pieces) return fail(TP_ERR_INVALID_ARG, "NULL output pointer");
+  *pieces = tpk::flash_attn_pieces(batch, seq, hq, causal ? 1 : 0);
+  return ok();
+}
+
 tp_status tp_gemm_plan(int64_t m, int64_t n, int64_t k, int32_t kind, int32_t* bm_main, int32_t* split,
                        int32_t* bm_tail, int32_t* split_k) {
   if (m <= 0 || n <= 0 || k <= 0) return fail(TP_ERR_SHAPE, "m, n and k must be positive");
@@ -646,12 +653,13 @@ size_t tp_shard_attn_workspace_bytes(int64_t batch, int64_t seq, int32_t hq, int
   return attn_layout(batch, seq, hq, hkv, head_dim).total;
 }
 
-tp_status tp_shard_attn(tp_dtype dt, int64_t batch, int64_t seq, int64_t h, int32_t hq, int32_t hkv,
-                        int32_t head_dim, float rope_base, int32_t causal, const void* x,
-                        const void* w_qkv, const void* w_o, void* ws, size_t ws_bytes,
-                        float* partial, void* stream) {
-  if (dt == TP_F32) return fail(TP_ERR_UNSUPPORTED, "tp_shard_attn: only bf16 attention is built");
-  if (dt != TP_BF16) return fail(TP_ERR_INVALID_ARG, "unknown dtype %d", (int)dt);
+namespace {
+
+// tp_shard_attn with the flash attention's split workspace given (NULL: the
+// library's per-stream one).
+tp_status shard_attn(int64_t batch, int64_t seq, int64_t h, int32_t hq, int32_t hkv, int32_t head_dim,
+                     float rope_base, int32_t causal, const void* x, const void* w_qkv, const void* w_o, void* ws,
+                     size_t ws_bytes, float* partial, void* stream, const tpk::FaSplitWs* fws) {
   TRY(check_attn_shape(batch, seq, hq, hkv, head_dim));
   const int64_t m = batch * seq;
   const int64_t qd = (int64_t)hq * head_dim;
@@ -664,9 +672,22 @@ tp_status tp_shard_attn(tp_dtype dt, int64_t batch, int64_t seq, int64_t h, int3
   char* base = static_cast<char*>(ws);
   TRY(tp_qkv_rope(batch, seq, h, hq, hkv, head_dim, rope_base, x, w_qkv, nullptr, base + L.q, base + L.k,
                   base + L.vt, stream));
-  TRY(tp_flash_attn(batch, seq, hq, hkv, head_dim, causal, base + L.q, base + L.k, base + L.vt,
-                    base + L.o, stream));
+  TRY(launched(tpk::launch_flash_attn(batch, seq, seq_pad_of(seq), hq, hkv, causal, base + L.q, base + L.k,
+                                      base + L.vt, base + L.o, as_stream(stream), nullptr, fws),
+               "tp_flash_attn"));
   return tp_rowwise(TP_BF16, m, qd, h, base + L.o, w_o, partial, stream);
+}
+
+}  // namespace
+
+tp_status tp_shard_attn(tp_dtype dt, int64_t batch, int64_t seq, int64_t h, int32_t hq, int32_t hkv,
+                        int32_t head_dim, float rope_base, int32_t causal, const void* x,
+                        const void* w_qkv, const void* w_o, void* ws, size_t ws_bytes,
+                        float* partial, void* stream) {
+  if (dt == TP_F32) return fail(TP_ERR_UNSUPPORTED, "tp_shard_attn: only bf16 attention is built");
+  if (dt != TP_BF16) return fail(TP_ERR_INVALID_ARG, "unknown dtype %d", (int)dt);
+  return shard_attn(batch, seq, h, hq, hkv, head_dim, rope_base, causal, x, w_qkv, w_o, ws, ws_bytes, partial,
+                    stream, nullptr);
 }
 
 tp_status tp_shard_attn_noalloc(tp_dtype dt, int64_t batch, int64_t seq, int64_t h, int32_t hq, int32_t hkv,
@@ -675,7 +696,10 @@ tp_status tp_shard_attn_noalloc(tp_dtype dt, int64_t batch, int64_t seq, int64_t
   if (dt == TP_F32) return fail(TP_ERR_UNSUPPORTED, "tp_shard_attn_noalloc: only bf16 attention is built");
   if (dt != TP_BF16) return fail(TP_ERR_INVALID_ARG, "unknown dtype %d", (int)dt);
   TRY(check_attn_shape(batch, seq, hq, hkv, head_dim));
-  const size_t need = attn_layout(batch, seq, hq, hkv, head_dim).total;
+  // the array: the split flags, then q, k, vt and o, then the split partials
+  const size_t layout = attn_layout(batch, seq, hq, hkv, head_dim).total;
+  const size_t split = tpk::flash_attn_split_bytes(batch, seq, hq, causal ? 1 : 0);
+  const size_t need = tpk::kStaticFlagBytes + layout + split;
   if (need > tpk::kStaticScratchBytes)
     return fail(TP_ERR_WORKSPACE,
                 "tp_shard_attn_noalloc: this shape needs %zu bytes of workspace, beyond the %zu-byte static "
@@ -683,11 +707,18 @@ tp_status tp_shard_attn_noalloc(tp_dtype dt, int64_t batch, int64_t seq, int64_t
                 need, tpk::kStaticScratchBytes);
   if (batch * seq == 0) return ok();
   TRY(device_check());
-  void* ws = nullptr;
-  const hipError_t e = tpk::static_scratch(&ws);
+  void* base = nullptr;
+  hipError_t e = tpk::static_scratch(&base);
   if (e != hipSuccess) return fail(TP_ERR_HIP, "static scratch address lookup failed: %s", hipGetErrorString(e));
-  return tp_shard_attn(dt, batch, seq, h, hq, hkv, head_dim, rope_base, causal, x, w_qkv, w_o, ws,
-                       tpk::kStaticScratchBytes, partial, stream);
+  tpk::FaSplitWs fws;
+  e = tpk::static_scratch_epoch(&fws.epoch);
+  if (e != hipSuccess) return fail(TP_ERR_HIP, "static scratch epoch: %s", hipGetErrorString(e));
+  char* const b = static_cast<char*>(base);
+  fws.flag = reinterpret_cast<unsigned*>(b);
+  char* const ws = b + tpk::kStaticFlagBytes;
+  fws.part = reinterpret_cast<float*>(ws + layout);
+  return shard_attn(batch, seq, h, hq, hkv, head_dim, rope_base, causal, x, w_qkv, w_o, ws, layout, partial,
+                    stream, &fws);
 }
 
 tp_status tp_shard_sum(int32_t t, int64_t n, const float* const* partials, const void* residual,

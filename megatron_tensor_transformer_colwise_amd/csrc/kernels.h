@@ -60,12 +60,35 @@ hipError_t launch_gemm_bf16_group(int epi, int groups, int64_t M, int64_t N, int
 hipError_t launch_gemm_f32(int epi, int64_t M, int64_t N, int64_t K, const float* x, const float* w,
                            float* out, hipStream_t s, const float* bias = nullptr, int64_t lda = 0);
 
+// Flash attention forward.  Query blocks of 128 rows are taken in pairs
+// (p, last - p) and each pair's key tiles are cut into equal pieces, one per
+// workgroup; a block whose keys are split over pieces is merged by the
+// piece holding its last key tile from the float32 partials of the others,
+// handed over through a split workspace:
+//   part  FA_MAX_SLOTS slots of FA_SLOT_FLOATS floats
+//   flag  FA_MAX_SLOTS words that only ever hold launch epochs (zero at first)
+//   epoch this launch's epoch, distinct from every earlier one on these flags
+// Calls that share a split workspace must not overlap.  ws = NULL: the
+// per-(device, stream) workspace of the library, allocated at the first
+// split launch on a stream (without it the launch runs unsplit).
 // lse (optional): [batch, hq, seq_pad] float32 (entries past seq untouched),
 // the log-sum-exp of the scores scaled to log2 units:
 // P = exp2(s * log2(e) / sqrt(d) - lse).
+constexpr int FA_MAX_SLOTS = 512;
+constexpr int FA_SLOT_FLOATS = 128 * 128 + 2 * 256;  // O^T partial of 128 queries, then max and sum per thread
+constexpr size_t FA_SLOT_BYTES = (size_t)FA_SLOT_FLOATS * 4;
+struct FaSplitWs {
+  float* part;
+  unsigned* flag;
+  unsigned epoch;
+};
+// Pieces per pair of query blocks the launch uses (1: unsplit); the split
+// workspace holds (pieces - 1) x pairs x batch x hq slots.
+int flash_attn_pieces(int64_t batch, int64_t seq, int hq, int causal);
+size_t flash_attn_split_bytes(int64_t batch, int64_t seq, int hq, int causal);
 hipError_t launch_flash_attn(int64_t batch, int64_t seq, int64_t seq_pad, int hq, int hkv,
                              int causal, const void* q, const void* k, const void* vt, void* o,
-                             hipStream_t s, float* lse = nullptr);
+                             hipStream_t s, float* lse = nullptr, const FaSplitWs* ws = nullptr);
 
 // Backward of launch_flash_attn for head_dim 128.  Inputs as the forward's
 // (q, k token-major, vt per head transposed, seq_pad columns) plus kt
@@ -152,6 +175,11 @@ hipError_t launch_sum_rmsnorm_bwd(int t, int64_t nrun, int64_t run_rows, int64_t
 // device, then cached; no allocation).
 constexpr size_t kStaticScratchBytes = (size_t)64 << 20;
 hipError_t static_scratch(void** ptr);
+// The first kStaticFlagBytes of that array hold the flags of the attention's
+// split workspace (only ever written with launch epochs); epoch receives the
+// next epoch of this device.
+constexpr size_t kStaticFlagBytes = (size_t)FA_MAX_SLOTS * sizeof(unsigned);
+hipError_t static_scratch_epoch(unsigned* epoch);
 
 hipError_t launch_act_backward(int swiglu, int64_t m, int64_t n, const void* pre, const void* dy, void* dpre,
                                void* y, hipStream_t s);

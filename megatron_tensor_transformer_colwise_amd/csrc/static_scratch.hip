@@ -20,6 +20,7 @@ static __device__ __align__(256) char scratch[tpk::kStaticScratchBytes];
 constexpr int kMaxDevices = 64;
 std::mutex g_mu;
 void* g_ptr[kMaxDevices];  // device address of scratch on each device, once looked up
+unsigned g_epoch[kMaxDevices];  // last epoch handed out for the flags at the start of scratch
 
 }  // namespace
 
@@ -40,6 +41,17 @@ hipError_t static_scratch(void** ptr) {
     g_ptr[dev] = p;
   }
   *ptr = g_ptr[dev];
+  return hipSuccess;
+}
+
+hipError_t static_scratch_epoch(unsigned* epoch) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(g_mu);
+  *epoch = ++g_epoch[dev];
+  if (*epoch == 0) *epoch = ++g_epoch[dev];  // 0 is the flags' initial value (the array starts zeroed)
   return hipSuccess;
 }
 

@@ -59,6 +59,7 @@ _SIGS = {
     "tp_shard_sum_rmsnorm": [_i32, _i64, _i64, _i64, _i64, ctypes.POINTER(_vp), _vp, _vp, _i32, _vp, _vp,
                              _f32, _vp, _vp],
     "tp_gemm_plan": [_i64, _i64, _i64, _i32] + [ctypes.POINTER(_i32)] * 4,
+    "tp_flash_attn_plan": [_i64, _i64, _i32, _i32, ctypes.POINTER(_i32)],
     "tp_embedding": [_i64, _i64, _i64, _i64, _vp, _vp, _vp, _i64, _vp],
     "tp_shard_mlp_backward_workspace_bytes": [_i32, _i64, _i64, _i64],
     "tp_shard_mlp_backward": [_i32, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t,
@@ -154,6 +155,13 @@ def tp_gemm_plan(m, n, k=64, kind="rowwise") -> tuple[int, int, int, int]:
     _check(lib().tp_gemm_plan(m, n, k, _PLAN_KIND[kind], ctypes.byref(a), ctypes.byref(b), ctypes.byref(c),
                               ctypes.byref(d)))
     return a.value, b.value, c.value, d.value
+
+
+def tp_flash_attn_plan(batch, seq, hq, causal=True) -> int:
+    """Pieces each pair of query blocks is cut into by the flash attention."""
+    p = _i32()
+    _check(lib().tp_flash_attn_plan(batch, seq, hq, 1 if causal else 0, ctypes.byref(p)))
+    return p.value
 
 
 def tp_device_check() -> None:

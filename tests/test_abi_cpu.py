@@ -186,6 +186,23 @@ def test_gemm_plans(L):
     assert L.tp_gemm_plan(16, 16, 16, 7, *[ctypes.byref(ctypes.c_int32()) for _ in range(4)]) == tp.TP_ERR_INVALID_ARG
 
 
+def test_flash_attn_plans(L):
+    """Pieces per pair of query blocks (host-only call): about two
+    workgroups per CU on 256 CUs, at least 4 key tiles per piece."""
+    assert tp.tp_flash_attn_plan(4, 2048, 8) == 2      # 70B t=8 rank: 8 pairs x 32 = 256 units
+    assert tp.tp_flash_attn_plan(4, 2048, 4) == 4      # 70B t=16 rank
+    assert tp.tp_flash_attn_plan(2, 2048, 8) == 4      # Llama-8B rank
+    assert tp.tp_flash_attn_plan(1, 2048, 1) == 8      # 34 tiles per pair: at most 8 pieces
+    assert tp.tp_flash_attn_plan(1, 1000, 1) == 4      # 18 tiles per pair
+    assert tp.tp_flash_attn_plan(1, 900, 2, False) == 7  # all keys: 30 tiles per pair
+    assert tp.tp_flash_attn_plan(1, 130, 4) == 1       # 5 tiles: no split
+    assert tp.tp_flash_attn_plan(64, 2048, 16) == 1    # enough pairs to fill the chip
+    assert tp.tp_flash_attn_plan(0, 2048, 8) == 1
+    with pytest.raises(tp.TpError):
+        tp.tp_flash_attn_plan(1, -1, 8)
+    assert L.tp_flash_attn_plan(1, 16, 1, 1, None) == tp.TP_ERR_INVALID_ARG
+
+
 def test_binding_raises_with_message(L):
     with pytest.raises(tp.TpError) as e:
         tp.tp_colwise("gelu", "bf16", 4, 12, 16, A16, A16, A16, stream=0)

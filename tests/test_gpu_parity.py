@@ -525,6 +525,46 @@ def test_flash_attn_lse(device, batch, seq, hq, hkv, causal):
     assert worst <= 1e-3
 
 
+@pytest.mark.parametrize("batch,seq,hq,hkv,causal,pieces", [
+    (1, 700, 2, 1, True, 3), (1, 1000, 1, 1, True, 4), (1, 900, 2, 2, False, 7),
+    (2, 333, 4, 2, True, 2), (1, 2048, 1, 1, True, 8)])
+def test_flash_attn_split_pieces(device, batch, seq, hq, hkv, causal, pieces):
+    """Few heads, so each pair of query blocks is cut into several pieces and
+    blocks are completed from other workgroups' float32 partials: output and
+    log-sum-exp against the oracle, bitwise equal on a second run.  Ragged
+    sequences, an odd number of query blocks (the middle block cut on its
+    own), GQA and attention over all keys."""
+    say(f"case flash split b={batch} s={seq} hq={hq} hkv={hkv} causal={causal}")
+    assert tp.tp_flash_attn_plan(batch, seq, hq, causal) == pieces
+    d = 128
+    t_in = _attn_core_inputs(device, batch, seq, hq, hkv, 83)
+    m = batch * seq
+    dev = {k: v.to(device) for k, v in t_in.items() if torch.is_tensor(v)}
+    outs = []
+    for _ in range(2):
+        o = torch.full((m, hq * d), float("nan"), dtype=torch.bfloat16, device=device)
+        lse = torch.full((batch, hq, t_in["seq_pad"]), -7.0, dtype=torch.float32, device=device)
+        tp.tp_flash_attn_lse(batch, seq, hq, hkv, d, causal, dev["q"], dev["k"], dev["vt"], o, lse)
+        torch.cuda.synchronize()
+        outs.append((o, lse))
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+    got, got_lse = host(outs[0][0]), outs[0][1].cpu().double().numpy()
+    assert np.all(got_lse[:, :, seq:] == -7.0)
+    qh, kh, vh = (t_in[n].double().numpy() for n in ("q", "k", "v"))
+    worst = worst_lse = 0.0
+    for b in range(batch):
+        rows = slice(b * seq, (b + 1) * seq)
+        for j in range(hq):
+            g = j // (hq // hkv)
+            qq, kk, vv = qh[rows, j * d:(j + 1) * d], kh[rows, g * d:(g + 1) * d], vh[rows, g * d:(g + 1) * d]
+            ref = oracle.causal_attention(qq, kk, vv) if causal else oracle.full_attention(qq, kk, vv)
+            worst = max(worst, rel_err(got[rows, j * d:(j + 1) * d], ref))
+            ref_lse = oracle.attention_lse(qq, kk, causal) / math.log(2.0)
+            worst_lse = max(worst_lse, float(np.max(np.abs(got_lse[b, j, :seq] - ref_lse))))
+    say(f"  max rel err {worst:.3e}, max|lse gpu - oracle| {worst_lse:.3e}")
+    assert worst <= BF16_TOL and worst_lse <= 1e-3
+
+
 @pytest.mark.parametrize("batch,seq,hq,hkv,causal,rope", [
     (2, 130, 4, 2, True, 0.0), (1, 300, 4, 1, True, 500000.0), (2, 64, 2, 2, True, 10000.0),
     (1, 200, 4, 2, False, 0.0), (1, 1, 2, 1, True, 500000.0), (1, 257, 8, 1, True, 500000.0)])
