@@ -4,16 +4,23 @@
 // so a rank runs attention over its own a/t query heads with no exchange; with
 // grouped-query attention the rank's query heads read the KV heads it holds.
 //
-// One workgroup = (sequence b, query head j, 128 query rows); 4 waves, 32 query
-// rows each.  Keys/values stream through LDS 64 at a time (two stages).
+// Work: query blocks of 128 rows, taken in pairs (p, last - p) per (sequence
+// b, query head j), so that with the causal mask every pair walks about the
+// same number of 64-key tiles; each pair's tiles, block p's then block
+// last - p's, are cut into equal pieces, one workgroup each (two per CU).  A
+// workgroup walks one or two segments (a query block over a range of its key
+// tiles); a block whose tiles span pieces is completed by the piece holding
+// its last tile from the others' float32 partials.  4 waves of 32 query rows;
+// keys/values stream through LDS 64 at a time (two stages).
 //
 // Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16:
 // a lane then owns one query (its column) and 16 keys per 32-key block, so the
 // running max and sum of the online softmax are per-lane scalars.  The value
 // product is O^T = V^T P^T: P^T is the B operand straight from the score
 // registers (rounded to bf16; the K rows are fed to the score MFMA in an
-// order that leaves each lane's 8 keys of a value step in place), and V^T is read from LDS as rows of the
-// transposed-V layout the projection writes.  Exponentials are the hardware
+// order that leaves each lane's 8 keys of a value step in place), and V^T is
+// read from LDS as rows of the transposed-V layout the projection writes.
+// Exponentials are the hardware
 // exp2 of one FMA (the 1/sqrt(d) * log2(e) scale folded in; probabilities
 // below 2^-126 may flush to zero, far below the bf16 P they feed and the
 // float32 sum they join); the running max moves, and
