@@ -506,7 +506,9 @@ tp_status tp_shard_attn_backward(int64_t batch, int64_t seq, int64_t h, int32_t 
  * bm_tail (heights 256, 192 or 128 rows); with *split_k = 2 the remaining
  * columns run as 256-row tiles each summed by two workgroups over half of k
  * (single bf16-output launches of depth k >= 4096, when that shortens the
- * last round).  kind: TP_PLAN_ROWWISE (float32 partial), TP_PLAN_COLWISE
+ * last round).  bm_main = bm_tail = 64 reports small tiles (64 rows x 128
+ * columns, 64 output columns for SwiGLU; split = their tile columns), used
+ * when large tiles would leave most of the chip idle (not for Q/K/V).  kind: TP_PLAN_ROWWISE (float32 partial), TP_PLAN_COLWISE
  * (bf16, plain or GeLU), TP_PLAN_SWIGLU, TP_PLAN_QKV.  Host-only; launches
  * nothing.  TP_ERR_SHAPE for non-positive sizes, TP_ERR_INVALID_ARG for an
  * unknown kind or a NULL output.

@@ -146,6 +146,32 @@ __device__ __forceinline__ void tile_coords(int id, int nb, int num_bm, int num_
   bn = inner / gs;
 }
 
+// GeLU for bf16 outputs: 0.5 x erfc(-x / sqrt 2) with erfc from the
+// Chebyshev fit of Numerical Recipes (Press et al., 2nd ed., section 6.2,
+// "erfcc": fractional error below 1.2e-7 for every argument): one exp2, one
+// reciprocal and a degree-9 polynomial, without branches, so a wave's
+// elements interleave (the library erff branches on the argument's range).
+// Its error stays far below a bf16 rounding step.
+__device__ __forceinline__ float gelu_bf16out(float x) {
+  const float u = -0.70710678118654752440f * x;
+  const float z = fabsf(u);
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.5f, z, 1.0f));
+  float p = 0.17087277f;
+  p = fmaf(t, p, -0.82215223f);
+  p = fmaf(t, p, 1.48851587f);
+  p = fmaf(t, p, -1.13520398f);
+  p = fmaf(t, p, 0.27886807f);
+  p = fmaf(t, p, -0.18628806f);
+  p = fmaf(t, p, 0.09678418f);
+  p = fmaf(t, p, 0.37409196f);
+  p = fmaf(t, p, 1.00002368f);
+  p = fmaf(t, p, -1.26551223f);
+  // t exp(-z^2 + p) with exp(y) = exp2(y log2 e)
+  const float e = t * __builtin_amdgcn_exp2f((p - z * z) * 1.44269504088896340736f);
+  const float erfc_u = u >= 0.0f ? e : 2.0f - e;
+  return 0.5f * x * erfc_u;
+}
+
 constexpr bool is_swiglu(int epi) { return epi == EPI_SWIGLU || epi == EPI_SWIGLU_SAVE; }
 constexpr bool is_gelu(int epi) { return epi == EPI_GELU || epi == EPI_GELU_SAVE; }
 constexpr bool saves_pre(int epi) { return epi == EPI_GELU_SAVE || epi == EPI_SWIGLU_SAVE; }
@@ -563,7 +589,7 @@ __global__ __launch_bounds__((Cfg<BMT, W4>::NW * 64), 1) void gemm_bf16_kernel(A
           for (int e = 0; e < 4; ++e) {
             v[e] = acc[i][j][4 * g + e] + bcol[j];
             if (saves_pre(EPI)) pv[e] = v[e];
-            if (is_gelu(EPI)) v[e] = gelu_erf(v[e]);
+            if (is_gelu(EPI)) v[e] = gelu_bf16out(v[e]);
           }
           quad_transpose(v, q);
           const int64_t row = row_base + i * 32 + 8 * g + q;
@@ -1178,7 +1204,7 @@ __global__ __launch_bounds__(256, 1) void gemm16_kernel(Args args) {
         for (int e = 0; e < 4; ++e) {
           v[e] = acc[i][j][e] + bcol[j];
           if (saves_pre(EPI)) pv[e] = v[e];
-          if (is_gelu(EPI)) v[e] = gelu_erf(v[e]);
+          if (is_gelu(EPI)) v[e] = gelu_bf16out(v[e]);
         }
         quad_transpose(v, q);
         const int64_t row = row_base + i * 16 + q;
@@ -1214,6 +1240,271 @@ __global__ __launch_bounds__(256, 1) void gemm16_kernel(Args args) {
             pu[e] = acc[i][j + 4][e] + bu[j];
           }
           v[e] = silu_fast(acc[i][j][e] + bg[j]) * (acc[i][j + 4][e] + bu[j]);
+        }
+        quad_transpose(v, q);
+        const int64_t row = row_base + i * 16 + q;
+        const int64_t col = ocol0 + 16 * j + cq;
+        if (row < M && col < N)
+          *reinterpret_cast<u32x2*>(reinterpret_cast<bf16_t*>(outg) + row * N + col) =
+              u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+        if (saves_pre(EPI)) {
+          quad_transpose(pg, q);
+          quad_transpose(pu, q);
+          bf16_t* pr = reinterpret_cast<bf16_t*>(args.pre[blockIdx.y]) + row * 2 * N + col;
+          if (row < M && col < N) {
+            *reinterpret_cast<u32x2*>(pr) = u32x2{pack_bf16x2(pg[0], pg[1]), pack_bf16x2(pg[2], pg[3])};
+            *reinterpret_cast<u32x2*>(pr + N) = u32x2{pack_bf16x2(pu[0], pu[1]), pack_bf16x2(pu[2], pu[3])};
+          }
+        }
+      }
+  }
+}
+
+// ---- small tiles for launches that would leave most of the chip idle -----
+//
+// A GEMM whose large-tile plan runs in one partly filled round (the GPT-sized
+// shard, 2048 x 1024 x 1024: 64 tiles of 128 x 256 on 256 CUs) leaves most
+// CUs idle while each busy one streams its whole k range.  Here a tile is 64
+// rows x 128 weight rows (SwiGLU: 64 outputs), four times as many tiles,
+// worked by four waves in a 2 x 2 grid of 32 x 64 with
+// v_mfma_f32_16x16x32_bf16 (two 16-row by four 16-column blocks per wave).
+// Stages of 64 k (24 KiB) cycle through a four-slot LDS ring with one barrier
+// per stage: after the barrier of stage kt every wave has finished reading
+// stage kt - 1, so the loads of stage kt + 3 go out into its slot at once.
+// Measured per stage (timestamps): ~1000 cycles against 256 of matrix work,
+// the same with 32 or 256 busy CUs and with rings of 3 to 6 slots, while the
+// same loads alone stream at ~58 B per cycle per CU (400 cycles a stage): the
+// stage's LDS traffic (24 KiB of DMA writes, 48 KiB of fragment reads) and
+// its barrier set the pace, not the memory behind it.  Fragment addressing,
+// the chunk permutation (swz16) and the output layout are those of the 16x16
+// kernel, and each output's sum runs over k in the same order with the same
+// instruction, so results are bitwise those of the large tiles.  SwiGLU tiles
+// hold, for each 32-output half, the 32 gate rows and then the 32 up rows, so
+// gate block j and up block j + 2 of a wave are the same outputs in the same
+// lane.
+constexpr int SBM = 64;    // small tile rows
+constexpr int SBN = 128;   // small tile weight rows
+constexpr int SNS = 4;     // LDS ring slots
+constexpr int SPD = SNS - 1;  // stages loaded ahead
+
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int EPI>
+__global__ __launch_bounds__(256, 1) void gemm_small_kernel(Args args) {
+  static_assert(EPI != EPI_QKV, "the QKV epilogue runs on the 32x32 kernel");
+  constexpr int A_T = SBM * ROWB;
+  constexpr int B_T = SBN * ROWB;
+  constexpr int ST = A_T + B_T;
+  constexpr int LA = SBM * CH / 64 / 4, LB = SBN * CH / 64 / 4;  // wave-instructions per wave and stage
+  static_assert(LA * 256 == SBM * CH && LB * 256 == SBN * CH && SNS * ST <= 160 * 1024, "tile");
+  __shared__ __attribute__((aligned(1024))) char smem[SNS * ST];
+
+  const int lane = lane_id();
+  const int wave = wave_id();
+  const bf16_t* const xg = args.x[blockIdx.y];
+  const bf16_t* const wg = args.w[blockIdx.y];
+  void* const outg = args.out[blockIdx.y];
+  int bm, bn;
+  tile_coords((int)blockIdx.x, args.num_bm * args.num_bn, args.num_bm, args.num_bn, bm, bn);
+  bm = __builtin_amdgcn_readfirstlane(bm);
+  bn = __builtin_amdgcn_readfirstlane(bn);
+  const int64_t M = args.M, N = args.N, K = args.K, lda = args.lda;
+  const int64_t m0 = (int64_t)bm * SBM;
+  const uint32_t row_bytes = (uint32_t)(K * 2);
+  const uint32_t a_row_bytes = (uint32_t)(lda * 2);
+  const int m_rows = (int)min<int64_t>(SBM, M - m0);
+  const __amdgpu_buffer_rsrc_t rsrc_a = make_rsrc(xg + m0 * lda, (uint32_t)m_rows * a_row_bytes);
+  __amdgpu_buffer_rsrc_t rsrc_b;
+  int n_valid;  // valid weight rows (plain) or valid output columns (SwiGLU)
+  if (is_swiglu(EPI)) {
+    const int64_t o0 = (int64_t)bn * (SBN / 2);
+    n_valid = (int)min<int64_t>(SBN / 2, N - o0);
+    rsrc_b = make_rsrc(wg + o0 * K, (uint32_t)((N + n_valid) * K * 2));
+  } else {
+    const int64_t n0 = (int64_t)bn * SBN;
+    n_valid = (int)min<int64_t>(SBN, N - n0);
+    rsrc_b = make_rsrc(wg + n0 * K, (uint32_t)n_valid * row_bytes);
+  }
+
+  // global -> LDS: wave-instruction j of an operand fills tile row slot / CH,
+  // physical chunk slot % CH, from logical chunk (slot % CH) ^ swz16(row)
+  uint32_t a_off[LA], b_off[LB];
+  int a_k[LA], b_k[LB];
+#pragma unroll
+  for (int j = 0; j < LA; ++j) {
+    const int slot = (j * 4 + wave) * 64 + lane;
+    const int r = slot / CH;
+    const int c = (slot % CH) ^ swz16(r);
+    a_k[j] = c * 8;
+    a_off[j] = (uint32_t)r * a_row_bytes + (uint32_t)c * 16;
+  }
+#pragma unroll
+  for (int j = 0; j < LB; ++j) {
+    const int slot = (j * 4 + wave) * 64 + lane;
+    const int r = slot / CH;
+    const int c = (slot % CH) ^ swz16(r);
+    b_k[j] = c * 8;
+    if (is_swiglu(EPI)) {
+      const int qq = r & 63;
+      const int o_rel = (r >> 6) * 32 + (qq & 31);
+      const int64_t rel_row = qq < 32 ? o_rel : N + o_rel;
+      b_off[j] = o_rel < n_valid ? (uint32_t)(rel_row * K * 2) + (uint32_t)c * 16 : TP_OOB_OFFSET;
+    } else {
+      b_off[j] = (uint32_t)r * row_bytes + (uint32_t)c * 16;
+    }
+  }
+  const int nk = (int)((K + BK - 1) / BK);
+  const int nfull = (int)(K / BK);  // k-steps without a k tail
+  // load j (0 .. LA + LB - 1) of stage kt: the A loads, then the B loads
+  auto load_one = [&](int kt, int j) __attribute__((always_inline)) {
+    char* const st = smem + (kt % SNS) * ST;
+    const uint32_t kb = (uint32_t)kt * (uint32_t)(BK * 2);
+    if (j < LA) {
+      char* const dst = st + (j * 4 + wave) * 1024;
+      if (kt < nfull) buffer_load_lds16_so(rsrc_a, dst, a_off[j], kb);
+      else buffer_load_lds16(rsrc_a, dst, ((int64_t)kt * BK + a_k[j]) < K ? a_off[j] + kb : TP_OOB_OFFSET);
+    } else {
+      const int jb = j - LA;
+      char* const dst = st + A_T + (jb * 4 + wave) * 1024;
+      if (kt < nfull) buffer_load_lds16_so(rsrc_b, dst, b_off[jb], kb);
+      else
+        buffer_load_lds16(rsrc_b, dst,
+                          ((int64_t)kt * BK + b_k[jb]) < K && b_off[jb] != TP_OOB_OFFSET ? b_off[jb] + kb
+                                                                                          : TP_OOB_OFFSET);
+    }
+  };
+
+  const int wm = wave >> 1, wn = wave & 1;
+  const int l15 = lane & 15, kq = lane >> 4;
+  // block 0's fragment address per 32-deep k-step s; block i at + 2048 i
+  uint32_t ra[2], rb[2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    const int c = (4 * s + kq) ^ swz16(l15);
+    ra[s] = (uint32_t)((wm * 32 + l15) * ROWB + (c << 4));
+    rb[s] = (uint32_t)(A_T + (wn * 64 + l15) * ROWB + (c << 4));
+  }
+  f32x4 acc[2][4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{};
+
+  for (int kt = 0; kt < SPD && kt < nk; ++kt)
+#pragma unroll
+    for (int j = 0; j < LA + LB; ++j) load_one(kt, j);
+  for (int kt = 0; kt < nk; ++kt) {
+    // this wave's loads of stage kt have landed (those of the later stages
+    // already issued may not), then every wave's have, and every wave is
+    // done reading stage kt - 1
+    static_assert(SPD <= 6, "the waits below");
+    switch (min(nk - 1 - kt, SPD - 1)) {
+      case 5: wait_vmcnt<5 * (LA + LB)>(); break;
+      case 4: wait_vmcnt<4 * (LA + LB)>(); break;
+      case 3: wait_vmcnt<3 * (LA + LB)>(); break;
+      case 2: wait_vmcnt<2 * (LA + LB)>(); break;
+      case 1: wait_vmcnt<LA + LB>(); break;
+      default: wait_vmcnt0(); break;
+    }
+    lds_barrier();
+    // the loads of stage kt + SPD at once (spread between the MFMAs they
+    // were slower), then all 12 fragment reads of the stage and its 16 MFMAs
+    const char* const st = smem + (kt % SNS) * ST;
+    if (kt + SPD < nk) {
+#pragma unroll
+      for (int j = 0; j < LA + LB; ++j) load_one(kt + SPD, j);
+    }
+    u32x4 fa[2][2], fb[2][4];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) fa[s][i] = lds_read16(st + ra[s] + 2048 * i);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) fb[s][j] = lds_read16(st + rb[s] + 2048 * j);
+    }
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int s = q >> 3, i = (q >> 2) & 1, j = q & 3;
+      acc[i][j] = mfma16x16x32(fa[s][i], fb[s][j], acc[i][j]);
+    }
+  }
+
+  // ---- epilogue: after a quad transpose a lane holds 4 consecutive columns
+  // of row 4 kq + q of each block
+  const int64_t row_base = m0 + wm * 32 + 4 * kq;
+  const int q = lane & 3;
+  const int cq = 4 * (l15 >> 2);
+  if constexpr (EPI == EPI_F32) {
+    const int64_t col_base = (int64_t)bn * SBN + wn * 64 + cq;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float v[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
+        quad_transpose(v, q);
+        const int64_t row = row_base + i * 16 + q;
+        const int64_t col = col_base + j * 16;
+        if (row < M && col < N)
+          __builtin_nontemporal_store(f32x4{v[0], v[1], v[2], v[3]},
+                                      reinterpret_cast<f32x4*>(reinterpret_cast<float*>(outg) + row * N + col));
+      }
+  } else if constexpr (EPI == EPI_BF16 || is_gelu(EPI)) {
+    const int64_t col_base = (int64_t)bn * SBN + wn * 64 + cq;
+    float bcol[4];  // bias of the lane's column of each block (-0: none)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t c = (int64_t)bn * SBN + wn * 64 + 16 * j + l15;
+      bcol[j] = (args.bias && c < N) ? args.bias[c] : -0.0f;
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float v[4], pv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          v[e] = acc[i][j][e] + bcol[j];
+          if (saves_pre(EPI)) pv[e] = v[e];
+          if (is_gelu(EPI)) v[e] = gelu_bf16out(v[e]);
+        }
+        quad_transpose(v, q);
+        const int64_t row = row_base + i * 16 + q;
+        const int64_t col = col_base + j * 16;
+        if (row < M && col < N)
+          *reinterpret_cast<u32x2*>(reinterpret_cast<bf16_t*>(outg) + row * N + col) =
+              u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+        if (saves_pre(EPI)) {
+          quad_transpose(pv, q);
+          if (row < M && col < N)
+            *reinterpret_cast<u32x2*>(reinterpret_cast<bf16_t*>(args.pre[blockIdx.y]) + row * N + col) =
+                u32x2{pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3])};
+        }
+      }
+  } else {  // SwiGLU: gate block j and up block j + 2 of a wave are the same 16 outputs
+    const int64_t ocol0 = (int64_t)bn * (SBN / 2) + wn * 32;
+    float bg[2], bu[2];  // gate and up biases of the lane's output column (-0: none)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int64_t o = ocol0 + 16 * j + l15;
+      bg[j] = (args.bias && o < N) ? args.bias[o] : -0.0f;
+      bu[j] = (args.bias && o < N) ? args.bias[N + o] : -0.0f;
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        float v[4], pg[4], pu[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (saves_pre(EPI)) {
+            pg[e] = acc[i][j][e] + bg[j];
+            pu[e] = acc[i][j + 2][e] + bu[j];
+          }
+          v[e] = silu_fast(acc[i][j][e] + bg[j]) * (acc[i][j + 2][e] + bu[j]);
         }
         quad_transpose(v, q);
         const int64_t row = row_base + i * 16 + q;
@@ -1305,10 +1596,19 @@ Plan plan_for(int64_t M, int64_t nbn, int groups) {
 // instead of the 4 tile columns as a round of 128-row tiles.
 constexpr int SK_MAX_TILES = 128;
 
-Plan plan_with_split(int64_t M, int64_t nbn, int64_t K, int groups, bool bf16_out) {
+// Small tiles (64 rows x 128 weight rows) cost 64 + 128 per round on the
+// same scale; they replace a plain plan they beat (bm_main = 64 then, with
+// split = the small tile columns).  nbn_small = 0: not available (Q/K/V).
+Plan with_small(Plan p, int64_t M, int64_t nbn_small, int groups) {
+  if (p.split_k || nbn_small <= 0) return p;
+  const int64_t c = rounds_of(((M + SBM - 1) / SBM) * nbn_small * groups) * (SBM + SBN);
+  return c < p.cost ? Plan{SBM, (int)nbn_small, SBM, 0, c} : p;
+}
+
+Plan plan_with_split(int64_t M, int64_t nbn, int64_t K, int groups, bool bf16_out, int64_t nbn_small) {
   Plan p = plan_for(M, nbn, groups);
   const int64_t nk = (K + BK - 1) / BK;
-  if (!bf16_out || groups != 1 || K < MFMA16_MIN_K || nk < 4) return p;
+  if (!bf16_out || groups != 1 || K < MFMA16_MIN_K || nk < 4) return with_small(p, M, nbn_small, groups);
   const int64_t nbm = (M + 255) / 256;
   for (int64_t c = nbn - 1; c >= 0; --c) {
     const int64_t main_t = nbm * c, tail_t = nbm * (nbn - c);
@@ -1318,7 +1618,7 @@ Plan plan_with_split(int64_t M, int64_t nbn, int64_t K, int groups, bool bf16_ou
     if (c_split < p.cost) p = Plan{256, (int)c, 256, 2, c_split};
     break;
   }
-  return p;
+  return with_small(p, M, nbn_small, groups);
 }
 
 // Workspace of the split-k pairs: one float32 256 x 256 partial and one flag
@@ -1378,10 +1678,28 @@ void launch_part(Args a, int bn0, int cols, int groups, hipStream_t s) {
   hipLaunchKernelGGL((gemm_bf16_kernel<EPI, BMT, false>), dim3(nb, groups), dim3(Cfg<BMT>::NW * 64), 0, s, a);
 }
 
+// Small tile columns of an n-column output (0 for Q/K/V, which has no
+// small-tile epilogue).
+int64_t small_cols(int epi, int64_t N) {
+  if (epi == EPI_QKV) return 0;
+  const int64_t w = is_swiglu(epi) ? SBN / 2 : SBN;
+  return (N + w - 1) / w;
+}
+
 template <int EPI>
 void launch_planned(const Args& a, int64_t nbn, int groups, hipStream_t s) {
   constexpr bool BF16_OUT = EPI == EPI_BF16 || is_gelu(EPI) || is_swiglu(EPI);
-  const Plan p = plan_with_split(a.M, nbn, a.K, groups, BF16_OUT);
+  const Plan p = plan_with_split(a.M, nbn, a.K, groups, BF16_OUT, small_cols(EPI, a.N));
+  if constexpr (EPI != EPI_QKV) {
+    if (p.bm_main == SBM) {
+      Args b = a;
+      b.bn0 = 0;
+      b.num_bn = p.split;
+      b.num_bm = (int)((a.M + SBM - 1) / SBM);
+      hipLaunchKernelGGL((gemm_small_kernel<EPI>), dim3(b.num_bm * b.num_bn, groups), dim3(256), 0, s, b);
+      return;
+    }
+  }
   if constexpr (BF16_OUT) {
     unsigned epoch = 0;
     SkSlot* sk = p.split_k ? sk_acquire(s, &epoch) : nullptr;
@@ -1420,7 +1738,8 @@ void gemm_plan(int64_t M, int64_t N, int64_t K, int kind, int groups, int* bm_ma
   const bool swiglu = kind == GEMM_PLAN_SWIGLU;
   const int64_t nbn = (N + (swiglu ? BN / 2 : BN) - 1) / (swiglu ? BN / 2 : BN);
   const bool bf16_out = kind == GEMM_PLAN_COLWISE || kind == GEMM_PLAN_SWIGLU;
-  const Plan p = plan_with_split(M, nbn, K, groups, bf16_out);
+  const int epi = kind == GEMM_PLAN_QKV ? EPI_QKV : swiglu ? EPI_SWIGLU : EPI_BF16;
+  const Plan p = plan_with_split(M, nbn, K, groups, bf16_out, small_cols(epi, N));
   *bm_main = p.bm_main;
   *split = p.split;
   *bm_tail = p.bm_tail;

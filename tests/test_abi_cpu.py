@@ -173,7 +173,14 @@ def test_gemm_plans(L):
     assert tp.tp_gemm_plan(8192, 1280, 8192, "qkv") == (192, 5, 192, 0)    # QKV, 70B t=8
     assert tp.tp_gemm_plan(8192, 768, 8192, "qkv") == (128, 3, 128, 0)     # QKV, 70B t=16
     assert tp.tp_gemm_plan(4096, 3584, 4096, "swiglu") == (256, 28, 256, 0)  # SwiGLU, Llama-8B
-    assert tp.tp_gemm_plan(2048, 1024, 1024, "colwise") == (128, 4, 128, 0)  # GPT MLP
+    # GPT MLP (2048 x 1024 x 1024): 256 small tiles of 64 x 128 instead of 64 of 128 x 256
+    assert tp.tp_gemm_plan(2048, 1024, 1024, "colwise") == (64, 8, 64, 0)
+    assert tp.tp_gemm_plan(2048, 1024, 1024) == (64, 8, 64, 0)
+    assert tp.tp_gemm_plan(1000, 520, 136, "swiglu") == (64, 9, 64, 0)    # 64 outputs per small tile
+    # small tiles only where they beat the large ones (a tie keeps the large tiles)
+    assert tp.tp_gemm_plan(2048, 1024, 1024, "swiglu") == (128, 8, 128, 0)
+    assert tp.tp_gemm_plan(4000, 776, 136) == (128, 4, 128, 0)
+    assert tp.tp_gemm_plan(300, 264, 520, "qkv")[0] != 64               # Q/K/V: large tiles only
     # split-k only for bf16 outputs of depth >= 4096
     assert tp.tp_gemm_plan(520, 768, 4104, "colwise") == (256, 0, 256, 2)
     assert tp.tp_gemm_plan(520, 768, 4104, "rowwise")[3] == 0

@@ -106,12 +106,18 @@ def test_rowwise_gemm_integer_bit_exact(device, m, k, n):
     (4096, 64, 4096, (256, 16, 256)),     # 256-row tiles
     (8192, 72, 1280, (192, 5, 192)),      # 192-row tiles, k tail of 8
     (8192, 64, 7168, (256, 24, 128)),     # main range at 256, tail columns at 128
-    (1000, 136, 776, (128, 4, 128)),      # 128-row tiles, ragged m and n
+    (4000, 136, 776, (128, 4, 128)),      # 128-row tiles, ragged m and n
+    (1000, 136, 776, (64, 7, 64)),        # small tiles (64 x 128): ragged m and n, k tail of 8
+    (2048, 1024, 1024, (64, 8, 64)),      # small tiles, the GPT MLP shape: whole k-steps only
+    (130, 128, 200, (64, 2, 64)),         # small tiles, two k-steps (the ring never wraps)
+    (130, 192, 200, (64, 2, 64)),         # small tiles, three k-steps (each ring slot once)
+    (300, 4104, 264, (64, 3, 64)),        # small tiles, deep k with a tail
     (7777, 72, 1280, (192, 5, 192)),      # 192-row tiles (96-row waves), ragged m
     (5000, 64, 3584, (192, 8, 128)),      # 192-row main range, 128-row tail, ragged m
     (4000, 2056, 4000, (256, 16, 256)),   # four-wave 256-row tiles: ragged m and n, k tail of 8
     (4096, 2048, 4096, (256, 16, 256)),   # four-wave 256-row tiles, whole k-steps only
-    (300, 4104, 264, (128, 2, 128)),      # four-wave 128-row tiles, deep k
+    (4000, 2056, 776, (128, 4, 128)),     # four-wave 128-row tiles, ragged m and n, k tail
+    (4000, 4104, 776, (128, 4, 128)),     # 16x16-MFMA 128-row tiles, deep k
     (4000, 2056, 2560, (192, 10, 192)),   # four-wave 192-row tiles, ragged m, k tail
     (5000, 2056, 3584, (192, 8, 128)),    # four-wave 192/128 split launch, ragged m, k tail
     (4000, 4104, 4000, (256, 16, 256)),   # 16x16-MFMA 256-row tiles: ragged m and n, k tail of 8
@@ -992,6 +998,8 @@ def test_colwise_activation_slices(device):
 
 @pytest.mark.parametrize("act,m,h,f,plan", [
     ("swiglu", 3000, 64, 1536, (192, 12, 192)),
+    ("swiglu", 1000, 136, 520, (64, 9, 64)),        # small tiles: 64 outputs each, ragged m and f
+    ("gelu", 1000, 1032, 776, (64, 7, 64)),         # small tiles, ragged m and f, k tail
     ("swiglu", 5000, 64, 1792, (192, 8, 128)),
     ("swiglu", 4000, 2056, 2048, (256, 16, 256)),   # four-wave tiles, ragged m, k tail
     ("gelu", 4000, 2056, 4000, (256, 16, 256)),     # four-wave tiles, ragged m and n
