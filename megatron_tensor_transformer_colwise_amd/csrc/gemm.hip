@@ -872,7 +872,8 @@ __global__ __launch_bounds__((Cfg<BMT, W4>::NW * 64), 1) void gemm_bf16_kernel(A
 // time per flop, which deep k loops amortise: at k = 8192 the SwiGLU GEMM of
 // the 70B shard and an 8192^3 GEMM run 5-7% faster this way; at k = 3584 it
 // is 1% slower, so shorter k stays on the 32x32 kernel.  Accumulation order
-// and results are bitwise those of the 32x32 kernel.
+// and results are bitwise those of the 32x32 kernel.  Every epilogue runs
+// here, Q/K/V + RoPE included (a wave's 128 columns are one head).
 //
 // Fragment of a 16-row block for k-step s: lane l reads row l % 16, 16-byte
 // chunk 4 s + l / 16 of the 64-deep stage.  The LDS chunk permutation here
@@ -895,7 +896,6 @@ __device__ __forceinline__ int swz16(int r) { return (r >> 1) & 7; }
 
 template <int EPI, int BMT>
 __global__ __launch_bounds__(256, 1) void gemm16_kernel(Args args) {
-  static_assert(EPI != EPI_QKV, "the QKV epilogue runs on the 32x32 kernel");
   constexpr int NW = 4;
   constexpr int WROWS = BMT / 2;  // 2 x 2 waves
   constexpr int MI = WROWS / 16;  // 16-row blocks per wave
@@ -1219,6 +1219,180 @@ __global__ __launch_bounds__(256, 1) void gemm16_kernel(Args args) {
                 u32x2{pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3])};
         }
       }
+  } else if constexpr (EPI == EPI_QKV) {
+    // One wave's 128 columns are one head (hd): Q and K heads rotated (the
+    // pair (c1, c1 + 64) is blocks j and j + 4 of a lane), V heads stored
+    // transposed per sequence.  The RoPE angles follow the 32x32 kernel's
+    // epilogue (turns as an unevaluated float sum, rows of a lane's 4-row
+    // group by angle addition).
+    const QkvOut o = args.qkv;
+    const int hd = bn * 2 + wn;
+    const int nheads = o.hq + 2 * o.hkv;
+    // V heads are transposed through LDS; every wave of the tile passes this
+    // barrier (before any returns) so no wave still reads the k loop's stages
+    __syncthreads();
+    if (hd >= nheads) return;
+    const uint32_t seq = (uint32_t)o.seq;
+    const uint32_t b_base = (uint32_t)(row_base / seq);
+    const uint32_t p_base = (uint32_t)(row_base - (int64_t)b_base * seq);
+    auto split_pos = [&](int off, uint32_t& b, uint32_t& p) {
+      p = p_base + (uint32_t)off;
+      b = b_base;
+      if (p >= seq) {
+        if ((uint32_t)off < seq) {
+          p -= seq;
+          ++b;
+        } else {
+          b += p / seq;
+          p %= seq;
+        }
+      }
+    };
+    if (hd < o.hq + o.hkv) {
+      const bool is_q = hd < o.hq;
+      bf16_t* dst = reinterpret_cast<bf16_t*>(is_q ? o.q : o.k);
+      const int64_t ld = (int64_t)(is_q ? o.hq : o.hkv) * 128;
+      dst += (int64_t)(is_q ? hd : hd - o.hq) * 128;
+      float hb1[4], hb2[4], f_hi[4], f_lo[4], c1p[4], s1p[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int c1 = 16 * j + l15;
+        hb1[j] = args.bias ? args.bias[(int64_t)hd * 128 + c1] : -0.0f;
+        hb2[j] = args.bias ? args.bias[(int64_t)hd * 128 + c1 + 64] : -0.0f;
+        const double fd = exp2(-(double)(2 * c1) * (1.0 / 128.0) * (double)o.log2_base) * 0.15915494309189533577;
+        f_hi[j] = (float)fd;
+        f_lo[j] = (float)(fd - (double)f_hi[j]);
+        c1p[j] = __builtin_amdgcn_cosf(f_hi[j]);
+        s1p[j] = __builtin_amdgcn_sinf(f_hi[j]);
+      }
+      auto angle = [&](uint32_t pos, int j, float& cs, float& sn) {
+        const float pf = (float)pos;  // exact: positions are below 2^24
+        const float a = pf * f_hi[j];
+        const float err = fmaf(pf, f_hi[j], -a);
+        const float frac = (a - floorf(a)) + fmaf(pf, f_lo[j], err);
+        sn = __builtin_amdgcn_sinf(frac);
+        cs = __builtin_amdgcn_cosf(frac);
+      };
+#pragma unroll
+      for (int i = 0; i < MI; ++i) {
+        uint32_t b0, p0;
+        split_pos(i * 16, b0, p0);
+        const bool run = p0 + 3 < seq;  // the group stays inside one sequence
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          float cs[4], sn[4];
+          angle(p0, j, cs[0], sn[0]);
+          if (run) {
+#pragma unroll
+            for (int e = 1; e < 4; ++e) {
+              cs[e] = cs[e - 1] * c1p[j] - sn[e - 1] * s1p[j];
+              sn[e] = sn[e - 1] * c1p[j] + cs[e - 1] * s1p[j];
+            }
+          } else {
+#pragma unroll
+            for (int e = 1; e < 4; ++e) {
+              uint32_t bb, pos;
+              split_pos(i * 16 + e, bb, pos);
+              angle(pos, j, cs[e], sn[e]);
+            }
+          }
+          float y1[4], y2[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float x1 = acc[i][j][e] + hb1[j], x2 = acc[i][j + 4][e] + hb2[j];
+            y1[e] = x1 * cs[e] - x2 * sn[e];
+            y2[e] = x2 * cs[e] + x1 * sn[e];
+          }
+          quad_transpose(y1, q);
+          quad_transpose(y2, q);
+          const int64_t row = row_base + i * 16 + q;
+          if (row < M) {
+            bf16_t* line = dst + row * ld + 16 * j + cq;
+            *reinterpret_cast<u32x2*>(line) = u32x2{pack_bf16x2(y1[0], y1[1]), pack_bf16x2(y1[2], y1[3])};
+            *reinterpret_cast<u32x2*>(line + 64) = u32x2{pack_bf16x2(y2[0], y2[1]), pack_bf16x2(y2[2], y2[3])};
+          }
+        }
+      }
+    } else {
+      // V head, stored transposed per sequence: Vt[b][g][c][p].  A lane
+      // holds 4-row runs of one channel; through the wave's own LDS region
+      // as [channel][row] (rows padded by 8), read back 8 rows of a channel
+      // per lane, each 16-byte store extends a run of a channel row of Vt.
+      // With seq a multiple of 8 an 8-row chunk never straddles two
+      // sequences; passes of PI 16-row blocks keep the regions in the LDS.
+      const int g = hd - o.hq - o.hkv;
+      bf16_t* vt = reinterpret_cast<bf16_t*>(o.vt);
+      float vb[8];  // bias of this lane's channel of each block
+#pragma unroll
+      for (int j = 0; j < 8; ++j) vb[j] = args.bias ? args.bias[(int64_t)hd * 128 + 16 * j + l15] : -0.0f;
+      if ((seq & 7u) == 0) {
+        constexpr int PI = (NW * 128 * (MI * 16 + 8) * 2 <= SMEM) ? MI : MI / 2;
+        constexpr int RP = PI * 16 + 8;  // padded row length of a channel in LDS
+        static_assert(MI % PI == 0 && NW * 128 * RP * 2 <= SMEM, "V staging region");
+        constexpr int CPC = PI * 2;      // 8-row chunks per channel per pass
+        bf16_t* reg = reinterpret_cast<bf16_t*>(smem) + wave * 128 * RP;
+        const int64_t wrow0 = m0 + wm * WROWS;  // the wave's first row (a multiple of 8)
+        const uint32_t vb0 = (uint32_t)(wrow0 / seq), vp0 = (uint32_t)(wrow0 - (int64_t)vb0 * seq);
+#pragma unroll
+        for (int i0 = 0; i0 < MI; i0 += PI) {
+          if (i0 > 0) wait_lgkmcnt0();  // the previous pass's reads are done
+#pragma unroll
+          for (int ii = 0; ii < PI; ++ii)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+              const u32x2 pr = {pack_bf16x2(acc[i0 + ii][j][0] + vb[j], acc[i0 + ii][j][1] + vb[j]),
+                                pack_bf16x2(acc[i0 + ii][j][2] + vb[j], acc[i0 + ii][j][3] + vb[j])};
+              *reinterpret_cast<u32x2*>(reg + (16 * j + l15) * RP + ii * 16 + 4 * kq) = pr;
+            }
+          wait_lgkmcnt0();
+#pragma unroll
+          for (int it = 0; it < 128 * CPC / 64; ++it) {
+            const int idx = it * 64 + lane;
+            const int cl = idx / CPC, kk = idx % CPC;
+            const u32x4 v = lds_read16(reg + cl * RP + 8 * kk);
+            const int off = i0 * 16 + 8 * kk;  // row offset within the wave
+            if (wrow0 + off < M) {
+              uint32_t b = vb0, p = vp0 + (uint32_t)off;
+              if (p >= seq) {
+                b += p / seq;
+                p %= seq;
+              }
+              *reinterpret_cast<u32x4*>(vt + (((int64_t)b * o.hkv + g) * 128 + cl) * o.seq_pad + p) = v;
+            }
+          }
+        }
+      } else {
+        const bool vec = (seq & 3u) == 0;  // groups of 4 never straddle sequences
+#pragma unroll
+        for (int i = 0; i < MI; ++i) {
+          const int64_t row0 = row_base + i * 16;
+          if (row0 >= M) continue;
+          uint32_t b0, p0;
+          split_pos(i * 16, b0, p0);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const int c = 16 * j + l15;
+            if (vec && row0 + 3 < M) {
+              bf16_t* line = vt + (((int64_t)b0 * o.hkv + g) * 128 + c) * o.seq_pad;
+              const u32x2 pr = {pack_bf16x2(acc[i][j][0] + vb[j], acc[i][j][1] + vb[j]),
+                                pack_bf16x2(acc[i][j][2] + vb[j], acc[i][j][3] + vb[j])};
+              *reinterpret_cast<u32x2*>(line + p0) = pr;
+            } else {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                if (row0 + e >= M) continue;
+                uint32_t b = b0, pos = p0 + e;
+                if (pos >= seq) {
+                  pos -= seq;
+                  ++b;
+                }
+                vt[(((int64_t)b * o.hkv + g) * 128 + c) * o.seq_pad + pos] = f32_to_bf16(acc[i][j][e] + vb[j]);
+              }
+            }
+          }
+        }
+      }
+    }
   } else {  // SwiGLU: gate block j and up block j + 4 of a wave are the same 16 outputs
     const int64_t ocol0 = (int64_t)bn * (BN / 2) + wn * 64;
     float bg[4], bu[4];  // gate and up biases of the lane's output column (-0: none)
@@ -1295,7 +1469,7 @@ __device__ __forceinline__ void lds_barrier() {
 
 template <int EPI>
 __global__ __launch_bounds__(256, 1) void gemm_small_kernel(Args args) {
-  static_assert(EPI != EPI_QKV, "the QKV epilogue runs on the 32x32 kernel");
+  static_assert(EPI != EPI_QKV, "the QKV epilogue runs on the large tiles");
   constexpr int A_T = SBM * ROWB;
   constexpr int B_T = SBN * ROWB;
   constexpr int ST = A_T + B_T;
@@ -1664,12 +1838,10 @@ void launch_part(Args a, int bn0, int cols, int groups, hipStream_t s) {
   a.num_bm = (int)((a.M + BMT - 1) / BMT);
   const int nb = a.num_bm * cols;
   if (nb == 0) return;
-  if constexpr (EPI != EPI_QKV) {
-    if (a.K >= MFMA16_MIN_K) {
-      hipLaunchKernelGGL((gemm16_kernel<EPI, BMT>), dim3(a.sk_ws ? 16 * ((nb + 7) / 8) : nb, groups), dim3(256), 0,
-                         s, a);
-      return;
-    }
+  if (a.K >= MFMA16_MIN_K) {
+    hipLaunchKernelGGL((gemm16_kernel<EPI, BMT>), dim3(a.sk_ws ? 16 * ((nb + 7) / 8) : nb, groups), dim3(256), 0, s,
+                       a);
+    return;
   }
   if (a.K >= W4_MIN_K) {
     hipLaunchKernelGGL((gemm_bf16_kernel<EPI, BMT, true>), dim3(nb, groups), dim3(Cfg<BMT, true>::NW * 64), 0, s, a);

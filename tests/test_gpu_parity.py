@@ -304,6 +304,53 @@ def test_qkv_rope_bias(device):
         assert not vt[:, g, :, seq:].any()
 
 
+@pytest.mark.parametrize("batch,seq,h,hq,hkv,bm", [
+    (2, 100, 4104, 4, 2, 128),     # seq a multiple of 4, not 8: V in 4-row stores; k tail of 8
+    (3, 203, 4104, 8, 2, 128),     # odd seq: 4-row groups straddle sequences; ragged m
+    (2, 1000, 4096, 8, 1, 128),    # V staged through LDS in one pass; ragged last tile
+    (4, 2048, 4096, 8, 1, 192),    # the 70B t=8 rank's layout (192-row tiles) at k = 4096
+    (2, 2048, 4096, 24, 4, 256),   # 256-row tiles: V staged in two passes
+])
+def test_qkv_rope_16x16(device, batch, seq, h, hq, hkv, bm):
+    """Q/K/V + RoPE on the 16x16-MFMA kernel (depth >= 4096) at every tile
+    height, with biases, against the oracle on sampled rows (every row of a
+    tile's first and last 16-row block, plus random ones)."""
+    d = 128
+    say(f"case qkv_rope 16x16 batch={batch} seq={seq} h={h} hq={hq} hkv={hkv}")
+    m, n = batch * seq, (hq + 2 * hkv) * d
+    assert tp.tp_gemm_plan(m, n, h, "qkv")[0] == bm
+    x = inputs.normal(16, 0, (m, h), 1.0, "bf16")
+    w = inputs.normal(16, 1, (n, h), 0.02, "bf16")
+    b = inputs.normal(16, 2, (n,), 0.5, "f32").data
+    seq_pad = (seq + 63) // 64 * 64
+    q = torch.empty(m, hq * d, dtype=torch.bfloat16, device=device)
+    k = torch.empty(m, hkv * d, dtype=torch.bfloat16, device=device)
+    vt = torch.full((batch, hkv, d, seq_pad), float("nan"), dtype=torch.bfloat16, device=device)
+    tp.tp_qkv_rope(batch, seq, h, hq, hkv, d, 500000.0, to_dev(x, device), to_dev(w, device), q, k, vt,
+                   bias=torch.from_numpy(b).to(device))
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(16)
+    rows = np.unique(np.concatenate([
+        np.arange(m)[(np.arange(m) % bm < 16) | (np.arange(m) % bm >= bm - 16)][:512],
+        np.arange(max(0, m - 40), m), rng.integers(0, m, 256)]))
+    X, W, B = x.f64()[rows], w.f64(), b.astype(np.float64)
+    pos = rows % seq
+    qh, kh = host(q)[rows], host(k)[rows]
+    vtok = host(vt[:, :, :, :seq].permute(0, 3, 1, 2).reshape(m, hkv * d))[rows]
+    for j in range(hq):
+        ref = oracle.rope(oracle.linear(X, W[j * d:(j + 1) * d].T, B[j * d:(j + 1) * d]), pos, 500000.0)
+        assert rel_err(qh[:, j * d:(j + 1) * d], ref) <= BF16_TOL, ("q", j)
+    for g in range(hkv):
+        r0 = (hq + g) * d
+        ref = oracle.rope(oracle.linear(X, W[r0:r0 + d].T, B[r0:r0 + d]), pos, 500000.0)
+        assert rel_err(kh[:, g * d:(g + 1) * d], ref) <= BF16_TOL, ("k", g)
+        r0 = (hq + hkv + g) * d
+        refv = oracle.linear(X, W[r0:r0 + d].T, B[r0:r0 + d])
+        assert rel_err(vtok[:, g * d:(g + 1) * d], refv) <= BF16_TOL, ("v", g)
+    assert not torch.isnan(vt[:, :, :, :seq]).any()      # every V element written
+    assert not vt[:, :, :, seq:].any()                   # the padding zeroed
+
+
 @pytest.mark.parametrize("dt,m,k,n,t", [("bf16", 300, 4096, 264, 4), ("bf16", 6100, 1024, 5904, 2),
                                         ("f32", 37, 64, 40, 2)])
 def test_rowwise_split_input_bit_exact(device, dt, m, k, n, t):
