@@ -394,6 +394,21 @@ tp_status tp_colwise_save(tp_act act, int64_t m, int64_t k, int64_t n, const voi
  * tp_transpose: dst [cols, rows] = src [rows, cols]^T (bf16).
  * tp_mlp_act_backward: the dPre step alone (and Y if y is not NULL).
  * ------------------------------------------------------------------------ */
+/* --------------------------------------------------------------------------
+ * tp_gemm_kmajor: the product the backward calls use for a transposed
+ * operand ("MLP" and "Self-attention" sections: dX = dPre W_in,
+ * dW = dZ^T Y and the like), read where it lies instead of transposed first.
+ *   out[i, j] = sum_l x'[i, l] w'[l, j]       [m, n] float32 or bf16 (out_dt)
+ *   w  [k, n] bf16, row stride ldw >= n (k-major: w' = w)
+ *   x  x_kmajor = 0: [m, k] bf16, row stride ldx >= k (x' = x);
+ *      x_kmajor = 1: [k, m] bf16, row stride ldx >= m (x' = x^T)
+ * m, n, k, ldx, ldw multiples of 8; each operand under 2 GiB of offsets.
+ * bf16 operands, float32 accumulation, device pointers, async on stream.
+ * TP_ERR_SHAPE / TP_ERR_INVALID_ARG for bad sizes, strides or pointers.
+ * ------------------------------------------------------------------------ */
+tp_status tp_gemm_kmajor(tp_dtype out_dt, int32_t x_kmajor, int64_t m, int64_t n, int64_t k, const void* x,
+                         int64_t ldx, const void* w, int64_t ldw, void* out, void* stream);
+
 size_t tp_shard_mlp_backward_workspace_bytes(tp_act act, int64_t m, int64_t h, int64_t f_shard);
 tp_status tp_shard_mlp_backward(tp_act act, int64_t m, int64_t h, int64_t f_shard, const void* x,
                                 const void* w_in, const void* w_out, const void* dz, const void* xt,
@@ -436,8 +451,10 @@ tp_status tp_mlp_act_backward(tp_act act, int64_t m, int64_t n, const void* pre,
  *   dw_qkv     = dQKV^T x         [(hq + 2 hkv) d, h] float32
  *   dw_o       = dZ^T O           [h, hq d] float32
  *   x, dz      [batch*seq, h] bf16; batch*seq must be a multiple of 8
- *   xt, dzt    [h, batch*seq] bf16 transposes of x and dz, or NULL (then the
- *              call makes them in ws)
+ *   xt, dzt    ignored (pass NULL; kept so the signature stays): dW_qkv
+ *              and dW_o read x, dz, O and dQKV where they lie, as k-major
+ *              operands of tp_gemm_kmajor's product, so no transposed copies
+ *              are made (nor for w_o and w_qkv in dO and dX)
  *   saved_q, saved_k, saved_vt, saved_o, saved_lse: the forward's, as written
  *              by tp_shard_attn_save, all five or none (then recomputed)
  *   ws         at least tp_shard_attn_backward_workspace_bytes bytes

@@ -3,6 +3,7 @@
 // failures return a status and leave a message for tp_last_error().
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -134,27 +135,22 @@ AttnBwdLayout attn_bwd_layout(int64_t batch, int64_t seq, int32_t hq, int32_t hk
 }
 
 // Workspace of one rank's attention backward: the recomputed forward (Q, K,
-// V^T, O and the log-sum-exp), dO, the packed dQKV and the transposed
-// operands of the weight-gradient products, then the attention core's own.
+// V^T, O and the log-sum-exp), dO and the packed dQKV, then the attention
+// core's own.
 struct AttnShardBwdLayout {
-  size_t fwd, lse, dout, wo_t, dqkv, wqkv_t, dzt, o_t, dqkv_t, xt, core, total;
+  size_t fwd, lse, dout, dqkv, core, total;
 };
 
 AttnShardBwdLayout attn_shard_bwd_layout(int64_t batch, int64_t seq, int64_t h, int32_t hq, int32_t hkv,
                                          int32_t d) {
-  const size_t M = (size_t)(batch * seq), H = (size_t)h, QD = (size_t)hq * d, N = (size_t)(hq + 2 * hkv) * d;
+  const size_t M = (size_t)(batch * seq), QD = (size_t)hq * d, N = (size_t)(hq + 2 * hkv) * d;
+  (void)h;
   AttnShardBwdLayout L;
   L.fwd = 0;
   L.lse = L.fwd + attn_layout(batch, seq, hq, hkv, d).total;
   L.dout = L.lse + align256((size_t)batch * hq * (size_t)seq_pad_of(seq) * 4);
-  L.wo_t = L.dout + align256(M * QD * 2);
-  L.dqkv = L.wo_t + align256(QD * H * 2);
-  L.wqkv_t = L.dqkv + align256(M * N * 2);
-  L.dzt = L.wqkv_t + align256(H * N * 2);
-  L.o_t = L.dzt + align256(H * M * 2);
-  L.dqkv_t = L.o_t + align256(QD * M * 2);
-  L.xt = L.dqkv_t + align256(N * M * 2);
-  L.core = L.xt + align256(H * M * 2);
+  L.dqkv = L.dout + align256(M * QD * 2);
+  L.core = L.dqkv + align256(M * N * 2);
   L.total = L.core + attn_bwd_layout(batch, seq, hq, hkv, d).total;
   return L;
 }
@@ -528,8 +524,10 @@ tp_status tp_shard_attn_backward(int64_t batch, int64_t seq, int64_t h, int32_t 
   TRY(check_ptr(w_o, "w_o"));
   TRY(check_gemm(TP_ACT_NONE, TP_BF16, h, m, qd, ws, ws, dw_o, "ws", "ws", "dw_o"));
   TRY(check_gemm(TP_ACT_NONE, TP_BF16, n, m, h, ws, ws, dw_qkv, "ws", "ws", "dw_qkv"));
-  if (xt) TRY(check_ptr(xt, "xt"));
-  if (dzt) TRY(check_ptr(dzt, "dzt"));
+  (void)xt;  // the weight-gradient products read x and dz in place
+  (void)dzt;
+  if (m * std::max(h, n) * 2 >= kMaxOffset)
+    return fail(TP_ERR_SHAPE, "batch * seq x %lld activations exceed 2 GiB", (long long)std::max(h, n));
   const void* sv[5] = {saved_q, saved_k, saved_vt, saved_o, saved_lse};
   const int nsaved = (saved_q != nullptr) + (saved_k != nullptr) + (saved_vt != nullptr) + (saved_o != nullptr) +
                      (saved_lse != nullptr);
@@ -543,8 +541,9 @@ tp_status tp_shard_attn_backward(int64_t batch, int64_t seq, int64_t h, int32_t 
   char* b = static_cast<char*>(ws);
   const AttnLayout F = attn_layout(batch, seq, hq, hkv, head_dim);
   char* f = b + L.fwd;
-  auto gemm = [&](int epi, int64_t M, int64_t N, int64_t K, const void* a, const void* w, void* c) {
-    return tpk::launch_gemm_bf16(epi, M, N, K, a, w, c, nullptr, s);
+  auto km = [&](int epi, bool x_kmajor, int64_t M, int64_t N, int64_t K, const void* a, int64_t lda, const void* w,
+                int64_t ldw, void* c) {
+    return tpk::launch_gemm_bf16_km(epi, x_kmajor, M, N, K, a, lda, w, ldw, c, s);
   };
   hipError_t e;
 #define TP_STEP(call, what) \
@@ -566,30 +565,17 @@ tp_status tp_shard_attn_backward(int64_t batch, int64_t seq, int64_t h, int32_t 
     o = f + F.o;
     lse = reinterpret_cast<const float*>(b + L.lse);
   }
-  // dO = dZ W_o (W_o [h, hq d] transposed to [hq d, h])
-  TP_STEP(tpk::launch_transpose(h, qd, w_o, b + L.wo_t, s), "tp_shard_attn_backward (w_o^T)");
-  TP_STEP(gemm(tpk::EPI_BF16, m, qd, h, dz, b + L.wo_t, b + L.dout), "tp_shard_attn_backward (dO)");
+  // dO = dZ W_o (W_o [h, hq d] read as the k-major operand)
+  TP_STEP(km(tpk::EPI_BF16, false, m, qd, h, dz, h, w_o, qd, b + L.dout), "tp_shard_attn_backward (dO)");
   // the attention core: dQKV before RoPE, packed like the projection's output
   TRY(tp_flash_attn_backward(batch, seq, hq, hkv, head_dim, rope_base, causal, q, k, vt, o, lse, b + L.dout,
                              b + L.core, L.total - L.core, b + L.dqkv, n, stream));
-  // dX partial = dQKV W_qkv (W_qkv transposed to [h, n]); f's backward sums these over ranks
-  TP_STEP(tpk::launch_transpose(n, h, w_qkv, b + L.wqkv_t, s), "tp_shard_attn_backward (w_qkv^T)");
-  TP_STEP(gemm(tpk::EPI_F32, m, h, n, b + L.dqkv, b + L.wqkv_t, dx_partial), "tp_shard_attn_backward (dX)");
-  // dW_o = dZ^T O and dW_qkv = dQKV^T X, reducing over the tokens
-  const void* dzt_p = dzt;
-  if (!dzt_p) {
-    TP_STEP(tpk::launch_transpose(m, h, dz, b + L.dzt, s), "tp_shard_attn_backward (dZ^T)");
-    dzt_p = b + L.dzt;
-  }
-  const void* xt_p = xt;
-  if (!xt_p) {
-    TP_STEP(tpk::launch_transpose(m, h, x, b + L.xt, s), "tp_shard_attn_backward (X^T)");
-    xt_p = b + L.xt;
-  }
-  TP_STEP(tpk::launch_transpose(m, qd, o, b + L.o_t, s), "tp_shard_attn_backward (O^T)");
-  TP_STEP(gemm(tpk::EPI_F32, h, qd, m, dzt_p, b + L.o_t, dw_o), "tp_shard_attn_backward (dW_o)");
-  TP_STEP(tpk::launch_transpose(m, n, b + L.dqkv, b + L.dqkv_t, s), "tp_shard_attn_backward (dQKV^T)");
-  TP_STEP(gemm(tpk::EPI_F32, n, h, m, b + L.dqkv_t, xt_p, dw_qkv), "tp_shard_attn_backward (dW_qkv)");
+  // dX partial = dQKV W_qkv (W_qkv [n, h] read k-major); f's backward sums these over ranks
+  TP_STEP(km(tpk::EPI_F32, false, m, h, n, b + L.dqkv, n, w_qkv, h, dx_partial), "tp_shard_attn_backward (dX)");
+  // dW_o = dZ^T O and dW_qkv = dQKV^T X, reducing over the tokens: both
+  // operands read k-major (token rows) where they lie
+  TP_STEP(km(tpk::EPI_F32, true, h, qd, m, dz, h, o, qd, dw_o), "tp_shard_attn_backward (dW_o)");
+  TP_STEP(km(tpk::EPI_F32, true, n, h, m, b + L.dqkv, n, x, h, dw_qkv), "tp_shard_attn_backward (dW_qkv)");
 #undef TP_STEP
   return ok();
 }
@@ -873,6 +859,25 @@ tp_status tp_transpose(int64_t rows, int64_t cols, const void* src, void* dst, v
   if (src == dst) return fail(TP_ERR_INVALID_ARG, "dst aliases src");
   TRY(device_check());
   return launched(tpk::launch_transpose(rows, cols, src, dst, as_stream(stream)), "tp_transpose");
+}
+
+tp_status tp_gemm_kmajor(tp_dtype out_dt, int32_t x_kmajor, int64_t m, int64_t n, int64_t k, const void* x,
+                         int64_t ldx, const void* w, int64_t ldw, void* out, void* stream) {
+  if (out_dt != TP_F32 && out_dt != TP_BF16) return fail(TP_ERR_INVALID_ARG, "unknown output dtype %d", (int)out_dt);
+  if (m < 0 || n < 0 || k < 0) return fail(TP_ERR_SHAPE, "m, n and k must be >= 0");
+  if (m % 8 || n % 8 || k % 8) return fail(TP_ERR_SHAPE, "m, n and k must be multiples of 8");
+  if (ldx < (x_kmajor ? m : k) || ldw < n || ldx % 8 || ldw % 8)
+    return fail(TP_ERR_SHAPE, "ldx and ldw must be multiples of 8 covering a row of x and w");
+  if (k * ldx * 2 >= kMaxOffset || k * ldw * 2 >= kMaxOffset || (!x_kmajor && 256 * ldx * 2 >= kMaxOffset))
+    return fail(TP_ERR_SHAPE, "an operand exceeds the 2 GiB offset range");
+  if (m == 0 || n == 0) return ok();
+  TRY(check_ptr(x, "x"));
+  TRY(check_ptr(w, "w"));
+  TRY(check_ptr(out, "out"));
+  TRY(device_check());
+  return launched(tpk::launch_gemm_bf16_km(out_dt == TP_F32 ? tpk::EPI_F32 : tpk::EPI_BF16, x_kmajor != 0, m, n, k, x,
+                                           ldx, w, ldw, out, as_stream(stream)),
+                  "tp_gemm_kmajor");
 }
 
 tp_status tp_mlp_act_backward(tp_act act, int64_t m, int64_t n, const void* pre, const void* dy, void* dpre,

@@ -104,7 +104,8 @@ struct Args {
   const bf16_t* w[MAX_GROUP];
   void* out[MAX_GROUP];
   int64_t M, N, K;
-  int64_t lda;        // row stride of x in elements (>= K; a column slice when > K)
+  int64_t lda;        // row stride of x in elements (>= K; a column slice when > K); k-major x: of its k rows
+  int64_t ldb;        // k-major w (the 16x16 kernel's KM >= 1): row stride of its k rows (>= N)
   const float* bias;  // per output column, added before the epilogue's nonlinearity, or NULL
   void* pre[MAX_GROUP];  // _SAVE epilogues: bf16 pre-activation rows (GeLU N, SwiGLU 2 N wide)
   int num_bm;  // tile rows of this launch (height BMT)
@@ -894,8 +895,42 @@ __device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
 
 __device__ __forceinline__ int swz16(int r) { return (r >> 1) & 7; }
 
-template <int EPI, int BMT>
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+
+// LDS-DMA load issued from inline asm, for the kernels that read LDS with
+// transposing reads.  The compiler assumes such a read may alias any LDS-DMA
+// store it knows to be in flight and waits for all of them (vmcnt(0)) before
+// each one, which drains the prefetch; loads issued here are not tracked by
+// it, and the kernel's own waits before every barrier cover them.  The load
+// writes LDS only (no register result), and M0, its LDS base, is set in the
+// same statement.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma_lds16_asm(__amdgpu_buffer_rsrc_t rsrc, void* lds_wave_base, uint32_t voffset,
+                                              uint32_t soffset) {
+  const uint32_t base = (uint32_t)(uintptr_t)LDS_PTR(lds_wave_base);
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds" ::"s"(base), "v"(voffset), "s"(rsrc),
+               "s"(soffset)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// KM: operand layouts.  0: x [M, K] and w [N, K] (k contiguous); 1: w stored
+// k-major, [K, N]; 2: x [K, M] and w [K, N] both k-major.  A k-major tile
+// sits in LDS as groups of 8 k rows, each group as the tile's 16-row blocks
+// of 8 x 32 bytes: one DMA instruction fills 4 blocks x 8 k rows from 8
+// global segments of 128 bytes, and fragments come from pairs of transposing
+// reads (ds_read_b64_tr_b16: 16 lanes give 4 k rows x 16 rows, each lane
+// gets one row's 4 k values).  The MFMA's k slots run through the 32 k of a
+// step in the order 8 g + 4 h + t -> 16 (g >> 1) + 8 h + 4 (g & 1) + t (lane
+// group g, read h, t < 4), the same for both operands, so each half wave
+// reads 8 consecutive k rows of a block (256 contiguous bytes: no bank
+// conflicts) and block, step and read offsets are immediates.  A
+// k-contiguous x beside a k-major w takes the same order with 8-byte reads.
+template <int EPI, int BMT, int KM = 0>
 __global__ __launch_bounds__(256, 1) void gemm16_kernel(Args args) {
+  constexpr bool KA = KM == 2, KB = KM >= 1;
+  static_assert(!KB || (EPI == EPI_F32 || EPI == EPI_BF16), "k-major operands: plain epilogues");
   constexpr int NW = 4;
   constexpr int WROWS = BMT / 2;  // 2 x 2 waves
   constexpr int MI = WROWS / 16;  // 16-row blocks per wave
@@ -933,18 +968,25 @@ __global__ __launch_bounds__(256, 1) void gemm16_kernel(Args args) {
   const uint32_t row_bytes = (uint32_t)(K * 2);
   const uint32_t a_row_bytes = (uint32_t)(lda * 2);
   const int m_rows = (int)min<int64_t>(BMT, M - m0);
-  __amdgpu_buffer_rsrc_t rsrc_a = make_rsrc(xg + m0 * lda, (uint32_t)m_rows * a_row_bytes);
+  __amdgpu_buffer_rsrc_t rsrc_a = KA ? make_rsrc(xg, (uint32_t)(K * lda * 2))
+                                     : make_rsrc(xg + m0 * lda, (uint32_t)m_rows * a_row_bytes);
   __amdgpu_buffer_rsrc_t rsrc_b;
   int n_valid;  // valid weight rows (plain) or valid output columns (SwiGLU)
   if (is_swiglu(EPI)) {
     const int64_t o0 = (int64_t)bn * (BN / 2);
     n_valid = (int)min<int64_t>(BN / 2, N - o0);
     rsrc_b = make_rsrc(wg + o0 * K, (uint32_t)((N + n_valid) * K * 2));
+  } else if (KB) {
+    n_valid = (int)min<int64_t>(BN, N - (int64_t)bn * BN);
+    rsrc_b = make_rsrc(wg, (uint32_t)(K * args.ldb * 2));
   } else {
     const int64_t n0 = (int64_t)bn * BN;
     n_valid = (int)min<int64_t>(BN, N - n0);
     rsrc_b = make_rsrc(wg + n0 * K, (uint32_t)n_valid * row_bytes);
   }
+  // k-major operands: a stage moves 64 k rows of its tile, BK * ld * 2 bytes
+  const uint32_t a_step = KA ? (uint32_t)(BK * lda * 2) : (uint32_t)(BK * 2);
+  const uint32_t b_step = KB ? (uint32_t)(BK * args.ldb * 2) : (uint32_t)(BK * 2);
 
   // global -> LDS: wave-instruction blk of a stage fills tile row slot / CH,
   // physical chunk slot % CH, from logical chunk (slot % CH) ^ swz16(row).
@@ -952,9 +994,24 @@ __global__ __launch_bounds__(256, 1) void gemm16_kernel(Args args) {
   // each 64-output half (the same interleave as the 32x32 kernel).
   uint32_t a_off[LA], b_off[LB];
   int a_k[LA], b_k[LB];
+  // k-major tile of R rows: instruction q covers k rows 8 (q / (R / 64)) ..
+  // + 7 of the 16-row blocks 4 (q % (R / 64)) .. + 3; lane L reads block
+  // + L / 16, k row (L % 16) / 2, 8 columns from 8 (L % 2).  The k row is
+  // returned in *kk; the offset is TP_OOB_OFFSET past the valid columns.
+  auto km_off = [&](int q, int R, int64_t col0, int64_t ncol, int64_t ld, int* kk) -> uint32_t {
+    const int kg = q / (R / 64), b4 = q % (R / 64);
+    const int blk = 4 * b4 + (lane >> 4), krow = kg * 8 + ((lane & 15) >> 1);
+    const int64_t col = 16 * blk + 8 * (lane & 1);
+    *kk = krow;
+    return col < ncol ? (uint32_t)(krow * ld * 2 + (col0 + col) * 2) : TP_OOB_OFFSET;
+  };
 #pragma unroll
   for (int j = 0; j < LA; ++j) {
     const int slot = (j * NW + wave) * 64 + lane;
+    if (KA) {
+      a_off[j] = km_off(j * NW + wave, BMT, m0, m_rows, lda, &a_k[j]);
+      continue;
+    }
     const int r = slot / CH;
     const int c = (slot % CH) ^ swz16(r);
     a_k[j] = c * 8;
@@ -963,6 +1020,10 @@ __global__ __launch_bounds__(256, 1) void gemm16_kernel(Args args) {
 #pragma unroll
   for (int j = 0; j < LB; ++j) {
     const int slot = (j * NW + wave) * 64 + lane;
+    if (KB) {
+      b_off[j] = km_off(j * NW + wave, BN, (int64_t)bn * BN, n_valid, args.ldb, &b_k[j]);
+      continue;
+    }
     const int r = slot / CH;
     const int c = (slot % CH) ^ swz16(r);
     b_k[j] = c * 8;
@@ -975,21 +1036,35 @@ __global__ __launch_bounds__(256, 1) void gemm16_kernel(Args args) {
       b_off[j] = (uint32_t)r * row_bytes + (uint32_t)c * 16;
     }
   }
+  // (k-major variants: every load from inline asm, see dma_lds16_asm)
+  auto dma = [&](__amdgpu_buffer_rsrc_t r, char* dst, uint32_t voff, uint32_t soff) {
+    if constexpr (KM != 0) dma_lds16_asm(r, dst, voff, soff);
+    else if (soff) buffer_load_lds16_so(r, dst, voff, soff);
+    else buffer_load_lds16(r, dst, voff);
+  };
   auto load_a = [&](auto stage_tag, auto full_tag, int kn, int j) {
     constexpr int S = decltype(stage_tag)::value;
     char* const dst = smem + S * A_TILE + (j * NW + wave) * 1024;
-    const uint32_t kb = (uint32_t)kn * (uint32_t)(BK * 2);
-    if (decltype(full_tag)::value) buffer_load_lds16_so(rsrc_a, dst, a_off[j], kb);
-    else buffer_load_lds16(rsrc_a, dst, ((int64_t)kn * BK + a_k[j]) < K ? a_off[j] + kb : TP_OOB_OFFSET);
+    const uint32_t kb = (uint32_t)kn * a_step;
+    if (decltype(full_tag)::value) {
+      if constexpr (KM != 0) dma_lds16_asm(rsrc_a, dst, a_off[j], kb);
+      else buffer_load_lds16_so(rsrc_a, dst, a_off[j], kb);
+    } else {
+      dma(rsrc_a, dst,
+          ((int64_t)kn * BK + a_k[j]) < K && a_off[j] != TP_OOB_OFFSET ? a_off[j] + kb : TP_OOB_OFFSET, 0u);
+    }
   };
   auto load_b = [&](auto stage_tag, auto full_tag, int kn, int j) {
     constexpr int S = decltype(stage_tag)::value;
     char* const dst = smem + B_BASE + S * B_TILE + (j * NW + wave) * 1024;
-    const uint32_t kb = (uint32_t)kn * (uint32_t)(BK * 2);
-    if (decltype(full_tag)::value) buffer_load_lds16_so(rsrc_b, dst, b_off[j], kb);
-    else
-      buffer_load_lds16(rsrc_b, dst,
-                        ((int64_t)kn * BK + b_k[j]) < K && b_off[j] != TP_OOB_OFFSET ? b_off[j] + kb : TP_OOB_OFFSET);
+    const uint32_t kb = (uint32_t)kn * b_step;
+    if (decltype(full_tag)::value) {
+      if constexpr (KM != 0) dma_lds16_asm(rsrc_b, dst, b_off[j], kb);
+      else buffer_load_lds16_so(rsrc_b, dst, b_off[j], kb);
+    } else {
+      dma(rsrc_b, dst,
+          ((int64_t)kn * BK + b_k[j]) < K && b_off[j] != TP_OOB_OFFSET ? b_off[j] + kb : TP_OOB_OFFSET, 0u);
+    }
   };
   // load j (0 .. LA + LB - 1) of a stage: the A loads, then the B loads
   auto load_one = [&](auto stage_tag, auto full_tag, int kn, int j) {
@@ -1011,14 +1086,53 @@ __global__ __launch_bounds__(256, 1) void gemm16_kernel(Args args) {
     ra[s] = (uint32_t)(r_a * ROWB + ((c ^ swz16(r_a)) << 4));
     rb[s] = (uint32_t)(B_BASE + r_b * ROWB + ((c ^ swz16(r_b)) << 4));
   }
+  // k-major fragments: the lane's address in its block's group of 8 k rows
+  // (half wave g >> 1 two groups further); + 256 per block, + (4 s + h) x
+  // blocks x 256 per step s and read h.  A k-contiguous x beside a k-major w:
+  // two 8-byte reads at k chunk 4 s + 2 (g >> 1) + h, bytes 8 (g & 1) on.
+  const uint32_t tr_lane = (uint32_t)((4 * (kq & 1) + (l15 >> 2)) * 32 + 8 * (l15 & 3));
+  const uint32_t ra_km = (uint32_t)((kq >> 1) * 2 * (BMT / 16) * 256 + wm * (WROWS / 16) * 256) + tr_lane;
+  const uint32_t rb_km = (uint32_t)(B_BASE + (kq >> 1) * 2 * (BN / 16) * 256 + wn * 8 * 256) + tr_lane;
+  uint32_t ra_pi[KS][2];
+#pragma unroll
+  for (int s = 0; s < KS; ++s)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int r_a = wm * WROWS + l15;
+      const int c = 4 * s + 2 * (kq >> 1) + h;
+      ra_pi[s][h] = (uint32_t)(r_a * ROWB + ((c ^ swz16(r_a)) << 4) + 8 * (kq & 1));
+    }
   f32x4 acc[MI][NJ];
 #pragma unroll
   for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int j = 0; j < NJ; ++j) acc[i][j] = f32x4{};
   u32x4 fa[MI], fb[2][NJ];
-  auto rd_a = [&](const char* a, int s, int i) { fa[i] = lds_read16(a + ra[s] + 2048 * i); };
-  auto rd_b = [&](const char* b, int s, int j) { fb[s & 1][j] = lds_read16(b + rb[s] + 2048 * j); };
+  auto tr_pair = [](const char* p0, const char* p1) {
+    typedef __attribute__((address_space(3))) v4i16_t* lds_v4;
+    const u32x2 lo = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4)(LDS_PTR(p0))));
+    const u32x2 hi = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4)(LDS_PTR(p1))));
+    return u32x4{lo[0], lo[1], hi[0], hi[1]};
+  };
+  auto rd_a = [&](const char* a, int s, int i) {
+    if constexpr (KA) {
+      const char* p = a + ra_km + 256 * i + 4 * s * (BMT / 16) * 256;
+      fa[i] = tr_pair(p, p + (BMT / 16) * 256);
+    } else if constexpr (KB) {
+      const u32x2 lo = lds_read8(a + ra_pi[s][0] + 2048 * i), hi = lds_read8(a + ra_pi[s][1] + 2048 * i);
+      fa[i] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+    } else {
+      fa[i] = lds_read16(a + ra[s] + 2048 * i);
+    }
+  };
+  auto rd_b = [&](const char* b, int s, int j) {
+    if constexpr (KB) {
+      const char* p = b + rb_km + 256 * j + 4 * s * (BN / 16) * 256;
+      fb[s & 1][j] = tr_pair(p, p + (BN / 16) * 256);
+    } else {
+      fb[s & 1][j] = lds_read16(b + rb[s] + 2048 * j);
+    }
+  };
 
   const int nfull = (int)(K / BK);  // k-steps without a k tail
   // this workgroup's k-steps [kb, ke)
@@ -1737,11 +1851,15 @@ int64_t cost(int64_t M, int64_t cols, int bmt, int groups) {
   return rounds_of(tiles) * (bmt + 256);
 }
 
-Plan plan_for(int64_t M, int64_t nbn, int groups) {
+// max_h: the tallest tile height allowed (256, or 192 for the k-major
+// variants, whose 256-row tiles do not fit the register file: the allocator
+// then shuffles accumulators through the k loop).
+Plan plan_for(int64_t M, int64_t nbn, int groups, int max_h = 256) {
   static const int H[3] = {256, 192, 128};
-  Plan best{256, (int)nbn, 256, 0, 0};
-  int64_t best_cost = cost(M, nbn, 256, groups);
+  Plan best{max_h, (int)nbn, max_h, 0, 0};
+  int64_t best_cost = cost(M, nbn, max_h, groups);
   for (int hm : H) {
+    if (hm > max_h) continue;
     const int64_t one = cost(M, nbn, hm, groups);
     if (one < best_cost) {
       best_cost = one;
@@ -1903,7 +2021,63 @@ void launch_planned(const Args& a, int64_t nbn, int groups, hipStream_t s) {
   if (p.split < nbn) part(p.bm_tail, p.split, (int)(nbn - p.split));
 }
 
+template <int EPI, int KM>
+void launch_km(Args a, int64_t nbn, hipStream_t s) {
+  const Plan p = plan_for(a.M, nbn, 1, 192);
+  auto part = [&](int bmt, int bn0, int cols) {
+    a.bn0 = bn0;
+    a.num_bn = cols;
+    if (cols <= 0) return;
+    switch (bmt) {
+      case 192:
+        a.num_bm = (int)((a.M + 191) / 192);
+        hipLaunchKernelGGL((gemm16_kernel<EPI, 192, KM>), dim3(a.num_bm * cols), dim3(256), 0, s, a);
+        break;
+      default:
+        a.num_bm = (int)((a.M + 127) / 128);
+        hipLaunchKernelGGL((gemm16_kernel<EPI, 128, KM>), dim3(a.num_bm * cols), dim3(256), 0, s, a);
+        break;
+    }
+  };
+  part(p.bm_main, 0, p.split);
+  part(p.bm_tail, p.split, (int)(nbn - p.split));
+}
+
 }  // namespace
+
+hipError_t launch_gemm_bf16_km(int epi, bool x_kmajor, int64_t M, int64_t N, int64_t K, const void* x, int64_t ldx,
+                               const void* w, int64_t ldw, void* out, hipStream_t s) {
+  if (epi != EPI_F32 && epi != EPI_BF16) return hipErrorInvalidValue;
+  Args a;
+  for (int g = 0; g < MAX_GROUP; ++g) {
+    a.x[g] = reinterpret_cast<const bf16_t*>(x);
+    a.w[g] = reinterpret_cast<const bf16_t*>(w);
+    a.out[g] = out;
+    a.pre[g] = nullptr;
+  }
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  a.lda = ldx;
+  a.ldb = ldw;
+  a.bias = nullptr;
+  a.num_bm = a.num_bn = a.bn0 = 0;
+  a.sk_ws = nullptr;
+  a.sk_flag = nullptr;
+  a.sk_epoch = 0;
+  a.sk_half = 0;
+  a.qkv = QkvOut{};
+  const int64_t nbn = (N + BN - 1) / BN;
+  if (M == 0 || nbn == 0) return hipSuccess;
+  if (epi == EPI_F32) {
+    if (x_kmajor) launch_km<EPI_F32, 2>(a, nbn, s);
+    else launch_km<EPI_F32, 1>(a, nbn, s);
+  } else {
+    if (x_kmajor) launch_km<EPI_BF16, 2>(a, nbn, s);
+    else launch_km<EPI_BF16, 1>(a, nbn, s);
+  }
+  return hipGetLastError();
+}
 
 void gemm_plan(int64_t M, int64_t N, int64_t K, int kind, int groups, int* bm_main, int* split, int* bm_tail,
                int* split_k) {
@@ -1936,6 +2110,7 @@ hipError_t launch_gemm_bf16_group(int epi, int groups, int64_t M, int64_t N, int
   a.N = N;
   a.K = K;
   a.lda = lda > 0 ? lda : K;
+  a.ldb = 0;
   a.bias = bias;
   a.num_bm = a.num_bn = a.bn0 = 0;
   a.sk_ws = nullptr;

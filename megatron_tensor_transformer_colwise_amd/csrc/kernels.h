@@ -49,6 +49,14 @@ enum { GEMM_PLAN_ROWWISE = 0, GEMM_PLAN_COLWISE = 1, GEMM_PLAN_SWIGLU = 2, GEMM_
 void gemm_plan(int64_t M, int64_t N, int64_t K, int kind, int groups, int* bm_main, int* split, int* bm_tail,
                int* split_k);
 
+// out = epi(x' w') with w' = w stored k-major ([K, N], row stride ldw >= N)
+// and x' = x either k-contiguous ([M, K], row stride ldx >= K) or, with
+// x_kmajor, k-major too ([K, M], row stride ldx >= M): the backward's
+// products of a transposed operand without a transpose pass.  epi: EPI_F32
+// or EPI_BF16.  M, N, K multiples of 8; K * ldx * 2 and K * ldw * 2 bytes
+// below 2 GiB.
+hipError_t launch_gemm_bf16_km(int epi, bool x_kmajor, int64_t M, int64_t N, int64_t K, const void* x, int64_t ldx,
+                               const void* w, int64_t ldw, void* out, hipStream_t s);
 // G (<= 16) GEMMs of the same shape in one launch: out[g] = epi(x[g] . w[g]^T).
 hipError_t launch_gemm_bf16_group(int epi, int groups, int64_t M, int64_t N, int64_t K,
                                   const void* const* x, const void* const* w, void* const* out,

@@ -66,6 +66,7 @@ _SIGS = {
                               _vp, _vp, _vp, _vp],
     "tp_colwise_save": [_i32, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp],
     "tp_transpose": [_i64, _i64, _vp, _vp, _vp],
+    "tp_gemm_kmajor": [_i32, _i32, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _vp],
     "tp_mlp_act_backward": [_i32, _i64, _i64, _vp, _vp, _vp, _vp, _vp],
     "tp_shard_sum_rmsnorm_backward_workspace_bytes": [_i64, _i64],
     "tp_shard_sum_rmsnorm_backward": [_i32, _i64, _i64, _i64, _i64, ctypes.POINTER(_vp), _vp, _i32, _vp, _f32, _vp,
@@ -324,6 +325,11 @@ def tp_shard_attn_save(batch, seq, h, hq, hkv, head_dim, rope_base, causal, x, w
 
 def tp_transpose(rows, cols, src, dst, stream=None) -> None:
     _check(lib().tp_transpose(rows, cols, _p(src), _p(dst), _s(stream)))
+
+
+def tp_gemm_kmajor(out_dt, x_kmajor, m, n, k, x, ldx, w, ldw, out, stream=None) -> None:
+    _check(lib().tp_gemm_kmajor(_e(out_dt, DTYPES), int(bool(x_kmajor)), m, n, k, _p(x), ldx, _p(w), ldw, _p(out),
+                                _s(stream)))
 
 
 def tp_mlp_act_backward(act, m, n, pre, dy, dpre, y, stream=None) -> None:

@@ -348,6 +348,15 @@ def test_mlp_backward_validation(L):
     assert save(2, pre=A16 + 4096) == tp.TP_ERR_INVALID_ARG                          # pre aliases y
     assert save(1, n=12) == tp.TP_ERR_SHAPE
     assert status("tp_transpose", 4, 4, A16, A16, None) == tp.TP_ERR_INVALID_ARG    # in place
+    # the k-major product: sizes, strides and dtype checked before any launch
+    assert status("tp_gemm_kmajor", 9, 1, 16, 16, 16, A16, 16, A16, 16, A16, None) == tp.TP_ERR_INVALID_ARG
+    assert status("tp_gemm_kmajor", tp.TP_F32, 1, 12, 16, 16, A16, 16, A16, 16, A16, None) == tp.TP_ERR_SHAPE
+    assert status("tp_gemm_kmajor", tp.TP_F32, 1, 16, 16, 16, A16, 8, A16, 16, A16, None) == tp.TP_ERR_SHAPE  # ldx < m
+    assert status("tp_gemm_kmajor", tp.TP_F32, 0, 16, 16, 24, A16, 16, A16, 16, A16, None) == tp.TP_ERR_SHAPE  # ldx < k
+    assert status("tp_gemm_kmajor", tp.TP_F32, 0, 16, 16, 16, A16, 16, A16, 8, A16, None) == tp.TP_ERR_SHAPE   # ldw < n
+    assert status("tp_gemm_kmajor", tp.TP_BF16, 1, 16, 16, 1 << 20, A16, 1 << 10, A16, 16, A16, None) == tp.TP_ERR_SHAPE
+    assert status("tp_gemm_kmajor", tp.TP_F32, 1, 0, 16, 16, None, 16, None, 16, None, None) == tp.TP_OK
+    assert status("tp_gemm_kmajor", tp.TP_F32, 1, 16, 16, 16, None, 16, A16, 16, A16, None) == tp.TP_ERR_INVALID_ARG
     assert status("tp_transpose", 0, 4, None, None, None) == tp.TP_OK
     assert status("tp_mlp_act_backward", 0, 4, 16, A16, A16, A16, None, None) == tp.TP_ERR_INVALID_ARG
     assert status("tp_mlp_act_backward", 1, 4, 12, A16, A16, A16, None, None) == tp.TP_ERR_SHAPE

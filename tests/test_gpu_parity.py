@@ -156,6 +156,40 @@ def test_rowwise_gemm_many_tiles_bit_exact(device, m, k, n, plan):
     assert np.array_equal(host(out), y.f64() @ w.f64().T)
 
 
+@pytest.mark.parametrize("out,xk,m,n,k", [
+    ("f32", True, 4000, 4000, 520),     # x and w k-major, ragged m and n, k tail
+    ("f32", True, 4000, 2560, 136),     # 192-row tiles (three block groups per k group)
+    ("f32", True, 4000, 776, 1032),     # 128-row tiles, ragged n
+    ("f32", False, 4000, 4000, 520),    # k-contiguous x beside k-major w
+    ("f32", False, 4000, 2560, 4104),   # the same, deep k with a tail
+    ("bf16", False, 4000, 776, 4104),   # bf16 output
+    ("bf16", True, 1000, 4000, 64),     # one k step, ragged m
+])
+def test_gemm_kmajor_bit_exact(device, out, xk, m, n, k):
+    """tp_gemm_kmajor (the backward's products of a transposed operand) on
+    integer inputs in [-2, 2], strided operands: float32 outputs equal the
+    exact sums, bf16 outputs their rounding.  Its launches use 192- and
+    128-row tiles (the shapes here take both, main ranges and tails)."""
+    say(f"case gemm k-major out={out} x_kmajor={xk} m={m} n={n} k={k}")
+    xl = inputs.integers(17, 0, (m, k), -2, 2)             # the logical x'
+    wl = inputs.integers(17, 1, (k, n), -2, 2)             # w' = w, [k, n]
+    ldx = (m if xk else k) + 8
+    ldw = n + 16
+    xs = torch.zeros((k, ldx) if xk else (m, ldx), dtype=torch.bfloat16)
+    if xk:
+        xs[:, :m] = xl.torch().T
+    else:
+        xs[:, :k] = xl.torch()
+    ws = torch.zeros((k, ldw), dtype=torch.bfloat16)
+    ws[:, :n] = wl.torch()
+    dt = torch.float32 if out == "f32" else torch.bfloat16
+    o = torch.full((m, n), float("nan"), dtype=dt, device=device)
+    tp.tp_gemm_kmajor(out, xk, m, n, k, xs.to(device), ldx, ws.to(device), ldw, o)
+    torch.cuda.synchronize()
+    ref = xl.f64() @ wl.f64()
+    assert np.array_equal(host(o), ref if out == "f32" else _bf16_rne(ref))
+
+
 def _bf16_rne(v: np.ndarray) -> np.ndarray:
     """float64 values that float32 holds exactly, rounded to bfloat16 (nearest,
     ties to even) and widened back: the rounding of a bf16 store."""
