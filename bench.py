@@ -709,7 +709,7 @@ def main():
             "parallelism": f"tp{t} (ranks serialised on one GPU)",
         },
         "roofline": {
-            "kernel": "gemm_bf16_kernel<SWIGLU> (column-parallel W1|W3 GEMM + SwiGLU)",
+            "kernel": "gemm16_kernel<SWIGLU, 256> (column-parallel W1|W3 GEMM + SwiGLU, main and split-k launches)",
             "bound": "mfma",
             "achieved": round(col_tflops, 2),
             "peak": MFMA_BF16_PEAK_TFLOPS,

@@ -52,14 +52,17 @@ def pmc_summary(db_path: str) -> str:
     for did, name, counter, value, start, end in rows:
         d = disp.setdefault(did, {"name": _short(name), "us": (end - start) / 1000.0})
         d[counter] = value
+    # launches of one kernel that do different matrix work (a main launch and
+    # a split-k tail) are told apart by their MFMA op count
     per_kernel = collections.OrderedDict()
     for d in disp.values():
-        per_kernel.setdefault(d["name"], []).append(d)
-    lines = []
-    for name, ds in per_kernel.items():
+        key = (d["name"], d.get("SQ_INSTS_VALU_MFMA_MOPS_BF16"))
+        per_kernel.setdefault(key, []).append(d)
+
+    def describe(ds):
         counters = sorted(k for k in ds[0] if k not in ("name", "us"))
         us = [d["us"] for d in ds]
-        parts = [f"{name}: {len(ds)} dispatches, {min(us):.1f}-{max(us):.1f} us"]
+        parts = [f"{len(ds)} dispatches, {min(us):.1f}-{max(us):.1f} us"]
         if "GRBM_GUI_ACTIVE" in counters and "SQ_VALU_MFMA_BUSY_CYCLES" in counters:
             busy = [d["SQ_VALU_MFMA_BUSY_CYCLES"] / (d["GRBM_GUI_ACTIVE"] / XCDS * SIMDS) for d in ds]
             clk = [d["GRBM_GUI_ACTIVE"] / XCDS / d["us"] / 1e3 for d in ds if d["us"] > 0]
@@ -69,7 +72,13 @@ def pmc_summary(db_path: str) -> str:
         for c in counters:
             v = [d[c] for d in ds]
             parts.append(f"{c} {min(v):.4g}-{max(v):.4g}")
-        lines.append("; ".join(parts))
+        return "; ".join(parts)
+
+    lines = []
+    for (name, _), ds in per_kernel.items():
+        lines.append(f"{name}: " + describe(ds))
+        if len(ds) > 2:  # the first dispatch of a pass also counts what ran before it on the idle chip
+            lines.append(f"{name}, after the first: " + describe(ds[1:]))
     return "\n".join(lines)
 
 
