@@ -496,14 +496,20 @@ int flash_attn_pieces(int64_t batch, int64_t seq, int hq, int causal) {
   const int64_t nqb = (seq + BQ - 1) / BQ;
   const int64_t units = (nqb + 1) / 2 * hq * batch;
   if (units <= 0) return 1;
-  // Two workgroups per CU on 256 CUs; a piece keeps at least 4 key tiles
-  // (the first pair's list is the longest) and the partials fit their slots.
+  // Measured (forced piece counts, 16 causal shapes on one MI355X): a cut
+  // costs more than the chip it fills.  From 512 pair units (two workgroups
+  // per CU) one piece is fastest (4 x 4096 tokens, 8 heads: 177 us against
+  // 190 with 2 to 8); from 32 to 511 units two pieces are (the Llama-8B and
+  // 70B t=16 ranks: 39.6 us against 43 with 4 and 45 with 8; 70B t=8: 49.9
+  // against 59 unsplit and 65 with 3 or more; even 32 units, 64 workgroups,
+  // beat 256 workgroups of 8 pieces).  Below 32 units the cut fills the chip
+  // toward two workgroups per CU.  A piece keeps at least 4 key tiles (the
+  // first pair's list is the longest) and the partials fit their slots.
   const int64_t last = std::min<int64_t>(BQ - 1, seq - 1);
   const int64_t nx = causal ? last / BKV + 1 : (seq + BKV - 1) / BKV;
   const int64_t ny = nqb > 1 ? (seq + BKV - 1) / BKV : 0;
   const int64_t list = nx + ny;
-  int64_t p = (512 + units / 2) / units;
-  p = std::max<int64_t>(1, std::min<int64_t>(p, 8));
+  int64_t p = units >= 512 ? 1 : units >= 32 ? 2 : std::min<int64_t>((512 + units / 2) / units, 8);
   while (p > 1 && (list < 4 * p || (p - 1) * units > FA_MAX_SLOTS)) --p;
   return (int)p;
 }

@@ -194,11 +194,15 @@ def test_gemm_plans(L):
 
 
 def test_flash_attn_plans(L):
-    """Pieces per pair of query blocks (host-only call): about two
-    workgroups per CU on 256 CUs, at least 4 key tiles per piece."""
+    """Pieces per pair of query blocks (host-only call): one from 512 pair
+    units, two from 32, below that toward two workgroups per CU; at least 4
+    key tiles per piece."""
     assert tp.tp_flash_attn_plan(4, 2048, 8) == 2      # 70B t=8 rank: 8 pairs x 32 = 256 units
-    assert tp.tp_flash_attn_plan(4, 2048, 4) == 4      # 70B t=16 rank
-    assert tp.tp_flash_attn_plan(2, 2048, 8) == 4      # Llama-8B rank
+    assert tp.tp_flash_attn_plan(4, 2048, 4) == 2      # 70B t=16 rank: 128 units
+    assert tp.tp_flash_attn_plan(2, 2048, 8) == 2      # Llama-8B rank: 128 units
+    assert tp.tp_flash_attn_plan(1, 2048, 4) == 2      # 32 units
+    assert tp.tp_flash_attn_plan(1, 2048, 2) == 8      # 16 units
+    assert tp.tp_flash_attn_plan(4, 4096, 8) == 1      # 512 units
     assert tp.tp_flash_attn_plan(1, 2048, 1) == 8      # 34 tiles per pair: at most 8 pieces
     assert tp.tp_flash_attn_plan(1, 1000, 1) == 4      # 18 tiles per pair
     assert tp.tp_flash_attn_plan(1, 900, 2, False) == 7  # all keys: 30 tiles per pair
