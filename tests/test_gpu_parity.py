@@ -1077,6 +1077,35 @@ def test_colwise_activation_slices(device):
             assert rel_err(host(mlp.act_ws), ref) <= BF16_TOL
 
 
+@pytest.mark.parametrize("m,k,plan", [(64, 256, 64), (4096, 1024, 128), (1024, 4096, 256)])
+def test_gelu_epilogue_elementwise(device, m, k, plan):
+    """The bf16 GEMM's GeLU epilogue (erfc from a Chebyshev fit) element by
+    element over [-14, 14], signed zeros and the tails, through an identity
+    weight so each output is GeLU of one bf16 input exactly: within a bf16
+    rounding step of the oracle's erf form (plus the oracle's own float64
+    error in the far negative tail), on small tiles, the eight-wave 32x32 kernel and
+    the 16x16 kernel (k = 4096, as split-k pairs)."""
+    say(f"case gelu epilogue m={m} k={k}")
+    assert tp.tp_gemm_plan(m, k, k, "colwise")[0] == plan
+    vals = np.linspace(-14.0, 14.0, m * k).reshape(m, k)
+    vals[0, :4] = [0.0, -0.0, 1e-6, -1e-6]
+    xb = inputs.from_f32(vals.astype(np.float32), "bf16")
+    w = inputs.from_f32(np.eye(k, dtype=np.float32), "bf16")
+    y = torch.empty(m, k, dtype=torch.bfloat16, device=device)
+    tp.tp_colwise("gelu", "bf16", m, k, k, to_dev(xb, device), to_dev(w, device), y)
+    torch.cuda.synchronize()
+    got = host(y)
+    ref = oracle.gelu(xb.f64())
+    err = np.abs(got - ref)
+    # the oracle's float64 1 + erf(x / sqrt 2) cancels below x ~ -8 (its
+    # absolute error there is ~1e-16 while GeLU falls below it), hence the
+    # absolute term; elsewhere a bf16 rounding step of the value
+    bound = 2.0 ** -8 * np.abs(ref) + 1e-15
+    worst = float(np.max(err / bound))
+    say(f"  max |err| / (2^-8 |ref| + 1e-15) = {worst:.3f}")
+    assert worst <= 1.0
+
+
 @pytest.mark.parametrize("act,m,h,f,plan", [
     ("swiglu", 3000, 64, 1536, (192, 12, 192)),
     ("swiglu", 1000, 136, 520, (64, 9, 64)),        # small tiles: 64 outputs each, ragged m and f
