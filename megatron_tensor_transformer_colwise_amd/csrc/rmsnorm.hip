@@ -56,10 +56,8 @@ __device__ __forceinline__ float row_inv_rms(float ss, int64_t h, float eps, flo
   return 1.0f / sqrtf(tot / (float)h + eps);
 }
 
-// y[e .. e + 8) = bf16(v * inv * gain[e .. e + 8)).
-__device__ __forceinline__ void emit8(const float (&v)[8], float inv, const float* gain, int64_t gi,
-                                      bf16_t* y, int64_t e) {
-  float gv[8];
+// gv = gain[8 gi .. 8 gi + 8), or ones without a gain.
+__device__ __forceinline__ void load_gain8(const float* gain, int64_t gi, float (&gv)[8]) {
   if (gain) {
     const f32x4 a = *reinterpret_cast<const f32x4*>(gain + gi * 8);
     const f32x4 b = *reinterpret_cast<const f32x4*>(gain + gi * 8 + 4);
@@ -72,11 +70,22 @@ __device__ __forceinline__ void emit8(const float (&v)[8], float inv, const floa
 #pragma unroll
     for (int i = 0; i < 8; ++i) gv[i] = 1.0f;
   }
+}
+
+// y[e .. e + 8) = bf16(v * inv * gv), gv the group's gains.
+__device__ __forceinline__ void emit8g(const float (&v)[8], float inv, const float (&gv)[8], bf16_t* y, int64_t e) {
   u32x4 o;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
     o[i] = pack_bf16x2(v[2 * i] * inv * gv[2 * i], v[2 * i + 1] * inv * gv[2 * i + 1]);
   *reinterpret_cast<u32x4*>(y + e) = o;
+}
+
+__device__ __forceinline__ void emit8(const float (&v)[8], float inv, const float* gain, int64_t gi,
+                                      bf16_t* y, int64_t e) {
+  float gv[8];
+  load_gain8(gain, gi, gv);
+  emit8g(v, inv, gv, y, e);
 }
 
 template <bool IN_BF16>
@@ -87,12 +96,16 @@ __global__ __launch_bounds__(NT) void rmsnorm_kernel(const void* x, const float*
   const int64_t base = row * h;
   const int64_t groups = h >> 3;
   float cache[MAX_CACHED][8];
+  // the gains of the cached groups are loaded with the row, so the
+  // normalisation after the row's reduction waits on no further load
+  float gcache[MAX_CACHED][8];
   float ss = 0.0f;
 #pragma unroll
   for (int i = 0; i < MAX_CACHED; ++i) {
     const int64_t gi = threadIdx.x + (int64_t)i * NT;
     if (gi < groups) {
       load8<IN_BF16>(x, base + gi * 8, cache[i]);
+      load_gain8(gain, gi, gcache[i]);
 #pragma unroll
       for (int e = 0; e < 8; ++e) ss += cache[i][e] * cache[i][e];
     }
@@ -107,7 +120,7 @@ __global__ __launch_bounds__(NT) void rmsnorm_kernel(const void* x, const float*
 #pragma unroll
   for (int i = 0; i < MAX_CACHED; ++i) {
     const int64_t gi = threadIdx.x + (int64_t)i * NT;
-    if (gi < groups) emit8(cache[i], inv, gain, gi, y, base + gi * 8);
+    if (gi < groups) emit8g(cache[i], inv, gcache[i], y, base + gi * 8);
   }
   for (int64_t gi = threadIdx.x + (int64_t)MAX_CACHED * NT; gi < groups; gi += NT) {
     float v[8];
@@ -205,16 +218,26 @@ __device__ __forceinline__ void sum_groups(const SumNormArgs& a, const int64_t (
 
 template <int T>
 __global__ __launch_bounds__(NT) void sum_rmsnorm_kernel(SumNormArgs a) {
-  // two groups loaded together (all their loads in flight before any add)
-  // while the registers hold them, else one
-  constexpr int G = T <= 8 ? 2 : 1;
-  static_assert(MAX_CACHED % G == 0, "cached groups come in batches of G");
+  // one group's loads (every partial's) in flight at a time: fewer registers
+  // than two, so more rows share a CU, which measured faster (t = 8, 8192 x
+  // 8192: 516 against 525 us per call back to back)
+  constexpr int G = 1;
   __shared__ float red[NT / 64];
   const int64_t h = a.h;
   const int64_t r = blockIdx.x;
   const int64_t base = ((r / a.run_rows) * a.run_stride + r % a.run_rows) * h;
   const int64_t groups = h >> 3;
   float cache[MAX_CACHED][8];
+  // the gains of the cached groups, loaded before the row so the
+  // normalisation after the row's reduction waits on no further load
+  float gcache[MAX_CACHED][8];
+  if (a.y) {
+#pragma unroll
+    for (int i = 0; i < MAX_CACHED; ++i) {
+      const int64_t gi = threadIdx.x + (int64_t)i * NT;
+      if (gi < groups) load_gain8(a.gain, gi, gcache[i]);
+    }
+  }
   float ss = 0.0f;
 #pragma unroll
   for (int i0 = 0; i0 < MAX_CACHED; i0 += G) {
@@ -252,7 +275,7 @@ __global__ __launch_bounds__(NT) void sum_rmsnorm_kernel(SumNormArgs a) {
 #pragma unroll
   for (int i = 0; i < MAX_CACHED; ++i) {
     const int64_t gi = threadIdx.x + (int64_t)i * NT;
-    if (gi < groups) emit8(cache[i], inv, a.gain, gi, a.y, base + gi * 8);
+    if (gi < groups) emit8g(cache[i], inv, gcache[i], a.y, base + gi * 8);
   }
   // rows wider than the register cache: the group's sum again (from the
   // sums this thread stored above, ordered by the barrier in row_inv_rms,
